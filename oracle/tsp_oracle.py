@@ -1,0 +1,271 @@
+"""fp64 CPU oracle for the TSP rank-share layer.  TEST INFRASTRUCTURE ONLY.
+
+Only ``tests/``, ``__graft_entry__.smoke()`` and the ``cpu_baseline`` leg of
+``bench.py`` may import this module.  The product path (the HIP library and its
+Python binding) never imports, links or calls it, and this module imports
+nothing from the product package.
+
+What it computes.  Tensor + Sequence Parallelism folds the tensor-parallel and
+sequence-parallel axes onto one mesh axis of size D: a device holds 1/D of every
+weight matrix and 1/D of the tokens (zubnet.ai, "Zyphra TSP folds TP+SP onto one
+GPU axis", para. 1).  The attention weight shards are applied one after another
+to the local tokens, K/V are gathered over a zigzag partition of the sequence,
+and the MLP weight shard pairs travel a ring while each device sums the partial
+products of its own tokens, which is what removes tensor parallelism's
+all-reduce (same page, para. 2).  All of this is an exact re-partitioning of one
+decoder layer, so the oracle computes the *plain, unsharded* layer for the
+rank's own tokens, in fp64, directly from its definition; the shard arrays are
+only reassembled into whole matrices.  Sharded forms appear in
+:func:`mlp_sharded` alone, which the pins use to check the method's identity
+(sum over shards = unsharded MLP) on the oracle itself.
+
+Readings of points the pages leave open:
+
+* zigzag partition: 2D equal chunks of C = S/(2D); rank r owns chunks r and
+  2D-1-r; local rows are the owned positions in ascending order;
+* ring order of shards: (r + k) mod D, k = 0..D-1;
+* layer: h1 = x + Attn(x), out = h1 + MLP(h1); MHA; no bias, no norm, no
+  positional encoding; GELU in its tanh form;
+* attention: causal with the diagonal included, scale 1/sqrt(hd);
+* O projection: row blocks of W_o by head shard (the shard's heads are the
+  input columns of ``wo[d]``);
+* the rank's own rows of the gathered K/V are the ones it projects itself;
+  the caller-supplied rows at those positions are replaced.
+
+Inputs are bf16 tensors (converted exactly to fp64); no intermediate is rounded.
+Matrix products use ``torch.matmul`` in fp64 as a library step; everything else
+(GELU, masking, softmax) is written out below.
+
+Parity status: every function here is pinned by ``tests/test_oracle_*.py``
+(library special cases, closed forms, invariants and brute force); none is
+"parity unpinned".
+"""
+from __future__ import annotations
+
+import math
+from dataclasses import dataclass
+
+import torch
+
+F64 = torch.float64
+
+
+def f64(t: torch.Tensor) -> torch.Tensor:
+    """Exact widening of a bf16 (or any float) tensor to fp64 on the CPU."""
+    return t.detach().to("cpu").to(F64)
+
+
+# ---------------------------------------------------------------------------
+# zigzag plan (para. 2: "zigzag partition" for load balancing of K/V)
+# ---------------------------------------------------------------------------
+@dataclass
+class Plan:
+    seq_len: int
+    D: int
+    rank: int
+    chunk_len: int
+    chunk_ids: list
+    chunk_starts: list
+    local_to_global: torch.Tensor  # int64 [S/D]
+    ring: list                     # shard visit order
+
+
+def zigzag_plan(seq_len: int, D: int, rank: int) -> Plan:
+    """The rank's share of the sequence under the zigzag partition.
+
+    The sequence is cut into 2D chunks of equal length; chunk c belongs to the
+    rank min(c, 2D-1-c), so every rank gets one chunk from the front half and
+    its mirror from the back half (equal causal work per rank).  The local rows
+    are the owned positions in ascending order.  Written as an enumeration over
+    all chunks (not a closed form) so it is independent of the HIP planner.
+    """
+    if D < 1 or not (0 <= rank < D) or seq_len <= 0 or seq_len % (2 * D) != 0:
+        raise ValueError("zigzag plan needs D >= 1, 0 <= rank < D and seq_len a positive multiple of 2D")
+    n_chunks = 2 * D
+    C = seq_len // n_chunks
+    owned = [c for c in range(n_chunks) if min(c, n_chunks - 1 - c) == rank]
+    positions = []
+    for c in owned:
+        positions.extend(range(c * C, (c + 1) * C))
+    l2g = torch.tensor(positions, dtype=torch.int64)
+    ring = [(rank + k) % D for k in range(D)]
+    return Plan(seq_len, D, rank, C, owned, [c * C for c in owned], l2g, ring)
+
+
+# ---------------------------------------------------------------------------
+# whole matrices from the shard arrays (para. 1: each device holds 1/D of each weight)
+# ---------------------------------------------------------------------------
+@dataclass
+class Whole:
+    wq: torch.Tensor  # [h, h] out x in
+    wk: torch.Tensor
+    wv: torch.Tensor
+    wo: torch.Tensor  # [h, h]
+    w1: torch.Tensor  # [F, h]
+    w2: torch.Tensor  # [h, F]
+
+
+def assemble(wqkv=None, wo=None, w1=None, w2=None, head_dim: int | None = None) -> Whole:
+    """Concatenate the D shards of each weight back into one fp64 matrix.
+
+    ``wqkv[d]`` holds, as output rows, shard d's Q heads, then its K heads, then
+    its V heads; shard d owns the contiguous head block d*H_s .. (d+1)*H_s-1.
+    ``wo[d]`` takes shard d's heads as input columns; ``w1[d]`` / ``w2[d]`` hold
+    the FFN block d as output rows / input columns.
+    """
+    wq = wk = wv = wo_ = w1_ = w2_ = None
+    if wqkv:
+        qs, ks, vs = [], [], []
+        for w in wqkv:
+            w = f64(w)
+            third = w.shape[0] // 3
+            qs.append(w[:third])
+            ks.append(w[third:2 * third])
+            vs.append(w[2 * third:])
+        wq, wk, wv = torch.cat(qs, 0), torch.cat(ks, 0), torch.cat(vs, 0)
+    if wo:
+        wo_ = torch.cat([f64(w) for w in wo], 1)
+    if w1:
+        w1_ = torch.cat([f64(w) for w in w1], 0)
+    if w2:
+        w2_ = torch.cat([f64(w) for w in w2], 1)
+    return Whole(wq, wk, wv, wo_, w1_, w2_)
+
+
+# ---------------------------------------------------------------------------
+# elementwise pieces
+# ---------------------------------------------------------------------------
+def gelu_tanh(u: torch.Tensor) -> torch.Tensor:
+    """GELU in its tanh form: 0.5 u (1 + tanh(sqrt(2/pi) (u + 0.044715 u^3)))."""
+    return 0.5 * u * (1.0 + torch.tanh(math.sqrt(2.0 / math.pi) * (u + 0.044715 * u * u * u)))
+
+
+def linear(x: torch.Tensor, w: torch.Tensor) -> torch.Tensor:
+    """x W^T for a weight stored out x in."""
+    return torch.matmul(x, w.t())
+
+
+# ---------------------------------------------------------------------------
+# causal attention of local queries against the full gathered K/V
+# ---------------------------------------------------------------------------
+def causal_attention(q: torch.Tensor, positions: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
+                     n_heads: int, head_dim: int) -> torch.Tensor:
+    """o[t, a] = sum_{j <= p_t} softmax_j(q[t,a] . k[j,a] / sqrt(hd)) v[j,a].
+
+    ``q`` [m, H*hd] are the query rows at global positions ``positions`` [m];
+    ``k``/``v`` [S, H*hd] the full-sequence keys and values (fp64).  Keys at
+    positions greater than the query's are excluded (causal; the diagonal is
+    included).  The softmax is written out: subtract the row maximum,
+    exponentiate, divide by the sum.
+    """
+    m = q.shape[0]
+    S = k.shape[0]
+    out = torch.empty((m, n_heads * head_dim), dtype=F64)
+    key_pos = torch.arange(S, dtype=torch.int64)
+    future = key_pos[None, :] > positions[:, None]          # [m, S]
+    scale = 1.0 / math.sqrt(head_dim)
+    for a in range(n_heads):
+        cols = slice(a * head_dim, (a + 1) * head_dim)
+        s = torch.matmul(q[:, cols], k[:, cols].t()) * scale  # [m, S]
+        s = s.masked_fill(future, float("-inf"))
+        s_max = s.max(dim=1, keepdim=True).values
+        e = torch.exp(s - s_max)
+        p = e / e.sum(dim=1, keepdim=True)
+        out[:, cols] = torch.matmul(p, v[:, cols])
+    return out
+
+
+def softmax_rows(q: torch.Tensor, positions: torch.Tensor, k: torch.Tensor, head: int,
+                 head_dim: int) -> torch.Tensor:
+    """The causal probability rows of one head (used by the pins)."""
+    S = k.shape[0]
+    cols = slice(head * head_dim, (head + 1) * head_dim)
+    s = torch.matmul(q[:, cols], k[:, cols].t()) / math.sqrt(head_dim)
+    future = torch.arange(S)[None, :] > positions[:, None]
+    s = s.masked_fill(future, float("-inf"))
+    e = torch.exp(s - s.max(dim=1, keepdim=True).values)
+    return e / e.sum(dim=1, keepdim=True)
+
+
+# ---------------------------------------------------------------------------
+# the layer's two halves for the rank's own tokens
+# ---------------------------------------------------------------------------
+def qkv_projection(x_local, wqkv, head_dim):
+    """q, k, v of the local tokens (fp64), all heads: the attention projections
+    produced by applying every attention weight shard to the local tokens (para. 2)."""
+    W = assemble(wqkv=wqkv, head_dim=head_dim)
+    x = f64(x_local)
+    return linear(x, W.wq), linear(x, W.wk), linear(x, W.wv)
+
+
+def gathered_kv(plan: Plan, k_own, v_own, k_full=None, v_full=None):
+    """Full-sequence K/V as the K/V all-gather delivers it (para. 2).
+
+    Rows at the rank's own positions are its own projections; all other rows are
+    the caller-supplied ones (``k_full``/``v_full``, bf16, the other ranks'
+    contributions).  With ``k_full`` None the own rows must cover the sequence
+    (D = 1).
+    """
+    S = plan.seq_len
+    h = k_own.shape[1]
+    if k_full is None:
+        k = torch.full((S, h), float("nan"), dtype=F64)
+        v = torch.full((S, h), float("nan"), dtype=F64)
+    else:
+        k, v = f64(k_full).clone(), f64(v_full).clone()
+    k[plan.local_to_global] = k_own
+    v[plan.local_to_global] = v_own
+    return k, v
+
+
+def attn_forward(plan: Plan, x_local, wqkv, wo, n_heads, head_dim, k_full=None, v_full=None,
+                 residual=True, rows=None, k_own=None, v_own=None):
+    """Attention half of the layer for the rank's local rows (or the subset ``rows``).
+
+    Returns (out [m, h], q_own [n, h], k_own [n, h], v_own [n, h]) in fp64, where
+    out = [x +] concat_a(o_a) W_o^T.  ``k_own``/``v_own`` may be passed in to skip
+    recomputing them.
+    """
+    W = assemble(wqkv=wqkv, wo=wo, head_dim=head_dim)
+    x = f64(x_local)
+    sel = torch.arange(x.shape[0]) if rows is None else torch.as_tensor(rows, dtype=torch.int64)
+    q = linear(x[sel], W.wq)
+    if k_own is None:
+        k_own = linear(x, W.wk)
+        v_own = linear(x, W.wv)
+    k, v = gathered_kv(plan, k_own, v_own, k_full, v_full)
+    o = causal_attention(q, plan.local_to_global[sel], k, v, n_heads, head_dim)
+    out = linear(o, W.wo)
+    if residual:
+        out = out + x[sel]
+    return out, q, k_own, v_own
+
+
+def mlp_forward(x, w1, w2, residual=True, rows=None):
+    """y = [x +] GELU(x W1^T) W2^T for the given rows (unsharded form)."""
+    W = assemble(w1=w1, w2=w2)
+    xx = f64(x)
+    if rows is not None:
+        xx = xx[torch.as_tensor(rows, dtype=torch.int64)]
+    y = linear(gelu_tanh(linear(xx, W.w1)), W.w2)
+    return xx + y if residual else y
+
+
+def mlp_sharded(x, w1, w2, order):
+    """The method's MLP: shard pairs visited in ``order``, partial products summed
+    locally in place of the all-reduce (para. 2).  Used only to pin the identity
+    sum over shards = unsharded MLP."""
+    xx = f64(x)
+    y = torch.zeros((xx.shape[0], f64(w2[0]).shape[0]), dtype=F64)
+    for d in order:
+        y = y + linear(gelu_tanh(linear(xx, f64(w1[d]))), f64(w2[d]))
+    return y
+
+
+def layer_forward(plan: Plan, x_local, wqkv, wo, w1, w2, n_heads, head_dim, k_full=None,
+                  v_full=None, rows=None):
+    """One decoder layer for the local rows: h1 = x + Attn(x); out = h1 + MLP(h1)."""
+    h1, _, k_own, v_own = attn_forward(plan, x_local, wqkv, wo, n_heads, head_dim, k_full, v_full,
+                                       residual=True, rows=rows)
+    out = mlp_forward(h1, w1, w2, residual=True)
+    return out, k_own, v_own
