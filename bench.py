@@ -1,0 +1,238 @@
+#!/usr/bin/env python3
+"""Benchmark of the TSP rank-share layer on one MI355X.
+
+Default workload: the full rank-share forward of the 7B dense decoder at 128K
+(32 layers, h=4096, 32 heads x 128, FFN 16384, bf16, D=8, S=131072, rank 0,
+16384 local tokens).  One step = the whole hot path over one batch: for each of
+the 32 layers, the shard-iterated QKV projection with the K/V scatter, causal
+attention of the two zigzag chunks against that layer's gathered K/V, the O
+projection split-K with the residual, and the ring MLP with the residual; the
+output of layer l is the input of layer l+1.  All inputs (weights, generated
+per-layer K/V, x) are resident in HBM before timing starts.
+
+The step calls the library's step-level entry points in the order
+tsp_layer_forward composes them, with HIP events recorded between them on the
+launch stream: the per-launch time of the attention kernel (the dominant one,
+about 73% of the layer's FLOPs) gives the roofline figure.
+
+Prints ONE JSON line.  ``--gpus`` above 1 is refused: this build runs on one GPU.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import torch
+
+from folded_tensor_sequence_tsp_amd import synth, tsp
+
+PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
+PEAK_HBM_GBS = 8000.0        # MI355X HBM3E
+METRIC = "local tokens/sec per 7B TSP layer (D=8, 128K seq) + % bf16 MFMA peak"
+
+
+def layer_flops(n, S, D, C, d):
+    """Algorithmic FLOPs of one rank-share layer, by step."""
+    h, F, H, hd = d.hidden, d.ffn, d.n_heads, d.head_dim
+    pairs = 2 * D * C * C + C  # (query, key) pairs with key <= query, per head
+    return {
+        "qkv": 2.0 * n * h * 3 * h,
+        "attn": 4.0 * hd * H * pairs,
+        "oproj": 2.0 * n * h * h,
+        "mlp": 4.0 * n * h * F,
+    }
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=5)
+    ap.add_argument("--warmup", type=int, default=2)
+    ap.add_argument("--workload", default="full_7b_128k", choices=["full_7b_128k", "stream_7b_16k"])
+    ap.add_argument("--layers", type=int, default=None, help="layers per step (default: the workload's)")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-rows", type=int, default=4, help="oracle sample rows per timing call")
+    return ap.parse_args()
+
+
+def build_inputs(W, n_layers, dev):
+    d, D, S = W.dims, W.D, W.seq_len
+    layers = []
+    for l in range(n_layers):
+        lw = synth.layer_weights(W.wid, d, D, layer=l, device=dev)
+        kf, vf = synth.gathered_kv(W.wid, S, d.hidden, layer=l, device=dev)
+        layers.append((lw, kf, vf))
+    return layers
+
+
+def cpu_baseline(W, plan, x_local, layer0, rows_per_call):
+    """Time the fp64 oracle on a bounded sample of layer 0 of the same workload
+    and extrapolate to local tokens/s per layer.
+
+    Call A: attention half for `rows_per_call` rows, which also computes the K/V
+    projections of all local rows (the fixed cost).  Call B: attention half for
+    2*rows_per_call other rows with those K/V reused (per-row cost).  Call C:
+    the MLP for the same rows.  Full layer = fixed + n * per-row."""
+    from oracle import tsp_oracle as O  # test infrastructure, used only here
+    lw, kf, vf = layer0
+    d = W.dims
+    lc = lw.to("cpu")
+    x = x_local.cpu()
+    kf_c, vf_c = kf.cpu(), vf.cpu()
+    oplan = O.zigzag_plan(W.seq_len, W.D, W.rank)
+    n = plan.n_local
+    g = torch.Generator().manual_seed(7)
+    perm = torch.randperm(n, generator=g)
+    ra, rb = perm[:rows_per_call], perm[rows_per_call:3 * rows_per_call]
+    t0 = time.perf_counter()
+    _, _, k_own, v_own = O.attn_forward(oplan, x, lc.wqkv, lc.wo, d.n_heads, d.head_dim, kf_c, vf_c, rows=ra)
+    t1 = time.perf_counter()
+    h1, _, _, _ = O.attn_forward(oplan, x, lc.wqkv, lc.wo, d.n_heads, d.head_dim, kf_c, vf_c, rows=rb,
+                                 k_own=k_own, v_own=v_own)
+    t2 = time.perf_counter()
+    O.mlp_forward(h1, lc.w1, lc.w2, residual=True)
+    t3 = time.perf_counter()
+    per_row = (t2 - t1 + t3 - t2) / len(rb)
+    fixed = max((t1 - t0) - len(ra) * (t2 - t1) / len(rb), 0.0)
+    layer_s = fixed + n * per_row
+    return {
+        "value": n / layer_s,
+        "unit": "local tokens/s per layer",
+        "cores": torch.get_num_threads(),
+        "kind": "oracle",
+        "sample": (f"fp64 oracle on layer 0 of the same workload: attention half for {len(ra)} rows with the K/V "
+                   f"projection of all {n} local rows ({t1 - t0:.1f} s), attention half + MLP for {len(rb)} more "
+                   f"rows ({t3 - t1:.1f} s); per layer = fixed + {n} x per-row = {layer_s:.0f} s"),
+        "measured_s": round(t3 - t0, 2),
+    }
+
+
+def main():
+    args = parse()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures the rank-share layer of ONE GPU; runs on more than one GPU "
+              "(--gpus above 1) are not supported.", file=sys.stderr)
+        sys.exit(2)
+    if not torch.cuda.is_available():
+        print("no HIP device", file=sys.stderr)
+        sys.exit(1)
+    torch.cuda.set_device(0)
+    dev = "cuda"
+    tsp.lib()
+
+    W = synth.WORKLOADS[args.workload]
+    n_layers = args.layers or W.n_layers
+    d, D, S = W.dims, W.D, W.seq_len
+    plan, _, _ = tsp.zigzag_plan(S, D, W.rank)
+    n, h = plan.n_local, d.hidden
+    dims = tsp.make_dims(d.hidden, d.n_heads, d.head_dim, d.ffn)
+
+    print(f"[bench] generating inputs: {W.name}, {n_layers} layers", file=sys.stderr, flush=True)
+    layers = build_inputs(W, n_layers, dev)
+    x0 = synth.activations(W.wid, n, h, device=dev)
+    q = torch.empty(n, h, dtype=torch.bfloat16, device=dev)
+    a = torch.empty(n, h, dtype=torch.bfloat16, device=dev)
+    h1 = torch.empty(n, h, dtype=torch.bfloat16, device=dev)
+    bufs = [torch.empty(n, h, dtype=torch.bfloat16, device=dev) for _ in range(2)]
+    ws = tsp.alloc_workspace(n, dims, D, tsp.WS_MLP)
+    torch.cuda.synchronize()
+
+    stream = torch.cuda.current_stream()
+    stages = ["qkv", "attn", "oproj", "mlp"]
+
+    def step(events=None):
+        x = x0
+        for l, (lw, kf, vf) in enumerate(layers):
+            out = bufs[l % 2]
+            ev = events[l] if events is not None else None
+            if ev: ev[0].record(stream)
+            tsp.attn_project(plan, dims, x, lw.wqkv, kf, vf, q)
+            if ev: ev[1].record(stream)
+            tsp.attn_core(plan, dims, q, kf, vf, a)
+            if ev: ev[2].record(stream)
+            tsp.attn_out(dims, D, plan.rank, a, lw.wo, x, h1)
+            if ev: ev[3].record(stream)
+            tsp.mlp_forward(dims, D, plan.rank, h1, lw.w1, lw.w2, h1, out, ws)
+            if ev: ev[4].record(stream)
+            x = out
+        return x
+
+    print(f"[bench] warmup {args.warmup}", file=sys.stderr, flush=True)
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+
+    events = [[[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(n_layers)]
+              for _ in range(args.steps)]
+    print(f"[bench] timing {args.steps} steps", file=sys.stderr, flush=True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for s in range(args.steps):
+        step(events[s])
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+
+    stage_ms = {k: 0.0 for k in stages}
+    for s in range(args.steps):
+        for l in range(n_layers):
+            ev = events[s][l]
+            for i, k in enumerate(stages):
+                stage_ms[k] += ev[i].elapsed_time(ev[i + 1])
+    launches = args.steps * n_layers
+    stage_ms = {k: v / launches for k, v in stage_ms.items()}   # ms per launch
+    fl = layer_flops(n, S, D, plan.chunk_len, d)
+
+    ms_per_step = elapsed * 1e3 / args.steps
+    layer_ms = ms_per_step / n_layers
+    value = n / (layer_ms * 1e-3)
+    total_flops = sum(fl.values())
+    attn_tflops = fl["attn"] / (stage_ms["attn"] * 1e-3) / 1e12
+
+    result = {
+        "metric": METRIC,
+        "value": round(value, 1),
+        "unit": "local tokens/s per layer",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 3),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {
+            "workload": W.name,
+            "layers_per_step": n_layers,
+            "seq_len": S, "D": D, "rank": W.rank, "n_local": n,
+            "hidden": d.hidden, "n_heads": d.n_heads, "head_dim": d.head_dim, "ffn": d.ffn,
+        },
+        "layer_ms": round(layer_ms, 4),
+        "layer_tflops": round(total_flops / (layer_ms * 1e-3) / 1e12, 1),
+        "layer_mfma_frac": round(total_flops / (layer_ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4),
+        "stages_ms_per_launch": {k: round(v, 4) for k, v in stage_ms.items()},
+        "stages_tflops": {k: round(fl[k] / (stage_ms[k] * 1e-3) / 1e12, 1) for k in stages},
+        "roofline": {
+            "kernel": "attn_kernel<128> (tsp_attn_core)",
+            "bound": "mfma",
+            "achieved": round(attn_tflops, 1),
+            "peak": PEAK_BF16_TFLOPS,
+            "unit": "TFLOP/s",
+            "frac": round(attn_tflops / PEAK_BF16_TFLOPS, 4),
+            "flops_per_launch": fl["attn"],
+            "ms_per_launch": round(stage_ms["attn"], 4),
+            "traffic": None,
+        },
+        "cpu_baseline": None,
+    }
+    if not args.no_cpu_baseline:
+        print("[bench] cpu baseline (fp64 oracle, bounded sample)", file=sys.stderr, flush=True)
+        result["cpu_baseline"] = cpu_baseline(W, plan, x0, layers[0], args.cpu_rows)
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,62 @@
+"""Build libtsp.so (HIP for gfx950) in-tree with hipcc.
+
+``python -m folded_tensor_sequence_tsp_amd.build`` or :func:`build`.  The
+library lands next to this file; the ctypes binding loads it from there.
+"""
+from __future__ import annotations
+
+import os
+import shutil
+import subprocess
+import sys
+import tempfile
+from concurrent.futures import ThreadPoolExecutor
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+ROOT = os.path.dirname(PKG)
+CSRC = os.path.join(PKG, "csrc")
+LIB = os.path.join(PKG, "libtsp.so")
+SOURCES = ["tsp_api.cpp", "gemm.hip", "attention.hip"]
+
+ARCH = "gfx950"
+# Packed fp32 VALU forms are switched off (they are only a codegen choice here).
+HIP_FLAGS = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}",
+             "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+             "-I", os.path.join(ROOT, "include"), "-I", CSRC]
+
+
+def hipcc() -> str:
+    for cand in (os.environ.get("HIPCC"), shutil.which("hipcc"), "/opt/rocm/bin/hipcc"):
+        if cand and os.path.exists(cand):
+            return cand
+    raise RuntimeError("hipcc not found")
+
+
+def build(verbose: bool = False) -> str:
+    cc = hipcc()
+    with tempfile.TemporaryDirectory(prefix="tsp_build_") as tmp:
+        objs = []
+        cmds = []
+        for src in SOURCES:
+            obj = os.path.join(tmp, src + ".o")
+            lang = ["-x", "hip"]
+            cmds.append([cc, *lang, *HIP_FLAGS, "-c", os.path.join(CSRC, src), "-o", obj])
+            objs.append(obj)
+
+        def run(cmd):
+            r = subprocess.run(cmd, capture_output=True, text=True)
+            if r.returncode != 0:
+                raise RuntimeError(f"hipcc failed ({r.returncode}):\n{' '.join(cmd)}\n{r.stderr}")
+            if verbose:
+                sys.stderr.write(r.stderr)
+
+        with ThreadPoolExecutor(max_workers=len(cmds)) as ex:
+            list(ex.map(run, cmds))
+        tmp_lib = LIB + ".tmp"
+        run([cc, f"--offload-arch={ARCH}", "-shared", "-fPIC", *objs, "-o", tmp_lib])
+        os.replace(tmp_lib, LIB)
+    return LIB
+
+
+if __name__ == "__main__":
+    print(build(verbose="-v" in sys.argv))

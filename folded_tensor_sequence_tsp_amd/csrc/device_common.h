@@ -1,0 +1,52 @@
+// Device helpers shared by the gfx950 kernels of libtsp: vector types for the
+// MFMA operands, bf16 rounding and the tanh-form GELU in fp32.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace tsp {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+
+// fp32 -> bf16 bits with the hardware conversion (v_cvt_pk_bf16_f32, round to
+// nearest even).
+__device__ __forceinline__ uint16_t f32_to_bf16(float f) {
+  return __builtin_bit_cast(uint16_t, (__bf16)f);
+}
+
+// Two fp32 -> packed bf16x2 (low half = a) in one v_cvt_pk_bf16_f32.
+__device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
+  bf16x2 v;
+  v[0] = (__bf16)a;
+  v[1] = (__bf16)b;
+  return __builtin_bit_cast(uint32_t, v);
+}
+
+__device__ __forceinline__ float bf16_to_f32(uint16_t b) { return __uint_as_float((uint32_t)b << 16); }
+
+// GELU, tanh form: 0.5 u (1 + tanh(sqrt(2/pi) (u + 0.044715 u^3))), with
+// tanh(z) = 1 - 2 / (exp(2z) + 1) and exp(2z) = 2^(2z log2 e) on the hardware
+// exp2.  Saturates correctly: exp2 -> inf gives tanh = 1, exp2 -> 0 gives -1.
+__device__ __forceinline__ float gelu_tanh(float u) {
+  const float sqrt_2_over_pi = 0.79788456080286535588f;
+  const float two_log2e = 2.88539008177792681472f;
+  float z = sqrt_2_over_pi * (u + 0.044715f * u * u * u);
+  float e = __builtin_amdgcn_exp2f(two_log2e * z);
+  float t = 1.0f - 2.0f * __builtin_amdgcn_rcpf(e + 1.0f);
+  return 0.5f * u * (1.0f + t);
+}
+
+__device__ __forceinline__ f32x16 mfma32(const bf16x8& a, const bf16x8& b, const f32x16& c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+
+__device__ __forceinline__ bf16x8 as_bf16x8(const u32x4& v) { return __builtin_bit_cast(bf16x8, v); }
+
+}  // namespace tsp

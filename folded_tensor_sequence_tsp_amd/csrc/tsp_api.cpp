@@ -1,0 +1,365 @@
+// C-ABI entry points of libtsp: zigzag planner, argument validation and the
+// composition of the rank-share layer out of the HIP kernels.  Every check runs
+// before the first launch, so an error status means nothing was enqueued.
+#include <string.h>
+
+#include "kernels.h"
+
+using namespace tsp;
+
+namespace {
+
+constexpr int64_t MLP_TOKEN_BLOCK = 16384;  // tokens per GELU(x W1^T) workspace block
+constexpr size_t WS_ALIGN = 256;
+
+size_t round_up(size_t x) { return (x + WS_ALIGN - 1) / WS_ALIGN * WS_ALIGN; }
+
+bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+
+tsp_status check_ptr(const void* p) {
+  if (!p) return TSP_ERR_INVALID_ARG;
+  if (!aligned16(p)) return TSP_ERR_ALIGNMENT;
+  return TSP_OK;
+}
+
+tsp_status check_ptr_nullable(const void* p) { return (p && !aligned16(p)) ? TSP_ERR_ALIGNMENT : TSP_OK; }
+
+tsp_status check_shards(const uint16_t* const* w, int32_t D) {
+  if (!w) return TSP_ERR_INVALID_ARG;
+  for (int d = 0; d < D; ++d) {
+    tsp_status s = check_ptr(w[d]);
+    if (s != TSP_OK) return s;
+  }
+  return TSP_OK;
+}
+
+// Shape rules shared by every call.  `need_attn` / `need_mlp` add the widths
+// the attention and MLP kernels need.
+tsp_status check_dims(const tsp_dims* d, int32_t D, bool need_attn, bool need_mlp) {
+  if (!d) return TSP_ERR_INVALID_ARG;
+  if (D < 1 || D > TSP_MAX_D) return TSP_ERR_INVALID_ARG;
+  if (d->hidden <= 0 || d->n_heads <= 0 || d->head_dim <= 0 || d->ffn <= 0) return TSP_ERR_SHAPE;
+  if ((int64_t)d->n_heads * d->head_dim != d->hidden) return TSP_ERR_SHAPE;
+  if (d->hidden % 64 != 0) return TSP_ERR_UNSUPPORTED;
+  if (need_attn) {
+    if (d->n_heads % D != 0) return TSP_ERR_SHAPE;
+    if (d->head_dim != 64 && d->head_dim != 128) return TSP_ERR_UNSUPPORTED;
+  }
+  if (need_mlp) {
+    if (d->ffn % D != 0) return TSP_ERR_SHAPE;
+    if ((d->ffn / D) % 64 != 0) return TSP_ERR_UNSUPPORTED;
+  }
+  return TSP_OK;
+}
+
+// A plan must be exactly what tsp_zigzag_plan produces for its (S, D, rank).
+tsp_status check_plan(const tsp_plan* p) {
+  if (!p) return TSP_ERR_INVALID_ARG;
+  tsp_plan ref;
+  tsp_status s = tsp_zigzag_plan(p->seq_len, p->D, p->rank, &ref, nullptr, nullptr);
+  if (s != TSP_OK) return s;
+  if (memcmp(&ref, p, sizeof(ref)) != 0) {
+    // compare field by field (padding bytes of the caller's struct may differ)
+    if (ref.seq_len != p->seq_len || ref.chunk_len != p->chunk_len || ref.n_local != p->n_local ||
+        ref.D != p->D || ref.rank != p->rank || ref.chunk_id[0] != p->chunk_id[0] ||
+        ref.chunk_id[1] != p->chunk_id[1] || ref.chunk_start[0] != p->chunk_start[0] ||
+        ref.chunk_start[1] != p->chunk_start[1])
+      return TSP_ERR_SHAPE;
+  }
+  return TSP_OK;
+}
+
+size_t ws_attn(int64_t n, const tsp_dims* d) { return 2 * round_up((size_t)n * d->hidden * 2); }
+
+size_t ws_mlp(int64_t n, const tsp_dims* d) {
+  const int64_t mb = n < MLP_TOKEN_BLOCK ? n : MLP_TOKEN_BLOCK;
+  return round_up((size_t)mb * d->ffn * 2);
+}
+
+tsp_status from_hip(hipError_t e) { return e == hipSuccess ? TSP_OK : TSP_ERR_HIP; }
+
+// ---- launches (arguments already validated) ---------------------------------
+
+tsp_status run_project(const tsp_plan* plan, const tsp_dims* dims, const uint16_t* x,
+                       const uint16_t* const* wqkv, uint16_t* k_full, uint16_t* v_full, uint16_t* q_out,
+                       hipStream_t stream) {
+  GemmArgs g{};
+  g.A = x;
+  g.lda = dims->hidden;
+  for (int d = 0; d < plan->D; ++d) g.B[d] = wqkv[d];
+  const int hs = dims->n_heads / plan->D;
+  g.M = (int32_t)plan->n_local;
+  g.N_s = 3 * hs * dims->head_dim;
+  g.K_s = dims->hidden;
+  g.n_shards = plan->D;
+  g.k_shards = 1;
+  g.ring_start = 0;
+  g.epilogue = EPI_QKV;
+  g.q_out = q_out;
+  g.k_full = k_full;
+  g.v_full = v_full;
+  g.heads_per_shard = hs;
+  g.head_dim = dims->head_dim;
+  g.hidden = dims->hidden;
+  g.chunk_len = plan->chunk_len;
+  g.chunk_start0 = plan->chunk_start[0];
+  g.chunk_start1 = plan->chunk_start[1];
+  return from_hip(launch_gemm(g, stream));
+}
+
+tsp_status run_core(const tsp_plan* plan, const tsp_dims* dims, const uint16_t* q, const uint16_t* k_full,
+                    const uint16_t* v_full, uint16_t* attn_out, hipStream_t stream) {
+  AttnArgs a{};
+  a.q = q;
+  a.k = k_full;
+  a.v = v_full;
+  a.o = attn_out;
+  a.seq_len = plan->seq_len;
+  a.chunk_len = plan->chunk_len;
+  a.chunk_start0 = plan->chunk_start[0];
+  a.chunk_start1 = plan->chunk_start[1];
+  a.hidden = dims->hidden;
+  a.n_heads = dims->n_heads;
+  a.head_dim = dims->head_dim;
+  return from_hip(launch_attention(a, stream));
+}
+
+tsp_status run_out(int64_t n, const tsp_dims* dims, int32_t D, int32_t start, const uint16_t* attn,
+                   const uint16_t* const* wo, const uint16_t* residual, uint16_t* out, hipStream_t stream) {
+  GemmArgs g{};
+  g.A = attn;
+  g.lda = dims->hidden;
+  for (int d = 0; d < D; ++d) g.B[d] = wo[d];
+  g.M = (int32_t)n;
+  g.N_s = dims->hidden;
+  g.K_s = (dims->n_heads / D) * dims->head_dim;
+  g.n_shards = 1;
+  g.k_shards = D;
+  g.ring_start = start;
+  g.epilogue = EPI_RESID;
+  g.out = out;
+  g.ldo = dims->hidden;
+  g.residual = residual;
+  return from_hip(launch_gemm(g, stream));
+}
+
+tsp_status run_mlp(int64_t n, const tsp_dims* dims, int32_t D, int32_t start, const uint16_t* x,
+                   const uint16_t* const* w1, const uint16_t* const* w2, const uint16_t* residual, uint16_t* y,
+                   void* ws, hipStream_t stream) {
+  uint16_t* hbuf = static_cast<uint16_t*>(ws);
+  const int64_t h = dims->hidden;
+  const int32_t fs = dims->ffn / D;
+  for (int64_t b0 = 0; b0 < n; b0 += MLP_TOKEN_BLOCK) {
+    const int64_t mb = (n - b0) < MLP_TOKEN_BLOCK ? (n - b0) : MLP_TOKEN_BLOCK;
+    // GELU(x W1_d^T) for every shard d -> hbuf[:, d*F_s .. (d+1)*F_s)
+    GemmArgs g1{};
+    g1.A = x + b0 * h;
+    g1.lda = h;
+    for (int d = 0; d < D; ++d) g1.B[d] = w1[d];
+    g1.M = (int32_t)mb;
+    g1.N_s = fs;
+    g1.K_s = (int32_t)h;
+    g1.n_shards = D;
+    g1.k_shards = 1;
+    g1.epilogue = EPI_GELU;
+    g1.out = hbuf;
+    g1.ldo = dims->ffn;
+    tsp_status s = from_hip(launch_gemm(g1, stream));
+    if (s != TSP_OK) return s;
+    // y = [residual +] sum over shards in ring order of hbuf[:, d block] W2_d^T
+    GemmArgs g2{};
+    g2.A = hbuf;
+    g2.lda = dims->ffn;
+    for (int d = 0; d < D; ++d) g2.B[d] = w2[d];
+    g2.M = (int32_t)mb;
+    g2.N_s = (int32_t)h;
+    g2.K_s = fs;
+    g2.n_shards = 1;
+    g2.k_shards = D;
+    g2.ring_start = start;
+    g2.epilogue = EPI_RESID;
+    g2.out = y + b0 * h;
+    g2.ldo = h;
+    g2.residual = residual ? residual + b0 * h : nullptr;
+    s = from_hip(launch_gemm(g2, stream));
+    if (s != TSP_OK) return s;
+  }
+  return TSP_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+tsp_status tsp_zigzag_plan(int64_t seq_len, int32_t D, int32_t rank, tsp_plan* plan, int64_t* local_to_global,
+                           int32_t* ring_order) {
+  if (!plan) return TSP_ERR_INVALID_ARG;
+  if (D < 1 || D > TSP_MAX_D) return TSP_ERR_INVALID_ARG;
+  if (rank < 0 || rank >= D) return TSP_ERR_INVALID_ARG;
+  if (seq_len <= 0 || seq_len % (2 * (int64_t)D) != 0) return TSP_ERR_SHAPE;
+  if (seq_len / D > INT32_MAX) return TSP_ERR_UNSUPPORTED;
+  tsp_plan p;
+  memset(&p, 0, sizeof(p));
+  p.seq_len = seq_len;
+  p.D = D;
+  p.rank = rank;
+  p.chunk_len = seq_len / (2 * (int64_t)D);
+  p.n_local = 2 * p.chunk_len;
+  p.chunk_id[0] = rank;
+  p.chunk_id[1] = 2 * D - 1 - rank;
+  p.chunk_start[0] = (int64_t)p.chunk_id[0] * p.chunk_len;
+  p.chunk_start[1] = (int64_t)p.chunk_id[1] * p.chunk_len;
+  if (local_to_global) {
+    for (int64_t i = 0; i < p.n_local; ++i)
+      local_to_global[i] = i < p.chunk_len ? p.chunk_start[0] + i : p.chunk_start[1] + (i - p.chunk_len);
+  }
+  if (ring_order) {
+    for (int k = 0; k < D; ++k) ring_order[k] = (rank + k) % D;
+  }
+  *plan = p;
+  return TSP_OK;
+}
+
+size_t tsp_workspace_size(int64_t n_tokens, const tsp_dims* dims, int32_t D, int32_t kind) {
+  if (n_tokens < 0) return 0;
+  switch (kind) {
+    case TSP_WS_ATTN:
+      if (check_dims(dims, D, true, false) != TSP_OK) return 0;
+      return ws_attn(n_tokens, dims);
+    case TSP_WS_MLP:
+      if (check_dims(dims, D, false, true) != TSP_OK) return 0;
+      return ws_mlp(n_tokens, dims);
+    case TSP_WS_LAYER: {
+      if (check_dims(dims, D, true, true) != TSP_OK) return 0;
+      const size_t a = ws_attn(n_tokens, dims), m = ws_mlp(n_tokens, dims);
+      return round_up((size_t)n_tokens * dims->hidden * 2) + (a > m ? a : m);
+    }
+    default:
+      return 0;
+  }
+}
+
+tsp_status tsp_attn_project(const tsp_plan* plan, const tsp_dims* dims, const uint16_t* x_local,
+                            const uint16_t* const* wqkv, uint16_t* k_full, uint16_t* v_full, uint16_t* q_out,
+                            hipStream_t stream) {
+  tsp_status s;
+  if ((s = check_plan(plan)) != TSP_OK) return s;
+  if ((s = check_dims(dims, plan->D, true, false)) != TSP_OK) return s;
+  if ((s = check_ptr(x_local)) != TSP_OK || (s = check_shards(wqkv, plan->D)) != TSP_OK ||
+      (s = check_ptr(k_full)) != TSP_OK || (s = check_ptr(v_full)) != TSP_OK || (s = check_ptr(q_out)) != TSP_OK)
+    return s;
+  return run_project(plan, dims, x_local, wqkv, k_full, v_full, q_out, stream);
+}
+
+tsp_status tsp_attn_core(const tsp_plan* plan, const tsp_dims* dims, const uint16_t* q, const uint16_t* k_full,
+                         const uint16_t* v_full, uint16_t* attn_out, hipStream_t stream) {
+  tsp_status s;
+  if ((s = check_plan(plan)) != TSP_OK) return s;
+  if ((s = check_dims(dims, plan->D, true, false)) != TSP_OK) return s;
+  if ((s = check_ptr(q)) != TSP_OK || (s = check_ptr(k_full)) != TSP_OK || (s = check_ptr(v_full)) != TSP_OK ||
+      (s = check_ptr(attn_out)) != TSP_OK)
+    return s;
+  if (attn_out == q) return TSP_ERR_INVALID_ARG;
+  return run_core(plan, dims, q, k_full, v_full, attn_out, stream);
+}
+
+tsp_status tsp_attn_out(int64_t n_tokens, const tsp_dims* dims, int32_t D, int32_t start_shard,
+                        const uint16_t* attn, const uint16_t* const* wo, const uint16_t* residual, uint16_t* out,
+                        hipStream_t stream) {
+  tsp_status s;
+  if ((s = check_dims(dims, D, true, false)) != TSP_OK) return s;
+  if (n_tokens < 0) return TSP_ERR_SHAPE;
+  if (n_tokens > INT32_MAX) return TSP_ERR_UNSUPPORTED;
+  if (start_shard < 0 || start_shard >= D) return TSP_ERR_INVALID_ARG;
+  if ((s = check_ptr(attn)) != TSP_OK || (s = check_shards(wo, D)) != TSP_OK ||
+      (s = check_ptr_nullable(residual)) != TSP_OK || (s = check_ptr(out)) != TSP_OK)
+    return s;
+  if (out == attn) return TSP_ERR_INVALID_ARG;
+  return run_out(n_tokens, dims, D, start_shard, attn, wo, residual, out, stream);
+}
+
+tsp_status tsp_attn_forward(const tsp_plan* plan, const tsp_dims* dims, const uint16_t* x_local,
+                            const uint16_t* const* wqkv, const uint16_t* const* wo, uint16_t* k_full,
+                            uint16_t* v_full, const uint16_t* residual, uint16_t* out, void* workspace,
+                            size_t ws_bytes, hipStream_t stream) {
+  tsp_status s;
+  if ((s = check_plan(plan)) != TSP_OK) return s;
+  if ((s = check_dims(dims, plan->D, true, false)) != TSP_OK) return s;
+  if ((s = check_ptr(x_local)) != TSP_OK || (s = check_shards(wqkv, plan->D)) != TSP_OK ||
+      (s = check_shards(wo, plan->D)) != TSP_OK || (s = check_ptr(k_full)) != TSP_OK ||
+      (s = check_ptr(v_full)) != TSP_OK || (s = check_ptr_nullable(residual)) != TSP_OK ||
+      (s = check_ptr(out)) != TSP_OK)
+    return s;
+  if (out == x_local) return TSP_ERR_INVALID_ARG;
+  if (!workspace) return TSP_ERR_WORKSPACE;
+  if (!aligned16(workspace)) return TSP_ERR_ALIGNMENT;
+  if (ws_bytes < ws_attn(plan->n_local, dims)) return TSP_ERR_WORKSPACE;
+  uint16_t* qbuf = static_cast<uint16_t*>(workspace);
+  uint16_t* abuf = qbuf + round_up((size_t)plan->n_local * dims->hidden * 2) / 2;
+  if ((s = run_project(plan, dims, x_local, wqkv, k_full, v_full, qbuf, stream)) != TSP_OK) return s;
+  if ((s = run_core(plan, dims, qbuf, k_full, v_full, abuf, stream)) != TSP_OK) return s;
+  return run_out(plan->n_local, dims, plan->D, plan->rank, abuf, wo, residual, out, stream);
+}
+
+tsp_status tsp_mlp_forward(int64_t n_tokens, const tsp_dims* dims, int32_t D, int32_t start_shard,
+                           const uint16_t* x, const uint16_t* const* w1, const uint16_t* const* w2,
+                           const uint16_t* residual, uint16_t* y, void* workspace, size_t ws_bytes,
+                           hipStream_t stream) {
+  tsp_status s;
+  if ((s = check_dims(dims, D, false, true)) != TSP_OK) return s;
+  if (n_tokens < 0) return TSP_ERR_SHAPE;
+  if (n_tokens > INT32_MAX) return TSP_ERR_UNSUPPORTED;
+  if (start_shard < 0 || start_shard >= D) return TSP_ERR_INVALID_ARG;
+  if ((s = check_ptr(x)) != TSP_OK || (s = check_shards(w1, D)) != TSP_OK || (s = check_shards(w2, D)) != TSP_OK ||
+      (s = check_ptr_nullable(residual)) != TSP_OK || (s = check_ptr(y)) != TSP_OK)
+    return s;
+  if (y == x && residual != x) return TSP_ERR_INVALID_ARG;
+  if (!workspace) return TSP_ERR_WORKSPACE;
+  if (!aligned16(workspace)) return TSP_ERR_ALIGNMENT;
+  if (ws_bytes < ws_mlp(n_tokens, dims)) return TSP_ERR_WORKSPACE;
+  return run_mlp(n_tokens, dims, D, start_shard, x, w1, w2, residual, y, workspace, stream);
+}
+
+tsp_status tsp_layer_forward(const tsp_plan* plan, const tsp_dims* dims, const uint16_t* x_local,
+                             const uint16_t* const* wqkv, const uint16_t* const* wo, const uint16_t* const* w1,
+                             const uint16_t* const* w2, uint16_t* k_full, uint16_t* v_full, uint16_t* out,
+                             void* workspace, size_t ws_bytes, hipStream_t stream) {
+  tsp_status s;
+  if ((s = check_plan(plan)) != TSP_OK) return s;
+  if ((s = check_dims(dims, plan->D, true, true)) != TSP_OK) return s;
+  if ((s = check_ptr(x_local)) != TSP_OK || (s = check_shards(wqkv, plan->D)) != TSP_OK ||
+      (s = check_shards(wo, plan->D)) != TSP_OK || (s = check_shards(w1, plan->D)) != TSP_OK ||
+      (s = check_shards(w2, plan->D)) != TSP_OK || (s = check_ptr(k_full)) != TSP_OK ||
+      (s = check_ptr(v_full)) != TSP_OK || (s = check_ptr(out)) != TSP_OK)
+    return s;
+  if (out == x_local) return TSP_ERR_INVALID_ARG;
+  if (!workspace) return TSP_ERR_WORKSPACE;
+  if (!aligned16(workspace)) return TSP_ERR_ALIGNMENT;
+  const int64_t n = plan->n_local;
+  const size_t h1_bytes = round_up((size_t)n * dims->hidden * 2);
+  const size_t a = ws_attn(n, dims), m = ws_mlp(n, dims);
+  if (ws_bytes < h1_bytes + (a > m ? a : m)) return TSP_ERR_WORKSPACE;
+  uint16_t* h1 = static_cast<uint16_t*>(workspace);
+  uint16_t* rest = h1 + h1_bytes / 2;
+  uint16_t* qbuf = rest;
+  uint16_t* abuf = qbuf + round_up((size_t)n * dims->hidden * 2) / 2;
+  if ((s = run_project(plan, dims, x_local, wqkv, k_full, v_full, qbuf, stream)) != TSP_OK) return s;
+  if ((s = run_core(plan, dims, qbuf, k_full, v_full, abuf, stream)) != TSP_OK) return s;
+  if ((s = run_out(n, dims, plan->D, plan->rank, abuf, wo, x_local, h1, stream)) != TSP_OK) return s;
+  return run_mlp(n, dims, plan->D, plan->rank, h1, w1, w2, h1, out, rest, stream);
+}
+
+const char* tsp_status_string(tsp_status status) {
+  switch (status) {
+    case TSP_OK: return "TSP_OK";
+    case TSP_ERR_INVALID_ARG: return "TSP_ERR_INVALID_ARG: null pointer, bad enum or out-of-range index";
+    case TSP_ERR_SHAPE: return "TSP_ERR_SHAPE: shapes inconsistent with the zigzag plan or the layer";
+    case TSP_ERR_ALIGNMENT: return "TSP_ERR_ALIGNMENT: device pointer not 16-byte aligned";
+    case TSP_ERR_WORKSPACE: return "TSP_ERR_WORKSPACE: workspace missing or too small";
+    case TSP_ERR_UNSUPPORTED: return "TSP_ERR_UNSUPPORTED: head_dim or width not supported by the kernels";
+    case TSP_ERR_HIP: return "TSP_ERR_HIP: a kernel launch failed";
+    default: return "TSP: unknown status";
+  }
+}
+
+}  // extern "C"

@@ -1,0 +1,216 @@
+"""Thin ctypes binding of libtsp.so (C ABI in include/tsp.h).
+
+Argument marshalling only: tensors are checked for dtype, device, contiguity
+and shape (so that no kernel is handed a buffer smaller than it will touch),
+then their device pointers and torch's current HIP stream are passed to the C
+entry point of the same name.  Every step of the layer runs in the HIP
+kernels; there is no fallback path: if ``libtsp.so`` is missing, every call
+raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from ctypes import POINTER, c_int32, c_int64, c_size_t, c_void_p
+
+import torch
+
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libtsp.so")
+
+TSP_OK, TSP_ERR_INVALID_ARG, TSP_ERR_SHAPE, TSP_ERR_ALIGNMENT, TSP_ERR_WORKSPACE, TSP_ERR_UNSUPPORTED, TSP_ERR_HIP = range(7)
+WS_ATTN, WS_MLP, WS_LAYER = 0, 1, 2
+MAX_D = 16
+
+EXPORTS = ["tsp_zigzag_plan", "tsp_workspace_size", "tsp_attn_project", "tsp_attn_core", "tsp_attn_out",
+           "tsp_attn_forward", "tsp_mlp_forward", "tsp_layer_forward", "tsp_status_string"]
+
+
+class TSPError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        self.status = status
+        super().__init__(f"{where}: {status_string(status)}")
+
+
+class Plan(ctypes.Structure):
+    _fields_ = [("seq_len", c_int64), ("chunk_len", c_int64), ("n_local", c_int64), ("D", c_int32),
+                ("rank", c_int32), ("chunk_id", c_int32 * 2), ("chunk_start", c_int64 * 2)]
+
+
+class Dims(ctypes.Structure):
+    _fields_ = [("hidden", c_int32), ("n_heads", c_int32), ("head_dim", c_int32), ("ffn", c_int32)]
+
+
+_lib = None
+
+
+def lib() -> ctypes.CDLL:
+    """The loaded library (raises if it has not been built)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"{LIB_PATH} is not built: run `python -m folded_tensor_sequence_tsp_amd.build`")
+        L = ctypes.CDLL(LIB_PATH)
+        P, PP = c_void_p, POINTER(c_void_p)
+        sig = {
+            "tsp_zigzag_plan": [c_int64, c_int32, c_int32, POINTER(Plan), P, P],
+            "tsp_workspace_size": [c_int64, POINTER(Dims), c_int32, c_int32],
+            "tsp_attn_project": [POINTER(Plan), POINTER(Dims), P, PP, P, P, P, P],
+            "tsp_attn_core": [POINTER(Plan), POINTER(Dims), P, P, P, P, P],
+            "tsp_attn_out": [c_int64, POINTER(Dims), c_int32, c_int32, P, PP, P, P, P],
+            "tsp_attn_forward": [POINTER(Plan), POINTER(Dims), P, PP, PP, P, P, P, P, P, c_size_t, P],
+            "tsp_mlp_forward": [c_int64, POINTER(Dims), c_int32, c_int32, P, PP, PP, P, P, P, c_size_t, P],
+            "tsp_layer_forward": [POINTER(Plan), POINTER(Dims), P, PP, PP, PP, PP, P, P, P, P, c_size_t, P],
+            "tsp_status_string": [c_int32],
+        }
+        for name, args in sig.items():
+            f = getattr(L, name)
+            f.argtypes = args
+            f.restype = c_int32
+        L.tsp_workspace_size.restype = c_size_t
+        L.tsp_status_string.restype = ctypes.c_char_p
+        _lib = L
+    return _lib
+
+
+def status_string(status: int) -> str:
+    return lib().tsp_status_string(int(status)).decode()
+
+
+def _check(status: int, where: str) -> None:
+    if status != TSP_OK:
+        raise TSPError(status, where)
+
+
+# ---------------------------------------------------------------- marshalling
+def _dev_tensor(t: torch.Tensor, shape, name: str) -> c_void_p:
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name}: expected a torch.Tensor")
+    if t.dtype != torch.bfloat16:
+        raise ValueError(f"{name}: expected bfloat16, got {t.dtype}")
+    if t.device.type != "cuda" or t.device.index != torch.cuda.current_device():
+        raise ValueError(f"{name}: expected a tensor on the current HIP device, got {t.device}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name}: must be contiguous")
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name}: expected shape {tuple(shape)}, got {tuple(t.shape)}")
+    return c_void_p(t.data_ptr())
+
+
+def _opt_tensor(t, shape, name):
+    return c_void_p(None) if t is None else _dev_tensor(t, shape, name)
+
+
+def _shards(ts, D: int, shape, name: str):
+    if len(ts) != D:
+        raise ValueError(f"{name}: expected {D} shards, got {len(ts)}")
+    arr = (c_void_p * D)()
+    for d, t in enumerate(ts):
+        arr[d] = _dev_tensor(t, shape, f"{name}[{d}]").value
+    return arr
+
+
+def _workspace(ws: torch.Tensor, need: int) -> tuple:
+    if ws.device.type != "cuda" or not ws.is_contiguous():
+        raise ValueError("workspace: expected a contiguous tensor on the HIP device")
+    nbytes = ws.numel() * ws.element_size()
+    if nbytes < need:
+        raise ValueError(f"workspace: {nbytes} bytes, need {need}")
+    return c_void_p(ws.data_ptr()), nbytes
+
+
+def _stream(stream) -> c_void_p:
+    s = torch.cuda.current_stream() if stream is None else stream
+    return c_void_p(s.cuda_stream)
+
+
+# ------------------------------------------------------------------ entry points
+def make_dims(hidden: int, n_heads: int, head_dim: int, ffn: int) -> Dims:
+    return Dims(hidden, n_heads, head_dim, ffn)
+
+
+def zigzag_plan(seq_len: int, D: int, rank: int):
+    """(Plan, local_to_global int64 CPU tensor, ring order list) from the C planner."""
+    plan = Plan()
+    if D < 1 or D > MAX_D:
+        _check(TSP_ERR_INVALID_ARG, "tsp_zigzag_plan")
+    n = max(seq_len // D, 0) if seq_len > 0 else 0
+    l2g = torch.empty(max(n, 1), dtype=torch.int64)
+    ring = (c_int32 * D)()
+    _check(lib().tsp_zigzag_plan(seq_len, D, rank, ctypes.byref(plan), c_void_p(l2g.data_ptr()),
+                                 ctypes.cast(ring, c_void_p)), "tsp_zigzag_plan")
+    return plan, l2g[:plan.n_local], list(ring)
+
+
+def workspace_size(n_tokens: int, dims: Dims, D: int, kind: int) -> int:
+    return int(lib().tsp_workspace_size(n_tokens, ctypes.byref(dims), D, kind))
+
+
+def attn_project(plan: Plan, dims: Dims, x_local, wqkv, k_full, v_full, q_out, stream=None):
+    n, h, S, D = plan.n_local, dims.hidden, plan.seq_len, plan.D
+    Hs = dims.n_heads // D if D > 0 else 0
+    args = (_dev_tensor(x_local, (n, h), "x_local"), _shards(wqkv, D, (3 * Hs * dims.head_dim, h), "wqkv"),
+            _dev_tensor(k_full, (S, h), "k_full"), _dev_tensor(v_full, (S, h), "v_full"),
+            _dev_tensor(q_out, (n, h), "q_out"))
+    _check(lib().tsp_attn_project(ctypes.byref(plan), ctypes.byref(dims), *args, _stream(stream)),
+           "tsp_attn_project")
+
+
+def attn_core(plan: Plan, dims: Dims, q, k_full, v_full, attn_out, stream=None):
+    n, h, S = plan.n_local, dims.hidden, plan.seq_len
+    args = (_dev_tensor(q, (n, h), "q"), _dev_tensor(k_full, (S, h), "k_full"), _dev_tensor(v_full, (S, h), "v_full"),
+            _dev_tensor(attn_out, (n, h), "attn_out"))
+    _check(lib().tsp_attn_core(ctypes.byref(plan), ctypes.byref(dims), *args, _stream(stream)), "tsp_attn_core")
+
+
+def attn_out(dims: Dims, D: int, start_shard: int, attn, wo, residual, out, stream=None):
+    n, h = attn.shape[0], dims.hidden
+    Hs = dims.n_heads // D if D > 0 else 0
+    args = (_dev_tensor(attn, (n, h), "attn"), _shards(wo, D, (h, Hs * dims.head_dim), "wo"),
+            _opt_tensor(residual, (n, h), "residual"), _dev_tensor(out, (n, h), "out"))
+    _check(lib().tsp_attn_out(n, ctypes.byref(dims), D, start_shard, *args, _stream(stream)), "tsp_attn_out")
+
+
+def attn_forward(plan: Plan, dims: Dims, x_local, wqkv, wo, k_full, v_full, residual, out, workspace, stream=None):
+    n, h, S, D = plan.n_local, dims.hidden, plan.seq_len, plan.D
+    Hs = dims.n_heads // D if D > 0 else 0
+    need = workspace_size(n, dims, D, WS_ATTN)
+    ws, nbytes = _workspace(workspace, need)
+    args = (_dev_tensor(x_local, (n, h), "x_local"), _shards(wqkv, D, (3 * Hs * dims.head_dim, h), "wqkv"),
+            _shards(wo, D, (h, Hs * dims.head_dim), "wo"), _dev_tensor(k_full, (S, h), "k_full"),
+            _dev_tensor(v_full, (S, h), "v_full"), _opt_tensor(residual, (n, h), "residual"),
+            _dev_tensor(out, (n, h), "out"))
+    _check(lib().tsp_attn_forward(ctypes.byref(plan), ctypes.byref(dims), *args, ws, nbytes, _stream(stream)),
+           "tsp_attn_forward")
+
+
+def mlp_forward(dims: Dims, D: int, start_shard: int, x, w1, w2, residual, y, workspace, stream=None):
+    n, h = x.shape[0], dims.hidden
+    Fs = dims.ffn // D if D > 0 else 0
+    need = workspace_size(n, dims, D, WS_MLP)
+    ws, nbytes = _workspace(workspace, need)
+    args = (_dev_tensor(x, (n, h), "x"), _shards(w1, D, (Fs, h), "w1"), _shards(w2, D, (h, Fs), "w2"),
+            _opt_tensor(residual, (n, h), "residual"), _dev_tensor(y, (n, h), "y"))
+    _check(lib().tsp_mlp_forward(n, ctypes.byref(dims), D, start_shard, *args, ws, nbytes, _stream(stream)),
+           "tsp_mlp_forward")
+
+
+def layer_forward(plan: Plan, dims: Dims, x_local, wqkv, wo, w1, w2, k_full, v_full, out, workspace, stream=None):
+    n, h, S, D = plan.n_local, dims.hidden, plan.seq_len, plan.D
+    Hs = dims.n_heads // D if D > 0 else 0
+    Fs = dims.ffn // D if D > 0 else 0
+    need = workspace_size(n, dims, D, WS_LAYER)
+    ws, nbytes = _workspace(workspace, need)
+    args = (_dev_tensor(x_local, (n, h), "x_local"), _shards(wqkv, D, (3 * Hs * dims.head_dim, h), "wqkv"),
+            _shards(wo, D, (h, Hs * dims.head_dim), "wo"), _shards(w1, D, (Fs, h), "w1"),
+            _shards(w2, D, (h, Fs), "w2"), _dev_tensor(k_full, (S, h), "k_full"),
+            _dev_tensor(v_full, (S, h), "v_full"), _dev_tensor(out, (n, h), "out"))
+    _check(lib().tsp_layer_forward(ctypes.byref(plan), ctypes.byref(dims), *args, ws, nbytes, _stream(stream)),
+           "tsp_layer_forward")
+
+
+def alloc_workspace(n_tokens: int, dims: Dims, D: int, kind: int, device=None) -> torch.Tensor:
+    """A uint8 device tensor large enough for the given kind of call."""
+    nbytes = workspace_size(n_tokens, dims, D, kind)
+    if nbytes == 0 and n_tokens > 0:
+        raise ValueError("invalid dims for a workspace")
+    return torch.empty(max(nbytes, 256), dtype=torch.uint8, device=device or torch.cuda.current_device())

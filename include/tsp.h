@@ -1,0 +1,208 @@
+/*
+ * tsp.h - C ABI of the MI355X (gfx950) TSP rank-share layer library (libtsp.so).
+ *
+ * Tensor + Sequence Parallelism (TSP) folds tensor parallelism (weights
+ * sharded) and sequence parallelism (tokens sharded) onto one device-mesh axis
+ * of size D: each device holds 1/D of every weight matrix and 1/D of the
+ * sequence (zubnet.ai, "Zyphra TSP folds TP+SP onto one GPU axis", para. 1).
+ * For attention the weight shards are applied one after another to the local
+ * tokens and K/V are gathered over a zigzag partition; for the MLP the weight
+ * shard pairs are applied in ring order and the partial products are summed
+ * locally, which replaces the all-reduce of tensor parallelism (same page,
+ * para. 2).  This library is the computation of ONE device for one decoder
+ * layer.  The collectives are not part of it: the gathered K/V and the weight
+ * shards are caller-owned device buffers.
+ *
+ * Conventions for every entry point:
+ *   - bf16 tensors are passed as uint16_t bit patterns; all tensors are dense
+ *     row-major.  Weights are stored out x in (nn.Linear layout).
+ *   - "device" pointers point to memory of the current HIP device, must be
+ *     16-byte aligned and must not alias outputs unless stated.
+ *   - weight shards are a HOST array of D device pointers (D <= TSP_MAX_D).
+ *   - the caller owns every buffer, including the workspace; the library keeps
+ *     no global state, allocates nothing and never synchronises.  Calls are
+ *     reentrant; calls on different streams that write the same buffers race.
+ *   - all arguments are validated before anything is enqueued; a status other
+ *     than TSP_OK means nothing was enqueued, except TSP_ERR_HIP (a launch
+ *     failed; earlier launches of the same call may have been enqueued).
+ *     Faults inside kernels surface at the caller's next synchronisation.
+ *   - work is enqueued on `stream` (0 = the null stream) and returns at once.
+ *
+ * Layer (one rank, local rows in plan order):
+ *   q,k,v  = x W_q^T, x W_k^T, x W_v^T       (shard-iterated, tsp_attn_project)
+ *   k_full/v_full rows at the rank's own positions <- k, v
+ *   a      = causal softmax(q k_full^T / sqrt(hd)) v_full    (tsp_attn_core)
+ *   h1     = x + a W_o^T                     (split-K over head shards, tsp_attn_out)
+ *   out    = h1 + GELU_tanh(h1 W1^T) W2^T    (ring split-K over FFN shards, tsp_mlp_forward)
+ */
+#ifndef TSP_H
+#define TSP_H
+
+#include <stddef.h>
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define TSP_MAX_D 16
+
+typedef enum {
+  TSP_OK = 0,
+  TSP_ERR_INVALID_ARG = 1, /* null pointer, bad enum value, out-of-range rank or start shard */
+  TSP_ERR_SHAPE = 2,       /* shapes inconsistent with the method (see each call) */
+  TSP_ERR_ALIGNMENT = 3,   /* a device pointer is not 16-byte aligned */
+  TSP_ERR_WORKSPACE = 4,   /* workspace null or smaller than tsp_workspace_size() */
+  TSP_ERR_UNSUPPORTED = 5, /* valid for the method but not implemented (head_dim, widths) */
+  TSP_ERR_HIP = 6          /* a kernel launch failed */
+} tsp_status;
+
+/* Rank's share of the sequence (plain data, host memory). */
+typedef struct {
+  int64_t seq_len;        /* S, total sequence length */
+  int64_t chunk_len;      /* C = S / (2D) */
+  int64_t n_local;        /* n = S / D = 2C local tokens */
+  int32_t D;              /* TSP axis size */
+  int32_t rank;           /* r in [0, D) */
+  int32_t chunk_id[2];    /* r and 2D-1-r */
+  int64_t chunk_start[2]; /* chunk_id[i] * C */
+} tsp_plan;
+
+/* Layer shape. hidden = n_heads * head_dim. */
+typedef struct {
+  int32_t hidden;
+  int32_t n_heads;
+  int32_t head_dim;
+  int32_t ffn;
+} tsp_dims;
+
+/* Workspace kinds for tsp_workspace_size(). */
+typedef enum { TSP_WS_ATTN = 0, TSP_WS_MLP = 1, TSP_WS_LAYER = 2 } tsp_ws_kind;
+
+/*
+ * Zigzag plan (zubnet.ai TSP page, para. 2: K/V are gathered over a zigzag
+ * partition for load balance).  The sequence is cut into 2D chunks of C = S/(2D)
+ * tokens; rank r holds chunks r and 2D-1-r, so every rank has the same causal
+ * work.  Local row i < C is global position chunk_start[0] + i, row i >= C is
+ * chunk_start[1] + (i - C).  Ring order of weight shards for the MLP:
+ * ring_order[k] = (r + k) mod D.
+ *   seq_len, D, rank: S > 0, D in [1, TSP_MAX_D], S % (2D) == 0, 0 <= rank < D.
+ *   plan            : host out, required.
+ *   local_to_global : host out, nullable; int64[n_local].
+ *   ring_order      : host out, nullable; int32[D].
+ * Errors: TSP_ERR_INVALID_ARG (plan null, rank out of range, D out of range),
+ *         TSP_ERR_SHAPE (S <= 0 or S % 2D != 0).  Host only; no device work.
+ */
+tsp_status tsp_zigzag_plan(int64_t seq_len, int32_t D, int32_t rank, tsp_plan* plan,
+                           int64_t* local_to_global, int32_t* ring_order);
+
+/*
+ * Bytes of workspace that tsp_attn_forward (TSP_WS_ATTN), tsp_mlp_forward
+ * (TSP_WS_MLP) or tsp_layer_forward (TSP_WS_LAYER) need for n_tokens local
+ * tokens.  Returns 0 for invalid dims or kind.
+ */
+size_t tsp_workspace_size(int64_t n_tokens, const tsp_dims* dims, int32_t D, int32_t kind);
+
+/*
+ * QKV projection, shard-iterated (para. 2: the attention weight shards are
+ * applied one after another to the local tokens).  For d = 0..D-1:
+ *   [Q_d | K_d | V_d] = x_local W_qkv_d^T
+ * Q_d goes to q_out[:, heads of shard d]; K_d and V_d rows are written into
+ * k_full / v_full at the rank's own global positions (the rank's contribution
+ * to the K/V all-gather).  Other rows of k_full / v_full are not touched.
+ *   plan      : from tsp_zigzag_plan; its D is the shard count.
+ *   dims      : n_heads % D == 0, hidden = n_heads * head_dim, head_dim in {64, 128},
+ *               hidden % 64 == 0.
+ *   x_local   : device, bf16 [n_local x hidden].
+ *   wqkv      : host array of D device pointers, each bf16 [3 * H_s * head_dim x hidden],
+ *               rows = shard d's Q heads, then its K heads, then its V heads
+ *               (H_s = n_heads / D; shard d owns heads d*H_s .. (d+1)*H_s - 1).
+ *   k_full, v_full : device, bf16 [seq_len x hidden], in/out.
+ *   q_out     : device, bf16 [n_local x hidden], out.
+ */
+tsp_status tsp_attn_project(const tsp_plan* plan, const tsp_dims* dims, const uint16_t* x_local,
+                            const uint16_t* const* wqkv, uint16_t* k_full, uint16_t* v_full,
+                            uint16_t* q_out, hipStream_t stream);
+
+/*
+ * Causal attention of the local queries (two zigzag chunks) against the whole
+ * gathered K/V (para. 2).  Per head a and local row t at global position p:
+ *   attn[t, a] = sum_{j <= p} softmax_j(q[t, a] . k_full[j, a] / sqrt(head_dim)) v_full[j, a]
+ * (the diagonal is included).  fp32 online softmax, bf16 MFMA products.
+ *   q      : device, bf16 [n_local x hidden] (as tsp_attn_project writes it).
+ *   k_full, v_full : device, bf16 [seq_len x hidden], read only.
+ *   attn_out : device, bf16 [n_local x hidden], out; must not alias q.
+ */
+tsp_status tsp_attn_core(const tsp_plan* plan, const tsp_dims* dims, const uint16_t* q,
+                         const uint16_t* k_full, const uint16_t* v_full, uint16_t* attn_out,
+                         hipStream_t stream);
+
+/*
+ * O projection as a split-K over the D head shards (the attention projections
+ * iterated over the weight shards, para. 2; W_o is taken in row blocks by head
+ * shard).  Shards are visited in ring order d_k = (start_shard + k) mod D with
+ * one fp32 accumulator across all of them:
+ *   out = [residual +] sum_k attn[:, heads of d_k] W_o_{d_k}^T
+ *   n_tokens  : rows of attn / out (>= 0; 0 enqueues nothing).
+ *   attn      : device, bf16 [n_tokens x hidden].
+ *   wo        : host array of D device pointers, each bf16 [hidden x H_s * head_dim].
+ *   residual  : device, bf16 [n_tokens x hidden], nullable (then no residual).
+ *   out       : device, bf16 [n_tokens x hidden]; may alias residual, not attn.
+ */
+tsp_status tsp_attn_out(int64_t n_tokens, const tsp_dims* dims, int32_t D, int32_t start_shard,
+                        const uint16_t* attn, const uint16_t* const* wo, const uint16_t* residual,
+                        uint16_t* out, hipStream_t stream);
+
+/*
+ * Attention half of the layer: tsp_attn_project, tsp_attn_core, then
+ * tsp_attn_out with start_shard = plan->rank.
+ *   residual  : nullable; the layer passes x_local.
+ *   out       : device, bf16 [n_local x hidden]; must not alias x_local.
+ *   workspace : device, >= tsp_workspace_size(n_local, dims, D, TSP_WS_ATTN) bytes.
+ */
+tsp_status tsp_attn_forward(const tsp_plan* plan, const tsp_dims* dims, const uint16_t* x_local,
+                            const uint16_t* const* wqkv, const uint16_t* const* wo,
+                            uint16_t* k_full, uint16_t* v_full, const uint16_t* residual,
+                            uint16_t* out, void* workspace, size_t ws_bytes, hipStream_t stream);
+
+/*
+ * MLP with the shard pairs in ring order (para. 2): the shard loop is a split-K
+ * over the FFN dimension with one fp32 accumulator, in place of the
+ * all-reduce of tensor parallelism:
+ *   y = [residual +] sum_{k=0}^{D-1} GELU_tanh(x W1_{d_k}^T) W2_{d_k}^T,  d_k = (start_shard + k) mod D
+ *   n_tokens : rows (>= 0).
+ *   dims     : ffn % D == 0, ffn / D % 64 == 0, hidden % 64 == 0.
+ *   x        : device, bf16 [n_tokens x hidden].
+ *   w1       : host array of D device pointers, each bf16 [ffn/D x hidden].
+ *   w2       : host array of D device pointers, each bf16 [hidden x ffn/D].
+ *   residual : device, nullable.  y: device, bf16 [n_tokens x hidden]; may alias
+ *              residual, must not alias x unless residual == x.
+ *   workspace: >= tsp_workspace_size(n_tokens, dims, D, TSP_WS_MLP) bytes.
+ */
+tsp_status tsp_mlp_forward(int64_t n_tokens, const tsp_dims* dims, int32_t D, int32_t start_shard,
+                           const uint16_t* x, const uint16_t* const* w1, const uint16_t* const* w2,
+                           const uint16_t* residual, uint16_t* y, void* workspace, size_t ws_bytes,
+                           hipStream_t stream);
+
+/*
+ * One decoder layer for the rank's local tokens:
+ *   h1 = x + Attn(x) (tsp_attn_forward), out = h1 + MLP(h1) (tsp_mlp_forward with
+ *   start_shard = plan->rank).  No norm, no bias.
+ *   out       : device, bf16 [n_local x hidden]; must not alias x_local.
+ *   workspace : >= tsp_workspace_size(n_local, dims, D, TSP_WS_LAYER) bytes.
+ */
+tsp_status tsp_layer_forward(const tsp_plan* plan, const tsp_dims* dims, const uint16_t* x_local,
+                             const uint16_t* const* wqkv, const uint16_t* const* wo,
+                             const uint16_t* const* w1, const uint16_t* const* w2,
+                             uint16_t* k_full, uint16_t* v_full, uint16_t* out, void* workspace,
+                             size_t ws_bytes, hipStream_t stream);
+
+/* Static text for a status code (never null). */
+const char* tsp_status_string(tsp_status status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* TSP_H */

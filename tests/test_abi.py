@@ -1,0 +1,203 @@
+"""The C-ABI library on the CPU: it loads, exports every entry point the header
+declares, its zigzag planner is bit-exact with the oracle's, and every invalid
+argument is rejected with its status before anything is launched (no GPU is
+touched: the pointers below are never dereferenced)."""
+import ctypes
+import os
+import re
+
+import pytest
+import torch
+
+from folded_tensor_sequence_tsp_amd import tsp
+from oracle import tsp_oracle as O
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def _header_functions():
+    text = open(os.path.join(ROOT, "include", "tsp.h")).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(tsp_[a-z_]+)\s*\(", text)))
+
+
+@pytest.fixture(scope="module")
+def L():
+    return tsp.lib()
+
+
+def test_exports_every_declared_symbol(L):
+    declared = _header_functions()
+    assert declared, "no declarations parsed from include/tsp.h"
+    assert sorted(declared) == sorted(tsp.EXPORTS)
+    for name in declared:
+        assert hasattr(L, name), name
+
+
+def test_status_strings(L):
+    for s in range(7):
+        assert tsp.status_string(s).startswith("TSP_")
+    assert "unknown" in tsp.status_string(99)
+
+
+GRID = [(2, 1), (8, 2), (24, 3), (64, 4), (2048, 4), (96, 6), (256, 8), (16384, 8), (131072, 8), (1024, 16)]
+
+
+@pytest.mark.parametrize("S,D", GRID)
+def test_plan_bit_exact_with_oracle(S, D):
+    for r in range(D):
+        plan, l2g, ring = tsp.zigzag_plan(S, D, r)
+        ref = O.zigzag_plan(S, D, r)
+        assert plan.seq_len == S and plan.D == D and plan.rank == r
+        assert plan.chunk_len == ref.chunk_len
+        assert plan.n_local == S // D
+        assert list(plan.chunk_id) == ref.chunk_ids
+        assert list(plan.chunk_start) == ref.chunk_starts
+        assert torch.equal(l2g, ref.local_to_global)
+        assert ring == ref.ring
+
+
+def test_plan_golden_cases(golden):
+    for S, D, r, C, c0, c1, s0, s1 in (map(int, row) for row in golden("zigzag_plans.txt")):
+        plan, l2g, _ = tsp.zigzag_plan(S, D, r)
+        assert (plan.chunk_len, list(plan.chunk_id), list(plan.chunk_start)) == (C, [c0, c1], [s0, s1])
+
+
+@pytest.mark.parametrize("S,D,r,status", [
+    (30, 4, 0, tsp.TSP_ERR_SHAPE), (0, 2, 0, tsp.TSP_ERR_SHAPE), (-8, 2, 0, tsp.TSP_ERR_SHAPE),
+    (16, 2, 2, tsp.TSP_ERR_INVALID_ARG), (16, 2, -1, tsp.TSP_ERR_INVALID_ARG),
+    (64, 0, 0, tsp.TSP_ERR_INVALID_ARG), (64, 17, 0, tsp.TSP_ERR_INVALID_ARG)])
+def test_plan_rejects(L, S, D, r, status):
+    plan = tsp.Plan()
+    assert L.tsp_zigzag_plan(S, D, r, ctypes.byref(plan), None, None) == status
+    assert L.tsp_zigzag_plan(64, 2, 0, None, None, None) == tsp.TSP_ERR_INVALID_ARG
+
+
+# ----------------------------------------------------------------- error paths
+A = 0x10000          # aligned fake device address, never dereferenced
+MIS = 0x10002        # misaligned fake device address
+
+
+def _arr(vals):
+    arr = (ctypes.c_void_p * len(vals))()
+    for i, v in enumerate(vals):
+        arr[i] = v
+    return arr
+
+
+def _plan(S=2048, D=4, r=1):
+    return tsp.zigzag_plan(S, D, r)[0]
+
+
+DIMS = dict(hidden=256, n_heads=4, head_dim=64, ffn=1024)
+
+
+def _dims(**kw):
+    d = dict(DIMS)
+    d.update(kw)
+    return tsp.Dims(d["hidden"], d["n_heads"], d["head_dim"], d["ffn"])
+
+
+def project(L, plan=None, dims=None, x=A, w=None, k=A, v=A, q=A):
+    plan = plan or _plan()
+    dims = dims or _dims()
+    w = w if w is not None else _arr([A] * plan.D)
+    return L.tsp_attn_project(ctypes.byref(plan) if plan is not False else None, ctypes.byref(dims), x, w, k, v, q, None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(x=None), tsp.TSP_ERR_INVALID_ARG),
+    (dict(k=None), tsp.TSP_ERR_INVALID_ARG),
+    (dict(q=MIS), tsp.TSP_ERR_ALIGNMENT),
+    (dict(v=MIS), tsp.TSP_ERR_ALIGNMENT),
+    (dict(w=_arr([A, A, 0, A])), tsp.TSP_ERR_INVALID_ARG),      # a lost shard
+    (dict(w=_arr([A, MIS, A, A])), tsp.TSP_ERR_ALIGNMENT),
+    (dict(dims=_dims(n_heads=3, hidden=192)), tsp.TSP_ERR_SHAPE),  # H % D != 0
+    (dict(dims=_dims(hidden=320)), tsp.TSP_ERR_SHAPE),             # hidden != H * hd
+    (dict(dims=_dims(head_dim=32, n_heads=8)), tsp.TSP_ERR_UNSUPPORTED),
+    (dict(dims=_dims(head_dim=96, n_heads=4, hidden=384)), tsp.TSP_ERR_UNSUPPORTED),
+])
+def test_project_rejects(L, kw, status):
+    assert project(L, **kw) == status
+
+
+def test_tampered_plan_rejected(L):
+    p = _plan()
+    p.chunk_start[1] = 1537
+    assert project(L, plan=p) == tsp.TSP_ERR_SHAPE
+    p = _plan()
+    p.n_local = 1024
+    assert project(L, plan=p) == tsp.TSP_ERR_SHAPE
+    p = _plan()
+    p.rank = 4
+    assert project(L, plan=p) == tsp.TSP_ERR_INVALID_ARG
+
+
+def test_core_rejects(L):
+    p, d = _plan(), _dims()
+    assert L.tsp_attn_core(None, ctypes.byref(d), A, A, A, A + 64, None) == tsp.TSP_ERR_INVALID_ARG
+    assert L.tsp_attn_core(ctypes.byref(p), ctypes.byref(d), A, A, A, A, None) == tsp.TSP_ERR_INVALID_ARG  # alias
+    assert L.tsp_attn_core(ctypes.byref(p), ctypes.byref(d), A, A, MIS, A + 64, None) == tsp.TSP_ERR_ALIGNMENT
+    assert L.tsp_attn_core(ctypes.byref(p), None, A, A, A, A + 64, None) == tsp.TSP_ERR_INVALID_ARG
+
+
+def test_out_rejects(L):
+    d = _dims()
+    w = _arr([A] * 4)
+    assert L.tsp_attn_out(512, ctypes.byref(d), 4, 4, A, w, None, A + 64, None) == tsp.TSP_ERR_INVALID_ARG
+    assert L.tsp_attn_out(512, ctypes.byref(d), 4, -1, A, w, None, A + 64, None) == tsp.TSP_ERR_INVALID_ARG
+    assert L.tsp_attn_out(-1, ctypes.byref(d), 4, 0, A, w, None, A + 64, None) == tsp.TSP_ERR_SHAPE
+    assert L.tsp_attn_out(512, ctypes.byref(d), 4, 0, A, w, MIS, A + 64, None) == tsp.TSP_ERR_ALIGNMENT
+    assert L.tsp_attn_out(512, ctypes.byref(d), 4, 0, A, w, None, A, None) == tsp.TSP_ERR_INVALID_ARG
+    assert L.tsp_attn_out(512, ctypes.byref(d), 4, 0, A, None, None, A + 64, None) == tsp.TSP_ERR_INVALID_ARG
+    assert L.tsp_attn_out(512, ctypes.byref(d), 0, 0, A, w, None, A + 64, None) == tsp.TSP_ERR_INVALID_ARG
+
+
+def test_mlp_rejects(L):
+    d = _dims()
+    w = _arr([A] * 4)
+    ws = tsp.workspace_size(512, d, 4, tsp.WS_MLP)
+    assert ws == 512 * 1024 * 2
+    call = lambda **k: L.tsp_mlp_forward(k.get("n", 512), ctypes.byref(k.get("dims", d)), k.get("D", 4),
+                                         k.get("start", 0), k.get("x", A), k.get("w1", w), k.get("w2", w),
+                                         k.get("res", None), k.get("y", A + 64), k.get("ws", A + 128),
+                                         k.get("nb", ws), None)
+    assert call(ws=None) == tsp.TSP_ERR_WORKSPACE
+    assert call(nb=ws - 1) == tsp.TSP_ERR_WORKSPACE
+    assert call(ws=MIS) == tsp.TSP_ERR_ALIGNMENT
+    assert call(dims=_dims(ffn=1002)) == tsp.TSP_ERR_SHAPE          # F % D != 0
+    assert call(dims=_dims(ffn=1152)) == tsp.TSP_ERR_UNSUPPORTED    # F_s = 288 not a multiple of 64
+    assert call(start=4) == tsp.TSP_ERR_INVALID_ARG
+    assert call(y=A) == tsp.TSP_ERR_INVALID_ARG                     # y aliases x without being the residual
+    assert call(w2=_arr([A, A, A, 0])) == tsp.TSP_ERR_INVALID_ARG
+    assert call(n=-5) == tsp.TSP_ERR_SHAPE
+
+
+def test_layer_and_forward_reject(L):
+    p, d = _plan(), _dims()
+    w = _arr([A] * 4)
+    need = tsp.workspace_size(p.n_local, d, 4, tsp.WS_LAYER)
+    assert need > 0
+    args = lambda ws, nb, out=A + 64: (ctypes.byref(p), ctypes.byref(d), A, w, w, w, w, A, A, out, ws, nb, None)
+    assert L.tsp_layer_forward(*args(A + 128, need - 1)) == tsp.TSP_ERR_WORKSPACE
+    assert L.tsp_layer_forward(*args(None, need)) == tsp.TSP_ERR_WORKSPACE
+    assert L.tsp_layer_forward(*args(A + 128, need, out=A)) == tsp.TSP_ERR_INVALID_ARG
+    need_a = tsp.workspace_size(p.n_local, d, 4, tsp.WS_ATTN)
+    assert L.tsp_attn_forward(ctypes.byref(p), ctypes.byref(d), A, w, w, A, A, None, A + 64, A + 128, need_a - 16,
+                              None) == tsp.TSP_ERR_WORKSPACE
+    assert L.tsp_attn_forward(ctypes.byref(p), ctypes.byref(d), A, w, w, A, A, MIS, A + 64, A + 128, need_a,
+                              None) == tsp.TSP_ERR_ALIGNMENT
+
+
+def test_workspace_sizes(L):
+    d = _dims()
+    n = 512
+    attn = tsp.workspace_size(n, d, 4, tsp.WS_ATTN)
+    mlp = tsp.workspace_size(n, d, 4, tsp.WS_MLP)
+    layer = tsp.workspace_size(n, d, 4, tsp.WS_LAYER)
+    assert attn >= 2 * n * 256 * 2
+    assert mlp >= n * 1024 * 2
+    assert layer >= n * 256 * 2 + max(attn, mlp)
+    assert tsp.workspace_size(n, d, 4, 7) == 0
+    assert tsp.workspace_size(n, _dims(hidden=300), 4, tsp.WS_LAYER) == 0
+    assert tsp.workspace_size(-1, d, 4, tsp.WS_ATTN) == 0
