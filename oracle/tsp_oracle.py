@@ -31,14 +31,16 @@ Readings of points the pages leave open:
   input columns of ``wo[d]``);
 * the rank's own rows of the gathered K/V are the ones it projects itself;
   the caller-supplied rows at those positions are replaced;
-* the gathered K/V is a bf16 tensor, like every tensor of the bf16 model the
-  page describes (para. 1) and the gathered K/V the workloads hand over: the
-  rank's projected K/V rows enter it rounded to bf16 (round to nearest even),
-  exactly as they would travel through the all-gather.  ``kv_bf16=False``
-  keeps them in fp64, for the pins that compare with exact library routines.
+* the outputs of the attention projections are bf16 tensors, like every
+  tensor of the bf16 model the page describes (para. 1): each weight shard,
+  applied to the local tokens, produces its heads' Q, K and V as bf16 tensors
+  (round to nearest even), and the gathered K/V that the workloads hand over
+  is bf16, so the rank's own K/V rows enter it rounded exactly as they would
+  travel through the all-gather.  ``proj_bf16=False`` keeps Q, K and V in
+  fp64, for the pins that compare with exact library routines.
 
-Inputs are bf16 tensors (converted exactly to fp64); apart from the gathered
-K/V above, no intermediate is rounded.
+Inputs are bf16 tensors (converted exactly to fp64); apart from the
+projection outputs above, no intermediate is rounded.
 Matrix products use ``torch.matmul`` in fp64 as a library step; everything else
 (GELU, masking, softmax) is written out below.
 
@@ -204,20 +206,20 @@ def qkv_projection(x_local, wqkv, head_dim):
     return linear(x, W.wq), linear(x, W.wk), linear(x, W.wv)
 
 
-def kv_rows(t: torch.Tensor, kv_bf16: bool = True) -> torch.Tensor:
-    """Rows as the gathered K/V holds them: rounded to bf16 (nearest even) when
-    ``kv_bf16``, else unchanged (fp64)."""
+def proj_rows(t: torch.Tensor, proj_bf16: bool = True) -> torch.Tensor:
+    """A projection output as the bf16 model holds it: rounded to bf16 (nearest
+    even) when ``proj_bf16``, else unchanged (fp64)."""
     t = f64(t)
-    return t.to(torch.bfloat16).to(F64) if kv_bf16 else t
+    return t.to(torch.bfloat16).to(F64) if proj_bf16 else t
 
 
-def gathered_kv(plan: Plan, k_own, v_own, k_full=None, v_full=None, kv_bf16: bool = True):
+def gathered_kv(plan: Plan, k_own, v_own, k_full=None, v_full=None, proj_bf16: bool = True):
     """Full-sequence K/V as the K/V all-gather delivers it (para. 2).
 
     Rows at the rank's own positions are its own projections; all other rows are
     the caller-supplied ones (``k_full``/``v_full``, the other ranks'
     contributions).  With ``k_full`` None the own rows must cover the sequence
-    (D = 1).  Every row is as the bf16 gathered tensor holds it (``kv_rows``).
+    (D = 1).  Every row is as the bf16 gathered tensor holds it (``proj_rows``).
     """
     S = plan.seq_len
     h = k_own.shape[1]
@@ -225,14 +227,14 @@ def gathered_kv(plan: Plan, k_own, v_own, k_full=None, v_full=None, kv_bf16: boo
         k = torch.full((S, h), float("nan"), dtype=F64)
         v = torch.full((S, h), float("nan"), dtype=F64)
     else:
-        k, v = kv_rows(k_full, kv_bf16).clone(), kv_rows(v_full, kv_bf16).clone()
-    k[plan.local_to_global] = kv_rows(k_own, kv_bf16)
-    v[plan.local_to_global] = kv_rows(v_own, kv_bf16)
+        k, v = proj_rows(k_full, proj_bf16).clone(), proj_rows(v_full, proj_bf16).clone()
+    k[plan.local_to_global] = proj_rows(k_own, proj_bf16)
+    v[plan.local_to_global] = proj_rows(v_own, proj_bf16)
     return k, v
 
 
 def attn_forward(plan: Plan, x_local, wqkv, wo, n_heads, head_dim, k_full=None, v_full=None,
-                 residual=True, rows=None, k_own=None, v_own=None, kv_bf16: bool = True):
+                 residual=True, rows=None, k_own=None, v_own=None, proj_bf16: bool = True):
     """Attention half of the layer for the rank's local rows (or the subset ``rows``).
 
     Returns (out [m, h], q_own [n, h], k_own [n, h], v_own [n, h]) in fp64, where
@@ -242,11 +244,11 @@ def attn_forward(plan: Plan, x_local, wqkv, wo, n_heads, head_dim, k_full=None, 
     W = assemble(wqkv=wqkv, wo=wo, head_dim=head_dim)
     x = f64(x_local)
     sel = torch.arange(x.shape[0]) if rows is None else torch.as_tensor(rows, dtype=torch.int64)
-    q = linear(x[sel], W.wq)
+    q = proj_rows(linear(x[sel], W.wq), proj_bf16)
     if k_own is None:
         k_own = linear(x, W.wk)
         v_own = linear(x, W.wv)
-    k, v = gathered_kv(plan, k_own, v_own, k_full, v_full, kv_bf16)
+    k, v = gathered_kv(plan, k_own, v_own, k_full, v_full, proj_bf16)
     o = causal_attention(q, plan.local_to_global[sel], k, v, n_heads, head_dim)
     out = linear(o, W.wo)
     if residual:
@@ -276,9 +278,9 @@ def mlp_sharded(x, w1, w2, order):
 
 
 def layer_forward(plan: Plan, x_local, wqkv, wo, w1, w2, n_heads, head_dim, k_full=None,
-                  v_full=None, rows=None, kv_bf16: bool = True):
+                  v_full=None, rows=None, proj_bf16: bool = True):
     """One decoder layer for the local rows: h1 = x + Attn(x); out = h1 + MLP(h1)."""
     h1, _, k_own, v_own = attn_forward(plan, x_local, wqkv, wo, n_heads, head_dim, k_full, v_full,
-                                       residual=True, rows=rows, kv_bf16=kv_bf16)
+                                       residual=True, rows=rows, proj_bf16=proj_bf16)
     out = mlp_forward(h1, w1, w2, residual=True)
     return out, k_own, v_own

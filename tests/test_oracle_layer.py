@@ -33,13 +33,13 @@ def _weights(h, H, hd, Fd, D, seed):
     return wqkv, wo, w1, w2
 
 
-def _library_layer(x, wq, wk, wv, wo, w1, w2, H, hd, kv_round=False):
-    """A plain decoder layer from torch library calls (fp64); with kv_round the
-    keys and values pass through torch's bf16 conversion first."""
+def _library_layer(x, wq, wk, wv, wo, w1, w2, H, hd, proj_round=False):
+    """A plain decoder layer from torch library calls (fp64); with proj_round the
+    queries, keys and values pass through torch's bf16 conversion first."""
     S, h = x.shape
     q, k, v = F.linear(x, wq), F.linear(x, wk), F.linear(x, wv)
-    if kv_round:
-        k, v = k.to(torch.bfloat16).double(), v.to(torch.bfloat16).double()
+    if proj_round:
+        q, k, v = (t.to(torch.bfloat16).double() for t in (q, k, v))
     heads = lambda t: t.view(S, H, hd).transpose(0, 1)
     a = F.scaled_dot_product_attention(heads(q), heads(k), heads(v), is_causal=True)
     h1 = x + F.linear(a.transpose(0, 1).reshape(S, h), wo)
@@ -51,14 +51,14 @@ def test_d1_layer_matches_library_layer(h, H, hd, Fd, S):
     wqkv, wo, w1, w2 = _weights(h, H, hd, Fd, 1, 10)
     x = _bf((S, h), 1)
     plan = O.zigzag_plan(S, 1, 0)
-    out, _, _ = O.layer_forward(plan, x, wqkv, wo, w1, w2, H, hd, kv_bf16=False)
+    out, _, _ = O.layer_forward(plan, x, wqkv, wo, w1, w2, H, hd, proj_bf16=False)
     W = O.f64(wqkv[0])
     ref = _library_layer(O.f64(x), W[:h], W[h:2 * h], W[2 * h:], O.f64(wo[0]), O.f64(w1[0]), O.f64(w2[0]), H, hd)
     assert torch.allclose(out, ref, rtol=1e-11, atol=1e-11)
-    # with the gathered K/V held in bf16: the library layer with K and V rounded to bf16
+    # with Q, K and V held in bf16: the library layer with them rounded to bf16
     out16, _, _ = O.layer_forward(plan, x, wqkv, wo, w1, w2, H, hd)
     ref16 = _library_layer(O.f64(x), W[:h], W[h:2 * h], W[2 * h:], O.f64(wo[0]), O.f64(w1[0]), O.f64(w2[0]), H,
-                           hd, kv_round=True)
+                           hd, proj_round=True)
     assert torch.allclose(out16, ref16, rtol=1e-11, atol=1e-11)
     assert not torch.allclose(out16, out, rtol=1e-6, atol=1e-6)
 
@@ -108,15 +108,15 @@ def test_shards_equal_whole_weights():
         assert torch.equal(O.f64(wqkv[d])[2 * Hs * hd:], W.wv[d * Hs * hd:(d + 1) * Hs * hd])
 
 
-@pytest.mark.parametrize("kv_bf16", [False, True])
+@pytest.mark.parametrize("proj_bf16", [False, True])
 @pytest.mark.parametrize("D,S", [(2, 32), (4, 64)])
-def test_rank_emulation_reassembles_unsharded_layer(D, S, kv_bf16):
+def test_rank_emulation_reassembles_unsharded_layer(D, S, proj_bf16):
     """All D ranks, each with its zigzag rows and the gathered K/V, give the
     unsharded layer over the whole sequence."""
     h, H, hd, Fd = 32, 4, 8, 64
     wqkv, wo, w1, w2 = _weights(h, H, hd, Fd, D, 50)
     x_all = _bf((S, h), 7)
-    full, _, _ = O.layer_forward(O.zigzag_plan(S, 1, 0), x_all, wqkv, wo, w1, w2, H, hd, kv_bf16=kv_bf16)
+    full, _, _ = O.layer_forward(O.zigzag_plan(S, 1, 0), x_all, wqkv, wo, w1, w2, H, hd, proj_bf16=proj_bf16)
     # phase 1: every rank projects its own K/V rows into the gathered buffers
     kf = torch.full((S, h), float("nan"), dtype=F64)
     vf = torch.full((S, h), float("nan"), dtype=F64)
@@ -129,7 +129,7 @@ def test_rank_emulation_reassembles_unsharded_layer(D, S, kv_bf16):
     got = torch.empty_like(full)
     for r in range(D):
         p = O.zigzag_plan(S, D, r)
-        out, _, _ = O.layer_forward(p, x_all[p.local_to_global], wqkv, wo, w1, w2, H, hd, kf, vf, kv_bf16=kv_bf16)
+        out, _, _ = O.layer_forward(p, x_all[p.local_to_global], wqkv, wo, w1, w2, H, hd, kf, vf, proj_bf16=proj_bf16)
         got[p.local_to_global] = out
     assert torch.allclose(got, full, rtol=1e-12, atol=1e-12)
 
@@ -174,7 +174,7 @@ def test_attention_is_sum_over_head_shards(D):
     h, H, hd, Fd, S = 32, 4, 8, 64, 24
     wqkv, wo, _, _ = _weights(h, H, hd, Fd, D, 80)
     x = _bf((S, h), 14)
-    got, _, _, _ = O.attn_forward(O.zigzag_plan(S, 1, 0), x, wqkv, wo, H, hd, residual=False, kv_bf16=False)
+    got, _, _, _ = O.attn_forward(O.zigzag_plan(S, 1, 0), x, wqkv, wo, H, hd, residual=False, proj_bf16=False)
     xx = O.f64(x)
     Hs = H // D
     ref = torch.zeros(S, h, dtype=F64)
