@@ -10,10 +10,10 @@ projection split-K with the residual, and the ring MLP with the residual; the
 output of layer l is the input of layer l+1.  All inputs (weights, generated
 per-layer K/V, x) are resident in HBM before timing starts.
 
-The step calls the library's step-level entry points in the order
-tsp_layer_forward composes them, with HIP events recorded between them on the
-launch stream: the per-launch time of the attention kernel (the dominant one,
-about 73% of the layer's FLOPs) gives the roofline figure.
+The step calls the three entry points that tsp_layer_forward composes
+(tsp_attn_project, tsp_attn_core, tsp_layer_post), with HIP events recorded
+between them on the launch stream: the per-launch time of the attention kernel
+(the dominant one, about 73% of the layer's FLOPs) gives the roofline figure.
 
 Prints ONE JSON line.  ``--gpus`` above 1 is refused: this build runs on one GPU.
 """
@@ -27,7 +27,12 @@ import time
 
 import torch
 
-from folded_tensor_sequence_tsp_amd import synth, tsp
+from folded_tensor_sequence_tsp_amd import profile_summary, synth, tsp
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+# rocprofv3 counter summary of the attention kernel on the default workload: its
+# traffic figure is used only while the kernel's sources are the ones profiled.
+TRAFFIC_SUMMARY = os.path.join(ROOT, "profiles", "attn_kernel_7b_128k_rank0.md")
 
 PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
 PEAK_HBM_GBS = 8000.0        # MI355X HBM3E
@@ -41,7 +46,7 @@ def layer_flops(n, S, D, C, d):
     return {
         "qkv": 2.0 * n * h * 3 * h,
         "attn": 4.0 * hd * H * pairs,
-        "oproj": 2.0 * n * h * h,
+        "oproj": 2.0 * n * h * h,  # O projection
         "mlp": 4.0 * n * h * F,
     }
 
@@ -55,6 +60,9 @@ def parse():
     ap.add_argument("--layers", type=int, default=None, help="layers per step (default: the workload's)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-rows", type=int, default=4, help="oracle sample rows per timing call")
+    ap.add_argument("--copy-probe-mib", type=int, default=0,
+                    help="also run one plain device copy of this many MiB before timing, so that a counter "
+                         "profile of the same command holds a reference kernel of known traffic")
     return ap.parse_args()
 
 
@@ -135,15 +143,16 @@ def main():
     x0 = synth.activations(W.wid, n, h, device=dev)
     q = torch.empty(n, h, dtype=torch.bfloat16, device=dev)
     a = torch.empty(n, h, dtype=torch.bfloat16, device=dev)
-    h1 = torch.empty(n, h, dtype=torch.bfloat16, device=dev)
+    a_lo = torch.empty(n, h, dtype=torch.bfloat16, device=dev)
     bufs = [torch.empty(n, h, dtype=torch.bfloat16, device=dev) for _ in range(2)]
-    ws = tsp.alloc_workspace(n, dims, D, tsp.WS_MLP)
+    ws = tsp.alloc_workspace(n, dims, D, tsp.WS_POST)
     torch.cuda.synchronize()
 
     stream = torch.cuda.current_stream()
-    stages = ["qkv", "attn", "oproj", "mlp"]
+    stages = ["qkv", "attn", "post"]
 
     def step(events=None):
+        # tsp_layer_forward's three parts, with events between them on the launch stream
         x = x0
         for l, (lw, kf, vf) in enumerate(layers):
             out = bufs[l % 2]
@@ -151,21 +160,28 @@ def main():
             if ev: ev[0].record(stream)
             tsp.attn_project(plan, dims, x, lw.wqkv, kf, vf, q)
             if ev: ev[1].record(stream)
-            tsp.attn_core(plan, dims, q, kf, vf, a)
+            tsp.attn_core(plan, dims, q, kf, vf, a, a_lo)
             if ev: ev[2].record(stream)
-            tsp.attn_out(dims, D, plan.rank, a, lw.wo, x, h1)
+            tsp.layer_post(dims, D, plan.rank, a, x, lw.wo, lw.w1, lw.w2, out, ws, attn_lo=a_lo)
             if ev: ev[3].record(stream)
-            tsp.mlp_forward(dims, D, plan.rank, h1, lw.w1, lw.w2, h1, out, ws)
-            if ev: ev[4].record(stream)
             x = out
         return x
+
+    if args.copy_probe_mib > 0:
+        nb = args.copy_probe_mib << 20
+        src = torch.ones(nb // 2, dtype=torch.bfloat16, device=dev)
+        dst = torch.empty_like(src)
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        print(f"[bench] copy probe: {nb} bytes read, {nb} bytes written", file=sys.stderr, flush=True)
+        del src, dst
 
     print(f"[bench] warmup {args.warmup}", file=sys.stderr, flush=True)
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
 
-    events = [[[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(n_layers)]
+    events = [[[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(n_layers)]
               for _ in range(args.steps)]
     print(f"[bench] timing {args.steps} steps", file=sys.stderr, flush=True)
     torch.cuda.synchronize()
@@ -184,6 +200,7 @@ def main():
     launches = args.steps * n_layers
     stage_ms = {k: v / launches for k, v in stage_ms.items()}   # ms per launch
     fl = layer_flops(n, S, D, plan.chunk_len, d)
+    fl["post"] = fl.pop("oproj") + fl.pop("mlp")
 
     ms_per_step = elapsed * 1e3 / args.steps
     layer_ms = ms_per_step / n_layers
@@ -224,7 +241,8 @@ def main():
             "frac": round(attn_tflops / PEAK_BF16_TFLOPS, 4),
             "flops_per_launch": fl["attn"],
             "ms_per_launch": round(stage_ms["attn"], 4),
-            "traffic": None,
+            "traffic": profile_summary.read_traffic(TRAFFIC_SUMMARY, "attn_kernel"),
+            "traffic_source": os.path.relpath(TRAFFIC_SUMMARY, ROOT),
         },
         "cpu_baseline": None,
     }

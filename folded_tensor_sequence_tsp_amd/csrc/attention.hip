@@ -247,15 +247,24 @@ __global__ __launch_bounds__(NTHREADS) void attn_kernel(const AttnArgs a) {
     const float l_tot = l_run + __shfl_xor(l_run, 32);
     if (wave_first + ql < valid) {
       const float inv = 1.0f / l_tot;
-      uint16_t* op = a.o + (row0 + wave_first + ql) * ld + hcol + 4 * half;
+      const int64_t off = (row0 + wave_first + ql) * ld + hcol + 4 * half;
 #pragma unroll
       for (int dt = 0; dt < C::DT; ++dt) {
 #pragma unroll
         for (int g = 0; g < 4; ++g) {
+          float r[4];
+#pragma unroll
+          for (int j = 0; j < 4; ++j) r[j] = o[dt][4 * g + j] * inv;
           u32x2 v;
-          v[0] = pack_bf16x2(o[dt][4 * g] * inv, o[dt][4 * g + 1] * inv);
-          v[1] = pack_bf16x2(o[dt][4 * g + 2] * inv, o[dt][4 * g + 3] * inv);
-          *reinterpret_cast<u32x2*>(op + dt * 32 + 8 * g) = v;
+          v[0] = pack_bf16x2(r[0], r[1]);
+          v[1] = pack_bf16x2(r[2], r[3]);
+          *reinterpret_cast<u32x2*>(a.o + off + dt * 32 + 8 * g) = v;
+          if (a.o_lo) {  // rounding residual: r - bf16(r), itself rounded to bf16
+            u32x2 w;
+            w[0] = pack_bf16x2(r[0] - __uint_as_float(v[0] << 16), r[1] - __uint_as_float(v[0] & 0xffff0000u));
+            w[1] = pack_bf16x2(r[2] - __uint_as_float(v[1] << 16), r[3] - __uint_as_float(v[1] & 0xffff0000u));
+            *reinterpret_cast<u32x2*>(a.o_lo + off + dt * 32 + 8 * g) = w;
+          }
         }
       }
     }

@@ -14,6 +14,10 @@ typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
+
+constexpr float F16_MAX = 65504.0f;
 
 // fp32 -> bf16 bits with the hardware conversion (v_cvt_pk_bf16_f32, round to
 // nearest even).
@@ -26,6 +30,15 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
   bf16x2 v;
   v[0] = (__bf16)a;
   v[1] = (__bf16)b;
+  return __builtin_bit_cast(uint32_t, v);
+}
+
+// Two fp32 -> packed fp16x2 (low half = a), round to nearest even, saturated
+// to the finite fp16 range (one v_cvt_pk_f16_f32 after the clamps).
+__device__ __forceinline__ uint32_t pack_f16x2_sat(float a, float b) {
+  f16x2 v;
+  v[0] = (_Float16)fminf(fmaxf(a, -F16_MAX), F16_MAX);
+  v[1] = (_Float16)fminf(fmaxf(b, -F16_MAX), F16_MAX);
   return __builtin_bit_cast(uint32_t, v);
 }
 
@@ -47,6 +60,20 @@ __device__ __forceinline__ f32x16 mfma32(const bf16x8& a, const bf16x8& b, const
   return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
 }
 
+__device__ __forceinline__ f32x16 mfma32_f16(const f16x8& a, const f16x8& b, const f32x16& c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_f16(a, b, c, 0, 0, 0);
+}
+
 __device__ __forceinline__ bf16x8 as_bf16x8(const u32x4& v) { return __builtin_bit_cast(bf16x8, v); }
+__device__ __forceinline__ f16x8 as_f16x8(const u32x4& v) { return __builtin_bit_cast(f16x8, v); }
+
+// 32x32x16 MFMA on 16-bit operands given as raw bits: fp16 when F16, else bf16.
+template <bool F16>
+__device__ __forceinline__ f32x16 mfma32_bits(const u32x4& a, const u32x4& b, const f32x16& c) {
+  if constexpr (F16)
+    return mfma32_f16(as_f16x8(a), as_f16x8(b), c);
+  else
+    return mfma32(as_bf16x8(a), as_bf16x8(b), c);
+}
 
 }  // namespace tsp

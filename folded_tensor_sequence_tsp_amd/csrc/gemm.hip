@@ -1,4 +1,4 @@
-// Shard-iterated bf16 GEMM engine for gfx950 (CDNA4) on v_mfma_f32_32x32x16_bf16.
+// Shard-iterated 16-bit GEMM engine for gfx950 (CDNA4) on v_mfma_f32_32x32x16_{bf16,f16}.
 //
 // C = A . B^T with both operands K-contiguous (weights stored out x in).  The
 // weight operand arrives as D separate shards, the way TSP hands them to a
@@ -37,31 +37,75 @@ struct Cfg {
   static constexpr int LDS_ELEMS = 2 * (BM + BN) * LDK;
 };
 
+// Epilogue of 8 consecutive output columns of one row (fp32 values v[0..7]):
+// GELU (stored as fp16 scaled by 2^-row_exp) / row rescale and residual /
+// Q-K-V routing, then 16-byte stores.  `col` is the column inside the shard's
+// N_s block and a multiple of 8, so the 8 values never straddle a head or a
+// Q/K/V part (head_dim is a multiple of 32).
 template <int EPI>
-__device__ __forceinline__ void store_elem(const GemmArgs& g, int nshard, int row, int col, float acc) {
+__device__ __forceinline__ void store_row8(const GemmArgs& g, int nshard, int row, int col, float* v) {
+  u32x4 packed;
   if constexpr (EPI == EPI_RESID) {
     const int64_t idx = (int64_t)row * g.ldo + col;
-    float v = acc;
-    if (g.residual) v += bf16_to_f32(g.residual[idx]);
-    g.out[idx] = f32_to_bf16(v);
+    if (g.row_exp) {
+      const int e = g.row_exp[row];
+#pragma unroll
+      for (int j = 0; j < 8; ++j) v[j] = __builtin_amdgcn_ldexpf(v[j], e);
+    }
+    if (g.residual) {
+      if (g.res_f32) {
+        const float* rp = static_cast<const float*>(g.residual) + idx;
+        const f32x4 r0 = *reinterpret_cast<const f32x4*>(rp);
+        const f32x4 r1 = *reinterpret_cast<const f32x4*>(rp + 4);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          v[j] += r0[j];
+          v[4 + j] += r1[j];
+        }
+      } else {
+        const u32x4 r = *reinterpret_cast<const u32x4*>(static_cast<const uint16_t*>(g.residual) + idx);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          v[2 * j] += __uint_as_float(r[j] << 16);
+          v[2 * j + 1] += __uint_as_float(r[j] & 0xffff0000u);
+        }
+      }
+    }
+    if (g.out_f32) {
+      float* op = static_cast<float*>(g.out) + idx;
+      *reinterpret_cast<f32x4*>(op) = f32x4{v[0], v[1], v[2], v[3]};
+      *reinterpret_cast<f32x4*>(op + 4) = f32x4{v[4], v[5], v[6], v[7]};
+    } else {
+#pragma unroll
+      for (int j = 0; j < 4; ++j) packed[j] = pack_bf16x2(v[2 * j], v[2 * j + 1]);
+      *reinterpret_cast<u32x4*>(static_cast<uint16_t*>(g.out) + idx) = packed;
+    }
   } else if constexpr (EPI == EPI_GELU) {
-    g.out[(int64_t)row * g.ldo + (int64_t)nshard * g.N_s + col] = f32_to_bf16(gelu_tanh(acc));
+    const int e = g.row_exp ? g.row_exp[row] : 0;
+    const int e_in = g.gelu_in_scaled ? e : 0;
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+      packed[j] = pack_f16x2_sat(__builtin_amdgcn_ldexpf(gelu_tanh(__builtin_amdgcn_ldexpf(v[2 * j], e_in)), -e),
+                                 __builtin_amdgcn_ldexpf(gelu_tanh(__builtin_amdgcn_ldexpf(v[2 * j + 1], e_in)), -e));
+    *reinterpret_cast<u32x4*>(static_cast<uint16_t*>(g.out) + (int64_t)row * g.ldo + (int64_t)nshard * g.N_s +
+                              col) = packed;
   } else {
+#pragma unroll
+    for (int j = 0; j < 4; ++j) packed[j] = pack_bf16x2(v[2 * j], v[2 * j + 1]);
     const int hs_hd = g.heads_per_shard * g.head_dim;
-    const int part = col / hs_hd;  // 0 = Q, 1 = K, 2 = V
+    const int part = col >= 2 * hs_hd ? 2 : (col >= hs_hd ? 1 : 0);  // 0 = Q, 1 = K, 2 = V
     const int gcol = nshard * hs_hd + (col - part * hs_hd);
-    const uint16_t b = f32_to_bf16(acc);
     if (part == 0) {
-      g.q_out[(int64_t)row * g.hidden + gcol] = b;
+      *reinterpret_cast<u32x4*>(g.q_out + (int64_t)row * g.hidden + gcol) = packed;
     } else {
       const int64_t gpos = row < g.chunk_len ? g.chunk_start0 + row : g.chunk_start1 + (row - g.chunk_len);
       uint16_t* dst = part == 1 ? g.k_full : g.v_full;
-      dst[gpos * g.hidden + gcol] = b;
+      *reinterpret_cast<u32x4*>(dst + gpos * g.hidden + gcol) = packed;
     }
   }
 }
 
-template <int BM, int BN, int EPI>
+template <int BM, int BN, int EPI, bool F16>
 __global__ __launch_bounds__(NTHREADS) void gemm_kernel(const GemmArgs g) {
   using C = Cfg<BM, BN>;
   __shared__ __attribute__((aligned(16))) uint16_t lds[C::LDS_ELEMS];
@@ -91,18 +135,20 @@ __global__ __launch_bounds__(NTHREADS) void gemm_kernel(const GemmArgs g) {
   const int m0 = tm * BM;
 
   const int kt_per_shard = g.K_s / BK;
-  const int k_tiles = kt_per_shard * g.k_shards;
+  const int reps = g.A_lo ? 2 : 1;  // K range of a shard walked once per part of A
+  const int kt_per_rep = kt_per_shard * reps;
+  const int k_tiles = kt_per_rep * g.k_shards;
 
   // Per-thread load coordinates: chunk c = i*256 + tid -> row c/8, 16-byte column c%8.
   const int ld_row = tid >> 3;
   const int ld_kc = (tid & 7) * 8;
   constexpr int ROWS_PER_PASS = NTHREADS / 8;  // 32
 
-  const uint16_t* a_rows[C::A_CHUNKS];
+  int64_t a_off[C::A_CHUNKS];
 #pragma unroll
   for (int i = 0; i < C::A_CHUNKS; ++i) {
     const int r = min(m0 + i * ROWS_PER_PASS + ld_row, g.M - 1);
-    a_rows[i] = g.A + (int64_t)r * g.lda + ld_kc;
+    a_off[i] = (int64_t)r * g.lda + ld_kc;
   }
   int64_t b_off[C::B_CHUNKS];
 #pragma unroll
@@ -113,8 +159,11 @@ __global__ __launch_bounds__(NTHREADS) void gemm_kernel(const GemmArgs g) {
 
   u32x4 ra[C::A_CHUNKS], rb[C::B_CHUNKS];
   auto load_tile = [&](int t) {
-    const int s = t / kt_per_shard;
-    const int kt = t - s * kt_per_shard;
+    const int s = t / kt_per_rep;
+    int kt = t - s * kt_per_rep;
+    const bool lo = kt >= kt_per_shard;
+    if (lo) kt -= kt_per_shard;
+    const uint16_t* abase = lo ? g.A_lo : g.A;
     int d;
     int64_t acol;
     if (g.k_shards > 1) {
@@ -127,7 +176,7 @@ __global__ __launch_bounds__(NTHREADS) void gemm_kernel(const GemmArgs g) {
     }
     const uint16_t* bp = g.B[d] + kt * BK;
 #pragma unroll
-    for (int i = 0; i < C::A_CHUNKS; ++i) ra[i] = *reinterpret_cast<const u32x4*>(a_rows[i] + acol);
+    for (int i = 0; i < C::A_CHUNKS; ++i) ra[i] = *reinterpret_cast<const u32x4*>(abase + a_off[i] + acol);
 #pragma unroll
     for (int i = 0; i < C::B_CHUNKS; ++i) rb[i] = *reinterpret_cast<const u32x4*>(bp + b_off[i]);
   };
@@ -159,37 +208,54 @@ __global__ __launch_bounds__(NTHREADS) void gemm_kernel(const GemmArgs g) {
     const uint16_t* b_base = Bs + (buf * BN + wn * C::WN + frag_row) * LDK + frag_k;
 #pragma unroll
     for (int kk = 0; kk < BK / 16; ++kk) {
-      bf16x8 af[C::FM], bfv[C::FN];
+      u32x4 af[C::FM], bfv[C::FN];
+#pragma unroll
+      for (int i = 0; i < C::FM; ++i) af[i] = *reinterpret_cast<const u32x4*>(a_base + i * 32 * LDK + kk * 16);
+#pragma unroll
+      for (int j = 0; j < C::FN; ++j) bfv[j] = *reinterpret_cast<const u32x4*>(b_base + j * 32 * LDK + kk * 16);
 #pragma unroll
       for (int i = 0; i < C::FM; ++i)
-        af[i] = as_bf16x8(*reinterpret_cast<const u32x4*>(a_base + i * 32 * LDK + kk * 16));
 #pragma unroll
-      for (int j = 0; j < C::FN; ++j)
-        bfv[j] = as_bf16x8(*reinterpret_cast<const u32x4*>(b_base + j * 32 * LDK + kk * 16));
-#pragma unroll
-      for (int i = 0; i < C::FM; ++i)
-#pragma unroll
-        for (int j = 0; j < C::FN; ++j) acc[i][j] = mfma32(af[i], bfv[j], acc[i][j]);
+        for (int j = 0; j < C::FN; ++j) acc[i][j] = mfma32_bits<F16>(af[i], bfv[j], acc[i][j]);
     }
     if (t + 1 < k_tiles) store_tile(buf ^ 1);
     __syncthreads();
   }
 
-  // Epilogue.  32x32 accumulator layout: lane holds column (lane % 32) and rows
-  // 8*(e/4) + 4*(lane/32) + e%4 for its 16 values e.
-  const int col_l = lane & 31;
-  const int row_l = 4 * (lane >> 5);
+  // Epilogue, staged through LDS (free after the last barrier of the K loop) so
+  // that global stores are 16-byte row segments.  The 32x32 accumulator layout:
+  // lane holds column (lane % 32) and rows 8*(e/4) + 4*(lane/32) + e%4 of its
+  // 16 values e.  Each wave stages one 32-row strip of its sub-tile at a time
+  // in fp32 ([32][WN + 4] floats), then reads it back as 8-column row pieces.
+  {
+    constexpr int SLD = C::WN + 4;  // padded fp32 row
+    float* stage = reinterpret_cast<float*>(lds) + wave * 32 * SLD;
+    const int col_l = lane & 31;
+    const int row_l = 4 * (lane >> 5);
+    constexpr int PIECES = 32 * (C::WN / 8);  // 8-column pieces in a strip
 #pragma unroll
-  for (int i = 0; i < C::FM; ++i) {
+    for (int i = 0; i < C::FM; ++i) {
 #pragma unroll
-    for (int j = 0; j < C::FN; ++j) {
-      const int col = n0 + wn * C::WN + j * 32 + col_l;
-      if (col >= g.N_s) continue;
+      for (int j = 0; j < C::FN; ++j)
 #pragma unroll
-      for (int e = 0; e < 16; ++e) {
-        const int row = m0 + wm * C::WM + i * 32 + 8 * (e >> 2) + row_l + (e & 3);
-        if (row < g.M) store_elem<EPI>(g, nshard, row, col, acc[i][j][e]);
+        for (int e = 0; e < 16; ++e)
+          stage[(8 * (e >> 2) + row_l + (e & 3)) * SLD + j * 32 + col_l] = acc[i][j][e];
+      __syncthreads();
+#pragma unroll
+      for (int it = 0; it < PIECES / 64; ++it) {
+        const int piece = it * 64 + lane;
+        const int r = piece / (C::WN / 8);
+        const int c8 = (piece - r * (C::WN / 8)) * 8;
+        const int row = m0 + wm * C::WM + i * 32 + r;
+        const int col = n0 + wn * C::WN + c8;
+        float v[8];
+        const f32x4 lo = *reinterpret_cast<const f32x4*>(stage + r * SLD + c8);
+        const f32x4 hi = *reinterpret_cast<const f32x4*>(stage + r * SLD + c8 + 4);
+#pragma unroll
+        for (int k = 0; k < 4; ++k) { v[k] = lo[k]; v[4 + k] = hi[k]; }
+        if (row < g.M && col < g.N_s) store_row8<EPI>(g, nshard, row, col, v);
       }
+      __syncthreads();
     }
   }
 }
@@ -199,10 +265,21 @@ hipError_t launch_tiles(const GemmArgs& g, hipStream_t stream) {
   const int tiles_m = (g.M + BM - 1) / BM;
   const int tiles_n = ((g.N_s + BN - 1) / BN) * g.n_shards;
   const dim3 grid(tiles_m * tiles_n), block(NTHREADS);
+  // Instantiated: QKV (bf16), W1 + GELU (bf16 or fp16), O projection (bf16), W2 (fp16).
   switch (g.epilogue) {
-    case EPI_QKV: hipLaunchKernelGGL((gemm_kernel<BM, BN, EPI_QKV>), grid, block, 0, stream, g); break;
-    case EPI_GELU: hipLaunchKernelGGL((gemm_kernel<BM, BN, EPI_GELU>), grid, block, 0, stream, g); break;
-    default: hipLaunchKernelGGL((gemm_kernel<BM, BN, EPI_RESID>), grid, block, 0, stream, g); break;
+    case EPI_QKV: hipLaunchKernelGGL((gemm_kernel<BM, BN, EPI_QKV, false>), grid, block, 0, stream, g); break;
+    case EPI_GELU:
+      if (g.f16)
+        hipLaunchKernelGGL((gemm_kernel<BM, BN, EPI_GELU, true>), grid, block, 0, stream, g);
+      else
+        hipLaunchKernelGGL((gemm_kernel<BM, BN, EPI_GELU, false>), grid, block, 0, stream, g);
+      break;
+    default:
+      if (g.f16)
+        hipLaunchKernelGGL((gemm_kernel<BM, BN, EPI_RESID, true>), grid, block, 0, stream, g);
+      else
+        hipLaunchKernelGGL((gemm_kernel<BM, BN, EPI_RESID, false>), grid, block, 0, stream, g);
+      break;
   }
   return hipGetLastError();
 }

@@ -10,28 +10,42 @@
 namespace tsp {
 
 enum GemmEpilogue : int32_t {
-  EPI_QKV = 0,    // Q -> q_out, K/V rows -> k_full/v_full at global zigzag positions
-  EPI_GELU = 1,   // out[:, shard block] = bf16(GELU(acc))
-  EPI_RESID = 2,  // out = bf16(acc [+ residual])
+  EPI_QKV = 0,    // Q -> q_out, K/V rows -> k_full/v_full at global zigzag positions (bf16)
+  EPI_GELU = 1,   // out[:, shard block] = fp16(GELU(acc * 2^in_exp) * 2^-row_exp[row])
+  EPI_RESID = 2,  // out = (acc * 2^row_exp[row] [+ residual]) as bf16 or fp32
 };
 
-// C = A . B^T over bf16 operands with an fp32 accumulator.
+// C = A . B^T over 16-bit operands (bf16, or fp16 when f16 is set) with an fp32
+// accumulator.
 //  N-sharded ("column") mode, k_shards == 1: output columns come in n_shards
 //    blocks of N_s; block d uses B[d] ([N_s x K_s]); A is [M x K_s].
 //  K-sharded ("split-K") mode, n_shards == 1: B[d] is [N_s x K_s] and A is
 //    [M x k_shards*K_s]; shards are visited in ring order
 //    (ring_start + s) mod k_shards with one accumulator.
+// row_exp (nullable = all 0) holds a power-of-two exponent per output row:
+//  EPI_GELU scales its fp16 output by 2^-row_exp (and, when gelu_in_scaled, the
+//  accumulator by 2^+row_exp before GELU: the A rows were stored scaled);
+//  EPI_RESID scales the accumulator by 2^+row_exp before the residual.
 struct GemmArgs {
+  int32_t f16;  // operands are fp16 (else bf16)
   const uint16_t* A;
+  // Optional low part of A (bf16 residual of A's rounding, same layout): each
+  // shard's K range is then contracted twice against the same B columns, once
+  // with A and once with A_lo, into the same accumulator.
+  const uint16_t* A_lo;
   int64_t lda;
   const uint16_t* B[TSP_MAX_D];
   int32_t M, N_s, K_s;
   int32_t n_shards, k_shards, ring_start;
   int32_t epilogue;
   // EPI_GELU / EPI_RESID
-  uint16_t* out;
+  void* out;
   int64_t ldo;
-  const uint16_t* residual;  // EPI_RESID, nullable
+  const void* residual;  // EPI_RESID, nullable
+  int32_t res_f32;       // residual is fp32 (else bf16)
+  int32_t out_f32;       // EPI_RESID output is fp32 (else bf16)
+  const int32_t* row_exp;
+  int32_t gelu_in_scaled;
   // EPI_QKV
   uint16_t* q_out;
   uint16_t* k_full;
@@ -42,11 +56,23 @@ struct GemmArgs {
 
 hipError_t launch_gemm(const GemmArgs& args, hipStream_t stream);
 
+// For each row i of x [n x h] (fp32 when x_f32, else bf16):
+//   row_exp[i] = floor(log2(rms of the row)) (0 for a zero or non-finite rms),
+//   and, when x16 is not null, x16[i] = fp16(x[i] * 2^-row_exp[i]) (saturated).
+hipError_t launch_row_prep(const void* x, int32_t x_f32, int64_t n, int32_t h, int32_t* row_exp, uint16_t* x16,
+                           hipStream_t stream);
+
+// dst[d] = fp16(src[d]) for D shards of `count` bf16 elements each (count % 8 == 0);
+// values beyond the fp16 range saturate to +-65504.
+hipError_t launch_bf16_to_f16(const uint16_t* const* src, uint16_t* dst, int32_t D, int64_t count,
+                              hipStream_t stream);
+
 struct AttnArgs {
   const uint16_t* q;  // [n_local x hidden]
   const uint16_t* k;  // [seq_len x hidden]
   const uint16_t* v;  // [seq_len x hidden]
   uint16_t* o;        // [n_local x hidden]
+  uint16_t* o_lo;     // nullable: bf16(out - o), the rounding residual of o
   int64_t seq_len, chunk_len, chunk_start0, chunk_start1;
   int32_t hidden, n_heads, head_dim;
 };

@@ -34,15 +34,18 @@ tsp_status check_shards(const uint16_t* const* w, int32_t D) {
 }
 
 // Shape rules shared by every call.  `need_attn` / `need_mlp` add the widths
-// the attention and MLP kernels need.
-tsp_status check_dims(const tsp_dims* d, int32_t D, bool need_attn, bool need_mlp) {
+// the attention and MLP kernels need; `head_shards` (default: need_attn) adds
+// that the heads split evenly over the D weight shards, which the attention
+// core alone does not need.
+tsp_status check_dims(const tsp_dims* d, int32_t D, bool need_attn, bool need_mlp, int head_shards = -1) {
   if (!d) return TSP_ERR_INVALID_ARG;
   if (D < 1 || D > TSP_MAX_D) return TSP_ERR_INVALID_ARG;
   if (d->hidden <= 0 || d->n_heads <= 0 || d->head_dim <= 0 || d->ffn <= 0) return TSP_ERR_SHAPE;
   if ((int64_t)d->n_heads * d->head_dim != d->hidden) return TSP_ERR_SHAPE;
   if (d->hidden % 64 != 0) return TSP_ERR_UNSUPPORTED;
+  if (head_shards < 0) head_shards = need_attn ? 1 : 0;
+  if (head_shards && d->n_heads % D != 0) return TSP_ERR_SHAPE;
   if (need_attn) {
-    if (d->n_heads % D != 0) return TSP_ERR_SHAPE;
     if (d->head_dim != 64 && d->head_dim != 128) return TSP_ERR_UNSUPPORTED;
   }
   if (need_mlp) {
@@ -69,12 +72,26 @@ tsp_status check_plan(const tsp_plan* p) {
   return TSP_OK;
 }
 
-size_t ws_attn(int64_t n, const tsp_dims* d) { return 2 * round_up((size_t)n * d->hidden * 2); }
+// Attention workspace: Q, then the attention output as a bf16 pair (hi, lo).
+size_t ws_attn(int64_t n, const tsp_dims* d) { return 3 * round_up((size_t)n * d->hidden * 2); }
 
-size_t ws_mlp(int64_t n, const tsp_dims* d) {
+// MLP workspace: fp16 GELU output for one token block, the fp16 copy of all W2
+// shards, and one int32 row exponent per token.
+struct MlpWs {
+  size_t h_off, w2_off, exp_off, total;
+};
+
+MlpWs mlp_ws(int64_t n, const tsp_dims* d) {
   const int64_t mb = n < MLP_TOKEN_BLOCK ? n : MLP_TOKEN_BLOCK;
-  return round_up((size_t)mb * d->ffn * 2);
+  MlpWs w;
+  w.h_off = 0;
+  w.w2_off = round_up((size_t)mb * d->ffn * 2);
+  w.exp_off = w.w2_off + round_up((size_t)d->hidden * d->ffn * 2);
+  w.total = w.exp_off + round_up((size_t)n * 4);
+  return w;
 }
+
+size_t ws_mlp(int64_t n, const tsp_dims* d) { return mlp_ws(n, d).total; }
 
 tsp_status from_hip(hipError_t e) { return e == hipSuccess ? TSP_OK : TSP_ERR_HIP; }
 
@@ -108,12 +125,13 @@ tsp_status run_project(const tsp_plan* plan, const tsp_dims* dims, const uint16_
 }
 
 tsp_status run_core(const tsp_plan* plan, const tsp_dims* dims, const uint16_t* q, const uint16_t* k_full,
-                    const uint16_t* v_full, uint16_t* attn_out, hipStream_t stream) {
+                    const uint16_t* v_full, uint16_t* attn_out, uint16_t* attn_lo, hipStream_t stream) {
   AttnArgs a{};
   a.q = q;
   a.k = k_full;
   a.v = v_full;
   a.o = attn_out;
+  a.o_lo = attn_lo;
   a.seq_len = plan->seq_len;
   a.chunk_len = plan->chunk_len;
   a.chunk_start0 = plan->chunk_start[0];
@@ -125,9 +143,11 @@ tsp_status run_core(const tsp_plan* plan, const tsp_dims* dims, const uint16_t* 
 }
 
 tsp_status run_out(int64_t n, const tsp_dims* dims, int32_t D, int32_t start, const uint16_t* attn,
-                   const uint16_t* const* wo, const uint16_t* residual, uint16_t* out, hipStream_t stream) {
+                   const uint16_t* attn_lo, const uint16_t* const* wo, const uint16_t* residual, void* out,
+                   bool out_f32, hipStream_t stream) {
   GemmArgs g{};
   g.A = attn;
+  g.A_lo = attn_lo;
   g.lda = dims->hidden;
   for (int d = 0; d < D; ++d) g.B[d] = wo[d];
   g.M = (int32_t)n;
@@ -138,22 +158,27 @@ tsp_status run_out(int64_t n, const tsp_dims* dims, int32_t D, int32_t start, co
   g.ring_start = start;
   g.epilogue = EPI_RESID;
   g.out = out;
+  g.out_f32 = out_f32;
   g.ldo = dims->hidden;
   g.residual = residual;
   return from_hip(launch_gemm(g, stream));
 }
 
-tsp_status run_mlp(int64_t n, const tsp_dims* dims, int32_t D, int32_t start, const uint16_t* x,
-                   const uint16_t* const* w1, const uint16_t* const* w2, const uint16_t* residual, uint16_t* y,
-                   void* ws, hipStream_t stream) {
-  uint16_t* hbuf = static_cast<uint16_t*>(ws);
+// The two MLP GEMMs over token blocks.  `a` holds the MLP input rows: bf16, or
+// (a_f16) fp16 scaled by 2^-row_exp.  `w1` are bf16 or fp16 shards to match;
+// `w2h` is the fp16 copy of the W2 shards (D blocks of [hidden x F_s]).
+// y = [residual +] sum_k GELU(x W1_{d_k}^T) W2_{d_k}^T, fp32 across all shards.
+tsp_status run_mlp_core(int64_t n, const tsp_dims* dims, int32_t D, int32_t start, const uint16_t* a, bool a_f16,
+                        const uint16_t* const* w1, const uint16_t* w2h, const int32_t* row_exp,
+                        const void* residual, bool res_f32, uint16_t* y, uint16_t* hbuf, hipStream_t stream) {
   const int64_t h = dims->hidden;
   const int32_t fs = dims->ffn / D;
   for (int64_t b0 = 0; b0 < n; b0 += MLP_TOKEN_BLOCK) {
     const int64_t mb = (n - b0) < MLP_TOKEN_BLOCK ? (n - b0) : MLP_TOKEN_BLOCK;
-    // GELU(x W1_d^T) for every shard d -> hbuf[:, d*F_s .. (d+1)*F_s)
+    // fp16(GELU(x W1_d^T) * 2^-row_exp) for every shard d -> hbuf[:, d*F_s .. (d+1)*F_s)
     GemmArgs g1{};
-    g1.A = x + b0 * h;
+    g1.f16 = a_f16;
+    g1.A = a + b0 * h;
     g1.lda = h;
     for (int d = 0; d < D; ++d) g1.B[d] = w1[d];
     g1.M = (int32_t)mb;
@@ -164,13 +189,16 @@ tsp_status run_mlp(int64_t n, const tsp_dims* dims, int32_t D, int32_t start, co
     g1.epilogue = EPI_GELU;
     g1.out = hbuf;
     g1.ldo = dims->ffn;
+    g1.row_exp = row_exp + b0;
+    g1.gelu_in_scaled = a_f16;
     tsp_status s = from_hip(launch_gemm(g1, stream));
     if (s != TSP_OK) return s;
-    // y = [residual +] sum over shards in ring order of hbuf[:, d block] W2_d^T
+    // y = [residual +] 2^row_exp * sum over shards in ring order of hbuf[:, d block] W2_d^T
     GemmArgs g2{};
+    g2.f16 = 1;
     g2.A = hbuf;
     g2.lda = dims->ffn;
-    for (int d = 0; d < D; ++d) g2.B[d] = w2[d];
+    for (int d = 0; d < D; ++d) g2.B[d] = w2h + (int64_t)d * h * fs;
     g2.M = (int32_t)mb;
     g2.N_s = (int32_t)h;
     g2.K_s = fs;
@@ -180,11 +208,78 @@ tsp_status run_mlp(int64_t n, const tsp_dims* dims, int32_t D, int32_t start, co
     g2.epilogue = EPI_RESID;
     g2.out = y + b0 * h;
     g2.ldo = h;
-    g2.residual = residual ? residual + b0 * h : nullptr;
+    if (residual)
+      g2.residual = res_f32 ? (const void*)(static_cast<const float*>(residual) + b0 * h)
+                            : (const void*)(static_cast<const uint16_t*>(residual) + b0 * h);
+    g2.res_f32 = res_f32;
+    g2.row_exp = row_exp + b0;
     s = from_hip(launch_gemm(g2, stream));
     if (s != TSP_OK) return s;
   }
   return TSP_OK;
+}
+
+tsp_status run_mlp(int64_t n, const tsp_dims* dims, int32_t D, int32_t start, const uint16_t* x,
+                   const uint16_t* const* w1, const uint16_t* const* w2, const uint16_t* residual, uint16_t* y,
+                   void* ws, hipStream_t stream) {
+  if (n == 0) return TSP_OK;
+  const MlpWs lay = mlp_ws(n, dims);
+  char* base = static_cast<char*>(ws);
+  uint16_t* hbuf = reinterpret_cast<uint16_t*>(base + lay.h_off);
+  uint16_t* w2h = reinterpret_cast<uint16_t*>(base + lay.w2_off);
+  int32_t* row_exp = reinterpret_cast<int32_t*>(base + lay.exp_off);
+  tsp_status s = from_hip(launch_row_prep(x, 0, n, dims->hidden, row_exp, nullptr, stream));
+  if (s != TSP_OK) return s;
+  s = from_hip(launch_bf16_to_f16(w2, w2h, D, (int64_t)dims->hidden * (dims->ffn / D), stream));
+  if (s != TSP_OK) return s;
+  return run_mlp_core(n, dims, D, start, x, false, w1, w2h, row_exp, residual, false, y, hbuf, stream);
+}
+
+// Workspace of the post-attention half of the layer: fp32 h1, its scaled fp16
+// copy, row exponents, fp16 W1 and W2 shards and the fp16 GELU block.
+struct PostWs {
+  size_t h1_off, h16_off, exp_off, w1_off, w2_off, hbuf_off, total;
+};
+
+PostWs post_ws(int64_t n, const tsp_dims* d) {
+  const int64_t mb = n < MLP_TOKEN_BLOCK ? n : MLP_TOKEN_BLOCK;
+  PostWs w;
+  w.h1_off = 0;
+  w.h16_off = round_up((size_t)n * d->hidden * 4);
+  w.exp_off = w.h16_off + round_up((size_t)n * d->hidden * 2);
+  w.w1_off = w.exp_off + round_up((size_t)n * 4);
+  w.w2_off = w.w1_off + round_up((size_t)d->ffn * d->hidden * 2);
+  w.hbuf_off = w.w2_off + round_up((size_t)d->ffn * d->hidden * 2);
+  w.total = w.hbuf_off + round_up((size_t)mb * d->ffn * 2);
+  return w;
+}
+
+// Whole layer: Q and attention-output buffers, then the post workspace.
+size_t ws_layer(int64_t n, const tsp_dims* d) { return ws_attn(n, d) + post_ws(n, d).total; }
+
+// h1 = x + attn W_o^T (fp32, split-K over head shards from `start`), then
+// out = h1 + MLP(h1) on scaled fp16 operands with the ring from `start`.
+tsp_status run_post(int64_t n, const tsp_dims* dims, int32_t D, int32_t start, const uint16_t* attn,
+                    const uint16_t* attn_lo, const uint16_t* x, const uint16_t* const* wo, const uint16_t* const* w1,
+                    const uint16_t* const* w2, uint16_t* out, void* ws, hipStream_t stream) {
+  if (n == 0) return TSP_OK;
+  const PostWs lay = post_ws(n, dims);
+  char* base = static_cast<char*>(ws);
+  float* h1 = reinterpret_cast<float*>(base + lay.h1_off);
+  uint16_t* h16 = reinterpret_cast<uint16_t*>(base + lay.h16_off);
+  int32_t* row_exp = reinterpret_cast<int32_t*>(base + lay.exp_off);
+  uint16_t* w1h = reinterpret_cast<uint16_t*>(base + lay.w1_off);
+  uint16_t* w2h = reinterpret_cast<uint16_t*>(base + lay.w2_off);
+  uint16_t* hbuf = reinterpret_cast<uint16_t*>(base + lay.hbuf_off);
+  const int64_t shard_elems = (int64_t)dims->hidden * (dims->ffn / D);
+  tsp_status s;
+  if ((s = run_out(n, dims, D, start, attn, attn_lo, wo, x, h1, true, stream)) != TSP_OK) return s;
+  if ((s = from_hip(launch_row_prep(h1, 1, n, dims->hidden, row_exp, h16, stream))) != TSP_OK) return s;
+  if ((s = from_hip(launch_bf16_to_f16(w1, w1h, D, shard_elems, stream))) != TSP_OK) return s;
+  if ((s = from_hip(launch_bf16_to_f16(w2, w2h, D, shard_elems, stream))) != TSP_OK) return s;
+  const uint16_t* w1h_shards[TSP_MAX_D];
+  for (int d = 0; d < D; ++d) w1h_shards[d] = w1h + d * shard_elems;
+  return run_mlp_core(n, dims, D, start, h16, true, w1h_shards, w2h, row_exp, h1, true, out, hbuf, stream);
 }
 
 }  // namespace
@@ -229,11 +324,12 @@ size_t tsp_workspace_size(int64_t n_tokens, const tsp_dims* dims, int32_t D, int
     case TSP_WS_MLP:
       if (check_dims(dims, D, false, true) != TSP_OK) return 0;
       return ws_mlp(n_tokens, dims);
-    case TSP_WS_LAYER: {
+    case TSP_WS_LAYER:
       if (check_dims(dims, D, true, true) != TSP_OK) return 0;
-      const size_t a = ws_attn(n_tokens, dims), m = ws_mlp(n_tokens, dims);
-      return round_up((size_t)n_tokens * dims->hidden * 2) + (a > m ? a : m);
-    }
+      return ws_layer(n_tokens, dims);
+    case TSP_WS_POST:
+      if (check_dims(dims, D, true, true) != TSP_OK) return 0;
+      return post_ws(n_tokens, dims).total;
     default:
       return 0;
   }
@@ -252,30 +348,31 @@ tsp_status tsp_attn_project(const tsp_plan* plan, const tsp_dims* dims, const ui
 }
 
 tsp_status tsp_attn_core(const tsp_plan* plan, const tsp_dims* dims, const uint16_t* q, const uint16_t* k_full,
-                         const uint16_t* v_full, uint16_t* attn_out, hipStream_t stream) {
+                         const uint16_t* v_full, uint16_t* attn_out, uint16_t* attn_lo, hipStream_t stream) {
   tsp_status s;
   if ((s = check_plan(plan)) != TSP_OK) return s;
-  if ((s = check_dims(dims, plan->D, true, false)) != TSP_OK) return s;
+  if ((s = check_dims(dims, plan->D, true, false, 0)) != TSP_OK) return s;
   if ((s = check_ptr(q)) != TSP_OK || (s = check_ptr(k_full)) != TSP_OK || (s = check_ptr(v_full)) != TSP_OK ||
-      (s = check_ptr(attn_out)) != TSP_OK)
+      (s = check_ptr(attn_out)) != TSP_OK || (s = check_ptr_nullable(attn_lo)) != TSP_OK)
     return s;
-  if (attn_out == q) return TSP_ERR_INVALID_ARG;
-  return run_core(plan, dims, q, k_full, v_full, attn_out, stream);
+  if (attn_out == q || attn_lo == q || attn_lo == attn_out) return TSP_ERR_INVALID_ARG;
+  return run_core(plan, dims, q, k_full, v_full, attn_out, attn_lo, stream);
 }
 
 tsp_status tsp_attn_out(int64_t n_tokens, const tsp_dims* dims, int32_t D, int32_t start_shard,
-                        const uint16_t* attn, const uint16_t* const* wo, const uint16_t* residual, uint16_t* out,
-                        hipStream_t stream) {
+                        const uint16_t* attn, const uint16_t* attn_lo, const uint16_t* const* wo,
+                        const uint16_t* residual, uint16_t* out, hipStream_t stream) {
   tsp_status s;
   if ((s = check_dims(dims, D, true, false)) != TSP_OK) return s;
   if (n_tokens < 0) return TSP_ERR_SHAPE;
   if (n_tokens > INT32_MAX) return TSP_ERR_UNSUPPORTED;
   if (start_shard < 0 || start_shard >= D) return TSP_ERR_INVALID_ARG;
-  if ((s = check_ptr(attn)) != TSP_OK || (s = check_shards(wo, D)) != TSP_OK ||
-      (s = check_ptr_nullable(residual)) != TSP_OK || (s = check_ptr(out)) != TSP_OK)
+  if ((s = check_ptr(attn)) != TSP_OK || (s = check_ptr_nullable(attn_lo)) != TSP_OK ||
+      (s = check_shards(wo, D)) != TSP_OK || (s = check_ptr_nullable(residual)) != TSP_OK ||
+      (s = check_ptr(out)) != TSP_OK)
     return s;
-  if (out == attn) return TSP_ERR_INVALID_ARG;
-  return run_out(n_tokens, dims, D, start_shard, attn, wo, residual, out, stream);
+  if (out == attn || (attn_lo && out == attn_lo)) return TSP_ERR_INVALID_ARG;
+  return run_out(n_tokens, dims, D, start_shard, attn, attn_lo, wo, residual, out, false, stream);
 }
 
 tsp_status tsp_attn_forward(const tsp_plan* plan, const tsp_dims* dims, const uint16_t* x_local,
@@ -296,9 +393,10 @@ tsp_status tsp_attn_forward(const tsp_plan* plan, const tsp_dims* dims, const ui
   if (ws_bytes < ws_attn(plan->n_local, dims)) return TSP_ERR_WORKSPACE;
   uint16_t* qbuf = static_cast<uint16_t*>(workspace);
   uint16_t* abuf = qbuf + round_up((size_t)plan->n_local * dims->hidden * 2) / 2;
+  uint16_t* alo = abuf + round_up((size_t)plan->n_local * dims->hidden * 2) / 2;
   if ((s = run_project(plan, dims, x_local, wqkv, k_full, v_full, qbuf, stream)) != TSP_OK) return s;
-  if ((s = run_core(plan, dims, qbuf, k_full, v_full, abuf, stream)) != TSP_OK) return s;
-  return run_out(plan->n_local, dims, plan->D, plan->rank, abuf, wo, residual, out, stream);
+  if ((s = run_core(plan, dims, qbuf, k_full, v_full, abuf, alo, stream)) != TSP_OK) return s;
+  return run_out(plan->n_local, dims, plan->D, plan->rank, abuf, alo, wo, residual, out, false, stream);
 }
 
 tsp_status tsp_mlp_forward(int64_t n_tokens, const tsp_dims* dims, int32_t D, int32_t start_shard,
@@ -336,17 +434,34 @@ tsp_status tsp_layer_forward(const tsp_plan* plan, const tsp_dims* dims, const u
   if (!workspace) return TSP_ERR_WORKSPACE;
   if (!aligned16(workspace)) return TSP_ERR_ALIGNMENT;
   const int64_t n = plan->n_local;
-  const size_t h1_bytes = round_up((size_t)n * dims->hidden * 2);
-  const size_t a = ws_attn(n, dims), m = ws_mlp(n, dims);
-  if (ws_bytes < h1_bytes + (a > m ? a : m)) return TSP_ERR_WORKSPACE;
-  uint16_t* h1 = static_cast<uint16_t*>(workspace);
-  uint16_t* rest = h1 + h1_bytes / 2;
-  uint16_t* qbuf = rest;
+  if (ws_bytes < ws_layer(n, dims)) return TSP_ERR_WORKSPACE;
+  uint16_t* qbuf = static_cast<uint16_t*>(workspace);
   uint16_t* abuf = qbuf + round_up((size_t)n * dims->hidden * 2) / 2;
+  uint16_t* alo = abuf + round_up((size_t)n * dims->hidden * 2) / 2;
+  char* post = static_cast<char*>(workspace) + ws_attn(n, dims);
   if ((s = run_project(plan, dims, x_local, wqkv, k_full, v_full, qbuf, stream)) != TSP_OK) return s;
-  if ((s = run_core(plan, dims, qbuf, k_full, v_full, abuf, stream)) != TSP_OK) return s;
-  if ((s = run_out(n, dims, plan->D, plan->rank, abuf, wo, x_local, h1, stream)) != TSP_OK) return s;
-  return run_mlp(n, dims, plan->D, plan->rank, h1, w1, w2, h1, out, rest, stream);
+  if ((s = run_core(plan, dims, qbuf, k_full, v_full, abuf, alo, stream)) != TSP_OK) return s;
+  return run_post(n, dims, plan->D, plan->rank, abuf, alo, x_local, wo, w1, w2, out, post, stream);
+}
+
+tsp_status tsp_layer_post(int64_t n_tokens, const tsp_dims* dims, int32_t D, int32_t start_shard,
+                          const uint16_t* attn, const uint16_t* attn_lo, const uint16_t* x,
+                          const uint16_t* const* wo, const uint16_t* const* w1, const uint16_t* const* w2,
+                          uint16_t* out, void* workspace, size_t ws_bytes, hipStream_t stream) {
+  tsp_status s;
+  if ((s = check_dims(dims, D, true, true)) != TSP_OK) return s;
+  if (n_tokens < 0) return TSP_ERR_SHAPE;
+  if (n_tokens > INT32_MAX) return TSP_ERR_UNSUPPORTED;
+  if (start_shard < 0 || start_shard >= D) return TSP_ERR_INVALID_ARG;
+  if ((s = check_ptr(attn)) != TSP_OK || (s = check_ptr_nullable(attn_lo)) != TSP_OK ||
+      (s = check_ptr(x)) != TSP_OK || (s = check_shards(wo, D)) != TSP_OK ||
+      (s = check_shards(w1, D)) != TSP_OK || (s = check_shards(w2, D)) != TSP_OK || (s = check_ptr(out)) != TSP_OK)
+    return s;
+  if (out == x || out == attn || (attn_lo && out == attn_lo)) return TSP_ERR_INVALID_ARG;
+  if (!workspace) return TSP_ERR_WORKSPACE;
+  if (!aligned16(workspace)) return TSP_ERR_ALIGNMENT;
+  if (ws_bytes < post_ws(n_tokens, dims).total) return TSP_ERR_WORKSPACE;
+  return run_post(n_tokens, dims, D, start_shard, attn, attn_lo, x, wo, w1, w2, out, workspace, stream);
 }
 
 const char* tsp_status_string(tsp_status status) {

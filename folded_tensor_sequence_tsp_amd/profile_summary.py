@@ -1,0 +1,155 @@
+"""Short text summaries of rocprofv3 runs of the benchmark, for ``profiles/``.
+
+Reads the CSV output of three rocprofv3 runs of the same ``bench.py`` command:
+
+* ``--kernel-trace --stats`` (``*_kernel_stats.csv``): calls and average
+  duration per kernel;
+* ``--pmc FETCH_SIZE`` and ``--pmc WRITE_SIZE`` (``*_counter_collection.csv``):
+  KiB per dispatch.
+
+The counter runs also hold a plain device copy of known size (``bench.py
+--copy-probe-mib``); the ratio of its true bytes to what each counter reads for
+it is the calibration factor applied to the other kernels' counts (on gfx950
+FETCH_SIZE reads about half of the bytes a copy moves, WRITE_SIZE all of them).
+
+The summary ends with machine-readable lines that ``bench.py`` reads:
+``traffic_bytes_per_launch`` of the chosen kernel and ``source_sha256`` of the
+sources it was built from, so that the traffic figure is dropped (null) as soon
+as the kernel's sources change.
+
+    python -m folded_tensor_sequence_tsp_amd.profile_summary --trace DIR --fetch DIR --write DIR \\
+        --kernel attn_kernel --copy-mib 1024 --command "..." --out profiles/NAME.md
+"""
+from __future__ import annotations
+
+import argparse
+import csv
+import glob
+import hashlib
+import os
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+CSRC = os.path.join(PKG, "csrc")
+
+# Sources each summarised kernel is built from (hashed into the summary).
+KERNEL_SOURCES = {
+    "attn_kernel": ["attention.hip", "device_common.h", "kernels.h"],
+    "gemm_kernel": ["gemm.hip", "device_common.h", "kernels.h"],
+}
+
+
+def source_sha256(kernel: str) -> str:
+    h = hashlib.sha256()
+    for name in KERNEL_SOURCES[kernel]:
+        with open(os.path.join(CSRC, name), "rb") as f:
+            h.update(name.encode() + b"\0" + f.read())
+    return h.hexdigest()
+
+
+def _one(pattern: str) -> str:
+    found = sorted(glob.glob(pattern))
+    if not found:
+        raise FileNotFoundError(pattern)
+    return found[0]
+
+
+def _short(name: str) -> str:
+    name = name.replace("void ", "").replace("tsp::(anonymous namespace)::", "")
+    return name.split("(")[0] if "tsp::" in name or "gemm_kernel" in name or "attn_kernel" in name else name[:60]
+
+
+def kernel_stats(trace_dir: str):
+    rows = list(csv.DictReader(open(_one(os.path.join(trace_dir, "*kernel_stats.csv")))))
+    return [(_short(r["Name"]), int(r["Calls"]), float(r["AverageNs"]) / 1e6, float(r["Percentage"])) for r in rows]
+
+
+def counters(pmc_dir: str):
+    """{dispatch id: (kernel name, counter value KiB)}"""
+    rows = list(csv.DictReader(open(_one(os.path.join(pmc_dir, "*counter_collection.csv")))))
+    return {int(r["Dispatch_Id"]): (r["Kernel_Name"], float(r["Counter_Value"])) for r in rows}
+
+
+def _copy_factor(cnt, copy_bytes: int) -> tuple:
+    vals = [v for n, v in cnt.values() if "copyBuffer" in n]
+    if len(vals) != 1:
+        raise RuntimeError(f"expected one copy probe dispatch, found {len(vals)}")
+    return copy_bytes / (vals[0] * 1024.0), vals[0]
+
+
+def summarise(trace, fetch, write, kernel, copy_mib, command, workload):
+    stats = kernel_stats(trace)
+    f, w = counters(fetch), counters(write)
+    copy_bytes = copy_mib << 20
+    ff, f_copy = _copy_factor(f, copy_bytes)
+    wf, w_copy = _copy_factor(w, copy_bytes)
+    fk = [v for n, v in f.values() if kernel in n]
+    wk = [v for n, v in w.values() if kernel in n]
+    fetch_b = sum(fk) / len(fk) * 1024.0 * ff
+    write_b = sum(wk) / len(wk) * 1024.0 * wf
+    lines = [f"# rocprofv3 summary: {kernel}, {workload}", "",
+             "Commands (run from the repository root on the GPU; `-d`/`-o` name the output folders):", "",
+             "```", *command.split(" ;; "), "```", "",
+             "## Kernel time (--kernel-trace --stats)", "",
+             "| kernel | calls | avg ms | % of GPU time |", "|---|---|---|---|"]
+    lines += [f"| {n} | {c} | {ms:.4f} | {p:.2f} |" for n, c, ms, p in stats if "at::native" not in n]
+    lines += ["", "## HBM traffic (--pmc FETCH_SIZE, --pmc WRITE_SIZE; KiB per dispatch)", "",
+              f"Calibration: a plain {copy_mib} MiB device copy reads FETCH_SIZE = {f_copy:.0f} KiB and "
+              f"WRITE_SIZE = {w_copy:.0f} KiB, so fetch counts are scaled by {ff:.4f} and write counts by {wf:.4f}.",
+              "", "| kernel | FETCH_SIZE KiB | WRITE_SIZE KiB | fetched bytes (scaled) | written bytes (scaled) |",
+              "|---|---|---|---|---|"]
+    seen = set()
+    for d in sorted(f):
+        n, v = f[d]
+        if "tsp::" not in n or d not in w:
+            continue
+        key = _short(n)
+        if key in seen:
+            continue
+        seen.add(key)
+        lines.append(f"| {key} | {v:.0f} | {w[d][1]:.0f} | {v * 1024 * ff:.4e} | {w[d][1] * 1024 * wf:.4e} |")
+    lines += ["", "## Machine-readable (read by bench.py)", "",
+              f"kernel: {kernel}",
+              f"traffic_bytes_per_launch: {fetch_b + write_b:.0f}",
+              f"fetch_bytes_per_launch: {fetch_b:.0f}",
+              f"write_bytes_per_launch: {write_b:.0f}",
+              f"source_sha256: {source_sha256(kernel)}", ""]
+    return "\n".join(lines)
+
+
+def read_traffic(path: str, kernel: str):
+    """traffic_bytes_per_launch from a summary, or None when it is missing or
+    was taken from other sources of the kernel than the current ones."""
+    if not os.path.exists(path):
+        return None
+    vals = {}
+    for line in open(path):
+        if ":" in line and not line.startswith(("#", "|", " ")):
+            k, v = line.split(":", 1)
+            vals[k.strip()] = v.strip()
+    if vals.get("kernel") != kernel or vals.get("source_sha256") != source_sha256(kernel):
+        return None
+    try:
+        return float(vals["traffic_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--trace", required=True)
+    ap.add_argument("--fetch", required=True)
+    ap.add_argument("--write", required=True)
+    ap.add_argument("--kernel", default="attn_kernel", choices=sorted(KERNEL_SOURCES))
+    ap.add_argument("--copy-mib", type=int, default=1024)
+    ap.add_argument("--command", required=True, help="the profiling commands, separated by ' ;; '")
+    ap.add_argument("--workload", required=True)
+    ap.add_argument("--out", required=True)
+    a = ap.parse_args()
+    text = summarise(a.trace, a.fetch, a.write, a.kernel, a.copy_mib, a.command, a.workload)
+    with open(a.out, "w") as fh:
+        fh.write(text)
+    print(text)
+
+
+if __name__ == "__main__":
+    main()

@@ -18,11 +18,11 @@ import torch
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libtsp.so")
 
 TSP_OK, TSP_ERR_INVALID_ARG, TSP_ERR_SHAPE, TSP_ERR_ALIGNMENT, TSP_ERR_WORKSPACE, TSP_ERR_UNSUPPORTED, TSP_ERR_HIP = range(7)
-WS_ATTN, WS_MLP, WS_LAYER = 0, 1, 2
+WS_ATTN, WS_MLP, WS_LAYER, WS_POST = 0, 1, 2, 3
 MAX_D = 16
 
 EXPORTS = ["tsp_zigzag_plan", "tsp_workspace_size", "tsp_attn_project", "tsp_attn_core", "tsp_attn_out",
-           "tsp_attn_forward", "tsp_mlp_forward", "tsp_layer_forward", "tsp_status_string"]
+           "tsp_attn_forward", "tsp_mlp_forward", "tsp_layer_post", "tsp_layer_forward", "tsp_status_string"]
 
 
 class TSPError(RuntimeError):
@@ -55,10 +55,11 @@ def lib() -> ctypes.CDLL:
             "tsp_zigzag_plan": [c_int64, c_int32, c_int32, POINTER(Plan), P, P],
             "tsp_workspace_size": [c_int64, POINTER(Dims), c_int32, c_int32],
             "tsp_attn_project": [POINTER(Plan), POINTER(Dims), P, PP, P, P, P, P],
-            "tsp_attn_core": [POINTER(Plan), POINTER(Dims), P, P, P, P, P],
-            "tsp_attn_out": [c_int64, POINTER(Dims), c_int32, c_int32, P, PP, P, P, P],
+            "tsp_attn_core": [POINTER(Plan), POINTER(Dims), P, P, P, P, P, P],
+            "tsp_attn_out": [c_int64, POINTER(Dims), c_int32, c_int32, P, P, PP, P, P, P],
             "tsp_attn_forward": [POINTER(Plan), POINTER(Dims), P, PP, PP, P, P, P, P, P, c_size_t, P],
             "tsp_mlp_forward": [c_int64, POINTER(Dims), c_int32, c_int32, P, PP, PP, P, P, P, c_size_t, P],
+            "tsp_layer_post": [c_int64, POINTER(Dims), c_int32, c_int32, P, P, P, PP, PP, PP, P, P, c_size_t, P],
             "tsp_layer_forward": [POINTER(Plan), POINTER(Dims), P, PP, PP, PP, PP, P, P, P, P, c_size_t, P],
             "tsp_status_string": [c_int32],
         }
@@ -155,17 +156,18 @@ def attn_project(plan: Plan, dims: Dims, x_local, wqkv, k_full, v_full, q_out, s
            "tsp_attn_project")
 
 
-def attn_core(plan: Plan, dims: Dims, q, k_full, v_full, attn_out, stream=None):
+def attn_core(plan: Plan, dims: Dims, q, k_full, v_full, attn_out, attn_lo=None, stream=None):
     n, h, S = plan.n_local, dims.hidden, plan.seq_len
     args = (_dev_tensor(q, (n, h), "q"), _dev_tensor(k_full, (S, h), "k_full"), _dev_tensor(v_full, (S, h), "v_full"),
-            _dev_tensor(attn_out, (n, h), "attn_out"))
+            _dev_tensor(attn_out, (n, h), "attn_out"), _opt_tensor(attn_lo, (n, h), "attn_lo"))
     _check(lib().tsp_attn_core(ctypes.byref(plan), ctypes.byref(dims), *args, _stream(stream)), "tsp_attn_core")
 
 
-def attn_out(dims: Dims, D: int, start_shard: int, attn, wo, residual, out, stream=None):
+def attn_out(dims: Dims, D: int, start_shard: int, attn, wo, residual, out, attn_lo=None, stream=None):
     n, h = attn.shape[0], dims.hidden
     Hs = dims.n_heads // D if D > 0 else 0
-    args = (_dev_tensor(attn, (n, h), "attn"), _shards(wo, D, (h, Hs * dims.head_dim), "wo"),
+    args = (_dev_tensor(attn, (n, h), "attn"), _opt_tensor(attn_lo, (n, h), "attn_lo"),
+            _shards(wo, D, (h, Hs * dims.head_dim), "wo"),
             _opt_tensor(residual, (n, h), "residual"), _dev_tensor(out, (n, h), "out"))
     _check(lib().tsp_attn_out(n, ctypes.byref(dims), D, start_shard, *args, _stream(stream)), "tsp_attn_out")
 
@@ -192,6 +194,20 @@ def mlp_forward(dims: Dims, D: int, start_shard: int, x, w1, w2, residual, y, wo
             _opt_tensor(residual, (n, h), "residual"), _dev_tensor(y, (n, h), "y"))
     _check(lib().tsp_mlp_forward(n, ctypes.byref(dims), D, start_shard, *args, ws, nbytes, _stream(stream)),
            "tsp_mlp_forward")
+
+
+def layer_post(dims: Dims, D: int, start_shard: int, attn, x, wo, w1, w2, out, workspace, attn_lo=None,
+               stream=None):
+    n, h = attn.shape[0], dims.hidden
+    Hs = dims.n_heads // D if D > 0 else 0
+    Fs = dims.ffn // D if D > 0 else 0
+    need = workspace_size(n, dims, D, WS_POST)
+    ws, nbytes = _workspace(workspace, need)
+    args = (_dev_tensor(attn, (n, h), "attn"), _opt_tensor(attn_lo, (n, h), "attn_lo"), _dev_tensor(x, (n, h), "x"),
+            _shards(wo, D, (h, Hs * dims.head_dim), "wo"), _shards(w1, D, (Fs, h), "w1"),
+            _shards(w2, D, (h, Fs), "w2"), _dev_tensor(out, (n, h), "out"))
+    _check(lib().tsp_layer_post(n, ctypes.byref(dims), D, start_shard, *args, ws, nbytes, _stream(stream)),
+           "tsp_layer_post")
 
 
 def layer_forward(plan: Plan, dims: Dims, x_local, wqkv, wo, w1, w2, k_full, v_full, out, workspace, stream=None):

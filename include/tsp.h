@@ -78,7 +78,7 @@ typedef struct {
 } tsp_dims;
 
 /* Workspace kinds for tsp_workspace_size(). */
-typedef enum { TSP_WS_ATTN = 0, TSP_WS_MLP = 1, TSP_WS_LAYER = 2 } tsp_ws_kind;
+typedef enum { TSP_WS_ATTN = 0, TSP_WS_MLP = 1, TSP_WS_LAYER = 2, TSP_WS_POST = 3 } tsp_ws_kind;
 
 /*
  * Zigzag plan (zubnet.ai TSP page, para. 2: K/V are gathered over a zigzag
@@ -99,8 +99,9 @@ tsp_status tsp_zigzag_plan(int64_t seq_len, int32_t D, int32_t rank, tsp_plan* p
 
 /*
  * Bytes of workspace that tsp_attn_forward (TSP_WS_ATTN), tsp_mlp_forward
- * (TSP_WS_MLP) or tsp_layer_forward (TSP_WS_LAYER) need for n_tokens local
- * tokens.  Returns 0 for invalid dims or kind.
+ * (TSP_WS_MLP), tsp_layer_forward (TSP_WS_LAYER) or tsp_layer_post
+ * (TSP_WS_POST) need for n_tokens local tokens.  Returns 0 for invalid dims or
+ * kind.  Workspace contents are scratch: nothing persists between calls.
  */
 size_t tsp_workspace_size(int64_t n_tokens, const tsp_dims* dims, int32_t D, int32_t kind);
 
@@ -130,13 +131,19 @@ tsp_status tsp_attn_project(const tsp_plan* plan, const tsp_dims* dims, const ui
  * gathered K/V (para. 2).  Per head a and local row t at global position p:
  *   attn[t, a] = sum_{j <= p} softmax_j(q[t, a] . k_full[j, a] / sqrt(head_dim)) v_full[j, a]
  * (the diagonal is included).  fp32 online softmax, bf16 MFMA products.
+ *   dims   : hidden = n_heads * head_dim, head_dim in {64, 128}, hidden % 64 == 0
+ *            (the heads need not divide over D: no weight shard is read here).
  *   q      : device, bf16 [n_local x hidden] (as tsp_attn_project writes it).
  *   k_full, v_full : device, bf16 [seq_len x hidden], read only.
  *   attn_out : device, bf16 [n_local x hidden], out; must not alias q.
+ *   attn_lo  : device, bf16 [n_local x hidden], out, nullable: the rounding
+ *              residual bf16(attn - attn_out), so that attn_out + attn_lo carries
+ *              the fp32 result to about 16 significant bits (tsp_attn_out and
+ *              tsp_layer_post contract both parts).
  */
 tsp_status tsp_attn_core(const tsp_plan* plan, const tsp_dims* dims, const uint16_t* q,
                          const uint16_t* k_full, const uint16_t* v_full, uint16_t* attn_out,
-                         hipStream_t stream);
+                         uint16_t* attn_lo, hipStream_t stream);
 
 /*
  * O projection as a split-K over the D head shards (the attention projections
@@ -146,17 +153,20 @@ tsp_status tsp_attn_core(const tsp_plan* plan, const tsp_dims* dims, const uint1
  *   out = [residual +] sum_k attn[:, heads of d_k] W_o_{d_k}^T
  *   n_tokens  : rows of attn / out (>= 0; 0 enqueues nothing).
  *   attn      : device, bf16 [n_tokens x hidden].
+ *   attn_lo   : device, bf16 [n_tokens x hidden], nullable: low part of the
+ *               attention output (tsp_attn_core); when given, the product is
+ *               (attn + attn_lo) W_o^T.
  *   wo        : host array of D device pointers, each bf16 [hidden x H_s * head_dim].
  *   residual  : device, bf16 [n_tokens x hidden], nullable (then no residual).
  *   out       : device, bf16 [n_tokens x hidden]; may alias residual, not attn.
  */
 tsp_status tsp_attn_out(int64_t n_tokens, const tsp_dims* dims, int32_t D, int32_t start_shard,
-                        const uint16_t* attn, const uint16_t* const* wo, const uint16_t* residual,
-                        uint16_t* out, hipStream_t stream);
+                        const uint16_t* attn, const uint16_t* attn_lo, const uint16_t* const* wo,
+                        const uint16_t* residual, uint16_t* out, hipStream_t stream);
 
 /*
- * Attention half of the layer: tsp_attn_project, tsp_attn_core, then
- * tsp_attn_out with start_shard = plan->rank.
+ * Attention half of the layer: tsp_attn_project, tsp_attn_core (with the low
+ * part of its output), then tsp_attn_out with start_shard = plan->rank.
  *   residual  : nullable; the layer passes x_local.
  *   out       : device, bf16 [n_local x hidden]; must not alias x_local.
  *   workspace : device, >= tsp_workspace_size(n_local, dims, D, TSP_WS_ATTN) bytes.
@@ -171,6 +181,11 @@ tsp_status tsp_attn_forward(const tsp_plan* plan, const tsp_dims* dims, const ui
  * over the FFN dimension with one fp32 accumulator, in place of the
  * all-reduce of tensor parallelism:
  *   y = [residual +] sum_{k=0}^{D-1} GELU_tanh(x W1_{d_k}^T) W2_{d_k}^T,  d_k = (start_shard + k) mod D
+ * Precision: x W1^T runs on bf16 operands; the GELU output is held in fp16,
+ * each token row scaled by a power of two from the RMS of its x row (exact,
+ * undone before the residual), and W2 meets it as an fp16 copy of its shards
+ * (bf16 weights are exact in fp16 above 2^-14; smaller ones keep an absolute
+ * error below 2^-25; magnitudes beyond 65504 saturate).
  *   n_tokens : rows (>= 0).
  *   dims     : ffn % D == 0, ffn / D % 64 == 0, hidden % 64 == 0.
  *   x        : device, bf16 [n_tokens x hidden].
@@ -186,9 +201,29 @@ tsp_status tsp_mlp_forward(int64_t n_tokens, const tsp_dims* dims, int32_t D, in
                            hipStream_t stream);
 
 /*
- * One decoder layer for the rank's local tokens:
- *   h1 = x + Attn(x) (tsp_attn_forward), out = h1 + MLP(h1) (tsp_mlp_forward with
- *   start_shard = plan->rank).  No norm, no bias.
+ * Post-attention half of the layer for n_tokens rows:
+ *   h1  = x + attn W_o^T   (split-K over head shards in ring order from start_shard, fp32 result)
+ *   out = h1 + sum_k GELU_tanh(h1 W1_{d_k}^T) W2_{d_k}^T   (ring from start_shard)
+ * h1 stays in fp32 for the residual; both MLP GEMMs run on fp16 operands (h1
+ * and the GELU output scaled per row by a power of two from the RMS of the h1
+ * row, W1 and W2 as fp16 copies of the bf16 shards; see tsp_mlp_forward).
+ *   dims      : as for tsp_layer_forward.
+ *   attn      : device, bf16 [n_tokens x hidden] (tsp_attn_core output).
+ *   attn_lo   : device, bf16, nullable: its low part (see tsp_attn_core).
+ *   x         : device, bf16 [n_tokens x hidden] (the layer input, first residual).
+ *   wo, w1, w2: host arrays of D device pointers (layouts as above).
+ *   out       : device, bf16 [n_tokens x hidden]; must not alias x, attn or attn_lo.
+ *   workspace : >= tsp_workspace_size(n_tokens, dims, D, TSP_WS_POST) bytes.
+ */
+tsp_status tsp_layer_post(int64_t n_tokens, const tsp_dims* dims, int32_t D, int32_t start_shard,
+                          const uint16_t* attn, const uint16_t* attn_lo, const uint16_t* x,
+                          const uint16_t* const* wo, const uint16_t* const* w1, const uint16_t* const* w2,
+                          uint16_t* out, void* workspace, size_t ws_bytes, hipStream_t stream);
+
+/*
+ * One decoder layer for the rank's local tokens: tsp_attn_project, then
+ * tsp_attn_core, then tsp_layer_post with start_shard = plan->rank, i.e.
+ *   h1 = x + Attn(x), out = h1 + MLP(h1).  No norm, no bias.
  *   out       : device, bf16 [n_local x hidden]; must not alias x_local.
  *   workspace : >= tsp_workspace_size(n_local, dims, D, TSP_WS_LAYER) bytes.
  */

@@ -135,29 +135,32 @@ def test_tampered_plan_rejected(L):
 
 def test_core_rejects(L):
     p, d = _plan(), _dims()
-    assert L.tsp_attn_core(None, ctypes.byref(d), A, A, A, A + 64, None) == tsp.TSP_ERR_INVALID_ARG
-    assert L.tsp_attn_core(ctypes.byref(p), ctypes.byref(d), A, A, A, A, None) == tsp.TSP_ERR_INVALID_ARG  # alias
-    assert L.tsp_attn_core(ctypes.byref(p), ctypes.byref(d), A, A, MIS, A + 64, None) == tsp.TSP_ERR_ALIGNMENT
-    assert L.tsp_attn_core(ctypes.byref(p), None, A, A, A, A + 64, None) == tsp.TSP_ERR_INVALID_ARG
+    assert L.tsp_attn_core(None, ctypes.byref(d), A, A, A, A + 64, None, None) == tsp.TSP_ERR_INVALID_ARG
+    assert L.tsp_attn_core(ctypes.byref(p), ctypes.byref(d), A, A, A, A, None, None) == tsp.TSP_ERR_INVALID_ARG  # alias
+    assert L.tsp_attn_core(ctypes.byref(p), ctypes.byref(d), A, A, MIS, A + 64, None, None) == tsp.TSP_ERR_ALIGNMENT
+    assert L.tsp_attn_core(ctypes.byref(p), None, A, A, A, A + 64, None, None) == tsp.TSP_ERR_INVALID_ARG
+    assert L.tsp_attn_core(ctypes.byref(p), ctypes.byref(d), A, A, A, A + 64, A + 64, None) == tsp.TSP_ERR_INVALID_ARG
+    assert L.tsp_attn_core(ctypes.byref(p), ctypes.byref(d), A, A, A, A + 64, MIS, None) == tsp.TSP_ERR_ALIGNMENT
 
 
 def test_out_rejects(L):
     d = _dims()
     w = _arr([A] * 4)
-    assert L.tsp_attn_out(512, ctypes.byref(d), 4, 4, A, w, None, A + 64, None) == tsp.TSP_ERR_INVALID_ARG
-    assert L.tsp_attn_out(512, ctypes.byref(d), 4, -1, A, w, None, A + 64, None) == tsp.TSP_ERR_INVALID_ARG
-    assert L.tsp_attn_out(-1, ctypes.byref(d), 4, 0, A, w, None, A + 64, None) == tsp.TSP_ERR_SHAPE
-    assert L.tsp_attn_out(512, ctypes.byref(d), 4, 0, A, w, MIS, A + 64, None) == tsp.TSP_ERR_ALIGNMENT
-    assert L.tsp_attn_out(512, ctypes.byref(d), 4, 0, A, w, None, A, None) == tsp.TSP_ERR_INVALID_ARG
-    assert L.tsp_attn_out(512, ctypes.byref(d), 4, 0, A, None, None, A + 64, None) == tsp.TSP_ERR_INVALID_ARG
-    assert L.tsp_attn_out(512, ctypes.byref(d), 0, 0, A, w, None, A + 64, None) == tsp.TSP_ERR_INVALID_ARG
+    assert L.tsp_attn_out(512, ctypes.byref(d), 4, 4, A, None, w, None, A + 64, None) == tsp.TSP_ERR_INVALID_ARG
+    assert L.tsp_attn_out(512, ctypes.byref(d), 4, -1, A, None, w, None, A + 64, None) == tsp.TSP_ERR_INVALID_ARG
+    assert L.tsp_attn_out(-1, ctypes.byref(d), 4, 0, A, None, w, None, A + 64, None) == tsp.TSP_ERR_SHAPE
+    assert L.tsp_attn_out(512, ctypes.byref(d), 4, 0, A, None, w, MIS, A + 64, None) == tsp.TSP_ERR_ALIGNMENT
+    assert L.tsp_attn_out(512, ctypes.byref(d), 4, 0, A, None, w, None, A, None) == tsp.TSP_ERR_INVALID_ARG
+    assert L.tsp_attn_out(512, ctypes.byref(d), 4, 0, A, None, None, None, A + 64, None) == tsp.TSP_ERR_INVALID_ARG
+    assert L.tsp_attn_out(512, ctypes.byref(d), 0, 0, A, None, w, None, A + 64, None) == tsp.TSP_ERR_INVALID_ARG
 
 
 def test_mlp_rejects(L):
     d = _dims()
     w = _arr([A] * 4)
     ws = tsp.workspace_size(512, d, 4, tsp.WS_MLP)
-    assert ws == 512 * 1024 * 2
+    # fp16 GELU block + fp16 copy of the W2 shards + int32 row exponents (256-byte aligned parts)
+    assert ws == 512 * 1024 * 2 + 256 * 1024 * 2 + 512 * 4
     call = lambda **k: L.tsp_mlp_forward(k.get("n", 512), ctypes.byref(k.get("dims", d)), k.get("D", 4),
                                          k.get("start", 0), k.get("x", A), k.get("w1", w), k.get("w2", w),
                                          k.get("res", None), k.get("y", A + 64), k.get("ws", A + 128),
@@ -189,6 +192,29 @@ def test_layer_and_forward_reject(L):
                               None) == tsp.TSP_ERR_ALIGNMENT
 
 
+def test_layer_post_rejects(L):
+    d = _dims()
+    w = _arr([A] * 4)
+    need = tsp.workspace_size(512, d, 4, tsp.WS_POST)
+    assert need > 0
+    call = lambda **k: L.tsp_layer_post(k.get("n", 512), ctypes.byref(k.get("dims", d)), k.get("D", 4),
+                                        k.get("start", 0), k.get("attn", A), k.get("lo", None), k.get("x", A + 64),
+                                        k.get("wo", w), k.get("w1", w), k.get("w2", w), k.get("out", A + 128),
+                                        k.get("ws", A + 192), k.get("nb", need), None)
+    assert call(nb=need - 1) == tsp.TSP_ERR_WORKSPACE
+    assert call(ws=None) == tsp.TSP_ERR_WORKSPACE
+    assert call(ws=MIS) == tsp.TSP_ERR_ALIGNMENT
+    assert call(out=A + 64) == tsp.TSP_ERR_INVALID_ARG             # out aliases x
+    assert call(out=A) == tsp.TSP_ERR_INVALID_ARG                  # out aliases attn
+    assert call(lo=A + 128) == tsp.TSP_ERR_INVALID_ARG             # out aliases attn_lo
+    assert call(lo=MIS) == tsp.TSP_ERR_ALIGNMENT
+    assert call(start=-1) == tsp.TSP_ERR_INVALID_ARG
+    assert call(w1=_arr([A, 0, A, A])) == tsp.TSP_ERR_INVALID_ARG
+    assert call(x=MIS) == tsp.TSP_ERR_ALIGNMENT
+    assert call(dims=_dims(ffn=1002)) == tsp.TSP_ERR_SHAPE
+    assert call(n=-1) == tsp.TSP_ERR_SHAPE
+
+
 def test_workspace_sizes(L):
     d = _dims()
     n = 512
@@ -196,8 +222,12 @@ def test_workspace_sizes(L):
     mlp = tsp.workspace_size(n, d, 4, tsp.WS_MLP)
     layer = tsp.workspace_size(n, d, 4, tsp.WS_LAYER)
     assert attn >= 2 * n * 256 * 2
-    assert mlp >= n * 1024 * 2
-    assert layer >= n * 256 * 2 + max(attn, mlp)
+    assert mlp >= n * 1024 * 2 + 256 * 1024 * 2 + n * 4
+    post = tsp.workspace_size(n, d, 4, tsp.WS_POST)
+    # post: fp32 h1, fp16 h1, row exponents, fp16 W1 and W2, fp16 GELU block
+    assert post == n * 256 * 4 + n * 256 * 2 + n * 4 + 2 * 1024 * 256 * 2 + n * 1024 * 2
+    assert attn == 3 * n * 256 * 2  # Q and the attention output as a (hi, lo) bf16 pair
+    assert layer == attn + post
     assert tsp.workspace_size(n, d, 4, 7) == 0
     assert tsp.workspace_size(n, _dims(hidden=300), 4, tsp.WS_LAYER) == 0
     assert tsp.workspace_size(-1, d, 4, tsp.WS_ATTN) == 0

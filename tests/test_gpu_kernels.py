@@ -269,3 +269,92 @@ def test_determinism():
     torch.cuda.synchronize()
     for t1, t2 in zip(*res):
         assert torch.equal(t1, t2)
+
+
+# (h, H, hd, F, D, n)
+POST_CASES = [(256, 4, 64, 1024, 4, 512), (512, 4, 128, 2048, 2, 300), (384, 6, 64, 768, 2, 65)]
+
+
+@pytest.mark.parametrize("h,H,hd,F,D,n", POST_CASES)
+def test_layer_post(h, H, hd, F, D, n):
+    """O projection + residual + ring MLP + residual (the part of the layer after
+    the attention core) against the oracle's h1 = x + a W_o^T, out = h1 + MLP(h1),
+    for every ring start."""
+    require_gpu()
+    _, wo, w1, w2 = _weights(h, H, hd, F, D, 120)
+    a = _rnd((n, h), 9) * 0.3
+    x = _rnd((n, h), 10)
+    W = O.assemble(wo=wo)
+    h1 = O.f64(x) + O.linear(O.f64(a), W.wo)
+    ref = O.mlp_forward(h1, w1, w2, residual=True)
+    dims = tsp.make_dims(h, H, hd, F)
+    ws = tsp.alloc_workspace(n, dims, D, tsp.WS_POST)
+    for start in range(D):
+        say(f"layer_post h={h} hd={hd} F={F} D={D} n={n} start={start}")
+        out = bf16_nan((n, h), DEV)
+        tsp.layer_post(dims, D, start, a.to(DEV), x.to(DEV), _dev(wo), _dev(w1), _dev(w2), out, ws)
+        torch.cuda.synchronize()
+        check(out, ref, f"layer_post start={start}")
+
+
+def test_mlp_row_scaling_wide_range():
+    """Rows whose magnitudes span 2^-20 .. 2^20 (the fp16 operands are scaled per
+    row by a power of two, so every row keeps its relative precision)."""
+    require_gpu()
+    h, F, D, n = 256, 1024, 4, 96
+    _, _, w1, w2 = _weights(h, 4, 64, F, D, 130)
+    x = _rnd((n, h), 11).float()
+    x *= torch.pow(2.0, torch.linspace(-20, 20, n)).unsqueeze(1)
+    x = x.to(torch.bfloat16)
+    ref = O.mlp_forward(x, w1, w2, residual=False)
+    dims = tsp.make_dims(h, 4, 64, F)
+    ws = tsp.alloc_workspace(n, dims, D, tsp.WS_MLP)
+    y = bf16_nan((n, h), DEV)
+    say("mlp rows spanning 2^-20 .. 2^20")
+    tsp.mlp_forward(dims, D, 0, x.to(DEV), _dev(w1), _dev(w2), None, y, ws)
+    torch.cuda.synchronize()
+    g = y.cpu().double()
+    for i in range(n):  # per row: relative error against that row's own scale
+        rr = ((g[i] - ref[i]).norm() / ref[i].norm()).item()
+        assert rr <= 5e-3, f"row {i}: relative RMS {rr:.3e}"
+
+
+def test_attn_core_low_part():
+    """attn_lo is the rounding residual of attn_out (at most half a bf16 ulp of
+    it, i.e. |lo| <= 2^-8 |hi|) and the pair is closer to the oracle than the
+    bf16 output alone, on a case whose outputs are O(1) (early queries see few
+    keys)."""
+    require_gpu()
+    H, hd, D, S, r = 2, 128, 2, 512, 0
+    h = H * hd
+    plan, l2g, _ = tsp.zigzag_plan(S, D, r)
+    q, k, v = _attn_inputs(S, plan.n_local, h, 140)
+    hi, lo = bf16_nan((plan.n_local, h), DEV), bf16_nan((plan.n_local, h), DEV)
+    say("attn_core with low part")
+    tsp.attn_core(plan, tsp.make_dims(h, H, hd, 4 * h), q.to(DEV), k.to(DEV), v.to(DEV), hi, lo)
+    torch.cuda.synchronize()
+    ref = O.causal_attention(O.f64(q), l2g, O.f64(k), O.f64(v), H, hd)
+    check(hi, ref, "attention hi part")
+    hd_, ld_ = hi.cpu().double(), lo.cpu().double()
+    assert bool((ld_.abs() <= 2.0 ** -8 * hd_.abs()).all()), "low part larger than half an ulp of the high part"
+    rr_hi = ((hd_ - ref).norm() / ref.norm()).item()
+    rr_pair = ((hd_ + ld_ - ref).norm() / ref.norm()).item()
+    assert rr_pair < 0.8 * rr_hi, (rr_pair, rr_hi)
+
+
+@pytest.mark.parametrize("D", [1, 4])
+def test_attn_out_with_low_part(D):
+    require_gpu()
+    h, H, hd, n = 256, 4, 64, 333
+    _, wo, _, _ = _weights(h, H, hd, 4 * h, D, 150)
+    a32 = torch.randn(n, h, generator=torch.Generator().manual_seed(151), dtype=torch.float64)
+    hi = a32.to(torch.bfloat16)
+    lo = (a32 - hi.double()).to(torch.bfloat16)
+    x = _rnd((n, h), 12)
+    ref = O.linear(hi.double() + lo.double(), O.assemble(wo=wo).wo) + O.f64(x)
+    dims = tsp.make_dims(h, H, hd, 4 * h)
+    out = bf16_nan((n, h), DEV)
+    say(f"attn_out with low part D={D}")
+    tsp.attn_out(dims, D, D - 1, hi.to(DEV), _dev(wo), x.to(DEV), out, attn_lo=lo.to(DEV))
+    torch.cuda.synchronize()
+    check(out, ref, "attn_out hi + lo")
