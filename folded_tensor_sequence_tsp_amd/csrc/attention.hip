@@ -7,58 +7,129 @@
 // queries of chunk i sit at global positions chunk_start[i] + row; a query at
 // position p attends to keys 0..p of the full sequence.
 //
-// Design (one workgroup = one head x one tile of QT = 32 * NWAVES queries of
-// one chunk; each wave owns 32 queries):
+// Design (one workgroup = one head x QT = 256 queries of one chunk, 8 waves of
+// 32 queries, two waves per SIMD):
 //   * scores are computed transposed, S^T = K Q^T, with v_mfma_f32_32x32x16_bf16:
 //     each lane then holds ONE query (lane % 32) and 16 keys per 32-key block,
-//     so the row max needs a single exchange with lane ^ 32 and the row sums
-//     stay per lane until the end;
-//   * O^T = V^T P^T reuses the score registers directly as the B operand (no
-//     LDS round trip for P); V is staged in LDS transposed, [d][key], with the
-//     keys of each 16-key group permuted so every lane's 8 keys of a k-step are
-//     one 16-byte read;
-//   * online softmax in fp32 in the log2 domain (scale folded into one FMA,
-//     hardware exp2), masking only on the tiles that cross the diagonal, and
-//     whole tiles past a wave's last query skipped;
-//   * K/V tiles of 64 keys are double-buffered in LDS with a register prefetch
-//     of the next tile; one barrier per tile;
-//   * workgroups are ordered so each XCD works through a contiguous range of
-//     heads (its concurrent tiles stream the same K/V through its L2), heaviest
-//     (latest) query tiles first.
+//     so the row max needs a single exchange with lane ^ 32 and row sums stay
+//     per lane until the end;
+//   * O^T = V^T P^T takes the probabilities from the score registers as the B
+//     operand.  V is first rewritten per head as V^T tiles [64-key tile][d][64]
+//     with the keys of each 16-key group in the order the score registers hold
+//     them (vt_prep_kernel), so every lane's 8 keys of a k-step are one 16-byte
+//     LDS read;
+//   * K and V^T tiles of 64 keys stream into a 4-stage LDS ring with direct
+//     global->LDS loads (global_load_lds_dwordx4; no register staging), the 16-
+//     byte chunks of each row XOR-swizzled by the row index so that fragment
+//     reads of 32 rows are conflict-free; per tile one vmcnt wait and one
+//     barrier; loads run three tiles ahead;
+//   * software pipeline: the MFMAs of S for tile t+1 are issued in the same
+//     block as the softmax of tile t, so matrix and vector work overlap;
+//   * online softmax in fp32, log2 domain, scale folded into one FMA, hardware
+//     exp2, and lazy rescaling: the running max moves (and O, l are rescaled)
+//     only when a tile's max exceeds it by more than 2^8, so probabilities stay
+//     below 256 and most tiles skip the rescale;
+//   * masking only on tiles that cross a wave's diagonal; tiles past a wave's
+//     last query are not computed;
+//   * workgroups ordered so each XCD works through a contiguous range of heads,
+//     heaviest (latest) query tiles first.
 #include "device_common.h"
 #include "kernels.h"
 
 namespace tsp {
 namespace {
 
-constexpr int NWAVES = 4;
-constexpr int NTHREADS = 64 * NWAVES;
-constexpr int QT = 32 * NWAVES;  // queries per workgroup
-constexpr int BKV = 64;          // keys per tile
+constexpr int NW = 8;              // waves per workgroup
+constexpr int NTHREADS = 64 * NW;
+constexpr int QT = 32 * NW;        // queries per workgroup
+constexpr int BKV = 64;            // keys per tile
+constexpr int NSTAGE = 4;          // LDS ring depth
+constexpr float LAZY_TAU = 8.0f;   // rescale threshold (log2 units)
 
 template <int HD>
 struct ACfg {
-  static constexpr int KLD = HD + 8;          // K row in LDS (bf16), padded
-  static constexpr int VLD = BKV + 8;         // V^T row in LDS (bf16), padded
-  static constexpr int K_ELEMS = BKV * KLD;
-  static constexpr int V_ELEMS = HD * VLD;
-  static constexpr int BUF_ELEMS = K_ELEMS + V_ELEMS;
-  static constexpr int DCH = HD / 8;                    // 16-byte chunks per key row
-  static constexpr int K_CHUNKS = BKV * DCH / NTHREADS; // K loads per thread
-  static constexpr int V_BLOCKS = (BKV / 4) * DCH;      // 4 keys x 8 dims blocks
-  static constexpr int KK = HD / 16;                    // MFMA k-steps over head_dim
-  static constexpr int DT = HD / 32;                    // 32-wide d tiles of O
+  static constexpr int NCH = HD / 8;              // 16-byte chunks per K row
+  static constexpr int K_BYTES = BKV * HD * 2;    // K tile [64][HD]
+  static constexpr int V_BYTES = HD * BKV * 2;    // V^T tile [HD][64]
+  static constexpr int STAGE_BYTES = K_BYTES + V_BYTES;
+  static constexpr int K_LOADS = K_BYTES / (NTHREADS * 16);  // DMA instructions per thread per tile
+  static constexpr int V_LOADS = V_BYTES / (NTHREADS * 16);
+  static constexpr int LOADS = K_LOADS + V_LOADS;
+  static constexpr int K_ROWS_PER_LOAD = 64 / NCH;            // K rows one wave instruction fills
+  static constexpr int KK = HD / 16;                          // MFMA k-steps over head_dim
+  static constexpr int DT = HD / 32;                          // 32-wide d tiles of O
+  static_assert(K_LOADS >= 1 && V_LOADS >= 1, "tile too small for the workgroup");
 };
 
-// Physical slot of logical key w (0..15) inside a 16-key group of V^T: the
-// 4-key blocks are stored in the order 0, 2, 1, 3 so that lane half h finds
-// its keys {4h..4h+3, 8+4h..8+4h+3} at slots 8h..8h+7.
-__device__ __forceinline__ int vt_block_slot(int block4) { return ((block4 & 1) << 1) | (block4 >> 1); }
+// Position k (0..15) of a 16-key group of V^T holds key perm(k): bits 2 and 3
+// swapped.  A lane of half h holds in its score registers the keys
+// {4h..4h+3, 8+4h..8+4h+3} of each 16-key group, i.e. perm(8h + j), j = 0..7.
+__device__ __forceinline__ int key_perm16(int k) { return (k & 3) | ((k & 4) << 1) | ((k & 8) >> 1); }
+
+// s_waitcnt vmcnt(N) alone (expcnt and lgkmcnt left at their maxima).
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | 0x0F70);
+}
+
+// Direct global->LDS load of 16 bytes per lane (global_load_lds_dwordx4): lane L
+// of the wave writes its 16 bytes at lds_block + 16 * L; lds_block is wave-uniform.
+__device__ __forceinline__ void dma16(const void* src, void* lds_block) {
+  __builtin_amdgcn_global_load_lds(const_cast<void*>(src), (__attribute__((address_space(3))) void*)lds_block, 16,
+                                   0, 0);
+}
+
+// Workgroup barrier that the compiler may not move memory operations across.
+__device__ __forceinline__ void lds_barrier() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
+// V [S x ld] (head columns head*HD .. +HD-1) -> V^T tiles
+// vt[((head * n_kv_tiles + t) * HD + d) * 64 + k] = V[t*64 + key_perm16-order(k)][head*HD + d], 0 past S.
+// One thread moves 8 keys x 8 dims: eight 16-byte row reads, an 8x8 transpose
+// in registers, eight 16-byte writes (8 consecutive lanes write one 128-byte row).
+template <int HD>
+__global__ __launch_bounds__(128) void vt_prep_kernel(const uint16_t* __restrict__ v, int64_t S, int32_t ld,
+                                                      uint16_t* __restrict__ vt, int64_t n_kv_tiles) {
+  constexpr int NCH = HD / 8;
+  const int t = blockIdx.x;
+  const int head = blockIdx.y;
+  for (int item = threadIdx.x; item < 8 * NCH; item += 128) {
+    const int kg = item & 7;     // 8-slot group: slots 8*kg .. 8*kg+7 of the tile
+    const int dc = item >> 3;    // dims 8*dc .. 8*dc+7
+    uint32_t r[8][4];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const int slot = 8 * kg + j;
+      const int64_t key = (int64_t)t * 64 + (slot & ~15) + key_perm16(slot & 15);
+      if (key < S) {
+        const u32x4 x = *reinterpret_cast<const u32x4*>(v + key * ld + head * HD + dc * 8);
+        r[j][0] = x[0]; r[j][1] = x[1]; r[j][2] = x[2]; r[j][3] = x[3];
+      } else {
+        r[j][0] = r[j][1] = r[j][2] = r[j][3] = 0u;
+      }
+    }
+    uint16_t* dst = vt + (((int64_t)head * n_kv_tiles + t) * HD + dc * 8) * 64 + 8 * kg;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {  // dim dc*8 + i: keys j = 0..7
+      u32x4 w;
+#pragma unroll
+      for (int m = 0; m < 4; ++m) {
+        const uint32_t a0 = (i & 1) ? (r[2 * m][i >> 1] >> 16) : (r[2 * m][i >> 1] & 0xffffu);
+        const uint32_t a1 = (i & 1) ? (r[2 * m + 1][i >> 1] & 0xffff0000u) : (r[2 * m + 1][i >> 1] << 16);
+        w[m] = a0 | a1;
+      }
+      *reinterpret_cast<u32x4*>(dst + i * 64) = w;
+    }
+  }
+}
 
 template <int HD>
 __global__ __launch_bounds__(NTHREADS) void attn_kernel(const AttnArgs a) {
   using C = ACfg<HD>;
-  __shared__ __attribute__((aligned(16))) uint16_t lds[2 * C::BUF_ELEMS];
+  __shared__ __attribute__((aligned(1024))) uint8_t smem[NSTAGE * C::STAGE_BYTES];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -91,6 +162,7 @@ __global__ __launch_bounds__(NTHREADS) void attn_kernel(const AttnArgs a) {
   const bool wave_active = wave_first < valid;
   const int64_t wave_min_pos = pos0 + wave_first;
   const int64_t wave_max_pos = pos0 + min(wave_first + 31, valid - 1);
+  const int wave_tiles = wave_active ? (int)(wave_max_pos / BKV) + 1 : 0;  // tiles 0..wave_tiles-1 computed
 
   const int hcol = head * HD;
   const int64_t ld = a.hidden;
@@ -103,62 +175,62 @@ __global__ __launch_bounds__(NTHREADS) void attn_kernel(const AttnArgs a) {
     for (int kk = 0; kk < C::KK; ++kk) qf[kk] = as_bf16x8(*reinterpret_cast<const u32x4*>(qp + kk * 16));
   }
 
-  // ---- K/V tile loading.
-  // K: chunk c = i*NTHREADS + tid -> key c / DCH, dims (c % DCH) * 8.
-  // V: block tid -> keys 4*(tid % 16) .. +3, dims (tid / 16) * 8 .. +7 (16
-  // consecutive lanes fill one 128-byte row of V^T: conflict-free LDS writes).
-  u32x4 rk[C::K_CHUNKS];
-  u32x4 rv[4];
-  const bool v_loader = tid < C::V_BLOCKS;
-  const int v_kg = tid & 15;
-  const int v_dc = tid >> 4;
-  auto load_tile = [&](int t) {
+  // ---- direct global->LDS loads.  Instruction i of wave w fills the 1 KB
+  // block (i*NW + w) of a tile region; lane L writes its 16 bytes at L*16.
+  int k_row[C::K_LOADS];       // K row (key within the tile) this lane fetches
+  int k_col[C::K_LOADS];       // element column within the head (swizzled chunk)
+#pragma unroll
+  for (int i = 0; i < C::K_LOADS; ++i) {
+    const int r = (i * NW + wave) * C::K_ROWS_PER_LOAD + lane / C::NCH;
+    const int p = lane % C::NCH;
+    k_row[i] = r;
+    k_col[i] = (p ^ (r & (C::NCH - 1))) * 8;
+  }
+  int v_off[C::V_LOADS];       // element offset within the V^T tile
+#pragma unroll
+  for (int i = 0; i < C::V_LOADS; ++i) {
+    const int d = (i * NW + wave) * 8 + lane / 8;
+    const int p = lane % 8;
+    v_off[i] = d * 64 + (p ^ (d & 7)) * 8;
+  }
+  const uint16_t* vt_head = a.vt + (int64_t)head * a.n_kv_tiles * HD * 64;
+
+  auto issue_tile = [&](int t) __attribute__((always_inline)) {
+    uint8_t* stage = smem + (t % NSTAGE) * C::STAGE_BYTES;
     const int64_t k0 = (int64_t)t * BKV;
 #pragma unroll
-    for (int i = 0; i < C::K_CHUNKS; ++i) {
-      const int c = i * NTHREADS + tid;
-      const int key = c / C::DCH;
-      const int dc = c - key * C::DCH;
-      const int64_t gk = min(k0 + key, key_end - 1);
-      rk[i] = *reinterpret_cast<const u32x4*>(a.k + gk * ld + hcol + dc * 8);
+    for (int i = 0; i < C::K_LOADS; ++i) {
+      const int64_t key = min(k0 + k_row[i], key_end - 1);
+      dma16(a.k + key * ld + hcol + k_col[i], stage + (i * NW + wave) * 1024);
     }
-    if (v_loader) {
+    const uint16_t* vtile = vt_head + (int64_t)t * HD * 64;
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const int64_t gk = min(k0 + 4 * v_kg + j, key_end - 1);
-        rv[j] = *reinterpret_cast<const u32x4*>(a.v + gk * ld + hcol + v_dc * 8);
-      }
-    }
+    for (int i = 0; i < C::V_LOADS; ++i)
+      dma16(vtile + v_off[i], stage + C::K_BYTES + (i * NW + wave) * 1024);
   };
-  auto store_tile = [&](int buf) {
-    uint16_t* ks = lds + buf * C::BUF_ELEMS;
-    uint16_t* vt = ks + C::K_ELEMS;
+
+  // ---- fragment read addresses (bytes within a stage).  K row r = kb*32 + ql,
+  // logical chunk 2*kk + half, physical chunk (2*kk + half) ^ (r % NCH):
+  // address = (row base | ((half ^ r%NCH) << 4)) ^ (kk << 5).  V^T row
+  // d = dt*32 + ql, chunk 2*ks + half: (row base | ((half ^ d%8) << 4)) ^ (ks << 5).
+  const uint32_t k_a0 = (uint32_t)ql * (HD * 2) + ((uint32_t)(half ^ (ql & (C::NCH - 1))) << 4);
+  const uint32_t v_a0 = C::K_BYTES + (uint32_t)ql * 128 + ((uint32_t)(half ^ (ql & 7)) << 4);
+
+  auto compute_s = [&](int t, f32x16 (&s)[2]) __attribute__((always_inline)) {
+    const uint8_t* stage = smem + (t % NSTAGE) * C::STAGE_BYTES;
 #pragma unroll
-    for (int i = 0; i < C::K_CHUNKS; ++i) {
-      const int c = i * NTHREADS + tid;
-      const int key = c / C::DCH;
-      const int dc = c - key * C::DCH;
-      *reinterpret_cast<u32x4*>(ks + key * C::KLD + dc * 8) = rk[i];
-    }
-    if (v_loader) {
-      // transpose the 4 keys x 8 dims block: for dim j, pack keys 0..3.
-      const int slot = (v_kg >> 2) * 16 + vt_block_slot(v_kg & 3) * 4;
+    for (int kb = 0; kb < 2; ++kb) {
+      s[kb] = f32x16{};
 #pragma unroll
-      for (int jw = 0; jw < 4; ++jw) {
-        const uint32_t x0 = rv[0][jw], x1 = rv[1][jw], x2 = rv[2][jw], x3 = rv[3][jw];
-        u32x2 lo, hi;  // dims 2*jw (low halves) and 2*jw+1 (high halves)
-        lo[0] = (x0 & 0xffffu) | (x1 << 16);
-        lo[1] = (x2 & 0xffffu) | (x3 << 16);
-        hi[0] = (x0 >> 16) | (x1 & 0xffff0000u);
-        hi[1] = (x2 >> 16) | (x3 & 0xffff0000u);
-        const int d = v_dc * 8 + 2 * jw;
-        *reinterpret_cast<u32x2*>(vt + d * C::VLD + slot) = lo;
-        *reinterpret_cast<u32x2*>(vt + (d + 1) * C::VLD + slot) = hi;
+      for (int kk = 0; kk < C::KK; ++kk) {
+        const u32x4 kf = *reinterpret_cast<const u32x4*>(stage + kb * 32 * (HD * 2) + (k_a0 ^ (uint32_t)(kk << 5)));
+        s[kb] = mfma32(as_bf16x8(kf), qf[kk], s[kb]);
       }
     }
   };
 
-  // ---- running state (log2 domain): m = max of scaled scores, l = lane-partial sum.
+  // ---- running state (log2 domain): m = running reference max of the scaled
+  // scores, l = lane-partial sum of exp2(score*scale - m).
   constexpr float inv_sqrt_hd = HD == 128 ? 0.08838834764831844055f : 0.125f;
   const float scale_log2 = 1.44269504088896340736f * inv_sqrt_hd;
   float m_run = -INFINITY;
@@ -167,80 +239,97 @@ __global__ __launch_bounds__(NTHREADS) void attn_kernel(const AttnArgs a) {
 #pragma unroll
   for (int dt = 0; dt < C::DT; ++dt) o[dt] = f32x16{};
 
-  load_tile(0);
-  store_tile(0);
-  __syncthreads();
-
-  for (int t = 0; t < n_tiles; ++t) {
-    const int buf = t & 1;
-    if (t + 1 < n_tiles) load_tile(t + 1);
+  // softmax of tile t (scores in s) and O^T += V^T(t) P^T(t)
+  auto softmax_pv = [&](int t, f32x16 (&s)[2]) __attribute__((always_inline)) {
     const int64_t k0 = (int64_t)t * BKV;
-    if (wave_active && k0 <= wave_max_pos) {
-      const uint16_t* ks = lds + buf * C::BUF_ELEMS;
-      const uint16_t* vt = ks + C::K_ELEMS;
-      // S^T for two 32-key blocks: lane holds query ql, keys 8*(e/4)+4*half+e%4.
-      f32x16 s[2];
+    if (k0 + BKV - 1 > wave_min_pos) {  // tile crosses the wave's diagonal (wave-uniform)
+      // key k0 + kb*32 + 8*(e/4) + 4*half + e%4 is masked when it exceeds qpos,
+      // i.e. when the lane-independent part kb*32 + 8*(e/4) + e%4 exceeds lim.
+      const int lim = (int)min(max(qpos - k0, (int64_t)-1), (int64_t)BKV) - 4 * half;
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb) {
-        s[kb] = f32x16{};
-        const uint16_t* kp = ks + (kb * 32 + ql) * C::KLD + 8 * half;
+      for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-        for (int kk = 0; kk < C::KK; ++kk)
-          s[kb] = mfma32(as_bf16x8(*reinterpret_cast<const u32x4*>(kp + kk * 16)), qf[kk], s[kb]);
-      }
-      // scale into the log2 domain; mask keys past the query on diagonal tiles.
-      const bool diag = k0 + BKV - 1 > wave_min_pos;
-      float mloc = -INFINITY;
+        for (int e = 0; e < 16; ++e)
+          if (kb * 32 + 8 * (e >> 2) + (e & 3) > lim) s[kb][e] = -INFINITY;
+    }
+    float mx = -INFINITY;
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb) {
+    for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-        for (int e = 0; e < 16; ++e) {
-          float x = s[kb][e] * scale_log2;
-          if (diag) {
-            const int64_t key = k0 + kb * 32 + 8 * (e >> 2) + 4 * half + (e & 3);
-            if (key > qpos) x = -INFINITY;
-          }
-          s[kb][e] = x;
-          mloc = fmaxf(mloc, x);
-        }
-      }
-      mloc = fmaxf(mloc, __shfl_xor(mloc, 32));
-      const float m_new = fmaxf(m_run, mloc);
+      for (int e = 0; e < 16; ++e) mx = fmaxf(mx, s[kb][e]);
+    mx = fmaxf(mx, __shfl_xor(mx, 32));
+    const float mt = mx * scale_log2;
+    if (__builtin_amdgcn_ballot_w64(mt > m_run + LAZY_TAU) != 0) {  // wave-uniform
+      const float m_new = fmaxf(m_run, mt);
       const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
       m_run = m_new;
-      // probabilities -> bf16 B operands; lane-partial row sum.
-      bf16x8 pf[4];
-      float lsum = 0.0f;
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb) {
-#pragma unroll
-        for (int g = 0; g < 2; ++g) {
-          u32x4 packed;
-#pragma unroll
-          for (int j = 0; j < 4; ++j) {
-            const float p0 = __builtin_amdgcn_exp2f(s[kb][8 * g + 2 * j] - m_new);
-            const float p1 = __builtin_amdgcn_exp2f(s[kb][8 * g + 2 * j + 1] - m_new);
-            lsum += p0 + p1;
-            packed[j] = pack_bf16x2(p0, p1);
-          }
-          pf[2 * kb + g] = as_bf16x8(packed);
-        }
-      }
-      l_run = l_run * alpha + lsum;
+      l_run *= alpha;
 #pragma unroll
       for (int dt = 0; dt < C::DT; ++dt) o[dt] *= alpha;
-      // O^T += V^T P^T over the tile's four 16-key steps.
+    }
+    const float neg_m = -m_run;
+    bf16x8 pf[4];
+    float lsum = 0.0f;
 #pragma unroll
-      for (int dt = 0; dt < C::DT; ++dt) {
-        const uint16_t* vp = vt + (dt * 32 + ql) * C::VLD + 8 * half;
+    for (int kb = 0; kb < 2; ++kb) {
 #pragma unroll
-        for (int ks16 = 0; ks16 < 4; ++ks16)
-          o[dt] = mfma32(as_bf16x8(*reinterpret_cast<const u32x4*>(vp + ks16 * 16)), pf[ks16], o[dt]);
+      for (int g = 0; g < 2; ++g) {
+        u32x4 packed;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const float p0 = __builtin_amdgcn_exp2f(fmaf(s[kb][8 * g + 2 * j], scale_log2, neg_m));
+          const float p1 = __builtin_amdgcn_exp2f(fmaf(s[kb][8 * g + 2 * j + 1], scale_log2, neg_m));
+          lsum += p0 + p1;
+          packed[j] = pack_bf16x2(p0, p1);
+        }
+        pf[2 * kb + g] = as_bf16x8(packed);
       }
     }
-    if (t + 1 < n_tiles) store_tile(buf ^ 1);
-    __syncthreads();
+    l_run += lsum;
+    const uint8_t* stage = smem + (t % NSTAGE) * C::STAGE_BYTES;
+#pragma unroll
+    for (int dt = 0; dt < C::DT; ++dt) {
+#pragma unroll
+      for (int ks = 0; ks < 4; ++ks) {
+        const u32x4 vf = *reinterpret_cast<const u32x4*>(stage + dt * 32 * 128 + (v_a0 ^ (uint32_t)(ks << 5)));
+        o[dt] = mfma32(as_bf16x8(vf), pf[ks], o[dt]);
+      }
+    }
+  };
+
+  // One pipeline step: make tile t+1 visible (and the stage of tile t-1 free),
+  // issue tile t+NSTAGE-1, then S(t+1) next to softmax(t) and PV(t).
+  auto step = [&](int t, f32x16 (&s_cu)[2], f32x16 (&s_nx)[2]) __attribute__((always_inline)) {
+    if (t + 1 < n_tiles) {
+      if (t + 2 < n_tiles)
+        wait_vmcnt<C::LOADS>();
+      else
+        wait_vmcnt<0>();
+    }
+    lds_barrier();
+    if (t + NSTAGE - 1 < n_tiles) issue_tile(t + NSTAGE - 1);
+    if (t + 1 < wave_tiles) compute_s(t + 1, s_nx);
+    if (t < wave_tiles) softmax_pv(t, s_cu);
+  };
+
+  // ---- prologue: tiles 0 .. NSTAGE-2 in flight, wait for tile 0.
+  const int pro = min(NSTAGE - 1, n_tiles);
+  for (int t = 0; t < pro; ++t) issue_tile(t);
+  if (pro >= 3)
+    wait_vmcnt<2 * C::LOADS>();
+  else if (pro == 2)
+    wait_vmcnt<C::LOADS>();
+  else
+    wait_vmcnt<0>();
+  lds_barrier();
+
+  f32x16 sA[2], sB[2];
+  if (wave_tiles > 0) compute_s(0, sA);
+  for (int t = 0; t < n_tiles; t += 2) {
+    step(t, sA, sB);
+    if (t + 1 < n_tiles) step(t + 1, sB, sA);
   }
+  wait_vmcnt<0>();
 
   // ---- normalise and store: lane holds query ql, dims dt*32 + 8*(e/4) + 4*half + e%4.
   if (wave_active) {
@@ -260,10 +349,10 @@ __global__ __launch_bounds__(NTHREADS) void attn_kernel(const AttnArgs a) {
           v[1] = pack_bf16x2(r[2], r[3]);
           *reinterpret_cast<u32x2*>(a.o + off + dt * 32 + 8 * g) = v;
           if (a.o_lo) {  // rounding residual: r - bf16(r), itself rounded to bf16
-            u32x2 w;
-            w[0] = pack_bf16x2(r[0] - __uint_as_float(v[0] << 16), r[1] - __uint_as_float(v[0] & 0xffff0000u));
-            w[1] = pack_bf16x2(r[2] - __uint_as_float(v[1] << 16), r[3] - __uint_as_float(v[1] & 0xffff0000u));
-            *reinterpret_cast<u32x2*>(a.o_lo + off + dt * 32 + 8 * g) = w;
+            u32x2 wv;
+            wv[0] = pack_bf16x2(r[0] - __uint_as_float(v[0] << 16), r[1] - __uint_as_float(v[0] & 0xffff0000u));
+            wv[1] = pack_bf16x2(r[2] - __uint_as_float(v[1] << 16), r[3] - __uint_as_float(v[1] & 0xffff0000u));
+            *reinterpret_cast<u32x2*>(a.o_lo + off + dt * 32 + 8 * g) = wv;
           }
         }
       }
@@ -273,8 +362,21 @@ __global__ __launch_bounds__(NTHREADS) void attn_kernel(const AttnArgs a) {
 
 }  // namespace
 
+int64_t attn_kv_tiles(int64_t seq_len) { return (seq_len + BKV - 1) / BKV; }
+
+hipError_t launch_vt_prep(const AttnArgs& a, hipStream_t stream) {
+  const dim3 grid((unsigned)a.n_kv_tiles, (unsigned)a.n_heads), block(128);
+  if (a.head_dim == 128)
+    hipLaunchKernelGGL(vt_prep_kernel<128>, grid, block, 0, stream, a.v, a.seq_len, a.hidden, a.vt, a.n_kv_tiles);
+  else
+    hipLaunchKernelGGL(vt_prep_kernel<64>, grid, block, 0, stream, a.v, a.seq_len, a.hidden, a.vt, a.n_kv_tiles);
+  return hipGetLastError();
+}
+
 hipError_t launch_attention(const AttnArgs& a, hipStream_t stream) {
   if (a.chunk_len <= 0) return hipSuccess;
+  hipError_t e = launch_vt_prep(a, stream);
+  if (e != hipSuccess) return e;
   const int tpc = (int)((a.chunk_len + QT - 1) / QT);
   const dim3 grid(a.n_heads * 2 * tpc), block(NTHREADS);
   if (a.head_dim == 128)

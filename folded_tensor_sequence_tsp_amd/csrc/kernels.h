@@ -75,8 +75,16 @@ struct AttnArgs {
   uint16_t* o_lo;     // nullable: bf16(out - o), the rounding residual of o
   int64_t seq_len, chunk_len, chunk_start0, chunk_start1;
   int32_t hidden, n_heads, head_dim;
+  // V^T tiles written by the attention launch before the attention kernel:
+  // [n_heads][n_kv_tiles][head_dim][64] bf16, keys permuted within 16-key groups.
+  uint16_t* vt;
+  int64_t n_kv_tiles;  // attn_kv_tiles(seq_len)
 };
 
+// 64-key tiles covering seq_len keys.
+int64_t attn_kv_tiles(int64_t seq_len);
+
+// V -> V^T tiles, then the attention kernel (both on `stream`).
 hipError_t launch_attention(const AttnArgs& args, hipStream_t stream);
 
 }  // namespace tsp

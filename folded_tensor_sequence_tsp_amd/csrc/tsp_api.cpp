@@ -72,8 +72,16 @@ tsp_status check_plan(const tsp_plan* p) {
   return TSP_OK;
 }
 
-// Attention workspace: Q, then the attention output as a bf16 pair (hi, lo).
-size_t ws_attn(int64_t n, const tsp_dims* d) { return 3 * round_up((size_t)n * d->hidden * 2); }
+// Attention core workspace: the V^T tiles of the gathered V for S = D * n keys.
+size_t ws_core(int64_t n, const tsp_dims* d, int32_t D) {
+  return round_up((size_t)attn_kv_tiles(n * D) * 64 * d->hidden * 2);
+}
+
+// Attention workspace: Q, the attention output as a bf16 pair (hi, lo), then
+// the core's V^T tiles.
+size_t ws_attn(int64_t n, const tsp_dims* d, int32_t D) {
+  return 3 * round_up((size_t)n * d->hidden * 2) + ws_core(n, d, D);
+}
 
 // MLP workspace: fp16 GELU output for one token block, the fp16 copy of all W2
 // shards, and one int32 row exponent per token.
@@ -125,7 +133,8 @@ tsp_status run_project(const tsp_plan* plan, const tsp_dims* dims, const uint16_
 }
 
 tsp_status run_core(const tsp_plan* plan, const tsp_dims* dims, const uint16_t* q, const uint16_t* k_full,
-                    const uint16_t* v_full, uint16_t* attn_out, uint16_t* attn_lo, hipStream_t stream) {
+                    const uint16_t* v_full, uint16_t* attn_out, uint16_t* attn_lo, void* core_ws,
+                    hipStream_t stream) {
   AttnArgs a{};
   a.q = q;
   a.k = k_full;
@@ -139,6 +148,8 @@ tsp_status run_core(const tsp_plan* plan, const tsp_dims* dims, const uint16_t* 
   a.hidden = dims->hidden;
   a.n_heads = dims->n_heads;
   a.head_dim = dims->head_dim;
+  a.vt = static_cast<uint16_t*>(core_ws);
+  a.n_kv_tiles = attn_kv_tiles(plan->seq_len);
   return from_hip(launch_attention(a, stream));
 }
 
@@ -255,7 +266,7 @@ PostWs post_ws(int64_t n, const tsp_dims* d) {
 }
 
 // Whole layer: Q and attention-output buffers, then the post workspace.
-size_t ws_layer(int64_t n, const tsp_dims* d) { return ws_attn(n, d) + post_ws(n, d).total; }
+size_t ws_layer(int64_t n, const tsp_dims* d, int32_t D) { return ws_attn(n, d, D) + post_ws(n, d).total; }
 
 // h1 = x + attn W_o^T (fp32, split-K over head shards from `start`), then
 // out = h1 + MLP(h1) on scaled fp16 operands with the ring from `start`.
@@ -320,13 +331,16 @@ size_t tsp_workspace_size(int64_t n_tokens, const tsp_dims* dims, int32_t D, int
   switch (kind) {
     case TSP_WS_ATTN:
       if (check_dims(dims, D, true, false) != TSP_OK) return 0;
-      return ws_attn(n_tokens, dims);
+      return ws_attn(n_tokens, dims, D);
+    case TSP_WS_CORE:
+      if (check_dims(dims, D, true, false, 0) != TSP_OK) return 0;
+      return ws_core(n_tokens, dims, D);
     case TSP_WS_MLP:
       if (check_dims(dims, D, false, true) != TSP_OK) return 0;
       return ws_mlp(n_tokens, dims);
     case TSP_WS_LAYER:
       if (check_dims(dims, D, true, true) != TSP_OK) return 0;
-      return ws_layer(n_tokens, dims);
+      return ws_layer(n_tokens, dims, D);
     case TSP_WS_POST:
       if (check_dims(dims, D, true, true) != TSP_OK) return 0;
       return post_ws(n_tokens, dims).total;
@@ -348,7 +362,8 @@ tsp_status tsp_attn_project(const tsp_plan* plan, const tsp_dims* dims, const ui
 }
 
 tsp_status tsp_attn_core(const tsp_plan* plan, const tsp_dims* dims, const uint16_t* q, const uint16_t* k_full,
-                         const uint16_t* v_full, uint16_t* attn_out, uint16_t* attn_lo, hipStream_t stream) {
+                         const uint16_t* v_full, uint16_t* attn_out, uint16_t* attn_lo, void* workspace,
+                         size_t ws_bytes, hipStream_t stream) {
   tsp_status s;
   if ((s = check_plan(plan)) != TSP_OK) return s;
   if ((s = check_dims(dims, plan->D, true, false, 0)) != TSP_OK) return s;
@@ -356,7 +371,10 @@ tsp_status tsp_attn_core(const tsp_plan* plan, const tsp_dims* dims, const uint1
       (s = check_ptr(attn_out)) != TSP_OK || (s = check_ptr_nullable(attn_lo)) != TSP_OK)
     return s;
   if (attn_out == q || attn_lo == q || attn_lo == attn_out) return TSP_ERR_INVALID_ARG;
-  return run_core(plan, dims, q, k_full, v_full, attn_out, attn_lo, stream);
+  if (!workspace) return TSP_ERR_WORKSPACE;
+  if (!aligned16(workspace)) return TSP_ERR_ALIGNMENT;
+  if (ws_bytes < ws_core(plan->n_local, dims, plan->D)) return TSP_ERR_WORKSPACE;
+  return run_core(plan, dims, q, k_full, v_full, attn_out, attn_lo, workspace, stream);
 }
 
 tsp_status tsp_attn_out(int64_t n_tokens, const tsp_dims* dims, int32_t D, int32_t start_shard,
@@ -390,12 +408,13 @@ tsp_status tsp_attn_forward(const tsp_plan* plan, const tsp_dims* dims, const ui
   if (out == x_local) return TSP_ERR_INVALID_ARG;
   if (!workspace) return TSP_ERR_WORKSPACE;
   if (!aligned16(workspace)) return TSP_ERR_ALIGNMENT;
-  if (ws_bytes < ws_attn(plan->n_local, dims)) return TSP_ERR_WORKSPACE;
+  if (ws_bytes < ws_attn(plan->n_local, dims, plan->D)) return TSP_ERR_WORKSPACE;
   uint16_t* qbuf = static_cast<uint16_t*>(workspace);
   uint16_t* abuf = qbuf + round_up((size_t)plan->n_local * dims->hidden * 2) / 2;
   uint16_t* alo = abuf + round_up((size_t)plan->n_local * dims->hidden * 2) / 2;
+  void* core_ws = alo + round_up((size_t)plan->n_local * dims->hidden * 2) / 2;
   if ((s = run_project(plan, dims, x_local, wqkv, k_full, v_full, qbuf, stream)) != TSP_OK) return s;
-  if ((s = run_core(plan, dims, qbuf, k_full, v_full, abuf, alo, stream)) != TSP_OK) return s;
+  if ((s = run_core(plan, dims, qbuf, k_full, v_full, abuf, alo, core_ws, stream)) != TSP_OK) return s;
   return run_out(plan->n_local, dims, plan->D, plan->rank, abuf, alo, wo, residual, out, false, stream);
 }
 
@@ -434,13 +453,14 @@ tsp_status tsp_layer_forward(const tsp_plan* plan, const tsp_dims* dims, const u
   if (!workspace) return TSP_ERR_WORKSPACE;
   if (!aligned16(workspace)) return TSP_ERR_ALIGNMENT;
   const int64_t n = plan->n_local;
-  if (ws_bytes < ws_layer(n, dims)) return TSP_ERR_WORKSPACE;
+  if (ws_bytes < ws_layer(n, dims, plan->D)) return TSP_ERR_WORKSPACE;
   uint16_t* qbuf = static_cast<uint16_t*>(workspace);
   uint16_t* abuf = qbuf + round_up((size_t)n * dims->hidden * 2) / 2;
   uint16_t* alo = abuf + round_up((size_t)n * dims->hidden * 2) / 2;
-  char* post = static_cast<char*>(workspace) + ws_attn(n, dims);
+  void* core_ws = alo + round_up((size_t)n * dims->hidden * 2) / 2;
+  char* post = static_cast<char*>(workspace) + ws_attn(n, dims, plan->D);
   if ((s = run_project(plan, dims, x_local, wqkv, k_full, v_full, qbuf, stream)) != TSP_OK) return s;
-  if ((s = run_core(plan, dims, qbuf, k_full, v_full, abuf, alo, stream)) != TSP_OK) return s;
+  if ((s = run_core(plan, dims, qbuf, k_full, v_full, abuf, alo, core_ws, stream)) != TSP_OK) return s;
   return run_post(n, dims, plan->D, plan->rank, abuf, alo, x_local, wo, w1, w2, out, post, stream);
 }
 

@@ -18,7 +18,7 @@ import torch
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libtsp.so")
 
 TSP_OK, TSP_ERR_INVALID_ARG, TSP_ERR_SHAPE, TSP_ERR_ALIGNMENT, TSP_ERR_WORKSPACE, TSP_ERR_UNSUPPORTED, TSP_ERR_HIP = range(7)
-WS_ATTN, WS_MLP, WS_LAYER, WS_POST = 0, 1, 2, 3
+WS_ATTN, WS_MLP, WS_LAYER, WS_POST, WS_CORE = 0, 1, 2, 3, 4
 MAX_D = 16
 
 EXPORTS = ["tsp_zigzag_plan", "tsp_workspace_size", "tsp_attn_project", "tsp_attn_core", "tsp_attn_out",
@@ -55,7 +55,7 @@ def lib() -> ctypes.CDLL:
             "tsp_zigzag_plan": [c_int64, c_int32, c_int32, POINTER(Plan), P, P],
             "tsp_workspace_size": [c_int64, POINTER(Dims), c_int32, c_int32],
             "tsp_attn_project": [POINTER(Plan), POINTER(Dims), P, PP, P, P, P, P],
-            "tsp_attn_core": [POINTER(Plan), POINTER(Dims), P, P, P, P, P, P],
+            "tsp_attn_core": [POINTER(Plan), POINTER(Dims), P, P, P, P, P, P, c_size_t, P],
             "tsp_attn_out": [c_int64, POINTER(Dims), c_int32, c_int32, P, P, PP, P, P, P],
             "tsp_attn_forward": [POINTER(Plan), POINTER(Dims), P, PP, PP, P, P, P, P, P, c_size_t, P],
             "tsp_mlp_forward": [c_int64, POINTER(Dims), c_int32, c_int32, P, PP, PP, P, P, P, c_size_t, P],
@@ -156,11 +156,18 @@ def attn_project(plan: Plan, dims: Dims, x_local, wqkv, k_full, v_full, q_out, s
            "tsp_attn_project")
 
 
-def attn_core(plan: Plan, dims: Dims, q, k_full, v_full, attn_out, attn_lo=None, stream=None):
+def attn_core(plan: Plan, dims: Dims, q, k_full, v_full, attn_out, attn_lo=None, workspace=None, stream=None):
+    """Causal attention of the plan's local queries; ``workspace`` defaults to a
+    fresh allocation of tsp_workspace_size(..., WS_CORE) bytes."""
     n, h, S = plan.n_local, dims.hidden, plan.seq_len
+    need = workspace_size(n, dims, plan.D, WS_CORE)
+    if workspace is None:
+        workspace = torch.empty(max(need, 256), dtype=torch.uint8, device=q.device)
+    ws, nbytes = _workspace(workspace, need)
     args = (_dev_tensor(q, (n, h), "q"), _dev_tensor(k_full, (S, h), "k_full"), _dev_tensor(v_full, (S, h), "v_full"),
             _dev_tensor(attn_out, (n, h), "attn_out"), _opt_tensor(attn_lo, (n, h), "attn_lo"))
-    _check(lib().tsp_attn_core(ctypes.byref(plan), ctypes.byref(dims), *args, _stream(stream)), "tsp_attn_core")
+    _check(lib().tsp_attn_core(ctypes.byref(plan), ctypes.byref(dims), *args, ws, nbytes, _stream(stream)),
+           "tsp_attn_core")
 
 
 def attn_out(dims: Dims, D: int, start_shard: int, attn, wo, residual, out, attn_lo=None, stream=None):

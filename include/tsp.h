@@ -78,7 +78,7 @@ typedef struct {
 } tsp_dims;
 
 /* Workspace kinds for tsp_workspace_size(). */
-typedef enum { TSP_WS_ATTN = 0, TSP_WS_MLP = 1, TSP_WS_LAYER = 2, TSP_WS_POST = 3 } tsp_ws_kind;
+typedef enum { TSP_WS_ATTN = 0, TSP_WS_MLP = 1, TSP_WS_LAYER = 2, TSP_WS_POST = 3, TSP_WS_CORE = 4 } tsp_ws_kind;
 
 /*
  * Zigzag plan (zubnet.ai TSP page, para. 2: K/V are gathered over a zigzag
@@ -99,8 +99,9 @@ tsp_status tsp_zigzag_plan(int64_t seq_len, int32_t D, int32_t rank, tsp_plan* p
 
 /*
  * Bytes of workspace that tsp_attn_forward (TSP_WS_ATTN), tsp_mlp_forward
- * (TSP_WS_MLP), tsp_layer_forward (TSP_WS_LAYER) or tsp_layer_post
- * (TSP_WS_POST) need for n_tokens local tokens.  Returns 0 for invalid dims or
+ * (TSP_WS_MLP), tsp_layer_forward (TSP_WS_LAYER), tsp_layer_post (TSP_WS_POST)
+ * or tsp_attn_core (TSP_WS_CORE) need for n_tokens local tokens (the kinds
+ * that hold attention state size it for a sequence of D * n_tokens keys).  Returns 0 for invalid dims or
  * kind.  Workspace contents are scratch: nothing persists between calls.
  */
 size_t tsp_workspace_size(int64_t n_tokens, const tsp_dims* dims, int32_t D, int32_t kind);
@@ -140,10 +141,12 @@ tsp_status tsp_attn_project(const tsp_plan* plan, const tsp_dims* dims, const ui
  *              residual bf16(attn - attn_out), so that attn_out + attn_lo carries
  *              the fp32 result to about 16 significant bits (tsp_attn_out and
  *              tsp_layer_post contract both parts).
+ *   workspace: device, >= tsp_workspace_size(n_local, dims, D, TSP_WS_CORE) bytes
+ *              (a head-blocked transposed copy of v_full).
  */
 tsp_status tsp_attn_core(const tsp_plan* plan, const tsp_dims* dims, const uint16_t* q,
                          const uint16_t* k_full, const uint16_t* v_full, uint16_t* attn_out,
-                         uint16_t* attn_lo, hipStream_t stream);
+                         uint16_t* attn_lo, void* workspace, size_t ws_bytes, hipStream_t stream);
 
 /*
  * O projection as a split-K over the D head shards (the attention projections

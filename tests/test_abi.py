@@ -135,12 +135,17 @@ def test_tampered_plan_rejected(L):
 
 def test_core_rejects(L):
     p, d = _plan(), _dims()
-    assert L.tsp_attn_core(None, ctypes.byref(d), A, A, A, A + 64, None, None) == tsp.TSP_ERR_INVALID_ARG
-    assert L.tsp_attn_core(ctypes.byref(p), ctypes.byref(d), A, A, A, A, None, None) == tsp.TSP_ERR_INVALID_ARG  # alias
-    assert L.tsp_attn_core(ctypes.byref(p), ctypes.byref(d), A, A, MIS, A + 64, None, None) == tsp.TSP_ERR_ALIGNMENT
-    assert L.tsp_attn_core(ctypes.byref(p), None, A, A, A, A + 64, None, None) == tsp.TSP_ERR_INVALID_ARG
-    assert L.tsp_attn_core(ctypes.byref(p), ctypes.byref(d), A, A, A, A + 64, A + 64, None) == tsp.TSP_ERR_INVALID_ARG
-    assert L.tsp_attn_core(ctypes.byref(p), ctypes.byref(d), A, A, A, A + 64, MIS, None) == tsp.TSP_ERR_ALIGNMENT
+    assert L.tsp_attn_core(None, ctypes.byref(d), A, A, A, A + 64, None, A + 128, 1 << 40, None) == tsp.TSP_ERR_INVALID_ARG
+    assert L.tsp_attn_core(ctypes.byref(p), ctypes.byref(d), A, A, A, A, None, A + 128, 1 << 40, None) == tsp.TSP_ERR_INVALID_ARG  # alias
+    assert L.tsp_attn_core(ctypes.byref(p), ctypes.byref(d), A, A, MIS, A + 64, None, A + 128, 1 << 40, None) == tsp.TSP_ERR_ALIGNMENT
+    assert L.tsp_attn_core(ctypes.byref(p), None, A, A, A, A + 64, None, A + 128, 1 << 40, None) == tsp.TSP_ERR_INVALID_ARG
+    assert L.tsp_attn_core(ctypes.byref(p), ctypes.byref(d), A, A, A, A + 64, A + 64, A + 128, 1 << 40, None) == tsp.TSP_ERR_INVALID_ARG
+    assert L.tsp_attn_core(ctypes.byref(p), ctypes.byref(d), A, A, A, A + 64, MIS, A + 128, 1 << 40, None) == tsp.TSP_ERR_ALIGNMENT
+    need = tsp.workspace_size(p.n_local, d, p.D, tsp.WS_CORE)
+    assert need == p.seq_len * 256 * 2  # V^T copy of the gathered V (S a multiple of 64 here)
+    assert L.tsp_attn_core(ctypes.byref(p), ctypes.byref(d), A, A, A, A + 64, None, A + 128, need - 1, None) == tsp.TSP_ERR_WORKSPACE
+    assert L.tsp_attn_core(ctypes.byref(p), ctypes.byref(d), A, A, A, A + 64, None, None, need, None) == tsp.TSP_ERR_WORKSPACE
+    assert L.tsp_attn_core(ctypes.byref(p), ctypes.byref(d), A, A, A, A + 64, None, MIS, need, None) == tsp.TSP_ERR_ALIGNMENT
 
 
 def test_out_rejects(L):
@@ -226,7 +231,9 @@ def test_workspace_sizes(L):
     post = tsp.workspace_size(n, d, 4, tsp.WS_POST)
     # post: fp32 h1, fp16 h1, row exponents, fp16 W1 and W2, fp16 GELU block
     assert post == n * 256 * 4 + n * 256 * 2 + n * 4 + 2 * 1024 * 256 * 2 + n * 1024 * 2
-    assert attn == 3 * n * 256 * 2  # Q and the attention output as a (hi, lo) bf16 pair
+    core = tsp.workspace_size(n, d, 4, tsp.WS_CORE)
+    assert core == 4 * n * 256 * 2  # V^T tiles for S = D * n keys
+    assert attn == 3 * n * 256 * 2 + core  # Q, the attention output as a (hi, lo) bf16 pair, V^T
     assert layer == attn + post
     assert tsp.workspace_size(n, d, 4, 7) == 0
     assert tsp.workspace_size(n, _dims(hidden=300), 4, tsp.WS_LAYER) == 0
