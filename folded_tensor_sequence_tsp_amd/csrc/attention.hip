@@ -21,10 +21,12 @@
 //   * K and V^T tiles of 64 keys stream into a 4-stage LDS ring with direct
 //     global->LDS loads (global_load_lds_dwordx4; no register staging), the 16-
 //     byte chunks of each row XOR-swizzled by the row index so that fragment
-//     reads of 32 rows are conflict-free; per tile one vmcnt wait and one
-//     barrier; loads run three tiles ahead;
-//   * software pipeline: the MFMAs of S for tile t+1 are issued in the same
-//     block as the softmax of tile t, so matrix and vector work overlap;
+//     reads of 32 rows hit distinct banks of the 64-bank LDS; per tile one
+//     vmcnt wait and one barrier; loads run two to three tiles ahead;
+//   * software pipeline: the S MFMAs of tile t+1 sit in one basic block with
+//     the exponentials of tile t (all branches are wave-uniform), so matrix
+//     and vector work interleave; the PV MFMAs of tile t then overlap the mask
+//     and max of the next step;
 //   * online softmax in fp32, log2 domain, scale folded into one FMA, hardware
 //     exp2, and lazy rescaling: the running max moves (and O, l are rescaled)
 //     only when a tile's max exceeds it by more than 2^8, so probabilities stay
@@ -133,7 +135,7 @@ __global__ __launch_bounds__(NTHREADS) void attn_kernel(const AttnArgs a) {
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int wave = tid >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform (scalar) index
   const int half = lane >> 5;
   const int ql = lane & 31;
 
@@ -177,45 +179,58 @@ __global__ __launch_bounds__(NTHREADS) void attn_kernel(const AttnArgs a) {
 
   // ---- direct global->LDS loads.  Instruction i of wave w fills the 1 KB
   // block (i*NW + w) of a tile region; lane L writes its 16 bytes at L*16.
-  int k_row[C::K_LOADS];       // K row (key within the tile) this lane fetches
-  int k_col[C::K_LOADS];       // element column within the head (swizzled chunk)
+  // K: row r of the tile, logical 16-byte chunk (L % NCH) ^ (r % NCH).
+  int k_row[C::K_LOADS];             // K row (key within the tile) this lane fetches
+  int k_col[C::K_LOADS];             // element column within the head (swizzled chunk)
+  const uint16_t* k_src[C::K_LOADS];  // source for tile 0; tile t adds t * 64 rows
 #pragma unroll
   for (int i = 0; i < C::K_LOADS; ++i) {
     const int r = (i * NW + wave) * C::K_ROWS_PER_LOAD + lane / C::NCH;
     const int p = lane % C::NCH;
     k_row[i] = r;
     k_col[i] = (p ^ (r & (C::NCH - 1))) * 8;
+    k_src[i] = a.k + (int64_t)r * ld + hcol + k_col[i];
   }
-  int v_off[C::V_LOADS];       // element offset within the V^T tile
+  // V^T: row d of the tile, logical chunk (L % 8) ^ ((d / 2) % 8).
+  const uint16_t* v_src[C::V_LOADS];
+  {
+    const uint16_t* vt_head = a.vt + (int64_t)head * a.n_kv_tiles * HD * 64;
 #pragma unroll
-  for (int i = 0; i < C::V_LOADS; ++i) {
-    const int d = (i * NW + wave) * 8 + lane / 8;
-    const int p = lane % 8;
-    v_off[i] = d * 64 + (p ^ (d & 7)) * 8;
+    for (int i = 0; i < C::V_LOADS; ++i) {
+      const int d = (i * NW + wave) * 8 + lane / 8;
+      const int p = lane % 8;
+      v_src[i] = vt_head + d * 64 + (p ^ ((d >> 1) & 7)) * 8;
+    }
   }
-  const uint16_t* vt_head = a.vt + (int64_t)head * a.n_kv_tiles * HD * 64;
 
   auto issue_tile = [&](int t) __attribute__((always_inline)) {
     uint8_t* stage = smem + (t % NSTAGE) * C::STAGE_BYTES;
     const int64_t k0 = (int64_t)t * BKV;
+    if (k0 + BKV <= key_end) {  // whole tile inside the key range (wave-uniform)
 #pragma unroll
-    for (int i = 0; i < C::K_LOADS; ++i) {
-      const int64_t key = min(k0 + k_row[i], key_end - 1);
-      dma16(a.k + key * ld + hcol + k_col[i], stage + (i * NW + wave) * 1024);
+      for (int i = 0; i < C::K_LOADS; ++i) dma16(k_src[i] + k0 * ld, stage + (i * NW + wave) * 1024);
+    } else {                    // last tile: rows past the range re-read the last key (masked anyway)
+#pragma unroll
+      for (int i = 0; i < C::K_LOADS; ++i) {
+        const int64_t key = min(k0 + k_row[i], key_end - 1);
+        dma16(a.k + key * ld + hcol + k_col[i], stage + (i * NW + wave) * 1024);
+      }
     }
-    const uint16_t* vtile = vt_head + (int64_t)t * HD * 64;
 #pragma unroll
     for (int i = 0; i < C::V_LOADS; ++i)
-      dma16(vtile + v_off[i], stage + C::K_BYTES + (i * NW + wave) * 1024);
+      dma16(v_src[i] + (int64_t)t * HD * 64, stage + C::K_BYTES + (i * NW + wave) * 1024);
   };
 
   // ---- fragment read addresses (bytes within a stage).  K row r = kb*32 + ql,
   // logical chunk 2*kk + half, physical chunk (2*kk + half) ^ (r % NCH):
   // address = (row base | ((half ^ r%NCH) << 4)) ^ (kk << 5).  V^T row
-  // d = dt*32 + ql, chunk 2*ks + half: (row base | ((half ^ d%8) << 4)) ^ (ks << 5).
+  // d = dt*32 + ql (128 bytes), chunk 2*ks + half, physical chunk
+  // (2*ks + half) ^ ((d/2) % 8): with 64 LDS banks two consecutive rows cover
+  // all banks, so 16 lanes (rows d..d+15) then hit distinct banks.
   const uint32_t k_a0 = (uint32_t)ql * (HD * 2) + ((uint32_t)(half ^ (ql & (C::NCH - 1))) << 4);
-  const uint32_t v_a0 = C::K_BYTES + (uint32_t)ql * 128 + ((uint32_t)(half ^ (ql & 7)) << 4);
+  const uint32_t v_a0 = C::K_BYTES + (uint32_t)ql * 128 + ((uint32_t)(half ^ ((ql >> 1) & 7)) << 4);
 
+  // S^T for tile t: lane holds query ql, keys 8*(e/4) + 4*half + e%4 of each 32-key block.
   auto compute_s = [&](int t, f32x16 (&s)[2]) __attribute__((always_inline)) {
     const uint8_t* stage = smem + (t % NSTAGE) * C::STAGE_BYTES;
 #pragma unroll
@@ -239,10 +254,10 @@ __global__ __launch_bounds__(NTHREADS) void attn_kernel(const AttnArgs a) {
 #pragma unroll
   for (int dt = 0; dt < C::DT; ++dt) o[dt] = f32x16{};
 
-  // softmax of tile t (scores in s) and O^T += V^T(t) P^T(t)
-  auto softmax_pv = [&](int t, f32x16 (&s)[2]) __attribute__((always_inline)) {
+  // Causal mask of tile t's scores when the tile crosses the wave's diagonal.
+  auto mask_tile = [&](int t, f32x16 (&s)[2]) __attribute__((always_inline)) {
     const int64_t k0 = (int64_t)t * BKV;
-    if (k0 + BKV - 1 > wave_min_pos) {  // tile crosses the wave's diagonal (wave-uniform)
+    if (k0 + BKV - 1 > wave_min_pos) {  // wave-uniform
       // key k0 + kb*32 + 8*(e/4) + 4*half + e%4 is masked when it exceeds qpos,
       // i.e. when the lane-independent part kb*32 + 8*(e/4) + e%4 exceeds lim.
       const int lim = (int)min(max(qpos - k0, (int64_t)-1), (int64_t)BKV) - 4 * half;
@@ -252,53 +267,85 @@ __global__ __launch_bounds__(NTHREADS) void attn_kernel(const AttnArgs a) {
         for (int e = 0; e < 16; ++e)
           if (kb * 32 + 8 * (e >> 2) + (e & 3) > lim) s[kb][e] = -INFINITY;
     }
+  };
+
+  // Scaled row max of a tile's (masked) scores, combined over the lane pair.
+  auto tile_max = [&](f32x16 (&s)[2]) __attribute__((always_inline)) {
     float mx = -INFINITY;
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
       for (int e = 0; e < 16; ++e) mx = fmaxf(mx, s[kb][e]);
     mx = fmaxf(mx, __shfl_xor(mx, 32));
-    const float mt = mx * scale_log2;
-    if (__builtin_amdgcn_ballot_w64(mt > m_run + LAZY_TAU) != 0) {  // wave-uniform
-      const float m_new = fmaxf(m_run, mt);
-      const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
-      m_run = m_new;
-      l_run *= alpha;
-#pragma unroll
-      for (int dt = 0; dt < C::DT; ++dt) o[dt] *= alpha;
-    }
+    return mx * scale_log2;
+  };
+
+  // The fused block of a step: S of tile t+1 as two interleaved MFMA chains
+  // (the two 32-key blocks) over the head_dim steps, with the K fragments of
+  // the next step read before the current MFMAs and the exponentials of tile t
+  // spread over the steps; then PV of tile t as DT independent chains over the
+  // four 16-key steps, V^T fragments again one step ahead.  The order is
+  // written out so that LDS latency and vector work hide behind MFMAs.
+  auto fused_block = [&](int t, f32x16 (&s_cu)[2], f32x16 (&s_nx)[2]) __attribute__((always_inline)) {
+    const uint8_t* kst = smem + ((t + 1) % NSTAGE) * C::STAGE_BYTES;
+    const uint8_t* vst = smem + (t % NSTAGE) * C::STAGE_BYTES;
+    auto kfrag = [&](int kb, int kk) __attribute__((always_inline)) {
+      return *reinterpret_cast<const u32x4*>(kst + kb * 32 * (HD * 2) + (k_a0 ^ (uint32_t)(kk << 5)));
+    };
+    auto vfrag = [&](int dt, int ks) __attribute__((always_inline)) {
+      return *reinterpret_cast<const u32x4*>(vst + dt * 32 * 128 + (v_a0 ^ (uint32_t)(ks << 5)));
+    };
+    constexpr int PAIRS = 16 / C::KK;  // probability pairs per head_dim step
     const float neg_m = -m_run;
-    bf16x8 pf[4];
     float lsum = 0.0f;
+    uint32_t pk[16];  // bf16 pairs: pk[4*ks + j] holds keys of 16-key step ks
+    u32x4 a0 = kfrag(0, 0), a1 = kfrag(1, 0);
+    s_nx[0] = f32x16{};
+    s_nx[1] = f32x16{};
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb) {
-#pragma unroll
-      for (int g = 0; g < 2; ++g) {
-        u32x4 packed;
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          const float p0 = __builtin_amdgcn_exp2f(fmaf(s[kb][8 * g + 2 * j], scale_log2, neg_m));
-          const float p1 = __builtin_amdgcn_exp2f(fmaf(s[kb][8 * g + 2 * j + 1], scale_log2, neg_m));
-          lsum += p0 + p1;
-          packed[j] = pack_bf16x2(p0, p1);
-        }
-        pf[2 * kb + g] = as_bf16x8(packed);
+    for (int kk = 0; kk < C::KK; ++kk) {
+      u32x4 b0 = a0, b1 = a1;
+      if (kk + 1 < C::KK) {
+        b0 = kfrag(0, kk + 1);
+        b1 = kfrag(1, kk + 1);
       }
+      s_nx[0] = mfma32(as_bf16x8(a0), qf[kk], s_nx[0]);
+      s_nx[1] = mfma32(as_bf16x8(a1), qf[kk], s_nx[1]);
+#pragma unroll
+      for (int q = 0; q < PAIRS; ++q) {
+        const int idx = kk * PAIRS + q;  // pair of scores 2*idx, 2*idx+1 (kb = idx / 8)
+        const int kb = idx >> 3, e = (2 * idx) & 15;
+        const float p0 = __builtin_amdgcn_exp2f(fmaf(s_cu[kb][e], scale_log2, neg_m));
+        const float p1 = __builtin_amdgcn_exp2f(fmaf(s_cu[kb][e + 1], scale_log2, neg_m));
+        lsum += p0 + p1;
+        pk[idx] = pack_bf16x2(p0, p1);
+      }
+      a0 = b0;
+      a1 = b1;
     }
     l_run += lsum;
-    const uint8_t* stage = smem + (t % NSTAGE) * C::STAGE_BYTES;
+    u32x4 v[C::DT];
 #pragma unroll
-    for (int dt = 0; dt < C::DT; ++dt) {
+    for (int dt = 0; dt < C::DT; ++dt) v[dt] = vfrag(dt, 0);
 #pragma unroll
-      for (int ks = 0; ks < 4; ++ks) {
-        const u32x4 vf = *reinterpret_cast<const u32x4*>(stage + dt * 32 * 128 + (v_a0 ^ (uint32_t)(ks << 5)));
-        o[dt] = mfma32(as_bf16x8(vf), pf[ks], o[dt]);
-      }
+    for (int ks = 0; ks < 4; ++ks) {
+      u32x4 w[C::DT];
+#pragma unroll
+      for (int dt = 0; dt < C::DT; ++dt) w[dt] = ks + 1 < 4 ? vfrag(dt, ks + 1) : v[dt];
+      const bf16x8 p = as_bf16x8(u32x4{pk[4 * ks], pk[4 * ks + 1], pk[4 * ks + 2], pk[4 * ks + 3]});
+#pragma unroll
+      for (int dt = 0; dt < C::DT; ++dt) o[dt] = mfma32(as_bf16x8(v[dt]), p, o[dt]);
+#pragma unroll
+      for (int dt = 0; dt < C::DT; ++dt) v[dt] = w[dt];
     }
   };
 
-  // One pipeline step: make tile t+1 visible (and the stage of tile t-1 free),
-  // issue tile t+NSTAGE-1, then S(t+1) next to softmax(t) and PV(t).
+  // One pipeline step: make tile t+1 visible (and the stage of tile t-1 free);
+  // for tile t: mask, max and the rare lazy rescale (wave-uniform branches),
+  // then the fused block (S of tile t+1, exponentials and PV of tile t); last,
+  // issue the loads of tile t+NSTAGE-1 (issued after the compute, the loads do
+  // not hold up the wave's MFMAs).  The PV MFMAs still in flight overlap the
+  // next step's mask and max.
   auto step = [&](int t, f32x16 (&s_cu)[2], f32x16 (&s_nx)[2]) __attribute__((always_inline)) {
     if (t + 1 < n_tiles) {
       if (t + 2 < n_tiles)
@@ -307,9 +354,22 @@ __global__ __launch_bounds__(NTHREADS) void attn_kernel(const AttnArgs a) {
         wait_vmcnt<0>();
     }
     lds_barrier();
+    if (t < wave_tiles) {  // wave-uniform
+      mask_tile(t, s_cu);
+      const float mt = tile_max(s_cu);
+      if (__builtin_amdgcn_ballot_w64(mt > m_run + LAZY_TAU) != 0) {  // wave-uniform, rare
+        const float m_new = fmaxf(m_run, mt);
+        const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
+        m_run = m_new;
+        l_run *= alpha;
+#pragma unroll
+        for (int dt = 0; dt < C::DT; ++dt) o[dt] *= alpha;
+      }
+      // S of tile t+1 is computed even past the wave's last tile (it then reads
+      // a stale stage and is never used), keeping the block branch-free.
+      fused_block(t, s_cu, s_nx);
+    }
     if (t + NSTAGE - 1 < n_tiles) issue_tile(t + NSTAGE - 1);
-    if (t + 1 < wave_tiles) compute_s(t + 1, s_nx);
-    if (t < wave_tiles) softmax_pv(t, s_cu);
   };
 
   // ---- prologue: tiles 0 .. NSTAGE-2 in flight, wait for tile 0.
