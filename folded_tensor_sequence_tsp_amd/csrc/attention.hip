@@ -68,26 +68,6 @@ struct ACfg {
 // {4h..4h+3, 8+4h..8+4h+3} of each 16-key group, i.e. perm(8h + j), j = 0..7.
 __device__ __forceinline__ int key_perm16(int k) { return (k & 3) | ((k & 4) << 1) | ((k & 8) >> 1); }
 
-// s_waitcnt vmcnt(N) alone (expcnt and lgkmcnt left at their maxima).
-template <int N>
-__device__ __forceinline__ void wait_vmcnt() {
-  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | 0x0F70);
-}
-
-// Direct global->LDS load of 16 bytes per lane (global_load_lds_dwordx4): lane L
-// of the wave writes its 16 bytes at lds_block + 16 * L; lds_block is wave-uniform.
-__device__ __forceinline__ void dma16(const void* src, void* lds_block) {
-  __builtin_amdgcn_global_load_lds(const_cast<void*>(src), (__attribute__((address_space(3))) void*)lds_block, 16,
-                                   0, 0);
-}
-
-// Workgroup barrier that the compiler may not move memory operations across.
-__device__ __forceinline__ void lds_barrier() {
-  asm volatile("" ::: "memory");
-  __builtin_amdgcn_s_barrier();
-  asm volatile("" ::: "memory");
-}
-
 // V [S x ld] (head columns head*HD .. +HD-1) -> V^T tiles
 // vt[((head * n_kv_tiles + t) * HD + d) * 64 + k] = V[t*64 + key_perm16-order(k)][head*HD + d], 0 past S.
 // One thread moves 8 keys x 8 dims: eight 16-byte row reads, an 8x8 transpose

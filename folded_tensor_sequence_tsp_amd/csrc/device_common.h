@@ -76,4 +76,25 @@ __device__ __forceinline__ f32x16 mfma32_bits(const u32x4& a, const u32x4& b, co
     return mfma32(as_bf16x8(a), as_bf16x8(b), c);
 }
 
+// ---- direct global->LDS loads and their synchronisation (shared by the kernels).
+// s_waitcnt vmcnt(N) alone (expcnt and lgkmcnt left at their maxima).
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | 0x0F70);
+}
+
+// Direct global->LDS load of 16 bytes per lane (global_load_lds_dwordx4): lane L
+// of the wave writes its 16 bytes at lds_block + 16 * L; lds_block is wave-uniform.
+__device__ __forceinline__ void dma16(const void* src, void* lds_block) {
+  __builtin_amdgcn_global_load_lds(const_cast<void*>(src), (__attribute__((address_space(3))) void*)lds_block, 16,
+                                   0, 0);
+}
+
+// Workgroup barrier that the compiler may not move memory operations across.
+__device__ __forceinline__ void lds_barrier() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
 }  // namespace tsp

@@ -11,11 +11,14 @@
 //     fp32 accumulator held in registers, which is the local sum that stands
 //     in for tensor parallelism's all-reduce.
 //
-// Tiling: BM x BN x 64 block tile, 256 threads = 4 waves in a 2 x 2 grid, each
-// wave owning a (BM/2) x (BN/2) sub-tile of 32 x 32 MFMA tiles.  Global ->
-// register prefetch of the next K tile overlaps the MFMAs of the current one;
-// LDS is double-buffered (one barrier per K tile) and rows are padded by 16
-// bytes so the 16-byte fragment reads of 8 consecutive rows hit disjoint banks.
+// Tiling: BM x BN x 32 block tile; waves of WM x WN (256 x 256 tiles: eight
+// waves of 128 x 64, two per SIMD; 128 x 128 tiles: four waves of 64 x 64), each
+// a grid of 32 x 32 MFMA tiles.  A and B k-tiles stream into a 4-stage LDS ring
+// with direct global->LDS loads (global_load_lds_dwordx4, no register staging),
+// three k-tiles ahead, one vmcnt wait and one barrier per k-tile.  LDS rows are
+// 64 bytes (32 k values); the four 16-byte chunks of row r sit at chunk
+// positions c ^ ((r / 4) % 4), so the 16 lanes of one LDS cycle, reading 16
+// consecutive rows at one k offset, hit distinct banks of the 64-bank LDS.
 // Workgroup ids are remapped so each XCD (ids = x mod 8) gets a contiguous run
 // of tiles, then rasterised in groups of 8 tile rows for L2 reuse of B.
 #include "device_common.h"
@@ -24,17 +27,23 @@
 namespace tsp {
 namespace {
 
-constexpr int BK = 64;
-constexpr int LDK = BK + 8;  // padded LDS row, bf16 elements (144 bytes)
-constexpr int NTHREADS = 256;
+constexpr int BK = 32;       // k per tile: one 64-byte LDS row per operand row
+constexpr int STAGES = 4;    // LDS ring depth
 
 template <int BM, int BN>
 struct Cfg {
-  static constexpr int WM = BM / 2, WN = BN / 2;
+  static constexpr int WM = BM == 256 ? 128 : 64;  // wave tile
+  static constexpr int WN = 64;
+  static constexpr int WAVES_M = BM / WM, WAVES_N = BN / WN;
+  static constexpr int NW = WAVES_M * WAVES_N;
+  static constexpr int NT = 64 * NW;
   static constexpr int FM = WM / 32, FN = WN / 32;
-  static constexpr int A_CHUNKS = BM * BK / 8 / NTHREADS;  // 16-byte chunks per thread
-  static constexpr int B_CHUNKS = BN * BK / 8 / NTHREADS;
-  static constexpr int LDS_ELEMS = 2 * (BM + BN) * LDK;
+  static constexpr int A_BYTES = BM * BK * 2, B_BYTES = BN * BK * 2;
+  static constexpr int STAGE_BYTES = A_BYTES + B_BYTES;
+  static constexpr int A_LOADS = A_BYTES / (NT * 16), B_LOADS = B_BYTES / (NT * 16);  // per thread per k-tile
+  static constexpr int LOADS = A_LOADS + B_LOADS;
+  static constexpr int LDS_BYTES = STAGES * STAGE_BYTES;
+  static_assert(A_LOADS >= 1 && B_LOADS >= 1 && A_BYTES % (NT * 16) == 0 && B_BYTES % (NT * 16) == 0, "tile split");
 };
 
 // Epilogue of 8 consecutive output columns of one row (fp32 values v[0..7]):
@@ -106,16 +115,14 @@ __device__ __forceinline__ void store_row8(const GemmArgs& g, int nshard, int ro
 }
 
 template <int BM, int BN, int EPI, bool F16>
-__global__ __launch_bounds__(NTHREADS) void gemm_kernel(const GemmArgs g) {
+__global__ __launch_bounds__((Cfg<BM, BN>::NT)) void gemm_kernel(const GemmArgs g) {
   using C = Cfg<BM, BN>;
-  __shared__ __attribute__((aligned(16))) uint16_t lds[C::LDS_ELEMS];
-  uint16_t* As = lds;                 // [2][BM][LDK]
-  uint16_t* Bs = lds + 2 * BM * LDK;  // [2][BN][LDK]
+  __shared__ __attribute__((aligned(1024))) uint8_t smem[C::LDS_BYTES];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int wave = tid >> 6;
-  const int wm = wave >> 1, wn = wave & 1;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wm = wave / C::WAVES_N, wn = wave % C::WAVES_N;
 
   const int tiles_m = (g.M + BM - 1) / BM;
   const int tiles_n_shard = (g.N_s + BN - 1) / BN;
@@ -139,31 +146,29 @@ __global__ __launch_bounds__(NTHREADS) void gemm_kernel(const GemmArgs g) {
   const int kt_per_rep = kt_per_shard * reps;
   const int k_tiles = kt_per_rep * g.k_shards;
 
-  // Per-thread load coordinates: chunk c = i*256 + tid -> row c/8, 16-byte column c%8.
-  const int ld_row = tid >> 3;
-  const int ld_kc = (tid & 7) * 8;
-  constexpr int ROWS_PER_PASS = NTHREADS / 8;  // 32
-
-  int64_t a_off[C::A_CHUNKS];
+  // ---- direct-load sources.  Instruction i of wave w fills the 1 KB block
+  // (i*NW + w) of the A (or B) region: 16 rows of 64 bytes; lane L -> row
+  // L/4 of the block, physical chunk L%4 = logical chunk (L%4) ^ ((row/4)%4).
+  int64_t a_off[C::A_LOADS];
 #pragma unroll
-  for (int i = 0; i < C::A_CHUNKS; ++i) {
-    const int r = min(m0 + i * ROWS_PER_PASS + ld_row, g.M - 1);
-    a_off[i] = (int64_t)r * g.lda + ld_kc;
+  for (int i = 0; i < C::A_LOADS; ++i) {
+    const int r = (i * C::NW + wave) * 16 + lane / 4;
+    const int c = (lane & 3) ^ ((r >> 2) & 3);
+    a_off[i] = (int64_t)min(m0 + r, g.M - 1) * g.lda + c * 8;
   }
-  int64_t b_off[C::B_CHUNKS];
+  int64_t b_off[C::B_LOADS];
 #pragma unroll
-  for (int i = 0; i < C::B_CHUNKS; ++i) {
-    const int n = min(n0 + i * ROWS_PER_PASS + ld_row, g.N_s - 1);
-    b_off[i] = (int64_t)n * g.K_s + ld_kc;
+  for (int i = 0; i < C::B_LOADS; ++i) {
+    const int r = (i * C::NW + wave) * 16 + lane / 4;
+    const int c = (lane & 3) ^ ((r >> 2) & 3);
+    b_off[i] = (int64_t)min(n0 + r, g.N_s - 1) * g.K_s + c * 8;
   }
 
-  u32x4 ra[C::A_CHUNKS], rb[C::B_CHUNKS];
-  auto load_tile = [&](int t) {
+  auto issue_tile = [&](int t) __attribute__((always_inline)) {
     const int s = t / kt_per_rep;
     int kt = t - s * kt_per_rep;
     const bool lo = kt >= kt_per_shard;
     if (lo) kt -= kt_per_shard;
-    const uint16_t* abase = lo ? g.A_lo : g.A;
     int d;
     int64_t acol;
     if (g.k_shards > 1) {
@@ -174,19 +179,14 @@ __global__ __launch_bounds__(NTHREADS) void gemm_kernel(const GemmArgs g) {
       d = nshard;
       acol = kt * BK;
     }
-    const uint16_t* bp = g.B[d] + kt * BK;
+    const uint16_t* abase = (lo ? g.A_lo : g.A) + acol;
+    const uint16_t* bbase = g.B[d] + kt * BK;
+    uint8_t* stage = smem + (t % STAGES) * C::STAGE_BYTES;
 #pragma unroll
-    for (int i = 0; i < C::A_CHUNKS; ++i) ra[i] = *reinterpret_cast<const u32x4*>(abase + a_off[i] + acol);
+    for (int i = 0; i < C::A_LOADS; ++i) dma16(abase + a_off[i], stage + (i * C::NW + wave) * 1024);
 #pragma unroll
-    for (int i = 0; i < C::B_CHUNKS; ++i) rb[i] = *reinterpret_cast<const u32x4*>(bp + b_off[i]);
-  };
-  auto store_tile = [&](int buf) {
-#pragma unroll
-    for (int i = 0; i < C::A_CHUNKS; ++i)
-      *reinterpret_cast<u32x4*>(As + (buf * BM + i * ROWS_PER_PASS + ld_row) * LDK + ld_kc) = ra[i];
-#pragma unroll
-    for (int i = 0; i < C::B_CHUNKS; ++i)
-      *reinterpret_cast<u32x4*>(Bs + (buf * BN + i * ROWS_PER_PASS + ld_row) * LDK + ld_kc) = rb[i];
+    for (int i = 0; i < C::B_LOADS; ++i)
+      dma16(bbase + b_off[i], stage + C::A_BYTES + (i * C::NW + wave) * 1024);
   };
 
   f32x16 acc[C::FM][C::FN];
@@ -195,41 +195,59 @@ __global__ __launch_bounds__(NTHREADS) void gemm_kernel(const GemmArgs g) {
 #pragma unroll
     for (int j = 0; j < C::FN; ++j) acc[i][j] = f32x16{};
 
-  const int frag_row = lane & 31;
-  const int frag_k = (lane >> 5) * 8;
+  // ---- fragment reads: row r = (wave rows) + 32*i + lane%32, logical chunk
+  // 2*kk + lane/32, physical chunk (2*kk + lane/32) ^ ((r/4) % 4); the wave
+  // row offsets are multiples of 32, so (r/4) % 4 = ((lane%32)/4) % 4.
+  const int ql = lane & 31;
+  const uint32_t xr = (uint32_t)(((lane >> 5) ^ ((ql >> 2) & 3)) << 4);
+  const uint32_t a_row = (uint32_t)(wm * C::WM + ql) * 64;
+  const uint32_t b_row = (uint32_t)C::A_BYTES + (uint32_t)(wn * C::WN + ql) * 64;
 
-  load_tile(0);
-  store_tile(0);
-  __syncthreads();
-  for (int t = 0; t < k_tiles; ++t) {
-    const int buf = t & 1;
-    if (t + 1 < k_tiles) load_tile(t + 1);
-    const uint16_t* a_base = As + (buf * BM + wm * C::WM + frag_row) * LDK + frag_k;
-    const uint16_t* b_base = Bs + (buf * BN + wn * C::WN + frag_row) * LDK + frag_k;
+  auto compute_tile = [&](int t) __attribute__((always_inline)) {
+    const uint8_t* stage = smem + (t % STAGES) * C::STAGE_BYTES;
 #pragma unroll
     for (int kk = 0; kk < BK / 16; ++kk) {
+      const uint32_t kx = xr ^ (uint32_t)(kk << 5);
       u32x4 af[C::FM], bfv[C::FN];
 #pragma unroll
-      for (int i = 0; i < C::FM; ++i) af[i] = *reinterpret_cast<const u32x4*>(a_base + i * 32 * LDK + kk * 16);
+      for (int i = 0; i < C::FM; ++i) af[i] = *reinterpret_cast<const u32x4*>(stage + a_row + i * 32 * 64 + kx);
 #pragma unroll
-      for (int j = 0; j < C::FN; ++j) bfv[j] = *reinterpret_cast<const u32x4*>(b_base + j * 32 * LDK + kk * 16);
+      for (int j = 0; j < C::FN; ++j) bfv[j] = *reinterpret_cast<const u32x4*>(stage + b_row + j * 32 * 64 + kx);
 #pragma unroll
       for (int i = 0; i < C::FM; ++i)
 #pragma unroll
         for (int j = 0; j < C::FN; ++j) acc[i][j] = mfma32_bits<F16>(af[i], bfv[j], acc[i][j]);
     }
-    if (t + 1 < k_tiles) store_tile(buf ^ 1);
-    __syncthreads();
-  }
+  };
 
-  // Epilogue, staged through LDS (free after the last barrier of the K loop) so
-  // that global stores are 16-byte row segments.  The 32x32 accumulator layout:
-  // lane holds column (lane % 32) and rows 8*(e/4) + 4*(lane/32) + e%4 of its
-  // 16 values e.  Each wave stages one 32-row strip of its sub-tile at a time
-  // in fp32 ([32][WN + 4] floats), then reads it back as 8-column row pieces.
+  // ---- main loop: wait for tile t (tiles t+1, t+2 may still be in flight),
+  // barrier (tile t visible to all waves; everyone is done with tile t-1),
+  // compute tile t, then refill the stage of tile t-1 with tile t+3.
+  const int pro = min(STAGES - 1, k_tiles);
+  for (int t = 0; t < pro; ++t) issue_tile(t);
+  for (int t = 0; t < k_tiles; ++t) {
+    const int ahead = min(k_tiles - 1 - t, STAGES - 2);  // tiles issued after t
+    if (ahead >= 2)
+      wait_vmcnt<2 * C::LOADS>();
+    else if (ahead == 1)
+      wait_vmcnt<C::LOADS>();
+    else
+      wait_vmcnt<0>();
+    lds_barrier();
+    compute_tile(t);
+    if (t + STAGES - 1 < k_tiles) issue_tile(t + STAGES - 1);
+  }
+  wait_vmcnt<0>();
+  __syncthreads();
+
+  // Epilogue, staged through LDS (free after the barrier above) so that global
+  // stores are 16-byte row segments.  The 32x32 accumulator layout: lane holds
+  // column (lane % 32) and rows 8*(e/4) + 4*(lane/32) + e%4 of its 16 values e.
+  // Each wave stages one 32-row strip of its sub-tile at a time in fp32
+  // ([32][WN + 4] floats), then reads it back as 8-column row pieces.
   {
     constexpr int SLD = C::WN + 4;  // padded fp32 row
-    float* stage = reinterpret_cast<float*>(lds) + wave * 32 * SLD;
+    float* stage = reinterpret_cast<float*>(smem) + wave * 32 * SLD;
     const int col_l = lane & 31;
     const int row_l = 4 * (lane >> 5);
     constexpr int PIECES = 32 * (C::WN / 8);  // 8-column pieces in a strip
@@ -264,7 +282,7 @@ template <int BM, int BN>
 hipError_t launch_tiles(const GemmArgs& g, hipStream_t stream) {
   const int tiles_m = (g.M + BM - 1) / BM;
   const int tiles_n = ((g.N_s + BN - 1) / BN) * g.n_shards;
-  const dim3 grid(tiles_m * tiles_n), block(NTHREADS);
+  const dim3 grid(tiles_m * tiles_n), block(Cfg<BM, BN>::NT);
   // Instantiated: QKV (bf16), W1 + GELU (bf16 or fp16), O projection (bf16), W2 (fp16).
   switch (g.epilogue) {
     case EPI_QKV: hipLaunchKernelGGL((gemm_kernel<BM, BN, EPI_QKV, false>), grid, block, 0, stream, g); break;
