@@ -164,23 +164,21 @@ __global__ __launch_bounds__((Cfg<BM, BN>::NT)) void gemm_kernel(const GemmArgs 
     b_off[i] = (int64_t)min(n0 + r, g.N_s - 1) * g.K_s + c * 8;
   }
 
+  // Tiles are issued in order t = 0, 1, ...; the position of the next one
+  // (k-tile within the shard, part of A, shard step of the ring) is walked
+  // incrementally (wave-uniform scalars, no divisions).
+  int nx_kt = 0, nx_part = 0, nx_d = g.k_shards > 1 ? g.ring_start : nshard;
   auto issue_tile = [&](int t) __attribute__((always_inline)) {
-    const int s = t / kt_per_rep;
-    int kt = t - s * kt_per_rep;
-    const bool lo = kt >= kt_per_shard;
-    if (lo) kt -= kt_per_shard;
-    int d;
-    int64_t acol;
-    if (g.k_shards > 1) {
-      d = g.ring_start + s;
-      if (d >= g.k_shards) d -= g.k_shards;
-      acol = (int64_t)d * g.K_s + kt * BK;
-    } else {
-      d = nshard;
-      acol = kt * BK;
+    const int64_t acol = (g.k_shards > 1 ? (int64_t)nx_d * g.K_s : 0) + nx_kt * BK;
+    const uint16_t* abase = (nx_part ? g.A_lo : g.A) + acol;
+    const uint16_t* bbase = g.B[nx_d] + nx_kt * BK;
+    if (++nx_kt == kt_per_shard) {
+      nx_kt = 0;
+      if (++nx_part == reps) {
+        nx_part = 0;
+        if (g.k_shards > 1 && ++nx_d == g.k_shards) nx_d = 0;
+      }
     }
-    const uint16_t* abase = (lo ? g.A_lo : g.A) + acol;
-    const uint16_t* bbase = g.B[d] + kt * BK;
     uint8_t* stage = smem + (t % STAGES) * C::STAGE_BYTES;
 #pragma unroll
     for (int i = 0; i < C::A_LOADS; ++i) dma16(abase + a_off[i], stage + (i * C::NW + wave) * 1024);
@@ -203,21 +201,24 @@ __global__ __launch_bounds__((Cfg<BM, BN>::NT)) void gemm_kernel(const GemmArgs 
   const uint32_t a_row = (uint32_t)(wm * C::WM + ql) * 64;
   const uint32_t b_row = (uint32_t)C::A_BYTES + (uint32_t)(wn * C::WN + ql) * 64;
 
+  // Both k-steps' fragments are read before the first step's MFMAs.
   auto compute_tile = [&](int t) __attribute__((always_inline)) {
     const uint8_t* stage = smem + (t % STAGES) * C::STAGE_BYTES;
+    u32x4 af[2][C::FM], bfv[2][C::FN];
 #pragma unroll
     for (int kk = 0; kk < BK / 16; ++kk) {
       const uint32_t kx = xr ^ (uint32_t)(kk << 5);
-      u32x4 af[C::FM], bfv[C::FN];
 #pragma unroll
-      for (int i = 0; i < C::FM; ++i) af[i] = *reinterpret_cast<const u32x4*>(stage + a_row + i * 32 * 64 + kx);
+      for (int i = 0; i < C::FM; ++i) af[kk][i] = *reinterpret_cast<const u32x4*>(stage + a_row + i * 32 * 64 + kx);
 #pragma unroll
-      for (int j = 0; j < C::FN; ++j) bfv[j] = *reinterpret_cast<const u32x4*>(stage + b_row + j * 32 * 64 + kx);
+      for (int j = 0; j < C::FN; ++j) bfv[kk][j] = *reinterpret_cast<const u32x4*>(stage + b_row + j * 32 * 64 + kx);
+    }
+#pragma unroll
+    for (int kk = 0; kk < BK / 16; ++kk)
 #pragma unroll
       for (int i = 0; i < C::FM; ++i)
 #pragma unroll
-        for (int j = 0; j < C::FN; ++j) acc[i][j] = mfma32_bits<F16>(af[i], bfv[j], acc[i][j]);
-    }
+        for (int j = 0; j < C::FN; ++j) acc[i][j] = mfma32_bits<F16>(af[kk][i], bfv[kk][j], acc[i][j]);
   };
 
   // ---- main loop: wait for tile t (tiles t+1, t+2 may still be in flight),
