@@ -32,7 +32,7 @@ from folded_tensor_sequence_tsp_amd import profile_summary, synth, tsp
 ROOT = os.path.dirname(os.path.abspath(__file__))
 # rocprofv3 counter summary of the attention kernel on the default workload: its
 # traffic figure is used only while the kernel's sources are the ones profiled.
-TRAFFIC_SUMMARY = os.path.join(ROOT, "profiles", "attn_kernel_7b_128k_rank0.md")
+TRAFFIC_SUMMARY = os.path.join(ROOT, "profiles", "tsp_attn_core_7b_128k_rank0_32layers.md")
 
 PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
 PEAK_HBM_GBS = 8000.0        # MI355X HBM3E
@@ -192,11 +192,15 @@ def main():
     elapsed = time.perf_counter() - t0
 
     stage_ms = {k: 0.0 for k in stages}
+    first_ms = {k: 0.0 for k in stages}  # layer 0 alone: unit-scale activations
     for s in range(args.steps):
         for l in range(n_layers):
             ev = events[s][l]
             for i, k in enumerate(stages):
-                stage_ms[k] += ev[i].elapsed_time(ev[i + 1])
+                t = ev[i].elapsed_time(ev[i + 1])
+                stage_ms[k] += t
+                if l == 0:
+                    first_ms[k] += t / args.steps
     launches = args.steps * n_layers
     stage_ms = {k: v / launches for k, v in stage_ms.items()}   # ms per launch
     fl = layer_flops(n, S, D, plan.chunk_len, d)
@@ -232,8 +236,9 @@ def main():
         "layer_mfma_frac": round(total_flops / (layer_ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4),
         "stages_ms_per_launch": {k: round(v, 4) for k, v in stage_ms.items()},
         "stages_tflops": {k: round(fl[k] / (stage_ms[k] * 1e-3) / 1e12, 1) for k in stages},
+        "stages_ms_layer0": {k: round(v, 4) for k, v in first_ms.items()},
         "roofline": {
-            "kernel": "attn_kernel<128> (tsp_attn_core)",
+            "kernel": "tsp_attn_core (vt_prep_kernel + attn_kernel<128>)",
             "bound": "mfma",
             "achieved": round(attn_tflops, 1),
             "peak": PEAK_BF16_TFLOPS,
@@ -241,8 +246,9 @@ def main():
             "frac": round(attn_tflops / PEAK_BF16_TFLOPS, 4),
             "flops_per_launch": fl["attn"],
             "ms_per_launch": round(stage_ms["attn"], 4),
-            "traffic": profile_summary.read_traffic(TRAFFIC_SUMMARY, "attn_kernel"),
+            "traffic": profile_summary.read_traffic(TRAFFIC_SUMMARY, "tsp_attn_core"),
             "traffic_source": os.path.relpath(TRAFFIC_SUMMARY, ROOT),
+            "profile_ms_per_launch": profile_summary.read_avg_ms(TRAFFIC_SUMMARY, "tsp_attn_core"),
         },
         "cpu_baseline": None,
     }

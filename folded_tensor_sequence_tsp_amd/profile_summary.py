@@ -7,18 +7,22 @@ Reads the CSV output of three rocprofv3 runs of the same ``bench.py`` command:
 * ``--pmc FETCH_SIZE`` and ``--pmc WRITE_SIZE`` (``*_counter_collection.csv``):
   KiB per dispatch.
 
+A summary covers one unit: an entry point's kernels (``tsp_attn_core`` launches
+``vt_prep_kernel`` then ``attn_kernel``), whose per-launch durations and bytes
+are summed.
+
 The counter runs also hold a plain device copy of known size (``bench.py
 --copy-probe-mib``); the ratio of its true bytes to what each counter reads for
 it is the calibration factor applied to the other kernels' counts (on gfx950
 FETCH_SIZE reads about half of the bytes a copy moves, WRITE_SIZE all of them).
 
 The summary ends with machine-readable lines that ``bench.py`` reads:
-``traffic_bytes_per_launch`` of the chosen kernel and ``source_sha256`` of the
-sources it was built from, so that the traffic figure is dropped (null) as soon
-as the kernel's sources change.
+``avg_ms_per_launch`` and ``traffic_bytes_per_launch`` of the chosen unit and
+``source_sha256`` of the sources it was built from, so that the figures are
+dropped (null) as soon as the kernels' sources change.
 
     python -m folded_tensor_sequence_tsp_amd.profile_summary --trace DIR --fetch DIR --write DIR \\
-        --kernel attn_kernel --copy-mib 1024 --command "..." --out profiles/NAME.md
+        --kernel tsp_attn_core --copy-mib 1024 --command "..." --out profiles/NAME.md
 """
 from __future__ import annotations
 
@@ -31,11 +35,14 @@ import os
 PKG = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(PKG, "csrc")
 
-# Sources each summarised kernel is built from (hashed into the summary).
-KERNEL_SOURCES = {
-    "attn_kernel": ["attention.hip", "device_common.h", "kernels.h"],
-    "gemm_kernel": ["gemm.hip", "device_common.h", "kernels.h"],
+# Units a summary can cover: an entry point's kernels (matched by name prefix)
+# and the sources they are built from (hashed into the summary).
+UNITS = {
+    "tsp_attn_core": (["vt_prep_kernel", "attn_kernel"], ["attention.hip", "device_common.h", "kernels.h"]),
+    "attn_kernel": (["attn_kernel"], ["attention.hip", "device_common.h", "kernels.h"]),
+    "gemm_kernel": (["gemm_kernel"], ["gemm.hip", "device_common.h", "kernels.h"]),
 }
+KERNEL_SOURCES = {k: v[1] for k, v in UNITS.items()}
 
 
 def source_sha256(kernel: str) -> str:
@@ -76,17 +83,21 @@ def _copy_factor(cnt, copy_bytes: int) -> tuple:
     return copy_bytes / (vals[0] * 1024.0), vals[0]
 
 
-def summarise(trace, fetch, write, kernel, copy_mib, command, workload):
+def summarise(trace, fetch, write, unit, copy_mib, command, workload):
     stats = kernel_stats(trace)
     f, w = counters(fetch), counters(write)
     copy_bytes = copy_mib << 20
     ff, f_copy = _copy_factor(f, copy_bytes)
     wf, w_copy = _copy_factor(w, copy_bytes)
-    fk = [v for n, v in f.values() if kernel in n]
-    wk = [v for n, v in w.values() if kernel in n]
-    fetch_b = sum(fk) / len(fk) * 1024.0 * ff
-    write_b = sum(wk) / len(wk) * 1024.0 * wf
-    lines = [f"# rocprofv3 summary: {kernel}, {workload}", "",
+    kernels = UNITS[unit][0]
+    fetch_b = write_b = avg_ms = 0.0
+    for k in kernels:
+        fk = [v for n, v in f.values() if k in n]
+        wk = [v for n, v in w.values() if k in n]
+        fetch_b += sum(fk) / len(fk) * 1024.0 * ff
+        write_b += sum(wk) / len(wk) * 1024.0 * wf
+        avg_ms += sum(ms for n, _, ms, _ in stats if n.startswith(k))
+    lines = [f"# rocprofv3 summary: {unit} ({' + '.join(kernels)}), {workload}", "",
              "Commands (run from the repository root on the GPU; `-d`/`-o` name the output folders):", "",
              "```", *command.split(" ;; "), "```", "",
              "## Kernel time (--kernel-trace --stats)", "",
@@ -108,25 +119,45 @@ def summarise(trace, fetch, write, kernel, copy_mib, command, workload):
         seen.add(key)
         lines.append(f"| {key} | {v:.0f} | {w[d][1]:.0f} | {v * 1024 * ff:.4e} | {w[d][1] * 1024 * wf:.4e} |")
     lines += ["", "## Machine-readable (read by bench.py)", "",
-              f"kernel: {kernel}",
+              f"kernel: {unit}",
+              f"kernels: {', '.join(kernels)}",
+              f"avg_ms_per_launch: {avg_ms:.4f}",
               f"traffic_bytes_per_launch: {fetch_b + write_b:.0f}",
               f"fetch_bytes_per_launch: {fetch_b:.0f}",
               f"write_bytes_per_launch: {write_b:.0f}",
-              f"source_sha256: {source_sha256(kernel)}", ""]
+              f"source_sha256: {source_sha256(unit)}", ""]
     return "\n".join(lines)
 
 
-def read_traffic(path: str, kernel: str):
-    """traffic_bytes_per_launch from a summary, or None when it is missing or
-    was taken from other sources of the kernel than the current ones."""
-    if not os.path.exists(path):
-        return None
+def _machine_values(path: str) -> dict:
     vals = {}
     for line in open(path):
         if ":" in line and not line.startswith(("#", "|", " ")):
             k, v = line.split(":", 1)
             vals[k.strip()] = v.strip()
-    if vals.get("kernel") != kernel or vals.get("source_sha256") != source_sha256(kernel):
+    return vals
+
+
+def read_avg_ms(path: str, unit: str):
+    """avg_ms_per_launch of a summary (None when missing or taken from other sources)."""
+    if not os.path.exists(path):
+        return None
+    vals = _machine_values(path)
+    if vals.get("kernel") != unit or vals.get("source_sha256") != source_sha256(unit):
+        return None
+    try:
+        return float(vals["avg_ms_per_launch"])
+    except (KeyError, ValueError):
+        return None
+
+
+def read_traffic(path: str, unit: str):
+    """traffic_bytes_per_launch from a summary, or None when it is missing or
+    was taken from other sources of the kernels than the current ones."""
+    if not os.path.exists(path):
+        return None
+    vals = _machine_values(path)
+    if vals.get("kernel") != unit or vals.get("source_sha256") != source_sha256(unit):
         return None
     try:
         return float(vals["traffic_bytes_per_launch"])
@@ -139,7 +170,7 @@ def main():
     ap.add_argument("--trace", required=True)
     ap.add_argument("--fetch", required=True)
     ap.add_argument("--write", required=True)
-    ap.add_argument("--kernel", default="attn_kernel", choices=sorted(KERNEL_SOURCES))
+    ap.add_argument("--kernel", default="tsp_attn_core", choices=sorted(UNITS))
     ap.add_argument("--copy-mib", type=int, default=1024)
     ap.add_argument("--command", required=True, help="the profiling commands, separated by ' ;; '")
     ap.add_argument("--workload", required=True)
