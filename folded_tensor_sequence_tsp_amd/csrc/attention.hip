@@ -249,24 +249,26 @@ __global__ __launch_bounds__(NTHREADS) void attn_kernel(const AttnArgs a) {
     }
   };
 
-  // Scaled row max of a tile's (masked) scores, combined over the lane pair.
+  // Scaled row max of a tile's (masked) scores, combined over the lane pair
+  // (lanes l and l+32 hold the two halves of a query's keys).
   auto tile_max = [&](f32x16 (&s)[2]) __attribute__((always_inline)) {
     float mx = -INFINITY;
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
       for (int e = 0; e < 16; ++e) mx = fmaxf(mx, s[kb][e]);
-    mx = fmaxf(mx, __shfl_xor(mx, 32));
-    return mx * scale_log2;
+    return pair_max(mx) * scale_log2;
   };
 
   // The fused block of a step: S of tile t+1 as two interleaved MFMA chains
   // (the two 32-key blocks) over the head_dim steps, with the K fragments of
-  // the next step read before the current MFMAs and the exponentials of tile t
-  // spread over the steps; then PV of tile t as DT independent chains over the
-  // four 16-key steps, V^T fragments again one step ahead.  The order is
-  // written out so that LDS latency and vector work hide behind MFMAs.
-  auto fused_block = [&](int t, f32x16 (&s_cu)[2], f32x16 (&s_nx)[2]) __attribute__((always_inline)) {
+  // the next step read before the current MFMAs and the exponentials of tile
+  // t's keys 0..31 spread over the steps; then PV of tile t as DT independent
+  // chains over the four 16-key steps, V^T fragments again one step ahead, the
+  // exponentials of keys 32..63 under its first two steps.  The vector work is
+  // split so that each MFMA carries a few vector instructions (co-issued), and
+  // LDS latency hides behind MFMAs.
+  auto fused_block = [&](int t, f32x16 (&s_cu)[2], f32x16 (&s_nx)[2], float& mt) __attribute__((always_inline)) {
     const uint8_t* kst = smem + ((t + 1) % NSTAGE) * C::STAGE_BYTES;
     const uint8_t* vst = smem + (t % NSTAGE) * C::STAGE_BYTES;
     auto kfrag = [&](int kb, int kk) __attribute__((always_inline)) {
@@ -275,10 +277,18 @@ __global__ __launch_bounds__(NTHREADS) void attn_kernel(const AttnArgs a) {
     auto vfrag = [&](int dt, int ks) __attribute__((always_inline)) {
       return *reinterpret_cast<const u32x4*>(vst + dt * 32 * 128 + (v_a0 ^ (uint32_t)(ks << 5)));
     };
-    constexpr int PAIRS = 16 / C::KK;  // probability pairs per head_dim step
+    constexpr int PAIRS = 8 / C::KK;  // probability pairs of keys 0..31 per head_dim step
     const float neg_m = -m_run;
     float lsum = 0.0f;
     uint32_t pk[16];  // bf16 pairs: pk[4*ks + j] holds keys of 16-key step ks
+    // probabilities of the score pair idx (keys 2*idx, 2*idx+1 of the lane's order)
+    auto prob_pair = [&](int idx) __attribute__((always_inline)) {
+      const int kb = idx >> 3, e = (2 * idx) & 15;
+      const float p0 = __builtin_amdgcn_exp2f(fmaf(s_cu[kb][e], scale_log2, neg_m));
+      const float p1 = __builtin_amdgcn_exp2f(fmaf(s_cu[kb][e + 1], scale_log2, neg_m));
+      lsum += p0 + p1;
+      pk[idx] = pack_bf16x2(p0, p1);
+    };
     u32x4 a0 = kfrag(0, 0), a1 = kfrag(1, 0);
     s_nx[0] = f32x16{};
     s_nx[1] = f32x16{};
@@ -292,18 +302,10 @@ __global__ __launch_bounds__(NTHREADS) void attn_kernel(const AttnArgs a) {
       s_nx[0] = mfma32(as_bf16x8(a0), qf[kk], s_nx[0]);
       s_nx[1] = mfma32(as_bf16x8(a1), qf[kk], s_nx[1]);
 #pragma unroll
-      for (int q = 0; q < PAIRS; ++q) {
-        const int idx = kk * PAIRS + q;  // pair of scores 2*idx, 2*idx+1 (kb = idx / 8)
-        const int kb = idx >> 3, e = (2 * idx) & 15;
-        const float p0 = __builtin_amdgcn_exp2f(fmaf(s_cu[kb][e], scale_log2, neg_m));
-        const float p1 = __builtin_amdgcn_exp2f(fmaf(s_cu[kb][e + 1], scale_log2, neg_m));
-        lsum += p0 + p1;
-        pk[idx] = pack_bf16x2(p0, p1);
-      }
+      for (int q = 0; q < PAIRS; ++q) prob_pair(kk * PAIRS + q);  // keys 0..31
       a0 = b0;
       a1 = b1;
     }
-    l_run += lsum;
     u32x4 v[C::DT];
 #pragma unroll
     for (int dt = 0; dt < C::DT; ++dt) v[dt] = vfrag(dt, 0);
@@ -315,18 +317,26 @@ __global__ __launch_bounds__(NTHREADS) void attn_kernel(const AttnArgs a) {
       const bf16x8 p = as_bf16x8(u32x4{pk[4 * ks], pk[4 * ks + 1], pk[4 * ks + 2], pk[4 * ks + 3]});
 #pragma unroll
       for (int dt = 0; dt < C::DT; ++dt) o[dt] = mfma32(as_bf16x8(v[dt]), p, o[dt]);
+      if (ks < 2) {  // keys 32..63, needed from step 2 on, under the MFMAs of steps 0 and 1
+#pragma unroll
+        for (int q = 0; q < 4; ++q) prob_pair(8 + 4 * ks + q);
+      }
 #pragma unroll
       for (int dt = 0; dt < C::DT; ++dt) v[dt] = w[dt];
     }
+    l_run += lsum;
+    // mask and max of tile t+1, under the PV MFMAs
+    mask_tile(t + 1, s_nx);
+    mt = tile_max(s_nx);
   };
 
   // One pipeline step: make tile t+1 visible (and the stage of tile t-1 free);
-  // for tile t: mask, max and the rare lazy rescale (wave-uniform branches),
-  // then the fused block (S of tile t+1, exponentials and PV of tile t); last,
-  // issue the loads of tile t+NSTAGE-1 (issued after the compute, the loads do
-  // not hold up the wave's MFMAs).  The PV MFMAs still in flight overlap the
-  // next step's mask and max.
-  auto step = [&](int t, f32x16 (&s_cu)[2], f32x16 (&s_nx)[2]) __attribute__((always_inline)) {
+  // for tile t: the rare lazy rescale (a wave-uniform branch on the max mt of
+  // tile t, found in the previous step), then the fused block (S of tile t+1,
+  // exponentials and PV of tile t, then the mask and max of tile t+1 under the
+  // PV MFMAs); last, issue the loads of tile t+NSTAGE-1 (issued after the
+  // compute, the loads do not hold up the wave's MFMAs).
+  auto step = [&](int t, f32x16 (&s_cu)[2], f32x16 (&s_nx)[2], float& mt) __attribute__((always_inline)) {
     if (t + 1 < n_tiles) {
       if (t + 2 < n_tiles)
         wait_vmcnt<C::LOADS>();
@@ -335,8 +345,6 @@ __global__ __launch_bounds__(NTHREADS) void attn_kernel(const AttnArgs a) {
     }
     lds_barrier();
     if (t < wave_tiles) {  // wave-uniform
-      mask_tile(t, s_cu);
-      const float mt = tile_max(s_cu);
       if (__builtin_amdgcn_ballot_w64(mt > m_run + LAZY_TAU) != 0) {  // wave-uniform, rare
         const float m_new = fmaxf(m_run, mt);
         const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
@@ -347,7 +355,7 @@ __global__ __launch_bounds__(NTHREADS) void attn_kernel(const AttnArgs a) {
       }
       // S of tile t+1 is computed even past the wave's last tile (it then reads
       // a stale stage and is never used), keeping the block branch-free.
-      fused_block(t, s_cu, s_nx);
+      fused_block(t, s_cu, s_nx, mt);
     }
     if (t + NSTAGE - 1 < n_tiles) issue_tile(t + NSTAGE - 1);
   };
@@ -364,10 +372,15 @@ __global__ __launch_bounds__(NTHREADS) void attn_kernel(const AttnArgs a) {
   lds_barrier();
 
   f32x16 sA[2], sB[2];
-  if (wave_tiles > 0) compute_s(0, sA);
+  float mt = -INFINITY;  // scaled max of the current tile's masked scores
+  if (wave_tiles > 0) {
+    compute_s(0, sA);
+    mask_tile(0, sA);
+    mt = tile_max(sA);
+  }
   for (int t = 0; t < n_tiles; t += 2) {
-    step(t, sA, sB);
-    if (t + 1 < n_tiles) step(t + 1, sB, sA);
+    step(t, sA, sB, mt);
+    if (t + 1 < n_tiles) step(t + 1, sB, sA, mt);
   }
   wait_vmcnt<0>();
 

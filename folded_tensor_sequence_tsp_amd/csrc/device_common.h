@@ -76,6 +76,13 @@ __device__ __forceinline__ f32x16 mfma32_bits(const u32x4& a, const u32x4& b, co
     return mfma32(as_bf16x8(a), as_bf16x8(b), c);
 }
 
+// max of x over the lane pair (l, l xor 32), one v_permlane32_swap (gfx950):
+// with both operands x, the swap leaves (x_lo | x_lo) and (x_hi | x_hi).
+__device__ __forceinline__ float pair_max(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+
 // ---- direct global->LDS loads and their synchronisation (shared by the kernels).
 // s_waitcnt vmcnt(N) alone (expcnt and lgkmcnt left at their maxima).
 template <int N>
