@@ -15,6 +15,10 @@ The step calls the three entry points that tsp_layer_forward composes
 between them on the launch stream: the per-launch time of the attention kernel
 (the dominant one, about 73% of the layer's FLOPs) gives the roofline figure.
 
+After the timed steps, each step's entry point is also timed alone on layer
+0's inputs (``rows_layer0``: QKV projection, attention, O projection, MLP),
+each against the bf16 MFMA peak.
+
 Prints ONE JSON line.  ``--gpus`` above 1 is refused: this build runs on one GPU.
 """
 from __future__ import annotations
@@ -49,6 +53,41 @@ def layer_flops(n, S, D, C, d):
         "oproj": 2.0 * n * h * h,  # O projection
         "mlp": 4.0 * n * h * F,
     }
+
+
+def row_timings(plan, dims, D, layer0, x0, q, a, a_lo, out, ws_core, fl, dev, reps=3):
+    """Each hot-path step's entry point alone, on layer 0's inputs, after the
+    timed steps: ms per call, FLOP/s and the fraction of the bf16 MFMA peak.
+    The O projection's FLOPs are the algorithmic ones (it contracts the
+    attention output's hi and lo parts, twice that many are executed)."""
+    lw, kf, vf = layer0
+    n = plan.n_local
+    ws_mlp = tsp.alloc_workspace(n, dims, D, tsp.WS_MLP, device=dev)
+    calls = [
+        ("A2 qkv projection (tsp_attn_project)", "qkv",
+         lambda: tsp.attn_project(plan, dims, x0, lw.wqkv, kf, vf, q)),
+        ("A4 causal attention (tsp_attn_core)", "attn",
+         lambda: tsp.attn_core(plan, dims, q, kf, vf, a, a_lo, workspace=ws_core)),
+        ("A5 O projection, split-K + residual (tsp_attn_out)", "oproj",
+         lambda: tsp.attn_out(dims, D, plan.rank, a, lw.wo, x0, out, attn_lo=a_lo)),
+        ("A6+A7 MLP: W1+GELU, W2 ring split-K + residual (tsp_mlp_forward)", "mlp",
+         lambda: tsp.mlp_forward(dims, D, plan.rank, x0, lw.w1, lw.w2, x0, out, ws_mlp)),
+    ]
+    stream = torch.cuda.current_stream()
+    rows = {}
+    for name, key, f in calls:
+        f()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(reps):
+            f()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        ms = e0.elapsed_time(e1) / reps
+        tf = fl[key] / (ms * 1e-3) / 1e12
+        rows[name] = {"ms": round(ms, 4), "tflops": round(tf, 1), "frac": round(tf / PEAK_BF16_TFLOPS, 4)}
+    del ws_mlp
+    return rows
 
 
 def parse():
@@ -146,6 +185,7 @@ def main():
     a_lo = torch.empty(n, h, dtype=torch.bfloat16, device=dev)
     bufs = [torch.empty(n, h, dtype=torch.bfloat16, device=dev) for _ in range(2)]
     ws = tsp.alloc_workspace(n, dims, D, tsp.WS_POST)
+    ws_core = tsp.alloc_workspace(n, dims, D, tsp.WS_CORE)
     torch.cuda.synchronize()
 
     stream = torch.cuda.current_stream()
@@ -160,7 +200,7 @@ def main():
             if ev: ev[0].record(stream)
             tsp.attn_project(plan, dims, x, lw.wqkv, kf, vf, q)
             if ev: ev[1].record(stream)
-            tsp.attn_core(plan, dims, q, kf, vf, a, a_lo)
+            tsp.attn_core(plan, dims, q, kf, vf, a, a_lo, workspace=ws_core)
             if ev: ev[2].record(stream)
             tsp.layer_post(dims, D, plan.rank, a, x, lw.wo, lw.w1, lw.w2, out, ws, attn_lo=a_lo)
             if ev: ev[3].record(stream)
@@ -203,7 +243,8 @@ def main():
                     first_ms[k] += t / args.steps
     launches = args.steps * n_layers
     stage_ms = {k: v / launches for k, v in stage_ms.items()}   # ms per launch
-    fl = layer_flops(n, S, D, plan.chunk_len, d)
+    fl_rows = layer_flops(n, S, D, plan.chunk_len, d)
+    fl = dict(fl_rows)
     fl["post"] = fl.pop("oproj") + fl.pop("mlp")
 
     ms_per_step = elapsed * 1e3 / args.steps
@@ -252,6 +293,8 @@ def main():
         },
         "cpu_baseline": None,
     }
+    print("[bench] per-step timing on layer 0", file=sys.stderr, flush=True)
+    result["rows_layer0"] = row_timings(plan, dims, D, layers[0], x0, q, a, a_lo, bufs[0], ws_core, fl_rows, dev)
     if not args.no_cpu_baseline:
         print("[bench] cpu baseline (fp64 oracle, bounded sample)", file=sys.stderr, flush=True)
         result["cpu_baseline"] = cpu_baseline(W, plan, x0, layers[0], args.cpu_rows)
