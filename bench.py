@@ -17,7 +17,9 @@ between them on the launch stream: the per-launch time of the attention kernel
 
 After the timed steps, each step's entry point is also timed alone on layer
 0's inputs (``rows_layer0``: QKV projection, attention, O projection, MLP),
-each against the bf16 MFMA peak.
+each against the bf16 MFMA peak, and so are the shard-streaming forms of the
+projections and the MLP (the D ring steps called one by one, weights
+resident).
 
 Prints ONE JSON line.  ``--gpus`` above 1 is refused: this build runs on one GPU.
 """
@@ -63,6 +65,22 @@ def row_timings(plan, dims, D, layer0, x0, q, a, a_lo, out, ws_core, fl, dev, re
     lw, kf, vf = layer0
     n = plan.n_local
     ws_mlp = tsp.alloc_workspace(n, dims, D, tsp.WS_MLP, device=dev)
+    ws_mlp_s = tsp.alloc_workspace(n, dims, D, tsp.WS_MLP_SHARD, device=dev)
+    ws_out_s = tsp.alloc_workspace(n, dims, D, tsp.WS_OUT_SHARD, device=dev)
+    ring = [(plan.rank + k) % D for k in range(D)]
+
+    def project_streamed():
+        for s in ring:
+            tsp.attn_project_shard(plan, dims, s, x0, lw.wqkv[s], kf, vf, q)
+
+    def out_streamed():
+        for pos, s in enumerate(ring):
+            tsp.attn_out_shard(dims, D, pos, s, a, lw.wo[s], x0, out, ws_out_s, attn_lo=a_lo)
+
+    def mlp_streamed():
+        for pos, s in enumerate(ring):
+            tsp.mlp_shard(dims, D, pos, x0, lw.w1[s], lw.w2[s], x0, out, ws_mlp_s)
+
     calls = [
         ("A2 qkv projection (tsp_attn_project)", "qkv",
          lambda: tsp.attn_project(plan, dims, x0, lw.wqkv, kf, vf, q)),
@@ -72,6 +90,9 @@ def row_timings(plan, dims, D, layer0, x0, q, a, a_lo, out, ws_core, fl, dev, re
          lambda: tsp.attn_out(dims, D, plan.rank, a, lw.wo, x0, out, attn_lo=a_lo)),
         ("A6+A7 MLP: W1+GELU, W2 ring split-K + residual (tsp_mlp_forward)", "mlp",
          lambda: tsp.mlp_forward(dims, D, plan.rank, x0, lw.w1, lw.w2, x0, out, ws_mlp)),
+        ("A2 streamed: D x tsp_attn_project_shard", "qkv", project_streamed),
+        ("A5 streamed: D x tsp_attn_out_shard", "oproj", out_streamed),
+        ("A6+A7 streamed: D x tsp_mlp_shard", "mlp", mlp_streamed),
     ]
     stream = torch.cuda.current_stream()
     rows = {}
@@ -86,7 +107,7 @@ def row_timings(plan, dims, D, layer0, x0, q, a, a_lo, out, ws_core, fl, dev, re
         ms = e0.elapsed_time(e1) / reps
         tf = fl[key] / (ms * 1e-3) / 1e12
         rows[name] = {"ms": round(ms, 4), "tflops": round(tf, 1), "frac": round(tf / PEAK_BF16_TFLOPS, 4)}
-    del ws_mlp
+    del ws_mlp, ws_mlp_s, ws_out_s
     return rows
 
 

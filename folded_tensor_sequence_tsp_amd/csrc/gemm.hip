@@ -103,7 +103,7 @@ __device__ __forceinline__ void store_row8(const GemmArgs& g, int nshard, int ro
     for (int j = 0; j < 4; ++j) packed[j] = pack_bf16x2(v[2 * j], v[2 * j + 1]);
     const int hs_hd = g.heads_per_shard * g.head_dim;
     const int part = col >= 2 * hs_hd ? 2 : (col >= hs_hd ? 1 : 0);  // 0 = Q, 1 = K, 2 = V
-    const int gcol = nshard * hs_hd + (col - part * hs_hd);
+    const int gcol = (nshard + g.shard0) * hs_hd + (col - part * hs_hd);
     if (part == 0) {
       *reinterpret_cast<u32x4*>(g.q_out + (int64_t)row * g.hidden + gcol) = packed;
     } else {

@@ -51,6 +51,7 @@ struct GemmArgs {
   uint16_t* k_full;
   uint16_t* v_full;
   int32_t heads_per_shard, head_dim, hidden;
+  int32_t shard0;  // index of the launch's first weight shard (its Q/K/V column block)
   int64_t chunk_len, chunk_start0, chunk_start1;
 };
 

@@ -293,6 +293,50 @@ tsp_status run_post(int64_t n, const tsp_dims* dims, int32_t D, int32_t start, c
   return run_mlp_core(n, dims, D, start, h16, true, w1h_shards, w2h, row_exp, h1, true, out, hbuf, stream);
 }
 
+// ---- shard streaming ---------------------------------------------------------
+
+// O projection ring step: the fp32 accumulator [n x h].
+size_t ws_out_shard(int64_t n, const tsp_dims* d) { return round_up((size_t)n * d->hidden * 4); }
+
+// MLP ring step: fp32 accumulator, row exponents, the fp16 copy of W2_d and the
+// fp16 GELU block of the shard (F_s columns).
+struct MlpShardWs {
+  size_t acc_off, exp_off, w2_off, h_off, total;
+};
+
+MlpShardWs mlp_shard_ws(int64_t n, const tsp_dims* d, int32_t D) {
+  const int64_t mb = n < MLP_TOKEN_BLOCK ? n : MLP_TOKEN_BLOCK;
+  const int64_t fs = d->ffn / D;
+  MlpShardWs w;
+  w.acc_off = 0;
+  w.exp_off = round_up((size_t)n * d->hidden * 4);
+  w.w2_off = w.exp_off + round_up((size_t)n * 4);
+  w.h_off = w.w2_off + round_up((size_t)d->hidden * fs * 2);
+  w.total = w.h_off + round_up((size_t)mb * fs * 2);
+  return w;
+}
+
+// Residual and output of ring step pos of D: the caller's residual (bf16,
+// nullable) at the first step, else the fp32 accumulator; the caller's bf16
+// output at the last step, else the accumulator.
+void ring_io(GemmArgs& g, int32_t D, int32_t pos, const uint16_t* residual, uint16_t* out, float* acc,
+             int64_t row0, int64_t ld) {
+  if (pos == 0) {
+    g.residual = residual ? (const void*)(residual + row0 * ld) : nullptr;
+    g.res_f32 = 0;
+  } else {
+    g.residual = acc + row0 * ld;
+    g.res_f32 = 1;
+  }
+  if (pos == D - 1) {
+    g.out = out + row0 * ld;
+    g.out_f32 = 0;
+  } else {
+    g.out = acc + row0 * ld;
+    g.out_f32 = 1;
+  }
+}
+
 }  // namespace
 
 extern "C" {
@@ -344,6 +388,12 @@ size_t tsp_workspace_size(int64_t n_tokens, const tsp_dims* dims, int32_t D, int
     case TSP_WS_POST:
       if (check_dims(dims, D, true, true) != TSP_OK) return 0;
       return post_ws(n_tokens, dims).total;
+    case TSP_WS_OUT_SHARD:
+      if (check_dims(dims, D, true, false) != TSP_OK) return 0;
+      return ws_out_shard(n_tokens, dims);
+    case TSP_WS_MLP_SHARD:
+      if (check_dims(dims, D, false, true) != TSP_OK) return 0;
+      return mlp_shard_ws(n_tokens, dims, D).total;
     default:
       return 0;
   }
@@ -482,6 +532,138 @@ tsp_status tsp_layer_post(int64_t n_tokens, const tsp_dims* dims, int32_t D, int
   if (!aligned16(workspace)) return TSP_ERR_ALIGNMENT;
   if (ws_bytes < post_ws(n_tokens, dims).total) return TSP_ERR_WORKSPACE;
   return run_post(n_tokens, dims, D, start_shard, attn, attn_lo, x, wo, w1, w2, out, workspace, stream);
+}
+
+tsp_status tsp_attn_project_shard(const tsp_plan* plan, const tsp_dims* dims, int32_t shard,
+                                  const uint16_t* x_local, const uint16_t* wqkv_d, uint16_t* k_full,
+                                  uint16_t* v_full, uint16_t* q_out, hipStream_t stream) {
+  tsp_status s;
+  if ((s = check_plan(plan)) != TSP_OK) return s;
+  if ((s = check_dims(dims, plan->D, true, false)) != TSP_OK) return s;
+  if (shard < 0 || shard >= plan->D) return TSP_ERR_INVALID_ARG;
+  if ((s = check_ptr(x_local)) != TSP_OK || (s = check_ptr(wqkv_d)) != TSP_OK ||
+      (s = check_ptr(k_full)) != TSP_OK || (s = check_ptr(v_full)) != TSP_OK || (s = check_ptr(q_out)) != TSP_OK)
+    return s;
+  GemmArgs g{};
+  g.A = x_local;
+  g.lda = dims->hidden;
+  g.B[0] = wqkv_d;
+  const int hs = dims->n_heads / plan->D;
+  g.M = (int32_t)plan->n_local;
+  g.N_s = 3 * hs * dims->head_dim;
+  g.K_s = dims->hidden;
+  g.n_shards = 1;
+  g.k_shards = 1;
+  g.epilogue = EPI_QKV;
+  g.q_out = q_out;
+  g.k_full = k_full;
+  g.v_full = v_full;
+  g.heads_per_shard = hs;
+  g.head_dim = dims->head_dim;
+  g.hidden = dims->hidden;
+  g.shard0 = shard;
+  g.chunk_len = plan->chunk_len;
+  g.chunk_start0 = plan->chunk_start[0];
+  g.chunk_start1 = plan->chunk_start[1];
+  return from_hip(launch_gemm(g, stream));
+}
+
+tsp_status tsp_attn_out_shard(int64_t n_tokens, const tsp_dims* dims, int32_t D, int32_t pos, int32_t shard,
+                              const uint16_t* attn, const uint16_t* attn_lo, const uint16_t* wo_d,
+                              const uint16_t* residual, uint16_t* out, void* workspace, size_t ws_bytes,
+                              hipStream_t stream) {
+  tsp_status s;
+  if ((s = check_dims(dims, D, true, false)) != TSP_OK) return s;
+  if (n_tokens < 0) return TSP_ERR_SHAPE;
+  if (n_tokens > INT32_MAX) return TSP_ERR_UNSUPPORTED;
+  if (pos < 0 || pos >= D || shard < 0 || shard >= D) return TSP_ERR_INVALID_ARG;
+  if ((s = check_ptr(attn)) != TSP_OK || (s = check_ptr_nullable(attn_lo)) != TSP_OK ||
+      (s = check_ptr(wo_d)) != TSP_OK || (s = check_ptr_nullable(residual)) != TSP_OK ||
+      (s = check_ptr(out)) != TSP_OK)
+    return s;
+  if (out == attn || (attn_lo && out == attn_lo)) return TSP_ERR_INVALID_ARG;
+  if (!workspace) return TSP_ERR_WORKSPACE;
+  if (!aligned16(workspace)) return TSP_ERR_ALIGNMENT;
+  if (ws_bytes < ws_out_shard(n_tokens, dims)) return TSP_ERR_WORKSPACE;
+  if (n_tokens == 0) return TSP_OK;
+  const int32_t ks = (dims->n_heads / D) * dims->head_dim;
+  GemmArgs g{};
+  g.A = attn + (int64_t)shard * ks;
+  g.A_lo = attn_lo ? attn_lo + (int64_t)shard * ks : nullptr;
+  g.lda = dims->hidden;
+  g.B[0] = wo_d;
+  g.M = (int32_t)n_tokens;
+  g.N_s = dims->hidden;
+  g.K_s = ks;
+  g.n_shards = 1;
+  g.k_shards = 1;
+  g.epilogue = EPI_RESID;
+  g.ldo = dims->hidden;
+  ring_io(g, D, pos, residual, out, static_cast<float*>(workspace), 0, dims->hidden);
+  return from_hip(launch_gemm(g, stream));
+}
+
+tsp_status tsp_mlp_shard(int64_t n_tokens, const tsp_dims* dims, int32_t D, int32_t pos, const uint16_t* x,
+                         const uint16_t* w1_d, const uint16_t* w2_d, const uint16_t* residual, uint16_t* y,
+                         void* workspace, size_t ws_bytes, hipStream_t stream) {
+  tsp_status s;
+  if ((s = check_dims(dims, D, false, true)) != TSP_OK) return s;
+  if (n_tokens < 0) return TSP_ERR_SHAPE;
+  if (n_tokens > INT32_MAX) return TSP_ERR_UNSUPPORTED;
+  if (pos < 0 || pos >= D) return TSP_ERR_INVALID_ARG;
+  if ((s = check_ptr(x)) != TSP_OK || (s = check_ptr(w1_d)) != TSP_OK || (s = check_ptr(w2_d)) != TSP_OK ||
+      (s = check_ptr_nullable(residual)) != TSP_OK || (s = check_ptr(y)) != TSP_OK)
+    return s;
+  if (y == x) return TSP_ERR_INVALID_ARG;
+  if (!workspace) return TSP_ERR_WORKSPACE;
+  if (!aligned16(workspace)) return TSP_ERR_ALIGNMENT;
+  const MlpShardWs lay = mlp_shard_ws(n_tokens, dims, D);
+  if (ws_bytes < lay.total) return TSP_ERR_WORKSPACE;
+  if (n_tokens == 0) return TSP_OK;
+  char* base = static_cast<char*>(workspace);
+  float* acc = reinterpret_cast<float*>(base + lay.acc_off);
+  int32_t* row_exp = reinterpret_cast<int32_t*>(base + lay.exp_off);
+  uint16_t* w2h = reinterpret_cast<uint16_t*>(base + lay.w2_off);
+  uint16_t* hbuf = reinterpret_cast<uint16_t*>(base + lay.h_off);
+  const int64_t h = dims->hidden;
+  const int32_t fs = dims->ffn / D;
+  if (pos == 0 && (s = from_hip(launch_row_prep(x, 0, n_tokens, dims->hidden, row_exp, nullptr, stream))) != TSP_OK)
+    return s;
+  const uint16_t* w2_one[1] = {w2_d};
+  if ((s = from_hip(launch_bf16_to_f16(w2_one, w2h, 1, h * fs, stream))) != TSP_OK) return s;
+  for (int64_t b0 = 0; b0 < n_tokens; b0 += MLP_TOKEN_BLOCK) {
+    const int64_t mb = (n_tokens - b0) < MLP_TOKEN_BLOCK ? (n_tokens - b0) : MLP_TOKEN_BLOCK;
+    GemmArgs g1{};
+    g1.A = x + b0 * h;
+    g1.lda = h;
+    g1.B[0] = w1_d;
+    g1.M = (int32_t)mb;
+    g1.N_s = fs;
+    g1.K_s = (int32_t)h;
+    g1.n_shards = 1;
+    g1.k_shards = 1;
+    g1.epilogue = EPI_GELU;
+    g1.out = hbuf;
+    g1.ldo = fs;
+    g1.row_exp = row_exp + b0;
+    if ((s = from_hip(launch_gemm(g1, stream))) != TSP_OK) return s;
+    GemmArgs g2{};
+    g2.f16 = 1;
+    g2.A = hbuf;
+    g2.lda = fs;
+    g2.B[0] = w2h;
+    g2.M = (int32_t)mb;
+    g2.N_s = (int32_t)h;
+    g2.K_s = fs;
+    g2.n_shards = 1;
+    g2.k_shards = 1;
+    g2.epilogue = EPI_RESID;
+    g2.ldo = h;
+    g2.row_exp = row_exp + b0;
+    ring_io(g2, D, pos, residual, y, acc, b0, h);
+    if ((s = from_hip(launch_gemm(g2, stream))) != TSP_OK) return s;
+  }
+  return TSP_OK;
 }
 
 const char* tsp_status_string(tsp_status status) {

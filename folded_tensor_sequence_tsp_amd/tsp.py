@@ -18,11 +18,12 @@ import torch
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libtsp.so")
 
 TSP_OK, TSP_ERR_INVALID_ARG, TSP_ERR_SHAPE, TSP_ERR_ALIGNMENT, TSP_ERR_WORKSPACE, TSP_ERR_UNSUPPORTED, TSP_ERR_HIP = range(7)
-WS_ATTN, WS_MLP, WS_LAYER, WS_POST, WS_CORE = 0, 1, 2, 3, 4
+WS_ATTN, WS_MLP, WS_LAYER, WS_POST, WS_CORE, WS_OUT_SHARD, WS_MLP_SHARD = 0, 1, 2, 3, 4, 5, 6
 MAX_D = 16
 
 EXPORTS = ["tsp_zigzag_plan", "tsp_workspace_size", "tsp_attn_project", "tsp_attn_core", "tsp_attn_out",
-           "tsp_attn_forward", "tsp_mlp_forward", "tsp_layer_post", "tsp_layer_forward", "tsp_status_string"]
+           "tsp_attn_forward", "tsp_mlp_forward", "tsp_layer_post", "tsp_layer_forward", "tsp_attn_project_shard",
+           "tsp_attn_out_shard", "tsp_mlp_shard", "tsp_status_string"]
 
 
 class TSPError(RuntimeError):
@@ -61,6 +62,9 @@ def lib() -> ctypes.CDLL:
             "tsp_mlp_forward": [c_int64, POINTER(Dims), c_int32, c_int32, P, PP, PP, P, P, P, c_size_t, P],
             "tsp_layer_post": [c_int64, POINTER(Dims), c_int32, c_int32, P, P, P, PP, PP, PP, P, P, c_size_t, P],
             "tsp_layer_forward": [POINTER(Plan), POINTER(Dims), P, PP, PP, PP, PP, P, P, P, P, c_size_t, P],
+            "tsp_attn_project_shard": [POINTER(Plan), POINTER(Dims), c_int32, P, P, P, P, P, P],
+            "tsp_attn_out_shard": [c_int64, POINTER(Dims), c_int32, c_int32, c_int32, P, P, P, P, P, P, c_size_t, P],
+            "tsp_mlp_shard": [c_int64, POINTER(Dims), c_int32, c_int32, P, P, P, P, P, P, c_size_t, P],
             "tsp_status_string": [c_int32],
         }
         for name, args in sig.items():
@@ -229,6 +233,40 @@ def layer_forward(plan: Plan, dims: Dims, x_local, wqkv, wo, w1, w2, k_full, v_f
             _dev_tensor(v_full, (S, h), "v_full"), _dev_tensor(out, (n, h), "out"))
     _check(lib().tsp_layer_forward(ctypes.byref(plan), ctypes.byref(dims), *args, ws, nbytes, _stream(stream)),
            "tsp_layer_forward")
+
+
+# ---- shard streaming: one ring step per call (see include/tsp.h)
+def attn_project_shard(plan: Plan, dims: Dims, shard: int, x_local, wqkv_d, k_full, v_full, q_out, stream=None):
+    n, h, S, D = plan.n_local, dims.hidden, plan.seq_len, plan.D
+    Hs = dims.n_heads // D if D > 0 else 0
+    args = (_dev_tensor(x_local, (n, h), "x_local"), _dev_tensor(wqkv_d, (3 * Hs * dims.head_dim, h), "wqkv_d"),
+            _dev_tensor(k_full, (S, h), "k_full"), _dev_tensor(v_full, (S, h), "v_full"),
+            _dev_tensor(q_out, (n, h), "q_out"))
+    _check(lib().tsp_attn_project_shard(ctypes.byref(plan), ctypes.byref(dims), shard, *args, _stream(stream)),
+           "tsp_attn_project_shard")
+
+
+def attn_out_shard(dims: Dims, D: int, pos: int, shard: int, attn, wo_d, residual, out, workspace, attn_lo=None,
+                   stream=None):
+    n, h = attn.shape[0], dims.hidden
+    Hs = dims.n_heads // D if D > 0 else 0
+    need = workspace_size(n, dims, D, WS_OUT_SHARD)
+    ws, nbytes = _workspace(workspace, need)
+    args = (_dev_tensor(attn, (n, h), "attn"), _opt_tensor(attn_lo, (n, h), "attn_lo"),
+            _dev_tensor(wo_d, (h, Hs * dims.head_dim), "wo_d"), _opt_tensor(residual, (n, h), "residual"),
+            _dev_tensor(out, (n, h), "out"))
+    _check(lib().tsp_attn_out_shard(n, ctypes.byref(dims), D, pos, shard, *args, ws, nbytes, _stream(stream)),
+           "tsp_attn_out_shard")
+
+
+def mlp_shard(dims: Dims, D: int, pos: int, x, w1_d, w2_d, residual, y, workspace, stream=None):
+    n, h = x.shape[0], dims.hidden
+    Fs = dims.ffn // D if D > 0 else 0
+    need = workspace_size(n, dims, D, WS_MLP_SHARD)
+    ws, nbytes = _workspace(workspace, need)
+    args = (_dev_tensor(x, (n, h), "x"), _dev_tensor(w1_d, (Fs, h), "w1_d"), _dev_tensor(w2_d, (h, Fs), "w2_d"),
+            _opt_tensor(residual, (n, h), "residual"), _dev_tensor(y, (n, h), "y"))
+    _check(lib().tsp_mlp_shard(n, ctypes.byref(dims), D, pos, *args, ws, nbytes, _stream(stream)), "tsp_mlp_shard")
 
 
 def alloc_workspace(n_tokens: int, dims: Dims, D: int, kind: int, device=None) -> torch.Tensor:

@@ -78,7 +78,15 @@ typedef struct {
 } tsp_dims;
 
 /* Workspace kinds for tsp_workspace_size(). */
-typedef enum { TSP_WS_ATTN = 0, TSP_WS_MLP = 1, TSP_WS_LAYER = 2, TSP_WS_POST = 3, TSP_WS_CORE = 4 } tsp_ws_kind;
+typedef enum {
+  TSP_WS_ATTN = 0,
+  TSP_WS_MLP = 1,
+  TSP_WS_LAYER = 2,
+  TSP_WS_POST = 3,
+  TSP_WS_CORE = 4,
+  TSP_WS_OUT_SHARD = 5,
+  TSP_WS_MLP_SHARD = 6
+} tsp_ws_kind;
 
 /*
  * Zigzag plan (zubnet.ai TSP page, para. 2: K/V are gathered over a zigzag
@@ -101,8 +109,12 @@ tsp_status tsp_zigzag_plan(int64_t seq_len, int32_t D, int32_t rank, tsp_plan* p
  * Bytes of workspace that tsp_attn_forward (TSP_WS_ATTN), tsp_mlp_forward
  * (TSP_WS_MLP), tsp_layer_forward (TSP_WS_LAYER), tsp_layer_post (TSP_WS_POST)
  * or tsp_attn_core (TSP_WS_CORE) need for n_tokens local tokens (the kinds
- * that hold attention state size it for a sequence of D * n_tokens keys).  Returns 0 for invalid dims or
- * kind.  Workspace contents are scratch: nothing persists between calls.
+ * that hold attention state size it for a sequence of D * n_tokens keys), and
+ * the shard-streaming calls tsp_attn_out_shard (TSP_WS_OUT_SHARD) and
+ * tsp_mlp_shard (TSP_WS_MLP_SHARD).  Returns 0 for invalid dims or kind.
+ * Workspace contents are scratch: nothing persists between calls, except the
+ * fp32 accumulator (and row exponents) that the D calls of one ring of a
+ * shard-streaming entry point pass from step to step.
  */
 size_t tsp_workspace_size(int64_t n_tokens, const tsp_dims* dims, int32_t D, int32_t kind);
 
@@ -235,6 +247,76 @@ tsp_status tsp_layer_forward(const tsp_plan* plan, const tsp_dims* dims, const u
                              const uint16_t* const* w1, const uint16_t* const* w2,
                              uint16_t* k_full, uint16_t* v_full, uint16_t* out, void* workspace,
                              size_t ws_bytes, hipStream_t stream);
+
+/*
+ * ---- Shard streaming (the ring one shard at a time) ----
+ * In TSP the weight shards of a layer reach a device one after another (para. 2:
+ * the MLP's shard pairs travel a ring, the attention weights are broadcast).
+ * The calls below do the work of one shard, so that a caller can start each
+ * shard's compute as soon as that shard has arrived: make the stream wait for
+ * the shard's arrival (hipStreamWaitEvent on the event recorded after its
+ * copy) before the call.  The D calls of one ring go on one stream, in ring
+ * order; they run the same kernels as the all-shard calls.
+ *
+ * tsp_attn_project_shard: the QKV projection of head shard `shard` alone
+ * (tsp_attn_project restricted to d = shard): Q columns of the shard's heads,
+ * and the shard's K/V columns of the rank's own rows of k_full / v_full.
+ * Results are bit-identical to tsp_attn_project's for those columns.
+ *   shard : 0 <= shard < plan->D.   wqkv_d: device, bf16 [3 * H_s * head_dim x hidden].
+ *   Other arguments and errors as tsp_attn_project.
+ */
+tsp_status tsp_attn_project_shard(const tsp_plan* plan, const tsp_dims* dims, int32_t shard,
+                                  const uint16_t* x_local, const uint16_t* wqkv_d, uint16_t* k_full,
+                                  uint16_t* v_full, uint16_t* q_out, hipStream_t stream);
+
+/*
+ * Step `pos` of the O projection's ring (tsp_attn_out one shard at a time):
+ *   acc  = [residual +] attn[:, heads of shard] W_o_shard^T          (pos == 0)
+ *   acc += attn[:, heads of shard] W_o_shard^T                       (0 < pos < D-1)
+ *   out  = bf16(acc + attn[:, heads of shard] W_o_shard^T)           (pos == D-1)
+ * acc is fp32 [n_tokens x hidden] at the start of the workspace; with D == 1
+ * the single step reads the residual and writes out.  The ring order is the
+ * order of the calls: for tsp_attn_out's order, call pos = 0..D-1 with
+ * shard = (start_shard + pos) mod D.  Each step's partial product is summed in
+ * fp32 registers over its K range and added to acc in fp32, so the result
+ * differs from tsp_attn_out's only in fp32 rounding order.
+ *   pos, shard : 0 <= pos, shard < D.
+ *   attn, attn_lo, residual, out : as tsp_attn_out (residual is read at pos 0,
+ *                 out written at pos D-1; out may alias residual).
+ *   wo_d      : device, bf16 [hidden x H_s * head_dim].
+ *   workspace : >= tsp_workspace_size(n_tokens, dims, D, TSP_WS_OUT_SHARD) bytes,
+ *               the same buffer for the D steps of one ring.
+ * Errors: as tsp_attn_out, plus TSP_ERR_INVALID_ARG for pos or shard out of
+ * range, TSP_ERR_WORKSPACE for a missing or short workspace.
+ */
+tsp_status tsp_attn_out_shard(int64_t n_tokens, const tsp_dims* dims, int32_t D, int32_t pos, int32_t shard,
+                              const uint16_t* attn, const uint16_t* attn_lo, const uint16_t* wo_d,
+                              const uint16_t* residual, uint16_t* out, void* workspace, size_t ws_bytes,
+                              hipStream_t stream);
+
+/*
+ * Step `pos` of the MLP ring (tsp_mlp_forward one shard pair at a time):
+ *   H    = GELU_tanh(x W1_d^T)                  (fp16, rows scaled as in tsp_mlp_forward)
+ *   acc  = [residual +] H W2_d^T    (pos == 0; also computes the row exponents of x)
+ *   acc += H W2_d^T                 (0 < pos < D-1)
+ *   y    = bf16(acc + H W2_d^T)     (pos == D-1)
+ * with acc fp32 [n_tokens x hidden] and the row exponents in the workspace.
+ * The shard index itself is not needed: a shard pair's contribution does not
+ * depend on which pair it is; the ring order is the order of the calls.
+ * Precision as tsp_mlp_forward; the result differs from it only in fp32
+ * rounding order.
+ *   pos       : 0 <= pos < D.
+ *   x         : device, bf16 [n_tokens x hidden], the same for the D steps.
+ *   w1_d      : device, bf16 [ffn/D x hidden];  w2_d: device, bf16 [hidden x ffn/D].
+ *   residual  : nullable, read at pos 0.  y: written at pos D-1; may alias
+ *               residual, must not alias x.
+ *   workspace : >= tsp_workspace_size(n_tokens, dims, D, TSP_WS_MLP_SHARD) bytes,
+ *               the same buffer for the D steps of one ring.
+ * Errors: as tsp_mlp_forward, plus TSP_ERR_INVALID_ARG for pos out of range.
+ */
+tsp_status tsp_mlp_shard(int64_t n_tokens, const tsp_dims* dims, int32_t D, int32_t pos, const uint16_t* x,
+                         const uint16_t* w1_d, const uint16_t* w2_d, const uint16_t* residual, uint16_t* y,
+                         void* workspace, size_t ws_bytes, hipStream_t stream);
 
 /* Static text for a status code (never null). */
 const char* tsp_status_string(tsp_status status);

@@ -238,3 +238,47 @@ def test_workspace_sizes(L):
     assert tsp.workspace_size(n, d, 4, 7) == 0
     assert tsp.workspace_size(n, _dims(hidden=300), 4, tsp.WS_LAYER) == 0
     assert tsp.workspace_size(-1, d, 4, tsp.WS_ATTN) == 0
+
+
+def test_shard_streaming_rejects(L):
+    p, d = _plan(), _dims()
+    n = p.n_local
+    # project one shard: shard index in [0, D)
+    pr = lambda shard=0, x=A, w=A + 64: L.tsp_attn_project_shard(ctypes.byref(p), ctypes.byref(d), shard, x, w,
+                                                                 A + 128, A + 192, A + 256, None)
+    assert pr(shard=4) == tsp.TSP_ERR_INVALID_ARG
+    assert pr(shard=-1) == tsp.TSP_ERR_INVALID_ARG
+    assert pr(w=None) == tsp.TSP_ERR_INVALID_ARG
+    assert pr(x=MIS) == tsp.TSP_ERR_ALIGNMENT
+    assert L.tsp_attn_project_shard(None, ctypes.byref(d), 0, A, A, A, A, A, None) == tsp.TSP_ERR_INVALID_ARG
+    # O projection ring step
+    need_o = tsp.workspace_size(n, d, 4, tsp.WS_OUT_SHARD)
+    assert need_o == n * 256 * 4  # the fp32 accumulator
+    out = lambda **k: L.tsp_attn_out_shard(k.get("n", n), ctypes.byref(d), 4, k.get("pos", 0), k.get("shard", 0),
+                                           k.get("attn", A), k.get("lo", None), k.get("wo", A + 64),
+                                           k.get("res", None), k.get("out", A + 128), k.get("ws", A + 192),
+                                           k.get("nb", need_o), None)
+    assert out(pos=4) == tsp.TSP_ERR_INVALID_ARG
+    assert out(pos=-1) == tsp.TSP_ERR_INVALID_ARG
+    assert out(shard=4) == tsp.TSP_ERR_INVALID_ARG
+    assert out(out=A) == tsp.TSP_ERR_INVALID_ARG          # out aliases attn
+    assert out(wo=None) == tsp.TSP_ERR_INVALID_ARG
+    assert out(nb=need_o - 1) == tsp.TSP_ERR_WORKSPACE
+    assert out(ws=None) == tsp.TSP_ERR_WORKSPACE
+    assert out(ws=MIS) == tsp.TSP_ERR_ALIGNMENT
+    assert out(n=-1) == tsp.TSP_ERR_SHAPE
+    # MLP ring step
+    need_m = tsp.workspace_size(512, d, 4, tsp.WS_MLP_SHARD)
+    # fp32 accumulator, row exponents, fp16 W2_d [256 x 256], fp16 GELU block [512 x 256]
+    assert need_m == 512 * 256 * 4 + 512 * 4 + 256 * 256 * 2 + 512 * 256 * 2
+    mlp = lambda **k: L.tsp_mlp_shard(k.get("n", 512), ctypes.byref(k.get("dims", d)), 4, k.get("pos", 0),
+                                      k.get("x", A), k.get("w1", A + 64), k.get("w2", A + 128), k.get("res", None),
+                                      k.get("y", A + 192), k.get("ws", A + 256), k.get("nb", need_m), None)
+    assert mlp(pos=4) == tsp.TSP_ERR_INVALID_ARG
+    assert mlp(y=A) == tsp.TSP_ERR_INVALID_ARG              # y aliases x
+    assert mlp(w2=None) == tsp.TSP_ERR_INVALID_ARG
+    assert mlp(w1=MIS) == tsp.TSP_ERR_ALIGNMENT
+    assert mlp(nb=need_m - 1) == tsp.TSP_ERR_WORKSPACE
+    assert mlp(dims=_dims(ffn=1002)) == tsp.TSP_ERR_SHAPE
+    assert mlp(n=-3) == tsp.TSP_ERR_SHAPE
+    assert tsp.workspace_size(512, _dims(ffn=1002), 4, tsp.WS_MLP_SHARD) == 0
