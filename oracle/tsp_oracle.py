@@ -44,6 +44,12 @@ projection outputs above, no intermediate is rounded.
 Matrix products use ``torch.matmul`` in fp64 as a library step; everything else
 (GELU, masking, softmax) is written out below.
 
+Layer variants at the end of the module (RMSNorm, rotary position embedding,
+grouped-query attention) are not on the pages: they are the published
+definitions (Zhang & Sennrich 2019; Su et al. 2021, RoFormer, with the
+interleaved pairs (x_{2i}, x_{2i+1}) of that paper; Ainslie et al. 2023),
+for the layer variants of a real decoder.
+
 Parity status: every function here is pinned by ``tests/test_oracle_*.py``
 (library special cases, closed forms, invariants and brute force); none is
 "parity unpinned".
@@ -284,3 +290,56 @@ def layer_forward(plan: Plan, x_local, wqkv, wo, w1, w2, n_heads, head_dim, k_fu
                                        residual=True, rows=rows, proj_bf16=proj_bf16)
     out = mlp_forward(h1, w1, w2, residual=True)
     return out, k_own, v_own
+
+
+# ---------------------------------------------------------------------------
+# layer variants of a real decoder (not on the pages: the pages' layer has no
+# norm, no positional encoding and MHA).  Each is the published definition,
+# written out in fp64.
+# ---------------------------------------------------------------------------
+def rms_norm(x: torch.Tensor, gain: torch.Tensor, eps: float) -> torch.Tensor:
+    """RMSNorm (Zhang & Sennrich, 2019): y = x / sqrt(mean_j x_j^2 + eps) * gain, per row."""
+    xx = f64(x)
+    ms = (xx * xx).mean(dim=-1, keepdim=True)
+    return xx / torch.sqrt(ms + eps) * f64(gain)
+
+
+def rope_angles(positions: torch.Tensor, head_dim: int, theta: float) -> torch.Tensor:
+    """Rotary angles (RoFormer, Su et al., 2021): angle[t, i] = p_t * theta^(-2i/hd),
+    i = 0 .. hd/2 - 1, in fp64."""
+    i = torch.arange(head_dim // 2, dtype=F64)
+    inv_freq = torch.pow(torch.tensor(theta, dtype=F64), -2.0 * i / head_dim)
+    return positions.to(F64)[:, None] * inv_freq[None, :]
+
+
+def rope(x: torch.Tensor, positions: torch.Tensor, n_heads: int, head_dim: int, theta: float) -> torch.Tensor:
+    """Rotary position embedding of rows ``x`` [m, n_heads*hd] at ``positions`` [m]:
+    in every head, the pair (x_{2i}, x_{2i+1}) is rotated by angle[t, i]:
+        (x_{2i} cos - x_{2i+1} sin,  x_{2i} sin + x_{2i+1} cos)."""
+    xx = f64(x).reshape(x.shape[0], n_heads, head_dim // 2, 2)
+    ang = rope_angles(positions, head_dim, theta)[:, None, :]
+    c, s = torch.cos(ang), torch.sin(ang)
+    a, b = xx[..., 0], xx[..., 1]
+    out = torch.stack([a * c - b * s, a * s + b * c], dim=-1)
+    return out.reshape(x.shape[0], n_heads * head_dim)
+
+
+def causal_attention_gqa(q: torch.Tensor, positions: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
+                         n_heads: int, n_kv_heads: int, head_dim: int) -> torch.Tensor:
+    """Grouped-query attention (Ainslie et al., 2023): query head a reads K/V head
+    a // (n_heads / n_kv_heads); ``k``/``v`` are [S, n_kv_heads*hd].  Otherwise as
+    :func:`causal_attention`, written out per head."""
+    group = n_heads // n_kv_heads
+    m, S = q.shape[0], k.shape[0]
+    out = torch.empty((m, n_heads * head_dim), dtype=F64)
+    future = torch.arange(S, dtype=torch.int64)[None, :] > positions[:, None]
+    scale = 1.0 / math.sqrt(head_dim)
+    for a in range(n_heads):
+        qc = slice(a * head_dim, (a + 1) * head_dim)
+        kvh = a // group
+        kc = slice(kvh * head_dim, (kvh + 1) * head_dim)
+        s = torch.matmul(q[:, qc], k[:, kc].t()) * scale
+        s = s.masked_fill(future, float("-inf"))
+        e = torch.exp(s - s.max(dim=1, keepdim=True).values)
+        out[:, qc] = torch.matmul(e / e.sum(dim=1, keepdim=True), v[:, kc])
+    return out
