@@ -19,7 +19,8 @@ After the timed steps, each step's entry point is also timed alone on layer
 0's inputs (``rows_layer0``: QKV projection, attention, O projection, MLP),
 each against the bf16 MFMA peak, and so are the shard-streaming forms of the
 projections and the MLP (the D ring steps called one by one, weights
-resident).
+resident) and the layer variants (RMSNorm and RoPE against the HBM peak,
+grouped-query attention with 8 K/V heads).
 
 Prints ONE JSON line.  ``--gpus`` above 1 is refused: this build runs on one GPU.
 """
@@ -94,6 +95,21 @@ def row_timings(plan, dims, D, layer0, x0, q, a, a_lo, out, ws_core, fl, dev, re
         ("A5 streamed: D x tsp_attn_out_shard", "oproj", out_streamed),
         ("A6+A7 streamed: D x tsp_mlp_shard", "mlp", mlp_streamed),
     ]
+    # layer variants on the same shapes: RMSNorm and RoPE (HBM-bound passes),
+    # attention with 8 K/V heads (grouped-query) on generated K/V of that width
+    h, H, hd = dims.hidden, dims.n_heads, dims.head_dim
+    gain = torch.ones(h, dtype=torch.bfloat16, device=dev)
+    kv8 = 8 * hd
+    k8 = torch.randn(plan.seq_len, kv8, device=dev).to(torch.bfloat16)
+    v8 = torch.randn(plan.seq_len, kv8, device=dev).to(torch.bfloat16)
+    calls += [
+        ("variant: RMSNorm (tsp_rms_norm)", "hbm:" + str(2 * n * h * 2 + h * 2),
+         lambda: tsp.rms_norm(x0, gain, 1e-6, out)),
+        ("variant: RoPE of q and own k rows (tsp_rope)", "hbm:" + str(2 * 2 * n * h * 2),
+         lambda: tsp.rope(plan, H, H, hd, 10000.0, q, kf)),
+        ("variant: GQA attention, 8 K/V heads (tsp_attn_core_gqa)", "attn",
+         lambda: tsp.attn_core_gqa(plan, dims, 8, q, k8, v8, a, a_lo, workspace=ws_core)),
+    ]
     stream = torch.cuda.current_stream()
     rows = {}
     for name, key, f in calls:
@@ -105,9 +121,13 @@ def row_timings(plan, dims, D, layer0, x0, q, a, a_lo, out, ws_core, fl, dev, re
         e1.record(stream)
         torch.cuda.synchronize()
         ms = e0.elapsed_time(e1) / reps
-        tf = fl[key] / (ms * 1e-3) / 1e12
-        rows[name] = {"ms": round(ms, 4), "tflops": round(tf, 1), "frac": round(tf / PEAK_BF16_TFLOPS, 4)}
-    del ws_mlp, ws_mlp_s, ws_out_s
+        if key.startswith("hbm:"):
+            gbs = int(key[4:]) / (ms * 1e-3) / 1e9
+            rows[name] = {"ms": round(ms, 4), "GB/s": round(gbs, 1), "frac": round(gbs / PEAK_HBM_GBS, 4)}
+        else:
+            tf = fl[key] / (ms * 1e-3) / 1e12
+            rows[name] = {"ms": round(ms, 4), "tflops": round(tf, 1), "frac": round(tf / PEAK_BF16_TFLOPS, 4)}
+    del ws_mlp, ws_mlp_s, ws_out_s, k8, v8
     return rows
 
 

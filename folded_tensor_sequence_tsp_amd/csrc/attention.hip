@@ -33,6 +33,9 @@
 //     below 256 and most tiles skip the rescale;
 //   * masking only on tiles that cross a wave's diagonal; tiles past a wave's
 //     last query are not computed;
+//   * grouped-query attention: query head a reads K/V head a / (H / H_kv); the
+//     query heads of one K/V head are neighbours in the workgroup order, so
+//     they meet its K/V in the same XCD's L2;
 //   * workgroups ordered so each XCD works through a contiguous range of heads,
 //     heaviest (latest) query tiles first.
 #include "device_common.h"
@@ -148,6 +151,9 @@ __global__ __launch_bounds__(NTHREADS) void attn_kernel(const AttnArgs a) {
 
   const int hcol = head * HD;
   const int64_t ld = a.hidden;
+  const int kvh = head / (a.n_heads / a.kv_heads);  // this head's K/V head
+  const int kcol = kvh * HD;
+  const int64_t kld = a.kv_ld;
 
   // ---- Q fragments in registers: lane holds query ql, dims kk*16 + 8*half .. +7.
   bf16x8 qf[C::KK];
@@ -169,12 +175,12 @@ __global__ __launch_bounds__(NTHREADS) void attn_kernel(const AttnArgs a) {
     const int p = lane % C::NCH;
     k_row[i] = r;
     k_col[i] = (p ^ (r & (C::NCH - 1))) * 8;
-    k_src[i] = a.k + (int64_t)r * ld + hcol + k_col[i];
+    k_src[i] = a.k + (int64_t)r * kld + kcol + k_col[i];
   }
   // V^T: row d of the tile, logical chunk (L % 8) ^ ((d / 2) % 8).
   const uint16_t* v_src[C::V_LOADS];
   {
-    const uint16_t* vt_head = a.vt + (int64_t)head * a.n_kv_tiles * HD * 64;
+    const uint16_t* vt_head = a.vt + (int64_t)kvh * a.n_kv_tiles * HD * 64;
 #pragma unroll
     for (int i = 0; i < C::V_LOADS; ++i) {
       const int d = (i * NW + wave) * 8 + lane / 8;
@@ -188,12 +194,12 @@ __global__ __launch_bounds__(NTHREADS) void attn_kernel(const AttnArgs a) {
     const int64_t k0 = (int64_t)t * BKV;
     if (k0 + BKV <= key_end) {  // whole tile inside the key range (wave-uniform)
 #pragma unroll
-      for (int i = 0; i < C::K_LOADS; ++i) dma16(k_src[i] + k0 * ld, stage + (i * NW + wave) * 1024);
+      for (int i = 0; i < C::K_LOADS; ++i) dma16(k_src[i] + k0 * kld, stage + (i * NW + wave) * 1024);
     } else {                    // last tile: rows past the range re-read the last key (masked anyway)
 #pragma unroll
       for (int i = 0; i < C::K_LOADS; ++i) {
         const int64_t key = min(k0 + k_row[i], key_end - 1);
-        dma16(a.k + key * ld + hcol + k_col[i], stage + (i * NW + wave) * 1024);
+        dma16(a.k + key * kld + kcol + k_col[i], stage + (i * NW + wave) * 1024);
       }
     }
 #pragma unroll
@@ -418,11 +424,11 @@ __global__ __launch_bounds__(NTHREADS) void attn_kernel(const AttnArgs a) {
 int64_t attn_kv_tiles(int64_t seq_len) { return (seq_len + BKV - 1) / BKV; }
 
 hipError_t launch_vt_prep(const AttnArgs& a, hipStream_t stream) {
-  const dim3 grid((unsigned)a.n_kv_tiles, (unsigned)a.n_heads), block(128);
+  const dim3 grid((unsigned)a.n_kv_tiles, (unsigned)a.kv_heads), block(128);
   if (a.head_dim == 128)
-    hipLaunchKernelGGL(vt_prep_kernel<128>, grid, block, 0, stream, a.v, a.seq_len, a.hidden, a.vt, a.n_kv_tiles);
+    hipLaunchKernelGGL(vt_prep_kernel<128>, grid, block, 0, stream, a.v, a.seq_len, a.kv_ld, a.vt, a.n_kv_tiles);
   else
-    hipLaunchKernelGGL(vt_prep_kernel<64>, grid, block, 0, stream, a.v, a.seq_len, a.hidden, a.vt, a.n_kv_tiles);
+    hipLaunchKernelGGL(vt_prep_kernel<64>, grid, block, 0, stream, a.v, a.seq_len, a.kv_ld, a.vt, a.n_kv_tiles);
   return hipGetLastError();
 }
 

@@ -101,15 +101,18 @@ __device__ __forceinline__ void store_row8(const GemmArgs& g, int nshard, int ro
   } else {
 #pragma unroll
     for (int j = 0; j < 4; ++j) packed[j] = pack_bf16x2(v[2 * j], v[2 * j + 1]);
+    // columns of a shard: [Q heads | K heads | V heads], K and V possibly fewer
     const int hs_hd = g.heads_per_shard * g.head_dim;
-    const int part = col >= 2 * hs_hd ? 2 : (col >= hs_hd ? 1 : 0);  // 0 = Q, 1 = K, 2 = V
-    const int gcol = (nshard + g.shard0) * hs_hd + (col - part * hs_hd);
-    if (part == 0) {
-      *reinterpret_cast<u32x4*>(g.q_out + (int64_t)row * g.hidden + gcol) = packed;
+    const int kv_hd = (g.kv_heads_per_shard ? g.kv_heads_per_shard : g.heads_per_shard) * g.head_dim;
+    const int shard = nshard + g.shard0;
+    if (col < hs_hd) {
+      *reinterpret_cast<u32x4*>(g.q_out + (int64_t)row * g.hidden + shard * hs_hd + col) = packed;
     } else {
+      const int is_v = col >= hs_hd + kv_hd;
+      const int kcol = shard * kv_hd + (col - hs_hd - is_v * kv_hd);
       const int64_t gpos = row < g.chunk_len ? g.chunk_start0 + row : g.chunk_start1 + (row - g.chunk_len);
-      uint16_t* dst = part == 1 ? g.k_full : g.v_full;
-      *reinterpret_cast<u32x4*>(dst + gpos * g.hidden + gcol) = packed;
+      uint16_t* dst = is_v ? g.v_full : g.k_full;
+      *reinterpret_cast<u32x4*>(dst + gpos * (g.kv_ld ? g.kv_ld : g.hidden) + kcol) = packed;
     }
   }
 }

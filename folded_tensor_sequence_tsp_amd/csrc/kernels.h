@@ -52,6 +52,9 @@ struct GemmArgs {
   uint16_t* v_full;
   int32_t heads_per_shard, head_dim, hidden;
   int32_t shard0;  // index of the launch's first weight shard (its Q/K/V column block)
+  // grouped-query projection: K/V heads per shard and the row stride of k_full /
+  // v_full (0: as many as the query heads, stride hidden)
+  int32_t kv_heads_per_shard, kv_ld;
   int64_t chunk_len, chunk_start0, chunk_start1;
 };
 
@@ -70,14 +73,17 @@ hipError_t launch_bf16_to_f16(const uint16_t* const* src, uint16_t* dst, int32_t
 
 struct AttnArgs {
   const uint16_t* q;  // [n_local x hidden]
-  const uint16_t* k;  // [seq_len x hidden]
-  const uint16_t* v;  // [seq_len x hidden]
+  const uint16_t* k;  // [seq_len x kv_ld]
+  const uint16_t* v;  // [seq_len x kv_ld]
   uint16_t* o;        // [n_local x hidden]
   uint16_t* o_lo;     // nullable: bf16(out - o), the rounding residual of o
   int64_t seq_len, chunk_len, chunk_start0, chunk_start1;
   int32_t hidden, n_heads, head_dim;
+  // K/V heads (n_heads for MHA; fewer for grouped-query attention, query head a
+  // reading K/V head a / (n_heads / kv_heads)) and the row stride of k and v.
+  int32_t kv_heads, kv_ld;
   // V^T tiles written by the attention launch before the attention kernel:
-  // [n_heads][n_kv_tiles][head_dim][64] bf16, keys permuted within 16-key groups.
+  // [kv_heads][n_kv_tiles][head_dim][64] bf16, keys permuted within 16-key groups.
   uint16_t* vt;
   int64_t n_kv_tiles;  // attn_kv_tiles(seq_len)
 };
@@ -87,5 +93,15 @@ int64_t attn_kv_tiles(int64_t seq_len);
 
 // V -> V^T tiles, then the attention kernel (both on `stream`).
 hipError_t launch_attention(const AttnArgs& args, hipStream_t stream);
+
+// y = x / sqrt(mean(x^2) + eps) * gain per row of x [n x h] (bf16; h % 8 == 0).
+hipError_t launch_rms_norm(const uint16_t* x, const uint16_t* gain, int64_t n, int32_t h, float eps, uint16_t* y,
+                           hipStream_t stream);
+
+// Rotary embedding in place of the n_rows local rows (positions from the zigzag
+// chunks), n_heads heads of head_dim each, row stride ld: rows of x itself, or
+// (at_global) the rows of x at the global positions.
+hipError_t launch_rope(uint16_t* x, int64_t n_rows, int64_t ld, int32_t n_heads, int32_t head_dim, double theta,
+                       int64_t chunk_len, int64_t start0, int64_t start1, int32_t at_global, hipStream_t stream);
 
 }  // namespace tsp

@@ -148,6 +148,8 @@ tsp_status run_core(const tsp_plan* plan, const tsp_dims* dims, const uint16_t* 
   a.hidden = dims->hidden;
   a.n_heads = dims->n_heads;
   a.head_dim = dims->head_dim;
+  a.kv_heads = dims->n_heads;
+  a.kv_ld = dims->hidden;
   a.vt = static_cast<uint16_t*>(core_ws);
   a.n_kv_tiles = attn_kv_tiles(plan->seq_len);
   return from_hip(launch_attention(a, stream));
@@ -291,6 +293,13 @@ tsp_status run_post(int64_t n, const tsp_dims* dims, int32_t D, int32_t start, c
   const uint16_t* w1h_shards[TSP_MAX_D];
   for (int d = 0; d < D; ++d) w1h_shards[d] = w1h + d * shard_elems;
   return run_mlp_core(n, dims, D, start, h16, true, w1h_shards, w2h, row_exp, h1, true, out, hbuf, stream);
+}
+
+// Shapes of grouped-query attention: query heads in groups over the K/V heads.
+tsp_status check_gqa(const tsp_dims* dims, int32_t D, int32_t n_kv_heads, bool sharded) {
+  if (n_kv_heads <= 0 || n_kv_heads > dims->n_heads || dims->n_heads % n_kv_heads != 0) return TSP_ERR_SHAPE;
+  if (sharded && n_kv_heads % D != 0) return TSP_ERR_SHAPE;
+  return TSP_OK;
 }
 
 // ---- shard streaming ---------------------------------------------------------
@@ -664,6 +673,104 @@ tsp_status tsp_mlp_shard(int64_t n_tokens, const tsp_dims* dims, int32_t D, int3
     if ((s = from_hip(launch_gemm(g2, stream))) != TSP_OK) return s;
   }
   return TSP_OK;
+}
+
+// ---- layer variants ------------------------------------------------------------
+
+tsp_status tsp_rms_norm(int64_t n_tokens, int32_t hidden, const uint16_t* x, const uint16_t* gain, float eps,
+                        uint16_t* y, hipStream_t stream) {
+  tsp_status s;
+  if (n_tokens < 0 || hidden <= 0) return TSP_ERR_SHAPE;
+  if (hidden % 8 != 0) return TSP_ERR_UNSUPPORTED;
+  if (!(eps >= 0.0f) || !(eps < 1.0e30f)) return TSP_ERR_INVALID_ARG;
+  if ((s = check_ptr(x)) != TSP_OK || (s = check_ptr(gain)) != TSP_OK || (s = check_ptr(y)) != TSP_OK) return s;
+  return from_hip(launch_rms_norm(x, gain, n_tokens, hidden, eps, y, stream));
+}
+
+tsp_status tsp_rope(const tsp_plan* plan, int32_t n_heads, int32_t n_kv_heads, int32_t head_dim, double theta,
+                    uint16_t* q, uint16_t* k_full, hipStream_t stream) {
+  tsp_status s;
+  if ((s = check_plan(plan)) != TSP_OK) return s;
+  if (n_heads <= 0 || n_kv_heads <= 0 || head_dim <= 0) return TSP_ERR_SHAPE;
+  if (head_dim % 8 != 0) return TSP_ERR_UNSUPPORTED;
+  if (!(theta > 1.0) || !(theta < 1.0e300)) return TSP_ERR_INVALID_ARG;
+  if ((s = check_ptr_nullable(q)) != TSP_OK || (s = check_ptr_nullable(k_full)) != TSP_OK) return s;
+  if (q && (s = from_hip(launch_rope(q, plan->n_local, (int64_t)n_heads * head_dim, n_heads, head_dim, theta,
+                                     plan->chunk_len, plan->chunk_start[0], plan->chunk_start[1], 0, stream))) != TSP_OK)
+    return s;
+  if (k_full)
+    return from_hip(launch_rope(k_full, plan->n_local, (int64_t)n_kv_heads * head_dim, n_kv_heads, head_dim, theta,
+                                plan->chunk_len, plan->chunk_start[0], plan->chunk_start[1], 1, stream));
+  return TSP_OK;
+}
+
+tsp_status tsp_attn_project_gqa(const tsp_plan* plan, const tsp_dims* dims, int32_t n_kv_heads,
+                                const uint16_t* x_local, const uint16_t* const* wqkv, uint16_t* k_full,
+                                uint16_t* v_full, uint16_t* q_out, hipStream_t stream) {
+  tsp_status s;
+  if ((s = check_plan(plan)) != TSP_OK) return s;
+  if ((s = check_dims(dims, plan->D, true, false)) != TSP_OK) return s;
+  if ((s = check_gqa(dims, plan->D, n_kv_heads, true)) != TSP_OK) return s;
+  if ((s = check_ptr(x_local)) != TSP_OK || (s = check_shards(wqkv, plan->D)) != TSP_OK ||
+      (s = check_ptr(k_full)) != TSP_OK || (s = check_ptr(v_full)) != TSP_OK || (s = check_ptr(q_out)) != TSP_OK)
+    return s;
+  GemmArgs g{};
+  g.A = x_local;
+  g.lda = dims->hidden;
+  for (int d = 0; d < plan->D; ++d) g.B[d] = wqkv[d];
+  const int hs = dims->n_heads / plan->D, kvs = n_kv_heads / plan->D;
+  g.M = (int32_t)plan->n_local;
+  g.N_s = (hs + 2 * kvs) * dims->head_dim;
+  g.K_s = dims->hidden;
+  g.n_shards = plan->D;
+  g.k_shards = 1;
+  g.epilogue = EPI_QKV;
+  g.q_out = q_out;
+  g.k_full = k_full;
+  g.v_full = v_full;
+  g.heads_per_shard = hs;
+  g.kv_heads_per_shard = kvs;
+  g.kv_ld = n_kv_heads * dims->head_dim;
+  g.head_dim = dims->head_dim;
+  g.hidden = dims->hidden;
+  g.chunk_len = plan->chunk_len;
+  g.chunk_start0 = plan->chunk_start[0];
+  g.chunk_start1 = plan->chunk_start[1];
+  return from_hip(launch_gemm(g, stream));
+}
+
+tsp_status tsp_attn_core_gqa(const tsp_plan* plan, const tsp_dims* dims, int32_t n_kv_heads, const uint16_t* q,
+                             const uint16_t* k_full, const uint16_t* v_full, uint16_t* attn_out, uint16_t* attn_lo,
+                             void* workspace, size_t ws_bytes, hipStream_t stream) {
+  tsp_status s;
+  if ((s = check_plan(plan)) != TSP_OK) return s;
+  if ((s = check_dims(dims, plan->D, true, false, 0)) != TSP_OK) return s;
+  if ((s = check_gqa(dims, plan->D, n_kv_heads, false)) != TSP_OK) return s;
+  if ((s = check_ptr(q)) != TSP_OK || (s = check_ptr(k_full)) != TSP_OK || (s = check_ptr(v_full)) != TSP_OK ||
+      (s = check_ptr(attn_out)) != TSP_OK || (s = check_ptr_nullable(attn_lo)) != TSP_OK)
+    return s;
+  if (attn_out == q || attn_lo == q || attn_lo == attn_out) return TSP_ERR_INVALID_ARG;
+  if (!workspace) return TSP_ERR_WORKSPACE;
+  if (!aligned16(workspace)) return TSP_ERR_ALIGNMENT;
+  if (ws_bytes < ws_core(plan->n_local, dims, plan->D)) return TSP_ERR_WORKSPACE;
+  AttnArgs a{};
+  a.q = q;
+  a.k = k_full;
+  a.v = v_full;
+  a.o = attn_out;
+  a.o_lo = attn_lo;
+  a.seq_len = plan->seq_len;
+  a.chunk_len = plan->chunk_len;
+  a.chunk_start0 = plan->chunk_start[0];
+  a.chunk_start1 = plan->chunk_start[1];
+  a.hidden = dims->hidden;
+  a.n_heads = dims->n_heads;
+  a.head_dim = dims->head_dim;
+  a.kv_heads = n_kv_heads;
+  a.kv_ld = n_kv_heads * dims->head_dim;
+  a.vt = static_cast<uint16_t*>(workspace);
+  a.n_kv_tiles = attn_kv_tiles(plan->seq_len);
+  return from_hip(launch_attention(a, stream));
 }
 
 const char* tsp_status_string(tsp_status status) {

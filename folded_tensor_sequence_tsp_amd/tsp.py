@@ -23,7 +23,8 @@ MAX_D = 16
 
 EXPORTS = ["tsp_zigzag_plan", "tsp_workspace_size", "tsp_attn_project", "tsp_attn_core", "tsp_attn_out",
            "tsp_attn_forward", "tsp_mlp_forward", "tsp_layer_post", "tsp_layer_forward", "tsp_attn_project_shard",
-           "tsp_attn_out_shard", "tsp_mlp_shard", "tsp_status_string"]
+           "tsp_attn_out_shard", "tsp_mlp_shard", "tsp_rms_norm", "tsp_rope", "tsp_attn_project_gqa",
+           "tsp_attn_core_gqa", "tsp_status_string"]
 
 
 class TSPError(RuntimeError):
@@ -65,6 +66,10 @@ def lib() -> ctypes.CDLL:
             "tsp_attn_project_shard": [POINTER(Plan), POINTER(Dims), c_int32, P, P, P, P, P, P],
             "tsp_attn_out_shard": [c_int64, POINTER(Dims), c_int32, c_int32, c_int32, P, P, P, P, P, P, c_size_t, P],
             "tsp_mlp_shard": [c_int64, POINTER(Dims), c_int32, c_int32, P, P, P, P, P, P, c_size_t, P],
+            "tsp_rms_norm": [c_int64, c_int32, P, P, ctypes.c_float, P, P],
+            "tsp_rope": [POINTER(Plan), c_int32, c_int32, c_int32, ctypes.c_double, P, P, P],
+            "tsp_attn_project_gqa": [POINTER(Plan), POINTER(Dims), c_int32, P, PP, P, P, P, P],
+            "tsp_attn_core_gqa": [POINTER(Plan), POINTER(Dims), c_int32, P, P, P, P, P, P, c_size_t, P],
             "tsp_status_string": [c_int32],
         }
         for name, args in sig.items():
@@ -267,6 +272,46 @@ def mlp_shard(dims: Dims, D: int, pos: int, x, w1_d, w2_d, residual, y, workspac
     args = (_dev_tensor(x, (n, h), "x"), _dev_tensor(w1_d, (Fs, h), "w1_d"), _dev_tensor(w2_d, (h, Fs), "w2_d"),
             _opt_tensor(residual, (n, h), "residual"), _dev_tensor(y, (n, h), "y"))
     _check(lib().tsp_mlp_shard(n, ctypes.byref(dims), D, pos, *args, ws, nbytes, _stream(stream)), "tsp_mlp_shard")
+
+
+# ---- layer variants (see include/tsp.h)
+def rms_norm(x, gain, eps: float, y, stream=None):
+    n, h = x.shape
+    args = (_dev_tensor(x, (n, h), "x"), _dev_tensor(gain, (h,), "gain"))
+    _check(lib().tsp_rms_norm(n, h, *args, float(eps), _dev_tensor(y, (n, h), "y"), _stream(stream)), "tsp_rms_norm")
+
+
+def rope(plan: Plan, n_heads: int, n_kv_heads: int, head_dim: int, theta: float, q=None, k_full=None, stream=None):
+    qa = _opt_tensor(q, (plan.n_local, n_heads * head_dim), "q")
+    ka = _opt_tensor(k_full, (plan.seq_len, n_kv_heads * head_dim), "k_full")
+    _check(lib().tsp_rope(ctypes.byref(plan), n_heads, n_kv_heads, head_dim, float(theta), qa, ka, _stream(stream)),
+           "tsp_rope")
+
+
+def attn_project_gqa(plan: Plan, dims: Dims, n_kv_heads: int, x_local, wqkv, k_full, v_full, q_out, stream=None):
+    n, h, S, D = plan.n_local, dims.hidden, plan.seq_len, plan.D
+    Hs = dims.n_heads // D if D > 0 else 0
+    Ks = n_kv_heads // D if D > 0 else 0
+    kvw = n_kv_heads * dims.head_dim
+    args = (_dev_tensor(x_local, (n, h), "x_local"), _shards(wqkv, D, ((Hs + 2 * Ks) * dims.head_dim, h), "wqkv"),
+            _dev_tensor(k_full, (S, kvw), "k_full"), _dev_tensor(v_full, (S, kvw), "v_full"),
+            _dev_tensor(q_out, (n, h), "q_out"))
+    _check(lib().tsp_attn_project_gqa(ctypes.byref(plan), ctypes.byref(dims), n_kv_heads, *args, _stream(stream)),
+           "tsp_attn_project_gqa")
+
+
+def attn_core_gqa(plan: Plan, dims: Dims, n_kv_heads: int, q, k_full, v_full, attn_out, attn_lo=None, workspace=None,
+                  stream=None):
+    n, h, S = plan.n_local, dims.hidden, plan.seq_len
+    kvw = n_kv_heads * dims.head_dim
+    need = workspace_size(n, dims, plan.D, WS_CORE)
+    if workspace is None:
+        workspace = torch.empty(max(need, 256), dtype=torch.uint8, device=q.device)
+    ws, nbytes = _workspace(workspace, need)
+    args = (_dev_tensor(q, (n, h), "q"), _dev_tensor(k_full, (S, kvw), "k_full"), _dev_tensor(v_full, (S, kvw), "v_full"),
+            _dev_tensor(attn_out, (n, h), "attn_out"), _opt_tensor(attn_lo, (n, h), "attn_lo"))
+    _check(lib().tsp_attn_core_gqa(ctypes.byref(plan), ctypes.byref(dims), n_kv_heads, *args, ws, nbytes,
+                                   _stream(stream)), "tsp_attn_core_gqa")
 
 
 def alloc_workspace(n_tokens: int, dims: Dims, D: int, kind: int, device=None) -> torch.Tensor:

@@ -318,6 +318,59 @@ tsp_status tsp_mlp_shard(int64_t n_tokens, const tsp_dims* dims, int32_t D, int3
                          const uint16_t* w1_d, const uint16_t* w2_d, const uint16_t* residual, uint16_t* y,
                          void* workspace, size_t ws_bytes, hipStream_t stream);
 
+/*
+ * ---- Layer variants of a real decoder ----
+ * Not on the TSP pages (their layer has no norm, no positional encoding, and
+ * 32 K/V heads for 32 query heads); these are the published definitions, for
+ * decoders that have them.
+ *
+ * RMSNorm (Zhang & Sennrich 2019) of each row of x [n_tokens x hidden]:
+ *   y = x / sqrt(mean_j x_j^2 + eps) * gain            (fp32 inside, bf16 out)
+ *   gain : device, bf16 [hidden].  y may alias x.  hidden % 8 == 0; eps >= 0.
+ * Errors: TSP_ERR_SHAPE (n < 0, hidden <= 0), TSP_ERR_UNSUPPORTED (hidden % 8),
+ *         TSP_ERR_INVALID_ARG (null pointer, eps negative or not finite),
+ *         TSP_ERR_ALIGNMENT.
+ */
+tsp_status tsp_rms_norm(int64_t n_tokens, int32_t hidden, const uint16_t* x, const uint16_t* gain, float eps,
+                        uint16_t* y, hipStream_t stream);
+
+/*
+ * Rotary position embedding (RoFormer, Su et al. 2021; the interleaved pairs of
+ * that paper), in place, at the tokens' global zigzag positions p: in every
+ * head the pair (x_{2i}, x_{2i+1}) is rotated by p * theta^(-2i/head_dim).
+ *   q      : device, bf16 [n_local x n_heads*head_dim], nullable; local row t
+ *            is at the plan's global position of t.
+ *   k_full : device, bf16 [seq_len x n_kv_heads*head_dim], nullable; only the
+ *            rank's own rows are rotated (the other ranks rotate theirs before
+ *            the all-gather).
+ *   theta  : > 1 (10000 in RoFormer).  Angles and their sine and cosine are
+ *            computed in fp64, the rotation in fp32, the result rounded to bf16.
+ * Errors: as tsp_zigzag_plan's plan check; TSP_ERR_SHAPE (non-positive sizes),
+ *         TSP_ERR_UNSUPPORTED (head_dim % 8), TSP_ERR_INVALID_ARG (theta).
+ */
+tsp_status tsp_rope(const tsp_plan* plan, int32_t n_heads, int32_t n_kv_heads, int32_t head_dim, double theta,
+                    uint16_t* q, uint16_t* k_full, hipStream_t stream);
+
+/*
+ * Grouped-query attention (Ainslie et al. 2023): n_kv_heads K/V heads, query
+ * head a reads K/V head a / (n_heads / n_kv_heads).
+ * tsp_attn_project_gqa: tsp_attn_project with shard d's weights
+ *   wqkv[d] bf16 [(H_s + 2 Hkv_s) * head_dim x hidden], columns [Q heads | K
+ *   heads | V heads] (H_s = n_heads / D query heads, Hkv_s = n_kv_heads / D K/V
+ *   heads), k_full / v_full [seq_len x n_kv_heads * head_dim].
+ * tsp_attn_core_gqa: tsp_attn_core with k_full / v_full
+ *   [seq_len x n_kv_heads * head_dim]; the workspace of tsp_attn_core
+ *   (TSP_WS_CORE) is enough.
+ *   n_kv_heads : divides n_heads (and, for the projection, is a multiple of D).
+ * Errors: as the MHA calls, plus TSP_ERR_SHAPE for n_kv_heads.
+ */
+tsp_status tsp_attn_project_gqa(const tsp_plan* plan, const tsp_dims* dims, int32_t n_kv_heads,
+                                const uint16_t* x_local, const uint16_t* const* wqkv, uint16_t* k_full,
+                                uint16_t* v_full, uint16_t* q_out, hipStream_t stream);
+tsp_status tsp_attn_core_gqa(const tsp_plan* plan, const tsp_dims* dims, int32_t n_kv_heads, const uint16_t* q,
+                             const uint16_t* k_full, const uint16_t* v_full, uint16_t* attn_out, uint16_t* attn_lo,
+                             void* workspace, size_t ws_bytes, hipStream_t stream);
+
 /* Static text for a status code (never null). */
 const char* tsp_status_string(tsp_status status);
 

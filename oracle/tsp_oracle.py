@@ -343,3 +343,18 @@ def causal_attention_gqa(q: torch.Tensor, positions: torch.Tensor, k: torch.Tens
         e = torch.exp(s - s.max(dim=1, keepdim=True).values)
         out[:, qc] = torch.matmul(e / e.sum(dim=1, keepdim=True), v[:, kc])
     return out
+
+
+def qkv_projection_gqa(x_local, wqkv, head_dim: int, heads_per_shard: int, kv_heads_per_shard: int):
+    """Q, K, V of the local rows for grouped-query attention: shard d's weights
+    are [(H_s + 2 Hkv_s) hd x h], columns [Q heads | K heads | V heads]; query
+    heads and K/V heads are numbered shard by shard.  fp64, unrounded."""
+    xx = f64(x_local)
+    qs, ks, vs = [], [], []
+    qw, kw = heads_per_shard * head_dim, kv_heads_per_shard * head_dim
+    for w in wqkv:
+        ww = f64(w)
+        qs.append(linear(xx, ww[:qw]))
+        ks.append(linear(xx, ww[qw:qw + kw]))
+        vs.append(linear(xx, ww[qw + kw:qw + 2 * kw]))
+    return torch.cat(qs, dim=1), torch.cat(ks, dim=1), torch.cat(vs, dim=1)

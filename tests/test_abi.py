@@ -282,3 +282,35 @@ def test_shard_streaming_rejects(L):
     assert mlp(dims=_dims(ffn=1002)) == tsp.TSP_ERR_SHAPE
     assert mlp(n=-3) == tsp.TSP_ERR_SHAPE
     assert tsp.workspace_size(512, _dims(ffn=1002), 4, tsp.WS_MLP_SHARD) == 0
+
+
+def test_variants_reject(L):
+    p, d = _plan(), _dims()
+    # RMSNorm
+    assert L.tsp_rms_norm(-1, 256, A, A + 64, ctypes.c_float(1e-6), A + 128, None) == tsp.TSP_ERR_SHAPE
+    assert L.tsp_rms_norm(10, 0, A, A + 64, ctypes.c_float(1e-6), A + 128, None) == tsp.TSP_ERR_SHAPE
+    assert L.tsp_rms_norm(10, 260, A, A + 64, ctypes.c_float(1e-6), A + 128, None) == tsp.TSP_ERR_UNSUPPORTED
+    assert L.tsp_rms_norm(10, 256, A, A + 64, ctypes.c_float(-1.0), A + 128, None) == tsp.TSP_ERR_INVALID_ARG
+    assert L.tsp_rms_norm(10, 256, A, A + 64, ctypes.c_float(float("nan")), A + 128, None) == tsp.TSP_ERR_INVALID_ARG
+    assert L.tsp_rms_norm(10, 256, A, None, ctypes.c_float(1e-6), A + 128, None) == tsp.TSP_ERR_INVALID_ARG
+    assert L.tsp_rms_norm(10, 256, MIS, A, ctypes.c_float(1e-6), A + 128, None) == tsp.TSP_ERR_ALIGNMENT
+    # RoPE
+    assert L.tsp_rope(ctypes.byref(p), 4, 4, 64, ctypes.c_double(1.0), A, A, None) == tsp.TSP_ERR_INVALID_ARG
+    assert L.tsp_rope(ctypes.byref(p), 4, 4, 60, ctypes.c_double(1e4), A, A, None) == tsp.TSP_ERR_UNSUPPORTED
+    assert L.tsp_rope(ctypes.byref(p), 0, 4, 64, ctypes.c_double(1e4), A, A, None) == tsp.TSP_ERR_SHAPE
+    assert L.tsp_rope(ctypes.byref(p), 4, 4, 64, ctypes.c_double(1e4), MIS, A, None) == tsp.TSP_ERR_ALIGNMENT
+    assert L.tsp_rope(None, 4, 4, 64, ctypes.c_double(1e4), A, A, None) == tsp.TSP_ERR_INVALID_ARG
+    assert L.tsp_rope(ctypes.byref(p), 4, 4, 64, ctypes.c_double(1e4), None, None, None) == tsp.TSP_OK  # nothing to do
+    # GQA
+    w = _arr([A] * 4)
+    need = tsp.workspace_size(p.n_local, d, 4, tsp.WS_CORE)
+    core = lambda kv, **k: L.tsp_attn_core_gqa(ctypes.byref(p), ctypes.byref(d), kv, A, A + 64, A + 128,
+                                               k.get("out", A + 192), None, k.get("ws", A + 256), k.get("nb", need), None)
+    assert core(3) == tsp.TSP_ERR_SHAPE          # 4 query heads do not group over 3 K/V heads
+    assert core(0) == tsp.TSP_ERR_SHAPE
+    assert core(8) == tsp.TSP_ERR_SHAPE          # more K/V heads than query heads
+    assert core(2, out=A) == tsp.TSP_ERR_INVALID_ARG
+    assert core(2, nb=need - 1) == tsp.TSP_ERR_WORKSPACE
+    proj = lambda kv: L.tsp_attn_project_gqa(ctypes.byref(p), ctypes.byref(d), kv, A, w, A + 64, A + 128, A + 192, None)
+    assert proj(2) == tsp.TSP_ERR_SHAPE          # 2 K/V heads do not split over D = 4 shards
+    assert proj(3) == tsp.TSP_ERR_SHAPE

@@ -121,3 +121,20 @@ def test_gqa_reduces_to_mha():
     sub = torch.tensor([3, 11, 29])
     assert torch.allclose(O.causal_attention_gqa(q[sub], sub, k, v, H, 2, hd),
                           O.causal_attention(q[sub], sub, kr, vr, H, hd), rtol=1e-13, atol=1e-14)
+
+
+def test_gqa_projection_reduces_to_mha_projection():
+    g = torch.Generator().manual_seed(8)
+    D, Hs, hd, h = 2, 2, 8, 32
+    x = torch.randn(5, h, generator=g, dtype=F64)
+    w = [torch.randn(3 * Hs * hd, h, generator=g, dtype=F64) for _ in range(D)]
+    a = O.qkv_projection_gqa(x, w, hd, Hs, Hs)
+    b = O.qkv_projection(x, w, hd)
+    for u, v in zip(a, b):
+        assert torch.allclose(u, v, rtol=1e-14, atol=1e-14)
+    # with one K/V head per shard: K/V columns are rows Hs*hd .. of each shard, by matmul
+    w1 = [torch.randn((Hs + 2) * hd, h, generator=g, dtype=F64) for _ in range(D)]
+    q, k, v = O.qkv_projection_gqa(x, w1, hd, Hs, 1)
+    assert torch.allclose(k[:, hd:2 * hd], x @ w1[1][Hs * hd:(Hs + 1) * hd].t(), rtol=1e-13)
+    assert torch.allclose(v[:, :hd], x @ w1[0][(Hs + 1) * hd:].t(), rtol=1e-13)
+    assert torch.allclose(q[:, Hs * hd:], x @ w1[1][:Hs * hd].t(), rtol=1e-13)
