@@ -358,3 +358,37 @@ def qkv_projection_gqa(x_local, wqkv, head_dim: int, heads_per_shard: int, kv_he
         ks.append(linear(xx, ww[qw:qw + kw]))
         vs.append(linear(xx, ww[qw + kw:qw + 2 * kw]))
     return torch.cat(qs, dim=1), torch.cat(ks, dim=1), torch.cat(vs, dim=1)
+
+
+# ---------------------------------------------------------------------------
+# backward pass of the MLP ring (not on the pages, which describe the forward
+# schedule; the rank's gradient contributions for its own tokens)
+# ---------------------------------------------------------------------------
+def gelu_tanh_grad(u: torch.Tensor) -> torch.Tensor:
+    """d/du of the tanh-form GELU: with z = c (u + a u^3), c = sqrt(2/pi), a = 0.044715,
+    0.5 (1 + tanh z) + 0.5 u (1 - tanh^2 z) c (1 + 3 a u^2)."""
+    c, a = math.sqrt(2.0 / math.pi), 0.044715
+    t = torch.tanh(c * (u + a * u * u * u))
+    return 0.5 * (1.0 + t) + 0.5 * u * (1.0 - t * t) * c * (1.0 + 3.0 * a * u * u)
+
+
+def mlp_backward(x, w1, w2, dy, residual=True):
+    """Gradients of y = [x +] sum_d GELU(x W1_d^T) W2_d^T for the rank's rows x,
+    given dy = dL/dy (all fp64, from the chain rule written out per shard):
+        U_d = x W1_d^T,  H_d = GELU(U_d),  dH_d = dy W2_d,  dU_d = dH_d * GELU'(U_d)
+        dx    = [dy +] sum_d dU_d W1_d
+        dW1_d = dU_d^T x        ([F_s x h], this rank's contribution)
+        dW2_d = dy^T H_d        ([h x F_s], this rank's contribution)
+    Returns (dx, [dW1_d], [dW2_d])."""
+    xx, g = f64(x), f64(dy)
+    dx = g.clone() if residual else torch.zeros_like(g)
+    dw1, dw2 = [], []
+    for a_w1, a_w2 in zip(w1, w2):
+        W1, W2 = f64(a_w1), f64(a_w2)
+        U = linear(xx, W1)
+        H = gelu_tanh(U)
+        dU = torch.matmul(g, W2) * gelu_tanh_grad(U)
+        dx = dx + torch.matmul(dU, W1)
+        dw1.append(torch.matmul(dU.t(), xx))
+        dw2.append(torch.matmul(g.t(), H))
+    return dx, dw1, dw2
