@@ -56,6 +56,18 @@ __device__ __forceinline__ float gelu_tanh(float u) {
   return 0.5f * u * (1.0f + t);
 }
 
+// Derivative of gelu_tanh: 0.5 (1 + t) + 0.5 u (1 - t^2) c (1 + 3 a u^2) with
+// t = tanh(c (u + a u^3)), c = sqrt(2/pi), a = 0.044715; t from the same exp2
+// form as gelu_tanh.
+__device__ __forceinline__ float gelu_tanh_grad(float u) {
+  const float c = 0.79788456080286535588f, a = 0.044715f;
+  const float two_log2e = 2.88539008177792681472f;
+  const float z = c * (u + a * u * u * u);
+  const float e = __builtin_amdgcn_exp2f(two_log2e * z);
+  const float t = 1.0f - 2.0f * __builtin_amdgcn_rcpf(e + 1.0f);
+  return 0.5f * (1.0f + t) + 0.5f * u * (1.0f - t * t) * c * (1.0f + 3.0f * a * u * u);
+}
+
 __device__ __forceinline__ f32x16 mfma32(const bf16x8& a, const bf16x8& b, const f32x16& c) {
   return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
 }

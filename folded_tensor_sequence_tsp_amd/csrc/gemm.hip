@@ -89,6 +89,19 @@ __device__ __forceinline__ void store_row8(const GemmArgs& g, int nshard, int ro
       for (int j = 0; j < 4; ++j) packed[j] = pack_bf16x2(v[2 * j], v[2 * j + 1]);
       *reinterpret_cast<u32x4*>(static_cast<uint16_t*>(g.out) + idx) = packed;
     }
+  } else if constexpr (EPI == EPI_DGELU) {
+    const float* up = g.aux + (int64_t)row * g.N_s + col;
+    const f32x4 u0 = *reinterpret_cast<const f32x4*>(up);
+    const f32x4 u1 = *reinterpret_cast<const f32x4*>(up + 4);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      v[j] *= gelu_tanh_grad(u0[j]);
+      v[4 + j] *= gelu_tanh_grad(u1[j]);
+    }
+#pragma unroll
+    for (int j = 0; j < 4; ++j) packed[j] = pack_bf16x2(v[2 * j], v[2 * j + 1]);
+    *reinterpret_cast<u32x4*>(static_cast<uint16_t*>(g.out) + (int64_t)row * g.ldo + (int64_t)nshard * g.N_s +
+                              col) = packed;
   } else if constexpr (EPI == EPI_GELU) {
     const int e = g.row_exp ? g.row_exp[row] : 0;
     const int e_in = g.gelu_in_scaled ? e : 0;
@@ -287,9 +300,11 @@ hipError_t launch_tiles(const GemmArgs& g, hipStream_t stream) {
   const int tiles_m = (g.M + BM - 1) / BM;
   const int tiles_n = ((g.N_s + BN - 1) / BN) * g.n_shards;
   const dim3 grid(tiles_m * tiles_n), block(Cfg<BM, BN>::NT);
-  // Instantiated: QKV (bf16), W1 + GELU (bf16 or fp16), O projection (bf16), W2 (fp16).
+  // Instantiated: QKV (bf16), W1 + GELU (bf16 or fp16), O projection (bf16), W2 (fp16),
+  // GELU-derivative product (bf16, MLP backward).
   switch (g.epilogue) {
     case EPI_QKV: hipLaunchKernelGGL((gemm_kernel<BM, BN, EPI_QKV, false>), grid, block, 0, stream, g); break;
+    case EPI_DGELU: hipLaunchKernelGGL((gemm_kernel<BM, BN, EPI_DGELU, false>), grid, block, 0, stream, g); break;
     case EPI_GELU:
       if (g.f16)
         hipLaunchKernelGGL((gemm_kernel<BM, BN, EPI_GELU, true>), grid, block, 0, stream, g);

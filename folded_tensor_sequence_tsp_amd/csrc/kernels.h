@@ -13,6 +13,7 @@ enum GemmEpilogue : int32_t {
   EPI_QKV = 0,    // Q -> q_out, K/V rows -> k_full/v_full at global zigzag positions (bf16)
   EPI_GELU = 1,   // out[:, shard block] = fp16(GELU(acc * 2^in_exp) * 2^-row_exp[row])
   EPI_RESID = 2,  // out = (acc * 2^row_exp[row] [+ residual]) as bf16 or fp32
+  EPI_DGELU = 3,  // out[:, shard block] = bf16(acc * GELU'(aux[row, col])), aux fp32 [M x N_s]
 };
 
 // C = A . B^T over 16-bit operands (bf16, or fp16 when f16 is set) with an fp32
@@ -41,6 +42,7 @@ struct GemmArgs {
   // EPI_GELU / EPI_RESID
   void* out;
   int64_t ldo;
+  const float* aux;       // EPI_DGELU: the GELU inputs, fp32, row stride N_s
   const void* residual;  // EPI_RESID, nullable
   int32_t res_f32;       // residual is fp32 (else bf16)
   int32_t out_f32;       // EPI_RESID output is fp32 (else bf16)
@@ -103,5 +105,11 @@ hipError_t launch_rms_norm(const uint16_t* x, const uint16_t* gain, int64_t n, i
 // (at_global) the rows of x at the global positions.
 hipError_t launch_rope(uint16_t* x, int64_t n_rows, int64_t ld, int32_t n_heads, int32_t head_dim, double theta,
                        int64_t chunk_len, int64_t start0, int64_t start1, int32_t at_global, hipStream_t stream);
+
+// dst[c * ld_out + r] = f(src[r * ld_in + c]) for r < R, c < C (C % 64 == 0), and 0
+// for R <= r < ld_out (ld_out % 64 == 0): a transpose of bf16 (src_f32: fp32)
+// rows into bf16, f = GELU (tanh form) when gelu, else the identity.
+hipError_t launch_transpose(const void* src, int32_t src_f32, int32_t gelu, int64_t R, int64_t C, int64_t ld_in,
+                            uint16_t* dst, int64_t ld_out, hipStream_t stream);
 
 }  // namespace tsp

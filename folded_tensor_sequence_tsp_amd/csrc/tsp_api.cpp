@@ -302,6 +302,32 @@ tsp_status check_gqa(const tsp_dims* dims, int32_t D, int32_t n_kv_heads, bool s
   return TSP_OK;
 }
 
+// ---- MLP backward --------------------------------------------------------------
+
+// Workspace of tsp_mlp_backward (n_pad = n rounded up to 64): x^T and dy^T
+// [h x n_pad], U_d fp32 [n x F_s], GELU(U_d)^T and dU_d^T [F_s x n_pad], dU of
+// all shards [n x F], W1_d^T of all shards [D][h x F_s], W2_d^T [F_s x h].
+struct MlpBwdWs {
+  size_t xt_off, dyt_off, u_off, ht_off, dut_off, du_off, w1t_off, w2t_off, total;
+};
+
+int64_t pad64(int64_t n) { return (n + 63) / 64 * 64; }
+
+MlpBwdWs mlp_bwd_ws(int64_t n, const tsp_dims* d, int32_t D) {
+  const int64_t np = pad64(n), h = d->hidden, F = d->ffn, fs = F / D;
+  MlpBwdWs w;
+  w.xt_off = 0;
+  w.dyt_off = w.xt_off + round_up((size_t)h * np * 2);
+  w.u_off = w.dyt_off + round_up((size_t)h * np * 2);
+  w.ht_off = w.u_off + round_up((size_t)n * fs * 4);
+  w.dut_off = w.ht_off + round_up((size_t)fs * np * 2);
+  w.du_off = w.dut_off + round_up((size_t)fs * np * 2);
+  w.w1t_off = w.du_off + round_up((size_t)n * F * 2);
+  w.w2t_off = w.w1t_off + round_up((size_t)h * F * 2);
+  w.total = w.w2t_off + round_up((size_t)fs * h * 2);
+  return w;
+}
+
 // ---- shard streaming ---------------------------------------------------------
 
 // O projection ring step: the fp32 accumulator [n x h].
@@ -403,6 +429,9 @@ size_t tsp_workspace_size(int64_t n_tokens, const tsp_dims* dims, int32_t D, int
     case TSP_WS_MLP_SHARD:
       if (check_dims(dims, D, false, true) != TSP_OK) return 0;
       return mlp_shard_ws(n_tokens, dims, D).total;
+    case TSP_WS_MLP_BWD:
+      if (check_dims(dims, D, false, true) != TSP_OK) return 0;
+      return mlp_bwd_ws(n_tokens, dims, D).total;
     default:
       return 0;
   }
@@ -771,6 +800,92 @@ tsp_status tsp_attn_core_gqa(const tsp_plan* plan, const tsp_dims* dims, int32_t
   a.vt = static_cast<uint16_t*>(workspace);
   a.n_kv_tiles = attn_kv_tiles(plan->seq_len);
   return from_hip(launch_attention(a, stream));
+}
+
+tsp_status tsp_mlp_backward(int64_t n_tokens, const tsp_dims* dims, int32_t D, int32_t start_shard,
+                            int32_t residual, const uint16_t* x, const uint16_t* const* w1,
+                            const uint16_t* const* w2, const uint16_t* dy, uint16_t* dx, float* const* dw1,
+                            float* const* dw2, void* workspace, size_t ws_bytes, hipStream_t stream) {
+  tsp_status s;
+  if ((s = check_dims(dims, D, false, true)) != TSP_OK) return s;
+  if (n_tokens < 0) return TSP_ERR_SHAPE;
+  if (n_tokens > INT32_MAX - 64) return TSP_ERR_UNSUPPORTED;
+  if (start_shard < 0 || start_shard >= D) return TSP_ERR_INVALID_ARG;
+  if ((s = check_ptr(x)) != TSP_OK || (s = check_shards(w1, D)) != TSP_OK || (s = check_shards(w2, D)) != TSP_OK ||
+      (s = check_ptr(dy)) != TSP_OK || (s = check_ptr(dx)) != TSP_OK)
+    return s;
+  if (!dw1 || !dw2) return TSP_ERR_INVALID_ARG;
+  for (int d = 0; d < D; ++d)
+    if ((s = check_ptr(dw1[d])) != TSP_OK || (s = check_ptr(dw2[d])) != TSP_OK) return s;
+  if (dx == x || dx == dy) return TSP_ERR_INVALID_ARG;
+  if (!workspace) return TSP_ERR_WORKSPACE;
+  if (!aligned16(workspace)) return TSP_ERR_ALIGNMENT;
+  const MlpBwdWs lay = mlp_bwd_ws(n_tokens, dims, D);
+  if (ws_bytes < lay.total) return TSP_ERR_WORKSPACE;
+  if (n_tokens == 0) return TSP_OK;
+  char* base = static_cast<char*>(workspace);
+  uint16_t* xt = reinterpret_cast<uint16_t*>(base + lay.xt_off);
+  uint16_t* dyt = reinterpret_cast<uint16_t*>(base + lay.dyt_off);
+  float* u = reinterpret_cast<float*>(base + lay.u_off);
+  uint16_t* ht = reinterpret_cast<uint16_t*>(base + lay.ht_off);
+  uint16_t* dut = reinterpret_cast<uint16_t*>(base + lay.dut_off);
+  uint16_t* du = reinterpret_cast<uint16_t*>(base + lay.du_off);
+  uint16_t* w1t = reinterpret_cast<uint16_t*>(base + lay.w1t_off);
+  uint16_t* w2t = reinterpret_cast<uint16_t*>(base + lay.w2t_off);
+  const int64_t n = n_tokens, np = pad64(n), h = dims->hidden, F = dims->ffn;
+  const int32_t fs = dims->ffn / D;
+  auto gemm = [&](const uint16_t* A, int64_t lda, const uint16_t* B, int32_t M, int32_t N, int32_t K, int epi,
+                  void* out, int64_t ldo, int32_t out_f32) {
+    GemmArgs g{};
+    g.A = A;
+    g.lda = lda;
+    g.B[0] = B;
+    g.M = M;
+    g.N_s = N;
+    g.K_s = K;
+    g.n_shards = 1;
+    g.k_shards = 1;
+    g.epilogue = epi;
+    g.out = out;
+    g.ldo = ldo;
+    g.out_f32 = out_f32;
+    g.aux = u;
+    return from_hip(launch_gemm(g, stream));
+  };
+  if ((s = from_hip(launch_transpose(x, 0, 0, n, h, h, xt, np, stream))) != TSP_OK) return s;
+  if ((s = from_hip(launch_transpose(dy, 0, 0, n, h, h, dyt, np, stream))) != TSP_OK) return s;
+  for (int k = 0; k < D; ++k) {
+    const int d = (start_shard + k) % D;
+    // U = x W1_d^T (fp32); GELU(U)^T; W2_d^T
+    if ((s = gemm(x, h, w1[d], (int32_t)n, fs, (int32_t)h, EPI_RESID, u, fs, 1)) != TSP_OK) return s;
+    if ((s = from_hip(launch_transpose(u, 1, 1, n, fs, fs, ht, np, stream))) != TSP_OK) return s;
+    if ((s = from_hip(launch_transpose(w2[d], 0, 0, h, fs, fs, w2t, h, stream))) != TSP_OK) return s;
+    // dU_d = (dy W2_d) * GELU'(U) -> block d of dU; its transpose
+    if ((s = gemm(dy, h, w2t, (int32_t)n, fs, (int32_t)h, EPI_DGELU, du + (int64_t)d * fs, F, 0)) != TSP_OK) return s;
+    if ((s = from_hip(launch_transpose(du + (int64_t)d * fs, 0, 0, n, fs, F, dut, np, stream))) != TSP_OK) return s;
+    // dW2_d = dy^T GELU(U); dW1_d = dU_d^T x  (contractions over the tokens)
+    if ((s = gemm(dyt, np, ht, (int32_t)h, fs, (int32_t)np, EPI_RESID, dw2[d], fs, 1)) != TSP_OK) return s;
+    if ((s = gemm(dut, np, xt, fs, (int32_t)h, (int32_t)np, EPI_RESID, dw1[d], h, 1)) != TSP_OK) return s;
+    // W1_d^T for dx
+    if ((s = from_hip(launch_transpose(w1[d], 0, 0, fs, h, h, w1t + (int64_t)d * h * fs, fs, stream))) != TSP_OK)
+      return s;
+  }
+  // dx = [dy +] sum_k dU[:, d_k block] W1_{d_k}: the ring's split-K, fp32 in registers
+  GemmArgs g{};
+  g.A = du;
+  g.lda = F;
+  for (int d = 0; d < D; ++d) g.B[d] = w1t + (int64_t)d * h * fs;
+  g.M = (int32_t)n;
+  g.N_s = (int32_t)h;
+  g.K_s = fs;
+  g.n_shards = 1;
+  g.k_shards = D;
+  g.ring_start = start_shard;
+  g.epilogue = EPI_RESID;
+  g.out = dx;
+  g.ldo = h;
+  g.residual = residual ? dy : nullptr;
+  return from_hip(launch_gemm(g, stream));
 }
 
 const char* tsp_status_string(tsp_status status) {

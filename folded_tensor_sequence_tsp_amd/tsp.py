@@ -18,13 +18,13 @@ import torch
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libtsp.so")
 
 TSP_OK, TSP_ERR_INVALID_ARG, TSP_ERR_SHAPE, TSP_ERR_ALIGNMENT, TSP_ERR_WORKSPACE, TSP_ERR_UNSUPPORTED, TSP_ERR_HIP = range(7)
-WS_ATTN, WS_MLP, WS_LAYER, WS_POST, WS_CORE, WS_OUT_SHARD, WS_MLP_SHARD = 0, 1, 2, 3, 4, 5, 6
+WS_ATTN, WS_MLP, WS_LAYER, WS_POST, WS_CORE, WS_OUT_SHARD, WS_MLP_SHARD, WS_MLP_BWD = 0, 1, 2, 3, 4, 5, 6, 7
 MAX_D = 16
 
 EXPORTS = ["tsp_zigzag_plan", "tsp_workspace_size", "tsp_attn_project", "tsp_attn_core", "tsp_attn_out",
            "tsp_attn_forward", "tsp_mlp_forward", "tsp_layer_post", "tsp_layer_forward", "tsp_attn_project_shard",
            "tsp_attn_out_shard", "tsp_mlp_shard", "tsp_rms_norm", "tsp_rope", "tsp_attn_project_gqa",
-           "tsp_attn_core_gqa", "tsp_status_string"]
+           "tsp_attn_core_gqa", "tsp_mlp_backward", "tsp_status_string"]
 
 
 class TSPError(RuntimeError):
@@ -70,6 +70,8 @@ def lib() -> ctypes.CDLL:
             "tsp_rope": [POINTER(Plan), c_int32, c_int32, c_int32, ctypes.c_double, P, P, P],
             "tsp_attn_project_gqa": [POINTER(Plan), POINTER(Dims), c_int32, P, PP, P, P, P, P],
             "tsp_attn_core_gqa": [POINTER(Plan), POINTER(Dims), c_int32, P, P, P, P, P, P, c_size_t, P],
+            "tsp_mlp_backward": [c_int64, POINTER(Dims), c_int32, c_int32, c_int32, P, PP, PP, P, P, PP, PP, P,
+                                 c_size_t, P],
             "tsp_status_string": [c_int32],
         }
         for name, args in sig.items():
@@ -312,6 +314,31 @@ def attn_core_gqa(plan: Plan, dims: Dims, n_kv_heads: int, q, k_full, v_full, at
             _dev_tensor(attn_out, (n, h), "attn_out"), _opt_tensor(attn_lo, (n, h), "attn_lo"))
     _check(lib().tsp_attn_core_gqa(ctypes.byref(plan), ctypes.byref(dims), n_kv_heads, *args, ws, nbytes,
                                    _stream(stream)), "tsp_attn_core_gqa")
+
+
+def _f32_shards(ts, D: int, shape, name: str):
+    if len(ts) != D:
+        raise ValueError(f"{name}: expected {D} shards, got {len(ts)}")
+    arr = (c_void_p * D)()
+    for d, t in enumerate(ts):
+        if not isinstance(t, torch.Tensor) or t.dtype != torch.float32 or t.device.type != "cuda" \
+                or not t.is_contiguous() or tuple(t.shape) != tuple(shape):
+            raise ValueError(f"{name}[{d}]: expected a contiguous float32 HIP tensor of shape {tuple(shape)}")
+        arr[d] = t.data_ptr()
+    return arr
+
+
+def mlp_backward(dims: Dims, D: int, start_shard: int, residual: bool, x, w1, w2, dy, dx, dw1, dw2, workspace,
+                 stream=None):
+    n, h = x.shape[0], dims.hidden
+    Fs = dims.ffn // D if D > 0 else 0
+    need = workspace_size(n, dims, D, WS_MLP_BWD)
+    ws, nbytes = _workspace(workspace, need)
+    args = (_dev_tensor(x, (n, h), "x"), _shards(w1, D, (Fs, h), "w1"), _shards(w2, D, (h, Fs), "w2"),
+            _dev_tensor(dy, (n, h), "dy"), _dev_tensor(dx, (n, h), "dx"), _f32_shards(dw1, D, (Fs, h), "dw1"),
+            _f32_shards(dw2, D, (h, Fs), "dw2"))
+    _check(lib().tsp_mlp_backward(n, ctypes.byref(dims), D, start_shard, int(bool(residual)), *args, ws, nbytes,
+                                  _stream(stream)), "tsp_mlp_backward")
 
 
 def alloc_workspace(n_tokens: int, dims: Dims, D: int, kind: int, device=None) -> torch.Tensor:

@@ -85,7 +85,8 @@ typedef enum {
   TSP_WS_POST = 3,
   TSP_WS_CORE = 4,
   TSP_WS_OUT_SHARD = 5,
-  TSP_WS_MLP_SHARD = 6
+  TSP_WS_MLP_SHARD = 6,
+  TSP_WS_MLP_BWD = 7
 } tsp_ws_kind;
 
 /*
@@ -111,7 +112,7 @@ tsp_status tsp_zigzag_plan(int64_t seq_len, int32_t D, int32_t rank, tsp_plan* p
  * or tsp_attn_core (TSP_WS_CORE) need for n_tokens local tokens (the kinds
  * that hold attention state size it for a sequence of D * n_tokens keys), and
  * the shard-streaming calls tsp_attn_out_shard (TSP_WS_OUT_SHARD) and
- * tsp_mlp_shard (TSP_WS_MLP_SHARD).  Returns 0 for invalid dims or kind.
+ * tsp_mlp_shard (TSP_WS_MLP_SHARD), and tsp_mlp_backward (TSP_WS_MLP_BWD).  Returns 0 for invalid dims or kind.
  * Workspace contents are scratch: nothing persists between calls, except the
  * fp32 accumulator (and row exponents) that the D calls of one ring of a
  * shard-streaming entry point pass from step to step.
@@ -370,6 +371,33 @@ tsp_status tsp_attn_project_gqa(const tsp_plan* plan, const tsp_dims* dims, int3
 tsp_status tsp_attn_core_gqa(const tsp_plan* plan, const tsp_dims* dims, int32_t n_kv_heads, const uint16_t* q,
                              const uint16_t* k_full, const uint16_t* v_full, uint16_t* attn_out, uint16_t* attn_lo,
                              void* workspace, size_t ws_bytes, hipStream_t stream);
+
+/*
+ * Backward pass of the MLP ring for the rank's own tokens (the pages describe
+ * the forward schedule; this is its chain rule).  For the forward
+ * y = [x +] sum_d GELU_tanh(x W1_d^T) W2_d^T and dy = dL/dy:
+ *   U_d = x W1_d^T,  dU_d = (dy W2_d) * GELU'(U_d)
+ *   dx    = [dy +] sum_k dU_{d_k} W1_{d_k},  d_k = (start_shard + k) mod D
+ *           (the ring's split-K, fp32 across all shards, like the forward W2)
+ *   dW1_d = dU_d^T x        fp32 [ffn/D x hidden]
+ *   dW2_d = dy^T GELU(U_d)  fp32 [hidden x ffn/D]
+ * The weight gradients are this rank's contributions over its tokens: shard
+ * d's full gradient is the sum of the D ranks' contributions (the
+ * reduce-scatter to the shard's owner).  Operands are bf16 with fp32
+ * accumulation; U is kept in fp32, dU and GELU(U) are rounded to bf16.
+ *   residual : nonzero when the forward added x (then dx includes dy).
+ *   x, dy    : device, bf16 [n_tokens x hidden].
+ *   w1, w2   : host arrays of D device pointers, bf16, as tsp_mlp_forward.
+ *   dx       : device, bf16 [n_tokens x hidden]; must not alias x or dy.
+ *   dw1, dw2 : host arrays of D device pointers, fp32 [ffn/D x hidden] and
+ *              [hidden x ffn/D], overwritten.
+ *   workspace: >= tsp_workspace_size(n_tokens, dims, D, TSP_WS_MLP_BWD) bytes.
+ * Errors: as tsp_mlp_forward.
+ */
+tsp_status tsp_mlp_backward(int64_t n_tokens, const tsp_dims* dims, int32_t D, int32_t start_shard,
+                            int32_t residual, const uint16_t* x, const uint16_t* const* w1,
+                            const uint16_t* const* w2, const uint16_t* dy, uint16_t* dx, float* const* dw1,
+                            float* const* dw2, void* workspace, size_t ws_bytes, hipStream_t stream);
 
 /* Static text for a status code (never null). */
 const char* tsp_status_string(tsp_status status);

@@ -235,7 +235,7 @@ def test_workspace_sizes(L):
     assert core == 4 * n * 256 * 2  # V^T tiles for S = D * n keys
     assert attn == 3 * n * 256 * 2 + core  # Q, the attention output as a (hi, lo) bf16 pair, V^T
     assert layer == attn + post
-    assert tsp.workspace_size(n, d, 4, 7) == 0
+    assert tsp.workspace_size(n, d, 4, 99) == 0
     assert tsp.workspace_size(n, _dims(hidden=300), 4, tsp.WS_LAYER) == 0
     assert tsp.workspace_size(-1, d, 4, tsp.WS_ATTN) == 0
 
@@ -314,3 +314,29 @@ def test_variants_reject(L):
     proj = lambda kv: L.tsp_attn_project_gqa(ctypes.byref(p), ctypes.byref(d), kv, A, w, A + 64, A + 128, A + 192, None)
     assert proj(2) == tsp.TSP_ERR_SHAPE          # 2 K/V heads do not split over D = 4 shards
     assert proj(3) == tsp.TSP_ERR_SHAPE
+
+
+def test_mlp_backward_rejects(L):
+    d = _dims()
+    n = 300
+    np_ = 320  # tokens rounded up to 64
+    need = tsp.workspace_size(n, d, 4, tsp.WS_MLP_BWD)
+    # x^T, dy^T, U (fp32), GELU(U)^T, dU^T, dU (all shards), W1^T (all shards), W2^T
+    assert need == (2 * 256 * np_ * 2 + n * 256 * 4 + 2 * 256 * np_ * 2 + n * 1024 * 2 + 256 * 1024 * 2
+                    + 256 * 256 * 2 + 256 * 32 * 0)
+    w = _arr([A] * 4)
+    g = _arr([A + 512] * 4)
+    call = lambda **k: L.tsp_mlp_backward(k.get("n", n), ctypes.byref(k.get("dims", d)), 4, k.get("start", 0), 1,
+                                          k.get("x", A), k.get("w1", w), k.get("w2", w), k.get("dy", A + 64),
+                                          k.get("dx", A + 128), k.get("dw1", g), k.get("dw2", g),
+                                          k.get("ws", A + 256), k.get("nb", need), None)
+    assert call(start=4) == tsp.TSP_ERR_INVALID_ARG
+    assert call(dx=A) == tsp.TSP_ERR_INVALID_ARG                    # dx aliases x
+    assert call(dx=A + 64) == tsp.TSP_ERR_INVALID_ARG               # dx aliases dy
+    assert call(dw1=None) == tsp.TSP_ERR_INVALID_ARG
+    assert call(dw2=_arr([A, A, 0, A])) == tsp.TSP_ERR_INVALID_ARG
+    assert call(dw1=_arr([A, MIS, A, A])) == tsp.TSP_ERR_ALIGNMENT
+    assert call(nb=need - 1) == tsp.TSP_ERR_WORKSPACE
+    assert call(ws=None) == tsp.TSP_ERR_WORKSPACE
+    assert call(dims=_dims(ffn=1002)) == tsp.TSP_ERR_SHAPE
+    assert call(n=-1) == tsp.TSP_ERR_SHAPE
