@@ -19,8 +19,9 @@ After the timed steps, each step's entry point is also timed alone on layer
 0's inputs (``rows_layer0``: QKV projection, attention, O projection, MLP),
 each against the bf16 MFMA peak, and so are the shard-streaming forms of the
 projections and the MLP (the D ring steps called one by one, weights
-resident) and the layer variants (RMSNorm and RoPE against the HBM peak,
-grouped-query attention with 8 K/V heads).
+resident), the MLP ring's backward, and the layer variants (RMSNorm and RoPE
+against the HBM peak, grouped-query attention with 8 K/V heads); ``--no-rows``
+skips them.
 
 Prints ONE JSON line.  ``--gpus`` above 1 is refused: this build runs on one GPU.
 """
@@ -95,6 +96,17 @@ def row_timings(plan, dims, D, layer0, x0, q, a, a_lo, out, ws_core, fl, dev, re
         ("A5 streamed: D x tsp_attn_out_shard", "oproj", out_streamed),
         ("A6+A7 streamed: D x tsp_mlp_shard", "mlp", mlp_streamed),
     ]
+    # backward of the MLP ring on layer 0's shapes: recomputes U = x W1^T, then
+    # dU, dW2, dW1 and dx (five n x h x F products, 10 n h F FLOPs)
+    dy = (torch.randn(n, dims.hidden, device=dev) * 0.02).to(torch.bfloat16)
+    dx = torch.empty_like(dy)
+    Fs = dims.ffn // D
+    dw1 = [torch.empty(Fs, dims.hidden, dtype=torch.float32, device=dev) for _ in range(D)]
+    dw2 = [torch.empty(dims.hidden, Fs, dtype=torch.float32, device=dev) for _ in range(D)]
+    ws_bwd = tsp.alloc_workspace(n, dims, D, tsp.WS_MLP_BWD, device=dev)
+    fl = dict(fl, mlp_bwd=10.0 * n * dims.hidden * dims.ffn)
+    calls.append(("MLP backward: dx ring + dW1, dW2 per shard (tsp_mlp_backward)", "mlp_bwd",
+                  lambda: tsp.mlp_backward(dims, D, plan.rank, True, x0, lw.w1, lw.w2, dy, dx, dw1, dw2, ws_bwd)))
     # layer variants on the same shapes: RMSNorm and RoPE (HBM-bound passes),
     # attention with 8 K/V heads (grouped-query) on generated K/V of that width
     h, H, hd = dims.hidden, dims.n_heads, dims.head_dim
@@ -127,7 +139,7 @@ def row_timings(plan, dims, D, layer0, x0, q, a, a_lo, out, ws_core, fl, dev, re
         else:
             tf = fl[key] / (ms * 1e-3) / 1e12
             rows[name] = {"ms": round(ms, 4), "tflops": round(tf, 1), "frac": round(tf / PEAK_BF16_TFLOPS, 4)}
-    del ws_mlp, ws_mlp_s, ws_out_s, k8, v8
+    del ws_mlp, ws_mlp_s, ws_out_s, k8, v8, ws_bwd, dw1, dw2, dy, dx
     return rows
 
 
@@ -139,6 +151,9 @@ def parse():
     ap.add_argument("--workload", default="full_7b_128k", choices=["full_7b_128k", "stream_7b_16k"])
     ap.add_argument("--layers", type=int, default=None, help="layers per step (default: the workload's)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-rows", action="store_true",
+                    help="skip the per-entry-point timings after the timed steps (a kernel-trace profile of the "
+                         "timed steps alone then averages only their launches)")
     ap.add_argument("--cpu-rows", type=int, default=4, help="oracle sample rows per timing call")
     ap.add_argument("--copy-probe-mib", type=int, default=0,
                     help="also run one plain device copy of this many MiB before timing, so that a counter "
@@ -335,7 +350,9 @@ def main():
         "cpu_baseline": None,
     }
     print("[bench] per-step timing on layer 0", file=sys.stderr, flush=True)
-    result["rows_layer0"] = row_timings(plan, dims, D, layers[0], x0, q, a, a_lo, bufs[0], ws_core, fl_rows, dev)
+    if not args.no_rows:
+        result["rows_layer0"] = row_timings(plan, dims, D, layers[0], x0, q, a, a_lo, bufs[0], ws_core, fl_rows,
+                                            dev)
     if not args.no_cpu_baseline:
         print("[bench] cpu baseline (fp64 oracle, bounded sample)", file=sys.stderr, flush=True)
         result["cpu_baseline"] = cpu_baseline(W, plan, x0, layers[0], args.cpu_rows)
