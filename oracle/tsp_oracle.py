@@ -50,6 +50,11 @@ definitions (Zhang & Sennrich 2019; Su et al. 2021, RoFormer, with the
 interleaved pairs (x_{2i}, x_{2i+1}) of that paper; Ainslie et al. 2023),
 for the layer variants of a real decoder.
 
+Backward passes at the end of the module (the MLP ring and causal attention)
+are the chain rule of the forward definitions above, written out per shard
+and per head; the pages name training as a use of the method but give no
+backward.
+
 Parity status: every function here is pinned by ``tests/test_oracle_*.py``
 (library special cases, closed forms, invariants and brute force); none is
 "parity unpinned".
@@ -392,3 +397,54 @@ def mlp_backward(x, w1, w2, dy, residual=True):
         dw1.append(torch.matmul(dU.t(), xx))
         dw2.append(torch.matmul(g.t(), H))
     return dx, dw1, dw2
+
+
+def attention_lse(q: torch.Tensor, positions: torch.Tensor, k: torch.Tensor, n_heads: int,
+                  head_dim: int) -> torch.Tensor:
+    """lse[a, t] = log sum_{j <= p_t} exp(q[t,a] . k[j,a] / sqrt(hd)): the natural
+    log of the causal softmax's normaliser, per head a and query row t
+    ([n_heads, m]).  Written out as the row maximum plus the log of the sum of
+    the shifted exponentials."""
+    m, S = q.shape[0], k.shape[0]
+    future = torch.arange(S, dtype=torch.int64)[None, :] > positions[:, None]
+    out = torch.empty((n_heads, m), dtype=F64)
+    for a in range(n_heads):
+        cols = slice(a * head_dim, (a + 1) * head_dim)
+        s = torch.matmul(q[:, cols], k[:, cols].t()) / math.sqrt(head_dim)
+        s = s.masked_fill(future, float("-inf"))
+        s_max = s.max(dim=1).values
+        out[a] = s_max + torch.log(torch.exp(s - s_max[:, None]).sum(dim=1))
+    return out
+
+
+def causal_attention_backward(q: torch.Tensor, positions: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
+                              dout: torch.Tensor, n_heads: int, head_dim: int):
+    """Gradients of o = causal_attention(q, positions, k, v) given dout = dL/do,
+    per head, from the chain rule through o = P V, P = softmax_rows(S),
+    S = q k^T / sqrt(hd) (causal mask as in the forward):
+        dV = P^T dO,   dP = dO V^T,
+        dS[t, j] = P[t, j] (dP[t, j] - sum_i P[t, i] dP[t, i])   (softmax Jacobian),
+        dQ = dS K / sqrt(hd),   dK = dS^T Q / sqrt(hd).
+    ``q`` [m, H*hd] are this rank's query rows at ``positions``; ``k``/``v``
+    [S, H*hd] the full sequence.  Returns (dq [m, H*hd], dk [S, H*hd],
+    dv [S, H*hd]); dk and dv are this rank's contributions for every key row
+    (the owners of the key rows would sum them over ranks), zero for keys no
+    local query sees."""
+    m, S = q.shape[0], k.shape[0]
+    future = torch.arange(S, dtype=torch.int64)[None, :] > positions[:, None]
+    scale = 1.0 / math.sqrt(head_dim)
+    dq = torch.zeros((m, n_heads * head_dim), dtype=F64)
+    dk = torch.zeros((S, n_heads * head_dim), dtype=F64)
+    dv = torch.zeros((S, n_heads * head_dim), dtype=F64)
+    for a in range(n_heads):
+        cols = slice(a * head_dim, (a + 1) * head_dim)
+        qa, ka, va, ga = q[:, cols], k[:, cols], v[:, cols], dout[:, cols]
+        s = (torch.matmul(qa, ka.t()) * scale).masked_fill(future, float("-inf"))
+        e = torch.exp(s - s.max(dim=1, keepdim=True).values)
+        p = e / e.sum(dim=1, keepdim=True)
+        dv[:, cols] = torch.matmul(p.t(), ga)
+        dp = torch.matmul(ga, va.t())
+        ds = p * (dp - (p * dp).sum(dim=1, keepdim=True))
+        dq[:, cols] = torch.matmul(ds, ka) * scale
+        dk[:, cols] = torch.matmul(ds.t(), qa) * scale
+    return dq, dk, dv
