@@ -19,7 +19,7 @@ After the timed steps, each step's entry point is also timed alone on layer
 0's inputs (``rows_layer0``: QKV projection, attention, O projection, MLP),
 each against the bf16 MFMA peak, and so are the shard-streaming forms of the
 projections and the MLP (the D ring steps called one by one, weights
-resident), the MLP ring's backward, and the layer variants (RMSNorm and RoPE
+resident), the MLP ring's and the attention's backward, and the layer variants (RMSNorm and RoPE
 against the HBM peak, grouped-query attention with 8 K/V heads); ``--no-rows``
 skips them.
 
@@ -107,6 +107,20 @@ def row_timings(plan, dims, D, layer0, x0, q, a, a_lo, out, ws_core, fl, dev, re
     fl = dict(fl, mlp_bwd=10.0 * n * dims.hidden * dims.ffn)
     calls.append(("MLP backward: dx ring + dW1, dW2 per shard (tsp_mlp_backward)", "mlp_bwd",
                   lambda: tsp.mlp_backward(dims, D, plan.rank, True, x0, lw.w1, lw.w2, dy, dx, dw1, dw2, ws_bwd)))
+    # backward of the causal attention on layer 0's shapes (forward with the
+    # normaliser first, outside the timing): 5 products of the forward's size,
+    # 2.5x its FLOPs (the dQ kernel recomputes S and dP: 7 are executed)
+    lse = torch.empty(dims.n_heads, n, dtype=torch.float32, device=dev)
+    tsp.attn_core_lse(plan, dims, q, kf, vf, a, lse, attn_lo=a_lo, workspace=ws_core)
+    d_attn = (torch.randn(n, dims.hidden, device=dev) * 0.02).to(torch.bfloat16)
+    dq_b = torch.empty(n, dims.hidden, dtype=torch.float32, device=dev)
+    dk_b = torch.empty(plan.seq_len, dims.hidden, dtype=torch.float32, device=dev)
+    dv_b = torch.empty(plan.seq_len, dims.hidden, dtype=torch.float32, device=dev)
+    ws_abwd = tsp.alloc_workspace(n, dims, D, tsp.WS_ATTN_BWD, device=dev)
+    fl["attn_bwd"] = 2.5 * fl["attn"]
+    calls.append(("attention backward: dq, dk, dv contributions (tsp_attn_core_backward)", "attn_bwd",
+                  lambda: tsp.attn_core_backward(plan, dims, q, kf, vf, a, lse, d_attn, dq_b, dk_b, dv_b,
+                                                 attn_lo=a_lo, workspace=ws_abwd)))
     # layer variants on the same shapes: RMSNorm and RoPE (HBM-bound passes),
     # attention with 8 K/V heads (grouped-query) on generated K/V of that width
     h, H, hd = dims.hidden, dims.n_heads, dims.head_dim
@@ -139,7 +153,7 @@ def row_timings(plan, dims, D, layer0, x0, q, a, a_lo, out, ws_core, fl, dev, re
         else:
             tf = fl[key] / (ms * 1e-3) / 1e12
             rows[name] = {"ms": round(ms, 4), "tflops": round(tf, 1), "frac": round(tf / PEAK_BF16_TFLOPS, 4)}
-    del ws_mlp, ws_mlp_s, ws_out_s, k8, v8, ws_bwd, dw1, dw2, dy, dx
+    del ws_mlp, ws_mlp_s, ws_out_s, k8, v8, ws_bwd, dw1, dw2, dy, dx, ws_abwd, dq_b, dk_b, dv_b, lse, d_attn
     return rows
 
 

@@ -393,6 +393,9 @@ __global__ __launch_bounds__(NTHREADS) void attn_kernel(const AttnArgs a) {
   // ---- normalise and store: lane holds query ql, dims dt*32 + 8*(e/4) + 4*half + e%4.
   if (wave_active) {
     const float l_tot = l_run + __shfl_xor(l_run, 32);
+    if (a.lse && half == 0 && wave_first + ql < valid)  // sum_j exp(s_j) = 2^m_run * l_tot
+      a.lse[(int64_t)head * 2 * a.chunk_len + row0 + wave_first + ql] =
+          (m_run + log2f(l_tot)) * 0.69314718055994530942f;
     if (wave_first + ql < valid) {
       const float inv = 1.0f / l_tot;
       const int64_t off = (row0 + wave_first + ql) * ld + hcol + 4 * half;
@@ -423,13 +426,19 @@ __global__ __launch_bounds__(NTHREADS) void attn_kernel(const AttnArgs a) {
 
 int64_t attn_kv_tiles(int64_t seq_len) { return (seq_len + BKV - 1) / BKV; }
 
-hipError_t launch_vt_prep(const AttnArgs& a, hipStream_t stream) {
-  const dim3 grid((unsigned)a.n_kv_tiles, (unsigned)a.kv_heads), block(128);
-  if (a.head_dim == 128)
-    hipLaunchKernelGGL(vt_prep_kernel<128>, grid, block, 0, stream, a.v, a.seq_len, a.kv_ld, a.vt, a.n_kv_tiles);
+hipError_t launch_vt_tiles(const uint16_t* src, int64_t rows, int32_t ld, int32_t heads, int32_t head_dim,
+                           uint16_t* dst, int64_t n_tiles, hipStream_t stream) {
+  if (rows <= 0 || n_tiles <= 0) return hipSuccess;
+  const dim3 grid((unsigned)n_tiles, (unsigned)heads), block(128);
+  if (head_dim == 128)
+    hipLaunchKernelGGL(vt_prep_kernel<128>, grid, block, 0, stream, src, rows, ld, dst, n_tiles);
   else
-    hipLaunchKernelGGL(vt_prep_kernel<64>, grid, block, 0, stream, a.v, a.seq_len, a.kv_ld, a.vt, a.n_kv_tiles);
+    hipLaunchKernelGGL(vt_prep_kernel<64>, grid, block, 0, stream, src, rows, ld, dst, n_tiles);
   return hipGetLastError();
+}
+
+hipError_t launch_vt_prep(const AttnArgs& a, hipStream_t stream) {
+  return launch_vt_tiles(a.v, a.seq_len, a.kv_ld, a.kv_heads, a.head_dim, a.vt, a.n_kv_tiles, stream);
 }
 
 hipError_t launch_attention(const AttnArgs& a, hipStream_t stream) {

@@ -1,0 +1,496 @@
+// Backward of the causal attention of a rank's two zigzag query chunks against
+// the whole gathered K/V, for gfx950 (CDNA4).
+//
+// With S = q k^T / sqrt(hd) (causal), P = softmax rows, o = P v and dO the
+// gradient of o: dV = P^T dO, dP = dO V^T, dS = P * (dP - delta) with
+// delta = rowsum(dO * o), dQ = dS K / sqrt(hd), dK = dS^T Q / sqrt(hd).  P is
+// rebuilt from the scores and the forward's normaliser (no probabilities are
+// stored).  dK and dV are this rank's contributions for every key row; in TSP
+// the owners of the key rows would sum them over ranks, the reverse of the
+// K/V all-gather (zubnet.ai, "Zyphra TSP folds TP+SP onto one GPU axis",
+// para. 2).
+//
+// Two kernels, both with v_mfma_f32_32x32x16_bf16 and the operands of every
+// product read straight from registers or LDS in the lane layout the MFMA
+// wants (a 32x32 result holds, per lane, one column and 16 rows; fed back as
+// the B operand those rows are the contraction index, in the order
+// bits-2-and-3-swapped within 16-row groups, so the other operand is stored
+// in that order by the transposed-tile pre-pass):
+//   * dK/dV: a workgroup owns 128 keys of one head (32 per wave, K and V
+//     fragments in registers as B operands); it streams the 64-query tiles of
+//     both chunks that see those keys (Q and dO row-major for S = Q K^T and
+//     dP = dO V^T, Q^T and dO^T transposed for dV^T += dO^T P and
+//     dK^T += Q^T dS) through a two-stage LDS ring with direct global->LDS
+//     loads.  Lane = key, so P and dS leave the score registers as B operands;
+//   * dQ: a workgroup owns 128 queries of one chunk (32 per wave, Q and dO
+//     fragments in registers); it streams the 64-key tiles (K and V row-major
+//     for S^T = K Q^T and dP^T = V dO^T, K^T for dQ^T += K^T dS^T).
+//     Lane = query, so the normaliser and delta are per-lane scalars.
+#include "device_common.h"
+#include "kernels.h"
+
+namespace tsp {
+namespace {
+
+constexpr int BW = 4;  // waves per workgroup
+constexpr int BTHREADS = 64 * BW;
+constexpr float LOG2E = 1.44269504088896340736f;
+
+template <int HD>
+struct BCfg {
+  static constexpr int NCH = HD / 8;                    // 16-byte chunks per row-major row
+  static constexpr int TILE_BYTES = 64 * HD * 2;        // a 64-row tile, row-major or transposed
+  static constexpr int TLOADS = TILE_BYTES / (BTHREADS * 16);  // DMA instructions per thread per tile
+  static constexpr int RPL = 64 / NCH;                  // row-major rows per 1 KB block
+  static constexpr int KK = HD / 16;                    // MFMA k-steps over head_dim
+  static constexpr int DT = HD / 32;                    // 32-wide d tiles
+  static constexpr float INV_SQRT_HD = HD == 128 ? 0.08838834764831844055f : 0.125f;
+};
+
+// ---- stats: per (64-query tile, chunk, head), thread r = query row of the tile.
+template <int HD>
+__global__ __launch_bounds__(64) void bwd_stats_kernel(const AttnBwdArgs a) {
+  const int t = blockIdx.x, c = blockIdx.y, head = blockIdx.z;
+  const int r = threadIdx.x;
+  const int64_t row_in_chunk = (int64_t)t * 64 + r;
+  float l2 = INFINITY, dl = 0.0f;  // padding rows: probability exp2(s - inf) = 0
+  if (row_in_chunk < a.chunk_len) {
+    const int64_t row = c * a.chunk_len + row_in_chunk;
+    l2 = a.lse[(int64_t)head * 2 * a.chunk_len + row] * LOG2E;
+    const int64_t off = row * a.hidden + head * HD;
+    for (int d = 0; d < HD; d += 8) {
+      const u32x4 g = *reinterpret_cast<const u32x4*>(a.dout + off + d);
+      const u32x4 o = *reinterpret_cast<const u32x4*>(a.o + off + d);
+      u32x4 lo = u32x4{0u, 0u, 0u, 0u};
+      if (a.o_lo) lo = *reinterpret_cast<const u32x4*>(a.o_lo + off + d);
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const float o0 = __uint_as_float(o[j] << 16) + __uint_as_float(lo[j] << 16);
+        const float o1 = __uint_as_float(o[j] & 0xffff0000u) + __uint_as_float(lo[j] & 0xffff0000u);
+        dl = fmaf(__uint_as_float(g[j] << 16), o0, dl);
+        dl = fmaf(__uint_as_float(g[j] & 0xffff0000u), o1, dl);
+      }
+    }
+  }
+  float* st = a.stats + ((c * (int64_t)a.n_heads + head) * a.tpc + t) * 256;
+  st[r] = l2;
+  st[64 + r] = dl;
+  st[128 + r] = 0.0f;
+  st[192 + r] = 0.0f;
+}
+
+// ---- dK, dV.
+template <int HD>
+__global__ __launch_bounds__(BTHREADS) void dkv_kernel(const AttnBwdArgs a) {
+  using C = BCfg<HD>;
+  constexpr int STATS = 1024;                       // per wave: its own copy of the tile's stats
+  constexpr int STAGE = 4 * C::TILE_BYTES + BW * STATS;
+  constexpr int LOADS = 4 * C::TLOADS + 1;          // DMA instructions per wave per tile
+  __shared__ __attribute__((aligned(1024))) uint8_t smem[2 * STAGE];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int half = lane >> 5;
+  const int ql = lane & 31;
+
+  // work item: (head, 128-key block), the earliest (most-seen) key blocks of a
+  // head first, heads contiguous per XCD.
+  const int64_t S = a.seq_len, CL = a.chunk_len;
+  const int nkb = (int)((S + 127) / 128);
+  const int nwg = gridDim.x;
+  int pid = blockIdx.x;
+  if ((nwg & 7) == 0) pid = (pid & 7) * (nwg >> 3) + (pid >> 3);
+  const int head = pid / nkb;
+  const int kblk = pid - head * nkb;
+  const int64_t kb0 = (int64_t)kblk * 128;
+  const int64_t kw0 = kb0 + 32 * wave;  // this wave's first key
+  const int64_t key = kw0 + ql;         // this lane's key
+  const int hcol = head * HD;
+  const int64_t ld = a.hidden;
+
+  // K and V fragments (B operands): lane holds key ql, dims 16*kk + 8*half .. +7.
+  u32x4 kf[C::KK], vf[C::KK];
+  {
+    const int64_t kr = min(key, S - 1);  // keys past S: any finite row (masked: past every query)
+    const uint16_t* kp = a.k + kr * ld + hcol + 8 * half;
+    const uint16_t* vp = a.v + kr * ld + hcol + 8 * half;
+#pragma unroll
+    for (int kk = 0; kk < C::KK; ++kk) {
+      kf[kk] = *reinterpret_cast<const u32x4*>(kp + kk * 16);
+      vf[kk] = *reinterpret_cast<const u32x4*>(vp + kk * 16);
+    }
+  }
+
+  // Query tiles that see the block: chunk c's tiles from the one holding the
+  // first query at or after kb0 to the chunk's end.
+  const int tpc = (int)a.tpc;
+  auto first_tile = [&](int64_t start) -> int {
+    if (kb0 >= start + CL) return tpc;
+    return (int)(max(kb0 - start, (int64_t)0) / 64);
+  };
+  const int f0 = first_tile(a.chunk_start0), f1 = first_tile(a.chunk_start1);
+  const int n0 = tpc - f0, n_all = n0 + tpc - f1;
+
+  // DMA sources.  Row-major tiles: instruction j of wave w fills 1 KB block
+  // b = j*BW + w, row b*RPL + lane/NCH, logical chunk (lane % NCH) ^ (row % NCH).
+  // Transposed tiles: row d = b*8 + lane/8 (128 bytes), chunk (lane % 8) ^ ((d/2) % 8).
+  int rm_row[C::TLOADS], rm_col[C::TLOADS], tr_off[C::TLOADS];
+#pragma unroll
+  for (int j = 0; j < C::TLOADS; ++j) {
+    const int b = j * BW + wave;
+    const int r = b * C::RPL + lane / C::NCH;
+    rm_row[j] = r;
+    rm_col[j] = ((lane % C::NCH) ^ (r & (C::NCH - 1))) * 8;
+    const int d = b * 8 + lane / 8;
+    tr_off[j] = d * 64 + ((lane % 8) ^ ((d >> 1) & 7)) * 8;
+  }
+
+  auto tile_of = [&](int i, int& c, int& t) __attribute__((always_inline)) {
+    if (i < n0) {
+      c = 0;
+      t = f0 + i;
+    } else {
+      c = 1;
+      t = f1 + (i - n0);
+    }
+  };
+
+  auto issue = [&](int i) __attribute__((always_inline)) {
+    int c, t;
+    tile_of(i, c, t);
+    uint8_t* stage = smem + (i & 1) * STAGE;
+    const int64_t rbase = c * CL;
+#pragma unroll
+    for (int j = 0; j < C::TLOADS; ++j) {
+      const int64_t row = rbase + min((int64_t)t * 64 + rm_row[j], CL - 1);  // padding rows: any row of the chunk
+      const int64_t off = row * ld + hcol + rm_col[j];
+      dma16(a.q + off, stage + (j * BW + wave) * 1024);
+      dma16(a.dout + off, stage + C::TILE_BYTES + (j * BW + wave) * 1024);
+    }
+    const int64_t tbase = ((c * (int64_t)a.n_heads + head) * a.tpc + t) * (int64_t)(HD * 64);
+#pragma unroll
+    for (int j = 0; j < C::TLOADS; ++j) {
+      dma16(a.qt + tbase + tr_off[j], stage + 2 * C::TILE_BYTES + (j * BW + wave) * 1024);
+      dma16(a.dot + tbase + tr_off[j], stage + 3 * C::TILE_BYTES + (j * BW + wave) * 1024);
+    }
+    const float* st = a.stats + ((c * (int64_t)a.n_heads + head) * a.tpc + t) * 256;
+    dma16(st + lane * 4, stage + 4 * C::TILE_BYTES + wave * STATS);
+  };
+
+  // fragment addresses within a stage (see the DMA swizzles above)
+  const uint32_t rm_a0 = (uint32_t)ql * (HD * 2) + ((uint32_t)(half ^ (ql & (C::NCH - 1))) << 4);
+  const uint32_t tr_a0 = (uint32_t)ql * 128 + ((uint32_t)(half ^ ((ql >> 1) & 7)) << 4);
+  const float scale_log2 = LOG2E * C::INV_SQRT_HD;
+
+  f32x16 dkT[C::DT], dvT[C::DT];  // [d][key]: lane holds key ql, dims dt*32 + 8*(e/4) + 4*half + e%4
+#pragma unroll
+  for (int dt = 0; dt < C::DT; ++dt) {
+    dkT[dt] = f32x16{};
+    dvT[dt] = f32x16{};
+  }
+
+  auto compute = [&](int i) __attribute__((always_inline)) {
+    int c, t;
+    tile_of(i, c, t);
+    const int64_t qp0 = (c ? a.chunk_start1 : a.chunk_start0) + (int64_t)t * 64;  // position of query 0
+    if (kw0 > qp0 + 63) return;  // every key of the wave is past every query of the tile (wave-uniform)
+    const bool need_mask = kw0 + 31 > qp0;
+    const uint8_t* stage = smem + (i & 1) * STAGE;
+    const uint8_t* q_st = stage;
+    const uint8_t* do_st = stage + C::TILE_BYTES;
+    const uint8_t* qt_st = stage + 2 * C::TILE_BYTES;
+    const uint8_t* dot_st = stage + 3 * C::TILE_BYTES;
+    const float* st = reinterpret_cast<const float*>(stage + 4 * C::TILE_BYTES + wave * STATS);
+    uint32_t pp[16], ps[16];  // bf16 pairs of P and dS: [4*ks + j], 16-query step ks
+#pragma unroll
+    for (int mb = 0; mb < 2; ++mb) {
+      f32x16 s = f32x16{}, dp = f32x16{};
+#pragma unroll
+      for (int kk = 0; kk < C::KK; ++kk) {
+        const uint32_t ad = mb * 32 * (HD * 2) + (rm_a0 ^ (uint32_t)(kk << 5));
+        const u32x4 qa = *reinterpret_cast<const u32x4*>(q_st + ad);
+        const u32x4 da = *reinterpret_cast<const u32x4*>(do_st + ad);
+        s = mfma32(as_bf16x8(qa), as_bf16x8(kf[kk]), s);
+        dp = mfma32(as_bf16x8(da), as_bf16x8(vf[kk]), dp);
+      }
+      // entry e: query 32*mb + 8*(e/4) + 4*half + e%4 of the tile, key = this lane's
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const int q0 = 32 * mb + 8 * g + 4 * half;
+        const f32x4 l2 = *reinterpret_cast<const f32x4*>(st + q0);
+        const f32x4 dl = *reinterpret_cast<const f32x4*>(st + 64 + q0);
+        float p[4], ds[4];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          p[j] = __builtin_amdgcn_exp2f(fmaf(s[4 * g + j], scale_log2, -l2[j]));
+          if (need_mask && key > qp0 + q0 + j) p[j] = 0.0f;
+          ds[j] = p[j] * (dp[4 * g + j] - dl[j]);
+        }
+        const int idx = 8 * mb + 2 * g;  // pairs (4*ks + j): ks = 2*mb + g/2, j = 2*(g%2) + 0/1
+        pp[idx] = pack_bf16x2(p[0], p[1]);
+        pp[idx + 1] = pack_bf16x2(p[2], p[3]);
+        ps[idx] = pack_bf16x2(ds[0], ds[1]);
+        ps[idx + 1] = pack_bf16x2(ds[2], ds[3]);
+      }
+    }
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) {
+      const u32x4 bp = u32x4{pp[4 * ks], pp[4 * ks + 1], pp[4 * ks + 2], pp[4 * ks + 3]};
+      const u32x4 bs = u32x4{ps[4 * ks], ps[4 * ks + 1], ps[4 * ks + 2], ps[4 * ks + 3]};
+#pragma unroll
+      for (int dt = 0; dt < C::DT; ++dt) {
+        const uint32_t ad = dt * 32 * 128 + (tr_a0 ^ (uint32_t)(ks << 5));
+        const u32x4 oa = *reinterpret_cast<const u32x4*>(dot_st + ad);
+        const u32x4 qa = *reinterpret_cast<const u32x4*>(qt_st + ad);
+        dvT[dt] = mfma32(as_bf16x8(oa), as_bf16x8(bp), dvT[dt]);
+        dkT[dt] = mfma32(as_bf16x8(qa), as_bf16x8(bs), dkT[dt]);
+      }
+    }
+  };
+
+  if (n_all > 0) issue(0);
+  for (int i = 0; i < n_all; ++i) {
+    if (i + 1 < n_all) {
+      issue(i + 1);
+      wait_vmcnt<LOADS>();
+    } else {
+      wait_vmcnt<0>();
+    }
+    lds_barrier();
+    compute(i);
+    lds_barrier();
+  }
+
+  // store this lane's key row of dK (scaled) and dV; zeros where no query sees the key
+  if (key < S) {
+    float* dkp = a.dk + key * ld + hcol + 4 * half;
+    float* dvp = a.dv + key * ld + hcol + 4 * half;
+#pragma unroll
+    for (int dt = 0; dt < C::DT; ++dt)
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const int d = dt * 32 + 8 * g;
+        *reinterpret_cast<f32x4*>(dkp + d) =
+            f32x4{dkT[dt][4 * g], dkT[dt][4 * g + 1], dkT[dt][4 * g + 2], dkT[dt][4 * g + 3]} * C::INV_SQRT_HD;
+        *reinterpret_cast<f32x4*>(dvp + d) =
+            f32x4{dvT[dt][4 * g], dvT[dt][4 * g + 1], dvT[dt][4 * g + 2], dvT[dt][4 * g + 3]};
+      }
+  }
+}
+
+// ---- dQ.
+template <int HD>
+__global__ __launch_bounds__(BTHREADS) void dq_kernel(const AttnBwdArgs a) {
+  using C = BCfg<HD>;
+  constexpr int QTB = 32 * BW;  // queries per workgroup
+  constexpr int STAGE = 3 * C::TILE_BYTES;
+  constexpr int LOADS = 3 * C::TLOADS;
+  __shared__ __attribute__((aligned(1024))) uint8_t smem[2 * STAGE];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int half = lane >> 5;
+  const int ql = lane & 31;
+
+  // work item: (head, chunk, 128-query tile), the latest (heaviest) tiles of a
+  // head first, heads contiguous per XCD.
+  const int64_t CL = a.chunk_len;
+  const int tpcb = (int)((CL + QTB - 1) / QTB);
+  const int per_head = 2 * tpcb;
+  const int nwg = gridDim.x;
+  int pid = blockIdx.x;
+  if ((nwg & 7) == 0) pid = (pid & 7) * (nwg >> 3) + (pid >> 3);
+  const int head = pid / per_head;
+  const int w = pid - head * per_head;
+  const int chunk = w < tpcb ? 1 : 0;
+  const int tile = w < tpcb ? tpcb - 1 - w : per_head - 1 - w;
+
+  const int64_t row0 = chunk * CL + (int64_t)tile * QTB;  // local row of query 0
+  const int64_t pos0 = (chunk ? a.chunk_start1 : a.chunk_start0) + (int64_t)tile * QTB;
+  const int valid = (int)min((int64_t)QTB, CL - (int64_t)tile * QTB);
+  const int64_t key_end = pos0 + valid;
+  const int n_tiles = (int)((key_end + 63) / 64);
+
+  const int qi = min(wave * 32 + ql, valid - 1);  // this lane's query (clamped in the ragged tail)
+  const int64_t qpos = pos0 + qi;
+  const int wave_first = wave * 32;
+  const bool wave_active = wave_first < valid;
+  const int64_t wave_min_pos = pos0 + wave_first;
+  const int64_t wave_max_pos = pos0 + min(wave_first + 31, valid - 1);
+  const int wave_tiles = wave_active ? (int)(wave_max_pos / 64) + 1 : 0;
+
+  const int hcol = head * HD;
+  const int64_t ld = a.hidden;
+
+  // Q and dO fragments (B operands): lane holds query qi, dims 16*kk + 8*half .. +7.
+  u32x4 qf[C::KK], df[C::KK];
+  {
+    const int64_t off = (row0 + qi) * ld + hcol + 8 * half;
+#pragma unroll
+    for (int kk = 0; kk < C::KK; ++kk) {
+      qf[kk] = *reinterpret_cast<const u32x4*>(a.q + off + kk * 16);
+      df[kk] = *reinterpret_cast<const u32x4*>(a.dout + off + kk * 16);
+    }
+  }
+  float l2q, dlq;
+  {
+    const int64_t rq = (int64_t)tile * QTB + qi;  // row within the chunk
+    const float* st = a.stats + ((chunk * (int64_t)a.n_heads + head) * a.tpc + rq / 64) * 256 + rq % 64;
+    l2q = st[0];
+    dlq = st[64];
+  }
+
+  int rm_row[C::TLOADS], rm_col[C::TLOADS], tr_off[C::TLOADS];
+#pragma unroll
+  for (int j = 0; j < C::TLOADS; ++j) {
+    const int b = j * BW + wave;
+    const int r = b * C::RPL + lane / C::NCH;
+    rm_row[j] = r;
+    rm_col[j] = ((lane % C::NCH) ^ (r & (C::NCH - 1))) * 8;
+    const int d = b * 8 + lane / 8;
+    tr_off[j] = d * 64 + ((lane % 8) ^ ((d >> 1) & 7)) * 8;
+  }
+  const uint16_t* kt_head = a.kt + (int64_t)head * a.n_kv_tiles * HD * 64;
+
+  auto issue = [&](int t) __attribute__((always_inline)) {
+    uint8_t* stage = smem + (t & 1) * STAGE;
+    const int64_t k0 = (int64_t)t * 64;
+#pragma unroll
+    for (int j = 0; j < C::TLOADS; ++j) {
+      const int64_t kr = min(k0 + rm_row[j], key_end - 1);  // rows past the range: masked anyway
+      const int64_t off = kr * ld + hcol + rm_col[j];
+      dma16(a.k + off, stage + (j * BW + wave) * 1024);
+      dma16(a.v + off, stage + C::TILE_BYTES + (j * BW + wave) * 1024);
+      dma16(kt_head + (int64_t)t * HD * 64 + tr_off[j], stage + 2 * C::TILE_BYTES + (j * BW + wave) * 1024);
+    }
+  };
+
+  const uint32_t rm_a0 = (uint32_t)ql * (HD * 2) + ((uint32_t)(half ^ (ql & (C::NCH - 1))) << 4);
+  const uint32_t tr_a0 = (uint32_t)ql * 128 + ((uint32_t)(half ^ ((ql >> 1) & 7)) << 4);
+  const float scale_log2 = LOG2E * C::INV_SQRT_HD;
+
+  f32x16 dqT[C::DT];  // [d][query]: lane holds query ql, dims dt*32 + 8*(e/4) + 4*half + e%4
+#pragma unroll
+  for (int dt = 0; dt < C::DT; ++dt) dqT[dt] = f32x16{};
+
+  auto compute = [&](int t) __attribute__((always_inline)) {
+    if (t >= wave_tiles) return;  // wave-uniform
+    const uint8_t* stage = smem + (t & 1) * STAGE;
+    const int64_t k0 = (int64_t)t * 64;
+    const bool need_mask = k0 + 63 > wave_min_pos;
+    uint32_t ps[16];
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb) {
+      f32x16 s = f32x16{}, dp = f32x16{};
+#pragma unroll
+      for (int kk = 0; kk < C::KK; ++kk) {
+        const uint32_t ad = kb * 32 * (HD * 2) + (rm_a0 ^ (uint32_t)(kk << 5));
+        const u32x4 ka = *reinterpret_cast<const u32x4*>(stage + ad);
+        const u32x4 va = *reinterpret_cast<const u32x4*>(stage + C::TILE_BYTES + ad);
+        s = mfma32(as_bf16x8(ka), as_bf16x8(qf[kk]), s);
+        dp = mfma32(as_bf16x8(va), as_bf16x8(df[kk]), dp);
+      }
+      // entry e: key k0 + 32*kb + 8*(e/4) + 4*half + e%4, query = this lane's
+#pragma unroll
+      for (int e = 0; e < 16; e += 2) {
+        float p0 = __builtin_amdgcn_exp2f(fmaf(s[e], scale_log2, -l2q));
+        float p1 = __builtin_amdgcn_exp2f(fmaf(s[e + 1], scale_log2, -l2q));
+        if (need_mask) {
+          const int64_t kx = k0 + 32 * kb + 8 * (e >> 2) + 4 * half + (e & 3);
+          if (kx > qpos) p0 = 0.0f;
+          if (kx + 1 > qpos) p1 = 0.0f;
+        }
+        ps[8 * kb + e / 2] = pack_bf16x2(p0 * (dp[e] - dlq), p1 * (dp[e + 1] - dlq));
+      }
+    }
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) {
+      const u32x4 bs = u32x4{ps[4 * ks], ps[4 * ks + 1], ps[4 * ks + 2], ps[4 * ks + 3]};
+#pragma unroll
+      for (int dt = 0; dt < C::DT; ++dt) {
+        const u32x4 ka = *reinterpret_cast<const u32x4*>(stage + 2 * C::TILE_BYTES + dt * 32 * 128 +
+                                                         (tr_a0 ^ (uint32_t)(ks << 5)));
+        dqT[dt] = mfma32(as_bf16x8(ka), as_bf16x8(bs), dqT[dt]);
+      }
+    }
+  };
+
+  issue(0);
+  for (int t = 0; t < n_tiles; ++t) {
+    if (t + 1 < n_tiles) {
+      issue(t + 1);
+      wait_vmcnt<LOADS>();
+    } else {
+      wait_vmcnt<0>();
+    }
+    lds_barrier();
+    compute(t);
+    lds_barrier();
+  }
+
+  if (wave_active && wave_first + ql < valid) {
+    float* dqp = a.dq + (row0 + wave_first + ql) * ld + hcol + 4 * half;
+#pragma unroll
+    for (int dt = 0; dt < C::DT; ++dt)
+#pragma unroll
+      for (int g = 0; g < 4; ++g)
+        *reinterpret_cast<f32x4*>(dqp + dt * 32 + 8 * g) =
+            f32x4{dqT[dt][4 * g], dqT[dt][4 * g + 1], dqT[dt][4 * g + 2], dqT[dt][4 * g + 3]} * C::INV_SQRT_HD;
+  }
+}
+
+}  // namespace
+
+size_t attn_bwd_ws_bytes(int64_t seq_len, int64_t chunk_len, int32_t n_heads, int32_t head_dim) {
+  const int64_t n_kv_tiles = (seq_len + 63) / 64, tpc = (chunk_len + 63) / 64;
+  const size_t kt = (size_t)n_heads * n_kv_tiles * head_dim * 64 * 2;
+  const size_t qt = (size_t)2 * n_heads * tpc * head_dim * 64 * 2;
+  const size_t stats = (size_t)2 * n_heads * tpc * 256 * 4;
+  return kt + 2 * qt + stats;
+}
+
+hipError_t launch_attention_backward(const AttnBwdArgs& a, hipStream_t stream) {
+  if (a.chunk_len <= 0) return hipSuccess;
+  const int H = a.n_heads, HD = a.head_dim;
+  hipError_t e;
+  {
+    const dim3 grid((unsigned)a.tpc, 2, (unsigned)H);
+    if (HD == 128)
+      hipLaunchKernelGGL(bwd_stats_kernel<128>, grid, dim3(64), 0, stream, a);
+    else
+      hipLaunchKernelGGL(bwd_stats_kernel<64>, grid, dim3(64), 0, stream, a);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+  }
+  if ((e = launch_vt_tiles(a.k, a.seq_len, a.hidden, H, HD, a.kt, a.n_kv_tiles, stream)) != hipSuccess) return e;
+  const size_t chunk_tiles = (size_t)H * a.tpc * HD * 64;
+  for (int c = 0; c < 2; ++c) {
+    const int64_t off = c * a.chunk_len * a.hidden;
+    if ((e = launch_vt_tiles(a.q + off, a.chunk_len, a.hidden, H, HD, a.qt + c * chunk_tiles, a.tpc, stream)) !=
+        hipSuccess)
+      return e;
+    if ((e = launch_vt_tiles(a.dout + off, a.chunk_len, a.hidden, H, HD, a.dot + c * chunk_tiles, a.tpc,
+                             stream)) != hipSuccess)
+      return e;
+  }
+  {
+    const dim3 grid((unsigned)(H * ((a.seq_len + 127) / 128)));
+    if (HD == 128)
+      hipLaunchKernelGGL(dkv_kernel<128>, grid, dim3(BTHREADS), 0, stream, a);
+    else
+      hipLaunchKernelGGL(dkv_kernel<64>, grid, dim3(BTHREADS), 0, stream, a);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+  }
+  {
+    const dim3 grid((unsigned)(H * 2 * ((a.chunk_len + 127) / 128)));
+    if (HD == 128)
+      hipLaunchKernelGGL(dq_kernel<128>, grid, dim3(BTHREADS), 0, stream, a);
+    else
+      hipLaunchKernelGGL(dq_kernel<64>, grid, dim3(BTHREADS), 0, stream, a);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+  }
+  return hipSuccess;
+}
+
+}  // namespace tsp

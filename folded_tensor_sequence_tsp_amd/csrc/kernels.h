@@ -88,6 +88,9 @@ struct AttnArgs {
   // [kv_heads][n_kv_tiles][head_dim][64] bf16, keys permuted within 16-key groups.
   uint16_t* vt;
   int64_t n_kv_tiles;  // attn_kv_tiles(seq_len)
+  // nullable: lse[head * 2 * chunk_len + row] = ln sum_j exp(score), the
+  // natural log of each query row's softmax normaliser (kept for the backward).
+  float* lse;
 };
 
 // 64-key tiles covering seq_len keys.
@@ -95,6 +98,44 @@ int64_t attn_kv_tiles(int64_t seq_len);
 
 // V -> V^T tiles, then the attention kernel (both on `stream`).
 hipError_t launch_attention(const AttnArgs& args, hipStream_t stream);
+
+// Rows [0, rows) of src (row stride ld, head h in columns h*head_dim ..) ->
+// transposed 64-row tiles dst[((h * n_tiles + t) * head_dim + d) * 64 + k] =
+// src[t*64 + perm16(k)][h*head_dim + d], zero past `rows`; the rows of each
+// 16-row group in the order (bits 2 and 3 of the index swapped) in which a
+// 32x32 MFMA result holds them.  Grid (n_tiles, heads).
+hipError_t launch_vt_tiles(const uint16_t* src, int64_t rows, int32_t ld, int32_t heads, int32_t head_dim,
+                           uint16_t* dst, int64_t n_tiles, hipStream_t stream);
+
+// Backward of the causal attention of the two zigzag chunks (MHA).
+struct AttnBwdArgs {
+  const uint16_t* q;     // [n_local x hidden]
+  const uint16_t* k;     // [seq_len x hidden]
+  const uint16_t* v;     // [seq_len x hidden]
+  const uint16_t* o;     // [n_local x hidden], the forward's output
+  const uint16_t* o_lo;  // nullable: its low part
+  const uint16_t* dout;  // [n_local x hidden]
+  const float* lse;      // [n_heads x n_local], natural log of each row's softmax normaliser
+  float* dq;             // [n_local x hidden]
+  float* dk;             // [seq_len x hidden]: this rank's contributions, every key row
+  float* dv;             // [seq_len x hidden]
+  int64_t seq_len, chunk_len, chunk_start0, chunk_start1;
+  int32_t hidden, n_heads, head_dim;
+  // workspace: K^T tiles [H][n_kv_tiles][hd][64]; Q^T and dO^T tiles
+  // [2 chunks][H][tpc][hd][64]; per 64-query tile of (chunk, head) 256 floats:
+  // log2-domain normaliser [64], delta = rowsum(dO * O) [64], zeros [128].
+  uint16_t* kt;
+  uint16_t* qt;
+  uint16_t* dot;
+  float* stats;
+  int64_t n_kv_tiles, tpc;  // 64-key tiles of the sequence; 64-query tiles per chunk
+};
+
+// Workspace bytes of launch_attention_backward.
+size_t attn_bwd_ws_bytes(int64_t seq_len, int64_t chunk_len, int32_t n_heads, int32_t head_dim);
+
+// Pre-passes (stats, K^T, Q^T, dO^T tiles), then the dK/dV and dQ kernels.
+hipError_t launch_attention_backward(const AttnBwdArgs& args, hipStream_t stream);
 
 // y = x / sqrt(mean(x^2) + eps) * gain per row of x [n x h] (bf16; h % 8 == 0).
 hipError_t launch_rms_norm(const uint16_t* x, const uint16_t* gain, int64_t n, int32_t h, float eps, uint16_t* y,

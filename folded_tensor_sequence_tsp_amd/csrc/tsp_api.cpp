@@ -134,8 +134,9 @@ tsp_status run_project(const tsp_plan* plan, const tsp_dims* dims, const uint16_
 
 tsp_status run_core(const tsp_plan* plan, const tsp_dims* dims, const uint16_t* q, const uint16_t* k_full,
                     const uint16_t* v_full, uint16_t* attn_out, uint16_t* attn_lo, void* core_ws,
-                    hipStream_t stream) {
+                    hipStream_t stream, float* lse = nullptr) {
   AttnArgs a{};
+  a.lse = lse;
   a.q = q;
   a.k = k_full;
   a.v = v_full;
@@ -432,6 +433,9 @@ size_t tsp_workspace_size(int64_t n_tokens, const tsp_dims* dims, int32_t D, int
     case TSP_WS_MLP_BWD:
       if (check_dims(dims, D, false, true) != TSP_OK) return 0;
       return mlp_bwd_ws(n_tokens, dims, D).total;
+    case TSP_WS_ATTN_BWD:
+      if (check_dims(dims, D, true, false, 0) != TSP_OK || n_tokens % 2 != 0) return 0;
+      return attn_bwd_ws_bytes(n_tokens * D, n_tokens / 2, dims->n_heads, dims->head_dim);
     default:
       return 0;
   }
@@ -463,6 +467,73 @@ tsp_status tsp_attn_core(const tsp_plan* plan, const tsp_dims* dims, const uint1
   if (!aligned16(workspace)) return TSP_ERR_ALIGNMENT;
   if (ws_bytes < ws_core(plan->n_local, dims, plan->D)) return TSP_ERR_WORKSPACE;
   return run_core(plan, dims, q, k_full, v_full, attn_out, attn_lo, workspace, stream);
+}
+
+tsp_status tsp_attn_core_lse(const tsp_plan* plan, const tsp_dims* dims, const uint16_t* q, const uint16_t* k_full,
+                             const uint16_t* v_full, uint16_t* attn_out, uint16_t* attn_lo, float* lse,
+                             void* workspace, size_t ws_bytes, hipStream_t stream) {
+  tsp_status s;
+  if ((s = check_plan(plan)) != TSP_OK) return s;
+  if ((s = check_dims(dims, plan->D, true, false, 0)) != TSP_OK) return s;
+  if ((s = check_ptr(q)) != TSP_OK || (s = check_ptr(k_full)) != TSP_OK || (s = check_ptr(v_full)) != TSP_OK ||
+      (s = check_ptr(attn_out)) != TSP_OK || (s = check_ptr_nullable(attn_lo)) != TSP_OK ||
+      (s = check_ptr(lse)) != TSP_OK)
+    return s;
+  if (attn_out == q || attn_lo == q || attn_lo == attn_out) return TSP_ERR_INVALID_ARG;
+  if (!workspace) return TSP_ERR_WORKSPACE;
+  if (!aligned16(workspace)) return TSP_ERR_ALIGNMENT;
+  if (ws_bytes < ws_core(plan->n_local, dims, plan->D)) return TSP_ERR_WORKSPACE;
+  return run_core(plan, dims, q, k_full, v_full, attn_out, attn_lo, workspace, stream, lse);
+}
+
+tsp_status tsp_attn_core_backward(const tsp_plan* plan, const tsp_dims* dims, const uint16_t* q,
+                                  const uint16_t* k_full, const uint16_t* v_full, const uint16_t* attn_out,
+                                  const uint16_t* attn_lo, const float* lse, const uint16_t* d_attn, float* dq,
+                                  float* dk_full, float* dv_full, void* workspace, size_t ws_bytes,
+                                  hipStream_t stream) {
+  tsp_status s;
+  if ((s = check_plan(plan)) != TSP_OK) return s;
+  if ((s = check_dims(dims, plan->D, true, false, 0)) != TSP_OK) return s;
+  if ((s = check_ptr(q)) != TSP_OK || (s = check_ptr(k_full)) != TSP_OK || (s = check_ptr(v_full)) != TSP_OK ||
+      (s = check_ptr(attn_out)) != TSP_OK || (s = check_ptr_nullable(attn_lo)) != TSP_OK ||
+      (s = check_ptr(lse)) != TSP_OK || (s = check_ptr(d_attn)) != TSP_OK || (s = check_ptr(dq)) != TSP_OK ||
+      (s = check_ptr(dk_full)) != TSP_OK || (s = check_ptr(dv_full)) != TSP_OK)
+    return s;
+  if (dk_full == dv_full || (void*)dq == (void*)dk_full || (void*)dq == (void*)dv_full) return TSP_ERR_INVALID_ARG;
+  const size_t need = attn_bwd_ws_bytes(plan->seq_len, plan->chunk_len, dims->n_heads, dims->head_dim);
+  if (!workspace) return TSP_ERR_WORKSPACE;
+  if (!aligned16(workspace)) return TSP_ERR_ALIGNMENT;
+  if (ws_bytes < need) return TSP_ERR_WORKSPACE;
+  AttnBwdArgs a{};
+  a.q = q;
+  a.k = k_full;
+  a.v = v_full;
+  a.o = attn_out;
+  a.o_lo = attn_lo;
+  a.dout = d_attn;
+  a.lse = lse;
+  a.dq = dq;
+  a.dk = dk_full;
+  a.dv = dv_full;
+  a.seq_len = plan->seq_len;
+  a.chunk_len = plan->chunk_len;
+  a.chunk_start0 = plan->chunk_start[0];
+  a.chunk_start1 = plan->chunk_start[1];
+  a.hidden = dims->hidden;
+  a.n_heads = dims->n_heads;
+  a.head_dim = dims->head_dim;
+  a.n_kv_tiles = (plan->seq_len + 63) / 64;
+  a.tpc = (plan->chunk_len + 63) / 64;
+  // workspace: K^T tiles, Q^T tiles, dO^T tiles, stats (each size a multiple of 1 KB)
+  uint8_t* w = static_cast<uint8_t*>(workspace);
+  a.kt = reinterpret_cast<uint16_t*>(w);
+  w += (size_t)dims->n_heads * a.n_kv_tiles * dims->head_dim * 64 * 2;
+  a.qt = reinterpret_cast<uint16_t*>(w);
+  w += (size_t)2 * dims->n_heads * a.tpc * dims->head_dim * 64 * 2;
+  a.dot = reinterpret_cast<uint16_t*>(w);
+  w += (size_t)2 * dims->n_heads * a.tpc * dims->head_dim * 64 * 2;
+  a.stats = reinterpret_cast<float*>(w);
+  return from_hip(launch_attention_backward(a, stream));
 }
 
 tsp_status tsp_attn_out(int64_t n_tokens, const tsp_dims* dims, int32_t D, int32_t start_shard,

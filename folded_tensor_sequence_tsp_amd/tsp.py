@@ -18,13 +18,14 @@ import torch
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libtsp.so")
 
 TSP_OK, TSP_ERR_INVALID_ARG, TSP_ERR_SHAPE, TSP_ERR_ALIGNMENT, TSP_ERR_WORKSPACE, TSP_ERR_UNSUPPORTED, TSP_ERR_HIP = range(7)
-WS_ATTN, WS_MLP, WS_LAYER, WS_POST, WS_CORE, WS_OUT_SHARD, WS_MLP_SHARD, WS_MLP_BWD = 0, 1, 2, 3, 4, 5, 6, 7
+WS_ATTN, WS_MLP, WS_LAYER, WS_POST, WS_CORE, WS_OUT_SHARD, WS_MLP_SHARD, WS_MLP_BWD, WS_ATTN_BWD = range(9)
 MAX_D = 16
 
 EXPORTS = ["tsp_zigzag_plan", "tsp_workspace_size", "tsp_attn_project", "tsp_attn_core", "tsp_attn_out",
            "tsp_attn_forward", "tsp_mlp_forward", "tsp_layer_post", "tsp_layer_forward", "tsp_attn_project_shard",
            "tsp_attn_out_shard", "tsp_mlp_shard", "tsp_rms_norm", "tsp_rope", "tsp_attn_project_gqa",
-           "tsp_attn_core_gqa", "tsp_mlp_backward", "tsp_status_string"]
+           "tsp_attn_core_gqa", "tsp_mlp_backward", "tsp_attn_core_lse", "tsp_attn_core_backward",
+           "tsp_status_string"]
 
 
 class TSPError(RuntimeError):
@@ -72,6 +73,8 @@ def lib() -> ctypes.CDLL:
             "tsp_attn_core_gqa": [POINTER(Plan), POINTER(Dims), c_int32, P, P, P, P, P, P, c_size_t, P],
             "tsp_mlp_backward": [c_int64, POINTER(Dims), c_int32, c_int32, c_int32, P, PP, PP, P, P, PP, PP, P,
                                  c_size_t, P],
+            "tsp_attn_core_lse": [POINTER(Plan), POINTER(Dims), P, P, P, P, P, P, P, c_size_t, P],
+            "tsp_attn_core_backward": [POINTER(Plan), POINTER(Dims), P, P, P, P, P, P, P, P, P, P, P, c_size_t, P],
             "tsp_status_string": [c_int32],
         }
         for name, args in sig.items():
@@ -179,6 +182,48 @@ def attn_core(plan: Plan, dims: Dims, q, k_full, v_full, attn_out, attn_lo=None,
             _dev_tensor(attn_out, (n, h), "attn_out"), _opt_tensor(attn_lo, (n, h), "attn_lo"))
     _check(lib().tsp_attn_core(ctypes.byref(plan), ctypes.byref(dims), *args, ws, nbytes, _stream(stream)),
            "tsp_attn_core")
+
+
+def _f32_tensor(t, shape, name: str) -> c_void_p:
+    if not isinstance(t, torch.Tensor) or t.dtype != torch.float32 or t.device.type != "cuda" \
+            or t.device.index != torch.cuda.current_device() or not t.is_contiguous() \
+            or tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name}: expected a contiguous float32 tensor of shape {tuple(shape)} on the HIP device")
+    return c_void_p(t.data_ptr())
+
+
+def attn_core_lse(plan: Plan, dims: Dims, q, k_full, v_full, attn_out, lse, attn_lo=None, workspace=None,
+                  stream=None):
+    """attn_core that also writes lse [n_heads, n_local] (fp32): the natural log
+    of each query row's softmax normaliser."""
+    n, h, S = plan.n_local, dims.hidden, plan.seq_len
+    need = workspace_size(n, dims, plan.D, WS_CORE)
+    if workspace is None:
+        workspace = torch.empty(max(need, 256), dtype=torch.uint8, device=q.device)
+    ws, nbytes = _workspace(workspace, need)
+    args = (_dev_tensor(q, (n, h), "q"), _dev_tensor(k_full, (S, h), "k_full"), _dev_tensor(v_full, (S, h), "v_full"),
+            _dev_tensor(attn_out, (n, h), "attn_out"), _opt_tensor(attn_lo, (n, h), "attn_lo"),
+            _f32_tensor(lse, (dims.n_heads, n), "lse"))
+    _check(lib().tsp_attn_core_lse(ctypes.byref(plan), ctypes.byref(dims), *args, ws, nbytes, _stream(stream)),
+           "tsp_attn_core_lse")
+
+
+def attn_core_backward(plan: Plan, dims: Dims, q, k_full, v_full, attn_out, lse, d_attn, dq, dk_full, dv_full,
+                       attn_lo=None, workspace=None, stream=None):
+    """Gradients of attn_core: dq [n_local, hidden], and this rank's
+    contributions dk_full, dv_full [seq_len, hidden] (all fp32)."""
+    n, h, S = plan.n_local, dims.hidden, plan.seq_len
+    need = workspace_size(n, dims, plan.D, WS_ATTN_BWD)
+    if workspace is None:
+        workspace = torch.empty(max(need, 256), dtype=torch.uint8, device=q.device)
+    ws, nbytes = _workspace(workspace, need)
+    args = (_dev_tensor(q, (n, h), "q"), _dev_tensor(k_full, (S, h), "k_full"), _dev_tensor(v_full, (S, h), "v_full"),
+            _dev_tensor(attn_out, (n, h), "attn_out"), _opt_tensor(attn_lo, (n, h), "attn_lo"),
+            _f32_tensor(lse, (dims.n_heads, n), "lse"), _dev_tensor(d_attn, (n, h), "d_attn"),
+            _f32_tensor(dq, (n, h), "dq"), _f32_tensor(dk_full, (S, h), "dk_full"),
+            _f32_tensor(dv_full, (S, h), "dv_full"))
+    _check(lib().tsp_attn_core_backward(ctypes.byref(plan), ctypes.byref(dims), *args, ws, nbytes, _stream(stream)),
+           "tsp_attn_core_backward")
 
 
 def attn_out(dims: Dims, D: int, start_shard: int, attn, wo, residual, out, attn_lo=None, stream=None):

@@ -86,7 +86,8 @@ typedef enum {
   TSP_WS_CORE = 4,
   TSP_WS_OUT_SHARD = 5,
   TSP_WS_MLP_SHARD = 6,
-  TSP_WS_MLP_BWD = 7
+  TSP_WS_MLP_BWD = 7,
+  TSP_WS_ATTN_BWD = 8
 } tsp_ws_kind;
 
 /*
@@ -160,6 +161,46 @@ tsp_status tsp_attn_project(const tsp_plan* plan, const tsp_dims* dims, const ui
 tsp_status tsp_attn_core(const tsp_plan* plan, const tsp_dims* dims, const uint16_t* q,
                          const uint16_t* k_full, const uint16_t* v_full, uint16_t* attn_out,
                          uint16_t* attn_lo, void* workspace, size_t ws_bytes, hipStream_t stream);
+
+/*
+ * tsp_attn_core that also keeps, for the backward, the natural log of each
+ * query row's softmax normaliser:
+ *   lse[a * n_local + t] = ln sum_{j <= p} exp(q[t, a] . k_full[j, a] / sqrt(head_dim))
+ *   lse : device, fp32 [n_heads x n_local], out.
+ * Everything else (arguments, workspace TSP_WS_CORE, errors) as tsp_attn_core.
+ */
+tsp_status tsp_attn_core_lse(const tsp_plan* plan, const tsp_dims* dims, const uint16_t* q,
+                             const uint16_t* k_full, const uint16_t* v_full, uint16_t* attn_out,
+                             uint16_t* attn_lo, float* lse, void* workspace, size_t ws_bytes,
+                             hipStream_t stream);
+
+/*
+ * Backward of tsp_attn_core (the TSP page names long-context training as a use
+ * of the method, zubnet.ai TSP page, paras. 2 and 4; the gradients are the
+ * chain rule of the forward above).  Per head, with P the causal softmax rows, o = P v_full and dO the
+ * gradient of o:
+ *   dv_full = P^T dO,  dS = P * (dO v_full^T - rowsum(dO * o)),
+ *   dq = dS k_full / sqrt(head_dim),  dk_full = dS^T q / sqrt(head_dim).
+ * dk_full / dv_full are this rank's contributions for every key row (zero for
+ * keys no local query sees); in TSP each key row's owner would sum them over
+ * the ranks, the reverse of the K/V all-gather (para. 2).  MHA only.
+ *   q, k_full, v_full : as tsp_attn_core (bf16).
+ *   attn_out, attn_lo : the forward's output (bf16; attn_lo nullable), read.
+ *   lse      : device, fp32 [n_heads x n_local], from tsp_attn_core_lse.
+ *   d_attn   : device, bf16 [n_local x hidden], the gradient of attn_out.
+ *   dq       : device, fp32 [n_local x hidden], out.
+ *   dk_full, dv_full : device, fp32 [seq_len x hidden], out (every row written).
+ *   workspace: device, >= tsp_workspace_size(n_local, dims, D, TSP_WS_ATTN_BWD)
+ *              bytes (transposed tiles of k_full, q and d_attn; per-row stats).
+ * P is rebuilt from the scores and lse; P and dS enter the products as bf16,
+ * accumulation is fp32.  Errors: as tsp_attn_core, plus TSP_ERR_INVALID_ARG
+ * when two of dq, dk_full, dv_full are the same buffer.
+ */
+tsp_status tsp_attn_core_backward(const tsp_plan* plan, const tsp_dims* dims, const uint16_t* q,
+                                  const uint16_t* k_full, const uint16_t* v_full, const uint16_t* attn_out,
+                                  const uint16_t* attn_lo, const float* lse, const uint16_t* d_attn, float* dq,
+                                  float* dk_full, float* dv_full, void* workspace, size_t ws_bytes,
+                                  hipStream_t stream);
 
 /*
  * O projection as a split-K over the D head shards (the attention projections

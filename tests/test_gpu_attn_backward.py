@@ -1,0 +1,122 @@
+"""GPU parity of the attention backward (tsp_attn_core_lse, tsp_attn_core_backward)
+against the fp64 oracle.
+
+  * the softmax normaliser from tsp_attn_core_lse against oracle.attention_lse,
+    and its output bit-identical to tsp_attn_core's;
+  * dq, and this rank's dk/dv contributions for every key row, against
+    oracle.causal_attention_backward: head_dim 64 and 128, both zigzag
+    chunks, ragged chunks (not a multiple of 64 queries), D = 1, with and
+    without the forward's low output part;
+  * keys past every local query get exact zeros.
+
+Tolerances.  The kernels feed P and dS to the MFMAs as bf16: one rounding of
+one operand of a dot product bounds its error by 2^-9 sum |a||b|, with the
+fp64 factors (P and |dS| <= P (|dP| + |delta|)).  delta = rowsum(dO * o) is
+taken from the forward's output, which carries the forward's rounding of P
+(2^-9 P|v| per element) and, without its low part, the bf16 rounding of o
+(at most as much again): e_t = 2^-9 (1 or 2) sum_d |dO| (P|v|), which reaches
+dq through P|k| e and dk through P^T (e |q|).  Each element is checked against
+twice the sum of these (margin 2), plus 1e-5 of the output's largest magnitude
+for the fp32 accumulation; and the whole against relative RMS <= 5e-3.
+"""
+import math
+
+import pytest
+import torch
+
+from folded_tensor_sequence_tsp_amd import synth, tsp
+from oracle import tsp_oracle as O
+from parity import REL_RMS, bf16_nan, gpu, require_gpu, say
+
+pytestmark = gpu
+DEV = "cuda"
+F64 = torch.float64
+
+
+def _rnd(shape, seed, std=1.0):
+    return synth.randn_bf16(shape, 9_800_000 + seed, std, "cpu")
+
+
+def _bounds(q, k, v, do, pos, H, hd, with_lo):
+    """Per-element rounding bounds of dq, dk, dv (fp64, [rows, H*hd]), in units
+    of 2^-9 (one bf16 rounding)."""
+    S, m = k.shape[0], q.shape[0]
+    bq, bk, bv = (torch.zeros(m, H * hd, dtype=F64), torch.zeros(S, H * hd, dtype=F64),
+                  torch.zeros(S, H * hd, dtype=F64))
+    for a in range(H):
+        cols = slice(a * hd, (a + 1) * hd)
+        p = O.softmax_rows(q, pos, k, a, hd)
+        dp = do[:, cols] @ v[:, cols].t()
+        delta = (p * dp).sum(1, keepdim=True)
+        ds_abs = p * (dp.abs() + delta.abs())
+        e = (1.0 if with_lo else 2.0) * (do[:, cols].abs() * (p @ v[:, cols].abs())).sum(1, keepdim=True)
+        bv[:, cols] = p.t() @ do[:, cols].abs()
+        bk[:, cols] = (ds_abs.t() @ q[:, cols].abs() + p.t() @ (e * q[:, cols].abs())) / math.sqrt(hd)
+        bq[:, cols] = (ds_abs @ k[:, cols].abs() + (p @ k[:, cols].abs()) * e) / math.sqrt(hd)
+    return bq, bk, bv
+
+
+def _check(got, ref, bound, name):
+    g = got.detach().cpu().to(F64)
+    assert torch.isfinite(g).all(), f"{name}: non-finite values"
+    err = (g - ref).abs()
+    lim = 2.0 ** -8 * bound + 1e-5 * ref.abs().max().item() + 1e-12
+    bad = err > lim
+    assert not bool(bad.any()), (f"{name}: {int(bad.sum())}/{g.numel()} elements beyond the bound; "
+                                 f"worst excess {float((err - lim).max()):.3e}")
+    rr = ((g - ref).norm() / ref.norm().clamp_min(1e-300)).item()
+    assert rr <= REL_RMS, f"{name}: relative RMS {rr:.3e}"
+    say(f"{name}: max err {float(err.max()):.3e}, rel rms {rr:.2e}")
+
+
+def _run(S, D, r, H, hd, with_lo, seed):
+    plan, l2g, _ = tsp.zigzag_plan(S, D, r)
+    n, h = plan.n_local, H * hd
+    dims = tsp.make_dims(h, H, hd, 4 * h)
+    q, k, v = _rnd((n, h), seed), _rnd((S, h), seed + 1), _rnd((S, h), seed + 2)
+    do = _rnd((n, h), seed + 3)
+    qd, kd, vd, dod = (t.to(DEV) for t in (q, k, v, do))
+    out = bf16_nan((n, h), DEV)
+    lo = bf16_nan((n, h), DEV) if with_lo else None
+    lse = torch.full((H, n), float("nan"), dtype=torch.float32, device=DEV)
+    say(f"attn backward S={S} D={D} r={r} H={H} hd={hd} lo={with_lo}: forward with lse")
+    tsp.attn_core_lse(plan, dims, qd, kd, vd, out, lse, attn_lo=lo)
+    dq = torch.full((n, h), float("nan"), dtype=torch.float32, device=DEV)
+    dk = torch.full((S, h), float("nan"), dtype=torch.float32, device=DEV)
+    dv = torch.full((S, h), float("nan"), dtype=torch.float32, device=DEV)
+    say("backward")
+    tsp.attn_core_backward(plan, dims, qd, kd, vd, out, lse, dod, dq, dk, dv, attn_lo=lo)
+    torch.cuda.synchronize()
+    return plan, l2g, (q, k, v, do), (out, lse, dq, dk, dv)
+
+
+@pytest.mark.parametrize("S,D,r,H,hd", [(2048, 4, 1, 4, 64), (1288, 2, 1, 2, 128), (640, 1, 0, 2, 64)])
+def test_lse_and_same_output(S, D, r, H, hd):
+    require_gpu()
+    plan, l2g, (q, k, v, _), (out, lse, _, _, _) = _run(S, D, r, H, hd, False, 10)
+    ref = O.attention_lse(O.f64(q), l2g, O.f64(k), H, hd)
+    err = (lse.cpu().to(F64) - ref).abs()
+    assert float(err.max()) <= 1e-4 + 1e-5 * float(ref.abs().max()), f"lse max err {float(err.max()):.3e}"
+    h = H * hd
+    dims = tsp.make_dims(h, H, hd, 4 * h)
+    out2 = bf16_nan((plan.n_local, h), DEV)
+    tsp.attn_core(plan, dims, q.to(DEV), k.to(DEV), v.to(DEV), out2)
+    torch.cuda.synchronize()
+    assert torch.equal(out, out2)
+
+
+@pytest.mark.parametrize("S,D,r,H,hd", [(2048, 4, 1, 4, 64), (2048, 2, 0, 2, 128), (1288, 2, 1, 2, 128),
+                                         (640, 1, 0, 2, 64), (4096, 4, 3, 2, 128)])
+@pytest.mark.parametrize("with_lo", [False, True])
+def test_attn_backward(S, D, r, H, hd, with_lo):
+    require_gpu()
+    plan, l2g, (q, k, v, do), (_, _, dq, dk, dv) = _run(S, D, r, H, hd, with_lo, 20)
+    qf, kf, vf, dof = (O.f64(t) for t in (q, k, v, do))
+    rq, rk, rv = O.causal_attention_backward(qf, l2g, kf, vf, dof, H, hd)
+    bq, bk, bv = _bounds(qf, kf, vf, dof, l2g, H, hd, with_lo)
+    _check(dq, rq, bq, "dq")
+    _check(dk, rk, bk, "dk")
+    _check(dv, rv, bv, "dv")
+    last = int(l2g.max()) + 1
+    if last < S:
+        assert torch.count_nonzero(dk[last:]).item() == 0 and torch.count_nonzero(dv[last:]).item() == 0
