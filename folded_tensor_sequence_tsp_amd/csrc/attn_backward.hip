@@ -22,7 +22,7 @@
 //     dP = dO V^T, Q^T and dO^T transposed for dV^T += dO^T P and
 //     dK^T += Q^T dS) through a two-stage LDS ring with direct global->LDS
 //     loads.  Lane = key, so P and dS leave the score registers as B operands;
-//   * dQ: a workgroup owns 128 queries of one chunk (32 per wave, Q and dO
+//   * dQ: a workgroup owns 256 queries of one chunk (32 per wave, Q and dO
 //     fragments in registers); it streams the 64-key tiles (K and V row-major
 //     for S^T = K Q^T and dP^T = V dO^T, K^T for dQ^T += K^T dS^T).
 //     Lane = query, so the normaliser and delta are per-lane scalars.
@@ -32,15 +32,15 @@
 namespace tsp {
 namespace {
 
-constexpr int BW = 4;  // waves per workgroup
-constexpr int BTHREADS = 64 * BW;
+constexpr int BW = 4;   // waves per workgroup of the dK/dV kernel
+constexpr int QW = 8;   // waves per workgroup of the dQ kernel
 constexpr float LOG2E = 1.44269504088896340736f;
 
-template <int HD>
+template <int HD, int NWAVES>
 struct BCfg {
   static constexpr int NCH = HD / 8;                    // 16-byte chunks per row-major row
   static constexpr int TILE_BYTES = 64 * HD * 2;        // a 64-row tile, row-major or transposed
-  static constexpr int TLOADS = TILE_BYTES / (BTHREADS * 16);  // DMA instructions per thread per tile
+  static constexpr int TLOADS = TILE_BYTES / (NWAVES * 64 * 16);  // DMA instructions per thread per tile
   static constexpr int RPL = 64 / NCH;                  // row-major rows per 1 KB block
   static constexpr int KK = HD / 16;                    // MFMA k-steps over head_dim
   static constexpr int DT = HD / 32;                    // 32-wide d tiles
@@ -81,11 +81,10 @@ __global__ __launch_bounds__(64) void bwd_stats_kernel(const AttnBwdArgs a) {
 
 // ---- dK, dV.
 template <int HD>
-__global__ __launch_bounds__(BTHREADS) void dkv_kernel(const AttnBwdArgs a) {
-  using C = BCfg<HD>;
+__global__ __launch_bounds__(64 * BW) void dkv_kernel(const AttnBwdArgs a) {
+  using C = BCfg<HD, BW>;
   constexpr int STATS = 1024;                       // per wave: its own copy of the tile's stats
   constexpr int STAGE = 4 * C::TILE_BYTES + BW * STATS;
-  constexpr int LOADS = 4 * C::TLOADS + 1;          // DMA instructions per wave per tile
   __shared__ __attribute__((aligned(1024))) uint8_t smem[2 * STAGE];
 
   const int tid = threadIdx.x;
@@ -190,76 +189,112 @@ __global__ __launch_bounds__(BTHREADS) void dkv_kernel(const AttnBwdArgs a) {
     dvT[dt] = f32x16{};
   }
 
+  // One tile as a software pipeline (one wave per SIMD: the wave itself has to
+  // hide its LDS latency and its vector work): A fragments are read one MFMA
+  // step ahead; the exponentials and dS of queries 0..31 run under the S/dP
+  // MFMAs of queries 32..63, those of queries 32..63 under the first half of
+  // the dV/dK MFMAs (which need only queries 0..31).
   auto compute = [&](int i) __attribute__((always_inline)) {
     int c, t;
     tile_of(i, c, t);
     const int64_t qp0 = (c ? a.chunk_start1 : a.chunk_start0) + (int64_t)t * 64;  // position of query 0
     if (kw0 > qp0 + 63) return;  // every key of the wave is past every query of the tile (wave-uniform)
-    const bool need_mask = kw0 + 31 > qp0;
+    // queries of the tile before this lane's key are masked: offsets below qmin
+    const int qmin = kw0 + 31 > qp0 ? (int)min(max(key - qp0, (int64_t)0), (int64_t)64) : 0;
     const uint8_t* stage = smem + (i & 1) * STAGE;
     const uint8_t* q_st = stage;
     const uint8_t* do_st = stage + C::TILE_BYTES;
     const uint8_t* qt_st = stage + 2 * C::TILE_BYTES;
     const uint8_t* dot_st = stage + 3 * C::TILE_BYTES;
     const float* st = reinterpret_cast<const float*>(stage + 4 * C::TILE_BYTES + wave * STATS);
+    auto rm = [&](const uint8_t* base, int mb, int kk) __attribute__((always_inline)) {
+      return *reinterpret_cast<const u32x4*>(base + mb * 32 * (HD * 2) + (rm_a0 ^ (uint32_t)(kk << 5)));
+    };
+    auto tr = [&](const uint8_t* base, int dt, int ks) __attribute__((always_inline)) {
+      return *reinterpret_cast<const u32x4*>(base + dt * 32 * 128 + (tr_a0 ^ (uint32_t)(ks << 5)));
+    };
     uint32_t pp[16], ps[16];  // bf16 pairs of P and dS: [4*ks + j], 16-query step ks
+    // P and dS of entries 4g..4g+3 of half mb: queries 32*mb + 8*g + 4*half + j
+    auto group = [&](const f32x16& sv, const f32x16& dpv, int mb, int g) __attribute__((always_inline)) {
+      const int q0 = 32 * mb + 8 * g + 4 * half;
+      const f32x4 l2 = *reinterpret_cast<const f32x4*>(st + q0);
+      const f32x4 dl = *reinterpret_cast<const f32x4*>(st + 64 + q0);
+      float p[4], ds[4];
 #pragma unroll
-    for (int mb = 0; mb < 2; ++mb) {
-      f32x16 s = f32x16{}, dp = f32x16{};
-#pragma unroll
-      for (int kk = 0; kk < C::KK; ++kk) {
-        const uint32_t ad = mb * 32 * (HD * 2) + (rm_a0 ^ (uint32_t)(kk << 5));
-        const u32x4 qa = *reinterpret_cast<const u32x4*>(q_st + ad);
-        const u32x4 da = *reinterpret_cast<const u32x4*>(do_st + ad);
-        s = mfma32(as_bf16x8(qa), as_bf16x8(kf[kk]), s);
-        dp = mfma32(as_bf16x8(da), as_bf16x8(vf[kk]), dp);
+      for (int j = 0; j < 4; ++j) {
+        p[j] = __builtin_amdgcn_exp2f(fmaf(sv[4 * g + j], scale_log2, -l2[j]));
+        p[j] = q0 + j < qmin ? 0.0f : p[j];
+        ds[j] = p[j] * (dpv[4 * g + j] - dl[j]);
       }
-      // entry e: query 32*mb + 8*(e/4) + 4*half + e%4 of the tile, key = this lane's
+      const int idx = 8 * mb + 2 * g;  // ks = 2*mb + g/2, pair 2*(g%2) + 0/1
+      pp[idx] = pack_bf16x2(p[0], p[1]);
+      pp[idx + 1] = pack_bf16x2(p[2], p[3]);
+      ps[idx] = pack_bf16x2(ds[0], ds[1]);
+      ps[idx + 1] = pack_bf16x2(ds[2], ds[3]);
+    };
+    constexpr int G2 = C::KK / 4;  // S/dP steps per group of vector work
+    constexpr int G3 = C::DT / 2;  // dV/dK steps per group
+    f32x16 s0 = f32x16{}, d0 = f32x16{}, s1 = f32x16{}, d1 = f32x16{};
+    u32x4 qa = rm(q_st, 0, 0), da = rm(do_st, 0, 0);
 #pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        const int q0 = 32 * mb + 8 * g + 4 * half;
-        const f32x4 l2 = *reinterpret_cast<const f32x4*>(st + q0);
-        const f32x4 dl = *reinterpret_cast<const f32x4*>(st + 64 + q0);
-        float p[4], ds[4];
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          p[j] = __builtin_amdgcn_exp2f(fmaf(s[4 * g + j], scale_log2, -l2[j]));
-          if (need_mask && key > qp0 + q0 + j) p[j] = 0.0f;
-          ds[j] = p[j] * (dp[4 * g + j] - dl[j]);
-        }
-        const int idx = 8 * mb + 2 * g;  // pairs (4*ks + j): ks = 2*mb + g/2, j = 2*(g%2) + 0/1
-        pp[idx] = pack_bf16x2(p[0], p[1]);
-        pp[idx + 1] = pack_bf16x2(p[2], p[3]);
-        ps[idx] = pack_bf16x2(ds[0], ds[1]);
-        ps[idx + 1] = pack_bf16x2(ds[2], ds[3]);
-      }
+    for (int kk = 0; kk < C::KK; ++kk) {  // S, dP of queries 0..31
+      const int nm = kk + 1 < C::KK ? 0 : 1, nk = (kk + 1) % C::KK;
+      const u32x4 qn = rm(q_st, nm, nk), dn = rm(do_st, nm, nk);
+      s0 = mfma32(as_bf16x8(qa), as_bf16x8(kf[kk]), s0);
+      d0 = mfma32(as_bf16x8(da), as_bf16x8(vf[kk]), d0);
+      __builtin_amdgcn_sched_barrier(0);  // keep each step's reads ahead of its MFMAs
+      qa = qn;
+      da = dn;
     }
 #pragma unroll
-    for (int ks = 0; ks < 4; ++ks) {
+    for (int kk = 0; kk < C::KK; ++kk) {  // S, dP of queries 32..63; P, dS of queries 0..31
+      u32x4 qn = qa, dn = da;
+      if (kk + 1 < C::KK) {
+        qn = rm(q_st, 1, kk + 1);
+        dn = rm(do_st, 1, kk + 1);
+      }
+      s1 = mfma32(as_bf16x8(qa), as_bf16x8(kf[kk]), s1);
+      d1 = mfma32(as_bf16x8(da), as_bf16x8(vf[kk]), d1);
+      if ((kk + 1) % G2 == 0) group(s0, d0, 0, (kk + 1) / G2 - 1);
+      __builtin_amdgcn_sched_barrier(0);
+      qa = qn;
+      da = dn;
+    }
+    u32x4 oa = tr(dot_st, 0, 0), ta = tr(qt_st, 0, 0);
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) {  // dV^T += dO^T P, dK^T += Q^T dS; P, dS of queries 32..63 under ks 0, 1
       const u32x4 bp = u32x4{pp[4 * ks], pp[4 * ks + 1], pp[4 * ks + 2], pp[4 * ks + 3]};
       const u32x4 bs = u32x4{ps[4 * ks], ps[4 * ks + 1], ps[4 * ks + 2], ps[4 * ks + 3]};
 #pragma unroll
       for (int dt = 0; dt < C::DT; ++dt) {
-        const uint32_t ad = dt * 32 * 128 + (tr_a0 ^ (uint32_t)(ks << 5));
-        const u32x4 oa = *reinterpret_cast<const u32x4*>(dot_st + ad);
-        const u32x4 qa = *reinterpret_cast<const u32x4*>(qt_st + ad);
+        u32x4 on = oa, tn = ta;
+        if (dt + 1 < C::DT) {
+          on = tr(dot_st, dt + 1, ks);
+          tn = tr(qt_st, dt + 1, ks);
+        } else if (ks + 1 < 4) {
+          on = tr(dot_st, 0, ks + 1);
+          tn = tr(qt_st, 0, ks + 1);
+        }
         dvT[dt] = mfma32(as_bf16x8(oa), as_bf16x8(bp), dvT[dt]);
-        dkT[dt] = mfma32(as_bf16x8(qa), as_bf16x8(bs), dkT[dt]);
+        dkT[dt] = mfma32(as_bf16x8(ta), as_bf16x8(bs), dkT[dt]);
+        const int step = ks * C::DT + dt;
+        if (ks < 2 && (step + 1) % G3 == 0) group(s1, d1, 1, (step + 1) / G3 - 1);
+        __builtin_amdgcn_sched_barrier(0);
+        oa = on;
+        ta = tn;
       }
     }
   };
 
+  // Two-stage ring, one barrier per tile: the barrier after tile i's wait also
+  // frees the stage that tile i-1 was computed from, so tile i+1's loads go
+  // there right after it, and land during tile i's compute.
   if (n_all > 0) issue(0);
   for (int i = 0; i < n_all; ++i) {
-    if (i + 1 < n_all) {
-      issue(i + 1);
-      wait_vmcnt<LOADS>();
-    } else {
-      wait_vmcnt<0>();
-    }
+    wait_vmcnt<0>();
     lds_barrier();
+    if (i + 1 < n_all) issue(i + 1);
     compute(i);
-    lds_barrier();
   }
 
   // store this lane's key row of dK (scaled) and dV; zeros where no query sees the key
@@ -281,11 +316,10 @@ __global__ __launch_bounds__(BTHREADS) void dkv_kernel(const AttnBwdArgs a) {
 
 // ---- dQ.
 template <int HD>
-__global__ __launch_bounds__(BTHREADS) void dq_kernel(const AttnBwdArgs a) {
-  using C = BCfg<HD>;
-  constexpr int QTB = 32 * BW;  // queries per workgroup
+__global__ __launch_bounds__(64 * QW) void dq_kernel(const AttnBwdArgs a) {
+  using C = BCfg<HD, QW>;
+  constexpr int QTB = 32 * QW;  // queries per workgroup
   constexpr int STAGE = 3 * C::TILE_BYTES;
-  constexpr int LOADS = 3 * C::TLOADS;
   __shared__ __attribute__((aligned(1024))) uint8_t smem[2 * STAGE];
 
   const int tid = threadIdx.x;
@@ -345,7 +379,7 @@ __global__ __launch_bounds__(BTHREADS) void dq_kernel(const AttnBwdArgs a) {
   int rm_row[C::TLOADS], rm_col[C::TLOADS], tr_off[C::TLOADS];
 #pragma unroll
   for (int j = 0; j < C::TLOADS; ++j) {
-    const int b = j * BW + wave;
+    const int b = j * QW + wave;
     const int r = b * C::RPL + lane / C::NCH;
     rm_row[j] = r;
     rm_col[j] = ((lane % C::NCH) ^ (r & (C::NCH - 1))) * 8;
@@ -361,9 +395,9 @@ __global__ __launch_bounds__(BTHREADS) void dq_kernel(const AttnBwdArgs a) {
     for (int j = 0; j < C::TLOADS; ++j) {
       const int64_t kr = min(k0 + rm_row[j], key_end - 1);  // rows past the range: masked anyway
       const int64_t off = kr * ld + hcol + rm_col[j];
-      dma16(a.k + off, stage + (j * BW + wave) * 1024);
-      dma16(a.v + off, stage + C::TILE_BYTES + (j * BW + wave) * 1024);
-      dma16(kt_head + (int64_t)t * HD * 64 + tr_off[j], stage + 2 * C::TILE_BYTES + (j * BW + wave) * 1024);
+      dma16(a.k + off, stage + (j * QW + wave) * 1024);
+      dma16(a.v + off, stage + C::TILE_BYTES + (j * QW + wave) * 1024);
+      dma16(kt_head + (int64_t)t * HD * 64 + tr_off[j], stage + 2 * C::TILE_BYTES + (j * QW + wave) * 1024);
     }
   };
 
@@ -418,16 +452,11 @@ __global__ __launch_bounds__(BTHREADS) void dq_kernel(const AttnBwdArgs a) {
   };
 
   issue(0);
-  for (int t = 0; t < n_tiles; ++t) {
-    if (t + 1 < n_tiles) {
-      issue(t + 1);
-      wait_vmcnt<LOADS>();
-    } else {
-      wait_vmcnt<0>();
-    }
+  for (int t = 0; t < n_tiles; ++t) {  // two-stage ring, one barrier per tile (as in dkv_kernel)
+    wait_vmcnt<0>();
     lds_barrier();
+    if (t + 1 < n_tiles) issue(t + 1);
     compute(t);
-    lds_barrier();
   }
 
   if (wave_active && wave_first + ql < valid) {
@@ -477,17 +506,17 @@ hipError_t launch_attention_backward(const AttnBwdArgs& a, hipStream_t stream) {
   {
     const dim3 grid((unsigned)(H * ((a.seq_len + 127) / 128)));
     if (HD == 128)
-      hipLaunchKernelGGL(dkv_kernel<128>, grid, dim3(BTHREADS), 0, stream, a);
+      hipLaunchKernelGGL(dkv_kernel<128>, grid, dim3(64 * BW), 0, stream, a);
     else
-      hipLaunchKernelGGL(dkv_kernel<64>, grid, dim3(BTHREADS), 0, stream, a);
+      hipLaunchKernelGGL(dkv_kernel<64>, grid, dim3(64 * BW), 0, stream, a);
     if ((e = hipGetLastError()) != hipSuccess) return e;
   }
   {
-    const dim3 grid((unsigned)(H * 2 * ((a.chunk_len + 127) / 128)));
+    const dim3 grid((unsigned)(H * 2 * ((a.chunk_len + 32 * QW - 1) / (32 * QW))));
     if (HD == 128)
-      hipLaunchKernelGGL(dq_kernel<128>, grid, dim3(BTHREADS), 0, stream, a);
+      hipLaunchKernelGGL(dq_kernel<128>, grid, dim3(64 * QW), 0, stream, a);
     else
-      hipLaunchKernelGGL(dq_kernel<64>, grid, dim3(BTHREADS), 0, stream, a);
+      hipLaunchKernelGGL(dq_kernel<64>, grid, dim3(64 * QW), 0, stream, a);
     if ((e = hipGetLastError()) != hipSuccess) return e;
   }
   return hipSuccess;
