@@ -120,3 +120,68 @@ def test_attn_backward(S, D, r, H, hd, with_lo):
     last = int(l2g.max()) + 1
     if last < S:
         assert torch.count_nonzero(dk[last:]).item() == 0 and torch.count_nonzero(dv[last:]).item() == 0
+
+
+def test_attn_backward_7b_sampled():
+    """The 7B shape the benchmark times (S = 131072, D = 8, 32 heads x 128, rank 3),
+    generated q, K/V and dO: dq on sampled rows (each row depends only on its
+    own query); dk/dv of the rank's last 8 keys, which only its last 8 queries
+    see (so the oracle on those rows gives them whole); and at every key, the
+    column sums fixed by the softmax: sum_j dv[j] = sum_t dO[t] within the bf16
+    rounding of P (each probability row then sums to 1 within 2^-9), and
+    sum_j dk[j] = 0 within the rounding of dS (sum_j |dS_tj| <= 2 |dO_t| max_j |v_j|
+    by Cauchy-Schwarz) and of delta."""
+    require_gpu()
+    W = synth.WORKLOADS["attn_7b"]
+    d, D, S = W.dims, W.D, W.seq_len
+    plan, l2g, _ = tsp.zigzag_plan(S, D, W.rank)
+    n, h, H, hd = plan.n_local, d.hidden, d.n_heads, d.head_dim
+    dims = tsp.make_dims(h, H, hd, d.ffn)
+    say(f"{W.name}: inputs")
+    q = synth.activations(W.wid, n, h, device=DEV)
+    kd, vd = synth.gathered_kv(W.wid, S, h, device=DEV)
+    do = synth.randn_bf16((n, h), 9_800_777, 1.0, DEV)
+    out, lo = bf16_nan((n, h), DEV), bf16_nan((n, h), DEV)
+    lse = torch.full((H, n), float("nan"), dtype=torch.float32, device=DEV)
+    say(f"{W.name}: forward with lse")
+    tsp.attn_core_lse(plan, dims, q, kd, vd, out, lse, attn_lo=lo)
+    dq = torch.full((n, h), float("nan"), dtype=torch.float32, device=DEV)
+    dk = torch.full((S, h), float("nan"), dtype=torch.float32, device=DEV)
+    dv = torch.full((S, h), float("nan"), dtype=torch.float32, device=DEV)
+    say(f"{W.name}: backward")
+    tsp.attn_core_backward(plan, dims, q, kd, vd, out, lse, do, dq, dk, dv, attn_lo=lo)
+    torch.cuda.synchronize()
+
+    say(f"{W.name}: column sums")
+    last = int(l2g.max()) + 1
+    assert torch.count_nonzero(dk[last:]).item() == 0 and torch.count_nonzero(dv[last:]).item() == 0
+    dk64, dv64 = dk[:last].to(F64), dv[:last].to(F64)
+    do64, q64 = do.to(F64), q.to(F64)
+    sum_dv, sum_do = dv64.sum(0), do64.sum(0)
+    lim_v = 2 * (2.0 ** -9 * do64.abs().sum(0)) + 1e-6 * dv64.abs().sum(0)
+    assert bool(((sum_dv - sum_do).abs() <= lim_v).all()), "sum_j dv[j] != sum_t dO[t]"
+    vmax = vd.to(F64).reshape(S, H, hd)
+    vnorm_max = vmax.norm(dim=2).max(dim=0).values           # [H]: max_j |v_j| per head
+    vabs_max = vmax.abs().max(dim=0).values                   # [H, hd]: max_j |v_jd|
+    do_h = do64.reshape(n, H, hd)
+    per_t = 2.0 ** -9 * 2 * do_h.norm(dim=2) * vnorm_max + 2.0 ** -8 * (do_h.abs() * vabs_max).sum(2)  # [n, H]
+    lim_k = 2 * (q64.reshape(n, H, hd).abs() * per_t[:, :, None]).sum(0).reshape(h) / math.sqrt(hd)
+    lim_k += 1e-6 * dk64.abs().sum(0)
+    assert bool((dk64.sum(0).abs() <= lim_k).all()), "sum_j dk[j] != 0"
+    del dk64, dv64
+
+    say(f"{W.name}: oracle on sampled rows")
+    g = torch.Generator().manual_seed(5)
+    C = plan.chunk_len
+    rows = torch.unique(torch.cat([torch.tensor([0, 1, C - 1, C, C + 1, n - 1]), torch.randint(0, n, (14,), generator=g)]))
+    kc, vc = O.f64(kd), O.f64(vd)
+    qc, dc = O.f64(q), O.f64(do)
+    rq, _, _ = O.causal_attention_backward(qc[rows], l2g[rows], kc, vc, dc[rows], H, hd)
+    bq, _, _ = _bounds(qc[rows], kc, vc, dc[rows], l2g[rows], H, hd, True)
+    _check(dq[rows.to(DEV)], rq, bq, "7B dq sampled rows")
+    tail = torch.arange(n - 8, n)
+    _, rk, rv = O.causal_attention_backward(qc[tail], l2g[tail], kc, vc, dc[tail], H, hd)
+    _, bk, bv = _bounds(qc[tail], kc, vc, dc[tail], l2g[tail], H, hd, True)
+    keys = torch.arange(last - 8, last)
+    _check(dk[keys.to(DEV)], rk[keys], bk[keys], "7B dk of the last 8 keys")
+    _check(dv[keys.to(DEV)], rv[keys], bv[keys], "7B dv of the last 8 keys")
