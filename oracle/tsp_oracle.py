@@ -448,3 +448,49 @@ def causal_attention_backward(q: torch.Tensor, positions: torch.Tensor, k: torch
         dq[:, cols] = torch.matmul(ds, ka) * scale
         dk[:, cols] = torch.matmul(ds.t(), qa) * scale
     return dq, dk, dv
+
+
+def attn_out_backward(attn, wo, d_out):
+    """Gradients of the O projection out = [residual +] sum_d attn[:, cols_d] W_o_d^T
+    (W_o taken in row blocks by head shard: ``wo[d]`` is [h, H_s*hd], the input
+    columns of shard d's heads), given d_out = dL/dout:
+        d_attn[:, cols_d] = d_out W_o_d,    dW_o_d = d_out^T attn[:, cols_d].
+    Returns (d_attn [n, h], [dW_o_d])."""
+    a, g = f64(attn), f64(d_out)
+    d_attn = torch.empty_like(a)
+    dwo = []
+    c0 = 0
+    for w in wo:
+        W = f64(w)
+        cols = slice(c0, c0 + W.shape[1])
+        d_attn[:, cols] = torch.matmul(g, W)
+        dwo.append(torch.matmul(g.t(), a[:, cols]))
+        c0 += W.shape[1]
+    return d_attn, dwo
+
+
+def qkv_projection_backward(x, wqkv, dq, dk, dv, head_dim, dy=None):
+    """Gradients of the shard-iterated projections [q_d | k_d | v_d] = x W_qkv_d^T
+    (``wqkv[d]`` rows: shard d's Q heads, then its K heads, then its V heads;
+    its heads are the columns c_d of q, k, v), given dq, dk, dv for the same
+    rows (dk and dv: the rows' own K and V gradients, i.e. after every rank's
+    contribution to them has been summed):
+        dx = [dy +] sum_d (dq[:, c_d] Wq_d + dk[:, c_d] Wk_d + dv[:, c_d] Wv_d)
+        dW_qkv_d = [dq[:, c_d]^T x ; dk[:, c_d]^T x ; dv[:, c_d]^T x].
+    ``dy`` is the gradient arriving through the layer's residual.  Returns
+    (dx [n, h], [dW_qkv_d])."""
+    xx = f64(x)
+    gq, gk, gv = f64(dq), f64(dk), f64(dv)
+    dx = f64(dy).clone() if dy is not None else torch.zeros_like(xx)
+    dw = []
+    c0 = 0
+    for w in wqkv:
+        W = f64(w)
+        hs = W.shape[0] // 3
+        cols = slice(c0, c0 + hs)
+        parts = (gq[:, cols], gk[:, cols], gv[:, cols])
+        for i, gp in enumerate(parts):
+            dx = dx + torch.matmul(gp, W[i * hs:(i + 1) * hs])
+        dw.append(torch.cat([torch.matmul(gp.t(), xx) for gp in parts], dim=0))
+        c0 += hs
+    return dx, dw
