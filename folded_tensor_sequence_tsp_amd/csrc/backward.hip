@@ -67,7 +67,30 @@ __global__ __launch_bounds__(256) void transpose_kernel(const void* __restrict__
   }
 }
 
+// 8 consecutive elements of one row per thread: two 16-byte loads, one 16-byte store.
+__global__ __launch_bounds__(256) void f32_to_bf16_kernel(const float* __restrict__ src, int64_t R, int64_t C,
+                                                          int64_t ld_in, uint16_t* __restrict__ dst, int64_t ld_out) {
+  const int64_t per_row = C / 8;
+  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (i >= R * per_row) return;
+  const int64_t r = i / per_row, c = (i - r * per_row) * 8;
+  const float* p = src + r * ld_in + c;
+  const f32x4 a = *reinterpret_cast<const f32x4*>(p);
+  const f32x4 b = *reinterpret_cast<const f32x4*>(p + 4);
+  *reinterpret_cast<u32x4*>(dst + r * ld_out + c) =
+      u32x4{pack_bf16x2(a[0], a[1]), pack_bf16x2(a[2], a[3]), pack_bf16x2(b[0], b[1]), pack_bf16x2(b[2], b[3])};
+}
+
 }  // namespace
+
+hipError_t launch_f32_to_bf16(const float* src, int64_t R, int64_t C, int64_t ld_in, uint16_t* dst, int64_t ld_out,
+                              hipStream_t stream) {
+  const int64_t items = R * (C / 8);
+  if (items <= 0) return hipSuccess;
+  hipLaunchKernelGGL(f32_to_bf16_kernel, dim3((unsigned)((items + 255) / 256)), dim3(256), 0, stream, src, R, C,
+                     ld_in, dst, ld_out);
+  return hipGetLastError();
+}
 
 hipError_t launch_transpose(const void* src, int32_t src_f32, int32_t gelu, int64_t R, int64_t C, int64_t ld_in,
                             uint16_t* dst, int64_t ld_out, hipStream_t stream) {

@@ -54,8 +54,8 @@ struct Cfg {
 template <int EPI>
 __device__ __forceinline__ void store_row8(const GemmArgs& g, int nshard, int row, int col, float* v) {
   u32x4 packed;
-  if constexpr (EPI == EPI_RESID) {
-    const int64_t idx = (int64_t)row * g.ldo + col;
+  if constexpr (EPI == EPI_RESID) {  // N-sharded: shard nshard writes column block nshard of the output
+    const int64_t idx = (int64_t)row * g.ldo + (int64_t)nshard * g.N_s + col;
     if (g.row_exp) {
       const int e = g.row_exp[row];
 #pragma unroll

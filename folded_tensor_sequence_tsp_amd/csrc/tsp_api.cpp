@@ -329,6 +329,59 @@ MlpBwdWs mlp_bwd_ws(int64_t n, const tsp_dims* d, int32_t D) {
   return w;
 }
 
+// Workspace of tsp_attn_out_backward: W_o_d^T of all shards [D][H_s*hd x h],
+// d_out^T [h x n_pad], one shard's attn^T [H_s*hd x n_pad].
+struct OutBwdWs {
+  size_t wot_off, dot_off, at_off, total;
+};
+OutBwdWs out_bwd_ws(int64_t n, const tsp_dims* d, int32_t D) {
+  const int64_t np = pad64(n), h = d->hidden, hs = (int64_t)(d->n_heads / D) * d->head_dim;
+  OutBwdWs w;
+  w.wot_off = 0;
+  w.dot_off = w.wot_off + round_up((size_t)h * h * 2);
+  w.at_off = w.dot_off + round_up((size_t)h * np * 2);
+  w.total = w.at_off + round_up((size_t)hs * np * 2);
+  return w;
+}
+
+// Workspace of tsp_attn_project_backward: G = bf16[dq | dk | dv] [n x 3h], x^T
+// [h x n_pad], one shard's [dq_d | dk_d | dv_d]^T [3 H_s*hd x n_pad], the
+// transposed Q, K and V weight blocks of all shards [3][D][h x H_s*hd], and the
+// fp32 accumulator of dx [n x h].
+struct ProjBwdWs {
+  size_t g_off, xt_off, gt_off, wt_off, acc_off, total;
+};
+ProjBwdWs proj_bwd_ws(int64_t n, const tsp_dims* d, int32_t D) {
+  const int64_t np = pad64(n), h = d->hidden, hs = (int64_t)(d->n_heads / D) * d->head_dim;
+  ProjBwdWs w;
+  w.g_off = 0;
+  w.xt_off = w.g_off + round_up((size_t)n * 3 * h * 2);
+  w.gt_off = w.xt_off + round_up((size_t)h * np * 2);
+  w.wt_off = w.gt_off + round_up((size_t)3 * hs * np * 2);
+  w.acc_off = w.wt_off + round_up((size_t)3 * h * h * 2);
+  w.total = w.acc_off + round_up((size_t)n * h * 4);
+  return w;
+}
+
+// One-shard GEMM C = A B^T (B [N x K], K-contiguous) with the plain epilogue.
+hipError_t plain_gemm(const uint16_t* A, int64_t lda, const uint16_t* B, int32_t M, int32_t N, int32_t K, void* out,
+                      int64_t ldo, int32_t out_f32, hipStream_t stream) {
+  GemmArgs g{};
+  g.A = A;
+  g.lda = lda;
+  g.B[0] = B;
+  g.M = M;
+  g.N_s = N;
+  g.K_s = K;
+  g.n_shards = 1;
+  g.k_shards = 1;
+  g.epilogue = EPI_RESID;
+  g.out = out;
+  g.ldo = ldo;
+  g.out_f32 = out_f32;
+  return launch_gemm(g, stream);
+}
+
 // ---- shard streaming ---------------------------------------------------------
 
 // O projection ring step: the fp32 accumulator [n x h].
@@ -433,6 +486,12 @@ size_t tsp_workspace_size(int64_t n_tokens, const tsp_dims* dims, int32_t D, int
     case TSP_WS_MLP_BWD:
       if (check_dims(dims, D, false, true) != TSP_OK) return 0;
       return mlp_bwd_ws(n_tokens, dims, D).total;
+    case TSP_WS_OUT_BWD:
+      if (check_dims(dims, D, true, false) != TSP_OK) return 0;
+      return out_bwd_ws(n_tokens, dims, D).total;
+    case TSP_WS_PROJ_BWD:
+      if (check_dims(dims, D, true, false) != TSP_OK) return 0;
+      return proj_bwd_ws(n_tokens, dims, D).total;
     case TSP_WS_ATTN_BWD:
       if (check_dims(dims, D, true, false, 0) != TSP_OK || n_tokens % 2 != 0) return 0;
       return attn_bwd_ws_bytes(n_tokens * D, n_tokens / 2, dims->n_heads, dims->head_dim);
@@ -957,6 +1016,140 @@ tsp_status tsp_mlp_backward(int64_t n_tokens, const tsp_dims* dims, int32_t D, i
   g.ldo = h;
   g.residual = residual ? dy : nullptr;
   return from_hip(launch_gemm(g, stream));
+}
+
+tsp_status tsp_attn_out_backward(int64_t n_tokens, const tsp_dims* dims, int32_t D, int32_t start_shard,
+                                 const uint16_t* attn, const uint16_t* const* wo, const uint16_t* d_out,
+                                 uint16_t* d_attn, float* const* dwo, void* workspace, size_t ws_bytes,
+                                 hipStream_t stream) {
+  tsp_status s;
+  if ((s = check_dims(dims, D, true, false)) != TSP_OK) return s;
+  if (n_tokens < 0) return TSP_ERR_SHAPE;
+  if (n_tokens > INT32_MAX - 64) return TSP_ERR_UNSUPPORTED;
+  if (start_shard < 0 || start_shard >= D) return TSP_ERR_INVALID_ARG;
+  if ((s = check_ptr(attn)) != TSP_OK || (s = check_shards(wo, D)) != TSP_OK || (s = check_ptr(d_out)) != TSP_OK ||
+      (s = check_ptr(d_attn)) != TSP_OK)
+    return s;
+  if (!dwo) return TSP_ERR_INVALID_ARG;
+  for (int d = 0; d < D; ++d)
+    if ((s = check_ptr(dwo[d])) != TSP_OK) return s;
+  if (d_attn == attn || d_attn == d_out) return TSP_ERR_INVALID_ARG;
+  if (!workspace) return TSP_ERR_WORKSPACE;
+  if (!aligned16(workspace)) return TSP_ERR_ALIGNMENT;
+  const OutBwdWs lay = out_bwd_ws(n_tokens, dims, D);
+  if (ws_bytes < lay.total) return TSP_ERR_WORKSPACE;
+  if (n_tokens == 0) return TSP_OK;
+  char* base = static_cast<char*>(workspace);
+  uint16_t* wot = reinterpret_cast<uint16_t*>(base + lay.wot_off);
+  uint16_t* dot = reinterpret_cast<uint16_t*>(base + lay.dot_off);
+  uint16_t* at = reinterpret_cast<uint16_t*>(base + lay.at_off);
+  const int64_t n = n_tokens, np = pad64(n), h = dims->hidden;
+  const int32_t hs = (dims->n_heads / D) * dims->head_dim;
+  if ((s = from_hip(launch_transpose(d_out, 0, 0, n, h, h, dot, np, stream))) != TSP_OK) return s;
+  for (int k = 0; k < D; ++k) {
+    const int d = (start_shard + k) % D;
+    // W_o_d^T, then dW_o_d = d_out^T attn[:, block d] (contraction over the tokens)
+    if ((s = from_hip(launch_transpose(wo[d], 0, 0, h, hs, hs, wot + (int64_t)d * hs * h, h, stream))) != TSP_OK)
+      return s;
+    if ((s = from_hip(launch_transpose(attn + (int64_t)d * hs, 0, 0, n, hs, h, at, np, stream))) != TSP_OK) return s;
+    if ((s = from_hip(plain_gemm(dot, np, at, (int32_t)h, hs, (int32_t)np, dwo[d], hs, 1, stream))) != TSP_OK)
+      return s;
+  }
+  // d_attn[:, block d] = d_out W_o_d: one N-sharded launch over the transposed shards
+  GemmArgs g{};
+  g.A = d_out;
+  g.lda = h;
+  for (int d = 0; d < D; ++d) g.B[d] = wot + (int64_t)d * hs * h;
+  g.M = (int32_t)n;
+  g.N_s = hs;
+  g.K_s = (int32_t)h;
+  g.n_shards = D;
+  g.k_shards = 1;
+  g.epilogue = EPI_RESID;
+  g.out = d_attn;
+  g.ldo = h;
+  return from_hip(launch_gemm(g, stream));
+}
+
+tsp_status tsp_attn_project_backward(int64_t n_tokens, const tsp_dims* dims, int32_t D, int32_t start_shard,
+                                     const uint16_t* x, const uint16_t* const* wqkv, const float* dq, const float* dk,
+                                     const float* dv, const uint16_t* dy, uint16_t* dx, float* const* dwqkv,
+                                     void* workspace, size_t ws_bytes, hipStream_t stream) {
+  tsp_status s;
+  if ((s = check_dims(dims, D, true, false)) != TSP_OK) return s;
+  if (n_tokens < 0) return TSP_ERR_SHAPE;
+  if (n_tokens > INT32_MAX - 64) return TSP_ERR_UNSUPPORTED;
+  if (start_shard < 0 || start_shard >= D) return TSP_ERR_INVALID_ARG;
+  if ((s = check_ptr(x)) != TSP_OK || (s = check_shards(wqkv, D)) != TSP_OK || (s = check_ptr(dq)) != TSP_OK ||
+      (s = check_ptr(dk)) != TSP_OK || (s = check_ptr(dv)) != TSP_OK || (s = check_ptr_nullable(dy)) != TSP_OK ||
+      (s = check_ptr(dx)) != TSP_OK)
+    return s;
+  if (!dwqkv) return TSP_ERR_INVALID_ARG;
+  for (int d = 0; d < D; ++d)
+    if ((s = check_ptr(dwqkv[d])) != TSP_OK) return s;
+  if (dx == x) return TSP_ERR_INVALID_ARG;
+  if (!workspace) return TSP_ERR_WORKSPACE;
+  if (!aligned16(workspace)) return TSP_ERR_ALIGNMENT;
+  const ProjBwdWs lay = proj_bwd_ws(n_tokens, dims, D);
+  if (ws_bytes < lay.total) return TSP_ERR_WORKSPACE;
+  if (n_tokens == 0) return TSP_OK;
+  char* base = static_cast<char*>(workspace);
+  uint16_t* G = reinterpret_cast<uint16_t*>(base + lay.g_off);
+  uint16_t* xt = reinterpret_cast<uint16_t*>(base + lay.xt_off);
+  uint16_t* gt = reinterpret_cast<uint16_t*>(base + lay.gt_off);
+  uint16_t* wt = reinterpret_cast<uint16_t*>(base + lay.wt_off);
+  float* acc = reinterpret_cast<float*>(base + lay.acc_off);
+  const int64_t n = n_tokens, np = pad64(n), h = dims->hidden;
+  const int32_t hs = (dims->n_heads / D) * dims->head_dim;
+  const float* parts[3] = {dq, dk, dv};
+  for (int p = 0; p < 3; ++p)
+    if ((s = from_hip(launch_f32_to_bf16(parts[p], n, h, h, G + p * h, 3 * h, stream))) != TSP_OK) return s;
+  if ((s = from_hip(launch_transpose(x, 0, 0, n, h, h, xt, np, stream))) != TSP_OK) return s;
+  for (int k = 0; k < D; ++k) {
+    const int d = (start_shard + k) % D;
+    // [dq_d | dk_d | dv_d]^T, then dW_qkv_d = that . x (contraction over the tokens)
+    for (int p = 0; p < 3; ++p)
+      if ((s = from_hip(launch_transpose(parts[p] + (int64_t)d * hs, 1, 0, n, hs, h, gt + (int64_t)p * hs * np, np,
+                                         stream))) != TSP_OK)
+        return s;
+    if ((s = from_hip(plain_gemm(gt, np, xt, 3 * hs, (int32_t)h, (int32_t)np, dwqkv[d], h, 1, stream))) != TSP_OK)
+      return s;
+    // the shard's Q, K and V weight blocks transposed, [h x H_s*hd] each
+    for (int p = 0; p < 3; ++p)
+      if ((s = from_hip(launch_transpose(wqkv[d] + (int64_t)p * hs * h, 0, 0, hs, h, h,
+                                         wt + ((int64_t)p * D + d) * h * hs, hs, stream))) != TSP_OK)
+        return s;
+  }
+  // dx = [dy +] sum_p sum_k G_p[:, block d_k] W_{p, d_k}: three ring split-Ks
+  // through one fp32 accumulator
+  for (int p = 0; p < 3; ++p) {
+    GemmArgs g{};
+    g.A = G + p * h;
+    g.lda = 3 * h;
+    for (int d = 0; d < D; ++d) g.B[d] = wt + ((int64_t)p * D + d) * h * hs;
+    g.M = (int32_t)n;
+    g.N_s = (int32_t)h;
+    g.K_s = hs;
+    g.n_shards = 1;
+    g.k_shards = D;
+    g.ring_start = start_shard;
+    g.epilogue = EPI_RESID;
+    g.ldo = h;
+    if (p == 0) {
+      g.residual = dy;
+    } else {
+      g.residual = acc;
+      g.res_f32 = 1;
+    }
+    if (p < 2) {
+      g.out = acc;
+      g.out_f32 = 1;
+    } else {
+      g.out = dx;
+    }
+    if ((s = from_hip(launch_gemm(g, stream))) != TSP_OK) return s;
+  }
+  return TSP_OK;
 }
 
 const char* tsp_status_string(tsp_status status) {

@@ -18,14 +18,15 @@ import torch
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libtsp.so")
 
 TSP_OK, TSP_ERR_INVALID_ARG, TSP_ERR_SHAPE, TSP_ERR_ALIGNMENT, TSP_ERR_WORKSPACE, TSP_ERR_UNSUPPORTED, TSP_ERR_HIP = range(7)
-WS_ATTN, WS_MLP, WS_LAYER, WS_POST, WS_CORE, WS_OUT_SHARD, WS_MLP_SHARD, WS_MLP_BWD, WS_ATTN_BWD = range(9)
+(WS_ATTN, WS_MLP, WS_LAYER, WS_POST, WS_CORE, WS_OUT_SHARD, WS_MLP_SHARD, WS_MLP_BWD, WS_ATTN_BWD, WS_OUT_BWD,
+ WS_PROJ_BWD) = range(11)
 MAX_D = 16
 
 EXPORTS = ["tsp_zigzag_plan", "tsp_workspace_size", "tsp_attn_project", "tsp_attn_core", "tsp_attn_out",
            "tsp_attn_forward", "tsp_mlp_forward", "tsp_layer_post", "tsp_layer_forward", "tsp_attn_project_shard",
            "tsp_attn_out_shard", "tsp_mlp_shard", "tsp_rms_norm", "tsp_rope", "tsp_attn_project_gqa",
            "tsp_attn_core_gqa", "tsp_mlp_backward", "tsp_attn_core_lse", "tsp_attn_core_backward",
-           "tsp_status_string"]
+           "tsp_attn_out_backward", "tsp_attn_project_backward", "tsp_status_string"]
 
 
 class TSPError(RuntimeError):
@@ -75,6 +76,9 @@ def lib() -> ctypes.CDLL:
                                  c_size_t, P],
             "tsp_attn_core_lse": [POINTER(Plan), POINTER(Dims), P, P, P, P, P, P, P, c_size_t, P],
             "tsp_attn_core_backward": [POINTER(Plan), POINTER(Dims), P, P, P, P, P, P, P, P, P, P, P, c_size_t, P],
+            "tsp_attn_out_backward": [c_int64, POINTER(Dims), c_int32, c_int32, P, PP, P, P, PP, P, c_size_t, P],
+            "tsp_attn_project_backward": [c_int64, POINTER(Dims), c_int32, c_int32, P, PP, P, P, P, P, P, PP, P,
+                                          c_size_t, P],
             "tsp_status_string": [c_int32],
         }
         for name, args in sig.items():
@@ -384,6 +388,31 @@ def mlp_backward(dims: Dims, D: int, start_shard: int, residual: bool, x, w1, w2
             _f32_shards(dw2, D, (h, Fs), "dw2"))
     _check(lib().tsp_mlp_backward(n, ctypes.byref(dims), D, start_shard, int(bool(residual)), *args, ws, nbytes,
                                   _stream(stream)), "tsp_mlp_backward")
+
+
+def attn_out_backward(dims: Dims, D: int, start_shard: int, attn, wo, d_out, d_attn, dwo, workspace, stream=None):
+    """Gradients of the O projection: d_attn (bf16) and this rank's dW_o_d (fp32)."""
+    n, h = attn.shape[0], dims.hidden
+    hs = (dims.n_heads // D) * dims.head_dim if D > 0 else 0
+    ws, nbytes = _workspace(workspace, workspace_size(n, dims, D, WS_OUT_BWD))
+    args = (_dev_tensor(attn, (n, h), "attn"), _shards(wo, D, (h, hs), "wo"), _dev_tensor(d_out, (n, h), "d_out"),
+            _dev_tensor(d_attn, (n, h), "d_attn"), _f32_shards(dwo, D, (h, hs), "dwo"))
+    _check(lib().tsp_attn_out_backward(n, ctypes.byref(dims), D, start_shard, *args, ws, nbytes, _stream(stream)),
+           "tsp_attn_out_backward")
+
+
+def attn_project_backward(dims: Dims, D: int, start_shard: int, x, wqkv, dq, dk, dv, dy, dx, dwqkv, workspace,
+                          stream=None):
+    """Gradients of the shard-iterated QKV projection: dx (bf16, plus dy when
+    given) and this rank's dW_qkv_d (fp32); dq, dk, dv are fp32."""
+    n, h = x.shape[0], dims.hidden
+    hs = (dims.n_heads // D) * dims.head_dim if D > 0 else 0
+    ws, nbytes = _workspace(workspace, workspace_size(n, dims, D, WS_PROJ_BWD))
+    args = (_dev_tensor(x, (n, h), "x"), _shards(wqkv, D, (3 * hs, h), "wqkv"), _f32_tensor(dq, (n, h), "dq"),
+            _f32_tensor(dk, (n, h), "dk"), _f32_tensor(dv, (n, h), "dv"), _opt_tensor(dy, (n, h), "dy"),
+            _dev_tensor(dx, (n, h), "dx"), _f32_shards(dwqkv, D, (3 * hs, h), "dwqkv"))
+    _check(lib().tsp_attn_project_backward(n, ctypes.byref(dims), D, start_shard, *args, ws, nbytes,
+                                           _stream(stream)), "tsp_attn_project_backward")
 
 
 def alloc_workspace(n_tokens: int, dims: Dims, D: int, kind: int, device=None) -> torch.Tensor:

@@ -87,7 +87,9 @@ typedef enum {
   TSP_WS_OUT_SHARD = 5,
   TSP_WS_MLP_SHARD = 6,
   TSP_WS_MLP_BWD = 7,
-  TSP_WS_ATTN_BWD = 8
+  TSP_WS_ATTN_BWD = 8,
+  TSP_WS_OUT_BWD = 9,
+  TSP_WS_PROJ_BWD = 10
 } tsp_ws_kind;
 
 /*
@@ -201,6 +203,54 @@ tsp_status tsp_attn_core_backward(const tsp_plan* plan, const tsp_dims* dims, co
                                   const uint16_t* attn_lo, const float* lse, const uint16_t* d_attn, float* dq,
                                   float* dk_full, float* dv_full, void* workspace, size_t ws_bytes,
                                   hipStream_t stream);
+
+/*
+ * Backward of the O projection (tsp_attn_out's product; the attention
+ * projections are iterated over the weight shards, zubnet.ai TSP page, para. 2):
+ * with out = [residual +] sum_d attn[:, block d] W_o_d^T and d_out its gradient,
+ *   d_attn[:, block d] = d_out W_o_d,    dwo[d] = d_out^T attn[:, block d]
+ * (block d: shard d's heads, columns d*H_s*hd ..).  dwo[d] is this rank's
+ * contribution to shard d's gradient (in TSP the shard's owner would sum the
+ * ranks' contributions); the residual's gradient is d_out itself.  Shards are
+ * visited in ring order from start_shard.
+ *   attn     : device, bf16 [n_tokens x hidden], the forward's attention output
+ *              (its high part: the low part's contribution is below bf16 rounding).
+ *   wo       : host array of D device pointers, bf16 [hidden x H_s*hd].
+ *   d_out    : device, bf16 [n_tokens x hidden].
+ *   d_attn   : device, bf16 [n_tokens x hidden], out; aliases neither attn nor d_out.
+ *   dwo      : host array of D device pointers, fp32 [hidden x H_s*hd], out.
+ *   workspace: >= tsp_workspace_size(n_tokens, dims, D, TSP_WS_OUT_BWD) bytes.
+ * Errors: as tsp_attn_out, plus TSP_ERR_WORKSPACE.
+ */
+tsp_status tsp_attn_out_backward(int64_t n_tokens, const tsp_dims* dims, int32_t D, int32_t start_shard,
+                                 const uint16_t* attn, const uint16_t* const* wo, const uint16_t* d_out,
+                                 uint16_t* d_attn, float* const* dwo, void* workspace, size_t ws_bytes,
+                                 hipStream_t stream);
+
+/*
+ * Backward of the shard-iterated QKV projection (para. 2): with
+ * [q_d | k_d | v_d] = x W_qkv_d^T for every shard d,
+ *   dx = [dy +] sum_d (dq[:, block d] Wq_d + dk[:, block d] Wk_d + dv[:, block d] Wv_d)
+ *   dwqkv[d] = [dq[:, block d]^T x ; dk[:, block d]^T x ; dv[:, block d]^T x]
+ * (Wq_d, Wk_d, Wv_d: the row blocks of wqkv[d]).  dk and dv are the rank's
+ * own K/V rows' gradients, i.e. its rows of every rank's dk_full / dv_full
+ * contributions summed (the reduce-scatter of tsp_attn_core_backward's output;
+ * on one rank, its own rows).  dy is the gradient that reaches x through the
+ * layer's residual (nullable).  dx is accumulated in fp32 over the shards in
+ * ring order from start_shard.
+ *   x        : device, bf16 [n_tokens x hidden], the forward's input.
+ *   wqkv     : as tsp_attn_project.
+ *   dq, dk, dv : device, fp32 [n_tokens x hidden] (rounded to bf16 for the products).
+ *   dy       : device, bf16 [n_tokens x hidden], nullable.
+ *   dx       : device, bf16 [n_tokens x hidden], out; must not alias x.
+ *   dwqkv    : host array of D device pointers, fp32 [3*H_s*hd x hidden], out.
+ *   workspace: >= tsp_workspace_size(n_tokens, dims, D, TSP_WS_PROJ_BWD) bytes.
+ * Errors: as tsp_attn_project, plus TSP_ERR_WORKSPACE.
+ */
+tsp_status tsp_attn_project_backward(int64_t n_tokens, const tsp_dims* dims, int32_t D, int32_t start_shard,
+                                     const uint16_t* x, const uint16_t* const* wqkv, const float* dq, const float* dk,
+                                     const float* dv, const uint16_t* dy, uint16_t* dx, float* const* dwqkv,
+                                     void* workspace, size_t ws_bytes, hipStream_t stream);
 
 /*
  * O projection as a split-K over the D head shards (the attention projections

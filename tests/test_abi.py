@@ -340,3 +340,60 @@ def test_mlp_backward_rejects(L):
     assert call(ws=None) == tsp.TSP_ERR_WORKSPACE
     assert call(dims=_dims(ffn=1002)) == tsp.TSP_ERR_SHAPE
     assert call(n=-1) == tsp.TSP_ERR_SHAPE
+
+
+def test_attn_backward_rejects(L):
+    d = _dims()
+    p, _, _ = tsp.zigzag_plan(2048, 4, 1)
+    n, S, C = p.n_local, 2048, p.chunk_len
+    need = tsp.workspace_size(n, d, 4, tsp.WS_ATTN_BWD)
+    # K^T tiles of the sequence, Q^T and dO^T tiles of both chunks, 1 KB of stats per 64-query tile
+    tiles_c = -(-C // 64)
+    assert need == 4 * (S // 64) * 64 * 64 * 2 + 2 * (2 * 4 * tiles_c * 64 * 64 * 2) + 2 * 4 * tiles_c * 1024
+    lse = lambda **k: L.tsp_attn_core_lse(ctypes.byref(p), ctypes.byref(d), A, A + 64, A + 128, k.get("out", A + 192),
+                                          None, k.get("lse", A + 512), A + 1024,
+                                          tsp.workspace_size(n, d, 4, tsp.WS_CORE), None)
+    assert lse(lse=None) == tsp.TSP_ERR_INVALID_ARG
+    assert lse(lse=MIS) == tsp.TSP_ERR_ALIGNMENT
+    assert lse(out=A) == tsp.TSP_ERR_INVALID_ARG                     # output aliases q
+    bwd = lambda **k: L.tsp_attn_core_backward(ctypes.byref(p), ctypes.byref(d), A, A + 64, A + 128, A + 192, None,
+                                               k.get("lse", A + 256), A + 320, k.get("dq", A + 384),
+                                               k.get("dk", A + 448), k.get("dv", A + 512), k.get("ws", A + 1024),
+                                               k.get("nb", need), None)
+    assert bwd(dk=A + 512) == tsp.TSP_ERR_INVALID_ARG                # dk = dv
+    assert bwd(dq=A + 448) == tsp.TSP_ERR_INVALID_ARG                # dq = dk
+    assert bwd(lse=None) == tsp.TSP_ERR_INVALID_ARG
+    assert bwd(nb=need - 1) == tsp.TSP_ERR_WORKSPACE
+    assert bwd(ws=None) == tsp.TSP_ERR_WORKSPACE
+    assert L.tsp_attn_core_backward(None, ctypes.byref(d), A, A, A, A, None, A, A, A + 64, A + 128, A + 192, A,
+                                    need, None) == tsp.TSP_ERR_INVALID_ARG
+
+
+def test_projection_backward_rejects(L):
+    d = _dims()
+    n, np_, h, hs = 300, 320, 256, 64
+    w = _arr([A] * 4)
+    g = _arr([A + 512] * 4)
+    need_o = tsp.workspace_size(n, d, 4, tsp.WS_OUT_BWD)
+    assert need_o == h * h * 2 + h * np_ * 2 + hs * np_ * 2       # W_o^T (all shards), d_out^T, one shard's attn^T
+    out = lambda **k: L.tsp_attn_out_backward(k.get("n", n), ctypes.byref(d), 4, k.get("start", 0), A, w,
+                                              A + 64, k.get("d_attn", A + 128), k.get("dwo", g),
+                                              k.get("ws", A + 256), k.get("nb", need_o), None)
+    assert out(start=4) == tsp.TSP_ERR_INVALID_ARG
+    assert out(d_attn=A) == tsp.TSP_ERR_INVALID_ARG                  # d_attn aliases attn
+    assert out(dwo=_arr([A, 0, A, A])) == tsp.TSP_ERR_INVALID_ARG
+    assert out(nb=need_o - 1) == tsp.TSP_ERR_WORKSPACE
+    assert out(n=-1) == tsp.TSP_ERR_SHAPE
+    need_p = tsp.workspace_size(n, d, 4, tsp.WS_PROJ_BWD)
+    # bf16 [dq | dk | dv], x^T, one shard's gradients transposed, W_qkv^T blocks, fp32 dx accumulator
+    assert need_p == n * 3 * h * 2 + h * np_ * 2 + 3 * hs * np_ * 2 + 3 * h * h * 2 + n * h * 4
+    prj = lambda **k: L.tsp_attn_project_backward(n, ctypes.byref(d), 4, k.get("start", 1), A, w, A + 64, A + 128,
+                                                  A + 192, k.get("dy", None), k.get("dx", A + 320),
+                                                  k.get("dw", g), k.get("ws", A + 1024), k.get("nb", need_p), None)
+    assert prj(dx=A) == tsp.TSP_ERR_INVALID_ARG                      # dx aliases x
+    assert prj(dy=MIS) == tsp.TSP_ERR_ALIGNMENT
+    assert prj(dw=None) == tsp.TSP_ERR_INVALID_ARG
+    assert prj(start=-1) == tsp.TSP_ERR_INVALID_ARG
+    assert prj(nb=need_p - 1) == tsp.TSP_ERR_WORKSPACE
+    assert L.tsp_attn_project_backward(n, ctypes.byref(_dims(n_heads=3, hidden=192)), 4, 0, A, w, A, A, A, None,
+                                       A + 64, g, A, need_p, None) == tsp.TSP_ERR_SHAPE
