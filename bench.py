@@ -19,7 +19,8 @@ After the timed steps, each step's entry point is also timed alone on layer
 0's inputs (``rows_layer0``: QKV projection, attention, O projection, MLP),
 each against the bf16 MFMA peak, and so are the shard-streaming forms of the
 projections and the MLP (the D ring steps called one by one, weights
-resident), the MLP ring's and the attention's backward, and the layer variants (RMSNorm and RoPE
+resident), the backward of every step (MLP ring, attention core, O and QKV
+projections), and the layer variants (RMSNorm and RoPE
 against the HBM peak, grouped-query attention with 8 K/V heads); ``--no-rows``
 skips them.
 
@@ -121,6 +122,24 @@ def row_timings(plan, dims, D, layer0, x0, q, a, a_lo, out, ws_core, fl, dev, re
     calls.append(("attention backward: dq, dk, dv contributions (tsp_attn_core_backward)", "attn_bwd",
                   lambda: tsp.attn_core_backward(plan, dims, q, kf, vf, a, lse, d_attn, dq_b, dk_b, dv_b,
                                                  attn_lo=a_lo, workspace=ws_abwd)))
+    # backward of the O and QKV projections on layer 0's shapes: twice the
+    # forward products' FLOPs each (the input and the weight gradients)
+    hs_ = (dims.n_heads // D) * dims.head_dim
+    dwo_b = [torch.empty(dims.hidden, hs_, dtype=torch.float32, device=dev) for _ in range(D)]
+    dwqkv_b = [torch.empty(3 * hs_, dims.hidden, dtype=torch.float32, device=dev) for _ in range(D)]
+    d_attn_b = torch.empty(n, dims.hidden, dtype=torch.bfloat16, device=dev)
+    dx_b = torch.empty(n, dims.hidden, dtype=torch.bfloat16, device=dev)
+    ws_obwd = tsp.alloc_workspace(n, dims, D, tsp.WS_OUT_BWD, device=dev)
+    ws_pbwd = tsp.alloc_workspace(n, dims, D, tsp.WS_PROJ_BWD, device=dev)
+    fl["oproj_bwd"] = 2.0 * fl["oproj"]
+    fl["qkv_bwd"] = 2.0 * fl["qkv"]
+    calls += [
+        ("O projection backward: d_attn, dW_o per shard (tsp_attn_out_backward)", "oproj_bwd",
+         lambda: tsp.attn_out_backward(dims, D, plan.rank, a, lw.wo, d_attn, d_attn_b, dwo_b, ws_obwd)),
+        ("QKV projection backward: dx, dW_qkv per shard (tsp_attn_project_backward)", "qkv_bwd",
+         lambda: tsp.attn_project_backward(dims, D, plan.rank, x0, lw.wqkv, dq_b, dq_b, dq_b,
+                                           d_attn, dx_b, dwqkv_b, ws_pbwd)),
+    ]
     # layer variants on the same shapes: RMSNorm and RoPE (HBM-bound passes),
     # attention with 8 K/V heads (grouped-query) on generated K/V of that width
     h, H, hd = dims.hidden, dims.n_heads, dims.head_dim
@@ -154,6 +173,7 @@ def row_timings(plan, dims, D, layer0, x0, q, a, a_lo, out, ws_core, fl, dev, re
             tf = fl[key] / (ms * 1e-3) / 1e12
             rows[name] = {"ms": round(ms, 4), "tflops": round(tf, 1), "frac": round(tf / PEAK_BF16_TFLOPS, 4)}
     del ws_mlp, ws_mlp_s, ws_out_s, k8, v8, ws_bwd, dw1, dw2, dy, dx, ws_abwd, dq_b, dk_b, dv_b, lse, d_attn
+    del dwo_b, dwqkv_b, d_attn_b, dx_b, ws_obwd, ws_pbwd
     return rows
 
 
