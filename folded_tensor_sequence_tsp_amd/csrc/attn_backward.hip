@@ -35,6 +35,17 @@ namespace {
 constexpr int BW = 4;   // waves per workgroup of the dK/dV kernel
 constexpr int QW = 8;   // waves per workgroup of the dQ kernel
 constexpr float LOG2E = 1.44269504088896340736f;
+constexpr float PAD_LSE2 = 65536.0f;
+
+// x as three bf16 parts (hi + mid + lo = x to about 2^-24 |x|), packed as the
+// first three k values of an MFMA fragment.
+__device__ __forceinline__ u32x4 bf16_split3(float x) {
+  const float hi = __uint_as_float((uint32_t)f32_to_bf16(x) << 16);
+  const float r1 = x - hi;
+  const float mid = __uint_as_float((uint32_t)f32_to_bf16(r1) << 16);
+  const float lo = r1 - mid;
+  return u32x4{pack_bf16x2(hi, mid), pack_bf16x2(lo, 0.0f), 0u, 0u};
+}
 
 template <int HD, int NWAVES>
 struct BCfg {
@@ -53,7 +64,9 @@ __global__ __launch_bounds__(64) void bwd_stats_kernel(const AttnBwdArgs a) {
   const int t = blockIdx.x, c = blockIdx.y, head = blockIdx.z;
   const int r = threadIdx.x;
   const int64_t row_in_chunk = (int64_t)t * 64 + r;
-  float l2 = INFINITY, dl = 0.0f;  // padding rows: probability exp2(s - inf) = 0
+  // padding rows: a normaliser so large that every probability is exp2(-2^16) = 0
+  // (finite, so that it can be split into bf16 parts)
+  float l2 = PAD_LSE2, dl = 0.0f;
   if (row_in_chunk < a.chunk_len) {
     const int64_t row = c * a.chunk_len + row_in_chunk;
     l2 = a.lse[(int64_t)head * 2 * a.chunk_len + row] * LOG2E;
@@ -181,6 +194,9 @@ __global__ __launch_bounds__(64 * BW) void dkv_kernel(const AttnBwdArgs a) {
   const uint32_t rm_a0 = (uint32_t)ql * (HD * 2) + ((uint32_t)(half ^ (ql & (C::NCH - 1))) << 4);
   const uint32_t tr_a0 = (uint32_t)ql * 128 + ((uint32_t)(half ^ ((ql >> 1) & 7)) << 4);
   const float scale_log2 = LOG2E * C::INV_SQRT_HD;
+  const float inv_scale_log2 = 1.0f / scale_log2;
+  // B fragment of the normaliser/delta k-step: ones at k = 0..2 (half 0)
+  const u32x4 ones = half ? u32x4{0u, 0u, 0u, 0u} : u32x4{0x3F803F80u, 0x00003F80u, 0u, 0u};
 
   f32x16 dkT[C::DT], dvT[C::DT];  // [d][key]: lane holds key ql, dims dt*32 + 8*(e/4) + 4*half + e%4
 #pragma unroll
@@ -214,17 +230,25 @@ __global__ __launch_bounds__(64 * BW) void dkv_kernel(const AttnBwdArgs a) {
       return *reinterpret_cast<const u32x4*>(base + dt * 32 * 128 + (tr_a0 ^ (uint32_t)(ks << 5)));
     };
     uint32_t pp[16], ps[16];  // bf16 pairs of P and dS: [4*ks + j], 16-query step ks
+    // The normaliser and delta enter the products as one extra k-step: A holds,
+    // for the lane's query row (32*mb + ql), -l2/scale and -delta as three bf16
+    // parts in k = 0..2 (lanes of half 0; half 1 and k >= 3 are zero), B holds
+    // ones there, so the MFMAs give s - l2/scale and dP - delta directly.
+    auto aug_s = [&](int mb) __attribute__((always_inline)) {
+      return half ? u32x4{0u, 0u, 0u, 0u} : bf16_split3(-st[32 * mb + ql] * inv_scale_log2);
+    };
+    auto aug_d = [&](int mb) __attribute__((always_inline)) {
+      return half ? u32x4{0u, 0u, 0u, 0u} : bf16_split3(-st[64 + 32 * mb + ql]);
+    };
     // P and dS of entries 4g..4g+3 of half mb: queries 32*mb + 8*g + 4*half + j
     auto group = [&](const f32x16& sv, const f32x16& dpv, int mb, int g) __attribute__((always_inline)) {
       const int q0 = 32 * mb + 8 * g + 4 * half;
-      const f32x4 l2 = *reinterpret_cast<const f32x4*>(st + q0);
-      const f32x4 dl = *reinterpret_cast<const f32x4*>(st + 64 + q0);
       float p[4], ds[4];
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
-        p[j] = __builtin_amdgcn_exp2f(fmaf(sv[4 * g + j], scale_log2, -l2[j]));
+        p[j] = __builtin_amdgcn_exp2f(sv[4 * g + j] * scale_log2);
         p[j] = q0 + j < qmin ? 0.0f : p[j];
-        ds[j] = p[j] * (dpv[4 * g + j] - dl[j]);
+        ds[j] = p[j] * dpv[4 * g + j];
       }
       const int idx = 8 * mb + 2 * g;  // ks = 2*mb + g/2, pair 2*(g%2) + 0/1
       pp[idx] = pack_bf16x2(p[0], p[1]);
@@ -234,8 +258,11 @@ __global__ __launch_bounds__(64 * BW) void dkv_kernel(const AttnBwdArgs a) {
     };
     constexpr int G2 = C::KK / 4;  // S/dP steps per group of vector work
     constexpr int G3 = C::DT / 2;  // dV/dK steps per group
-    f32x16 s0 = f32x16{}, d0 = f32x16{}, s1 = f32x16{}, d1 = f32x16{};
     u32x4 qa = rm(q_st, 0, 0), da = rm(do_st, 0, 0);
+    f32x16 s0 = mfma32(as_bf16x8(aug_s(0)), as_bf16x8(ones), f32x16{});
+    f32x16 d0 = mfma32(as_bf16x8(aug_d(0)), as_bf16x8(ones), f32x16{});
+    f32x16 s1 = mfma32(as_bf16x8(aug_s(1)), as_bf16x8(ones), f32x16{});
+    f32x16 d1 = mfma32(as_bf16x8(aug_d(1)), as_bf16x8(ones), f32x16{});
 #pragma unroll
     for (int kk = 0; kk < C::KK; ++kk) {  // S, dP of queries 0..31
       const int nm = kk + 1 < C::KK ? 0 : 1, nk = (kk + 1) % C::KK;
