@@ -41,6 +41,10 @@ UNITS = {
     "tsp_attn_core": (["vt_prep_kernel", "attn_kernel"], ["attention.hip", "device_common.h", "kernels.h"]),
     "attn_kernel": (["attn_kernel"], ["attention.hip", "device_common.h", "kernels.h"]),
     "gemm_kernel": (["gemm_kernel"], ["gemm.hip", "device_common.h", "kernels.h"]),
+    # backward of the attention core (its transposed-tile pre-passes share the
+    # forward's vt_prep_kernel and are listed in the table, not in the unit)
+    "tsp_attn_core_backward": (["bwd_stats_kernel", "dkv_kernel", "dq_kernel"],
+                               ["attn_backward.hip", "device_common.h", "kernels.h"]),
 }
 KERNEL_SOURCES = {k: v[1] for k, v in UNITS.items()}
 
@@ -84,25 +88,38 @@ def _copy_factor(cnt, copy_bytes: int) -> tuple:
 
 
 def summarise(trace, fetch, write, unit, copy_mib, command, workload):
+    """Markdown summary of a kernel-trace run and, when fetch and write are
+    given, of its two counter runs (traffic of the unit's kernels)."""
     stats = kernel_stats(trace)
-    f, w = counters(fetch), counters(write)
-    copy_bytes = copy_mib << 20
-    ff, f_copy = _copy_factor(f, copy_bytes)
-    wf, w_copy = _copy_factor(w, copy_bytes)
     kernels = UNITS[unit][0]
-    fetch_b = write_b = avg_ms = 0.0
+    avg_ms = 0.0
     for k in kernels:
-        fk = [v for n, v in f.values() if k in n]
-        wk = [v for n, v in w.values() if k in n]
-        fetch_b += sum(fk) / len(fk) * 1024.0 * ff
-        write_b += sum(wk) / len(wk) * 1024.0 * wf
         avg_ms += sum(ms for n, _, ms, _ in stats if n.startswith(k))
+    if fetch and write:
+        f, w = counters(fetch), counters(write)
+        copy_bytes = copy_mib << 20
+        ff, f_copy = _copy_factor(f, copy_bytes)
+        wf, w_copy = _copy_factor(w, copy_bytes)
+        fetch_b = write_b = 0.0
+        for k in kernels:
+            fk = [v for n, v in f.values() if k in n]
+            wk = [v for n, v in w.values() if k in n]
+            fetch_b += sum(fk) / len(fk) * 1024.0 * ff
+            write_b += sum(wk) / len(wk) * 1024.0 * wf
     lines = [f"# rocprofv3 summary: {unit} ({' + '.join(kernels)}), {workload}", "",
              "Commands (run from the repository root on the GPU; `-d`/`-o` name the output folders):", "",
              "```", *command.split(" ;; "), "```", "",
              "## Kernel time (--kernel-trace --stats)", "",
              "| kernel | calls | avg ms | % of GPU time |", "|---|---|---|---|"]
     lines += [f"| {n} | {c} | {ms:.4f} | {p:.2f} |" for n, c, ms, p in stats if "at::native" not in n]
+    if not (fetch and write):
+        lines += ["", "## Machine-readable", "",
+                  f"kernel: {unit}",
+                  f"kernels: {', '.join(kernels)}",
+                  f"avg_ms_per_launch: {avg_ms:.4f}",
+                  "traffic_bytes_per_launch: none (no counter runs)",
+                  f"source_sha256: {source_sha256(unit)}", ""]
+        return "\n".join(lines)
     lines += ["", "## HBM traffic (--pmc FETCH_SIZE, --pmc WRITE_SIZE; KiB per dispatch)", "",
               f"Calibration: a plain {copy_mib} MiB device copy reads FETCH_SIZE = {f_copy:.0f} KiB and "
               f"WRITE_SIZE = {w_copy:.0f} KiB, so fetch counts are scaled by {ff:.4f} and write counts by {wf:.4f}.",
@@ -168,8 +185,8 @@ def read_traffic(path: str, unit: str):
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--trace", required=True)
-    ap.add_argument("--fetch", required=True)
-    ap.add_argument("--write", required=True)
+    ap.add_argument("--fetch", default=None, help="FETCH_SIZE counter run (optional, with --write)")
+    ap.add_argument("--write", default=None, help="WRITE_SIZE counter run (optional, with --fetch)")
     ap.add_argument("--kernel", default="tsp_attn_core", choices=sorted(UNITS))
     ap.add_argument("--copy-mib", type=int, default=1024)
     ap.add_argument("--command", required=True, help="the profiling commands, separated by ' ;; '")
