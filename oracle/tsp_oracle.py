@@ -494,3 +494,50 @@ def qkv_projection_backward(x, wqkv, dq, dk, dv, head_dim, dy=None):
         dw.append(torch.cat([torch.matmul(gp.t(), xx) for gp in parts], dim=0))
         c0 += hs
     return dx, dw
+
+
+def rms_norm_backward(x, gain, eps: float, dy):
+    """Gradients of y = x / r * gain with r = sqrt(mean_j x_j^2 + eps), per row:
+        dx = (gain * dy) / r - x * sum_j(gain_j dy_j x_j) / (h r^3),
+        dgain = sum over rows of dy * x / r.
+    Returns (dx, dgain)."""
+    xx, g, w = f64(x), f64(dy), f64(gain)
+    h = xx.shape[1]
+    r = torch.sqrt((xx * xx).mean(dim=1, keepdim=True) + eps)
+    gw = g * w
+    dx = gw / r - xx * (gw * xx).sum(dim=1, keepdim=True) / (h * r ** 3)
+    dgain = (g * xx / r).sum(dim=0)
+    return dx, dgain
+
+
+def rope_backward(dy: torch.Tensor, positions: torch.Tensor, n_heads: int, head_dim: int, theta: float):
+    """Gradient of the rotary embedding: each pair was rotated by an orthogonal
+    2x2 matrix R(angle), so the gradient is R(angle)^T dy = R(-angle) dy."""
+    g = f64(dy)
+    m = g.shape[0]
+    ang = rope_angles(positions, head_dim, theta)          # [m, hd/2]
+    c, s = torch.cos(ang)[:, None, :], torch.sin(ang)[:, None, :]
+    pairs = g.reshape(m, n_heads, head_dim // 2, 2)
+    y0, y1 = pairs[..., 0], pairs[..., 1]
+    out = torch.stack([y0 * c + y1 * s, -y0 * s + y1 * c], dim=-1)
+    return out.reshape(m, n_heads * head_dim)
+
+
+def causal_attention_gqa_backward(q, positions, k, v, dout, n_heads: int, n_kv_heads: int, head_dim: int):
+    """Gradients of causal_attention_gqa: per query head a, the chain rule of
+    causal_attention_backward against K/V head a / (H / H_kv); the K/V
+    gradients of one K/V head sum over the query heads that read it.
+    Returns (dq [m, H*hd], dk [S, H_kv*hd], dv [S, H_kv*hd])."""
+    m, S = q.shape[0], k.shape[0]
+    group = n_heads // n_kv_heads
+    dq = torch.zeros((m, n_heads * head_dim), dtype=F64)
+    dk = torch.zeros((S, n_kv_heads * head_dim), dtype=F64)
+    dv = torch.zeros((S, n_kv_heads * head_dim), dtype=F64)
+    for a in range(n_heads):
+        qc = slice(a * head_dim, (a + 1) * head_dim)
+        kc = slice((a // group) * head_dim, (a // group + 1) * head_dim)
+        gq, gk, gv = causal_attention_backward(q[:, qc], positions, k[:, kc], v[:, kc], dout[:, qc], 1, head_dim)
+        dq[:, qc] = gq
+        dk[:, kc] += gk
+        dv[:, kc] += gv
+    return dq, dk, dv

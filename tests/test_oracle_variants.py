@@ -138,3 +138,56 @@ def test_gqa_projection_reduces_to_mha_projection():
     assert torch.allclose(k[:, hd:2 * hd], x @ w1[1][Hs * hd:(Hs + 1) * hd].t(), rtol=1e-13)
     assert torch.allclose(v[:, :hd], x @ w1[0][(Hs + 1) * hd:].t(), rtol=1e-13)
     assert torch.allclose(q[:, Hs * hd:], x @ w1[1][:Hs * hd].t(), rtol=1e-13)
+
+
+# ------------------------------------------------------------- backwards
+def test_rms_norm_backward_matches_autograd():
+    g = torch.Generator().manual_seed(41)
+    x = torch.randn(9, 48, generator=g, dtype=F64) * 2.0
+    w = torch.randn(48, generator=g, dtype=F64)
+    dy = torch.randn(9, 48, generator=g, dtype=F64)
+    for eps in (0.0, 1e-6, 1e-2):
+        xa, wa = x.clone().requires_grad_(True), w.clone().requires_grad_(True)
+        gx, gw = torch.autograd.grad(F.rms_norm(xa, (48,), weight=wa, eps=eps), (xa, wa), grad_outputs=dy)
+        dx, dgain = O.rms_norm_backward(x, w, eps, dy)
+        assert torch.allclose(dx, gx, rtol=1e-12, atol=1e-12)
+        assert torch.allclose(dgain, gw, rtol=1e-12, atol=1e-12)
+
+
+def test_rope_backward_is_the_inverse_rotation():
+    g = torch.Generator().manual_seed(42)
+    H, hd, m = 2, 16, 7
+    x = torch.randn(m, H * hd, generator=g, dtype=F64)
+    dy = torch.randn(m, H * hd, generator=g, dtype=F64)
+    pos = torch.randint(0, 131072, (m,), generator=g)
+    xa = x.clone().requires_grad_(True)
+    # autograd through the complex-number form of the rotation (not the oracle's code)
+    z = torch.view_as_complex(xa.reshape(m, H, hd // 2, 2))
+    i = torch.arange(hd // 2, dtype=F64)
+    ang = pos.to(F64)[:, None, None] * (10000.0 ** (-2.0 * i / hd))[None, None, :]
+    y = torch.view_as_real(z * torch.polar(torch.ones_like(ang), ang)).reshape(m, H * hd)
+    (gx,) = torch.autograd.grad(y, xa, grad_outputs=dy)
+    assert torch.allclose(O.rope_backward(dy, pos, H, hd, 10000.0), gx, rtol=1e-12, atol=1e-12)
+    # and undoes the forward exactly (orthogonal rotation)
+    assert torch.allclose(O.rope_backward(O.rope(x, pos, H, hd, 10000.0), pos, H, hd, 10000.0), x, rtol=1e-11, atol=1e-11)
+
+
+@pytest.mark.parametrize("H,Hkv", [(4, 1), (4, 2), (6, 3), (4, 4)])
+def test_gqa_backward_matches_library_autograd(H, Hkv):
+    S, hd, m = 24, 8, 10
+    q, k, v = _qkv(S, H, Hkv, hd, 43)
+    g = torch.Generator().manual_seed(44)
+    pos = torch.sort(torch.randperm(S, generator=g)[:m]).values
+    qm = q[pos]
+    do = torch.randn(m, H * hd, generator=g, dtype=F64)
+    mask = torch.arange(S)[None, :] <= pos[:, None]
+    qa = qm.reshape(m, H, hd).transpose(0, 1).clone().requires_grad_(True)
+    ka = k.reshape(S, Hkv, hd).transpose(0, 1).clone().requires_grad_(True)
+    va = v.reshape(S, Hkv, hd).transpose(0, 1).clone().requires_grad_(True)
+    o = F.scaled_dot_product_attention(qa[None], ka[None], va[None], attn_mask=mask[None, None], enable_gqa=True)[0]
+    gq, gk, gv = torch.autograd.grad(o, (qa, ka, va), grad_outputs=do.reshape(m, H, hd).transpose(0, 1))
+    dq, dk, dv = O.causal_attention_gqa_backward(qm, pos, k, v, do, H, Hkv, hd)
+    flat = lambda t: t.transpose(0, 1).reshape(t.shape[1], -1)
+    assert torch.allclose(dq, flat(gq), rtol=1e-11, atol=1e-12)
+    assert torch.allclose(dk, flat(gk), rtol=1e-11, atol=1e-12)
+    assert torch.allclose(dv, flat(gv), rtol=1e-11, atol=1e-12)
