@@ -16,9 +16,10 @@
 // the B operand those rows are the contraction index, in the order
 // bits-2-and-3-swapped within 16-row groups, so the other operand is stored
 // in that order by the transposed-tile pre-pass):
-//   * dK/dV: a workgroup owns 128 keys of one head (32 per wave, K and V
+//   * dK/dV: a workgroup owns 128 keys of one K/V head (32 per wave, K and V
 //     fragments in registers as B operands); it streams the 64-query tiles of
-//     both chunks that see those keys (Q and dO row-major for S = Q K^T and
+//     both chunks that see those keys, for every query head reading that K/V
+//     head (grouped-query attention; one for MHA) (Q and dO row-major for S = Q K^T and
 //     dP = dO V^T, Q^T and dO^T transposed for dV^T += dO^T P and
 //     dK^T += Q^T dS) through a two-stage LDS ring with direct global->LDS
 //     loads.  Lane = key, so P and dS leave the score registers as B operands;
@@ -106,27 +107,29 @@ __global__ __launch_bounds__(64 * BW) void dkv_kernel(const AttnBwdArgs a) {
   const int half = lane >> 5;
   const int ql = lane & 31;
 
-  // work item: (head, 128-key block), the earliest (most-seen) key blocks of a
-  // head first, heads contiguous per XCD.
+  // work item: (K/V head, 128-key block), the earliest (most-seen) key blocks
+  // of a head first, heads contiguous per XCD.  The block's dK, dV sum over the
+  // query heads that read this K/V head (one for MHA).
   const int64_t S = a.seq_len, CL = a.chunk_len;
   const int nkb = (int)((S + 127) / 128);
   const int nwg = gridDim.x;
   int pid = blockIdx.x;
   if ((nwg & 7) == 0) pid = (pid & 7) * (nwg >> 3) + (pid >> 3);
-  const int head = pid / nkb;
-  const int kblk = pid - head * nkb;
+  const int kvh = pid / nkb;
+  const int kblk = pid - kvh * nkb;
+  const int group = a.n_heads / a.kv_heads;
   const int64_t kb0 = (int64_t)kblk * 128;
   const int64_t kw0 = kb0 + 32 * wave;  // this wave's first key
   const int64_t key = kw0 + ql;         // this lane's key
-  const int hcol = head * HD;
-  const int64_t ld = a.hidden;
+  const int kcol = kvh * HD;
+  const int64_t ld = a.hidden, kld = a.kv_ld;
 
   // K and V fragments (B operands): lane holds key ql, dims 16*kk + 8*half .. +7.
   u32x4 kf[C::KK], vf[C::KK];
   {
     const int64_t kr = min(key, S - 1);  // keys past S: any finite row (masked: past every query)
-    const uint16_t* kp = a.k + kr * ld + hcol + 8 * half;
-    const uint16_t* vp = a.v + kr * ld + hcol + 8 * half;
+    const uint16_t* kp = a.k + kr * kld + kcol + 8 * half;
+    const uint16_t* vp = a.v + kr * kld + kcol + 8 * half;
 #pragma unroll
     for (int kk = 0; kk < C::KK; ++kk) {
       kf[kk] = *reinterpret_cast<const u32x4*>(kp + kk * 16);
@@ -142,7 +145,8 @@ __global__ __launch_bounds__(64 * BW) void dkv_kernel(const AttnBwdArgs a) {
     return (int)(max(kb0 - start, (int64_t)0) / 64);
   };
   const int f0 = first_tile(a.chunk_start0), f1 = first_tile(a.chunk_start1);
-  const int n0 = tpc - f0, n_all = n0 + tpc - f1;
+  const int n0 = tpc - f0, n_head = n0 + tpc - f1;  // tiles per query head
+  const int n_all = n_head * group;
 
   // DMA sources.  Row-major tiles: instruction j of wave w fills 1 KB block
   // b = j*BW + w, row b*RPL + lane/NCH, logical chunk (lane % NCH) ^ (row % NCH).
@@ -158,19 +162,24 @@ __global__ __launch_bounds__(64 * BW) void dkv_kernel(const AttnBwdArgs a) {
     tr_off[j] = d * 64 + ((lane % 8) ^ ((d >> 1) & 7)) * 8;
   }
 
-  auto tile_of = [&](int i, int& c, int& t) __attribute__((always_inline)) {
-    if (i < n0) {
+  // tile i: query head kvh*group + i / n_head, then chunk 0's tiles, chunk 1's
+  auto tile_of = [&](int i, int& c, int& t, int& qh) __attribute__((always_inline)) {
+    const int gi = i / n_head;
+    const int j = i - gi * n_head;
+    qh = kvh * group + gi;
+    if (j < n0) {
       c = 0;
-      t = f0 + i;
+      t = f0 + j;
     } else {
       c = 1;
-      t = f1 + (i - n0);
+      t = f1 + (j - n0);
     }
   };
 
   auto issue = [&](int i) __attribute__((always_inline)) {
-    int c, t;
-    tile_of(i, c, t);
+    int c, t, qh;
+    tile_of(i, c, t, qh);
+    const int hcol = qh * HD;
     uint8_t* stage = smem + (i & 1) * STAGE;
     const int64_t rbase = c * CL;
 #pragma unroll
@@ -180,13 +189,13 @@ __global__ __launch_bounds__(64 * BW) void dkv_kernel(const AttnBwdArgs a) {
       dma16(a.q + off, stage + (j * BW + wave) * 1024);
       dma16(a.dout + off, stage + C::TILE_BYTES + (j * BW + wave) * 1024);
     }
-    const int64_t tbase = ((c * (int64_t)a.n_heads + head) * a.tpc + t) * (int64_t)(HD * 64);
+    const int64_t tbase = ((c * (int64_t)a.n_heads + qh) * a.tpc + t) * (int64_t)(HD * 64);
 #pragma unroll
     for (int j = 0; j < C::TLOADS; ++j) {
       dma16(a.qt + tbase + tr_off[j], stage + 2 * C::TILE_BYTES + (j * BW + wave) * 1024);
       dma16(a.dot + tbase + tr_off[j], stage + 3 * C::TILE_BYTES + (j * BW + wave) * 1024);
     }
-    const float* st = a.stats + ((c * (int64_t)a.n_heads + head) * a.tpc + t) * 256;
+    const float* st = a.stats + ((c * (int64_t)a.n_heads + qh) * a.tpc + t) * 256;
     dma16(st + lane * 4, stage + 4 * C::TILE_BYTES + wave * STATS);
   };
 
@@ -211,8 +220,8 @@ __global__ __launch_bounds__(64 * BW) void dkv_kernel(const AttnBwdArgs a) {
   // MFMAs of queries 32..63, those of queries 32..63 under the first half of
   // the dV/dK MFMAs (which need only queries 0..31).
   auto compute = [&](int i) __attribute__((always_inline)) {
-    int c, t;
-    tile_of(i, c, t);
+    int c, t, qh;
+    tile_of(i, c, t, qh);
     const int64_t qp0 = (c ? a.chunk_start1 : a.chunk_start0) + (int64_t)t * 64;  // position of query 0
     if (kw0 > qp0 + 63) return;  // every key of the wave is past every query of the tile (wave-uniform)
     // queries of the tile before this lane's key are masked: offsets below qmin
@@ -326,8 +335,8 @@ __global__ __launch_bounds__(64 * BW) void dkv_kernel(const AttnBwdArgs a) {
 
   // store this lane's key row of dK (scaled) and dV; zeros where no query sees the key
   if (key < S) {
-    float* dkp = a.dk + key * ld + hcol + 4 * half;
-    float* dvp = a.dv + key * ld + hcol + 4 * half;
+    float* dkp = a.dk + key * kld + kcol + 4 * half;
+    float* dvp = a.dv + key * kld + kcol + 4 * half;
 #pragma unroll
     for (int dt = 0; dt < C::DT; ++dt)
 #pragma unroll
@@ -383,7 +392,9 @@ __global__ __launch_bounds__(64 * QW) void dq_kernel(const AttnBwdArgs a) {
   const int wave_tiles = wave_active ? (int)(wave_max_pos / 64) + 1 : 0;
 
   const int hcol = head * HD;
-  const int64_t ld = a.hidden;
+  const int64_t ld = a.hidden, kld = a.kv_ld;
+  const int kvh = head / (a.n_heads / a.kv_heads);  // this head's K/V head
+  const int kcol = kvh * HD;
 
   // Q and dO fragments (B operands): lane holds query qi, dims 16*kk + 8*half .. +7.
   u32x4 qf[C::KK], df[C::KK];
@@ -413,7 +424,7 @@ __global__ __launch_bounds__(64 * QW) void dq_kernel(const AttnBwdArgs a) {
     const int d = b * 8 + lane / 8;
     tr_off[j] = d * 64 + ((lane % 8) ^ ((d >> 1) & 7)) * 8;
   }
-  const uint16_t* kt_head = a.kt + (int64_t)head * a.n_kv_tiles * HD * 64;
+  const uint16_t* kt_head = a.kt + (int64_t)kvh * a.n_kv_tiles * HD * 64;
 
   auto issue = [&](int t) __attribute__((always_inline)) {
     uint8_t* stage = smem + (t & 1) * STAGE;
@@ -421,7 +432,7 @@ __global__ __launch_bounds__(64 * QW) void dq_kernel(const AttnBwdArgs a) {
 #pragma unroll
     for (int j = 0; j < C::TLOADS; ++j) {
       const int64_t kr = min(k0 + rm_row[j], key_end - 1);  // rows past the range: masked anyway
-      const int64_t off = kr * ld + hcol + rm_col[j];
+      const int64_t off = kr * kld + kcol + rm_col[j];
       dma16(a.k + off, stage + (j * QW + wave) * 1024);
       dma16(a.v + off, stage + C::TILE_BYTES + (j * QW + wave) * 1024);
       dma16(kt_head + (int64_t)t * HD * 64 + tr_off[j], stage + 2 * C::TILE_BYTES + (j * QW + wave) * 1024);
@@ -499,9 +510,9 @@ __global__ __launch_bounds__(64 * QW) void dq_kernel(const AttnBwdArgs a) {
 
 }  // namespace
 
-size_t attn_bwd_ws_bytes(int64_t seq_len, int64_t chunk_len, int32_t n_heads, int32_t head_dim) {
+size_t attn_bwd_ws_bytes(int64_t seq_len, int64_t chunk_len, int32_t n_heads, int32_t kv_heads, int32_t head_dim) {
   const int64_t n_kv_tiles = (seq_len + 63) / 64, tpc = (chunk_len + 63) / 64;
-  const size_t kt = (size_t)n_heads * n_kv_tiles * head_dim * 64 * 2;
+  const size_t kt = (size_t)kv_heads * n_kv_tiles * head_dim * 64 * 2;
   const size_t qt = (size_t)2 * n_heads * tpc * head_dim * 64 * 2;
   const size_t stats = (size_t)2 * n_heads * tpc * 256 * 4;
   return kt + 2 * qt + stats;
@@ -519,7 +530,8 @@ hipError_t launch_attention_backward(const AttnBwdArgs& a, hipStream_t stream) {
       hipLaunchKernelGGL(bwd_stats_kernel<64>, grid, dim3(64), 0, stream, a);
     if ((e = hipGetLastError()) != hipSuccess) return e;
   }
-  if ((e = launch_vt_tiles(a.k, a.seq_len, a.hidden, H, HD, a.kt, a.n_kv_tiles, stream)) != hipSuccess) return e;
+  if ((e = launch_vt_tiles(a.k, a.seq_len, a.kv_ld, a.kv_heads, HD, a.kt, a.n_kv_tiles, stream)) != hipSuccess)
+    return e;
   const size_t chunk_tiles = (size_t)H * a.tpc * HD * 64;
   for (int c = 0; c < 2; ++c) {
     const int64_t off = c * a.chunk_len * a.hidden;
@@ -531,7 +543,7 @@ hipError_t launch_attention_backward(const AttnBwdArgs& a, hipStream_t stream) {
       return e;
   }
   {
-    const dim3 grid((unsigned)(H * ((a.seq_len + 127) / 128)));
+    const dim3 grid((unsigned)(a.kv_heads * ((a.seq_len + 127) / 128)));
     if (HD == 128)
       hipLaunchKernelGGL(dkv_kernel<128>, grid, dim3(64 * BW), 0, stream, a);
     else

@@ -125,7 +125,10 @@ struct AttnBwdArgs {
   float* dv;             // [seq_len x hidden]
   int64_t seq_len, chunk_len, chunk_start0, chunk_start1;
   int32_t hidden, n_heads, head_dim;
-  // workspace: K^T tiles [H][n_kv_tiles][hd][64]; Q^T and dO^T tiles
+  // K/V heads (n_heads for MHA; grouped-query: query head a reads K/V head
+  // a / (n_heads / kv_heads)) and the row stride of k, v, dk, dv.
+  int32_t kv_heads, kv_ld;
+  // workspace: K^T tiles [H_kv][n_kv_tiles][hd][64]; Q^T and dO^T tiles
   // [2 chunks][H][tpc][hd][64]; per 64-query tile of (chunk, head) 256 floats:
   // log2-domain normaliser [64], delta = rowsum(dO * O) [64], zeros [128].
   uint16_t* kt;
@@ -136,7 +139,7 @@ struct AttnBwdArgs {
 };
 
 // Workspace bytes of launch_attention_backward.
-size_t attn_bwd_ws_bytes(int64_t seq_len, int64_t chunk_len, int32_t n_heads, int32_t head_dim);
+size_t attn_bwd_ws_bytes(int64_t seq_len, int64_t chunk_len, int32_t n_heads, int32_t kv_heads, int32_t head_dim);
 
 // Pre-passes (stats, K^T, Q^T, dO^T tiles), then the dK/dV and dQ kernels.
 hipError_t launch_attention_backward(const AttnBwdArgs& args, hipStream_t stream);
@@ -148,8 +151,17 @@ hipError_t launch_rms_norm(const uint16_t* x, const uint16_t* gain, int64_t n, i
 // Rotary embedding in place of the n_rows local rows (positions from the zigzag
 // chunks), n_heads heads of head_dim each, row stride ld: rows of x itself, or
 // (at_global) the rows of x at the global positions.
-hipError_t launch_rope(uint16_t* x, int64_t n_rows, int64_t ld, int32_t n_heads, int32_t head_dim, double theta,
-                       int64_t chunk_len, int64_t start0, int64_t start1, int32_t at_global, hipStream_t stream);
+// x_f32: the rows are fp32 (else bf16); inverse: rotate by -angle (the backward).
+hipError_t launch_rope(void* x, int32_t x_f32, int32_t inverse, int64_t n_rows, int64_t ld, int32_t n_heads,
+                       int32_t head_dim, double theta, int64_t chunk_len, int64_t start0, int64_t start1,
+                       int32_t at_global, hipStream_t stream);
+
+// Backward of RMSNorm over x [n x h] (bf16, h % 8 == 0, h <= 8192): dx (bf16)
+// and dgain (fp32 [h]); partial: fp32 [rms_norm_bwd_blocks(n) x h] scratch.
+int64_t rms_norm_bwd_blocks(int64_t n);
+hipError_t launch_rms_norm_backward(const uint16_t* x, const uint16_t* gain, const uint16_t* dy, int64_t n,
+                                    int32_t h, float eps, uint16_t* dx, float* dgain, float* partial,
+                                    hipStream_t stream);
 
 // dst[c * ld_out + r] = f(src[r * ld_in + c]) for r < R, c < C (C % 64 == 0), and 0
 // for R <= r < ld_out (ld_out % 64 == 0): a transpose of bf16 (src_f32: fp32)

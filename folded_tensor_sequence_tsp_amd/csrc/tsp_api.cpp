@@ -426,6 +426,55 @@ void ring_io(GemmArgs& g, int32_t D, int32_t pos, const uint16_t* residual, uint
   }
 }
 
+tsp_status run_attn_backward(const tsp_plan* plan, const tsp_dims* dims, int32_t kv_heads, const uint16_t* q,
+                             const uint16_t* k_full, const uint16_t* v_full, const uint16_t* attn_out,
+                             const uint16_t* attn_lo, const float* lse, const uint16_t* d_attn, float* dq,
+                             float* dk_full, float* dv_full, void* workspace, size_t ws_bytes, hipStream_t stream) {
+  tsp_status s;
+  if ((s = check_ptr(q)) != TSP_OK || (s = check_ptr(k_full)) != TSP_OK || (s = check_ptr(v_full)) != TSP_OK ||
+      (s = check_ptr(attn_out)) != TSP_OK || (s = check_ptr_nullable(attn_lo)) != TSP_OK ||
+      (s = check_ptr(lse)) != TSP_OK || (s = check_ptr(d_attn)) != TSP_OK || (s = check_ptr(dq)) != TSP_OK ||
+      (s = check_ptr(dk_full)) != TSP_OK || (s = check_ptr(dv_full)) != TSP_OK)
+    return s;
+  if (dk_full == dv_full || (void*)dq == (void*)dk_full || (void*)dq == (void*)dv_full) return TSP_ERR_INVALID_ARG;
+  const size_t need = attn_bwd_ws_bytes(plan->seq_len, plan->chunk_len, dims->n_heads, kv_heads, dims->head_dim);
+  if (!workspace) return TSP_ERR_WORKSPACE;
+  if (!aligned16(workspace)) return TSP_ERR_ALIGNMENT;
+  if (ws_bytes < need) return TSP_ERR_WORKSPACE;
+  AttnBwdArgs a{};
+  a.q = q;
+  a.k = k_full;
+  a.v = v_full;
+  a.o = attn_out;
+  a.o_lo = attn_lo;
+  a.dout = d_attn;
+  a.lse = lse;
+  a.dq = dq;
+  a.dk = dk_full;
+  a.dv = dv_full;
+  a.seq_len = plan->seq_len;
+  a.chunk_len = plan->chunk_len;
+  a.chunk_start0 = plan->chunk_start[0];
+  a.chunk_start1 = plan->chunk_start[1];
+  a.hidden = dims->hidden;
+  a.n_heads = dims->n_heads;
+  a.head_dim = dims->head_dim;
+  a.kv_heads = kv_heads;
+  a.kv_ld = kv_heads * dims->head_dim;
+  a.n_kv_tiles = (plan->seq_len + 63) / 64;
+  a.tpc = (plan->chunk_len + 63) / 64;
+  // workspace: K^T tiles, Q^T tiles, dO^T tiles, stats (each size a multiple of 1 KB)
+  uint8_t* w = static_cast<uint8_t*>(workspace);
+  a.kt = reinterpret_cast<uint16_t*>(w);
+  w += (size_t)kv_heads * a.n_kv_tiles * dims->head_dim * 64 * 2;
+  a.qt = reinterpret_cast<uint16_t*>(w);
+  w += (size_t)2 * dims->n_heads * a.tpc * dims->head_dim * 64 * 2;
+  a.dot = reinterpret_cast<uint16_t*>(w);
+  w += (size_t)2 * dims->n_heads * a.tpc * dims->head_dim * 64 * 2;
+  a.stats = reinterpret_cast<float*>(w);
+  return from_hip(launch_attention_backward(a, stream));
+}
+
 }  // namespace
 
 extern "C" {
@@ -492,9 +541,12 @@ size_t tsp_workspace_size(int64_t n_tokens, const tsp_dims* dims, int32_t D, int
     case TSP_WS_PROJ_BWD:
       if (check_dims(dims, D, true, false) != TSP_OK) return 0;
       return proj_bwd_ws(n_tokens, dims, D).total;
+    case TSP_WS_RMS_BWD:
+      if (!dims || dims->hidden <= 0) return 0;
+      return round_up((size_t)rms_norm_bwd_blocks(n_tokens) * dims->hidden * 4);
     case TSP_WS_ATTN_BWD:
       if (check_dims(dims, D, true, false, 0) != TSP_OK || n_tokens % 2 != 0) return 0;
-      return attn_bwd_ws_bytes(n_tokens * D, n_tokens / 2, dims->n_heads, dims->head_dim);
+      return attn_bwd_ws_bytes(n_tokens * D, n_tokens / 2, dims->n_heads, dims->n_heads, dims->head_dim);
     default:
       return 0;
   }
@@ -545,6 +597,7 @@ tsp_status tsp_attn_core_lse(const tsp_plan* plan, const tsp_dims* dims, const u
   return run_core(plan, dims, q, k_full, v_full, attn_out, attn_lo, workspace, stream, lse);
 }
 
+
 tsp_status tsp_attn_core_backward(const tsp_plan* plan, const tsp_dims* dims, const uint16_t* q,
                                   const uint16_t* k_full, const uint16_t* v_full, const uint16_t* attn_out,
                                   const uint16_t* attn_lo, const float* lse, const uint16_t* d_attn, float* dq,
@@ -553,46 +606,8 @@ tsp_status tsp_attn_core_backward(const tsp_plan* plan, const tsp_dims* dims, co
   tsp_status s;
   if ((s = check_plan(plan)) != TSP_OK) return s;
   if ((s = check_dims(dims, plan->D, true, false, 0)) != TSP_OK) return s;
-  if ((s = check_ptr(q)) != TSP_OK || (s = check_ptr(k_full)) != TSP_OK || (s = check_ptr(v_full)) != TSP_OK ||
-      (s = check_ptr(attn_out)) != TSP_OK || (s = check_ptr_nullable(attn_lo)) != TSP_OK ||
-      (s = check_ptr(lse)) != TSP_OK || (s = check_ptr(d_attn)) != TSP_OK || (s = check_ptr(dq)) != TSP_OK ||
-      (s = check_ptr(dk_full)) != TSP_OK || (s = check_ptr(dv_full)) != TSP_OK)
-    return s;
-  if (dk_full == dv_full || (void*)dq == (void*)dk_full || (void*)dq == (void*)dv_full) return TSP_ERR_INVALID_ARG;
-  const size_t need = attn_bwd_ws_bytes(plan->seq_len, plan->chunk_len, dims->n_heads, dims->head_dim);
-  if (!workspace) return TSP_ERR_WORKSPACE;
-  if (!aligned16(workspace)) return TSP_ERR_ALIGNMENT;
-  if (ws_bytes < need) return TSP_ERR_WORKSPACE;
-  AttnBwdArgs a{};
-  a.q = q;
-  a.k = k_full;
-  a.v = v_full;
-  a.o = attn_out;
-  a.o_lo = attn_lo;
-  a.dout = d_attn;
-  a.lse = lse;
-  a.dq = dq;
-  a.dk = dk_full;
-  a.dv = dv_full;
-  a.seq_len = plan->seq_len;
-  a.chunk_len = plan->chunk_len;
-  a.chunk_start0 = plan->chunk_start[0];
-  a.chunk_start1 = plan->chunk_start[1];
-  a.hidden = dims->hidden;
-  a.n_heads = dims->n_heads;
-  a.head_dim = dims->head_dim;
-  a.n_kv_tiles = (plan->seq_len + 63) / 64;
-  a.tpc = (plan->chunk_len + 63) / 64;
-  // workspace: K^T tiles, Q^T tiles, dO^T tiles, stats (each size a multiple of 1 KB)
-  uint8_t* w = static_cast<uint8_t*>(workspace);
-  a.kt = reinterpret_cast<uint16_t*>(w);
-  w += (size_t)dims->n_heads * a.n_kv_tiles * dims->head_dim * 64 * 2;
-  a.qt = reinterpret_cast<uint16_t*>(w);
-  w += (size_t)2 * dims->n_heads * a.tpc * dims->head_dim * 64 * 2;
-  a.dot = reinterpret_cast<uint16_t*>(w);
-  w += (size_t)2 * dims->n_heads * a.tpc * dims->head_dim * 64 * 2;
-  a.stats = reinterpret_cast<float*>(w);
-  return from_hip(launch_attention_backward(a, stream));
+  return run_attn_backward(plan, dims, dims->n_heads, q, k_full, v_full, attn_out, attn_lo, lse, d_attn, dq,
+                           dk_full, dv_full, workspace, ws_bytes, stream);
 }
 
 tsp_status tsp_attn_out(int64_t n_tokens, const tsp_dims* dims, int32_t D, int32_t start_shard,
@@ -854,13 +869,50 @@ tsp_status tsp_rope(const tsp_plan* plan, int32_t n_heads, int32_t n_kv_heads, i
   if (head_dim % 8 != 0) return TSP_ERR_UNSUPPORTED;
   if (!(theta > 1.0) || !(theta < 1.0e300)) return TSP_ERR_INVALID_ARG;
   if ((s = check_ptr_nullable(q)) != TSP_OK || (s = check_ptr_nullable(k_full)) != TSP_OK) return s;
-  if (q && (s = from_hip(launch_rope(q, plan->n_local, (int64_t)n_heads * head_dim, n_heads, head_dim, theta,
+  if (q && (s = from_hip(launch_rope(q, 0, 0, plan->n_local, (int64_t)n_heads * head_dim, n_heads, head_dim, theta,
                                      plan->chunk_len, plan->chunk_start[0], plan->chunk_start[1], 0, stream))) != TSP_OK)
     return s;
   if (k_full)
-    return from_hip(launch_rope(k_full, plan->n_local, (int64_t)n_kv_heads * head_dim, n_kv_heads, head_dim, theta,
-                                plan->chunk_len, plan->chunk_start[0], plan->chunk_start[1], 1, stream));
+    return from_hip(launch_rope(k_full, 0, 0, plan->n_local, (int64_t)n_kv_heads * head_dim, n_kv_heads, head_dim,
+                                theta, plan->chunk_len, plan->chunk_start[0], plan->chunk_start[1], 1, stream));
   return TSP_OK;
+}
+
+tsp_status tsp_rope_backward(const tsp_plan* plan, int32_t n_heads, int32_t n_kv_heads, int32_t head_dim,
+                             double theta, float* dq, float* dk_own, hipStream_t stream) {
+  tsp_status s;
+  if ((s = check_plan(plan)) != TSP_OK) return s;
+  if (n_heads <= 0 || n_kv_heads <= 0 || head_dim <= 0) return TSP_ERR_SHAPE;
+  if (head_dim % 8 != 0) return TSP_ERR_UNSUPPORTED;
+  if (!(theta > 1.0) || !(theta < 1.0e300)) return TSP_ERR_INVALID_ARG;
+  if ((s = check_ptr_nullable(dq)) != TSP_OK || (s = check_ptr_nullable(dk_own)) != TSP_OK) return s;
+  if (dq && (void*)dq == (void*)dk_own) return TSP_ERR_INVALID_ARG;
+  if (dq && (s = from_hip(launch_rope(dq, 1, 1, plan->n_local, (int64_t)n_heads * head_dim, n_heads, head_dim, theta,
+                                      plan->chunk_len, plan->chunk_start[0], plan->chunk_start[1], 0, stream))) != TSP_OK)
+    return s;
+  if (dk_own)
+    return from_hip(launch_rope(dk_own, 1, 1, plan->n_local, (int64_t)n_kv_heads * head_dim, n_kv_heads, head_dim,
+                                theta, plan->chunk_len, plan->chunk_start[0], plan->chunk_start[1], 0, stream));
+  return TSP_OK;
+}
+
+tsp_status tsp_rms_norm_backward(int64_t n_tokens, int32_t hidden, const uint16_t* x, const uint16_t* gain, float eps,
+                                 const uint16_t* dy, uint16_t* dx, float* dgain, void* workspace, size_t ws_bytes,
+                                 hipStream_t stream) {
+  tsp_status s;
+  if (n_tokens < 0 || hidden <= 0) return TSP_ERR_SHAPE;
+  if (hidden % 8 != 0 || hidden > 8192) return TSP_ERR_UNSUPPORTED;
+  if (!(eps >= 0.0f) || !(eps < 1.0e30f)) return TSP_ERR_INVALID_ARG;
+  if ((s = check_ptr(x)) != TSP_OK || (s = check_ptr(gain)) != TSP_OK || (s = check_ptr(dy)) != TSP_OK ||
+      (s = check_ptr(dx)) != TSP_OK || (s = check_ptr(dgain)) != TSP_OK)
+    return s;
+  if (dx == x || dx == dy) return TSP_ERR_INVALID_ARG;
+  const size_t need = round_up((size_t)rms_norm_bwd_blocks(n_tokens) * hidden * 4);
+  if (need > 0 && !workspace) return TSP_ERR_WORKSPACE;
+  if (workspace && !aligned16(workspace)) return TSP_ERR_ALIGNMENT;
+  if (ws_bytes < need) return TSP_ERR_WORKSPACE;
+  return from_hip(launch_rms_norm_backward(x, gain, dy, n_tokens, hidden, eps, dx, dgain,
+                                           static_cast<float*>(workspace), stream));
 }
 
 tsp_status tsp_attn_project_gqa(const tsp_plan* plan, const tsp_dims* dims, int32_t n_kv_heads,
@@ -930,6 +982,56 @@ tsp_status tsp_attn_core_gqa(const tsp_plan* plan, const tsp_dims* dims, int32_t
   a.vt = static_cast<uint16_t*>(workspace);
   a.n_kv_tiles = attn_kv_tiles(plan->seq_len);
   return from_hip(launch_attention(a, stream));
+}
+
+tsp_status tsp_attn_core_gqa_lse(const tsp_plan* plan, const tsp_dims* dims, int32_t n_kv_heads, const uint16_t* q,
+                                 const uint16_t* k_full, const uint16_t* v_full, uint16_t* attn_out,
+                                 uint16_t* attn_lo, float* lse, void* workspace, size_t ws_bytes,
+                                 hipStream_t stream) {
+  tsp_status s;
+  if ((s = check_ptr(lse)) != TSP_OK) return s;
+  if ((s = check_plan(plan)) != TSP_OK) return s;
+  if ((s = check_dims(dims, plan->D, true, false, 0)) != TSP_OK) return s;
+  if ((s = check_gqa(dims, plan->D, n_kv_heads, false)) != TSP_OK) return s;
+  if ((s = check_ptr(q)) != TSP_OK || (s = check_ptr(k_full)) != TSP_OK || (s = check_ptr(v_full)) != TSP_OK ||
+      (s = check_ptr(attn_out)) != TSP_OK || (s = check_ptr_nullable(attn_lo)) != TSP_OK)
+    return s;
+  if (attn_out == q || attn_lo == q || attn_lo == attn_out) return TSP_ERR_INVALID_ARG;
+  if (!workspace) return TSP_ERR_WORKSPACE;
+  if (!aligned16(workspace)) return TSP_ERR_ALIGNMENT;
+  if (ws_bytes < ws_core(plan->n_local, dims, plan->D)) return TSP_ERR_WORKSPACE;
+  AttnArgs a{};
+  a.q = q;
+  a.k = k_full;
+  a.v = v_full;
+  a.o = attn_out;
+  a.o_lo = attn_lo;
+  a.lse = lse;
+  a.seq_len = plan->seq_len;
+  a.chunk_len = plan->chunk_len;
+  a.chunk_start0 = plan->chunk_start[0];
+  a.chunk_start1 = plan->chunk_start[1];
+  a.hidden = dims->hidden;
+  a.n_heads = dims->n_heads;
+  a.head_dim = dims->head_dim;
+  a.kv_heads = n_kv_heads;
+  a.kv_ld = n_kv_heads * dims->head_dim;
+  a.vt = static_cast<uint16_t*>(workspace);
+  a.n_kv_tiles = attn_kv_tiles(plan->seq_len);
+  return from_hip(launch_attention(a, stream));
+}
+
+tsp_status tsp_attn_core_gqa_backward(const tsp_plan* plan, const tsp_dims* dims, int32_t n_kv_heads,
+                                      const uint16_t* q, const uint16_t* k_full, const uint16_t* v_full,
+                                      const uint16_t* attn_out, const uint16_t* attn_lo, const float* lse,
+                                      const uint16_t* d_attn, float* dq, float* dk_full, float* dv_full,
+                                      void* workspace, size_t ws_bytes, hipStream_t stream) {
+  tsp_status s;
+  if ((s = check_plan(plan)) != TSP_OK) return s;
+  if ((s = check_dims(dims, plan->D, true, false, 0)) != TSP_OK) return s;
+  if ((s = check_gqa(dims, plan->D, n_kv_heads, false)) != TSP_OK) return s;
+  return run_attn_backward(plan, dims, n_kv_heads, q, k_full, v_full, attn_out, attn_lo, lse, d_attn, dq, dk_full,
+                           dv_full, workspace, ws_bytes, stream);
 }
 
 tsp_status tsp_mlp_backward(int64_t n_tokens, const tsp_dims* dims, int32_t D, int32_t start_shard,

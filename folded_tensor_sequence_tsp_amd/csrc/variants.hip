@@ -1,7 +1,7 @@
 // Layer variants of a real decoder (not on the TSP pages, whose layer has no
 // norm and no positional encoding): RMSNorm and the rotary position embedding
 // of the local queries and the rank's own keys at their global zigzag
-// positions.  Both are bandwidth-bound row passes.
+// positions, and their backwards.  All are bandwidth-bound row passes.
 #include "device_common.h"
 #include "kernels.h"
 
@@ -54,8 +54,11 @@ __global__ __launch_bounds__(64 * NORM_WAVES) void rms_norm_kernel(const uint16_
 // rotated row is row `row` of x, or (at_global) row p of x: the rank's own
 // rows of a full-sequence tensor.  The angle and its cosine and sine are taken
 // in fp64 (p reaches 10^5 rad, where an fp32 angle would already be off by
-// about 1e-2), then the rotation runs in fp32.
-__global__ __launch_bounds__(256) void rope_kernel(uint16_t* __restrict__ x, int64_t n_rows, int64_t ld,
+// about 1e-2), then the rotation runs in fp32.  INVERSE rotates by -angle (the
+// transpose of the rotation: the gradient of the forward); F32 works on fp32
+// rows (gradients) instead of bf16.
+template <bool F32, bool INVERSE>
+__global__ __launch_bounds__(256) void rope_kernel(void* __restrict__ xv, int64_t n_rows, int64_t ld,
                                                    int32_t n_heads, int32_t head_dim, double log2_theta,
                                                    int64_t chunk_len, int64_t start0, int64_t start1,
                                                    int32_t at_global) {
@@ -68,13 +71,99 @@ __global__ __launch_bounds__(256) void rope_kernel(uint16_t* __restrict__ x, int
   const double ang = (double)pos * exp2(-2.0 * (double)i / (double)head_dim * log2_theta);
   double sd, cd;
   sincos(ang, &sd, &cd);
-  const float c = (float)cd, s = (float)sd;
-  uint32_t* p = reinterpret_cast<uint32_t*>(x + (at_global ? pos : row) * ld) + i;
-  for (int a = 0; a < n_heads; ++a) {
-    const uint32_t w = p[a * half];
-    const float x0 = __uint_as_float(w << 16), x1 = __uint_as_float(w & 0xffff0000u);
-    p[a * half] = pack_bf16x2(x0 * c - x1 * s, x0 * s + x1 * c);
+  const float c = (float)cd, s = INVERSE ? -(float)sd : (float)sd;
+  const int64_t r = at_global ? pos : row;
+  if constexpr (F32) {
+    float2* p = reinterpret_cast<float2*>(static_cast<float*>(xv) + r * ld) + i;
+    for (int a = 0; a < n_heads; ++a) {
+      const float2 w = p[a * half];
+      p[a * half] = make_float2(w.x * c - w.y * s, w.x * s + w.y * c);
+    }
+  } else {
+    uint32_t* p = reinterpret_cast<uint32_t*>(static_cast<uint16_t*>(xv) + r * ld) + i;
+    for (int a = 0; a < n_heads; ++a) {
+      const uint32_t w = p[a * half];
+      const float x0 = __uint_as_float(w << 16), x1 = __uint_as_float(w & 0xffff0000u);
+      p[a * half] = pack_bf16x2(x0 * c - x1 * s, x0 * s + x1 * c);
+    }
   }
+}
+
+// Backward of RMSNorm for a block of RMS_BWD_ROWS rows (one wave per row in
+// turn): with r = sqrt(mean x^2 + eps) and t = sum_j gain_j dy_j x_j,
+//   dx_j = gain_j dy_j / r - x_j t / (h r^3)    (bf16 out),
+// and the block's part of dgain_j = sum_rows dy_j x_j / r, accumulated per wave
+// in its own LDS row, then summed over the waves into partial[block][j].
+constexpr int RMS_BWD_ROWS = 64;
+__global__ __launch_bounds__(64 * NORM_WAVES) void rms_norm_bwd_kernel(
+    const uint16_t* __restrict__ x, const uint16_t* __restrict__ gain, const uint16_t* __restrict__ dy, int64_t n,
+    int32_t h, float eps, uint16_t* __restrict__ dx, float* __restrict__ partial) {
+  extern __shared__ float acc[];  // [NORM_WAVES][h]
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  float* mine = acc + (int64_t)wave * h;
+  for (int c = lane; c < h; c += 64) mine[c] = 0.0f;
+  const int64_t r0 = (int64_t)blockIdx.x * RMS_BWD_ROWS;
+  for (int k = wave; k < RMS_BWD_ROWS; k += NORM_WAVES) {
+    const int64_t row = r0 + k;
+    if (row >= n) break;
+    const uint16_t* xr = x + row * h;
+    const uint16_t* gr = dy + row * h;
+    float ss = 0.0f, t = 0.0f;
+    for (int c = lane * 8; c < h; c += 64 * 8) {
+      const u32x4 xv = *reinterpret_cast<const u32x4*>(xr + c);
+      const u32x4 gv = *reinterpret_cast<const u32x4*>(gr + c);
+      const u32x4 wv = *reinterpret_cast<const u32x4*>(gain + c);
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const float x0 = __uint_as_float(xv[j] << 16), x1 = __uint_as_float(xv[j] & 0xffff0000u);
+        const float g0 = __uint_as_float(gv[j] << 16), g1 = __uint_as_float(gv[j] & 0xffff0000u);
+        const float w0 = __uint_as_float(wv[j] << 16), w1 = __uint_as_float(wv[j] & 0xffff0000u);
+        ss = fmaf(x0, x0, fmaf(x1, x1, ss));
+        t = fmaf(w0 * g0, x0, fmaf(w1 * g1, x1, t));
+      }
+    }
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) {
+      ss += __shfl_xor(ss, off);
+      t += __shfl_xor(t, off);
+    }
+    const float inv = 1.0f / sqrtf(ss / (float)h + eps);
+    const float coef = t * inv * inv * inv / (float)h;
+    uint16_t* dr = dx + row * h;
+    for (int c = lane * 8; c < h; c += 64 * 8) {
+      const u32x4 xv = *reinterpret_cast<const u32x4*>(xr + c);
+      const u32x4 gv = *reinterpret_cast<const u32x4*>(gr + c);
+      const u32x4 wv = *reinterpret_cast<const u32x4*>(gain + c);
+      u32x4 o;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const float x0 = __uint_as_float(xv[j] << 16), x1 = __uint_as_float(xv[j] & 0xffff0000u);
+        const float g0 = __uint_as_float(gv[j] << 16), g1 = __uint_as_float(gv[j] & 0xffff0000u);
+        const float w0 = __uint_as_float(wv[j] << 16), w1 = __uint_as_float(wv[j] & 0xffff0000u);
+        o[j] = pack_bf16x2(w0 * g0 * inv - x0 * coef, w1 * g1 * inv - x1 * coef);
+        mine[c + 2 * j] += g0 * x0 * inv;
+        mine[c + 2 * j + 1] += g1 * x1 * inv;
+      }
+      *reinterpret_cast<u32x4*>(dr + c) = o;
+    }
+  }
+  __syncthreads();
+  for (int c = threadIdx.x; c < h; c += 64 * NORM_WAVES) {
+    float v = 0.0f;
+#pragma unroll
+    for (int w = 0; w < NORM_WAVES; ++w) v += acc[(int64_t)w * h + c];
+    partial[(int64_t)blockIdx.x * h + c] = v;
+  }
+}
+
+// dgain[c] = sum over the row blocks of partial[block][c].
+__global__ __launch_bounds__(256) void rms_norm_bwd_reduce_kernel(const float* __restrict__ partial, int64_t blocks,
+                                                                  int32_t h, float* __restrict__ dgain) {
+  const int c = blockIdx.x * 256 + threadIdx.x;
+  if (c >= h) return;
+  float v = 0.0f;
+  for (int64_t b = 0; b < blocks; ++b) v += partial[b * h + c];
+  dgain[c] = v;
 }
 
 }  // namespace
@@ -87,13 +176,42 @@ hipError_t launch_rms_norm(const uint16_t* x, const uint16_t* gain, int64_t n, i
   return hipGetLastError();
 }
 
-hipError_t launch_rope(uint16_t* x, int64_t n_rows, int64_t ld, int32_t n_heads, int32_t head_dim, double theta,
-                       int64_t chunk_len, int64_t start0, int64_t start1, int32_t at_global, hipStream_t stream) {
+hipError_t launch_rope(void* x, int32_t x_f32, int32_t inverse, int64_t n_rows, int64_t ld, int32_t n_heads,
+                       int32_t head_dim, double theta, int64_t chunk_len, int64_t start0, int64_t start1,
+                       int32_t at_global, hipStream_t stream) {
   if (n_rows <= 0) return hipSuccess;
   const int64_t threads = n_rows * (head_dim / 2);
-  const dim3 grid((unsigned)((threads + 255) / 256));
-  hipLaunchKernelGGL(rope_kernel, grid, dim3(256), 0, stream, x, n_rows, ld, n_heads, head_dim, log2(theta),
-                     chunk_len, start0, start1, at_global);
+  const dim3 grid((unsigned)((threads + 255) / 256)), block(256);
+  const double l2t = log2(theta);
+  if (x_f32 && inverse)
+    hipLaunchKernelGGL((rope_kernel<true, true>), grid, block, 0, stream, x, n_rows, ld, n_heads, head_dim, l2t,
+                       chunk_len, start0, start1, at_global);
+  else if (x_f32)
+    hipLaunchKernelGGL((rope_kernel<true, false>), grid, block, 0, stream, x, n_rows, ld, n_heads, head_dim, l2t,
+                       chunk_len, start0, start1, at_global);
+  else if (inverse)
+    hipLaunchKernelGGL((rope_kernel<false, true>), grid, block, 0, stream, x, n_rows, ld, n_heads, head_dim, l2t,
+                       chunk_len, start0, start1, at_global);
+  else
+    hipLaunchKernelGGL((rope_kernel<false, false>), grid, block, 0, stream, x, n_rows, ld, n_heads, head_dim, l2t,
+                       chunk_len, start0, start1, at_global);
+  return hipGetLastError();
+}
+
+int64_t rms_norm_bwd_blocks(int64_t n) { return (n + RMS_BWD_ROWS - 1) / RMS_BWD_ROWS; }
+
+hipError_t launch_rms_norm_backward(const uint16_t* x, const uint16_t* gain, const uint16_t* dy, int64_t n,
+                                    int32_t h, float eps, uint16_t* dx, float* dgain, float* partial,
+                                    hipStream_t stream) {
+  const int64_t blocks = rms_norm_bwd_blocks(n);
+  if (blocks > 0) {
+    hipLaunchKernelGGL(rms_norm_bwd_kernel, dim3((unsigned)blocks), dim3(64 * NORM_WAVES),
+                       (size_t)NORM_WAVES * h * sizeof(float), stream, x, gain, dy, n, h, eps, dx, partial);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  hipLaunchKernelGGL(rms_norm_bwd_reduce_kernel, dim3((unsigned)((h + 255) / 256)), dim3(256), 0, stream, partial,
+                     blocks, h, dgain);
   return hipGetLastError();
 }
 

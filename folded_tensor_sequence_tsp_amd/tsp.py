@@ -19,14 +19,15 @@ LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libtsp.so")
 
 TSP_OK, TSP_ERR_INVALID_ARG, TSP_ERR_SHAPE, TSP_ERR_ALIGNMENT, TSP_ERR_WORKSPACE, TSP_ERR_UNSUPPORTED, TSP_ERR_HIP = range(7)
 (WS_ATTN, WS_MLP, WS_LAYER, WS_POST, WS_CORE, WS_OUT_SHARD, WS_MLP_SHARD, WS_MLP_BWD, WS_ATTN_BWD, WS_OUT_BWD,
- WS_PROJ_BWD) = range(11)
+ WS_PROJ_BWD, WS_RMS_BWD) = range(12)
 MAX_D = 16
 
 EXPORTS = ["tsp_zigzag_plan", "tsp_workspace_size", "tsp_attn_project", "tsp_attn_core", "tsp_attn_out",
            "tsp_attn_forward", "tsp_mlp_forward", "tsp_layer_post", "tsp_layer_forward", "tsp_attn_project_shard",
            "tsp_attn_out_shard", "tsp_mlp_shard", "tsp_rms_norm", "tsp_rope", "tsp_attn_project_gqa",
            "tsp_attn_core_gqa", "tsp_mlp_backward", "tsp_attn_core_lse", "tsp_attn_core_backward",
-           "tsp_attn_out_backward", "tsp_attn_project_backward", "tsp_status_string"]
+           "tsp_attn_out_backward", "tsp_attn_project_backward", "tsp_rope_backward", "tsp_rms_norm_backward",
+           "tsp_attn_core_gqa_lse", "tsp_attn_core_gqa_backward", "tsp_status_string"]
 
 
 class TSPError(RuntimeError):
@@ -79,6 +80,11 @@ def lib() -> ctypes.CDLL:
             "tsp_attn_out_backward": [c_int64, POINTER(Dims), c_int32, c_int32, P, PP, P, P, PP, P, c_size_t, P],
             "tsp_attn_project_backward": [c_int64, POINTER(Dims), c_int32, c_int32, P, PP, P, P, P, P, P, PP, P,
                                           c_size_t, P],
+            "tsp_rope_backward": [POINTER(Plan), c_int32, c_int32, c_int32, ctypes.c_double, P, P, P],
+            "tsp_rms_norm_backward": [c_int64, c_int32, P, P, ctypes.c_float, P, P, P, P, c_size_t, P],
+            "tsp_attn_core_gqa_lse": [POINTER(Plan), POINTER(Dims), c_int32, P, P, P, P, P, P, P, c_size_t, P],
+            "tsp_attn_core_gqa_backward": [POINTER(Plan), POINTER(Dims), c_int32, P, P, P, P, P, P, P, P, P, P, P,
+                                           c_size_t, P],
             "tsp_status_string": [c_int32],
         }
         for name, args in sig.items():
@@ -363,6 +369,65 @@ def attn_core_gqa(plan: Plan, dims: Dims, n_kv_heads: int, q, k_full, v_full, at
             _dev_tensor(attn_out, (n, h), "attn_out"), _opt_tensor(attn_lo, (n, h), "attn_lo"))
     _check(lib().tsp_attn_core_gqa(ctypes.byref(plan), ctypes.byref(dims), n_kv_heads, *args, ws, nbytes,
                                    _stream(stream)), "tsp_attn_core_gqa")
+
+
+def rope_backward(plan: Plan, n_heads: int, n_kv_heads: int, head_dim: int, theta: float, dq=None, dk_own=None,
+                  stream=None):
+    """Inverse rotation of fp32 gradients in place: dq [n_local, H*hd], dk_own
+    [n_local, H_kv*hd] (the rank's own K rows, local order)."""
+    qa = _opt_f32(dq, (plan.n_local, n_heads * head_dim), "dq")
+    ka = _opt_f32(dk_own, (plan.n_local, n_kv_heads * head_dim), "dk_own")
+    _check(lib().tsp_rope_backward(ctypes.byref(plan), n_heads, n_kv_heads, head_dim, float(theta), qa, ka,
+                                   _stream(stream)), "tsp_rope_backward")
+
+
+def rms_norm_backward(x, gain, eps: float, dy, dx, dgain, workspace=None, stream=None):
+    """dx (bf16) and dgain (fp32 [h]) of y = rms_norm(x) * gain."""
+    n, h = x.shape
+    need = workspace_size(n, Dims(h, 1, h, 0), 1, WS_RMS_BWD)
+    if workspace is None:
+        workspace = torch.empty(max(need, 256), dtype=torch.uint8, device=x.device)
+    ws, nbytes = _workspace(workspace, need)
+    _check(lib().tsp_rms_norm_backward(n, h, _dev_tensor(x, (n, h), "x"), _dev_tensor(gain, (h,), "gain"), float(eps),
+                                       _dev_tensor(dy, (n, h), "dy"), _dev_tensor(dx, (n, h), "dx"),
+                                       _f32_tensor(dgain, (h,), "dgain"), ws, nbytes, _stream(stream)),
+           "tsp_rms_norm_backward")
+
+
+def attn_core_gqa_lse(plan: Plan, dims: Dims, n_kv_heads: int, q, k_full, v_full, attn_out, lse, attn_lo=None,
+                      workspace=None, stream=None):
+    n, h, S = plan.n_local, dims.hidden, plan.seq_len
+    kvw = n_kv_heads * dims.head_dim
+    need = workspace_size(n, dims, plan.D, WS_CORE)
+    if workspace is None:
+        workspace = torch.empty(max(need, 256), dtype=torch.uint8, device=q.device)
+    ws, nbytes = _workspace(workspace, need)
+    args = (_dev_tensor(q, (n, h), "q"), _dev_tensor(k_full, (S, kvw), "k_full"), _dev_tensor(v_full, (S, kvw), "v_full"),
+            _dev_tensor(attn_out, (n, h), "attn_out"), _opt_tensor(attn_lo, (n, h), "attn_lo"),
+            _f32_tensor(lse, (dims.n_heads, n), "lse"))
+    _check(lib().tsp_attn_core_gqa_lse(ctypes.byref(plan), ctypes.byref(dims), n_kv_heads, *args, ws, nbytes,
+                                       _stream(stream)), "tsp_attn_core_gqa_lse")
+
+
+def attn_core_gqa_backward(plan: Plan, dims: Dims, n_kv_heads: int, q, k_full, v_full, attn_out, lse, d_attn, dq,
+                           dk_full, dv_full, attn_lo=None, workspace=None, stream=None):
+    n, h, S = plan.n_local, dims.hidden, plan.seq_len
+    kvw = n_kv_heads * dims.head_dim
+    need = workspace_size(n, dims, plan.D, WS_ATTN_BWD)
+    if workspace is None:
+        workspace = torch.empty(max(need, 256), dtype=torch.uint8, device=q.device)
+    ws, nbytes = _workspace(workspace, need)
+    args = (_dev_tensor(q, (n, h), "q"), _dev_tensor(k_full, (S, kvw), "k_full"), _dev_tensor(v_full, (S, kvw), "v_full"),
+            _dev_tensor(attn_out, (n, h), "attn_out"), _opt_tensor(attn_lo, (n, h), "attn_lo"),
+            _f32_tensor(lse, (dims.n_heads, n), "lse"), _dev_tensor(d_attn, (n, h), "d_attn"),
+            _f32_tensor(dq, (n, h), "dq"), _f32_tensor(dk_full, (S, kvw), "dk_full"),
+            _f32_tensor(dv_full, (S, kvw), "dv_full"))
+    _check(lib().tsp_attn_core_gqa_backward(ctypes.byref(plan), ctypes.byref(dims), n_kv_heads, *args, ws, nbytes,
+                                            _stream(stream)), "tsp_attn_core_gqa_backward")
+
+
+def _opt_f32(t, shape, name):
+    return c_void_p(None) if t is None else _f32_tensor(t, shape, name)
 
 
 def _f32_shards(ts, D: int, shape, name: str):

@@ -89,7 +89,8 @@ typedef enum {
   TSP_WS_MLP_BWD = 7,
   TSP_WS_ATTN_BWD = 8,
   TSP_WS_OUT_BWD = 9,
-  TSP_WS_PROJ_BWD = 10
+  TSP_WS_PROJ_BWD = 10,
+  TSP_WS_RMS_BWD = 11
 } tsp_ws_kind;
 
 /*
@@ -444,6 +445,34 @@ tsp_status tsp_rope(const tsp_plan* plan, int32_t n_heads, int32_t n_kv_heads, i
                     uint16_t* q, uint16_t* k_full, hipStream_t stream);
 
 /*
+ * Backward of tsp_rope: the rotation of each pair is orthogonal, so the
+ * gradient is the rotation by -angle, applied in place to fp32 gradients:
+ *   dq     : device, fp32 [n_local x n_heads*head_dim], nullable; local rows.
+ *   dk_own : device, fp32 [n_local x n_kv_heads*head_dim], nullable: the
+ *            gradients of the rank's own K rows, in local row order (its rows
+ *            of the K gradients after every rank's contributions are summed).
+ * Errors: as tsp_rope, plus TSP_ERR_INVALID_ARG when dq and dk_own coincide.
+ */
+tsp_status tsp_rope_backward(const tsp_plan* plan, int32_t n_heads, int32_t n_kv_heads, int32_t head_dim,
+                             double theta, float* dq, float* dk_own, hipStream_t stream);
+
+/*
+ * Backward of tsp_rms_norm (Zhang & Sennrich 2019): with r = sqrt(mean x^2 + eps)
+ * per row and t = sum_j gain_j dy_j x_j,
+ *   dx_j = gain_j dy_j / r - x_j t / (hidden r^3)      (bf16 out)
+ *   dgain_j = sum over the rows of dy_j x_j / r        (fp32 out, summed in a
+ *                                                       fixed order: deterministic)
+ *   x, gain, dy : device, bf16 ([n x hidden], [hidden], [n x hidden]); hidden % 8 == 0, <= 8192.
+ *   dx     : device, bf16 [n x hidden], out; aliases neither x nor dy.
+ *   dgain  : device, fp32 [hidden], out.
+ *   workspace: >= tsp_workspace_size(n_tokens, dims with this hidden, 1, TSP_WS_RMS_BWD)
+ *              bytes (fp32 partial sums per 64-row block).
+ */
+tsp_status tsp_rms_norm_backward(int64_t n_tokens, int32_t hidden, const uint16_t* x, const uint16_t* gain, float eps,
+                                 const uint16_t* dy, uint16_t* dx, float* dgain, void* workspace, size_t ws_bytes,
+                                 hipStream_t stream);
+
+/*
  * Grouped-query attention (Ainslie et al. 2023): n_kv_heads K/V heads, query
  * head a reads K/V head a / (n_heads / n_kv_heads).
  * tsp_attn_project_gqa: tsp_attn_project with shard d's weights
@@ -462,6 +491,23 @@ tsp_status tsp_attn_project_gqa(const tsp_plan* plan, const tsp_dims* dims, int3
 tsp_status tsp_attn_core_gqa(const tsp_plan* plan, const tsp_dims* dims, int32_t n_kv_heads, const uint16_t* q,
                              const uint16_t* k_full, const uint16_t* v_full, uint16_t* attn_out, uint16_t* attn_lo,
                              void* workspace, size_t ws_bytes, hipStream_t stream);
+
+/*
+ * Grouped-query forms of tsp_attn_core_lse and tsp_attn_core_backward: k_full,
+ * v_full, dk_full and dv_full are [seq_len x n_kv_heads*head_dim]; the K/V
+ * gradients of one K/V head sum over the n_heads / n_kv_heads query heads that
+ * read it.  Workspaces: TSP_WS_CORE and TSP_WS_ATTN_BWD (those of MHA) are
+ * enough.  Errors: as the MHA calls, plus TSP_ERR_SHAPE for n_kv_heads.
+ */
+tsp_status tsp_attn_core_gqa_lse(const tsp_plan* plan, const tsp_dims* dims, int32_t n_kv_heads, const uint16_t* q,
+                                 const uint16_t* k_full, const uint16_t* v_full, uint16_t* attn_out,
+                                 uint16_t* attn_lo, float* lse, void* workspace, size_t ws_bytes,
+                                 hipStream_t stream);
+tsp_status tsp_attn_core_gqa_backward(const tsp_plan* plan, const tsp_dims* dims, int32_t n_kv_heads,
+                                      const uint16_t* q, const uint16_t* k_full, const uint16_t* v_full,
+                                      const uint16_t* attn_out, const uint16_t* attn_lo, const float* lse,
+                                      const uint16_t* d_attn, float* dq, float* dk_full, float* dv_full,
+                                      void* workspace, size_t ws_bytes, hipStream_t stream);
 
 /*
  * Backward pass of the MLP ring for the rank's own tokens (the pages describe
