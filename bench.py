@@ -155,6 +155,25 @@ def row_timings(plan, dims, D, layer0, x0, q, a, a_lo, out, ws_core, fl, dev, re
         ("variant: GQA attention, 8 K/V heads (tsp_attn_core_gqa)", "attn",
          lambda: tsp.attn_core_gqa(plan, dims, 8, q, k8, v8, a, a_lo, workspace=ws_core)),
     ]
+    # the variants' backwards: RMSNorm (x, dy read, dx written), RoPE of the fp32
+    # gradients of q and the own K rows (read and written), GQA attention
+    lse8 = torch.empty(H, n, dtype=torch.float32, device=dev)
+    tsp.attn_core_gqa_lse(plan, dims, 8, q, k8, v8, a, lse8, attn_lo=a_lo, workspace=ws_core)
+    dk8 = torch.empty(plan.seq_len, kv8, dtype=torch.float32, device=dev)
+    dv8 = torch.empty(plan.seq_len, kv8, dtype=torch.float32, device=dev)
+    dgain = torch.empty(h, dtype=torch.float32, device=dev)
+    dq_rope = torch.zeros(n, h, dtype=torch.float32, device=dev)
+    dk_rope = torch.zeros(n, h, dtype=torch.float32, device=dev)
+    ws_rms = tsp.alloc_workspace(n, dims, 1, tsp.WS_RMS_BWD, device=dev)
+    calls += [
+        ("variant backward: RMSNorm dx, dgain (tsp_rms_norm_backward)", "hbm:" + str(3 * n * h * 2 + h * 2),
+         lambda: tsp.rms_norm_backward(x0, gain, 1e-6, d_attn, d_attn_b, dgain, workspace=ws_rms)),
+        ("variant backward: RoPE of dq and own dk rows (tsp_rope_backward)", "hbm:" + str(2 * 2 * n * h * 4),
+         lambda: tsp.rope_backward(plan, H, H, hd, 10000.0, dq_rope, dk_rope)),
+        ("variant backward: GQA attention, 8 K/V heads (tsp_attn_core_gqa_backward)", "attn_bwd",
+         lambda: tsp.attn_core_gqa_backward(plan, dims, 8, q, k8, v8, a, lse8, d_attn, dq_b, dk8, dv8,
+                                            attn_lo=a_lo, workspace=ws_abwd)),
+    ]
     stream = torch.cuda.current_stream()
     rows = {}
     for name, key, f in calls:
@@ -173,7 +192,7 @@ def row_timings(plan, dims, D, layer0, x0, q, a, a_lo, out, ws_core, fl, dev, re
             tf = fl[key] / (ms * 1e-3) / 1e12
             rows[name] = {"ms": round(ms, 4), "tflops": round(tf, 1), "frac": round(tf / PEAK_BF16_TFLOPS, 4)}
     del ws_mlp, ws_mlp_s, ws_out_s, k8, v8, ws_bwd, dw1, dw2, dy, dx, ws_abwd, dq_b, dk_b, dv_b, lse, d_attn
-    del dwo_b, dwqkv_b, d_attn_b, dx_b, ws_obwd, ws_pbwd
+    del dwo_b, dwqkv_b, d_attn_b, dx_b, ws_obwd, ws_pbwd, lse8, dk8, dv8, dgain, dq_rope, dk_rope, ws_rms
     return rows
 
 

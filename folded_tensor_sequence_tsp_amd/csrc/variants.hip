@@ -92,16 +92,21 @@ __global__ __launch_bounds__(256) void rope_kernel(void* __restrict__ xv, int64_
 // Backward of RMSNorm for a block of RMS_BWD_ROWS rows (one wave per row in
 // turn): with r = sqrt(mean x^2 + eps) and t = sum_j gain_j dy_j x_j,
 //   dx_j = gain_j dy_j / r - x_j t / (h r^3)    (bf16 out),
-// and the block's part of dgain_j = sum_rows dy_j x_j / r, accumulated per wave
-// in its own LDS row, then summed over the waves into partial[block][j].
-constexpr int RMS_BWD_ROWS = 64;
+// and the block's part of dgain_j = sum_rows dy_j x_j / r: each lane keeps its
+// columns' sums in registers (columns lane*8 + 512*p .. +7), the waves add them
+// in LDS once per block, and the block writes partial[block][j].
+constexpr int RMS_BWD_ROWS = 32;
+constexpr int RMS_BWD_MAXP = 16;  // 512-column passes: hidden <= 8192
 __global__ __launch_bounds__(64 * NORM_WAVES) void rms_norm_bwd_kernel(
     const uint16_t* __restrict__ x, const uint16_t* __restrict__ gain, const uint16_t* __restrict__ dy, int64_t n,
     int32_t h, float eps, uint16_t* __restrict__ dx, float* __restrict__ partial) {
-  extern __shared__ float acc[];  // [NORM_WAVES][h]
+  extern __shared__ float acc_lds[];  // [NORM_WAVES][h]
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  float* mine = acc + (int64_t)wave * h;
-  for (int c = lane; c < h; c += 64) mine[c] = 0.0f;
+  float acc[RMS_BWD_MAXP][8];
+#pragma unroll
+  for (int p = 0; p < RMS_BWD_MAXP; ++p)
+#pragma unroll
+    for (int j = 0; j < 8; ++j) acc[p][j] = 0.0f;
   const int64_t r0 = (int64_t)blockIdx.x * RMS_BWD_ROWS;
   for (int k = wave; k < RMS_BWD_ROWS; k += NORM_WAVES) {
     const int64_t row = r0 + k;
@@ -109,17 +114,21 @@ __global__ __launch_bounds__(64 * NORM_WAVES) void rms_norm_bwd_kernel(
     const uint16_t* xr = x + row * h;
     const uint16_t* gr = dy + row * h;
     float ss = 0.0f, t = 0.0f;
-    for (int c = lane * 8; c < h; c += 64 * 8) {
-      const u32x4 xv = *reinterpret_cast<const u32x4*>(xr + c);
-      const u32x4 gv = *reinterpret_cast<const u32x4*>(gr + c);
-      const u32x4 wv = *reinterpret_cast<const u32x4*>(gain + c);
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const float x0 = __uint_as_float(xv[j] << 16), x1 = __uint_as_float(xv[j] & 0xffff0000u);
-        const float g0 = __uint_as_float(gv[j] << 16), g1 = __uint_as_float(gv[j] & 0xffff0000u);
-        const float w0 = __uint_as_float(wv[j] << 16), w1 = __uint_as_float(wv[j] & 0xffff0000u);
-        ss = fmaf(x0, x0, fmaf(x1, x1, ss));
-        t = fmaf(w0 * g0, x0, fmaf(w1 * g1, x1, t));
+    for (int p = 0; p < RMS_BWD_MAXP; ++p) {
+      const int c = lane * 8 + p * 512;
+      if (c < h) {
+        const u32x4 xv = *reinterpret_cast<const u32x4*>(xr + c);
+        const u32x4 gv = *reinterpret_cast<const u32x4*>(gr + c);
+        const u32x4 wv = *reinterpret_cast<const u32x4*>(gain + c);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const float x0 = __uint_as_float(xv[j] << 16), x1 = __uint_as_float(xv[j] & 0xffff0000u);
+          const float g0 = __uint_as_float(gv[j] << 16), g1 = __uint_as_float(gv[j] & 0xffff0000u);
+          const float w0 = __uint_as_float(wv[j] << 16), w1 = __uint_as_float(wv[j] & 0xffff0000u);
+          ss = fmaf(x0, x0, fmaf(x1, x1, ss));
+          t = fmaf(w0 * g0, x0, fmaf(w1 * g1, x1, t));
+        }
       }
     }
 #pragma unroll
@@ -130,40 +139,63 @@ __global__ __launch_bounds__(64 * NORM_WAVES) void rms_norm_bwd_kernel(
     const float inv = 1.0f / sqrtf(ss / (float)h + eps);
     const float coef = t * inv * inv * inv / (float)h;
     uint16_t* dr = dx + row * h;
-    for (int c = lane * 8; c < h; c += 64 * 8) {
-      const u32x4 xv = *reinterpret_cast<const u32x4*>(xr + c);
-      const u32x4 gv = *reinterpret_cast<const u32x4*>(gr + c);
-      const u32x4 wv = *reinterpret_cast<const u32x4*>(gain + c);
-      u32x4 o;
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const float x0 = __uint_as_float(xv[j] << 16), x1 = __uint_as_float(xv[j] & 0xffff0000u);
-        const float g0 = __uint_as_float(gv[j] << 16), g1 = __uint_as_float(gv[j] & 0xffff0000u);
-        const float w0 = __uint_as_float(wv[j] << 16), w1 = __uint_as_float(wv[j] & 0xffff0000u);
-        o[j] = pack_bf16x2(w0 * g0 * inv - x0 * coef, w1 * g1 * inv - x1 * coef);
-        mine[c + 2 * j] += g0 * x0 * inv;
-        mine[c + 2 * j + 1] += g1 * x1 * inv;
+    for (int p = 0; p < RMS_BWD_MAXP; ++p) {
+      const int c = lane * 8 + p * 512;
+      if (c < h) {
+        const u32x4 xv = *reinterpret_cast<const u32x4*>(xr + c);
+        const u32x4 gv = *reinterpret_cast<const u32x4*>(gr + c);
+        const u32x4 wv = *reinterpret_cast<const u32x4*>(gain + c);
+        u32x4 o;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const float x0 = __uint_as_float(xv[j] << 16), x1 = __uint_as_float(xv[j] & 0xffff0000u);
+          const float g0 = __uint_as_float(gv[j] << 16), g1 = __uint_as_float(gv[j] & 0xffff0000u);
+          const float w0 = __uint_as_float(wv[j] << 16), w1 = __uint_as_float(wv[j] & 0xffff0000u);
+          o[j] = pack_bf16x2(w0 * g0 * inv - x0 * coef, w1 * g1 * inv - x1 * coef);
+          acc[p][2 * j] = fmaf(g0 * x0, inv, acc[p][2 * j]);
+          acc[p][2 * j + 1] = fmaf(g1 * x1, inv, acc[p][2 * j + 1]);
+        }
+        *reinterpret_cast<u32x4*>(dr + c) = o;
       }
-      *reinterpret_cast<u32x4*>(dr + c) = o;
+    }
+  }
+  float* mine = acc_lds + (int64_t)wave * h;
+#pragma unroll
+  for (int p = 0; p < RMS_BWD_MAXP; ++p) {
+    const int c = lane * 8 + p * 512;
+    if (c < h) {
+#pragma unroll
+      for (int j = 0; j < 8; ++j) mine[c + j] = acc[p][j];
     }
   }
   __syncthreads();
   for (int c = threadIdx.x; c < h; c += 64 * NORM_WAVES) {
     float v = 0.0f;
 #pragma unroll
-    for (int w = 0; w < NORM_WAVES; ++w) v += acc[(int64_t)w * h + c];
+    for (int w = 0; w < NORM_WAVES; ++w) v += acc_lds[(int64_t)w * h + c];
     partial[(int64_t)blockIdx.x * h + c] = v;
   }
 }
 
-// dgain[c] = sum over the row blocks of partial[block][c].
+// dgain[c] = sum over the row blocks of partial[block][c]: a workgroup owns 64
+// columns; its 4 waves sum the blocks b = w, w+4, ... (one coalesced 256-byte
+// row segment per load), then add their 4 sums in a fixed order.
 __global__ __launch_bounds__(256) void rms_norm_bwd_reduce_kernel(const float* __restrict__ partial, int64_t blocks,
                                                                   int32_t h, float* __restrict__ dgain) {
-  const int c = blockIdx.x * 256 + threadIdx.x;
-  if (c >= h) return;
+  __shared__ float part[4][64];
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const int c = blockIdx.x * 64 + lane;
   float v = 0.0f;
-  for (int64_t b = 0; b < blocks; ++b) v += partial[b * h + c];
-  dgain[c] = v;
+  if (c < h) {
+    int64_t b = w;
+    for (; b + 12 < blocks; b += 16)  // four independent loads in flight
+      v += (partial[b * h + c] + partial[(b + 4) * h + c]) + (partial[(b + 8) * h + c] + partial[(b + 12) * h + c]);
+    for (; b < blocks; b += 4) v += partial[b * h + c];
+  }
+  part[w][lane] = v;
+  __syncthreads();
+  if (w == 0 && c < h) dgain[c] = (part[0][lane] + part[1][lane]) + (part[2][lane] + part[3][lane]);
 }
 
 }  // namespace
@@ -210,7 +242,7 @@ hipError_t launch_rms_norm_backward(const uint16_t* x, const uint16_t* gain, con
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
-  hipLaunchKernelGGL(rms_norm_bwd_reduce_kernel, dim3((unsigned)((h + 255) / 256)), dim3(256), 0, stream, partial,
+  hipLaunchKernelGGL(rms_norm_bwd_reduce_kernel, dim3((unsigned)((h + 63) / 64)), dim3(256), 0, stream, partial,
                      blocks, h, dgain);
   return hipGetLastError();
 }

@@ -397,3 +397,37 @@ def test_projection_backward_rejects(L):
     assert prj(nb=need_p - 1) == tsp.TSP_ERR_WORKSPACE
     assert L.tsp_attn_project_backward(n, ctypes.byref(_dims(n_heads=3, hidden=192)), 4, 0, A, w, A, A, A, None,
                                        A + 64, g, A, need_p, None) == tsp.TSP_ERR_SHAPE
+
+
+def test_variant_backward_rejects(L):
+    p, _, _ = tsp.zigzag_plan(2048, 4, 1)
+    rb = lambda **k: L.tsp_rope_backward(ctypes.byref(p), k.get("H", 4), 4, k.get("hd", 64), ctypes.c_double(1e4),
+                                         k.get("dq", A), k.get("dk", A + 64), None)
+    assert rb(dk=A) == tsp.TSP_ERR_INVALID_ARG                       # dq and dk_own coincide
+    assert rb(hd=60) == tsp.TSP_ERR_UNSUPPORTED
+    assert rb(H=0) == tsp.TSP_ERR_SHAPE
+    assert rb(dq=MIS) == tsp.TSP_ERR_ALIGNMENT
+    assert rb(dq=None, dk=None) == tsp.TSP_OK                        # nothing to do
+    n, h = 300, 256
+    need = tsp.workspace_size(n, _dims(), 1, tsp.WS_RMS_BWD)
+    assert need == 10 * h * 4                                        # fp32 partial sums per 32-row block
+    nb = lambda **k: L.tsp_rms_norm_backward(n, k.get("h", h), A, A + 64, ctypes.c_float(k.get("eps", 1e-6)), A + 128,
+                                             k.get("dx", A + 192), k.get("dgain", A + 256), k.get("ws", A + 512),
+                                             k.get("nb", need), None)
+    assert nb(dx=A) == tsp.TSP_ERR_INVALID_ARG                       # dx aliases x
+    assert nb(dx=A + 128) == tsp.TSP_ERR_INVALID_ARG                 # dx aliases dy
+    assert nb(h=8200) == tsp.TSP_ERR_UNSUPPORTED                     # wider than the LDS partial sums allow
+    assert nb(h=100) == tsp.TSP_ERR_UNSUPPORTED
+    assert nb(eps=-1.0) == tsp.TSP_ERR_INVALID_ARG
+    assert nb(dgain=None) == tsp.TSP_ERR_INVALID_ARG
+    assert nb(nb=need - 1) == tsp.TSP_ERR_WORKSPACE
+    d = _dims()
+    need_b = tsp.workspace_size(p.n_local, d, 4, tsp.WS_ATTN_BWD)
+    gb = lambda kv, **k: L.tsp_attn_core_gqa_backward(ctypes.byref(p), ctypes.byref(d), kv, A, A + 64, A + 128,
+                                                      A + 192, None, A + 256, A + 320, A + 384, k.get("dk", A + 448),
+                                                      A + 512, A + 1024, need_b, None)
+    assert gb(3) == tsp.TSP_ERR_SHAPE                                 # 4 query heads do not group over 3
+    assert gb(2, dk=A + 512) == tsp.TSP_ERR_INVALID_ARG               # dk = dv
+    gl = lambda kv: L.tsp_attn_core_gqa_lse(ctypes.byref(p), ctypes.byref(d), kv, A, A + 64, A + 128, A + 192, None,
+                                            None, A + 1024, need_b, None)
+    assert gl(2) == tsp.TSP_ERR_INVALID_ARG                           # lse missing
