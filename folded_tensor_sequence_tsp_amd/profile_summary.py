@@ -37,23 +37,35 @@ CSRC = os.path.join(PKG, "csrc")
 
 # Units a summary can cover: an entry point's kernels (matched by name prefix)
 # and the sources they are built from (hashed into the summary).
+# unit -> (kernel name prefixes, sources).  "kernels.h:Name" stands for the
+# definition of struct Name in kernels.h only (the arguments the kernels read),
+# so that unrelated declarations added there leave a summary valid.
 UNITS = {
-    "tsp_attn_core": (["vt_prep_kernel", "attn_kernel"], ["attention.hip", "device_common.h", "kernels.h"]),
-    "attn_kernel": (["attn_kernel"], ["attention.hip", "device_common.h", "kernels.h"]),
-    "gemm_kernel": (["gemm_kernel"], ["gemm.hip", "device_common.h", "kernels.h"]),
+    "tsp_attn_core": (["vt_prep_kernel", "attn_kernel"], ["attention.hip", "device_common.h", "kernels.h:AttnArgs"]),
+    "attn_kernel": (["attn_kernel"], ["attention.hip", "device_common.h", "kernels.h:AttnArgs"]),
+    "gemm_kernel": (["gemm_kernel"], ["gemm.hip", "device_common.h", "kernels.h:GemmArgs"]),
     # backward of the attention core (its transposed-tile pre-passes share the
     # forward's vt_prep_kernel and are listed in the table, not in the unit)
     "tsp_attn_core_backward": (["bwd_stats_kernel", "dkv_kernel", "dq_kernel"],
-                               ["attn_backward.hip", "device_common.h", "kernels.h"]),
+                               ["attn_backward.hip", "device_common.h", "kernels.h:AttnBwdArgs"]),
 }
 KERNEL_SOURCES = {k: v[1] for k, v in UNITS.items()}
+
+
+def _source_text(name: str) -> bytes:
+    fname, _, struct = name.partition(":")
+    with open(os.path.join(CSRC, fname), "rb") as f:
+        text = f.read()
+    if not struct:
+        return text
+    start = text.index(b"struct " + struct.encode() + b" {")
+    return text[start:text.index(b"\n};", start) + 3]
 
 
 def source_sha256(kernel: str) -> str:
     h = hashlib.sha256()
     for name in KERNEL_SOURCES[kernel]:
-        with open(os.path.join(CSRC, name), "rb") as f:
-            h.update(name.encode() + b"\0" + f.read())
+        h.update(name.encode() + b"\0" + _source_text(name))
     return h.hexdigest()
 
 
