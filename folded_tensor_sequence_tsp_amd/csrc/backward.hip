@@ -81,7 +81,18 @@ __global__ __launch_bounds__(256) void f32_to_bf16_kernel(const float* __restric
       u32x4{pack_bf16x2(a[0], a[1]), pack_bf16x2(a[2], a[3]), pack_bf16x2(b[0], b[1]), pack_bf16x2(b[2], b[3])};
 }
 
+__global__ __launch_bounds__(256) void fill_zero_kernel(float* __restrict__ p, int64_t count) {
+  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (i < count) p[i] = 0.0f;
+}
+
 }  // namespace
+
+hipError_t launch_zero_f32(float* p, int64_t count, hipStream_t stream) {
+  if (count <= 0) return hipSuccess;
+  hipLaunchKernelGGL(fill_zero_kernel, dim3((unsigned)((count + 255) / 256)), dim3(256), 0, stream, p, count);
+  return hipGetLastError();
+}
 
 hipError_t launch_f32_to_bf16(const float* src, int64_t R, int64_t C, int64_t ld_in, uint16_t* dst, int64_t ld_out,
                               hipStream_t stream) {

@@ -107,6 +107,9 @@ hipError_t launch_attention(const AttnArgs& args, hipStream_t stream);
 hipError_t launch_vt_tiles(const uint16_t* src, int64_t rows, int32_t ld, int32_t heads, int32_t head_dim,
                            uint16_t* dst, int64_t n_tiles, hipStream_t stream);
 
+// p[0 .. count) = 0 (a kernel, not a memset, so that the call can be captured).
+hipError_t launch_zero_f32(float* p, int64_t count, hipStream_t stream);
+
 // dst[r * ld_out + c] = bf16(src[r * ld_in + c]) for r < R, c < C (C % 8 == 0).
 hipError_t launch_f32_to_bf16(const float* src, int64_t R, int64_t C, int64_t ld_in, uint16_t* dst, int64_t ld_out,
                               hipStream_t stream);

@@ -903,9 +903,9 @@ tsp_status tsp_rms_norm_backward(int64_t n_tokens, int32_t hidden, const uint16_
   if (n_tokens < 0 || hidden <= 0) return TSP_ERR_SHAPE;
   if (hidden % 8 != 0 || hidden > 8192) return TSP_ERR_UNSUPPORTED;
   if (!(eps >= 0.0f) || !(eps < 1.0e30f)) return TSP_ERR_INVALID_ARG;
-  if ((s = check_ptr(x)) != TSP_OK || (s = check_ptr(gain)) != TSP_OK || (s = check_ptr(dy)) != TSP_OK ||
-      (s = check_ptr(dx)) != TSP_OK || (s = check_ptr(dgain)) != TSP_OK)
-    return s;
+  if ((s = check_ptr(gain)) != TSP_OK || (s = check_ptr(dgain)) != TSP_OK) return s;
+  if (n_tokens == 0) return from_hip(launch_zero_f32(dgain, hidden, stream));  // token buffers are not used
+  if ((s = check_ptr(x)) != TSP_OK || (s = check_ptr(dy)) != TSP_OK || (s = check_ptr(dx)) != TSP_OK) return s;
   if (dx == x || dx == dy) return TSP_ERR_INVALID_ARG;
   const size_t need = round_up((size_t)rms_norm_bwd_blocks(n_tokens) * hidden * 4);
   if (need > 0 && !workspace) return TSP_ERR_WORKSPACE;
@@ -1043,18 +1043,24 @@ tsp_status tsp_mlp_backward(int64_t n_tokens, const tsp_dims* dims, int32_t D, i
   if (n_tokens < 0) return TSP_ERR_SHAPE;
   if (n_tokens > INT32_MAX - 64) return TSP_ERR_UNSUPPORTED;
   if (start_shard < 0 || start_shard >= D) return TSP_ERR_INVALID_ARG;
-  if ((s = check_ptr(x)) != TSP_OK || (s = check_shards(w1, D)) != TSP_OK || (s = check_shards(w2, D)) != TSP_OK ||
-      (s = check_ptr(dy)) != TSP_OK || (s = check_ptr(dx)) != TSP_OK)
-    return s;
+  if ((s = check_shards(w1, D)) != TSP_OK || (s = check_shards(w2, D)) != TSP_OK) return s;
   if (!dw1 || !dw2) return TSP_ERR_INVALID_ARG;
   for (int d = 0; d < D; ++d)
     if ((s = check_ptr(dw1[d])) != TSP_OK || (s = check_ptr(dw2[d])) != TSP_OK) return s;
+  if (n_tokens == 0) {  // no tokens: the weight gradients are zero; token buffers are not used
+    const int64_t per = (int64_t)(dims->ffn / D) * dims->hidden;
+    for (int d = 0; d < D; ++d)
+      if ((s = from_hip(launch_zero_f32(dw1[d], per, stream))) != TSP_OK ||
+          (s = from_hip(launch_zero_f32(dw2[d], per, stream))) != TSP_OK)
+        return s;
+    return TSP_OK;
+  }
+  if ((s = check_ptr(x)) != TSP_OK || (s = check_ptr(dy)) != TSP_OK || (s = check_ptr(dx)) != TSP_OK) return s;
   if (dx == x || dx == dy) return TSP_ERR_INVALID_ARG;
   if (!workspace) return TSP_ERR_WORKSPACE;
   if (!aligned16(workspace)) return TSP_ERR_ALIGNMENT;
   const MlpBwdWs lay = mlp_bwd_ws(n_tokens, dims, D);
   if (ws_bytes < lay.total) return TSP_ERR_WORKSPACE;
-  if (n_tokens == 0) return TSP_OK;
   char* base = static_cast<char*>(workspace);
   uint16_t* xt = reinterpret_cast<uint16_t*>(base + lay.xt_off);
   uint16_t* dyt = reinterpret_cast<uint16_t*>(base + lay.dyt_off);
@@ -1129,18 +1135,23 @@ tsp_status tsp_attn_out_backward(int64_t n_tokens, const tsp_dims* dims, int32_t
   if (n_tokens < 0) return TSP_ERR_SHAPE;
   if (n_tokens > INT32_MAX - 64) return TSP_ERR_UNSUPPORTED;
   if (start_shard < 0 || start_shard >= D) return TSP_ERR_INVALID_ARG;
-  if ((s = check_ptr(attn)) != TSP_OK || (s = check_shards(wo, D)) != TSP_OK || (s = check_ptr(d_out)) != TSP_OK ||
-      (s = check_ptr(d_attn)) != TSP_OK)
-    return s;
+  if ((s = check_shards(wo, D)) != TSP_OK) return s;
   if (!dwo) return TSP_ERR_INVALID_ARG;
   for (int d = 0; d < D; ++d)
     if ((s = check_ptr(dwo[d])) != TSP_OK) return s;
+  if (n_tokens == 0) {  // no tokens: the weight gradients are zero; token buffers are not used
+    const int64_t per = (int64_t)(dims->n_heads / D) * dims->head_dim * dims->hidden;
+    for (int d = 0; d < D; ++d)
+      if ((s = from_hip(launch_zero_f32(dwo[d], per, stream))) != TSP_OK) return s;
+    return TSP_OK;
+  }
+  if ((s = check_ptr(attn)) != TSP_OK || (s = check_ptr(d_out)) != TSP_OK || (s = check_ptr(d_attn)) != TSP_OK)
+    return s;
   if (d_attn == attn || d_attn == d_out) return TSP_ERR_INVALID_ARG;
   if (!workspace) return TSP_ERR_WORKSPACE;
   if (!aligned16(workspace)) return TSP_ERR_ALIGNMENT;
   const OutBwdWs lay = out_bwd_ws(n_tokens, dims, D);
   if (ws_bytes < lay.total) return TSP_ERR_WORKSPACE;
-  if (n_tokens == 0) return TSP_OK;
   char* base = static_cast<char*>(workspace);
   uint16_t* wot = reinterpret_cast<uint16_t*>(base + lay.wot_off);
   uint16_t* dot = reinterpret_cast<uint16_t*>(base + lay.dot_off);
@@ -1182,19 +1193,24 @@ tsp_status tsp_attn_project_backward(int64_t n_tokens, const tsp_dims* dims, int
   if (n_tokens < 0) return TSP_ERR_SHAPE;
   if (n_tokens > INT32_MAX - 64) return TSP_ERR_UNSUPPORTED;
   if (start_shard < 0 || start_shard >= D) return TSP_ERR_INVALID_ARG;
-  if ((s = check_ptr(x)) != TSP_OK || (s = check_shards(wqkv, D)) != TSP_OK || (s = check_ptr(dq)) != TSP_OK ||
-      (s = check_ptr(dk)) != TSP_OK || (s = check_ptr(dv)) != TSP_OK || (s = check_ptr_nullable(dy)) != TSP_OK ||
-      (s = check_ptr(dx)) != TSP_OK)
-    return s;
+  if ((s = check_shards(wqkv, D)) != TSP_OK) return s;
   if (!dwqkv) return TSP_ERR_INVALID_ARG;
   for (int d = 0; d < D; ++d)
     if ((s = check_ptr(dwqkv[d])) != TSP_OK) return s;
+  if (n_tokens == 0) {  // no tokens: the weight gradients are zero; token buffers are not used
+    const int64_t per = (int64_t)3 * (dims->n_heads / D) * dims->head_dim * dims->hidden;
+    for (int d = 0; d < D; ++d)
+      if ((s = from_hip(launch_zero_f32(dwqkv[d], per, stream))) != TSP_OK) return s;
+    return TSP_OK;
+  }
+  if ((s = check_ptr(x)) != TSP_OK || (s = check_ptr(dq)) != TSP_OK || (s = check_ptr(dk)) != TSP_OK ||
+      (s = check_ptr(dv)) != TSP_OK || (s = check_ptr_nullable(dy)) != TSP_OK || (s = check_ptr(dx)) != TSP_OK)
+    return s;
   if (dx == x) return TSP_ERR_INVALID_ARG;
   if (!workspace) return TSP_ERR_WORKSPACE;
   if (!aligned16(workspace)) return TSP_ERR_ALIGNMENT;
   const ProjBwdWs lay = proj_bwd_ws(n_tokens, dims, D);
   if (ws_bytes < lay.total) return TSP_ERR_WORKSPACE;
-  if (n_tokens == 0) return TSP_OK;
   char* base = static_cast<char*>(workspace);
   uint16_t* G = reinterpret_cast<uint16_t*>(base + lay.g_off);
   uint16_t* xt = reinterpret_cast<uint16_t*>(base + lay.xt_off);

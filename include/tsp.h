@@ -221,6 +221,8 @@ tsp_status tsp_attn_core_backward(const tsp_plan* plan, const tsp_dims* dims, co
  *   d_attn   : device, bf16 [n_tokens x hidden], out; aliases neither attn nor d_out.
  *   dwo      : host array of D device pointers, fp32 [hidden x H_s*hd], out.
  *   workspace: >= tsp_workspace_size(n_tokens, dims, D, TSP_WS_OUT_BWD) bytes.
+ * n_tokens = 0 writes zero weight gradients and nothing else; the token
+ * buffers and the workspace may then be null.
  * Errors: as tsp_attn_out, plus TSP_ERR_WORKSPACE.
  */
 tsp_status tsp_attn_out_backward(int64_t n_tokens, const tsp_dims* dims, int32_t D, int32_t start_shard,
@@ -246,6 +248,8 @@ tsp_status tsp_attn_out_backward(int64_t n_tokens, const tsp_dims* dims, int32_t
  *   dx       : device, bf16 [n_tokens x hidden], out; must not alias x.
  *   dwqkv    : host array of D device pointers, fp32 [3*H_s*hd x hidden], out.
  *   workspace: >= tsp_workspace_size(n_tokens, dims, D, TSP_WS_PROJ_BWD) bytes.
+ * n_tokens = 0 writes zero weight gradients and nothing else; the token
+ * buffers and the workspace may then be null.
  * Errors: as tsp_attn_project, plus TSP_ERR_WORKSPACE.
  */
 tsp_status tsp_attn_project_backward(int64_t n_tokens, const tsp_dims* dims, int32_t D, int32_t start_shard,
@@ -466,7 +470,8 @@ tsp_status tsp_rope_backward(const tsp_plan* plan, int32_t n_heads, int32_t n_kv
  *   dx     : device, bf16 [n x hidden], out; aliases neither x nor dy.
  *   dgain  : device, fp32 [hidden], out.
  *   workspace: >= tsp_workspace_size(n_tokens, dims with this hidden, 1, TSP_WS_RMS_BWD)
- *              bytes (fp32 partial sums per 64-row block).
+ *              bytes (fp32 partial sums per 32-row block).
+ * n_tokens = 0 writes dgain = 0 and nothing else; x, dy, dx may then be null.
  */
 tsp_status tsp_rms_norm_backward(int64_t n_tokens, int32_t hidden, const uint16_t* x, const uint16_t* gain, float eps,
                                  const uint16_t* dy, uint16_t* dx, float* dgain, void* workspace, size_t ws_bytes,
@@ -529,6 +534,8 @@ tsp_status tsp_attn_core_gqa_backward(const tsp_plan* plan, const tsp_dims* dims
  *   dw1, dw2 : host arrays of D device pointers, fp32 [ffn/D x hidden] and
  *              [hidden x ffn/D], overwritten.
  *   workspace: >= tsp_workspace_size(n_tokens, dims, D, TSP_WS_MLP_BWD) bytes.
+ * n_tokens = 0 writes zero weight gradients and nothing else; the token
+ * buffers and the workspace may then be null.
  * Errors: as tsp_mlp_forward.
  */
 tsp_status tsp_mlp_backward(int64_t n_tokens, const tsp_dims* dims, int32_t D, int32_t start_shard,
