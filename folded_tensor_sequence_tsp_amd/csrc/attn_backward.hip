@@ -223,7 +223,9 @@ __global__ __launch_bounds__(64 * BW) void dkv_kernel(const AttnBwdArgs a) {
     int c, t, qh;
     tile_of(i, c, t, qh);
     const int64_t qp0 = (c ? a.chunk_start1 : a.chunk_start0) + (int64_t)t * 64;  // position of query 0
-    if (kw0 > qp0 + 63) return;  // every key of the wave is past every query of the tile (wave-uniform)
+    // (tiles whose queries all precede the wave's keys are computed too, the
+    // mask zeroes them: a wave-uniform skip here splits the accumulators' live
+    // ranges and costs register copies on every tile)
     // queries of the tile before this lane's key are masked: offsets below qmin
     const int qmin = kw0 + 31 > qp0 ? (int)min(max(key - qp0, (int64_t)0), (int64_t)64) : 0;
     const uint8_t* stage = smem + (i & 1) * STAGE;
