@@ -56,6 +56,18 @@ __device__ __forceinline__ void store_row8(const GemmArgs& g, int nshard, int ro
   u32x4 packed;
   if constexpr (EPI == EPI_RESID) {  // N-sharded: shard nshard writes column block nshard of the output
     const int64_t idx = (int64_t)row * g.ldo + (int64_t)nshard * g.N_s + col;
+    void* outp = g.out;  // separate output buffers per shard or per row block
+    int64_t oidx = idx;
+    if (g.outs[0]) {
+      if (g.rows_per_out > 0) {
+        const int k = row / g.rows_per_out;
+        outp = g.outs[k];
+        oidx = (int64_t)(row - k * g.rows_per_out) * g.ldo + col;
+      } else {
+        outp = g.outs[nshard];
+        oidx = (int64_t)row * g.ldo + col;
+      }
+    }
     if (g.row_exp) {
       const int e = g.row_exp[row];
 #pragma unroll
@@ -81,13 +93,13 @@ __device__ __forceinline__ void store_row8(const GemmArgs& g, int nshard, int ro
       }
     }
     if (g.out_f32) {
-      float* op = static_cast<float*>(g.out) + idx;
+      float* op = static_cast<float*>(outp) + oidx;
       *reinterpret_cast<f32x4*>(op) = f32x4{v[0], v[1], v[2], v[3]};
       *reinterpret_cast<f32x4*>(op + 4) = f32x4{v[4], v[5], v[6], v[7]};
     } else {
 #pragma unroll
       for (int j = 0; j < 4; ++j) packed[j] = pack_bf16x2(v[2 * j], v[2 * j + 1]);
-      *reinterpret_cast<u32x4*>(static_cast<uint16_t*>(g.out) + idx) = packed;
+      *reinterpret_cast<u32x4*>(static_cast<uint16_t*>(outp) + oidx) = packed;
     }
   } else if constexpr (EPI == EPI_DGELU) {
     const float* up = g.aux + (int64_t)row * g.N_s + col;

@@ -42,6 +42,12 @@ struct GemmArgs {
   // EPI_GELU / EPI_RESID
   void* out;
   int64_t ldo;
+  // EPI_RESID into separate buffers (out unused): when outs[0] is set, an
+  // N-sharded launch writes shard s's columns to outs[s] (columns from 0), and
+  // a launch with rows_per_out > 0 writes rows [k*rows_per_out, (k+1)*rows_per_out)
+  // to outs[k] (rows from 0); row stride ldo in both.
+  void* outs[TSP_MAX_D];
+  int32_t rows_per_out;
   const float* aux;       // EPI_DGELU: the GELU inputs, fp32, row stride N_s
   const void* residual;  // EPI_RESID, nullable
   int32_t res_f32;       // residual is fp32 (else bf16)

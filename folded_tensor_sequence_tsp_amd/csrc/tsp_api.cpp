@@ -306,8 +306,9 @@ tsp_status check_gqa(const tsp_dims* dims, int32_t D, int32_t n_kv_heads, bool s
 // ---- MLP backward --------------------------------------------------------------
 
 // Workspace of tsp_mlp_backward (n_pad = n rounded up to 64): x^T and dy^T
-// [h x n_pad], U_d fp32 [n x F_s], GELU(U_d)^T and dU_d^T [F_s x n_pad], dU of
-// all shards [n x F], W1_d^T of all shards [D][h x F_s], W2_d^T [F_s x h].
+// [h x n_pad], U_d fp32 [n x F_s], GELU(U)^T and dU^T of all shards
+// [F x n_pad], dU of all shards [n x F], W1_d^T of all shards [D][h x F_s],
+// W2_d^T [F_s x h].
 struct MlpBwdWs {
   size_t xt_off, dyt_off, u_off, ht_off, dut_off, du_off, w1t_off, w2t_off, total;
 };
@@ -321,8 +322,8 @@ MlpBwdWs mlp_bwd_ws(int64_t n, const tsp_dims* d, int32_t D) {
   w.dyt_off = w.xt_off + round_up((size_t)h * np * 2);
   w.u_off = w.dyt_off + round_up((size_t)h * np * 2);
   w.ht_off = w.u_off + round_up((size_t)n * fs * 4);
-  w.dut_off = w.ht_off + round_up((size_t)fs * np * 2);
-  w.du_off = w.dut_off + round_up((size_t)fs * np * 2);
+  w.dut_off = w.ht_off + round_up((size_t)F * np * 2);
+  w.du_off = w.dut_off + round_up((size_t)F * np * 2);
   w.w1t_off = w.du_off + round_up((size_t)n * F * 2);
   w.w2t_off = w.w1t_off + round_up((size_t)h * F * 2);
   w.total = w.w2t_off + round_up((size_t)fs * h * 2);
@@ -330,7 +331,7 @@ MlpBwdWs mlp_bwd_ws(int64_t n, const tsp_dims* d, int32_t D) {
 }
 
 // Workspace of tsp_attn_out_backward: W_o_d^T of all shards [D][H_s*hd x h],
-// d_out^T [h x n_pad], one shard's attn^T [H_s*hd x n_pad].
+// d_out^T [h x n_pad], attn^T [h x n_pad].
 struct OutBwdWs {
   size_t wot_off, dot_off, at_off, total;
 };
@@ -340,12 +341,12 @@ OutBwdWs out_bwd_ws(int64_t n, const tsp_dims* d, int32_t D) {
   w.wot_off = 0;
   w.dot_off = w.wot_off + round_up((size_t)h * h * 2);
   w.at_off = w.dot_off + round_up((size_t)h * np * 2);
-  w.total = w.at_off + round_up((size_t)hs * np * 2);
+  w.total = w.at_off + round_up((size_t)h * np * 2);
   return w;
 }
 
 // Workspace of tsp_attn_project_backward: G = bf16[dq | dk | dv] [n x 3h], x^T
-// [h x n_pad], one shard's [dq_d | dk_d | dv_d]^T [3 H_s*hd x n_pad], the
+// [h x n_pad], [dq_d | dk_d | dv_d]^T of all shards [D][3 H_s*hd x n_pad], the
 // transposed Q, K and V weight blocks of all shards [3][D][h x H_s*hd], and the
 // fp32 accumulator of dx [n x h].
 struct ProjBwdWs {
@@ -357,29 +358,10 @@ ProjBwdWs proj_bwd_ws(int64_t n, const tsp_dims* d, int32_t D) {
   w.g_off = 0;
   w.xt_off = w.g_off + round_up((size_t)n * 3 * h * 2);
   w.gt_off = w.xt_off + round_up((size_t)h * np * 2);
-  w.wt_off = w.gt_off + round_up((size_t)3 * hs * np * 2);
+  w.wt_off = w.gt_off + round_up((size_t)3 * h * np * 2);
   w.acc_off = w.wt_off + round_up((size_t)3 * h * h * 2);
   w.total = w.acc_off + round_up((size_t)n * h * 4);
   return w;
-}
-
-// One-shard GEMM C = A B^T (B [N x K], K-contiguous) with the plain epilogue.
-hipError_t plain_gemm(const uint16_t* A, int64_t lda, const uint16_t* B, int32_t M, int32_t N, int32_t K, void* out,
-                      int64_t ldo, int32_t out_f32, hipStream_t stream) {
-  GemmArgs g{};
-  g.A = A;
-  g.lda = lda;
-  g.B[0] = B;
-  g.M = M;
-  g.N_s = N;
-  g.K_s = K;
-  g.n_shards = 1;
-  g.k_shards = 1;
-  g.epilogue = EPI_RESID;
-  g.out = out;
-  g.ldo = ldo;
-  g.out_f32 = out_f32;
-  return launch_gemm(g, stream);
 }
 
 // ---- shard streaming ---------------------------------------------------------
@@ -1095,18 +1077,55 @@ tsp_status tsp_mlp_backward(int64_t n_tokens, const tsp_dims* dims, int32_t D, i
   for (int k = 0; k < D; ++k) {
     const int d = (start_shard + k) % D;
     // U = x W1_d^T (fp32); GELU(U)^T; W2_d^T
+    uint16_t* ht_d = ht + (int64_t)d * fs * np;
+    uint16_t* dut_d = dut + (int64_t)d * fs * np;
     if ((s = gemm(x, h, w1[d], (int32_t)n, fs, (int32_t)h, EPI_RESID, u, fs, 1)) != TSP_OK) return s;
-    if ((s = from_hip(launch_transpose(u, 1, 1, n, fs, fs, ht, np, stream))) != TSP_OK) return s;
+    if ((s = from_hip(launch_transpose(u, 1, 1, n, fs, fs, ht_d, np, stream))) != TSP_OK) return s;
     if ((s = from_hip(launch_transpose(w2[d], 0, 0, h, fs, fs, w2t, h, stream))) != TSP_OK) return s;
     // dU_d = (dy W2_d) * GELU'(U) -> block d of dU; its transpose
     if ((s = gemm(dy, h, w2t, (int32_t)n, fs, (int32_t)h, EPI_DGELU, du + (int64_t)d * fs, F, 0)) != TSP_OK) return s;
-    if ((s = from_hip(launch_transpose(du + (int64_t)d * fs, 0, 0, n, fs, F, dut, np, stream))) != TSP_OK) return s;
-    // dW2_d = dy^T GELU(U); dW1_d = dU_d^T x  (contractions over the tokens)
-    if ((s = gemm(dyt, np, ht, (int32_t)h, fs, (int32_t)np, EPI_RESID, dw2[d], fs, 1)) != TSP_OK) return s;
-    if ((s = gemm(dut, np, xt, fs, (int32_t)h, (int32_t)np, EPI_RESID, dw1[d], h, 1)) != TSP_OK) return s;
+    if ((s = from_hip(launch_transpose(du + (int64_t)d * fs, 0, 0, n, fs, F, dut_d, np, stream))) != TSP_OK) return s;
     // W1_d^T for dx
     if ((s = from_hip(launch_transpose(w1[d], 0, 0, fs, h, h, w1t + (int64_t)d * h * fs, fs, stream))) != TSP_OK)
       return s;
+  }
+  // weight gradients of all shards in two launches (contractions over the tokens):
+  // dW2_d = dy^T GELU(U_d) (N-sharded over the GELU(U)^T blocks) and
+  // dW1_d = dU_d^T x (rows of dU^T in blocks of F_s), each into its own buffer
+  {
+    GemmArgs g{};
+    g.A = dyt;
+    g.lda = np;
+    for (int d = 0; d < D; ++d) {
+      g.B[d] = ht + (int64_t)d * fs * np;
+      g.outs[d] = dw2[d];
+    }
+    g.M = (int32_t)h;
+    g.N_s = fs;
+    g.K_s = (int32_t)np;
+    g.n_shards = D;
+    g.k_shards = 1;
+    g.epilogue = EPI_RESID;
+    g.ldo = fs;
+    g.out_f32 = 1;
+    if ((s = from_hip(launch_gemm(g, stream))) != TSP_OK) return s;
+  }
+  {
+    GemmArgs g{};
+    g.A = dut;
+    g.lda = np;
+    g.B[0] = xt;
+    for (int d = 0; d < D; ++d) g.outs[d] = dw1[d];
+    g.rows_per_out = fs;
+    g.M = (int32_t)F;
+    g.N_s = (int32_t)h;
+    g.K_s = (int32_t)np;
+    g.n_shards = 1;
+    g.k_shards = 1;
+    g.epilogue = EPI_RESID;
+    g.ldo = h;
+    g.out_f32 = 1;
+    if ((s = from_hip(launch_gemm(g, stream))) != TSP_OK) return s;
   }
   // dx = [dy +] sum_k dU[:, d_k block] W1_{d_k}: the ring's split-K, fp32 in registers
   GemmArgs g{};
@@ -1159,14 +1178,31 @@ tsp_status tsp_attn_out_backward(int64_t n_tokens, const tsp_dims* dims, int32_t
   const int64_t n = n_tokens, np = pad64(n), h = dims->hidden;
   const int32_t hs = (dims->n_heads / D) * dims->head_dim;
   if ((s = from_hip(launch_transpose(d_out, 0, 0, n, h, h, dot, np, stream))) != TSP_OK) return s;
+  if ((s = from_hip(launch_transpose(attn, 0, 0, n, h, h, at, np, stream))) != TSP_OK) return s;
   for (int k = 0; k < D; ++k) {
     const int d = (start_shard + k) % D;
-    // W_o_d^T, then dW_o_d = d_out^T attn[:, block d] (contraction over the tokens)
     if ((s = from_hip(launch_transpose(wo[d], 0, 0, h, hs, hs, wot + (int64_t)d * hs * h, h, stream))) != TSP_OK)
       return s;
-    if ((s = from_hip(launch_transpose(attn + (int64_t)d * hs, 0, 0, n, hs, h, at, np, stream))) != TSP_OK) return s;
-    if ((s = from_hip(plain_gemm(dot, np, at, (int32_t)h, hs, (int32_t)np, dwo[d], hs, 1, stream))) != TSP_OK)
-      return s;
+  }
+  // dW_o_d = d_out^T attn[:, block d] for every shard in one N-sharded launch
+  // (contraction over the tokens), each into its own buffer
+  {
+    GemmArgs g{};
+    g.A = dot;
+    g.lda = np;
+    for (int d = 0; d < D; ++d) {
+      g.B[d] = at + (int64_t)d * hs * np;
+      g.outs[d] = dwo[d];
+    }
+    g.M = (int32_t)h;
+    g.N_s = hs;
+    g.K_s = (int32_t)np;
+    g.n_shards = D;
+    g.k_shards = 1;
+    g.epilogue = EPI_RESID;
+    g.ldo = hs;
+    g.out_f32 = 1;
+    if ((s = from_hip(launch_gemm(g, stream))) != TSP_OK) return s;
   }
   // d_attn[:, block d] = d_out W_o_d: one N-sharded launch over the transposed shards
   GemmArgs g{};
@@ -1225,18 +1261,35 @@ tsp_status tsp_attn_project_backward(int64_t n_tokens, const tsp_dims* dims, int
   if ((s = from_hip(launch_transpose(x, 0, 0, n, h, h, xt, np, stream))) != TSP_OK) return s;
   for (int k = 0; k < D; ++k) {
     const int d = (start_shard + k) % D;
-    // [dq_d | dk_d | dv_d]^T, then dW_qkv_d = that . x (contraction over the tokens)
+    // [dq_d | dk_d | dv_d]^T into block d of G^T
     for (int p = 0; p < 3; ++p)
-      if ((s = from_hip(launch_transpose(parts[p] + (int64_t)d * hs, 1, 0, n, hs, h, gt + (int64_t)p * hs * np, np,
-                                         stream))) != TSP_OK)
+      if ((s = from_hip(launch_transpose(parts[p] + (int64_t)d * hs, 1, 0, n, hs, h,
+                                         gt + ((int64_t)d * 3 + p) * hs * np, np, stream))) != TSP_OK)
         return s;
-    if ((s = from_hip(plain_gemm(gt, np, xt, 3 * hs, (int32_t)h, (int32_t)np, dwqkv[d], h, 1, stream))) != TSP_OK)
-      return s;
     // the shard's Q, K and V weight blocks transposed, [h x H_s*hd] each
     for (int p = 0; p < 3; ++p)
       if ((s = from_hip(launch_transpose(wqkv[d] + (int64_t)p * hs * h, 0, 0, hs, h, h,
                                          wt + ((int64_t)p * D + d) * h * hs, hs, stream))) != TSP_OK)
         return s;
+  }
+  // dW_qkv_d = G^T block d . x for every shard in one launch (rows of G^T in
+  // blocks of 3 H_s*hd; contraction over the tokens), each into its own buffer
+  {
+    GemmArgs g{};
+    g.A = gt;
+    g.lda = np;
+    g.B[0] = xt;
+    for (int d = 0; d < D; ++d) g.outs[d] = dwqkv[d];
+    g.rows_per_out = 3 * hs;
+    g.M = 3 * (int32_t)h;
+    g.N_s = (int32_t)h;
+    g.K_s = (int32_t)np;
+    g.n_shards = 1;
+    g.k_shards = 1;
+    g.epilogue = EPI_RESID;
+    g.ldo = h;
+    g.out_f32 = 1;
+    if ((s = from_hip(launch_gemm(g, stream))) != TSP_OK) return s;
   }
   // dx = [dy +] sum_p sum_k G_p[:, block d_k] W_{p, d_k}: three ring split-Ks
   // through one fp32 accumulator

@@ -321,9 +321,9 @@ def test_mlp_backward_rejects(L):
     n = 300
     np_ = 320  # tokens rounded up to 64
     need = tsp.workspace_size(n, d, 4, tsp.WS_MLP_BWD)
-    # x^T, dy^T, U (fp32), GELU(U)^T, dU^T, dU (all shards), W1^T (all shards), W2^T
-    assert need == (2 * 256 * np_ * 2 + n * 256 * 4 + 2 * 256 * np_ * 2 + n * 1024 * 2 + 256 * 1024 * 2
-                    + 256 * 256 * 2 + 256 * 32 * 0)
+    # x^T, dy^T, U (fp32), GELU(U)^T and dU^T (all shards), dU (all shards), W1^T (all shards), W2^T
+    assert need == (2 * 256 * np_ * 2 + n * 256 * 4 + 2 * 1024 * np_ * 2 + n * 1024 * 2 + 256 * 1024 * 2
+                    + 256 * 256 * 2)
     w = _arr([A] * 4)
     g = _arr([A + 512] * 4)
     call = lambda **k: L.tsp_mlp_backward(k.get("n", n), ctypes.byref(k.get("dims", d)), 4, k.get("start", 0), 1,
@@ -375,7 +375,7 @@ def test_projection_backward_rejects(L):
     w = _arr([A] * 4)
     g = _arr([A + 512] * 4)
     need_o = tsp.workspace_size(n, d, 4, tsp.WS_OUT_BWD)
-    assert need_o == h * h * 2 + h * np_ * 2 + hs * np_ * 2       # W_o^T (all shards), d_out^T, one shard's attn^T
+    assert need_o == h * h * 2 + h * np_ * 2 + h * np_ * 2        # W_o^T (all shards), d_out^T, attn^T
     out = lambda **k: L.tsp_attn_out_backward(k.get("n", n), ctypes.byref(d), 4, k.get("start", 0), A, w,
                                               A + 64, k.get("d_attn", A + 128), k.get("dwo", g),
                                               k.get("ws", A + 256), k.get("nb", need_o), None)
@@ -385,8 +385,8 @@ def test_projection_backward_rejects(L):
     assert out(nb=need_o - 1) == tsp.TSP_ERR_WORKSPACE
     assert out(n=-1) == tsp.TSP_ERR_SHAPE
     need_p = tsp.workspace_size(n, d, 4, tsp.WS_PROJ_BWD)
-    # bf16 [dq | dk | dv], x^T, one shard's gradients transposed, W_qkv^T blocks, fp32 dx accumulator
-    assert need_p == n * 3 * h * 2 + h * np_ * 2 + 3 * hs * np_ * 2 + 3 * h * h * 2 + n * h * 4
+    # bf16 [dq | dk | dv], x^T, every shard's gradients transposed, W_qkv^T blocks, fp32 dx accumulator
+    assert need_p == n * 3 * h * 2 + h * np_ * 2 + 3 * h * np_ * 2 + 3 * h * h * 2 + n * h * 4
     prj = lambda **k: L.tsp_attn_project_backward(n, ctypes.byref(d), 4, k.get("start", 1), A, w, A + 64, A + 128,
                                                   A + 192, k.get("dy", None), k.get("dx", A + 320),
                                                   k.get("dw", g), k.get("ws", A + 1024), k.get("nb", need_p), None)
