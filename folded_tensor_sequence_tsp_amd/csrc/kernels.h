@@ -35,7 +35,7 @@ struct GemmArgs {
   // with A and once with A_lo, into the same accumulator.
   const uint16_t* A_lo;
   int64_t lda;
-  const uint16_t* B[TSP_MAX_D];
+  const uint16_t* B[3 * TSP_MAX_D];  // up to 3*D K-shards: a split-K over the Q, K and V parts of D shards
   int32_t M, N_s, K_s;
   int32_t n_shards, k_shards, ring_start;
   int32_t epilogue;

@@ -346,11 +346,10 @@ OutBwdWs out_bwd_ws(int64_t n, const tsp_dims* d, int32_t D) {
 }
 
 // Workspace of tsp_attn_project_backward: G = bf16[dq | dk | dv] [n x 3h], x^T
-// [h x n_pad], [dq_d | dk_d | dv_d]^T of all shards [D][3 H_s*hd x n_pad], the
-// transposed Q, K and V weight blocks of all shards [3][D][h x H_s*hd], and the
-// fp32 accumulator of dx [n x h].
+// [h x n_pad], [dq_d | dk_d | dv_d]^T of all shards [D][3 H_s*hd x n_pad], and
+// the transposed Q, K and V weight blocks of all shards [3][D][h x H_s*hd].
 struct ProjBwdWs {
-  size_t g_off, xt_off, gt_off, wt_off, acc_off, total;
+  size_t g_off, xt_off, gt_off, wt_off, total;
 };
 ProjBwdWs proj_bwd_ws(int64_t n, const tsp_dims* d, int32_t D) {
   const int64_t np = pad64(n), h = d->hidden, hs = (int64_t)(d->n_heads / D) * d->head_dim;
@@ -359,8 +358,7 @@ ProjBwdWs proj_bwd_ws(int64_t n, const tsp_dims* d, int32_t D) {
   w.xt_off = w.g_off + round_up((size_t)n * 3 * h * 2);
   w.gt_off = w.xt_off + round_up((size_t)h * np * 2);
   w.wt_off = w.gt_off + round_up((size_t)3 * h * np * 2);
-  w.acc_off = w.wt_off + round_up((size_t)3 * h * h * 2);
-  w.total = w.acc_off + round_up((size_t)n * h * 4);
+  w.total = w.wt_off + round_up((size_t)3 * h * h * 2);
   return w;
 }
 
@@ -1252,7 +1250,6 @@ tsp_status tsp_attn_project_backward(int64_t n_tokens, const tsp_dims* dims, int
   uint16_t* xt = reinterpret_cast<uint16_t*>(base + lay.xt_off);
   uint16_t* gt = reinterpret_cast<uint16_t*>(base + lay.gt_off);
   uint16_t* wt = reinterpret_cast<uint16_t*>(base + lay.wt_off);
-  float* acc = reinterpret_cast<float*>(base + lay.acc_off);
   const int64_t n = n_tokens, np = pad64(n), h = dims->hidden;
   const int32_t hs = (dims->n_heads / D) * dims->head_dim;
   const float* parts[3] = {dq, dk, dv};
@@ -1291,36 +1288,25 @@ tsp_status tsp_attn_project_backward(int64_t n_tokens, const tsp_dims* dims, int
     g.out_f32 = 1;
     if ((s = from_hip(launch_gemm(g, stream))) != TSP_OK) return s;
   }
-  // dx = [dy +] sum_p sum_k G_p[:, block d_k] W_{p, d_k}: three ring split-Ks
-  // through one fp32 accumulator
-  for (int p = 0; p < 3; ++p) {
-    GemmArgs g{};
-    g.A = G + p * h;
-    g.lda = 3 * h;
-    for (int d = 0; d < D; ++d) g.B[d] = wt + ((int64_t)p * D + d) * h * hs;
-    g.M = (int32_t)n;
-    g.N_s = (int32_t)h;
-    g.K_s = hs;
-    g.n_shards = 1;
-    g.k_shards = D;
-    g.ring_start = start_shard;
-    g.epilogue = EPI_RESID;
-    g.ldo = h;
-    if (p == 0) {
-      g.residual = dy;
-    } else {
-      g.residual = acc;
-      g.res_f32 = 1;
-    }
-    if (p < 2) {
-      g.out = acc;
-      g.out_f32 = 1;
-    } else {
-      g.out = dx;
-    }
-    if ((s = from_hip(launch_gemm(g, stream))) != TSP_OK) return s;
-  }
-  return TSP_OK;
+  // dx = [dy +] sum_p sum_d G_p[:, block d] W_{p, d}: one split-K over the 3D
+  // blocks (K-shard j = p*D + d sits at columns j*H_s*hd of G, its weight
+  // block at slot j of the transposed weights), one fp32 accumulator in
+  // registers, blocks visited from j = start_shard round to start_shard - 1
+  GemmArgs g{};
+  g.A = G;
+  g.lda = 3 * h;
+  for (int j = 0; j < 3 * D; ++j) g.B[j] = wt + (int64_t)j * h * hs;
+  g.M = (int32_t)n;
+  g.N_s = (int32_t)h;
+  g.K_s = hs;
+  g.n_shards = 1;
+  g.k_shards = 3 * D;
+  g.ring_start = start_shard;
+  g.epilogue = EPI_RESID;
+  g.ldo = h;
+  g.residual = dy;
+  g.out = dx;
+  return from_hip(launch_gemm(g, stream));
 }
 
 const char* tsp_status_string(tsp_status status) {

@@ -239,8 +239,8 @@ tsp_status tsp_attn_out_backward(int64_t n_tokens, const tsp_dims* dims, int32_t
  * own K/V rows' gradients, i.e. its rows of every rank's dk_full / dv_full
  * contributions summed (the reduce-scatter of tsp_attn_core_backward's output;
  * on one rank, its own rows).  dy is the gradient that reaches x through the
- * layer's residual (nullable).  dx is accumulated in fp32 over the shards in
- * ring order from start_shard.
+ * layer's residual (nullable).  dx is accumulated in one fp32 accumulator over
+ * the 3D (part, shard) blocks, from block start_shard onwards.
  *   x        : device, bf16 [n_tokens x hidden], the forward's input.
  *   wqkv     : as tsp_attn_project.
  *   dq, dk, dv : device, fp32 [n_tokens x hidden] (rounded to bf16 for the products).

@@ -385,8 +385,8 @@ def test_projection_backward_rejects(L):
     assert out(nb=need_o - 1) == tsp.TSP_ERR_WORKSPACE
     assert out(n=-1) == tsp.TSP_ERR_SHAPE
     need_p = tsp.workspace_size(n, d, 4, tsp.WS_PROJ_BWD)
-    # bf16 [dq | dk | dv], x^T, every shard's gradients transposed, W_qkv^T blocks, fp32 dx accumulator
-    assert need_p == n * 3 * h * 2 + h * np_ * 2 + 3 * h * np_ * 2 + 3 * h * h * 2 + n * h * 4
+    # bf16 [dq | dk | dv], x^T, every shard's gradients transposed, W_qkv^T blocks
+    assert need_p == n * 3 * h * 2 + h * np_ * 2 + 3 * h * np_ * 2 + 3 * h * h * 2
     prj = lambda **k: L.tsp_attn_project_backward(n, ctypes.byref(d), 4, k.get("start", 1), A, w, A + 64, A + 128,
                                                   A + 192, k.get("dy", None), k.get("dx", A + 320),
                                                   k.get("dw", g), k.get("ws", A + 1024), k.get("nb", need_p), None)
