@@ -1309,6 +1309,49 @@ tsp_status tsp_attn_project_backward(int64_t n_tokens, const tsp_dims* dims, int
   return from_hip(launch_gemm(g, stream));
 }
 
+tsp_status tsp_memory_footprint(int64_t seq_len, const tsp_dims* dims, int32_t D, int32_t n_layers,
+                                int32_t scheme, int32_t training, tsp_memory* out) {
+  if (!out || !dims || n_layers < 0) return TSP_ERR_INVALID_ARG;
+  if (scheme != TSP_MEM_TSP && scheme != TSP_MEM_TP) return TSP_ERR_INVALID_ARG;
+  tsp_status s = check_dims(dims, D, true, true);
+  if (s != TSP_OK) return s;
+  tsp_plan plan;
+  if ((s = tsp_zigzag_plan(seq_len, D, 0, &plan, nullptr, nullptr)) != TSP_OK) return s;
+
+  const uint64_t h = (uint64_t)dims->hidden, F = (uint64_t)dims->ffn, S = (uint64_t)seq_len;
+  const uint64_t layer_params = 4 * h * h + 2 * h * F;  // W_q, W_k, W_v, W_o; W1, W2
+  const uint64_t own_params = (uint64_t)n_layers * layer_params / (uint64_t)D;
+  const bool tsp = scheme == TSP_MEM_TSP;
+  const uint64_t tokens = tsp ? (uint64_t)plan.n_local : S;
+
+  tsp_memory m{};
+  m.weights = own_params * 2;
+  m.streamed = tsp && n_layers > 0 ? (uint64_t)(D - 1) * (layer_params / (uint64_t)D) * 2 : 0;
+  if (tsp) {
+    m.kv = 2 * S * h * 2;
+    m.activations = 2 * round_up(tokens * h * 2) + ws_layer((int64_t)tokens, dims, D);
+  } else {
+    // The buffers of tsp_layer_forward (input and output rows, Q, attention
+    // output hi and lo, V^T tiles, fp32 h1, its scaled fp16 copy, row
+    // exponents, fp16 W1 and W2 copies, one GELU token block) for all S
+    // tokens, with the rank's H/D heads and F/D FFN columns.
+    const uint64_t wa = h / (uint64_t)D, wf = F / (uint64_t)D;
+    const uint64_t mb = tokens < (uint64_t)MLP_TOKEN_BLOCK ? tokens : (uint64_t)MLP_TOKEN_BLOCK;
+    m.kv = 2 * S * wa * 2;
+    m.activations = 2 * round_up(tokens * h * 2) + 3 * round_up(tokens * wa * 2) +
+                    round_up((uint64_t)attn_kv_tiles((int64_t)S) * 64 * wa * 2) + round_up(tokens * h * 4) +
+                    round_up(tokens * h * 2) + round_up(tokens * 4) + 2 * round_up(wf * h * 2) + round_up(mb * wf * 2);
+  }
+  if (training) {
+    m.train_state = own_params * 14 + (uint64_t)n_layers * tokens * h * 2;
+    m.grads = n_layers > 0 ? (tsp ? layer_params : layer_params / (uint64_t)D) * 4 : 0;
+  }
+  if (n_layers == 0) m.kv = m.activations = 0;
+  m.total = m.weights + m.streamed + m.kv + m.activations + m.train_state + m.grads;
+  *out = m;
+  return TSP_OK;
+}
+
 const char* tsp_status_string(tsp_status status) {
   switch (status) {
     case TSP_OK: return "TSP_OK";

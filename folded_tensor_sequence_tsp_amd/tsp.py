@@ -27,7 +27,8 @@ EXPORTS = ["tsp_zigzag_plan", "tsp_workspace_size", "tsp_attn_project", "tsp_att
            "tsp_attn_out_shard", "tsp_mlp_shard", "tsp_rms_norm", "tsp_rope", "tsp_attn_project_gqa",
            "tsp_attn_core_gqa", "tsp_mlp_backward", "tsp_attn_core_lse", "tsp_attn_core_backward",
            "tsp_attn_out_backward", "tsp_attn_project_backward", "tsp_rope_backward", "tsp_rms_norm_backward",
-           "tsp_attn_core_gqa_lse", "tsp_attn_core_gqa_backward", "tsp_status_string"]
+           "tsp_attn_core_gqa_lse", "tsp_attn_core_gqa_backward", "tsp_memory_footprint", "tsp_status_string"]
+MEM_TSP, MEM_TP = range(2)
 
 
 class TSPError(RuntimeError):
@@ -43,6 +44,11 @@ class Plan(ctypes.Structure):
 
 class Dims(ctypes.Structure):
     _fields_ = [("hidden", c_int32), ("n_heads", c_int32), ("head_dim", c_int32), ("ffn", c_int32)]
+
+
+class Memory(ctypes.Structure):
+    _fields_ = [(f, ctypes.c_uint64) for f in
+                ("weights", "streamed", "kv", "activations", "train_state", "grads", "total")]
 
 
 _lib = None
@@ -85,6 +91,7 @@ def lib() -> ctypes.CDLL:
             "tsp_attn_core_gqa_lse": [POINTER(Plan), POINTER(Dims), c_int32, P, P, P, P, P, P, P, c_size_t, P],
             "tsp_attn_core_gqa_backward": [POINTER(Plan), POINTER(Dims), c_int32, P, P, P, P, P, P, P, P, P, P, P,
                                            c_size_t, P],
+            "tsp_memory_footprint": [c_int64, POINTER(Dims), c_int32, c_int32, c_int32, c_int32, POINTER(Memory)],
             "tsp_status_string": [c_int32],
         }
         for name, args in sig.items():
@@ -168,6 +175,15 @@ def zigzag_plan(seq_len: int, D: int, rank: int):
 
 def workspace_size(n_tokens: int, dims: Dims, D: int, kind: int) -> int:
     return int(lib().tsp_workspace_size(n_tokens, ctypes.byref(dims), D, kind))
+
+
+def memory_footprint(seq_len: int, dims: Dims, D: int, n_layers: int, scheme: int = MEM_TSP,
+                     training: bool = False) -> dict:
+    """Per-rank memory accounting in bytes, by component (tsp_memory_footprint)."""
+    m = Memory()
+    _check(lib().tsp_memory_footprint(seq_len, ctypes.byref(dims), D, n_layers, scheme, int(training),
+                                      ctypes.byref(m)), "tsp_memory_footprint")
+    return {f: int(getattr(m, f)) for f, _ in Memory._fields_}
 
 
 def attn_project(plan: Plan, dims: Dims, x_local, wqkv, k_full, v_full, q_out, stream=None):

@@ -543,6 +543,62 @@ tsp_status tsp_mlp_backward(int64_t n_tokens, const tsp_dims* dims, int32_t D, i
                             const uint16_t* const* w2, const uint16_t* dy, uint16_t* dx, float* const* dw1,
                             float* const* dw2, void* workspace, size_t ws_bytes, hipStream_t stream);
 
+/* Per-rank memory of a decoder stack, in bytes (see tsp_memory_footprint). */
+typedef struct {
+  uint64_t weights;      /* own 1/D share of every layer's weights, bf16 */
+  uint64_t streamed;     /* TSP: the D-1 other weight shards of the layer being computed, bf16 */
+  uint64_t kv;           /* TSP: gathered K and V of one layer [S x hidden]; TP: own heads' K, V [S x hidden/D] */
+  uint64_t activations;  /* token buffers and workspace of one layer's forward */
+  uint64_t train_state;  /* training: bf16 grads, fp32 master weights, Adam m and v of the own share,
+                            and every layer's input kept for recomputation */
+  uint64_t grads;        /* training: fp32 weight-gradient contributions of one layer */
+  uint64_t total;
+} tsp_memory;
+
+/* Layouts compared by tsp_memory_footprint. */
+typedef enum {
+  TSP_MEM_TSP = 0, /* TSP: one axis of size D shards weights and tokens (S/D local tokens) */
+  TSP_MEM_TP = 1   /* plain tensor parallelism: heads and FFN sharded, all S tokens on every rank */
+} tsp_mem_scheme;
+
+/*
+ * Per-rank memory accounting for n_layers decoder layers of `dims` at total
+ * sequence seq_len on an axis of D ranks, for comparing TSP with plain tensor
+ * parallelism (zubnet.ai TSP page, para. 1: parameter and activation memory
+ * both fall by 1/D under TSP; para. 2: 38.8 GB per GPU for TSP against 70.0 GB
+ * for plain TP at 128K tokens on 8 GPUs, with what those hold not stated).
+ * Counted, per rank (host arithmetic only, nothing allocated):
+ *   weights     : n_layers * (4 h^2 + 2 h F) / D parameters, 2 bytes each (both schemes);
+ *   streamed    : TSP only, the other D-1 shards of one layer, which this
+ *                 library's per-layer calls take resident (0 for TP and D = 1);
+ *   kv          : TSP 2 * S * h * 2 bytes (the gathered K/V of one layer);
+ *                 TP 2 * S * (h/D) * 2 bytes (the rank's heads, no gather);
+ *   activations : one layer's forward with this library's kernels: the input
+ *                 and output rows plus tsp_workspace_size(n, ., D, TSP_WS_LAYER)
+ *                 for TSP (n = S/D tokens, all heads); for TP the same buffers
+ *                 for all S tokens with the rank's H/D heads and F/D FFN
+ *                 columns (attention state, fp16 weight copies and GELU
+ *                 block narrowed, token rows of width h full);
+ *   train_state : training != 0 only: 14 bytes per own parameter (bf16 grad,
+ *                 fp32 master, Adam m and v) plus n_layers layer inputs,
+ *                 [tokens x h] bf16 (full recomputation of each layer);
+ *   grads       : training != 0 only: the fp32 weight-gradient contributions
+ *                 of one layer that the backward writes before they are
+ *                 reduced to the shard owners: every shard under TSP
+ *                 ((4 h^2 + 2 h F) * 4 bytes), the own shard under TP;
+ *   total       : the sum.
+ * The backward calls' own workspaces (tsp_workspace_size, kinds *_BWD) and
+ * the embedding and output layers are not counted.  With D = 1 both schemes
+ * count the same buffers.
+ *   dims  : as tsp_layer_forward (head_dim 64 or 128, H % D == 0, F/D % 64 == 0).
+ *   out   : host out, required.
+ * Errors: TSP_ERR_INVALID_ARG (out or dims null, D out of range, n_layers < 0,
+ *         unknown scheme), TSP_ERR_SHAPE / TSP_ERR_UNSUPPORTED (as
+ *         tsp_zigzag_plan and tsp_layer_forward for S, D and dims).
+ */
+tsp_status tsp_memory_footprint(int64_t seq_len, const tsp_dims* dims, int32_t D, int32_t n_layers,
+                                int32_t scheme, int32_t training, tsp_memory* out);
+
 /* Static text for a status code (never null). */
 const char* tsp_status_string(tsp_status status);
 
