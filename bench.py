@@ -14,6 +14,9 @@ The step calls the three entry points that tsp_layer_forward composes
 (tsp_attn_project, tsp_attn_core, tsp_layer_post), with HIP events recorded
 between them on the launch stream: the per-launch time of the attention kernel
 (the dominant one, about 73% of the layer's FLOPs) gives the roofline figure.
+``--workload stream_7b_16k`` runs the weight-streaming regime instead (S =
+16384, 2048 local tokens, 32 distinct layers): there the roofline figure is the
+whole layer, and ``hbm`` reports its bytes per second against the HBM peak.
 
 After the timed steps, each step's entry point is also timed alone on layer
 0's inputs (``rows_layer0``: QKV projection, attention, O projection, MLP),
@@ -39,9 +42,16 @@ import torch
 from folded_tensor_sequence_tsp_amd import profile_summary, synth, tsp
 
 ROOT = os.path.dirname(os.path.abspath(__file__))
-# rocprofv3 counter summary of the attention kernel on the default workload: its
-# traffic figure is used only while the kernel's sources are the ones profiled.
-TRAFFIC_SUMMARY = os.path.join(ROOT, "profiles", "tsp_attn_core_7b_128k_rank0_32layers.md")
+# rocprofv3 counter summaries, per workload: (file, unit).  On the 128K
+# workload the dominant unit is the attention core; on the 16K weight-streaming
+# workload the whole layer is reported (its HBM traffic against the weights it
+# streams).  A figure is used only while the kernels' sources are the ones
+# profiled.
+TRAFFIC_SUMMARY = {
+    "full_7b_128k": (os.path.join(ROOT, "profiles", "tsp_attn_core_7b_128k_rank0_32layers.md"), "tsp_attn_core"),
+    "stream_7b_16k": (os.path.join(ROOT, "profiles", "tsp_layer_forward_7b_16k_rank0_32layers.md"),
+                      "tsp_layer_forward"),
+}
 
 PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
 PEAK_HBM_GBS = 8000.0        # MI355X HBM3E
@@ -58,6 +68,15 @@ def layer_flops(n, S, D, C, d):
         "oproj": 2.0 * n * h * h,  # O projection
         "mlp": 4.0 * n * h * F,
     }
+
+
+def layer_bytes(plan, d):
+    """Algorithmic HBM bytes of one rank-share layer: its weights (all D
+    shards, bf16), the gathered K and V rows up to the rank's last query
+    position, the input rows and the output rows."""
+    h, F = d.hidden, d.ffn
+    kv_rows = plan.chunk_start[1] + plan.chunk_len
+    return (4 * h * h + 2 * h * F) * 2 + 2 * kv_rows * h * 2 + 2 * plan.n_local * h * 2
 
 
 def row_timings(plan, dims, D, layer0, x0, q, a, a_lo, out, ws_core, fl, dev, reps=3):
@@ -360,7 +379,19 @@ def main():
     layer_ms = ms_per_step / n_layers
     value = n / (layer_ms * 1e-3)
     total_flops = sum(fl.values())
-    attn_tflops = fl["attn"] / (stage_ms["attn"] * 1e-3) / 1e12
+
+    summary, unit = TRAFFIC_SUMMARY[args.workload]
+    if unit == "tsp_attn_core":
+        roof = {"kernel": "tsp_attn_core (vt_prep_kernel + attn_kernel<128>)", "flops": fl["attn"],
+                "ms": stage_ms["attn"]}
+    else:
+        roof = {"kernel": "tsp_layer_forward (QKV, attention, O projection, MLP)", "flops": total_flops,
+                "ms": sum(stage_ms.values())}
+    roof_tflops = roof["flops"] / (roof["ms"] * 1e-3) / 1e12
+    traffic = profile_summary.read_traffic(summary, unit)
+    alg_bytes = layer_bytes(plan, d)
+    layer_stream_ms = sum(stage_ms.values())
+    layer_traffic = traffic if unit == "tsp_layer_forward" else None
 
     result = {
         "metric": METRIC,
@@ -388,17 +419,29 @@ def main():
         "stages_tflops": {k: round(fl[k] / (stage_ms[k] * 1e-3) / 1e12, 1) for k in stages},
         "stages_ms_layer0": {k: round(v, 4) for k, v in first_ms.items()},
         "roofline": {
-            "kernel": "tsp_attn_core (vt_prep_kernel + attn_kernel<128>)",
+            "kernel": roof["kernel"],
             "bound": "mfma",
-            "achieved": round(attn_tflops, 1),
+            "achieved": round(roof_tflops, 1),
             "peak": PEAK_BF16_TFLOPS,
             "unit": "TFLOP/s",
-            "frac": round(attn_tflops / PEAK_BF16_TFLOPS, 4),
-            "flops_per_launch": fl["attn"],
-            "ms_per_launch": round(stage_ms["attn"], 4),
-            "traffic": profile_summary.read_traffic(TRAFFIC_SUMMARY, "tsp_attn_core"),
-            "traffic_source": os.path.relpath(TRAFFIC_SUMMARY, ROOT),
-            "profile_ms_per_launch": profile_summary.read_avg_ms(TRAFFIC_SUMMARY, "tsp_attn_core"),
+            "frac": round(roof_tflops / PEAK_BF16_TFLOPS, 4),
+            "flops_per_launch": roof["flops"],
+            "ms_per_launch": round(roof["ms"], 4),
+            "traffic": traffic,
+            "traffic_source": os.path.relpath(summary, ROOT),
+            "profile_ms_per_launch": profile_summary.read_avg_ms(summary, unit),
+        },
+        # the layer against the HBM roof: algorithmic bytes (weights, the K/V
+        # rows read, input and output rows) and, from the counter summary when
+        # it covers the whole layer, the bytes actually moved
+        "hbm": {
+            "algorithmic_bytes_per_layer": alg_bytes,
+            "achieved_GBs": round(alg_bytes / (layer_stream_ms * 1e-3) / 1e9, 1),
+            "traffic_bytes_per_layer": layer_traffic,
+            "traffic_GBs": (round(layer_traffic / (layer_stream_ms * 1e-3) / 1e9, 1) if layer_traffic else None),
+            "peak": PEAK_HBM_GBS,
+            "frac": (round(layer_traffic / (layer_stream_ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 4) if layer_traffic
+                     else round(alg_bytes / (layer_stream_ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 4)),
         },
         "cpu_baseline": None,
     }

@@ -48,8 +48,17 @@ UNITS = {
     # forward's vt_prep_kernel and are listed in the table, not in the unit)
     "tsp_attn_core_backward": (["bwd_stats_kernel", "dkv_kernel", "dq_kernel"],
                                ["attn_backward.hip", "device_common.h", "kernels.h:AttnBwdArgs"]),
+    # one whole forward layer (tsp_attn_project + tsp_attn_core + tsp_layer_post)
+    "tsp_layer_forward": (["gemm_kernel", "vt_prep_kernel", "attn_kernel", "row_prep_kernel", "bf16_to_f16_kernel"],
+                          ["gemm.hip", "attention.hip", "prep.hip", "device_common.h", "kernels.h:GemmArgs",
+                           "kernels.h:AttnArgs"]),
 }
 KERNEL_SOURCES = {k: v[1] for k, v in UNITS.items()}
+# Units whose kernels launch several times per call, in different forms: their
+# figures are totals over all matching dispatches divided by the dispatch count
+# of the named kernel, which runs once per call (a layer has one attention
+# launch, four GEMMs and two weight conversions).
+PER_CALL = {"tsp_layer_forward": "attn_kernel"}
 
 
 def _source_text(name: str) -> bytes:
@@ -104,16 +113,25 @@ def summarise(trace, fetch, write, unit, copy_mib, command, workload):
     given, of its two counter runs (traffic of the unit's kernels)."""
     stats = kernel_stats(trace)
     kernels = UNITS[unit][0]
+    per = PER_CALL.get(unit)
     avg_ms = 0.0
-    for k in kernels:
-        avg_ms += sum(ms for n, _, ms, _ in stats if n.startswith(k))
+    if per:
+        calls = sum(c for n, c, _, _ in stats if n.startswith(per))
+        avg_ms = sum(c * ms for n, c, ms, _ in stats if n.startswith(tuple(kernels))) / calls
+    else:
+        for k in kernels:
+            avg_ms += sum(ms for n, _, ms, _ in stats if n.startswith(k))
     if fetch and write:
         f, w = counters(fetch), counters(write)
         copy_bytes = copy_mib << 20
         ff, f_copy = _copy_factor(f, copy_bytes)
         wf, w_copy = _copy_factor(w, copy_bytes)
         fetch_b = write_b = 0.0
-        for k in kernels:
+        if per:
+            mine = lambda n: "tsp::" in n and any(k in n for k in kernels)
+            fetch_b = sum(v for n, v in f.values() if mine(n)) * 1024.0 * ff / sum(per in n for n, _ in f.values())
+            write_b = sum(v for n, v in w.values() if mine(n)) * 1024.0 * wf / sum(per in n for n, _ in w.values())
+        for k in kernels if not per else []:
             fk = [v for n, v in f.values() if k in n]
             wk = [v for n, v in w.values() if k in n]
             fetch_b += sum(fk) / len(fk) * 1024.0 * ff
