@@ -382,7 +382,7 @@ def main():
 
     summary, unit = TRAFFIC_SUMMARY[args.workload]
     if unit == "tsp_attn_core":
-        roof = {"kernel": "tsp_attn_core (vt_prep_kernel + attn_kernel<128>)", "flops": fl["attn"],
+        roof = {"kernel": "tsp_attn_core (vt_prep_kernel + attn_kernel<128, false>)", "flops": fl["attn"],
                 "ms": stage_ms["attn"]}
     else:
         roof = {"kernel": "tsp_layer_forward (QKV, attention, O projection, MLP)", "flops": total_flops,

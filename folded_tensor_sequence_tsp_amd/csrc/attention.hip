@@ -37,7 +37,12 @@
 //     query heads of one K/V head are neighbours in the workgroup order, so
 //     they meet its K/V in the same XCD's L2;
 //   * workgroups ordered so each XCD works through a contiguous range of heads,
-//     heaviest (latest) query tiles first.
+//     heaviest (latest) query tiles first;
+//   * when the grid is small (few query tiles: short sequences), the late
+//     chunk's tiles, which see almost the whole sequence while the early
+//     chunk's see a few tiles, are split in two along the keys: each half
+//     writes its unnormalised output with its running max and sum, and a
+//     combine kernel merges the halves (the same algebra as the lazy rescale).
 #include "device_common.h"
 #include "kernels.h"
 
@@ -111,7 +116,7 @@ __global__ __launch_bounds__(128) void vt_prep_kernel(const uint16_t* __restrict
   }
 }
 
-template <int HD>
+template <int HD, bool SPLIT>
 __global__ __launch_bounds__(NTHREADS) void attn_kernel(const AttnArgs a) {
   using C = ACfg<HD>;
   __shared__ __attribute__((aligned(1024))) uint8_t smem[NSTAGE * C::STAGE_BYTES];
@@ -123,22 +128,35 @@ __global__ __launch_bounds__(NTHREADS) void attn_kernel(const AttnArgs a) {
   const int ql = lane & 31;
 
   // ---- work item: (head, chunk, tile), heaviest tiles of a head first, heads
-  // contiguous per XCD.
+  // contiguous per XCD.  SPLIT: (head, chunk 1, tile, key half) items first,
+  // then the chunk-0 tiles whole.
   const int tpc = (int)((a.chunk_len + QT - 1) / QT);
-  const int per_head = 2 * tpc;
+  const int per_head = (SPLIT ? 3 : 2) * tpc;
   const int nwg = gridDim.x;
   int pid = blockIdx.x;
   if ((nwg & 7) == 0) pid = (pid & 7) * (nwg >> 3) + (pid >> 3);
   const int head = pid / per_head;
   const int w = pid - head * per_head;
-  const int chunk = w < tpc ? 1 : 0;
-  const int tile = w < tpc ? tpc - 1 - w : per_head - 1 - w;
+  const int n1 = SPLIT ? 2 * tpc : tpc;  // items of chunk 1
+  const int chunk = w < n1 ? 1 : 0;
+  const int tile = w < n1 ? tpc - 1 - (SPLIT ? w >> 1 : w) : per_head - 1 - w;
+  const int part = SPLIT && chunk ? (w & 1) : -1;  // key half of a split item, -1: whole
 
   const int64_t row0 = (int64_t)chunk * a.chunk_len + (int64_t)tile * QT;  // local row of query 0
   const int64_t pos0 = (chunk ? a.chunk_start1 : a.chunk_start0) + (int64_t)tile * QT;
   const int valid = (int)min((int64_t)QT, a.chunk_len - (int64_t)tile * QT);
   const int64_t key_end = pos0 + valid;  // keys [0, key_end)
   const int n_tiles = (int)((key_end + BKV - 1) / BKV);
+  // key tiles [t_begin, t_end) of this item; a split's first half ends before
+  // the tile's first query, so only the second half crosses the diagonal
+  int t_begin = 0, t_end = n_tiles;
+  if (SPLIT && part >= 0) {
+    const int mid = (int)min((int64_t)(n_tiles / 2), pos0 / BKV);
+    if (part == 0)
+      t_end = mid;
+    else
+      t_begin = mid;
+  }
 
   // This lane's query (clamped to the last valid row for the ragged tail).
   const int qi = min(wave * 32 + ql, valid - 1);
@@ -343,8 +361,8 @@ __global__ __launch_bounds__(NTHREADS) void attn_kernel(const AttnArgs a) {
   // PV MFMAs); last, issue the loads of tile t+NSTAGE-1 (issued after the
   // compute, the loads do not hold up the wave's MFMAs).
   auto step = [&](int t, f32x16 (&s_cu)[2], f32x16 (&s_nx)[2], float& mt) __attribute__((always_inline)) {
-    if (t + 1 < n_tiles) {
-      if (t + 2 < n_tiles)
+    if (t + 1 < t_end) {
+      if (t + 2 < t_end)
         wait_vmcnt<C::LOADS>();
       else
         wait_vmcnt<0>();
@@ -363,12 +381,12 @@ __global__ __launch_bounds__(NTHREADS) void attn_kernel(const AttnArgs a) {
       // a stale stage and is never used), keeping the block branch-free.
       fused_block(t, s_cu, s_nx, mt);
     }
-    if (t + NSTAGE - 1 < n_tiles) issue_tile(t + NSTAGE - 1);
+    if (t + NSTAGE - 1 < t_end) issue_tile(t + NSTAGE - 1);
   };
 
-  // ---- prologue: tiles 0 .. NSTAGE-2 in flight, wait for tile 0.
-  const int pro = min(NSTAGE - 1, n_tiles);
-  for (int t = 0; t < pro; ++t) issue_tile(t);
+  // ---- prologue: tiles t_begin .. t_begin+NSTAGE-2 in flight, wait for the first.
+  const int pro = max(min(NSTAGE - 1, t_end - t_begin), 0);
+  for (int t = t_begin; t < t_begin + pro; ++t) issue_tile(t);
   if (pro >= 3)
     wait_vmcnt<2 * C::LOADS>();
   else if (pro == 2)
@@ -379,16 +397,37 @@ __global__ __launch_bounds__(NTHREADS) void attn_kernel(const AttnArgs a) {
 
   f32x16 sA[2], sB[2];
   float mt = -INFINITY;  // scaled max of the current tile's masked scores
-  if (wave_tiles > 0) {
-    compute_s(0, sA);
-    mask_tile(0, sA);
+  if (t_begin < t_end && t_begin < wave_tiles) {
+    compute_s(t_begin, sA);
+    mask_tile(t_begin, sA);
     mt = tile_max(sA);
   }
-  for (int t = 0; t < n_tiles; t += 2) {
+  for (int t = t_begin; t < t_end; t += 2) {
     step(t, sA, sB, mt);
-    if (t + 1 < n_tiles) step(t + 1, sB, sA, mt);
+    if (t + 1 < t_end) step(t + 1, sB, sA, mt);
   }
   wait_vmcnt<0>();
+
+  if (SPLIT && part >= 0) {
+    // unnormalised output, running max (log2 units) and sum of this key half
+    if (wave_active && wave_first + ql < valid) {
+      const float l_tot = l_run + __shfl_xor(l_run, 32);
+      const int64_t r1 = (int64_t)tile * QT + wave_first + ql;  // row within chunk 1
+      float* op = a.part_o + ((int64_t)part * a.chunk_len + r1) * ld + hcol + 4 * half;
+#pragma unroll
+      for (int dt = 0; dt < C::DT; ++dt)
+#pragma unroll
+        for (int g = 0; g < 4; ++g)
+          *reinterpret_cast<f32x4*>(op + dt * 32 + 8 * g) =
+              f32x4{o[dt][4 * g], o[dt][4 * g + 1], o[dt][4 * g + 2], o[dt][4 * g + 3]};
+      if (half == 0) {
+        float* ml = a.part_ml + (((int64_t)part * a.n_heads + head) * a.chunk_len + r1) * 2;
+        ml[0] = m_run;
+        ml[1] = l_tot;
+      }
+    }
+    return;
+  }
 
   // ---- normalise and store: lane holds query ql, dims dt*32 + 8*(e/4) + 4*half + e%4.
   if (wave_active) {
@@ -422,9 +461,72 @@ __global__ __launch_bounds__(NTHREADS) void attn_kernel(const AttnArgs a) {
   }
 }
 
+// Merge the two key halves of the late chunk's rows: with (m_p, l_p, o_p) the
+// running max (log2 units), sum and unnormalised output of half p and
+// M = max(m_0, m_1), the row's output is
+// (o_0 2^(m_0-M) + o_1 2^(m_1-M)) / (l_0 2^(m_0-M) + l_1 2^(m_1-M)).
+// One thread per (row, head, 8 columns); an empty first half has m_0 = -inf.
+template <int HD>
+__global__ __launch_bounds__(256) void attn_combine_kernel(const AttnArgs a) {
+  constexpr int G = HD / 8;  // 8-column groups per head
+  const int64_t idx = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  const int64_t total = a.chunk_len * a.n_heads * G;
+  if (idx >= total) return;
+  const int g = (int)(idx % G);
+  const int head = (int)((idx / G) % a.n_heads);
+  const int64_t r1 = idx / ((int64_t)G * a.n_heads);
+  const float* ml0 = a.part_ml + ((int64_t)head * a.chunk_len + r1) * 2;
+  const float* ml1 = a.part_ml + (((int64_t)a.n_heads + head) * a.chunk_len + r1) * 2;
+  const float m0 = ml0[0], l0 = ml0[1], m1 = ml1[0], l1 = ml1[1];
+  const float M = fmaxf(m0, m1);
+  const float w0 = __builtin_amdgcn_exp2f(m0 - M), w1 = __builtin_amdgcn_exp2f(m1 - M);
+  const float L = l0 * w0 + l1 * w1;
+  const float inv = 1.0f / L;
+  const int64_t col = (int64_t)head * HD + 8 * g;
+  const float* o0 = a.part_o + r1 * a.hidden + col;
+  const float* o1 = a.part_o + (a.chunk_len + r1) * a.hidden + col;
+  float r[8];
+#pragma unroll
+  for (int h4 = 0; h4 < 2; ++h4) {
+    const f32x4 x0 = *reinterpret_cast<const f32x4*>(o0 + 4 * h4);
+    const f32x4 x1 = *reinterpret_cast<const f32x4*>(o1 + 4 * h4);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) r[4 * h4 + j] = (x0[j] * w0 + x1[j] * w1) * inv;
+  }
+  const int64_t off = (a.chunk_len + r1) * a.hidden + col;  // local row of chunk 1
+  u32x4 v;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) v[j] = pack_bf16x2(r[2 * j], r[2 * j + 1]);
+  *reinterpret_cast<u32x4*>(a.o + off) = v;
+  if (a.o_lo) {
+    u32x4 wv;
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+      wv[j] = pack_bf16x2(r[2 * j] - __uint_as_float(v[j] << 16), r[2 * j + 1] - __uint_as_float(v[j] & 0xffff0000u));
+    *reinterpret_cast<u32x4*>(a.o_lo + off) = wv;
+  }
+  if (a.lse && g == 0) a.lse[(int64_t)head * 2 * a.chunk_len + a.chunk_len + r1] = (M + log2f(L)) * 0.69314718055994530942f;
+}
+
+constexpr int64_t SPLIT_BELOW = 512;  // split the late chunk's tiles when the grid has fewer items
+
+bool attn_split(int64_t chunk_len, int32_t n_heads) {
+  const int64_t tpc = (chunk_len + QT - 1) / QT;
+  return chunk_len > 0 && 2 * (int64_t)n_heads * tpc < SPLIT_BELOW;
+}
+
+size_t align256(size_t x) { return (x + 255) / 256 * 256; }
+
 }  // namespace
 
 int64_t attn_kv_tiles(int64_t seq_len) { return (seq_len + BKV - 1) / BKV; }
+
+size_t attn_core_workspace(int64_t seq_len, int64_t chunk_len, int32_t hidden, int32_t n_heads) {
+  size_t bytes = align256((size_t)attn_kv_tiles(seq_len) * 64 * hidden * 2);  // V^T tiles
+  if (attn_split(chunk_len, n_heads))
+    bytes += align256((size_t)2 * chunk_len * hidden * 4) + align256((size_t)2 * n_heads * chunk_len * 2 * 4);
+  return bytes;
+}
 
 hipError_t launch_vt_tiles(const uint16_t* src, int64_t rows, int32_t ld, int32_t heads, int32_t head_dim,
                            uint16_t* dst, int64_t n_tiles, hipStream_t stream) {
@@ -441,16 +543,34 @@ hipError_t launch_vt_prep(const AttnArgs& a, hipStream_t stream) {
   return launch_vt_tiles(a.v, a.seq_len, a.kv_ld, a.kv_heads, a.head_dim, a.vt, a.n_kv_tiles, stream);
 }
 
-hipError_t launch_attention(const AttnArgs& a, hipStream_t stream) {
-  if (a.chunk_len <= 0) return hipSuccess;
-  hipError_t e = launch_vt_prep(a, stream);
+hipError_t launch_attention(const AttnArgs& args, hipStream_t stream) {
+  if (args.chunk_len <= 0) return hipSuccess;
+  hipError_t e = launch_vt_prep(args, stream);
   if (e != hipSuccess) return e;
-  const int tpc = (int)((a.chunk_len + QT - 1) / QT);
-  const dim3 grid(a.n_heads * 2 * tpc), block(NTHREADS);
-  if (a.head_dim == 128)
-    hipLaunchKernelGGL(attn_kernel<128>, grid, block, 0, stream, a);
-  else
-    hipLaunchKernelGGL(attn_kernel<64>, grid, block, 0, stream, a);
+  const int tpc = (int)((args.chunk_len + QT - 1) / QT);
+  const dim3 block(NTHREADS);
+  if (!attn_split(args.chunk_len, args.n_heads)) {
+    const dim3 grid(args.n_heads * 2 * tpc);
+    if (args.head_dim == 128)
+      hipLaunchKernelGGL((attn_kernel<128, false>), grid, block, 0, stream, args);
+    else
+      hipLaunchKernelGGL((attn_kernel<64, false>), grid, block, 0, stream, args);
+    return hipGetLastError();
+  }
+  // the key halves' partials follow the V^T tiles in the workspace
+  AttnArgs a = args;
+  char* base = reinterpret_cast<char*>(a.vt) + align256((size_t)a.n_kv_tiles * 64 * a.hidden * 2);
+  a.part_o = reinterpret_cast<float*>(base);
+  a.part_ml = reinterpret_cast<float*>(base + align256((size_t)2 * a.chunk_len * a.hidden * 4));
+  const dim3 grid(a.n_heads * 3 * tpc);
+  const unsigned cgrid = (unsigned)((a.chunk_len * a.n_heads * (a.head_dim / 8) + 255) / 256);
+  if (a.head_dim == 128) {
+    hipLaunchKernelGGL((attn_kernel<128, true>), grid, block, 0, stream, a);
+    hipLaunchKernelGGL(attn_combine_kernel<128>, dim3(cgrid), dim3(256), 0, stream, a);
+  } else {
+    hipLaunchKernelGGL((attn_kernel<64, true>), grid, block, 0, stream, a);
+    hipLaunchKernelGGL(attn_combine_kernel<64>, dim3(cgrid), dim3(256), 0, stream, a);
+  }
   return hipGetLastError();
 }
 

@@ -97,10 +97,19 @@ struct AttnArgs {
   // nullable: lse[head * 2 * chunk_len + row] = ln sum_j exp(score), the
   // natural log of each query row's softmax normaliser (kept for the backward).
   float* lse;
+  // set by launch_attention when it splits the late chunk's keys in two
+  // (placed after the V^T tiles): the halves' unnormalised outputs
+  // [2][chunk_len][hidden] fp32 and (max, sum) pairs [2][n_heads][chunk_len][2]
+  float* part_o;
+  float* part_ml;
 };
 
 // 64-key tiles covering seq_len keys.
 int64_t attn_kv_tiles(int64_t seq_len);
+
+// Bytes of workspace launch_attention needs: the V^T tiles for seq_len keys
+// and hidden columns, plus the split partials when the grid is small.
+size_t attn_core_workspace(int64_t seq_len, int64_t chunk_len, int32_t hidden, int32_t n_heads);
 
 // V -> V^T tiles, then the attention kernel (both on `stream`).
 hipError_t launch_attention(const AttnArgs& args, hipStream_t stream);

@@ -72,9 +72,10 @@ tsp_status check_plan(const tsp_plan* p) {
   return TSP_OK;
 }
 
-// Attention core workspace: the V^T tiles of the gathered V for S = D * n keys.
+// Attention core workspace: the V^T tiles of the gathered V for S = D * n keys,
+// and, for short sequences, the partial outputs of the late chunk's key halves.
 size_t ws_core(int64_t n, const tsp_dims* d, int32_t D) {
-  return round_up((size_t)attn_kv_tiles(n * D) * 64 * d->hidden * 2);
+  return round_up(attn_core_workspace(n * D, n / 2, d->hidden, d->n_heads));
 }
 
 // Attention workspace: Q, the attention output as a bf16 pair (hi, lo), then
@@ -1332,15 +1333,16 @@ tsp_status tsp_memory_footprint(int64_t seq_len, const tsp_dims* dims, int32_t D
     m.activations = 2 * round_up(tokens * h * 2) + ws_layer((int64_t)tokens, dims, D);
   } else {
     // The buffers of tsp_layer_forward (input and output rows, Q, attention
-    // output hi and lo, V^T tiles, fp32 h1, its scaled fp16 copy, row
-    // exponents, fp16 W1 and W2 copies, one GELU token block) for all S
-    // tokens, with the rank's H/D heads and F/D FFN columns.
+    // output hi and lo, the attention core's workspace, fp32 h1, its scaled
+    // fp16 copy, row exponents, fp16 W1 and W2 copies, one GELU token block)
+    // for all S tokens, with the rank's H/D heads and F/D FFN columns.
     const uint64_t wa = h / (uint64_t)D, wf = F / (uint64_t)D;
     const uint64_t mb = tokens < (uint64_t)MLP_TOKEN_BLOCK ? tokens : (uint64_t)MLP_TOKEN_BLOCK;
     m.kv = 2 * S * wa * 2;
     m.activations = 2 * round_up(tokens * h * 2) + 3 * round_up(tokens * wa * 2) +
-                    round_up((uint64_t)attn_kv_tiles((int64_t)S) * 64 * wa * 2) + round_up(tokens * h * 4) +
-                    round_up(tokens * h * 2) + round_up(tokens * 4) + 2 * round_up(wf * h * 2) + round_up(mb * wf * 2);
+                    round_up(attn_core_workspace((int64_t)S, (int64_t)S / 2, (int32_t)wa, dims->n_heads / D)) +
+                    round_up(tokens * h * 4) + round_up(tokens * h * 2) + round_up(tokens * 4) +
+                    2 * round_up(wf * h * 2) + round_up(mb * wf * 2);
   }
   if (training) {
     m.train_state = own_params * 14 + (uint64_t)n_layers * tokens * h * 2;

@@ -41,7 +41,8 @@ CSRC = os.path.join(PKG, "csrc")
 # definition of struct Name in kernels.h only (the arguments the kernels read),
 # so that unrelated declarations added there leave a summary valid.
 UNITS = {
-    "tsp_attn_core": (["vt_prep_kernel", "attn_kernel"], ["attention.hip", "device_common.h", "kernels.h:AttnArgs"]),
+    "tsp_attn_core": (["vt_prep_kernel", "attn_kernel", "attn_combine_kernel"],
+                      ["attention.hip", "device_common.h", "kernels.h:AttnArgs"]),
     "attn_kernel": (["attn_kernel"], ["attention.hip", "device_common.h", "kernels.h:AttnArgs"]),
     "gemm_kernel": (["gemm_kernel"], ["gemm.hip", "device_common.h", "kernels.h:GemmArgs"]),
     # backward of the attention core (its transposed-tile pre-passes share the
@@ -49,7 +50,8 @@ UNITS = {
     "tsp_attn_core_backward": (["bwd_stats_kernel", "dkv_kernel", "dq_kernel"],
                                ["attn_backward.hip", "device_common.h", "kernels.h:AttnBwdArgs"]),
     # one whole forward layer (tsp_attn_project + tsp_attn_core + tsp_layer_post)
-    "tsp_layer_forward": (["gemm_kernel", "vt_prep_kernel", "attn_kernel", "row_prep_kernel", "bf16_to_f16_kernel"],
+    "tsp_layer_forward": (["gemm_kernel", "vt_prep_kernel", "attn_kernel", "attn_combine_kernel", "row_prep_kernel",
+                           "bf16_to_f16_kernel"],
                           ["gemm.hip", "attention.hip", "prep.hip", "device_common.h", "kernels.h:GemmArgs",
                            "kernels.h:AttnArgs"]),
 }

@@ -577,7 +577,7 @@ typedef enum {
  *                 and output rows plus tsp_workspace_size(n, ., D, TSP_WS_LAYER)
  *                 for TSP (n = S/D tokens, all heads); for TP the same buffers
  *                 for all S tokens with the rank's H/D heads and F/D FFN
- *                 columns (attention state, fp16 weight copies and GELU
+ *                 columns (attention workspace, fp16 weight copies and GELU
  *                 block narrowed, token rows of width h full);
  *   train_state : training != 0 only: 14 bytes per own parameter (bf16 grad,
  *                 fp32 master, Adam m and v) plus n_layers layer inputs,

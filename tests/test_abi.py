@@ -142,7 +142,10 @@ def test_core_rejects(L):
     assert L.tsp_attn_core(ctypes.byref(p), ctypes.byref(d), A, A, A, A + 64, A + 64, A + 128, 1 << 40, None) == tsp.TSP_ERR_INVALID_ARG
     assert L.tsp_attn_core(ctypes.byref(p), ctypes.byref(d), A, A, A, A + 64, MIS, A + 128, 1 << 40, None) == tsp.TSP_ERR_ALIGNMENT
     need = tsp.workspace_size(p.n_local, d, p.D, tsp.WS_CORE)
-    assert need == p.seq_len * 256 * 2  # V^T copy of the gathered V (S a multiple of 64 here)
+    # V^T copy of the gathered V (S a multiple of 64 here), then the partials of
+    # the late chunk's two key halves (a short sequence: the grid is small)
+    C, H = p.chunk_len, d.n_heads
+    assert need == p.seq_len * 256 * 2 + 2 * C * 256 * 4 + 2 * H * C * 2 * 4
     assert L.tsp_attn_core(ctypes.byref(p), ctypes.byref(d), A, A, A, A + 64, None, A + 128, need - 1, None) == tsp.TSP_ERR_WORKSPACE
     assert L.tsp_attn_core(ctypes.byref(p), ctypes.byref(d), A, A, A, A + 64, None, None, need, None) == tsp.TSP_ERR_WORKSPACE
     assert L.tsp_attn_core(ctypes.byref(p), ctypes.byref(d), A, A, A, A + 64, None, MIS, need, None) == tsp.TSP_ERR_ALIGNMENT
@@ -232,11 +235,19 @@ def test_workspace_sizes(L):
     # post: fp32 h1, fp16 h1, row exponents, fp16 W1 and W2, fp16 GELU block
     assert post == n * 256 * 4 + n * 256 * 2 + n * 4 + 2 * 1024 * 256 * 2 + n * 1024 * 2
     core = tsp.workspace_size(n, d, 4, tsp.WS_CORE)
-    assert core == 4 * n * 256 * 2  # V^T tiles for S = D * n keys
+    # V^T tiles for S = D * n keys; the grid of this short sequence is small
+    # (2 chunks x 4 heads x 1 query tile), so the late chunk's keys are split in
+    # two and the halves' fp32 outputs [2][C][h] and (max, sum) pairs
+    # [2][H][C][2] follow
+    C = n // 2
+    assert core == 4 * n * 256 * 2 + 2 * C * 256 * 4 + 2 * 4 * C * 2 * 4
     assert attn == 3 * n * 256 * 2 + core  # Q, the attention output as a (hi, lo) bf16 pair, V^T
     assert layer == attn + post
     assert tsp.workspace_size(n, d, 4, 99) == 0
     assert tsp.workspace_size(n, _dims(hidden=300), 4, tsp.WS_LAYER) == 0
+    # a long sequence (2 x 32 heads x 32 query tiles) is not split: V^T tiles only
+    big = tsp.make_dims(4096, 32, 128, 16384)
+    assert tsp.workspace_size(16384, big, 8, tsp.WS_CORE) == 131072 * 4096 * 2
     assert tsp.workspace_size(-1, d, 4, tsp.WS_ATTN) == 0
 
 
