@@ -136,6 +136,8 @@ def summarise(trace, fetch, write, unit, copy_mib, command, workload):
         for k in kernels if not per else []:
             fk = [v for n, v in f.values() if k in n]
             wk = [v for n, v in w.values() if k in n]
+            if not fk or not wk:  # a kernel of the unit that this workload does not launch
+                continue
             fetch_b += sum(fk) / len(fk) * 1024.0 * ff
             write_b += sum(wk) / len(wk) * 1024.0 * wf
     lines = [f"# rocprofv3 summary: {unit} ({' + '.join(kernels)}), {workload}", "",
