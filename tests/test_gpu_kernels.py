@@ -157,6 +157,13 @@ CORE_CASES = [
     (4, 128, 4, 4096, 2),
     (2, 64, 1, 130, 0),     # D = 1: plain causal attention, C = 65
     (1, 128, 8, 16, 5),     # C = 1: a single query per chunk
+    # The cases above have small grids (fewer than 512 workgroups), where the
+    # kernel splits the late chunk's keys in two and merges the halves; with
+    # C = 1 the first half is empty.  The next case splits over several query
+    # tiles with a ragged tail; the last has a 512-workgroup grid (64 heads x
+    # 2 chunks x 4 tiles), which runs unsplit.
+    (4, 128, 2, 8200, 1),   # C = 2050
+    (64, 64, 1, 2048, 0),
 ]
 
 
