@@ -12,8 +12,9 @@
 //     in for tensor parallelism's all-reduce.
 //
 // Tiling: BM x BN x 32 block tile; waves of WM x WN (256 x 256 tiles: eight
-// waves of 128 x 64, two per SIMD; 128 x 128 tiles: four waves of 64 x 64), each
-// a grid of 32 x 32 MFMA tiles.  A and B k-tiles stream into a 4-stage LDS ring
+// waves of 128 x 64, two per SIMD; 128 x 256 tiles: eight waves of 64 x 64, for
+// short token counts; 128 x 128 tiles: four waves of 64 x 64), each a grid of
+// 32 x 32 MFMA tiles.  A and B k-tiles stream into a 4-stage LDS ring
 // with direct global->LDS loads (global_load_lds_dwordx4, no register staging),
 // three k-tiles ahead, one vmcnt wait and one barrier per k-tile.  LDS rows are
 // 64 bytes (32 k values); the four 16-byte chunks of row r sit at chunk
@@ -341,6 +342,10 @@ hipError_t launch_gemm(const GemmArgs& g, hipStream_t stream) {
   // when the big tiles would leave most of the 256 CUs idle.
   const long big = (long)((g.M + 255) / 256) * (((g.N_s + 255) / 256) * g.n_shards);
   if (big >= 192) return launch_tiles<256, 256>(g, stream);
+  // short token counts: 128 x 256 tiles (eight waves, 1.33x the bytes per flop
+  // of 256 x 256) while they still fill the CUs, then 128 x 128
+  const long mid = (long)((g.M + 127) / 128) * (((g.N_s + 255) / 256) * g.n_shards);
+  if (mid >= 192 && g.N_s >= 256) return launch_tiles<128, 256>(g, stream);
   return launch_tiles<128, 128>(g, stream);
 }
 
