@@ -25,8 +25,10 @@
 //     vmcnt wait and one barrier; loads run two to three tiles ahead;
 //   * software pipeline: the S MFMAs of tile t+1 sit in one basic block with
 //     the exponentials of tile t (all branches are wave-uniform), so matrix
-//     and vector work interleave; the PV MFMAs of tile t then overlap the mask
-//     and max of the next step;
+//     and vector work interleave; the PV MFMAs of tile t then overlap the max
+//     of tile t+1's unmasked scores and the running sum of tile t (kept in that
+//     block); a tile that crosses a wave's diagonal is masked after the block
+//     and its max taken again;
 //   * online softmax in fp32, log2 domain, scale folded into one FMA, hardware
 //     exp2, and lazy rescaling: the running max moves (and O, l are rescaled)
 //     only when a tile's max exceeds it by more than 2^8, so probabilities stay
@@ -289,7 +291,8 @@ __global__ __launch_bounds__(NTHREADS) void attn_kernel(const AttnArgs a) {
   // the next step read before the current MFMAs and the exponentials of tile
   // t's keys 0..31 spread over the steps; then PV of tile t as DT independent
   // chains over the four 16-key steps, V^T fragments again one step ahead, the
-  // exponentials of keys 32..63 under its first two steps.  The vector work is
+  // exponentials of keys 32..63 under its first two steps and the max of tile
+  // t+1's (unmasked) scores under the last two.  The vector work is
   // split so that each MFMA carries a few vector instructions (co-issued), and
   // LDS latency hides behind MFMAs.
   auto fused_block = [&](int t, f32x16 (&s_cu)[2], f32x16 (&s_nx)[2], float& mt) __attribute__((always_inline)) {
@@ -333,6 +336,7 @@ __global__ __launch_bounds__(NTHREADS) void attn_kernel(const AttnArgs a) {
     u32x4 v[C::DT];
 #pragma unroll
     for (int dt = 0; dt < C::DT; ++dt) v[dt] = vfrag(dt, 0);
+    float mx = -INFINITY;  // max of tile t+1's unmasked scores, under the PV MFMAs
 #pragma unroll
     for (int ks = 0; ks < 4; ++ks) {
       u32x4 w[C::DT];
@@ -344,14 +348,16 @@ __global__ __launch_bounds__(NTHREADS) void attn_kernel(const AttnArgs a) {
       if (ks < 2) {  // keys 32..63, needed from step 2 on, under the MFMAs of steps 0 and 1
 #pragma unroll
         for (int q = 0; q < 4; ++q) prob_pair(8 + 4 * ks + q);
+      } else {
+#pragma unroll
+        for (int e = 0; e < 16; ++e) mx = fmaxf(mx, s_nx[ks - 2][e]);
       }
 #pragma unroll
       for (int dt = 0; dt < C::DT; ++dt) v[dt] = w[dt];
     }
     l_run += lsum;
-    // mask and max of tile t+1, under the PV MFMAs
-    mask_tile(t + 1, s_nx);
-    mt = tile_max(s_nx);
+    asm volatile("" : "+v"(l_run));  // keep the sum in this block, under the MFMAs
+    mt = pair_max(mx) * scale_log2;
   };
 
   // One pipeline step: make tile t+1 visible (and the stage of tile t-1 free);
@@ -380,6 +386,12 @@ __global__ __launch_bounds__(NTHREADS) void attn_kernel(const AttnArgs a) {
       // S of tile t+1 is computed even past the wave's last tile (it then reads
       // a stale stage and is never used), keeping the block branch-free.
       fused_block(t, s_cu, s_nx, mt);
+      // tile t+1 crosses the wave's diagonal (rare): mask it and take its max
+      // again (the block's max is of the unmasked scores)
+      if ((int64_t)(t + 1) * BKV + BKV - 1 > wave_min_pos) {  // wave-uniform
+        mask_tile(t + 1, s_nx);
+        mt = tile_max(s_nx);
+      }
     }
     if (t + NSTAGE - 1 < t_end) issue_tile(t + NSTAGE - 1);
   };
