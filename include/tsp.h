@@ -159,7 +159,9 @@ tsp_status tsp_attn_project(const tsp_plan* plan, const tsp_dims* dims, const ui
  *              the fp32 result to about 16 significant bits (tsp_attn_out and
  *              tsp_layer_post contract both parts).
  *   workspace: device, >= tsp_workspace_size(n_local, dims, D, TSP_WS_CORE) bytes
- *              (a head-blocked transposed copy of v_full).
+ *              (a head-blocked transposed copy of v_full; for short sequences,
+ *              where the late chunk's key range is processed in two halves,
+ *              also the halves' fp32 partial outputs, maxima and sums).
  */
 tsp_status tsp_attn_core(const tsp_plan* plan, const tsp_dims* dims, const uint16_t* q,
                          const uint16_t* k_full, const uint16_t* v_full, uint16_t* attn_out,
