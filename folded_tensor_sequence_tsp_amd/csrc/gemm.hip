@@ -22,6 +22,9 @@
 // consecutive rows at one k offset, hit distinct banks of the 64-bank LDS.
 // Workgroup ids are remapped so each XCD (ids = x mod 8) gets a contiguous run
 // of tiles, then rasterised in groups of 8 tile rows for L2 reuse of B.
+// With a low part of A (the O projection contracts the attention output's two
+// bf16 parts), A and A_lo share each k-tile: a stage holds three tiles, each B
+// fragment feeds two MFMAs, and the ring is three stages deep.
 #include "device_common.h"
 #include "kernels.h"
 
@@ -31,7 +34,9 @@ namespace {
 constexpr int BK = 32;       // k per tile: one 64-byte LDS row per operand row
 constexpr int STAGES = 4;    // LDS ring depth
 
-template <int BM, int BN>
+// LO: the low part of A (A_lo) shares each k-tile with A: a stage holds the
+// A, A_lo and B tiles, and every B fragment feeds two MFMAs (three stages).
+template <int BM, int BN, bool LO = false>
 struct Cfg {
   static constexpr int WM = BM == 256 ? 128 : 64;  // wave tile
   static constexpr int WN = 64;
@@ -40,10 +45,12 @@ struct Cfg {
   static constexpr int NT = 64 * NW;
   static constexpr int FM = WM / 32, FN = WN / 32;
   static constexpr int A_BYTES = BM * BK * 2, B_BYTES = BN * BK * 2;
-  static constexpr int STAGE_BYTES = A_BYTES + B_BYTES;
+  static constexpr int PARTS = LO ? 2 : 1;  // parts of A in a stage
+  static constexpr int STAGE_BYTES = PARTS * A_BYTES + B_BYTES;
   static constexpr int A_LOADS = A_BYTES / (NT * 16), B_LOADS = B_BYTES / (NT * 16);  // per thread per k-tile
-  static constexpr int LOADS = A_LOADS + B_LOADS;
-  static constexpr int LDS_BYTES = STAGES * STAGE_BYTES;
+  static constexpr int LOADS = PARTS * A_LOADS + B_LOADS;
+  static constexpr int ST = LO ? 3 : STAGES;  // ring depth
+  static constexpr int LDS_BYTES = ST * STAGE_BYTES;
   static_assert(A_LOADS >= 1 && B_LOADS >= 1 && A_BYTES % (NT * 16) == 0 && B_BYTES % (NT * 16) == 0, "tile split");
 };
 
@@ -143,9 +150,9 @@ __device__ __forceinline__ void store_row8(const GemmArgs& g, int nshard, int ro
   }
 }
 
-template <int BM, int BN, int EPI, bool F16>
+template <int BM, int BN, int EPI, bool F16, bool LO = false>
 __global__ __launch_bounds__((Cfg<BM, BN>::NT)) void gemm_kernel(const GemmArgs g) {
-  using C = Cfg<BM, BN>;
+  using C = Cfg<BM, BN, LO>;
   __shared__ __attribute__((aligned(1024))) uint8_t smem[C::LDS_BYTES];
 
   const int tid = threadIdx.x;
@@ -171,7 +178,7 @@ __global__ __launch_bounds__((Cfg<BM, BN>::NT)) void gemm_kernel(const GemmArgs 
   const int m0 = tm * BM;
 
   const int kt_per_shard = g.K_s / BK;
-  const int reps = g.A_lo ? 2 : 1;  // K range of a shard walked once per part of A
+  const int reps = !LO && g.A_lo ? 2 : 1;  // K range of a shard walked once per part of A
   const int kt_per_rep = kt_per_shard * reps;
   const int k_tiles = kt_per_rep * g.k_shards;
 
@@ -208,12 +215,18 @@ __global__ __launch_bounds__((Cfg<BM, BN>::NT)) void gemm_kernel(const GemmArgs 
         if (g.k_shards > 1 && ++nx_d == g.k_shards) nx_d = 0;
       }
     }
-    uint8_t* stage = smem + (t % STAGES) * C::STAGE_BYTES;
+    uint8_t* stage = smem + (t % C::ST) * C::STAGE_BYTES;
 #pragma unroll
     for (int i = 0; i < C::A_LOADS; ++i) dma16(abase + a_off[i], stage + (i * C::NW + wave) * 1024);
+    if constexpr (LO) {
+      const uint16_t* lbase = g.A_lo + acol;
+#pragma unroll
+      for (int i = 0; i < C::A_LOADS; ++i)
+        dma16(lbase + a_off[i], stage + C::A_BYTES + (i * C::NW + wave) * 1024);
+    }
 #pragma unroll
     for (int i = 0; i < C::B_LOADS; ++i)
-      dma16(bbase + b_off[i], stage + C::A_BYTES + (i * C::NW + wave) * 1024);
+      dma16(bbase + b_off[i], stage + C::PARTS * C::A_BYTES + (i * C::NW + wave) * 1024);
   };
 
   f32x16 acc[C::FM][C::FN];
@@ -228,11 +241,11 @@ __global__ __launch_bounds__((Cfg<BM, BN>::NT)) void gemm_kernel(const GemmArgs 
   const int ql = lane & 31;
   const uint32_t xr = (uint32_t)(((lane >> 5) ^ ((ql >> 2) & 3)) << 4);
   const uint32_t a_row = (uint32_t)(wm * C::WM + ql) * 64;
-  const uint32_t b_row = (uint32_t)C::A_BYTES + (uint32_t)(wn * C::WN + ql) * 64;
+  const uint32_t b_row = (uint32_t)(C::PARTS * C::A_BYTES) + (uint32_t)(wn * C::WN + ql) * 64;
 
   // Both k-steps' fragments are read before the first step's MFMAs.
   auto compute_tile = [&](int t) __attribute__((always_inline)) {
-    const uint8_t* stage = smem + (t % STAGES) * C::STAGE_BYTES;
+    const uint8_t* stage = smem + (t % C::ST) * C::STAGE_BYTES;
     u32x4 af[2][C::FM], bfv[2][C::FN];
 #pragma unroll
     for (int kk = 0; kk < BK / 16; ++kk) {
@@ -248,15 +261,30 @@ __global__ __launch_bounds__((Cfg<BM, BN>::NT)) void gemm_kernel(const GemmArgs 
       for (int i = 0; i < C::FM; ++i)
 #pragma unroll
         for (int j = 0; j < C::FN; ++j) acc[i][j] = mfma32_bits<F16>(af[kk][i], bfv[kk][j], acc[i][j]);
+    if constexpr (LO) {  // the low part of A against the same B fragments
+#pragma unroll
+      for (int kk = 0; kk < BK / 16; ++kk) {
+        const uint32_t kx = xr ^ (uint32_t)(kk << 5);
+#pragma unroll
+        for (int i = 0; i < C::FM; ++i)
+          af[kk][i] = *reinterpret_cast<const u32x4*>(stage + C::A_BYTES + a_row + i * 32 * 64 + kx);
+      }
+#pragma unroll
+      for (int kk = 0; kk < BK / 16; ++kk)
+#pragma unroll
+        for (int i = 0; i < C::FM; ++i)
+#pragma unroll
+          for (int j = 0; j < C::FN; ++j) acc[i][j] = mfma32_bits<F16>(af[kk][i], bfv[kk][j], acc[i][j]);
+    }
   };
 
   // ---- main loop: wait for tile t (tiles t+1, t+2 may still be in flight),
   // barrier (tile t visible to all waves; everyone is done with tile t-1),
   // compute tile t, then refill the stage of tile t-1 with tile t+3.
-  const int pro = min(STAGES - 1, k_tiles);
+  const int pro = min(C::ST - 1, k_tiles);
   for (int t = 0; t < pro; ++t) issue_tile(t);
   for (int t = 0; t < k_tiles; ++t) {
-    const int ahead = min(k_tiles - 1 - t, STAGES - 2);  // tiles issued after t
+    const int ahead = min(k_tiles - 1 - t, C::ST - 2);  // tiles issued after t
     if (ahead >= 2)
       wait_vmcnt<2 * C::LOADS>();
     else if (ahead == 1)
@@ -265,7 +293,7 @@ __global__ __launch_bounds__((Cfg<BM, BN>::NT)) void gemm_kernel(const GemmArgs 
       wait_vmcnt<0>();
     lds_barrier();
     compute_tile(t);
-    if (t + STAGES - 1 < k_tiles) issue_tile(t + STAGES - 1);
+    if (t + C::ST - 1 < k_tiles) issue_tile(t + C::ST - 1);
   }
   wait_vmcnt<0>();
   __syncthreads();
@@ -327,6 +355,8 @@ hipError_t launch_tiles(const GemmArgs& g, hipStream_t stream) {
     default:
       if (g.f16)
         hipLaunchKernelGGL((gemm_kernel<BM, BN, EPI_RESID, true>), grid, block, 0, stream, g);
+      else if (g.A_lo)  // O projection on the attention output's two parts
+        hipLaunchKernelGGL((gemm_kernel<BM, BN, EPI_RESID, false, true>), grid, block, 0, stream, g);
       else
         hipLaunchKernelGGL((gemm_kernel<BM, BN, EPI_RESID, false>), grid, block, 0, stream, g);
       break;
