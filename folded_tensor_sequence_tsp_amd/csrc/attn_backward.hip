@@ -15,14 +15,19 @@
 // wants (a 32x32 result holds, per lane, one column and 16 rows; fed back as
 // the B operand those rows are the contraction index, in the order
 // bits-2-and-3-swapped within 16-row groups, so the other operand is stored
-// in that order by the transposed-tile pre-pass):
+// in that order by the transposed-tile pre-pass, or gathered in that order by
+// transposing LDS reads):
 //   * dK/dV: a workgroup owns 128 keys of one K/V head (32 per wave, K and V
 //     fragments in registers as B operands); it streams the 64-query tiles of
 //     both chunks that see those keys, for every query head reading that K/V
-//     head (grouped-query attention; one for MHA) (Q and dO row-major for S = Q K^T and
-//     dP = dO V^T, Q^T and dO^T transposed for dV^T += dO^T P and
-//     dK^T += Q^T dS) through a two-stage LDS ring with direct global->LDS
-//     loads.  Lane = key, so P and dS leave the score registers as B operands;
+//     head (grouped-query attention; one for MHA), with direct global->LDS
+//     loads.  Q and dO row-major feed S = Q K^T and dP = dO V^T; Q^T and dO^T
+//     feed dV^T += dO^T P and dK^T += Q^T dS.  At head_dim 128 the transposed
+//     operands are read from the same row-major tiles with gfx950's
+//     transposing LDS read (ds_read_b64_tr_b16), so a stage holds two tiles
+//     and the ring is four stages deep; at head_dim 64 the stage also holds
+//     pre-transposed Q^T and dO^T tiles and the ring has two stages.  Lane =
+//     key, so P and dS leave the score registers as B operands;
 //   * dQ: a workgroup owns 256 queries of one chunk (32 per wave, Q and dO
 //     fragments in registers); it streams the 64-key tiles (K and V row-major
 //     for S^T = K Q^T and dP^T = V dO^T, K^T for dQ^T += K^T dS^T).
@@ -97,9 +102,12 @@ __global__ __launch_bounds__(64) void bwd_stats_kernel(const AttnBwdArgs a) {
 template <int HD>
 __global__ __launch_bounds__(64 * BW) void dkv_kernel(const AttnBwdArgs a) {
   using C = BCfg<HD, BW>;
-  constexpr int STATS = 1024;                       // per wave: its own copy of the tile's stats
-  constexpr int STAGE = 4 * C::TILE_BYTES + BW * STATS;
-  __shared__ __attribute__((aligned(1024))) uint8_t smem[2 * STAGE];
+  constexpr bool TR = !attn_bwd_stages_qt(HD);  // Q^T, dO^T by transposing reads of the row-major tiles
+  constexpr int STATS = 1024;                    // per wave: its own copy of the tile's stats
+  constexpr int STAGE = (TR ? 2 : 4) * C::TILE_BYTES + BW * STATS;
+  constexpr int NST = TR ? 4 : 2;                // ring depth: 144 KB of LDS either way
+  constexpr int PER_ISSUE = (TR ? 2 : 4) * C::TLOADS + 1;  // DMA instructions per thread per tile
+  __shared__ __attribute__((aligned(1024))) uint8_t smem[NST * STAGE];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -151,13 +159,21 @@ __global__ __launch_bounds__(64 * BW) void dkv_kernel(const AttnBwdArgs a) {
   // DMA sources.  Row-major tiles: instruction j of wave w fills 1 KB block
   // b = j*BW + w, row b*RPL + lane/NCH, logical chunk (lane % NCH) ^ (row % NCH).
   // Transposed tiles: row d = b*8 + lane/8 (128 bytes), chunk (lane % 8) ^ ((d/2) % 8).
+  // Row-major chunk swizzle.  With transposing reads (head_dim 128, 16 chunks
+  // a row) the two 2-bit fields of the row's low nibble, swapped: 16
+  // consecutive rows still cover all 16 chunk positions (row reads), and the
+  // 4 rows x 4 chunks of a transposing read's 32 lanes do too.
+  auto rm_swz = [](int r) -> int {
+    if constexpr (TR) return ((r & 3) << 2) | ((r >> 2) & 3);
+    else return r & (C::NCH - 1);
+  };
   int rm_row[C::TLOADS], rm_col[C::TLOADS], tr_off[C::TLOADS];
 #pragma unroll
   for (int j = 0; j < C::TLOADS; ++j) {
     const int b = j * BW + wave;
     const int r = b * C::RPL + lane / C::NCH;
     rm_row[j] = r;
-    rm_col[j] = ((lane % C::NCH) ^ (r & (C::NCH - 1))) * 8;
+    rm_col[j] = ((lane % C::NCH) ^ rm_swz(r)) * 8;
     const int d = b * 8 + lane / 8;
     tr_off[j] = d * 64 + ((lane % 8) ^ ((d >> 1) & 7)) * 8;
   }
@@ -180,7 +196,7 @@ __global__ __launch_bounds__(64 * BW) void dkv_kernel(const AttnBwdArgs a) {
     int c, t, qh;
     tile_of(i, c, t, qh);
     const int hcol = qh * HD;
-    uint8_t* stage = smem + (i & 1) * STAGE;
+    uint8_t* stage = smem + (i % NST) * STAGE;
     const int64_t rbase = c * CL;
 #pragma unroll
     for (int j = 0; j < C::TLOADS; ++j) {
@@ -189,19 +205,35 @@ __global__ __launch_bounds__(64 * BW) void dkv_kernel(const AttnBwdArgs a) {
       dma16(a.q + off, stage + (j * BW + wave) * 1024);
       dma16(a.dout + off, stage + C::TILE_BYTES + (j * BW + wave) * 1024);
     }
-    const int64_t tbase = ((c * (int64_t)a.n_heads + qh) * a.tpc + t) * (int64_t)(HD * 64);
+    if constexpr (!TR) {
+      const int64_t tbase = ((c * (int64_t)a.n_heads + qh) * a.tpc + t) * (int64_t)(HD * 64);
 #pragma unroll
-    for (int j = 0; j < C::TLOADS; ++j) {
-      dma16(a.qt + tbase + tr_off[j], stage + 2 * C::TILE_BYTES + (j * BW + wave) * 1024);
-      dma16(a.dot + tbase + tr_off[j], stage + 3 * C::TILE_BYTES + (j * BW + wave) * 1024);
+      for (int j = 0; j < C::TLOADS; ++j) {
+        dma16(a.qt + tbase + tr_off[j], stage + 2 * C::TILE_BYTES + (j * BW + wave) * 1024);
+        dma16(a.dot + tbase + tr_off[j], stage + 3 * C::TILE_BYTES + (j * BW + wave) * 1024);
+      }
     }
     const float* st = a.stats + ((c * (int64_t)a.n_heads + qh) * a.tpc + t) * 256;
-    dma16(st + lane * 4, stage + 4 * C::TILE_BYTES + wave * STATS);
+    dma16(st + lane * 4, stage + (TR ? 2 : 4) * C::TILE_BYTES + wave * STATS);
   };
 
   // fragment addresses within a stage (see the DMA swizzles above)
-  const uint32_t rm_a0 = (uint32_t)ql * (HD * 2) + ((uint32_t)(half ^ (ql & (C::NCH - 1))) << 4);
+  const uint32_t rm_a0 = (uint32_t)ql * (HD * 2) + ((uint32_t)(half ^ rm_swz(ql)) << 4);
   const uint32_t tr_a0 = (uint32_t)ql * 128 + ((uint32_t)(half ^ ((ql >> 1) & 7)) << 4);
+  // Transposing reads (ds_read_b64_tr_b16: within each 16 lanes, output lane j
+  // takes element j % 4 of the 8-byte pieces addressed by lanes j / 4,
+  // 4 + j / 4, 8 + j / 4, 12 + j / 4).  Lane 32h + 16g + 4m + p addresses row
+  // 16 ks + 8 s + 4h + m, dims 32 dt + 16g + 4p .. +3, so output lane
+  // 32h + 16g + j holds dim 32 dt + 16g + j at the four rows 16 ks + 8 s + 4h
+  // + 0..3: reads s = 0, 1 give k = 8h + 0..7 in the order the P and dS
+  // fragments hold their queries.  Byte offset within a stage's tile:
+  // 4096 ks + 2048 s + (tr_b ^ 64 dt ^ 32 s).
+  uint32_t tr_b = 0;
+  if constexpr (TR) {
+    const int m = (lane >> 2) & 3, p = lane & 3, g = (lane >> 4) & 1;
+    tr_b = (uint32_t)(4 * half + m) * 256 + (uint32_t)(p & 1) * 8 +
+           ((uint32_t)((2 * g + (p >> 1)) ^ (4 * m + half)) << 4);
+  }
   const float scale_log2 = LOG2E * C::INV_SQRT_HD;
   const float inv_scale_log2 = 1.0f / scale_log2;
   // B fragment of the normaliser/delta k-step: ones at k = 0..2 (half 0)
@@ -228,17 +260,28 @@ __global__ __launch_bounds__(64 * BW) void dkv_kernel(const AttnBwdArgs a) {
     // ranges and costs register copies on every tile)
     // queries of the tile before this lane's key are masked: offsets below qmin
     const int qmin = kw0 + 31 > qp0 ? (int)min(max(key - qp0, (int64_t)0), (int64_t)64) : 0;
-    const uint8_t* stage = smem + (i & 1) * STAGE;
+    const uint8_t* stage = smem + (i % NST) * STAGE;
     const uint8_t* q_st = stage;
     const uint8_t* do_st = stage + C::TILE_BYTES;
-    const uint8_t* qt_st = stage + 2 * C::TILE_BYTES;
-    const uint8_t* dot_st = stage + 3 * C::TILE_BYTES;
-    const float* st = reinterpret_cast<const float*>(stage + 4 * C::TILE_BYTES + wave * STATS);
+    const uint8_t* qt_st = TR ? q_st : stage + 2 * C::TILE_BYTES;
+    const uint8_t* dot_st = TR ? do_st : stage + 3 * C::TILE_BYTES;
+    const float* st = reinterpret_cast<const float*>(stage + (TR ? 2 : 4) * C::TILE_BYTES + wave * STATS);
     auto rm = [&](const uint8_t* base, int mb, int kk) __attribute__((always_inline)) {
       return *reinterpret_cast<const u32x4*>(base + mb * 32 * (HD * 2) + (rm_a0 ^ (uint32_t)(kk << 5)));
     };
     auto tr = [&](const uint8_t* base, int dt, int ks) __attribute__((always_inline)) {
-      return *reinterpret_cast<const u32x4*>(base + dt * 32 * 128 + (tr_a0 ^ (uint32_t)(ks << 5)));
+      if constexpr (TR) {
+        typedef short v4s __attribute__((ext_vector_type(4)));
+        typedef __attribute__((address_space(3))) v4s lds_v4s;
+        const uint8_t* sb = base + ks * 4096;
+        const uint32_t o = tr_b ^ (uint32_t)(dt << 6);
+        const v4s ra = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4s*)(sb + o));
+        const v4s rb = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4s*)(sb + 2048 + (o ^ 32u)));
+        const u32x2 wa = __builtin_bit_cast(u32x2, ra), wb = __builtin_bit_cast(u32x2, rb);
+        return u32x4{wa[0], wa[1], wb[0], wb[1]};
+      } else {
+        return *reinterpret_cast<const u32x4*>(base + dt * 32 * 128 + (tr_a0 ^ (uint32_t)(ks << 5)));
+      }
     };
     uint32_t pp[16], ps[16];  // bf16 pairs of P and dS: [4*ks + j], 16-query step ks
     // The normaliser and delta enter the products as one extra k-step: A holds,
@@ -324,14 +367,21 @@ __global__ __launch_bounds__(64 * BW) void dkv_kernel(const AttnBwdArgs a) {
     }
   };
 
-  // Two-stage ring, one barrier per tile: the barrier after tile i's wait also
-  // frees the stage that tile i-1 was computed from, so tile i+1's loads go
-  // there right after it, and land during tile i's compute.
-  if (n_all > 0) issue(0);
+  // NST-stage ring, one barrier per tile: the barrier after tile i's wait also
+  // frees the stage that tile i-1 was computed from, so tile i+NST-1's loads go
+  // there right after it, and land during the compute of tiles i..i+NST-2.
+  // The wait leaves the loads of the tiles issued after tile i in flight.
+  for (int i = 0; i < NST - 1 && i < n_all; ++i) issue(i);
   for (int i = 0; i < n_all; ++i) {
-    wait_vmcnt<0>();
+    const int ahead = min(NST - 2, n_all - 1 - i);  // tiles issued after tile i
+    if (NST >= 4 && ahead >= 2)
+      wait_vmcnt<2 * PER_ISSUE>();
+    else if (NST >= 3 && ahead >= 1)
+      wait_vmcnt<PER_ISSUE>();
+    else
+      wait_vmcnt<0>();
     lds_barrier();
-    if (i + 1 < n_all) issue(i + 1);
+    if (i + NST - 1 < n_all) issue(i + NST - 1);
     compute(i);
   }
 
@@ -492,7 +542,7 @@ __global__ __launch_bounds__(64 * QW) void dq_kernel(const AttnBwdArgs a) {
   };
 
   issue(0);
-  for (int t = 0; t < n_tiles; ++t) {  // two-stage ring, one barrier per tile (as in dkv_kernel)
+  for (int t = 0; t < n_tiles; ++t) {  // two-stage ring, one barrier per tile
     wait_vmcnt<0>();
     lds_barrier();
     if (t + 1 < n_tiles) issue(t + 1);
@@ -515,7 +565,7 @@ __global__ __launch_bounds__(64 * QW) void dq_kernel(const AttnBwdArgs a) {
 size_t attn_bwd_ws_bytes(int64_t seq_len, int64_t chunk_len, int32_t n_heads, int32_t kv_heads, int32_t head_dim) {
   const int64_t n_kv_tiles = (seq_len + 63) / 64, tpc = (chunk_len + 63) / 64;
   const size_t kt = (size_t)kv_heads * n_kv_tiles * head_dim * 64 * 2;
-  const size_t qt = (size_t)2 * n_heads * tpc * head_dim * 64 * 2;
+  const size_t qt = attn_bwd_stages_qt(head_dim) ? (size_t)2 * n_heads * tpc * head_dim * 64 * 2 : 0;
   const size_t stats = (size_t)2 * n_heads * tpc * 256 * 4;
   return kt + 2 * qt + stats;
 }
@@ -535,7 +585,7 @@ hipError_t launch_attention_backward(const AttnBwdArgs& a, hipStream_t stream) {
   if ((e = launch_vt_tiles(a.k, a.seq_len, a.kv_ld, a.kv_heads, HD, a.kt, a.n_kv_tiles, stream)) != hipSuccess)
     return e;
   const size_t chunk_tiles = (size_t)H * a.tpc * HD * 64;
-  for (int c = 0; c < 2; ++c) {
+  for (int c = 0; c < 2 && attn_bwd_stages_qt(HD); ++c) {
     const int64_t off = c * a.chunk_len * a.hidden;
     if ((e = launch_vt_tiles(a.q + off, a.chunk_len, a.hidden, H, HD, a.qt + c * chunk_tiles, a.tpc, stream)) !=
         hipSuccess)
