@@ -30,7 +30,9 @@
 //     key, so P and dS leave the score registers as B operands;
 //   * dQ: a workgroup owns 256 queries of one chunk (32 per wave, Q and dO
 //     fragments in registers); it streams the 64-key tiles (K and V row-major
-//     for S^T = K Q^T and dP^T = V dO^T, K^T for dQ^T += K^T dS^T).
+//     for S^T = K Q^T and dP^T = V dO^T, K^T for dQ^T += K^T dS^T: at
+//     head_dim 128 by transposing reads of the K tile, at 64 a pre-transposed
+//     tile).
 //     Lane = query, so the normaliser and delta are per-lane scalars.
 #include "device_common.h"
 #include "kernels.h"
@@ -40,6 +42,7 @@ namespace {
 
 constexpr int BW = 4;   // waves per workgroup of the dK/dV kernel
 constexpr int QW = 8;   // waves per workgroup of the dQ kernel
+constexpr int NST_DQ = 2;  // dQ ring depth with transposing reads (deeper rings spill registers)
 constexpr float LOG2E = 1.44269504088896340736f;
 constexpr float PAD_LSE2 = 65536.0f;
 
@@ -96,6 +99,31 @@ __global__ __launch_bounds__(64) void bwd_stats_kernel(const AttnBwdArgs a) {
   st[64 + r] = dl;
   st[128 + r] = 0.0f;
   st[192 + r] = 0.0f;
+}
+
+// Transposing reads of a row-major 64-row tile of head_dim 128 (256-byte
+// rows, 16-byte chunk c of row r at c ^ ((r & 3) << 2 | (r >> 2) & 3)) into
+// the A fragment of the transposed tile for d tile dt and 16-row step ks.
+// ds_read_b64_tr_b16: within each 16 lanes, output lane j takes element j % 4
+// of the 8-byte pieces addressed by lanes j / 4, 4 + j / 4, 8 + j / 4 and
+// 12 + j / 4.  Lane 32h + 16g + 4m + p addresses row 16 ks + 8 s + 4h + m,
+// dims 32 dt + 16g + 4p .. +3, so output lane 32h + 16g + j holds dim
+// 32 dt + 16g + j at rows 16 ks + 8 s + 4h + 0..3: reads s = 0, 1 give
+// k = 8h + 0..7 in the order a 32x32 result's registers hold their rows.
+// Byte offset within the tile: 4096 ks + 2048 s + (base ^ 64 dt ^ 32 s).
+__device__ __forceinline__ uint32_t tr_read_base(int lane) {
+  const int half = lane >> 5, m = (lane >> 2) & 3, p = lane & 3, g = (lane >> 4) & 1;
+  return (uint32_t)(4 * half + m) * 256 + (uint32_t)(p & 1) * 8 + ((uint32_t)((2 * g + (p >> 1)) ^ (4 * m + half)) << 4);
+}
+__device__ __forceinline__ u32x4 tr_read_frag(const uint8_t* tile, uint32_t base, int dt, int ks) {
+  typedef short v4s __attribute__((ext_vector_type(4)));
+  typedef __attribute__((address_space(3))) v4s lds_v4s;
+  const uint8_t* sb = tile + ks * 4096;
+  const uint32_t o = base ^ (uint32_t)(dt << 6);
+  const v4s ra = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4s*)(sb + o));
+  const v4s rb = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4s*)(sb + 2048 + (o ^ 32u)));
+  const u32x2 wa = __builtin_bit_cast(u32x2, ra), wb = __builtin_bit_cast(u32x2, rb);
+  return u32x4{wa[0], wa[1], wb[0], wb[1]};
 }
 
 // ---- dK, dV.
@@ -220,20 +248,8 @@ __global__ __launch_bounds__(64 * BW) void dkv_kernel(const AttnBwdArgs a) {
   // fragment addresses within a stage (see the DMA swizzles above)
   const uint32_t rm_a0 = (uint32_t)ql * (HD * 2) + ((uint32_t)(half ^ rm_swz(ql)) << 4);
   const uint32_t tr_a0 = (uint32_t)ql * 128 + ((uint32_t)(half ^ ((ql >> 1) & 7)) << 4);
-  // Transposing reads (ds_read_b64_tr_b16: within each 16 lanes, output lane j
-  // takes element j % 4 of the 8-byte pieces addressed by lanes j / 4,
-  // 4 + j / 4, 8 + j / 4, 12 + j / 4).  Lane 32h + 16g + 4m + p addresses row
-  // 16 ks + 8 s + 4h + m, dims 32 dt + 16g + 4p .. +3, so output lane
-  // 32h + 16g + j holds dim 32 dt + 16g + j at the four rows 16 ks + 8 s + 4h
-  // + 0..3: reads s = 0, 1 give k = 8h + 0..7 in the order the P and dS
-  // fragments hold their queries.  Byte offset within a stage's tile:
-  // 4096 ks + 2048 s + (tr_b ^ 64 dt ^ 32 s).
-  uint32_t tr_b = 0;
-  if constexpr (TR) {
-    const int m = (lane >> 2) & 3, p = lane & 3, g = (lane >> 4) & 1;
-    tr_b = (uint32_t)(4 * half + m) * 256 + (uint32_t)(p & 1) * 8 +
-           ((uint32_t)((2 * g + (p >> 1)) ^ (4 * m + half)) << 4);
-  }
+  // transposing reads: the queries come in the order the P and dS fragments hold them
+  const uint32_t tr_b = TR ? tr_read_base(lane) : 0u;
   const float scale_log2 = LOG2E * C::INV_SQRT_HD;
   const float inv_scale_log2 = 1.0f / scale_log2;
   // B fragment of the normaliser/delta k-step: ones at k = 0..2 (half 0)
@@ -271,14 +287,7 @@ __global__ __launch_bounds__(64 * BW) void dkv_kernel(const AttnBwdArgs a) {
     };
     auto tr = [&](const uint8_t* base, int dt, int ks) __attribute__((always_inline)) {
       if constexpr (TR) {
-        typedef short v4s __attribute__((ext_vector_type(4)));
-        typedef __attribute__((address_space(3))) v4s lds_v4s;
-        const uint8_t* sb = base + ks * 4096;
-        const uint32_t o = tr_b ^ (uint32_t)(dt << 6);
-        const v4s ra = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4s*)(sb + o));
-        const v4s rb = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4s*)(sb + 2048 + (o ^ 32u)));
-        const u32x2 wa = __builtin_bit_cast(u32x2, ra), wb = __builtin_bit_cast(u32x2, rb);
-        return u32x4{wa[0], wa[1], wb[0], wb[1]};
+        return tr_read_frag(base, tr_b, dt, ks);
       } else {
         return *reinterpret_cast<const u32x4*>(base + dt * 32 * 128 + (tr_a0 ^ (uint32_t)(ks << 5)));
       }
@@ -407,8 +416,11 @@ template <int HD>
 __global__ __launch_bounds__(64 * QW) void dq_kernel(const AttnBwdArgs a) {
   using C = BCfg<HD, QW>;
   constexpr int QTB = 32 * QW;  // queries per workgroup
-  constexpr int STAGE = 3 * C::TILE_BYTES;
-  __shared__ __attribute__((aligned(1024))) uint8_t smem[2 * STAGE];
+  constexpr bool TR = !attn_bwd_stages_kt(HD);  // K^T by transposing reads of the row-major K tile
+  constexpr int STAGE = (TR ? 2 : 3) * C::TILE_BYTES;
+  constexpr int NST = TR ? NST_DQ : 2;
+  constexpr int PER_ISSUE = (TR ? 2 : 3) * C::TLOADS;  // DMA instructions per thread per tile
+  __shared__ __attribute__((aligned(1024))) uint8_t smem[NST * STAGE];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -466,20 +478,24 @@ __global__ __launch_bounds__(64 * QW) void dq_kernel(const AttnBwdArgs a) {
     dlq = st[64];
   }
 
+  auto rm_swz = [](int r) -> int {  // as in dkv_kernel
+    if constexpr (TR) return ((r & 3) << 2) | ((r >> 2) & 3);
+    else return r & (C::NCH - 1);
+  };
   int rm_row[C::TLOADS], rm_col[C::TLOADS], tr_off[C::TLOADS];
 #pragma unroll
   for (int j = 0; j < C::TLOADS; ++j) {
     const int b = j * QW + wave;
     const int r = b * C::RPL + lane / C::NCH;
     rm_row[j] = r;
-    rm_col[j] = ((lane % C::NCH) ^ (r & (C::NCH - 1))) * 8;
+    rm_col[j] = ((lane % C::NCH) ^ rm_swz(r)) * 8;
     const int d = b * 8 + lane / 8;
     tr_off[j] = d * 64 + ((lane % 8) ^ ((d >> 1) & 7)) * 8;
   }
-  const uint16_t* kt_head = a.kt + (int64_t)kvh * a.n_kv_tiles * HD * 64;
+  const uint16_t* kt_head = TR ? nullptr : a.kt + (int64_t)kvh * a.n_kv_tiles * HD * 64;
 
   auto issue = [&](int t) __attribute__((always_inline)) {
-    uint8_t* stage = smem + (t & 1) * STAGE;
+    uint8_t* stage = smem + (t % NST) * STAGE;
     const int64_t k0 = (int64_t)t * 64;
 #pragma unroll
     for (int j = 0; j < C::TLOADS; ++j) {
@@ -487,12 +503,14 @@ __global__ __launch_bounds__(64 * QW) void dq_kernel(const AttnBwdArgs a) {
       const int64_t off = kr * kld + kcol + rm_col[j];
       dma16(a.k + off, stage + (j * QW + wave) * 1024);
       dma16(a.v + off, stage + C::TILE_BYTES + (j * QW + wave) * 1024);
-      dma16(kt_head + (int64_t)t * HD * 64 + tr_off[j], stage + 2 * C::TILE_BYTES + (j * QW + wave) * 1024);
+      if constexpr (!TR)
+        dma16(kt_head + (int64_t)t * HD * 64 + tr_off[j], stage + 2 * C::TILE_BYTES + (j * QW + wave) * 1024);
     }
   };
 
-  const uint32_t rm_a0 = (uint32_t)ql * (HD * 2) + ((uint32_t)(half ^ (ql & (C::NCH - 1))) << 4);
+  const uint32_t rm_a0 = (uint32_t)ql * (HD * 2) + ((uint32_t)(half ^ rm_swz(ql)) << 4);
   const uint32_t tr_a0 = (uint32_t)ql * 128 + ((uint32_t)(half ^ ((ql >> 1) & 7)) << 4);
+  const uint32_t tr_b = TR ? tr_read_base(lane) : 0u;  // transposing reads, as in dkv_kernel
   const float scale_log2 = LOG2E * C::INV_SQRT_HD;
 
   f32x16 dqT[C::DT];  // [d][query]: lane holds query ql, dims dt*32 + 8*(e/4) + 4*half + e%4
@@ -501,7 +519,7 @@ __global__ __launch_bounds__(64 * QW) void dq_kernel(const AttnBwdArgs a) {
 
   auto compute = [&](int t) __attribute__((always_inline)) {
     if (t >= wave_tiles) return;  // wave-uniform
-    const uint8_t* stage = smem + (t & 1) * STAGE;
+    const uint8_t* stage = smem + (t % NST) * STAGE;
     const int64_t k0 = (int64_t)t * 64;
     const bool need_mask = k0 + 63 > wave_min_pos;
     uint32_t ps[16];
@@ -534,18 +552,28 @@ __global__ __launch_bounds__(64 * QW) void dq_kernel(const AttnBwdArgs a) {
       const u32x4 bs = u32x4{ps[4 * ks], ps[4 * ks + 1], ps[4 * ks + 2], ps[4 * ks + 3]};
 #pragma unroll
       for (int dt = 0; dt < C::DT; ++dt) {
-        const u32x4 ka = *reinterpret_cast<const u32x4*>(stage + 2 * C::TILE_BYTES + dt * 32 * 128 +
-                                                         (tr_a0 ^ (uint32_t)(ks << 5)));
+        u32x4 ka;
+        if constexpr (TR)
+          ka = tr_read_frag(stage, tr_b, dt, ks);
+        else
+          ka = *reinterpret_cast<const u32x4*>(stage + 2 * C::TILE_BYTES + dt * 32 * 128 +
+                                               (tr_a0 ^ (uint32_t)(ks << 5)));
         dqT[dt] = mfma32(as_bf16x8(ka), as_bf16x8(bs), dqT[dt]);
       }
     }
   };
 
-  issue(0);
-  for (int t = 0; t < n_tiles; ++t) {  // two-stage ring, one barrier per tile
-    wait_vmcnt<0>();
+  for (int t = 0; t < NST - 1 && t < n_tiles; ++t) issue(t);
+  for (int t = 0; t < n_tiles; ++t) {  // NST-stage ring, one barrier per tile, as in dkv_kernel
+    const int ahead = min(NST - 2, n_tiles - 1 - t);
+    if (NST >= 4 && ahead >= 2)
+      wait_vmcnt<2 * PER_ISSUE>();
+    else if (NST >= 3 && ahead >= 1)
+      wait_vmcnt<PER_ISSUE>();
+    else
+      wait_vmcnt<0>();
     lds_barrier();
-    if (t + 1 < n_tiles) issue(t + 1);
+    if (t + NST - 1 < n_tiles) issue(t + NST - 1);
     compute(t);
   }
 
@@ -564,7 +592,7 @@ __global__ __launch_bounds__(64 * QW) void dq_kernel(const AttnBwdArgs a) {
 
 size_t attn_bwd_ws_bytes(int64_t seq_len, int64_t chunk_len, int32_t n_heads, int32_t kv_heads, int32_t head_dim) {
   const int64_t n_kv_tiles = (seq_len + 63) / 64, tpc = (chunk_len + 63) / 64;
-  const size_t kt = (size_t)kv_heads * n_kv_tiles * head_dim * 64 * 2;
+  const size_t kt = attn_bwd_stages_kt(head_dim) ? (size_t)kv_heads * n_kv_tiles * head_dim * 64 * 2 : 0;
   const size_t qt = attn_bwd_stages_qt(head_dim) ? (size_t)2 * n_heads * tpc * head_dim * 64 * 2 : 0;
   const size_t stats = (size_t)2 * n_heads * tpc * 256 * 4;
   return kt + 2 * qt + stats;
@@ -582,7 +610,8 @@ hipError_t launch_attention_backward(const AttnBwdArgs& a, hipStream_t stream) {
       hipLaunchKernelGGL(bwd_stats_kernel<64>, grid, dim3(64), 0, stream, a);
     if ((e = hipGetLastError()) != hipSuccess) return e;
   }
-  if ((e = launch_vt_tiles(a.k, a.seq_len, a.kv_ld, a.kv_heads, HD, a.kt, a.n_kv_tiles, stream)) != hipSuccess)
+  if (attn_bwd_stages_kt(HD) &&
+      (e = launch_vt_tiles(a.k, a.seq_len, a.kv_ld, a.kv_heads, HD, a.kt, a.n_kv_tiles, stream)) != hipSuccess)
     return e;
   const size_t chunk_tiles = (size_t)H * a.tpc * HD * 64;
   for (int c = 0; c < 2 && attn_bwd_stages_qt(HD); ++c) {

@@ -161,6 +161,8 @@ struct AttnBwdArgs {
 // 64) rather than reading the row-major Q and dO tiles with transposing LDS
 // reads (head_dim 128); the workspace holds those tiles only in the first case.
 constexpr bool attn_bwd_stages_qt(int head_dim) { return head_dim != 128; }
+// Likewise for the dQ kernel's K^T tiles.
+constexpr bool attn_bwd_stages_kt(int head_dim) { return head_dim != 128; }
 size_t attn_bwd_ws_bytes(int64_t seq_len, int64_t chunk_len, int32_t n_heads, int32_t kv_heads, int32_t head_dim);
 
 // Pre-passes (stats, K^T, Q^T, dO^T tiles), then the dK/dV and dQ kernels.

@@ -444,11 +444,13 @@ tsp_status run_attn_backward(const tsp_plan* plan, const tsp_dims* dims, int32_t
   a.kv_ld = kv_heads * dims->head_dim;
   a.n_kv_tiles = (plan->seq_len + 63) / 64;
   a.tpc = (plan->chunk_len + 63) / 64;
-  // workspace: K^T tiles, Q^T tiles, dO^T tiles (head_dim 64 only), stats
-  // (each size a multiple of 1 KB)
+  // workspace: K^T tiles, Q^T tiles, dO^T tiles (these three at head_dim 64
+  // only), stats (each size a multiple of 1 KB)
   uint8_t* w = static_cast<uint8_t*>(workspace);
-  a.kt = reinterpret_cast<uint16_t*>(w);
-  w += (size_t)kv_heads * a.n_kv_tiles * dims->head_dim * 64 * 2;
+  if (attn_bwd_stages_kt(dims->head_dim)) {
+    a.kt = reinterpret_cast<uint16_t*>(w);
+    w += (size_t)kv_heads * a.n_kv_tiles * dims->head_dim * 64 * 2;
+  }
   if (attn_bwd_stages_qt(dims->head_dim)) {
     a.qt = reinterpret_cast<uint16_t*>(w);
     w += (size_t)2 * dims->n_heads * a.tpc * dims->head_dim * 64 * 2;

@@ -196,8 +196,8 @@ tsp_status tsp_attn_core_lse(const tsp_plan* plan, const tsp_dims* dims, const u
  *   dq       : device, fp32 [n_local x hidden], out.
  *   dk_full, dv_full : device, fp32 [seq_len x hidden], out (every row written).
  *   workspace: device, >= tsp_workspace_size(n_local, dims, D, TSP_WS_ATTN_BWD)
- *              bytes (transposed tiles of k_full, and of q and d_attn at
- *              head_dim 64; per-row stats).
+ *              bytes (per-row stats; at head_dim 64 also transposed tiles of
+ *              k_full, q and d_attn).
  * P is rebuilt from the scores and lse; P and dS enter the products as bf16,
  * accumulation is fp32.  Errors: as tsp_attn_core, plus TSP_ERR_INVALID_ARG
  * when two of dq, dk_full, dv_full are the same buffer.

@@ -361,10 +361,9 @@ def test_attn_backward_rejects(L):
     # K^T tiles of the sequence, Q^T and dO^T tiles of both chunks, 1 KB of stats per 64-query tile
     tiles_c = -(-C // 64)
     assert need == 4 * (S // 64) * 64 * 64 * 2 + 2 * (2 * 4 * tiles_c * 64 * 64 * 2) + 2 * 4 * tiles_c * 1024
-    # head_dim 128: Q^T and dO^T come from transposing LDS reads, so no tiles of them
+    # head_dim 128: K^T, Q^T and dO^T come from transposing LDS reads, so only the stats
     d128 = tsp.make_dims(512, 4, 128, 1024)
-    assert tsp.workspace_size(n, d128, 4, tsp.WS_ATTN_BWD) == \
-        4 * (S // 64) * 128 * 64 * 2 + 2 * 4 * tiles_c * 1024
+    assert tsp.workspace_size(n, d128, 4, tsp.WS_ATTN_BWD) == 2 * 4 * tiles_c * 1024
     lse = lambda **k: L.tsp_attn_core_lse(ctypes.byref(p), ctypes.byref(d), A, A + 64, A + 128, k.get("out", A + 192),
                                           None, k.get("lse", A + 512), A + 1024,
                                           tsp.workspace_size(n, d, 4, tsp.WS_CORE), None)
