@@ -23,6 +23,11 @@ ARCH = "gfx950"
 HIP_FLAGS = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}",
              "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
              "-I", os.path.join(ROOT, "include"), "-I", CSRC]
+# Per-file additions.  The attention backward's dK/dV kernel runs one wave per
+# SIMD; by default its MFMA results land in AGPRs and are copied to VGPRs for
+# the vector work (112 copies per tile).  Selecting the VGPR form of the MFMAs
+# keeps the scores and dK/dV accumulators in VGPRs (47 copies left).
+FILE_FLAGS = {"attn_backward.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
 
 
 def hipcc() -> str:
@@ -40,7 +45,7 @@ def build(verbose: bool = False) -> str:
         for src in SOURCES:
             obj = os.path.join(tmp, src + ".o")
             lang = ["-x", "hip"]
-            cmds.append([cc, *lang, *HIP_FLAGS, "-c", os.path.join(CSRC, src), "-o", obj])
+            cmds.append([cc, *lang, *HIP_FLAGS, *FILE_FLAGS.get(src, []), "-c", os.path.join(CSRC, src), "-o", obj])
             objs.append(obj)
 
         def run(cmd):

@@ -34,6 +34,9 @@
 //     head_dim 128 by transposing reads of the K tile, at 64 a pre-transposed
 //     tile).
 //     Lane = query, so the normaliser and delta are per-lane scalars.
+//
+// Built with the VGPR form of the MFMAs selected (-mllvm
+// -amdgpu-mfma-vgpr-form, set for this file only by the build).
 #include "device_common.h"
 #include "kernels.h"
 
