@@ -186,9 +186,19 @@ __global__ __launch_bounds__(64 * BW) void dkv_kernel(const AttnBwdArgs a) {
   const int f0 = first_tile(a.chunk_start0), f1 = first_tile(a.chunk_start1);
   const int n0 = tpc - f0, n_head = n0 + tpc - f1;  // tiles per query head
   const int n_all = n_head * group;
+  // Of those, the first d0 (d1) of chunk 0 (1) hold a query before the
+  // block's last key, so they need the causal mask; the rest do not.
+  auto diag_tiles = [&](int64_t start, int f, int n) -> int {
+    const int64_t span = kb0 + 127 - start;  // tiles t with start + 64 t < kb0 + 127
+    const int64_t t_end = span > 0 ? (span + 63) / 64 : 0;
+    return (int)min(max(t_end - f, (int64_t)0), (int64_t)n);
+  };
+  const int d0 = diag_tiles(a.chunk_start0, f0, n0), d1 = diag_tiles(a.chunk_start1, f1, tpc - f1);
+  const int nd_head = d0 + d1, nr_head = n_head - nd_head;
+  const int n_diag = nd_head * group;
 
   // DMA sources.  Row-major tiles: instruction j of wave w fills 1 KB block
-  // b = j*BW + w, row b*RPL + lane/NCH, logical chunk (lane % NCH) ^ (row % NCH).
+  // b = j*BW + w, row b*RPL + lane/NCH, logical chunk (lane % NCH) ^ swizzle(row).
   // Transposed tiles: row d = b*8 + lane/8 (128 bytes), chunk (lane % 8) ^ ((d/2) % 8).
   // Row-major chunk swizzle.  With transposing reads (head_dim 128, 16 chunks
   // a row) the two 2-bit fields of the row's low nibble, swapped: 16
@@ -209,17 +219,31 @@ __global__ __launch_bounds__(64 * BW) void dkv_kernel(const AttnBwdArgs a) {
     tr_off[j] = d * 64 + ((lane % 8) ^ ((d >> 1) & 7)) * 8;
   }
 
-  // tile i: query head kvh*group + i / n_head, then chunk 0's tiles, chunk 1's
+  // tile i: first the masked tiles (per query head: chunk 0's, chunk 1's),
+  // then the others in the same order
   auto tile_of = [&](int i, int& c, int& t, int& qh) __attribute__((always_inline)) {
-    const int gi = i / n_head;
-    const int j = i - gi * n_head;
+    int gi, j, m0, s0, s1;
+    if (i < n_diag) {
+      gi = i / nd_head;
+      j = i - gi * nd_head;
+      m0 = d0;
+      s0 = f0;
+      s1 = f1;
+    } else {
+      const int r = i - n_diag;
+      gi = r / nr_head;
+      j = r - gi * nr_head;
+      m0 = n0 - d0;
+      s0 = f0 + d0;
+      s1 = f1 + d1;
+    }
     qh = kvh * group + gi;
-    if (j < n0) {
+    if (j < m0) {
       c = 0;
-      t = f0 + j;
+      t = s0 + j;
     } else {
       c = 1;
-      t = f1 + (j - n0);
+      t = s1 + (j - m0);
     }
   };
 
@@ -270,14 +294,16 @@ __global__ __launch_bounds__(64 * BW) void dkv_kernel(const AttnBwdArgs a) {
   // step ahead; the exponentials and dS of queries 0..31 run under the S/dP
   // MFMAs of queries 32..63, those of queries 32..63 under the first half of
   // the dV/dK MFMAs (which need only queries 0..31).
-  auto compute = [&](int i) __attribute__((always_inline)) {
+  auto compute = [&](int i, auto masked) __attribute__((always_inline)) {
+    constexpr bool MASKED = decltype(masked)::value;
     int c, t, qh;
     tile_of(i, c, t, qh);
     const int64_t qp0 = (c ? a.chunk_start1 : a.chunk_start0) + (int64_t)t * 64;  // position of query 0
     // (tiles whose queries all precede the wave's keys are computed too, the
     // mask zeroes them: a wave-uniform skip here splits the accumulators' live
     // ranges and costs register copies on every tile)
-    // queries of the tile before this lane's key are masked: offsets below qmin
+    // queries of the tile before this lane's key are masked (MASKED tiles
+    // only): offsets below qmin
     const int qmin = kw0 + 31 > qp0 ? (int)min(max(key - qp0, (int64_t)0), (int64_t)64) : 0;
     const uint8_t* stage = smem + (i % NST) * STAGE;
     const uint8_t* q_st = stage;
@@ -313,7 +339,7 @@ __global__ __launch_bounds__(64 * BW) void dkv_kernel(const AttnBwdArgs a) {
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
         p[j] = __builtin_amdgcn_exp2f(sv[4 * g + j] * scale_log2);
-        p[j] = q0 + j < qmin ? 0.0f : p[j];
+        if constexpr (MASKED) p[j] = q0 + j < qmin ? 0.0f : p[j];
         ds[j] = p[j] * dpv[4 * g + j];
       }
       const int idx = 8 * mb + 2 * g;  // ks = 2*mb + g/2, pair 2*(g%2) + 0/1
@@ -384,7 +410,7 @@ __global__ __launch_bounds__(64 * BW) void dkv_kernel(const AttnBwdArgs a) {
   // there right after it, and land during the compute of tiles i..i+NST-2.
   // The wait leaves the loads of the tiles issued after tile i in flight.
   for (int i = 0; i < NST - 1 && i < n_all; ++i) issue(i);
-  for (int i = 0; i < n_all; ++i) {
+  auto step = [&](int i, auto masked) __attribute__((always_inline)) {
     const int ahead = min(NST - 2, n_all - 1 - i);  // tiles issued after tile i
     if (NST >= 4 && ahead >= 2)
       wait_vmcnt<2 * PER_ISSUE>();
@@ -394,8 +420,13 @@ __global__ __launch_bounds__(64 * BW) void dkv_kernel(const AttnBwdArgs a) {
       wait_vmcnt<0>();
     lds_barrier();
     if (i + NST - 1 < n_all) issue(i + NST - 1);
-    compute(i);
-  }
+    compute(i, masked);
+  };
+  // two loops, so that the unmasked one carries no mask code (a branch per
+  // tile would split the accumulators' live ranges)
+  int i = 0;
+  for (; i < n_diag; ++i) step(i, std::true_type{});
+  for (; i < n_all; ++i) step(i, std::false_type{});
 
   // store this lane's key row of dK (scaled) and dV; zeros where no query sees the key
   if (key < S) {
