@@ -485,7 +485,6 @@ __global__ __launch_bounds__(64 * QW) void dq_kernel(const AttnBwdArgs a) {
   const int64_t qpos = pos0 + qi;
   const int wave_first = wave * 32;
   const bool wave_active = wave_first < valid;
-  const int64_t wave_min_pos = pos0 + wave_first;
   const int64_t wave_max_pos = pos0 + min(wave_first + 31, valid - 1);
   const int wave_tiles = wave_active ? (int)(wave_max_pos / 64) + 1 : 0;
 
@@ -551,11 +550,11 @@ __global__ __launch_bounds__(64 * QW) void dq_kernel(const AttnBwdArgs a) {
 #pragma unroll
   for (int dt = 0; dt < C::DT; ++dt) dqT[dt] = f32x16{};
 
-  auto compute = [&](int t) __attribute__((always_inline)) {
+  auto compute = [&](int t, auto masked) __attribute__((always_inline)) {
+    constexpr bool MASKED = decltype(masked)::value;
     if (t >= wave_tiles) return;  // wave-uniform
     const uint8_t* stage = smem + (t % NST) * STAGE;
     const int64_t k0 = (int64_t)t * 64;
-    const bool need_mask = k0 + 63 > wave_min_pos;
     uint32_t ps[16];
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb) {
@@ -573,10 +572,10 @@ __global__ __launch_bounds__(64 * QW) void dq_kernel(const AttnBwdArgs a) {
       for (int e = 0; e < 16; e += 2) {
         float p0 = __builtin_amdgcn_exp2f(fmaf(s[e], scale_log2, -l2q));
         float p1 = __builtin_amdgcn_exp2f(fmaf(s[e + 1], scale_log2, -l2q));
-        if (need_mask) {
+        if constexpr (MASKED) {
           const int64_t kx = k0 + 32 * kb + 8 * (e >> 2) + 4 * half + (e & 3);
-          if (kx > qpos) p0 = 0.0f;
-          if (kx + 1 > qpos) p1 = 0.0f;
+          p0 = kx > qpos ? 0.0f : p0;
+          p1 = kx + 1 > qpos ? 0.0f : p1;
         }
         ps[8 * kb + e / 2] = pack_bf16x2(p0 * (dp[e] - dlq), p1 * (dp[e + 1] - dlq));
       }
@@ -598,7 +597,8 @@ __global__ __launch_bounds__(64 * QW) void dq_kernel(const AttnBwdArgs a) {
   };
 
   for (int t = 0; t < NST - 1 && t < n_tiles; ++t) issue(t);
-  for (int t = 0; t < n_tiles; ++t) {  // NST-stage ring, one barrier per tile, as in dkv_kernel
+  auto step = [&](int t, auto masked) __attribute__((always_inline)) {
+    // NST-stage ring, one barrier per tile, as in dkv_kernel
     const int ahead = min(NST - 2, n_tiles - 1 - t);
     if (NST >= 4 && ahead >= 2)
       wait_vmcnt<2 * PER_ISSUE>();
@@ -608,8 +608,14 @@ __global__ __launch_bounds__(64 * QW) void dq_kernel(const AttnBwdArgs a) {
       wait_vmcnt<0>();
     lds_barrier();
     if (t + NST - 1 < n_tiles) issue(t + NST - 1);
-    compute(t);
-  }
+    compute(t, masked);
+  };
+  // key tiles wholly at or before the first query need no mask: a loop of
+  // their own, then the masked tail (as in dkv_kernel)
+  const int t_m = (int)min((int64_t)n_tiles, (pos0 + 1) / 64);
+  int t = 0;
+  for (; t < t_m; ++t) step(t, std::false_type{});
+  for (; t < n_tiles; ++t) step(t, std::true_type{});
 
   if (wave_active && wave_first + ql < valid) {
     float* dqp = a.dq + (row0 + wave_first + ql) * ld + hcol + 4 * half;
