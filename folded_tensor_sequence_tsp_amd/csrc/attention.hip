@@ -366,7 +366,7 @@ __global__ __launch_bounds__(NTHREADS) void attn_kernel(const AttnArgs a) {
   // exponentials and PV of tile t, then the mask and max of tile t+1 under the
   // PV MFMAs); last, issue the loads of tile t+NSTAGE-1 (issued after the
   // compute, the loads do not hold up the wave's MFMAs).
-  auto step = [&](int t, f32x16 (&s_cu)[2], f32x16 (&s_nx)[2], float& mt) __attribute__((always_inline)) {
+  auto step = [&](int t, f32x16 (&s_cu)[2], f32x16 (&s_nx)[2], float& mt, auto masked) __attribute__((always_inline)) {
     if (t + 1 < t_end) {
       if (t + 2 < t_end)
         wait_vmcnt<C::LOADS>();
@@ -388,9 +388,11 @@ __global__ __launch_bounds__(NTHREADS) void attn_kernel(const AttnArgs a) {
       fused_block(t, s_cu, s_nx, mt);
       // tile t+1 crosses the wave's diagonal (rare): mask it and take its max
       // again (the block's max is of the unmasked scores)
-      if ((int64_t)(t + 1) * BKV + BKV - 1 > wave_min_pos) {  // wave-uniform
-        mask_tile(t + 1, s_nx);
-        mt = tile_max(s_nx);
+      if constexpr (decltype(masked)::value) {
+        if ((int64_t)(t + 1) * BKV + BKV - 1 > wave_min_pos) {  // wave-uniform
+          mask_tile(t + 1, s_nx);
+          mt = tile_max(s_nx);
+        }
       }
     }
     if (t + NSTAGE - 1 < t_end) issue_tile(t + NSTAGE - 1);
@@ -414,9 +416,19 @@ __global__ __launch_bounds__(NTHREADS) void attn_kernel(const AttnArgs a) {
     mask_tile(t_begin, sA);
     mt = tile_max(sA);
   }
-  for (int t = t_begin; t < t_end; t += 2) {
-    step(t, sA, sB, mt);
-    if (t + 1 < t_end) step(t + 1, sB, sA, mt);
+  // Steps whose next tiles lie wholly at or before the workgroup's first
+  // query carry no mask code (a wave-uniform branch there is if-converted by
+  // the compiler into selects on every step); the rest, the diagonal tail,
+  // mask.  Pairs keep the two score buffers' roles.
+  const int t_m = (int)((pos0 + 1) / BKV);  // first tile that some wave masks
+  int t = t_begin;
+  for (; t + 1 < t_end && t + 2 < t_m; t += 2) {
+    step(t, sA, sB, mt, std::false_type{});
+    step(t + 1, sB, sA, mt, std::false_type{});
+  }
+  for (; t < t_end; t += 2) {
+    step(t, sA, sB, mt, std::true_type{});
+    if (t + 1 < t_end) step(t + 1, sB, sA, mt, std::true_type{});
   }
   wait_vmcnt<0>();
 
