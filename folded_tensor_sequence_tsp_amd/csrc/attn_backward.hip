@@ -556,42 +556,79 @@ __global__ __launch_bounds__(64 * QW) void dq_kernel(const AttnBwdArgs a) {
     const uint8_t* stage = smem + (t % NST) * STAGE;
     const int64_t k0 = (int64_t)t * 64;
     uint32_t ps[16];
+    // dS of entries 4g..4g+3 of key block kb: keys k0 + 32 kb + 8 g + 4 half + 0..3
+    auto group = [&](const f32x16& sv, const f32x16& dpv, int kb, int g) __attribute__((always_inline)) {
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb) {
-      f32x16 s = f32x16{}, dp = f32x16{};
-#pragma unroll
-      for (int kk = 0; kk < C::KK; ++kk) {
-        const uint32_t ad = kb * 32 * (HD * 2) + (rm_a0 ^ (uint32_t)(kk << 5));
-        const u32x4 ka = *reinterpret_cast<const u32x4*>(stage + ad);
-        const u32x4 va = *reinterpret_cast<const u32x4*>(stage + C::TILE_BYTES + ad);
-        s = mfma32(as_bf16x8(ka), as_bf16x8(qf[kk]), s);
-        dp = mfma32(as_bf16x8(va), as_bf16x8(df[kk]), dp);
-      }
-      // entry e: key k0 + 32*kb + 8*(e/4) + 4*half + e%4, query = this lane's
-#pragma unroll
-      for (int e = 0; e < 16; e += 2) {
-        float p0 = __builtin_amdgcn_exp2f(fmaf(s[e], scale_log2, -l2q));
-        float p1 = __builtin_amdgcn_exp2f(fmaf(s[e + 1], scale_log2, -l2q));
+      for (int e = 4 * g; e < 4 * g + 4; e += 2) {
+        float p0 = __builtin_amdgcn_exp2f(fmaf(sv[e], scale_log2, -l2q));
+        float p1 = __builtin_amdgcn_exp2f(fmaf(sv[e + 1], scale_log2, -l2q));
         if constexpr (MASKED) {
           const int64_t kx = k0 + 32 * kb + 8 * (e >> 2) + 4 * half + (e & 3);
           p0 = kx > qpos ? 0.0f : p0;
           p1 = kx + 1 > qpos ? 0.0f : p1;
         }
-        ps[8 * kb + e / 2] = pack_bf16x2(p0 * (dp[e] - dlq), p1 * (dp[e + 1] - dlq));
+        ps[8 * kb + e / 2] = pack_bf16x2(p0 * (dpv[e] - dlq), p1 * (dpv[e + 1] - dlq));
       }
+    };
+    auto kv = [&](int kb, int kk, u32x4& ka, u32x4& va) __attribute__((always_inline)) {
+      const uint32_t ad = kb * 32 * (HD * 2) + (rm_a0 ^ (uint32_t)(kk << 5));
+      ka = *reinterpret_cast<const u32x4*>(stage + ad);
+      va = *reinterpret_cast<const u32x4*>(stage + C::TILE_BYTES + ad);
+    };
+    auto kt = [&](int dt, int ks) __attribute__((always_inline)) {
+      if constexpr (TR)
+        return tr_read_frag(stage, tr_b, dt, ks);
+      else
+        return *reinterpret_cast<const u32x4*>(stage + 2 * C::TILE_BYTES + dt * 32 * 128 +
+                                               (tr_a0 ^ (uint32_t)(ks << 5)));
+    };
+    // Software pipeline (as in dkv_kernel): fragments one MFMA step ahead; dS
+    // of key block 0 under the S/dP MFMAs of block 1, dS of block 1 under the
+    // dQ MFMAs of the first two 16-key steps (which need only block 0).
+    constexpr int G2 = C::KK / 4, G3 = C::DT / 2;
+    f32x16 s0 = f32x16{}, d0 = f32x16{}, s1 = f32x16{}, d1 = f32x16{};
+    u32x4 ka, va;
+    kv(0, 0, ka, va);
+#pragma unroll
+    for (int kk = 0; kk < C::KK; ++kk) {
+      u32x4 kn, vn;
+      if (kk + 1 < C::KK)
+        kv(0, kk + 1, kn, vn);
+      else
+        kv(1, 0, kn, vn);
+      s0 = mfma32(as_bf16x8(ka), as_bf16x8(qf[kk]), s0);
+      d0 = mfma32(as_bf16x8(va), as_bf16x8(df[kk]), d0);
+      __builtin_amdgcn_sched_barrier(0);
+      ka = kn;
+      va = vn;
     }
+#pragma unroll
+    for (int kk = 0; kk < C::KK; ++kk) {
+      u32x4 kn = ka, vn = va;
+      if (kk + 1 < C::KK) kv(1, kk + 1, kn, vn);
+      s1 = mfma32(as_bf16x8(ka), as_bf16x8(qf[kk]), s1);
+      d1 = mfma32(as_bf16x8(va), as_bf16x8(df[kk]), d1);
+      if ((kk + 1) % G2 == 0) group(s0, d0, 0, (kk + 1) / G2 - 1);
+      __builtin_amdgcn_sched_barrier(0);
+      ka = kn;
+      va = vn;
+    }
+    u32x4 ta = kt(0, 0);
 #pragma unroll
     for (int ks = 0; ks < 4; ++ks) {
       const u32x4 bs = u32x4{ps[4 * ks], ps[4 * ks + 1], ps[4 * ks + 2], ps[4 * ks + 3]};
 #pragma unroll
       for (int dt = 0; dt < C::DT; ++dt) {
-        u32x4 ka;
-        if constexpr (TR)
-          ka = tr_read_frag(stage, tr_b, dt, ks);
-        else
-          ka = *reinterpret_cast<const u32x4*>(stage + 2 * C::TILE_BYTES + dt * 32 * 128 +
-                                               (tr_a0 ^ (uint32_t)(ks << 5)));
-        dqT[dt] = mfma32(as_bf16x8(ka), as_bf16x8(bs), dqT[dt]);
+        u32x4 tn = ta;
+        if (dt + 1 < C::DT)
+          tn = kt(dt + 1, ks);
+        else if (ks + 1 < 4)
+          tn = kt(0, ks + 1);
+        dqT[dt] = mfma32(as_bf16x8(ta), as_bf16x8(bs), dqT[dt]);
+        const int stp = ks * C::DT + dt;
+        if (ks < 2 && (stp + 1) % G3 == 0) group(s1, d1, 1, (stp + 1) / G3 - 1);
+        __builtin_amdgcn_sched_barrier(0);
+        ta = tn;
       }
     }
   };
