@@ -70,24 +70,28 @@ struct BCfg {
   static constexpr float INV_SQRT_HD = HD == 128 ? 0.08838834764831844055f : 0.125f;
 };
 
-// ---- stats: per (64-query tile, chunk, head), thread r = query row of the tile.
+// ---- stats: per (64-query tile, chunk, head); four waves of 16 rows, HD / 8
+// lanes per row (16-byte loads along the row, so a wave reads whole 2 HD-byte
+// row slices), the row's delta summed over those lanes with shuffles.
 template <int HD>
-__global__ __launch_bounds__(64) void bwd_stats_kernel(const AttnBwdArgs a) {
+__global__ __launch_bounds__(256) void bwd_stats_kernel(const AttnBwdArgs a) {
+  constexpr int LPR = HD / 8, RPP = 64 / LPR;  // lanes per row, rows per pass
   const int t = blockIdx.x, c = blockIdx.y, head = blockIdx.z;
-  const int r = threadIdx.x;
-  const int64_t row_in_chunk = (int64_t)t * 64 + r;
-  // padding rows: a normaliser so large that every probability is exp2(-2^16) = 0
-  // (finite, so that it can be split into bf16 parts)
-  float l2 = PAD_LSE2, dl = 0.0f;
-  if (row_in_chunk < a.chunk_len) {
-    const int64_t row = c * a.chunk_len + row_in_chunk;
-    l2 = a.lse[(int64_t)head * 2 * a.chunk_len + row] * LOG2E;
-    const int64_t off = row * a.hidden + head * HD;
-    for (int d = 0; d < HD; d += 8) {
-      const u32x4 g = *reinterpret_cast<const u32x4*>(a.dout + off + d);
-      const u32x4 o = *reinterpret_cast<const u32x4*>(a.o + off + d);
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int sub = lane % LPR;
+  float* st = a.stats + ((c * (int64_t)a.n_heads + head) * a.tpc + t) * 256;
+#pragma unroll
+  for (int pass = 0; pass < 16 / RPP; ++pass) {
+    const int r = wave * 16 + pass * RPP + lane / LPR;  // query row of the tile
+    const int64_t row_in_chunk = (int64_t)t * 64 + r;
+    const bool valid = row_in_chunk < a.chunk_len;
+    float dl = 0.0f;
+    if (valid) {
+      const int64_t off = (c * a.chunk_len + row_in_chunk) * a.hidden + head * HD + 8 * sub;
+      const u32x4 g = *reinterpret_cast<const u32x4*>(a.dout + off);
+      const u32x4 o = *reinterpret_cast<const u32x4*>(a.o + off);
       u32x4 lo = u32x4{0u, 0u, 0u, 0u};
-      if (a.o_lo) lo = *reinterpret_cast<const u32x4*>(a.o_lo + off + d);
+      if (a.o_lo) lo = *reinterpret_cast<const u32x4*>(a.o_lo + off);
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
         const float o0 = __uint_as_float(o[j] << 16) + __uint_as_float(lo[j] << 16);
@@ -96,12 +100,19 @@ __global__ __launch_bounds__(64) void bwd_stats_kernel(const AttnBwdArgs a) {
         dl = fmaf(__uint_as_float(g[j] & 0xffff0000u), o1, dl);
       }
     }
+#pragma unroll
+    for (int m = 1; m < LPR; m <<= 1) dl += __shfl_xor(dl, m);
+    if (sub == 0) {
+      // padding rows: a normaliser so large that every probability is
+      // exp2(-2^16) = 0 (finite, so that it can be split into bf16 parts)
+      const float l2 = valid ? a.lse[(int64_t)head * 2 * a.chunk_len + c * a.chunk_len + row_in_chunk] * LOG2E
+                             : PAD_LSE2;
+      st[r] = l2;
+      st[64 + r] = dl;
+      st[128 + r] = 0.0f;
+      st[192 + r] = 0.0f;
+    }
   }
-  float* st = a.stats + ((c * (int64_t)a.n_heads + head) * a.tpc + t) * 256;
-  st[r] = l2;
-  st[64 + r] = dl;
-  st[128 + r] = 0.0f;
-  st[192 + r] = 0.0f;
 }
 
 // Transposing reads of a row-major 64-row tile of head_dim 128 (256-byte
@@ -682,9 +693,9 @@ hipError_t launch_attention_backward(const AttnBwdArgs& a, hipStream_t stream) {
   {
     const dim3 grid((unsigned)a.tpc, 2, (unsigned)H);
     if (HD == 128)
-      hipLaunchKernelGGL(bwd_stats_kernel<128>, grid, dim3(64), 0, stream, a);
+      hipLaunchKernelGGL(bwd_stats_kernel<128>, grid, dim3(256), 0, stream, a);
     else
-      hipLaunchKernelGGL(bwd_stats_kernel<64>, grid, dim3(64), 0, stream, a);
+      hipLaunchKernelGGL(bwd_stats_kernel<64>, grid, dim3(256), 0, stream, a);
     if ((e = hipGetLastError()) != hipSuccess) return e;
   }
   if (attn_bwd_stages_kt(HD) &&
