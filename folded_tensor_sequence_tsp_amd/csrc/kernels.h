@@ -146,9 +146,10 @@ struct AttnBwdArgs {
   // K/V heads (n_heads for MHA; grouped-query: query head a reads K/V head
   // a / (n_heads / kv_heads)) and the row stride of k, v, dk, dv.
   int32_t kv_heads, kv_ld;
-  // workspace: K^T tiles [H_kv][n_kv_tiles][hd][64]; Q^T and dO^T tiles
-  // [2 chunks][H][tpc][hd][64]; per 64-query tile of (chunk, head) 256 floats:
-  // log2-domain normaliser [64], delta = rowsum(dO * O) [64], zeros [128].
+  // workspace (kt, qt, dot at head_dim 64 only; null otherwise): K^T tiles
+  // [H_kv][n_kv_tiles][hd][64]; Q^T and dO^T tiles [2 chunks][H][tpc][hd][64];
+  // per 64-query tile of (chunk, head) 256 floats: log2-domain normaliser
+  // [64], delta = rowsum(dO * O) [64], zeros [128].
   uint16_t* kt;
   uint16_t* qt;
   uint16_t* dot;
@@ -156,16 +157,16 @@ struct AttnBwdArgs {
   int64_t n_kv_tiles, tpc;  // 64-key tiles of the sequence; 64-query tiles per chunk
 };
 
-// Workspace bytes of launch_attention_backward.
 // Whether the dK/dV kernel streams pre-transposed Q^T and dO^T tiles (head_dim
 // 64) rather than reading the row-major Q and dO tiles with transposing LDS
 // reads (head_dim 128); the workspace holds those tiles only in the first case.
 constexpr bool attn_bwd_stages_qt(int head_dim) { return head_dim != 128; }
 // Likewise for the dQ kernel's K^T tiles.
 constexpr bool attn_bwd_stages_kt(int head_dim) { return head_dim != 128; }
+// Workspace bytes of launch_attention_backward.
 size_t attn_bwd_ws_bytes(int64_t seq_len, int64_t chunk_len, int32_t n_heads, int32_t kv_heads, int32_t head_dim);
 
-// Pre-passes (stats, K^T, Q^T, dO^T tiles), then the dK/dV and dQ kernels.
+// Pre-passes (stats; K^T, Q^T, dO^T tiles at head_dim 64), then the dK/dV and dQ kernels.
 hipError_t launch_attention_backward(const AttnBwdArgs& args, hipStream_t stream);
 
 // y = x / sqrt(mean(x^2) + eps) * gain per row of x [n x h] (bf16; h % 8 == 0).
