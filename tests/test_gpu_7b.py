@@ -8,13 +8,18 @@ of a GEMM or of attention is independent given its inputs).
     generated gathered K/V (the rank's own rows replaced by its projections);
   * whole layer at S=16384 (2048 local tokens, rank 0), generated K/V.
 
-Sampled rows always include the first and last row of each zigzag chunk."""
+Sampled rows always include the first and last row of each zigzag chunk.
+
+The gating oracle holds the projection outputs Q, K and V as the bf16 tensors
+the model stores; the attention and layer tests also compare, by relative RMS,
+with the oracle that keeps them unrounded (fp64), which charges the GPU path
+with the bf16 rounding of Q, K and V as well."""
 import pytest
 import torch
 
 from folded_tensor_sequence_tsp_amd import synth, tsp
 from oracle import tsp_oracle as O
-from parity import bf16_nan, check, gpu, require_gpu, say
+from parity import bf16_nan, check, check_rms, gpu, require_gpu, say
 
 pytestmark = gpu
 DEV = "cuda"
@@ -71,6 +76,11 @@ def test_attention_7b_sampled_rows():
     ref, _, k_own, v_own = O.attn_forward(oplan, x.cpu(), [t.cpu() for t in lw.wqkv], [t.cpu() for t in lw.wo],
                                           d.n_heads, d.head_dim, kf_cpu, vf_cpu, residual=False, rows=rows)
     check(out.cpu()[rows], ref, "7B attention + O projection sampled rows")
+    say(f"{W.name}: oracle with unrounded projections")
+    ref_x, _, _, _ = O.attn_forward(oplan, x.cpu(), [t.cpu() for t in lw.wqkv], [t.cpu() for t in lw.wo], d.n_heads,
+                                    d.head_dim, kf_cpu, vf_cpu, residual=False, rows=rows, k_own=k_own, v_own=v_own,
+                                    proj_bf16=False)
+    check_rms(out.cpu()[rows], ref_x, "7B attention + O projection sampled rows, unrounded Q/K/V")
     pos = l2g[rows]
     check(kf.cpu()[pos], k_own[rows], "7B own K rows")
     check(vf.cpu()[pos], v_own[rows], "7B own V rows")
@@ -98,3 +108,7 @@ def test_layer_16k_sampled_rows():
     ref, _, _ = O.layer_forward(O.zigzag_plan(S, D, W.rank), x.cpu(), lc.wqkv, lc.wo, lc.w1, lc.w2, d.n_heads,
                                 d.head_dim, kf_cpu, vf_cpu, rows=rows)
     check(out.cpu()[rows], ref, "16K layer sampled rows")
+    say(f"{W.name}: oracle with unrounded projections")
+    ref_x, _, _ = O.layer_forward(O.zigzag_plan(S, D, W.rank), x.cpu(), lc.wqkv, lc.wo, lc.w1, lc.w2, d.n_heads,
+                                  d.head_dim, kf_cpu, vf_cpu, rows=rows, proj_bf16=False)
+    check_rms(out.cpu()[rows], ref_x, "16K layer sampled rows, unrounded Q/K/V")

@@ -17,7 +17,9 @@ taken from the forward's output, which carries the forward's rounding of P
 (at most as much again): e_t = 2^-9 (1 or 2) sum_d |dO| (P|v|), which reaches
 dq through P|k| e and dk through P^T (e |q|).  Each element is checked against
 twice the sum of these (margin 2), plus 1e-5 of the output's largest magnitude
-for the fp32 accumulation; and the whole against relative RMS <= 5e-3.
+for the fp32 accumulation.  An element passes within the larger of that and
+the forward's bound 1e-2 + 2e-2 |o| (the elements that only the derived bound
+admits are tallied); the whole must meet relative RMS <= 5e-3.
 """
 import math
 
@@ -26,7 +28,7 @@ import torch
 
 from folded_tensor_sequence_tsp_amd import synth, tsp
 from oracle import tsp_oracle as O
-from parity import REL_RMS, bf16_nan, gpu, require_gpu, say
+from parity import bf16_nan, check_within, gpu, require_gpu, say
 
 pytestmark = gpu
 DEV = "cuda"
@@ -57,16 +59,12 @@ def _bounds(q, k, v, do, pos, H, hd, with_lo):
 
 
 def _check(got, ref, bound, name):
-    g = got.detach().cpu().to(F64)
-    assert torch.isfinite(g).all(), f"{name}: non-finite values"
-    err = (g - ref).abs()
+    """Per element |err| <= max(1e-2 + 2e-2 |ref|, 2^-8 bound + 1e-5 max|ref|),
+    relative RMS <= 5e-3; elements only the derived bound admits are tallied."""
     lim = 2.0 ** -8 * bound + 1e-5 * ref.abs().max().item() + 1e-12
-    bad = err > lim
-    assert not bool(bad.any()), (f"{name}: {int(bad.sum())}/{g.numel()} elements beyond the bound; "
-                                 f"worst excess {float((err - lim).max()):.3e}")
-    rr = ((g - ref).norm() / ref.norm().clamp_min(1e-300)).item()
-    assert rr <= REL_RMS, f"{name}: relative RMS {rr:.3e}"
-    say(f"{name}: max err {float(err.max()):.3e}, rel rms {rr:.2e}")
+    st = check_within(got, ref, lim, name)
+    say(f"{name}: max err {st['max_abs']:.3e}, rel rms {st['rel_rms']:.2e}, "
+        f"{st['derived_only']}/{st['n']} admitted by the derived bound only")
 
 
 def _run(S, D, r, H, hd, with_lo, seed):

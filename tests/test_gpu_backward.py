@@ -8,14 +8,16 @@ Tolerances.  dx meets the forward's bound (|err| <= 1e-2 + 2e-2 |o|).  The
 weight gradients sum over all tokens products one of whose factors (dU_d or
 GELU(U_d)) the GPU holds in bf16: one rounding of one operand of a dot product
 bounds its error by 2^-9 sum_k |a_k| |b_k| (the fp32 accumulation adds far
-less), so each element is checked against 2^-8 (|a|^T |b|) (a margin of 2),
-with the oracle's fp64 operands, and the whole against relative RMS <= 5e-3."""
+less).  Each element is checked against the larger of the forward's bound and
+2^-8 (|a|^T |b|) (a margin of 2), with the oracle's fp64 operands; the number
+of elements that only the second admits is tallied.  The whole is checked
+against relative RMS <= 5e-3."""
 import pytest
 import torch
 
 from folded_tensor_sequence_tsp_amd import synth, tsp
 from oracle import tsp_oracle as O
-from parity import REL_RMS, bf16_nan, check, gpu, require_gpu, say
+from parity import bf16_nan, check, check_within, gpu, require_gpu, say
 
 pytestmark = gpu
 DEV = "cuda"
@@ -26,16 +28,11 @@ def _rnd(shape, seed, std=1.0):
 
 
 def check_rounded_product(got, ref, a_abs, b_abs, name):
-    """|got - ref| <= 2^-8 (|a|^T |b|) per element (one bf16 rounding of one
-    operand, margin 2), and relative RMS <= REL_RMS."""
-    g = got.detach().cpu().to(torch.float64)
+    """|got - ref| <= max(1e-2 + 2e-2 |ref|, 2^-8 (|a|^T |b|)) per element (the
+    second: one bf16 rounding of one operand, margin 2), and relative RMS <=
+    REL_RMS; the elements only the derived bound admits are tallied."""
     bound = 2.0 ** -8 * (a_abs @ b_abs) + 1e-9
-    err = (g - ref).abs()
-    bad = err > bound
-    assert torch.isfinite(g).all(), f"{name}: non-finite values"
-    assert not bool(bad.any()), f"{name}: {int(bad.sum())}/{g.numel()} elements beyond the rounding bound"
-    rr = ((g - ref).norm() / ref.norm()).item()
-    assert rr <= REL_RMS, f"{name}: relative RMS {rr:.3e}"
+    check_within(got, ref, bound, name)
 
 
 @pytest.mark.parametrize("h,F,D,n", [(256, 1024, 4, 512), (256, 1024, 4, 300), (512, 2048, 8, 257),

@@ -14,7 +14,7 @@ import torch
 
 from folded_tensor_sequence_tsp_amd import synth, tsp
 from oracle import tsp_oracle as O
-from parity import bf16_nan, check, gpu, require_gpu, say
+from parity import bf16_nan, check, check_rms, gpu, require_gpu, say
 
 pytestmark = gpu
 DEV = "cuda"
@@ -63,6 +63,9 @@ def test_rank_emulation_reassembles_unsharded_layer(D):
     torch.cuda.synchronize()
     ref, _, _ = O.layer_forward(O.zigzag_plan(S, 1, 0), x_all, lw.wqkv, lw.wo, lw.w1, lw.w2, d.n_heads, d.head_dim)
     check(out_all, ref, f"reassembled layer D={D}")
+    ref_x, _, _ = O.layer_forward(O.zigzag_plan(S, 1, 0), x_all, lw.wqkv, lw.wo, lw.w1, lw.w2, d.n_heads, d.head_dim,
+                                  proj_bf16=False)
+    check_rms(out_all, ref_x, f"reassembled layer D={D}, unrounded Q/K/V")
 
 
 def test_tiny_layer_rank1_against_oracle_rank_view():
@@ -97,6 +100,13 @@ def test_tiny_layer_rank1_against_oracle_rank_view():
     ref_h1, _, _, _ = O.attn_forward(oplan, x_all[oplan.local_to_global], lw.wqkv, lw.wo, d.n_heads, d.head_dim,
                                      k_all, v_all, residual=True)
     check(h1, ref_h1, "tiny attention half rank 1")
+    # the same against the oracle that keeps Q, K and V unrounded
+    ref_x, _, _ = O.layer_forward(oplan, x_all[oplan.local_to_global], lw.wqkv, lw.wo, lw.w1, lw.w2, d.n_heads,
+                                  d.head_dim, k_all, v_all, proj_bf16=False)
+    check_rms(out, ref_x, "tiny layer rank 1, unrounded Q/K/V")
+    ref_h1x, _, _, _ = O.attn_forward(oplan, x_all[oplan.local_to_global], lw.wqkv, lw.wo, d.n_heads, d.head_dim,
+                                      k_all, v_all, residual=True, proj_bf16=False)
+    check_rms(h1, ref_h1x, "tiny attention half rank 1, unrounded Q/K/V")
 
 
 def test_layer_zero_weights_is_identity():

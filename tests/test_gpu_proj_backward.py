@@ -15,15 +15,16 @@ fp32; the fp32 gradients dq, dk, dv of the QKV backward are rounded to bf16
 first, which bounds the error of each product by 2^-9 sum |a||b|: the oracle's
 own function on the absolute values gives that sum, and each element is
 checked against 2^-8 of it (margin 2) plus the bf16 rounding of a bf16 output
-(2^-8 |ref|) plus 1e-6 of the largest magnitude; the whole against relative
-RMS <= 5e-3.
+(2^-8 |ref|) plus 1e-6 of the largest magnitude, or against the forward's
+bound 1e-2 + 2e-2 |ref| when that is larger (the elements that only the
+derived bound admits are tallied); the whole against relative RMS <= 5e-3.
 """
 import pytest
 import torch
 
 from folded_tensor_sequence_tsp_amd import synth, tsp
 from oracle import tsp_oracle as O
-from parity import REL_RMS, bf16_nan, check, gpu, require_gpu, say
+from parity import bf16_nan, check, check_within, gpu, require_gpu, say
 
 pytestmark = gpu
 DEV = "cuda"
@@ -40,15 +41,11 @@ def _f32(shape, seed, std=1.0):
 
 
 def _check_bound(got, ref, bound, name, out_bf16=False):
-    g = got.detach().cpu().to(F64)
-    assert torch.isfinite(g).all(), f"{name}: non-finite values"
-    err = (g - ref).abs()
+    """Per element |err| <= max(1e-2 + 2e-2 |ref|, derived), derived = 2^-8 bound
+    (+ 2^-8 |ref| for a bf16 output) + 1e-6 max|ref|; relative RMS <= 5e-3.
+    The elements only the derived bound admits are tallied."""
     lim = 2.0 ** -8 * bound + (2.0 ** -8 * ref.abs() if out_bf16 else 0) + 1e-6 * ref.abs().max().item() + 1e-12
-    bad = err > lim
-    assert not bool(bad.any()), (f"{name}: {int(bad.sum())}/{g.numel()} elements beyond the bound; "
-                                 f"worst excess {float((err - lim).max()):.3e}")
-    rr = ((g - ref).norm() / ref.norm().clamp_min(1e-300)).item()
-    assert rr <= REL_RMS, f"{name}: relative RMS {rr:.3e}"
+    check_within(got, ref, lim, name)
 
 
 def _f32_nan(shape):
