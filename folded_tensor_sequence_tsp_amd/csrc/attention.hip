@@ -14,25 +14,33 @@
 //     so the row max needs a single exchange with lane ^ 32 and row sums stay
 //     per lane until the end;
 //   * O^T = V^T P^T takes the probabilities from the score registers as the B
-//     operand.  V is first rewritten per head as V^T tiles [64-key tile][d][64]
-//     with the keys of each 16-key group in the order the score registers hold
-//     them (vt_prep_kernel), so every lane's 8 keys of a k-step are one 16-byte
-//     LDS read;
-//   * K and V^T tiles of 64 keys stream into a 4-stage LDS ring with direct
-//     global->LDS loads (global_load_lds_dwordx4; no register staging), the 16-
-//     byte chunks of each row XOR-swizzled by the row index so that fragment
-//     reads of 32 rows hit distinct banks of the 64-bank LDS; per tile one
-//     vmcnt wait and one barrier; loads run two to three tiles ahead;
+//     operand.  V stays row-major (as gathered); its A-operand fragments come
+//     from gfx950's transposing LDS reads (ds_read_b64_tr_b16), two per
+//     fragment, with the keys of each 16-key group taken in the order the
+//     score registers hold them;
+//   * K and V tiles of 64 keys stream into a 4-stage LDS ring with direct
+//     buffer->LDS loads (buffer_load_dwordx4 ... lds; no register staging).
+//     The buffer descriptors are rebased per tile in SGPRs, so the per-lane
+//     state is one 32-bit offset per load.  K rows are XOR-swizzled by the row
+//     index (fragment reads of 32 rows hit distinct banks); V rows by the row
+//     index mod 4 (the four rows of one transposing read fall in different
+//     bank ranges).  Per tile one vmcnt wait and one barrier; loads run two to
+//     three tiles ahead;
 //   * software pipeline: the S MFMAs of tile t+1 sit in one basic block with
 //     the exponentials of tile t (all branches are wave-uniform), so matrix
 //     and vector work interleave; the PV MFMAs of tile t then overlap the max
 //     of tile t+1's unmasked scores and the running sum of tile t (kept in that
 //     block); a tile that crosses a wave's diagonal is masked after the block
 //     and its max taken again;
-//   * online softmax in fp32, log2 domain, scale folded into one FMA, hardware
-//     exp2, and lazy rescaling: the running max moves (and O, l are rescaled)
-//     only when a tile's max exceeds it by more than 2^8, so probabilities stay
-//     below 256 and most tiles skip the rescale;
+//   * online softmax in fp32 with the hardware exp2 and lazy rescaling: the
+//     running max moves (and O, l are rescaled) only when a tile's max exceeds
+//     it by more than 2^8 after scaling, so probabilities stay below 256 and
+//     most tiles skip the rescale.  The running max is kept in raw score units
+//     and each exponent is (s - m) * log2(e)/sqrt(hd): the difference is exact
+//     for the scores near the max at any magnitude, so the exponent of the
+//     maximum is exactly 0 even when the scores are so large that their fp32
+//     spacing exceeds the exponent range (activations of a deep stack without
+//     a norm);
 //   * masking only on tiles that cross a wave's diagonal; tiles past a wave's
 //     last query are not computed;
 //   * grouped-query attention: query head a reads K/V head a / (H / H_kv); the
@@ -45,6 +53,9 @@
 //     chunk's see a few tiles, are split in two along the keys: each half
 //     writes its unnormalised output with its running max and sum, and a
 //     combine kernel merges the halves (the same algebra as the lazy rescale).
+//
+// The V^T tile pre-pass (vt_prep_kernel) is kept for the backward kernels,
+// which stage K^T, Q^T and dO^T tiles at head_dim 64.
 #include "device_common.h"
 #include "kernels.h"
 
@@ -53,24 +64,31 @@ namespace {
 
 constexpr int NW = 8;              // waves per workgroup
 constexpr int NTHREADS = 64 * NW;
-constexpr int QT = 32 * NW;        // queries per workgroup
-constexpr int BKV = 64;            // keys per tile
+constexpr int QT = ATTN_QT;        // queries per workgroup (32 per wave)
+constexpr int BKV = ATTN_BKV;      // keys per tile
 constexpr int NSTAGE = 4;          // LDS ring depth
 constexpr float LAZY_TAU = 8.0f;   // rescale threshold (log2 units)
+static_assert(QT == 32 * NW, "one 32-query block per wave");
 
 template <int HD>
 struct ACfg {
-  static constexpr int NCH = HD / 8;              // 16-byte chunks per K row
-  static constexpr int K_BYTES = BKV * HD * 2;    // K tile [64][HD]
-  static constexpr int V_BYTES = HD * BKV * 2;    // V^T tile [HD][64]
+  static constexpr int NCH = HD / 8;              // 16-byte chunks per K or V row
+  static constexpr int ROW_BYTES = HD * 2;
+  static constexpr int K_BYTES = BKV * HD * 2;    // K tile [64][HD], row-major
+  static constexpr int V_BYTES = BKV * HD * 2;    // V tile [64][HD], row-major
   static constexpr int STAGE_BYTES = K_BYTES + V_BYTES;
   static constexpr int K_LOADS = K_BYTES / (NTHREADS * 16);  // DMA instructions per thread per tile
   static constexpr int V_LOADS = V_BYTES / (NTHREADS * 16);
   static constexpr int LOADS = K_LOADS + V_LOADS;
-  static constexpr int K_ROWS_PER_LOAD = 64 / NCH;            // K rows one wave instruction fills
+  static constexpr int ROWS_PER_LOAD = 64 / NCH;              // rows one wave instruction fills (1 KB)
   static constexpr int KK = HD / 16;                          // MFMA k-steps over head_dim
   static constexpr int DT = HD / 32;                          // 32-wide d tiles of O
+  // V rows: the 16-byte chunk c of row r sits at c ^ ((r % 4) << VSH), which
+  // moves the 64-byte (HD 128) or 32-byte (HD 64) pieces of the four rows of a
+  // transposing read to four different bank ranges.
+  static constexpr int VSH = HD == 128 ? 2 : 1;
   static_assert(K_LOADS >= 1 && V_LOADS >= 1, "tile too small for the workgroup");
+  static_assert(HD == 64 || HD == 128, "head_dim 64 or 128");
 };
 
 // Position k (0..15) of a 16-key group of V^T holds key perm(k): bits 2 and 3
@@ -183,58 +201,78 @@ __global__ __launch_bounds__(NTHREADS) void attn_kernel(const AttnArgs a) {
     for (int kk = 0; kk < C::KK; ++kk) qf[kk] = as_bf16x8(*reinterpret_cast<const u32x4*>(qp + kk * 16));
   }
 
-  // ---- direct global->LDS loads.  Instruction i of wave w fills the 1 KB
-  // block (i*NW + w) of a tile region; lane L writes its 16 bytes at L*16.
-  // K: row r of the tile, logical 16-byte chunk (L % NCH) ^ (r % NCH).
-  int k_row[C::K_LOADS];             // K row (key within the tile) this lane fetches
-  int k_col[C::K_LOADS];             // element column within the head (swizzled chunk)
-  const uint16_t* k_src[C::K_LOADS];  // source for tile 0; tile t adds t * 64 rows
+  // ---- direct buffer->LDS loads.  Instruction i of wave w fills the 1 KB
+  // block (i*NW + w) of the K (or V) region of a stage; lane L writes its 16
+  // bytes at L*16: row r = block*ROWS_PER_LOAD + L/NCH, physical chunk L%NCH.
+  // K: logical chunk (L % NCH) ^ (r % NCH).  V: (L % NCH) ^ ((r % 4) << VSH).
+  // The byte offsets are relative to the tile's first key row at the head's
+  // first column (the descriptors' base, rebased per tile).
+  int k_row[C::K_LOADS], k_col[C::K_LOADS], v_row[C::V_LOADS], v_col[C::V_LOADS];
+  uint32_t k_off[C::K_LOADS], v_off[C::V_LOADS];
 #pragma unroll
   for (int i = 0; i < C::K_LOADS; ++i) {
-    const int r = (i * NW + wave) * C::K_ROWS_PER_LOAD + lane / C::NCH;
-    const int p = lane % C::NCH;
+    const int r = (i * NW + wave) * C::ROWS_PER_LOAD + lane / C::NCH;
     k_row[i] = r;
-    k_col[i] = (p ^ (r & (C::NCH - 1))) * 8;
-    k_src[i] = a.k + (int64_t)r * kld + kcol + k_col[i];
+    k_col[i] = ((lane % C::NCH) ^ (r & (C::NCH - 1))) * 8;
+    k_off[i] = (uint32_t)((r * kld + k_col[i]) * 2);
   }
-  // V^T: row d of the tile, logical chunk (L % 8) ^ ((d / 2) % 8).
-  const uint16_t* v_src[C::V_LOADS];
-  {
-    const uint16_t* vt_head = a.vt + (int64_t)kvh * a.n_kv_tiles * HD * 64;
 #pragma unroll
-    for (int i = 0; i < C::V_LOADS; ++i) {
-      const int d = (i * NW + wave) * 8 + lane / 8;
-      const int p = lane % 8;
-      v_src[i] = vt_head + d * 64 + (p ^ ((d >> 1) & 7)) * 8;
-    }
+  for (int i = 0; i < C::V_LOADS; ++i) {
+    const int r = (i * NW + wave) * C::ROWS_PER_LOAD + lane / C::NCH;
+    v_row[i] = r;
+    v_col[i] = ((lane % C::NCH) ^ ((r & 3) << C::VSH)) * 8;
+    v_off[i] = (uint32_t)((r * kld + v_col[i]) * 2);
   }
+  const uint16_t* k_head = a.k + kcol;
+  const uint16_t* v_head = a.v + kcol;
 
   auto issue_tile = [&](int t) __attribute__((always_inline)) {
     uint8_t* stage = smem + (t % NSTAGE) * C::STAGE_BYTES;
     const int64_t k0 = (int64_t)t * BKV;
+    // bytes from the tile's first row (head column) to the end of the sequence
+    const int64_t span = (a.seq_len - k0) * kld * 2 - (int64_t)kcol * 2;
+    const uint32_t bytes = (uint32_t)min(span, (int64_t)0x7fffffff);
+    const __amdgpu_buffer_rsrc_t rk = buffer_rsrc(k_head + k0 * kld, bytes);
+    const __amdgpu_buffer_rsrc_t rv = buffer_rsrc(v_head + k0 * kld, bytes);
     if (k0 + BKV <= key_end) {  // whole tile inside the key range (wave-uniform)
 #pragma unroll
-      for (int i = 0; i < C::K_LOADS; ++i) dma16(k_src[i] + k0 * kld, stage + (i * NW + wave) * 1024);
-    } else {                    // last tile: rows past the range re-read the last key (masked anyway)
+      for (int i = 0; i < C::K_LOADS; ++i) dma16_buf(rk, k_off[i], stage + (i * NW + wave) * 1024);
+#pragma unroll
+      for (int i = 0; i < C::V_LOADS; ++i) dma16_buf(rv, v_off[i], stage + C::K_BYTES + (i * NW + wave) * 1024);
+    } else {  // last tile: rows past the range re-read the last key (masked, and zero weight)
 #pragma unroll
       for (int i = 0; i < C::K_LOADS; ++i) {
-        const int64_t key = min(k0 + k_row[i], key_end - 1);
-        dma16(a.k + key * kld + kcol + k_col[i], stage + (i * NW + wave) * 1024);
+        const int r = (int)min((int64_t)k_row[i], key_end - 1 - k0);
+        dma16_buf(rk, (uint32_t)((r * kld + k_col[i]) * 2), stage + (i * NW + wave) * 1024);
+      }
+#pragma unroll
+      for (int i = 0; i < C::V_LOADS; ++i) {
+        const int r = (int)min((int64_t)v_row[i], key_end - 1 - k0);
+        dma16_buf(rv, (uint32_t)((r * kld + v_col[i]) * 2), stage + C::K_BYTES + (i * NW + wave) * 1024);
       }
     }
-#pragma unroll
-    for (int i = 0; i < C::V_LOADS; ++i)
-      dma16(v_src[i] + (int64_t)t * HD * 64, stage + C::K_BYTES + (i * NW + wave) * 1024);
   };
 
   // ---- fragment read addresses (bytes within a stage).  K row r = kb*32 + ql,
   // logical chunk 2*kk + half, physical chunk (2*kk + half) ^ (r % NCH):
-  // address = (row base | ((half ^ r%NCH) << 4)) ^ (kk << 5).  V^T row
-  // d = dt*32 + ql (128 bytes), chunk 2*ks + half, physical chunk
-  // (2*ks + half) ^ ((d/2) % 8): with 64 LDS banks two consecutive rows cover
-  // all banks, so 16 lanes (rows d..d+15) then hit distinct banks.
-  const uint32_t k_a0 = (uint32_t)ql * (HD * 2) + ((uint32_t)(half ^ (ql & (C::NCH - 1))) << 4);
-  const uint32_t v_a0 = C::K_BYTES + (uint32_t)ql * 128 + ((uint32_t)(half ^ ((ql >> 1) & 7)) << 4);
+  // address = (row base | ((half ^ r%NCH) << 4)) ^ (kk << 5).
+  const uint32_t k_a0 = (uint32_t)ql * C::ROW_BYTES + ((uint32_t)(half ^ (ql & (C::NCH - 1))) << 4);
+  // V: a V^T fragment (lane l: d = dt*32 + l%32, MFMA k values 8(l/32) .. +7
+  // of a 16-key step, i.e. keys key_perm16(8(l/32) + j)) is two transposing
+  // reads of four key rows each.  In 16-lane group g = l/16, lane 4m + q names
+  // key row key_perm16(8(g/2) + m) (first read) or key_perm16(8(g/2) + 4 + m)
+  // (second), columns dt*32 + 16(g%2) + 4q .. +3; both rows are = m (mod 4).
+  // Physical byte of that piece: row*ROW_BYTES + ((chunk ^ (m << VSH)) * 16 +
+  // 8(q%2) with chunk = 4dt + 2(g%2) + q/2, so d tile dt flips bit 6 and step
+  // ks adds 16 rows.
+  uint32_t vr_a, vr_b;
+  {
+    const int g = lane >> 4, m = (lane >> 2) & 3, q = lane & 3;
+    const int ka = key_perm16(8 * (g >> 1) + m), kb = key_perm16(8 * (g >> 1) + 4 + m);
+    const uint32_t piece = ((uint32_t)((2 * (g & 1) + (q >> 1)) ^ (m << C::VSH)) << 4) + (uint32_t)(q & 1) * 8;
+    vr_a = C::K_BYTES + (uint32_t)ka * C::ROW_BYTES + piece;
+    vr_b = C::K_BYTES + (uint32_t)kb * C::ROW_BYTES + piece;
+  }
 
   // S^T for tile t: lane holds query ql, keys 8*(e/4) + 4*half + e%4 of each 32-key block.
   auto compute_s = [&](int t, f32x16 (&s)[2]) __attribute__((always_inline)) {
@@ -244,16 +282,18 @@ __global__ __launch_bounds__(NTHREADS) void attn_kernel(const AttnArgs a) {
       s[kb] = f32x16{};
 #pragma unroll
       for (int kk = 0; kk < C::KK; ++kk) {
-        const u32x4 kf = *reinterpret_cast<const u32x4*>(stage + kb * 32 * (HD * 2) + (k_a0 ^ (uint32_t)(kk << 5)));
+        const u32x4 kf = *reinterpret_cast<const u32x4*>(stage + kb * 32 * C::ROW_BYTES + (k_a0 ^ (uint32_t)(kk << 5)));
         s[kb] = mfma32(as_bf16x8(kf), qf[kk], s[kb]);
       }
     }
   };
 
-  // ---- running state (log2 domain): m = running reference max of the scaled
-  // scores, l = lane-partial sum of exp2(score*scale - m).
+  // ---- running state: m = running reference max of the raw scores (the
+  // exponent of a score s is (s - m) * scale_log2), l = lane-partial sum of
+  // the probabilities.
   constexpr float inv_sqrt_hd = HD == 128 ? 0.08838834764831844055f : 0.125f;
   const float scale_log2 = 1.44269504088896340736f * inv_sqrt_hd;
+  const float tau_raw = LAZY_TAU / scale_log2;  // the rescale threshold in raw score units
   float m_run = -INFINITY;
   float l_run = 0.0f;
   f32x16 o[C::DT];
@@ -275,7 +315,7 @@ __global__ __launch_bounds__(NTHREADS) void attn_kernel(const AttnArgs a) {
     }
   };
 
-  // Scaled row max of a tile's (masked) scores, combined over the lane pair
+  // Raw row max of a tile's (masked) scores, combined over the lane pair
   // (lanes l and l+32 hold the two halves of a query's keys).
   auto tile_max = [&](f32x16 (&s)[2]) __attribute__((always_inline)) {
     float mx = -INFINITY;
@@ -283,14 +323,14 @@ __global__ __launch_bounds__(NTHREADS) void attn_kernel(const AttnArgs a) {
     for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
       for (int e = 0; e < 16; ++e) mx = fmaxf(mx, s[kb][e]);
-    return pair_max(mx) * scale_log2;
+    return pair_max(mx);
   };
 
   // The fused block of a step: S of tile t+1 as two interleaved MFMA chains
   // (the two 32-key blocks) over the head_dim steps, with the K fragments of
   // the next step read before the current MFMAs and the exponentials of tile
   // t's keys 0..31 spread over the steps; then PV of tile t as DT independent
-  // chains over the four 16-key steps, V^T fragments again one step ahead, the
+  // chains over the four 16-key steps, V fragments again one step ahead, the
   // exponentials of keys 32..63 under its first two steps and the max of tile
   // t+1's (unmasked) scores under the last two.  The vector work is
   // split so that each MFMA carries a few vector instructions (co-issued), and
@@ -299,20 +339,23 @@ __global__ __launch_bounds__(NTHREADS) void attn_kernel(const AttnArgs a) {
     const uint8_t* kst = smem + ((t + 1) % NSTAGE) * C::STAGE_BYTES;
     const uint8_t* vst = smem + (t % NSTAGE) * C::STAGE_BYTES;
     auto kfrag = [&](int kb, int kk) __attribute__((always_inline)) {
-      return *reinterpret_cast<const u32x4*>(kst + kb * 32 * (HD * 2) + (k_a0 ^ (uint32_t)(kk << 5)));
+      return *reinterpret_cast<const u32x4*>(kst + kb * 32 * C::ROW_BYTES + (k_a0 ^ (uint32_t)(kk << 5)));
     };
     auto vfrag = [&](int dt, int ks) __attribute__((always_inline)) {
-      return *reinterpret_cast<const u32x4*>(vst + dt * 32 * 128 + (v_a0 ^ (uint32_t)(ks << 5)));
+      const uint8_t* sb = vst + ks * 16 * C::ROW_BYTES;
+      const u32x2 ra = lds_read_tr16x4(sb + (vr_a ^ (uint32_t)(dt << 6)));
+      const u32x2 rb = lds_read_tr16x4(sb + (vr_b ^ (uint32_t)(dt << 6)));
+      return u32x4{ra[0], ra[1], rb[0], rb[1]};
     };
     constexpr int PAIRS = 8 / C::KK;  // probability pairs of keys 0..31 per head_dim step
-    const float neg_m = -m_run;
+    const float m_ref = m_run;
     float lsum = 0.0f;
     uint32_t pk[16];  // bf16 pairs: pk[4*ks + j] holds keys of 16-key step ks
     // probabilities of the score pair idx (keys 2*idx, 2*idx+1 of the lane's order)
     auto prob_pair = [&](int idx) __attribute__((always_inline)) {
       const int kb = idx >> 3, e = (2 * idx) & 15;
-      const float p0 = __builtin_amdgcn_exp2f(fmaf(s_cu[kb][e], scale_log2, neg_m));
-      const float p1 = __builtin_amdgcn_exp2f(fmaf(s_cu[kb][e + 1], scale_log2, neg_m));
+      const float p0 = __builtin_amdgcn_exp2f((s_cu[kb][e] - m_ref) * scale_log2);
+      const float p1 = __builtin_amdgcn_exp2f((s_cu[kb][e + 1] - m_ref) * scale_log2);
       lsum += p0 + p1;
       pk[idx] = pack_bf16x2(p0, p1);
     };
@@ -357,7 +400,7 @@ __global__ __launch_bounds__(NTHREADS) void attn_kernel(const AttnArgs a) {
     }
     l_run += lsum;
     asm volatile("" : "+v"(l_run));  // keep the sum in this block, under the MFMAs
-    mt = pair_max(mx) * scale_log2;
+    mt = pair_max(mx);
   };
 
   // One pipeline step: make tile t+1 visible (and the stage of tile t-1 free);
@@ -375,9 +418,9 @@ __global__ __launch_bounds__(NTHREADS) void attn_kernel(const AttnArgs a) {
     }
     lds_barrier();
     if (t < wave_tiles) {  // wave-uniform
-      if (__builtin_amdgcn_ballot_w64(mt > m_run + LAZY_TAU) != 0) {  // wave-uniform, rare
+      if (__builtin_amdgcn_ballot_w64(mt > m_run + tau_raw) != 0) {  // wave-uniform, rare
         const float m_new = fmaxf(m_run, mt);
-        const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
+        const float alpha = __builtin_amdgcn_exp2f((m_run - m_new) * scale_log2);
         m_run = m_new;
         l_run *= alpha;
 #pragma unroll
@@ -410,7 +453,7 @@ __global__ __launch_bounds__(NTHREADS) void attn_kernel(const AttnArgs a) {
   lds_barrier();
 
   f32x16 sA[2], sB[2];
-  float mt = -INFINITY;  // scaled max of the current tile's masked scores
+  float mt = -INFINITY;  // raw max of the current tile's masked scores
   if (t_begin < t_end && t_begin < wave_tiles) {
     compute_s(t_begin, sA);
     mask_tile(t_begin, sA);
@@ -433,7 +476,7 @@ __global__ __launch_bounds__(NTHREADS) void attn_kernel(const AttnArgs a) {
   wait_vmcnt<0>();
 
   if (SPLIT && part >= 0) {
-    // unnormalised output, running max (log2 units) and sum of this key half
+    // unnormalised output, running max (scaled to log2 units) and sum of this key half
     if (wave_active && wave_first + ql < valid) {
       const float l_tot = l_run + __shfl_xor(l_run, 32);
       const int64_t r1 = (int64_t)tile * QT + wave_first + ql;  // row within chunk 1
@@ -446,7 +489,7 @@ __global__ __launch_bounds__(NTHREADS) void attn_kernel(const AttnArgs a) {
               f32x4{o[dt][4 * g], o[dt][4 * g + 1], o[dt][4 * g + 2], o[dt][4 * g + 3]};
       if (half == 0) {
         float* ml = a.part_ml + (((int64_t)part * a.n_heads + head) * a.chunk_len + r1) * 2;
-        ml[0] = m_run;
+        ml[0] = m_run * scale_log2;
         ml[1] = l_tot;
       }
     }
@@ -456,9 +499,9 @@ __global__ __launch_bounds__(NTHREADS) void attn_kernel(const AttnArgs a) {
   // ---- normalise and store: lane holds query ql, dims dt*32 + 8*(e/4) + 4*half + e%4.
   if (wave_active) {
     const float l_tot = l_run + __shfl_xor(l_run, 32);
-    if (a.lse && half == 0 && wave_first + ql < valid)  // sum_j exp(s_j) = 2^m_run * l_tot
+    if (a.lse && half == 0 && wave_first + ql < valid)  // sum_j exp(s_j) = 2^(m_run * scale_log2) * l_tot
       a.lse[(int64_t)head * 2 * a.chunk_len + row0 + wave_first + ql] =
-          (m_run + log2f(l_tot)) * 0.69314718055994530942f;
+          (m_run * scale_log2 + log2f(l_tot)) * 0.69314718055994530942f;
     if (wave_first + ql < valid) {
       const float inv = 1.0f / l_tot;
       const int64_t off = (row0 + wave_first + ql) * ld + hcol + 4 * half;
@@ -532,25 +575,7 @@ __global__ __launch_bounds__(256) void attn_combine_kernel(const AttnArgs a) {
   if (a.lse && g == 0) a.lse[(int64_t)head * 2 * a.chunk_len + a.chunk_len + r1] = (M + log2f(L)) * 0.69314718055994530942f;
 }
 
-constexpr int64_t SPLIT_BELOW = 512;  // split the late chunk's tiles when the grid has fewer items
-
-bool attn_split(int64_t chunk_len, int32_t n_heads) {
-  const int64_t tpc = (chunk_len + QT - 1) / QT;
-  return chunk_len > 0 && 2 * (int64_t)n_heads * tpc < SPLIT_BELOW;
-}
-
-size_t align256(size_t x) { return (x + 255) / 256 * 256; }
-
 }  // namespace
-
-int64_t attn_kv_tiles(int64_t seq_len) { return (seq_len + BKV - 1) / BKV; }
-
-size_t attn_core_workspace(int64_t seq_len, int64_t chunk_len, int32_t hidden, int32_t n_heads) {
-  size_t bytes = align256((size_t)attn_kv_tiles(seq_len) * 64 * hidden * 2);  // V^T tiles
-  if (attn_split(chunk_len, n_heads))
-    bytes += align256((size_t)2 * chunk_len * hidden * 4) + align256((size_t)2 * n_heads * chunk_len * 2 * 4);
-  return bytes;
-}
 
 hipError_t launch_vt_tiles(const uint16_t* src, int64_t rows, int32_t ld, int32_t heads, int32_t head_dim,
                            uint16_t* dst, int64_t n_tiles, hipStream_t stream) {
@@ -563,14 +588,8 @@ hipError_t launch_vt_tiles(const uint16_t* src, int64_t rows, int32_t ld, int32_
   return hipGetLastError();
 }
 
-hipError_t launch_vt_prep(const AttnArgs& a, hipStream_t stream) {
-  return launch_vt_tiles(a.v, a.seq_len, a.kv_ld, a.kv_heads, a.head_dim, a.vt, a.n_kv_tiles, stream);
-}
-
 hipError_t launch_attention(const AttnArgs& args, hipStream_t stream) {
   if (args.chunk_len <= 0) return hipSuccess;
-  hipError_t e = launch_vt_prep(args, stream);
-  if (e != hipSuccess) return e;
   const int tpc = (int)((args.chunk_len + QT - 1) / QT);
   const dim3 block(NTHREADS);
   if (!attn_split(args.chunk_len, args.n_heads)) {
@@ -581,11 +600,11 @@ hipError_t launch_attention(const AttnArgs& args, hipStream_t stream) {
       hipLaunchKernelGGL((attn_kernel<64, false>), grid, block, 0, stream, args);
     return hipGetLastError();
   }
-  // the key halves' partials follow the V^T tiles in the workspace
+  // the key halves' partials in the workspace
   AttnArgs a = args;
-  char* base = reinterpret_cast<char*>(a.vt) + align256((size_t)a.n_kv_tiles * 64 * a.hidden * 2);
+  char* base = static_cast<char*>(a.ws);
   a.part_o = reinterpret_cast<float*>(base);
-  a.part_ml = reinterpret_cast<float*>(base + align256((size_t)2 * a.chunk_len * a.hidden * 4));
+  a.part_ml = reinterpret_cast<float*>(base + attn_align((size_t)2 * a.chunk_len * a.hidden * 4));
   const dim3 grid(a.n_heads * 3 * tpc);
   const unsigned cgrid = (unsigned)((a.chunk_len * a.n_heads * (a.head_dim / 8) + 255) / 256);
   if (a.head_dim == 128) {

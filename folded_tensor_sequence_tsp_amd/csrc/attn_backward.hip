@@ -678,14 +678,6 @@ __global__ __launch_bounds__(64 * QW) void dq_kernel(const AttnBwdArgs a) {
 
 }  // namespace
 
-size_t attn_bwd_ws_bytes(int64_t seq_len, int64_t chunk_len, int32_t n_heads, int32_t kv_heads, int32_t head_dim) {
-  const int64_t n_kv_tiles = (seq_len + 63) / 64, tpc = (chunk_len + 63) / 64;
-  const size_t kt = attn_bwd_stages_kt(head_dim) ? (size_t)kv_heads * n_kv_tiles * head_dim * 64 * 2 : 0;
-  const size_t qt = attn_bwd_stages_qt(head_dim) ? (size_t)2 * n_heads * tpc * head_dim * 64 * 2 : 0;
-  const size_t stats = (size_t)2 * n_heads * tpc * 256 * 4;
-  return kt + 2 * qt + stats;
-}
-
 hipError_t launch_attention_backward(const AttnBwdArgs& a, hipStream_t stream) {
   if (a.chunk_len <= 0) return hipSuccess;
   const int H = a.n_heads, HD = a.head_dim;

@@ -109,6 +109,32 @@ __device__ __forceinline__ void dma16(const void* src, void* lds_block) {
                                    0, 0);
 }
 
+// Buffer resource (V#) over `bytes` bytes from `base` (raw buffer: stride 0;
+// offsets at or past `bytes` read as zero).  Built from SGPRs when the
+// arguments are wave-uniform, so rebasing it per tile is scalar work.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t buffer_rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
+}
+
+// Direct buffer->LDS load of 16 bytes per lane (buffer_load_dwordx4 ... lds):
+// lane L reads rsrc + voffset and writes its 16 bytes at lds_block + 16 * L;
+// lds_block is wave-uniform.
+__device__ __forceinline__ void dma16_buf(__amdgpu_buffer_rsrc_t rsrc, uint32_t voffset, void* lds_block) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (__attribute__((address_space(3))) void*)lds_block, 16, voffset, 0,
+                                           0, 0);
+}
+
+// Transposing LDS read of four 16-bit values per lane (ds_read_b64_tr_b16,
+// gfx950).  Within each group of 16 lanes, lane 4m + q names 8 bytes (four
+// consecutive 16-bit columns of one row, row m of the group's four rows), and
+// lane j receives column j of the group's 16 columns from rows m = 0..3, in
+// order: a 4 x 16 block of rows comes back as 16 columns of 4.
+__device__ __forceinline__ u32x2 lds_read_tr16x4(const void* p) {
+  typedef short v4s __attribute__((ext_vector_type(4)));
+  typedef __attribute__((address_space(3))) v4s lds_v4s;
+  return __builtin_bit_cast(u32x2, __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4s*)p));
+}
+
 // Workgroup barrier that the compiler may not move memory operations across.
 __device__ __forceinline__ void lds_barrier() {
   asm volatile("" ::: "memory");

@@ -90,28 +90,40 @@ struct AttnArgs {
   // K/V heads (n_heads for MHA; fewer for grouped-query attention, query head a
   // reading K/V head a / (n_heads / kv_heads)) and the row stride of k and v.
   int32_t kv_heads, kv_ld;
-  // V^T tiles written by the attention launch before the attention kernel:
-  // [kv_heads][n_kv_tiles][head_dim][64] bf16, keys permuted within 16-key groups.
-  uint16_t* vt;
-  int64_t n_kv_tiles;  // attn_kv_tiles(seq_len)
+  // workspace of attn_core_workspace() bytes (nullable when that is 0)
+  void* ws;
   // nullable: lse[head * 2 * chunk_len + row] = ln sum_j exp(score), the
   // natural log of each query row's softmax normaliser (kept for the backward).
   float* lse;
   // set by launch_attention when it splits the late chunk's keys in two
-  // (placed after the V^T tiles): the halves' unnormalised outputs
-  // [2][chunk_len][hidden] fp32 and (max, sum) pairs [2][n_heads][chunk_len][2]
+  // (in the workspace): the halves' unnormalised outputs
+  // [2][chunk_len][hidden] fp32 and (max in log2 units, sum) pairs
+  // [2][n_heads][chunk_len][2]
   float* part_o;
   float* part_ml;
 };
 
+// Attention tiling shared by the kernel and the host-side sizes: queries per
+// workgroup, keys per tile, and the grid size below which the late chunk's
+// key range is split in two.
+constexpr int ATTN_QT = 256;
+constexpr int ATTN_BKV = 64;
+constexpr int64_t ATTN_SPLIT_BELOW = 512;
+
+// 256-byte rounding of the workspace parts.
+constexpr size_t attn_align(size_t x) { return (x + 255) / 256 * 256; }
+
+// Whether launch_attention splits the late chunk's key range (few query tiles).
+bool attn_split(int64_t chunk_len, int32_t n_heads);
+
 // 64-key tiles covering seq_len keys.
 int64_t attn_kv_tiles(int64_t seq_len);
 
-// Bytes of workspace launch_attention needs: the V^T tiles for seq_len keys
-// and hidden columns, plus the split partials when the grid is small.
+// Bytes of workspace launch_attention needs: the split partials when the grid
+// is small, else none.
 size_t attn_core_workspace(int64_t seq_len, int64_t chunk_len, int32_t hidden, int32_t n_heads);
 
-// V -> V^T tiles, then the attention kernel (both on `stream`).
+// The attention kernel (and, for split grids, the combine kernel) on `stream`.
 hipError_t launch_attention(const AttnArgs& args, hipStream_t stream);
 
 // Rows [0, rows) of src (row stride ld, head h in columns h*head_dim ..) ->
@@ -180,6 +192,9 @@ hipError_t launch_rms_norm(const uint16_t* x, const uint16_t* gain, int64_t n, i
 hipError_t launch_rope(void* x, int32_t x_f32, int32_t inverse, int64_t n_rows, int64_t ld, int32_t n_heads,
                        int32_t head_dim, double theta, int64_t chunk_len, int64_t start0, int64_t start1,
                        int32_t at_global, hipStream_t stream);
+
+// Rows per workgroup of the RMSNorm backward (its partial dgain rows).
+constexpr int RMS_BWD_ROWS = 32;
 
 // Backward of RMSNorm over x [n x h] (bf16, h % 8 == 0, h <= 8192): dx (bf16)
 // and dgain (fp32 [h]); partial: fp32 [rms_norm_bwd_blocks(n) x h] scratch.

@@ -24,6 +24,15 @@ tsp_status check_ptr(const void* p) {
 
 tsp_status check_ptr_nullable(const void* p) { return (p && !aligned16(p)) ? TSP_ERR_ALIGNMENT : TSP_OK; }
 
+// A workspace of `need` bytes: null, misaligned or short is an error unless
+// nothing is needed (then the pointer is not used and may be null).
+tsp_status check_ws(const void* ws, size_t bytes, size_t need) {
+  if (need == 0) return TSP_OK;
+  if (!ws) return TSP_ERR_WORKSPACE;
+  if (!aligned16(ws)) return TSP_ERR_ALIGNMENT;
+  return bytes < need ? TSP_ERR_WORKSPACE : TSP_OK;
+}
+
 tsp_status check_shards(const uint16_t* const* w, int32_t D) {
   if (!w) return TSP_ERR_INVALID_ARG;
   for (int d = 0; d < D; ++d) {
@@ -72,14 +81,14 @@ tsp_status check_plan(const tsp_plan* p) {
   return TSP_OK;
 }
 
-// Attention core workspace: the V^T tiles of the gathered V for S = D * n keys,
-// and, for short sequences, the partial outputs of the late chunk's key halves.
+// Attention core workspace: for short sequences, the partial outputs of the
+// late chunk's key halves (none otherwise).
 size_t ws_core(int64_t n, const tsp_dims* d, int32_t D) {
   return round_up(attn_core_workspace(n * D, n / 2, d->hidden, d->n_heads));
 }
 
 // Attention workspace: Q, the attention output as a bf16 pair (hi, lo), then
-// the core's V^T tiles.
+// the core's split partials.
 size_t ws_attn(int64_t n, const tsp_dims* d, int32_t D) {
   return 3 * round_up((size_t)n * d->hidden * 2) + ws_core(n, d, D);
 }
@@ -152,8 +161,7 @@ tsp_status run_core(const tsp_plan* plan, const tsp_dims* dims, const uint16_t* 
   a.head_dim = dims->head_dim;
   a.kv_heads = dims->n_heads;
   a.kv_ld = dims->hidden;
-  a.vt = static_cast<uint16_t*>(core_ws);
-  a.n_kv_tiles = attn_kv_tiles(plan->seq_len);
+  a.ws = core_ws;
   return from_hip(launch_attention(a, stream));
 }
 
@@ -560,9 +568,7 @@ tsp_status tsp_attn_core(const tsp_plan* plan, const tsp_dims* dims, const uint1
       (s = check_ptr(attn_out)) != TSP_OK || (s = check_ptr_nullable(attn_lo)) != TSP_OK)
     return s;
   if (attn_out == q || attn_lo == q || attn_lo == attn_out) return TSP_ERR_INVALID_ARG;
-  if (!workspace) return TSP_ERR_WORKSPACE;
-  if (!aligned16(workspace)) return TSP_ERR_ALIGNMENT;
-  if (ws_bytes < ws_core(plan->n_local, dims, plan->D)) return TSP_ERR_WORKSPACE;
+  if ((s = check_ws(workspace, ws_bytes, ws_core(plan->n_local, dims, plan->D))) != TSP_OK) return s;
   return run_core(plan, dims, q, k_full, v_full, attn_out, attn_lo, workspace, stream);
 }
 
@@ -577,9 +583,7 @@ tsp_status tsp_attn_core_lse(const tsp_plan* plan, const tsp_dims* dims, const u
       (s = check_ptr(lse)) != TSP_OK)
     return s;
   if (attn_out == q || attn_lo == q || attn_lo == attn_out) return TSP_ERR_INVALID_ARG;
-  if (!workspace) return TSP_ERR_WORKSPACE;
-  if (!aligned16(workspace)) return TSP_ERR_ALIGNMENT;
-  if (ws_bytes < ws_core(plan->n_local, dims, plan->D)) return TSP_ERR_WORKSPACE;
+  if ((s = check_ws(workspace, ws_bytes, ws_core(plan->n_local, dims, plan->D))) != TSP_OK) return s;
   return run_core(plan, dims, q, k_full, v_full, attn_out, attn_lo, workspace, stream, lse);
 }
 
@@ -947,9 +951,7 @@ tsp_status tsp_attn_core_gqa(const tsp_plan* plan, const tsp_dims* dims, int32_t
       (s = check_ptr(attn_out)) != TSP_OK || (s = check_ptr_nullable(attn_lo)) != TSP_OK)
     return s;
   if (attn_out == q || attn_lo == q || attn_lo == attn_out) return TSP_ERR_INVALID_ARG;
-  if (!workspace) return TSP_ERR_WORKSPACE;
-  if (!aligned16(workspace)) return TSP_ERR_ALIGNMENT;
-  if (ws_bytes < ws_core(plan->n_local, dims, plan->D)) return TSP_ERR_WORKSPACE;
+  if ((s = check_ws(workspace, ws_bytes, ws_core(plan->n_local, dims, plan->D))) != TSP_OK) return s;
   AttnArgs a{};
   a.q = q;
   a.k = k_full;
@@ -965,8 +967,7 @@ tsp_status tsp_attn_core_gqa(const tsp_plan* plan, const tsp_dims* dims, int32_t
   a.head_dim = dims->head_dim;
   a.kv_heads = n_kv_heads;
   a.kv_ld = n_kv_heads * dims->head_dim;
-  a.vt = static_cast<uint16_t*>(workspace);
-  a.n_kv_tiles = attn_kv_tiles(plan->seq_len);
+  a.ws = workspace;
   return from_hip(launch_attention(a, stream));
 }
 
@@ -983,9 +984,7 @@ tsp_status tsp_attn_core_gqa_lse(const tsp_plan* plan, const tsp_dims* dims, int
       (s = check_ptr(attn_out)) != TSP_OK || (s = check_ptr_nullable(attn_lo)) != TSP_OK)
     return s;
   if (attn_out == q || attn_lo == q || attn_lo == attn_out) return TSP_ERR_INVALID_ARG;
-  if (!workspace) return TSP_ERR_WORKSPACE;
-  if (!aligned16(workspace)) return TSP_ERR_ALIGNMENT;
-  if (ws_bytes < ws_core(plan->n_local, dims, plan->D)) return TSP_ERR_WORKSPACE;
+  if ((s = check_ws(workspace, ws_bytes, ws_core(plan->n_local, dims, plan->D))) != TSP_OK) return s;
   AttnArgs a{};
   a.q = q;
   a.k = k_full;
@@ -1002,8 +1001,7 @@ tsp_status tsp_attn_core_gqa_lse(const tsp_plan* plan, const tsp_dims* dims, int
   a.head_dim = dims->head_dim;
   a.kv_heads = n_kv_heads;
   a.kv_ld = n_kv_heads * dims->head_dim;
-  a.vt = static_cast<uint16_t*>(workspace);
-  a.n_kv_tiles = attn_kv_tiles(plan->seq_len);
+  a.ws = workspace;
   return from_hip(launch_attention(a, stream));
 }
 

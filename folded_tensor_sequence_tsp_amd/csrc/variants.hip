@@ -95,7 +95,6 @@ __global__ __launch_bounds__(256) void rope_kernel(void* __restrict__ xv, int64_
 // and the block's part of dgain_j = sum_rows dy_j x_j / r: each lane keeps its
 // columns' sums in registers (columns lane*8 + 512*p .. +7), the waves add them
 // in LDS once per block, and the block writes partial[block][j].
-constexpr int RMS_BWD_ROWS = 32;
 constexpr int RMS_BWD_MAXP = 16;  // 512-column passes: hidden <= 8192
 __global__ __launch_bounds__(64 * NORM_WAVES) void rms_norm_bwd_kernel(
     const uint16_t* __restrict__ x, const uint16_t* __restrict__ gain, const uint16_t* __restrict__ dy, int64_t n,
@@ -229,8 +228,6 @@ hipError_t launch_rope(void* x, int32_t x_f32, int32_t inverse, int64_t n_rows, 
                        chunk_len, start0, start1, at_global);
   return hipGetLastError();
 }
-
-int64_t rms_norm_bwd_blocks(int64_t n) { return (n + RMS_BWD_ROWS - 1) / RMS_BWD_ROWS; }
 
 hipError_t launch_rms_norm_backward(const uint16_t* x, const uint16_t* gain, const uint16_t* dy, int64_t n,
                                     int32_t h, float eps, uint16_t* dx, float* dgain, float* partial,

@@ -158,10 +158,11 @@ tsp_status tsp_attn_project(const tsp_plan* plan, const tsp_dims* dims, const ui
  *              residual bf16(attn - attn_out), so that attn_out + attn_lo carries
  *              the fp32 result to about 16 significant bits (tsp_attn_out and
  *              tsp_layer_post contract both parts).
- *   workspace: device, >= tsp_workspace_size(n_local, dims, D, TSP_WS_CORE) bytes
- *              (a head-blocked transposed copy of v_full; for short sequences,
- *              where the late chunk's key range is processed in two halves,
- *              also the halves' fp32 partial outputs, maxima and sums).
+ *   workspace: device, >= tsp_workspace_size(n_local, dims, D, TSP_WS_CORE) bytes:
+ *              for short sequences (fewer than 512 work items of 256 queries
+ *              and one head), where the late chunk's key range is processed in
+ *              two halves, the halves' fp32 partial outputs, maxima and sums;
+ *              otherwise no bytes, and workspace may be null.
  */
 tsp_status tsp_attn_core(const tsp_plan* plan, const tsp_dims* dims, const uint16_t* q,
                          const uint16_t* k_full, const uint16_t* v_full, uint16_t* attn_out,
@@ -322,6 +323,10 @@ tsp_status tsp_mlp_forward(int64_t n_tokens, const tsp_dims* dims, int32_t D, in
  * h1 stays in fp32 for the residual; both MLP GEMMs run on fp16 operands (h1
  * and the GELU output scaled per row by a power of two from the RMS of the h1
  * row, W1 and W2 as fp16 copies of the bf16 shards; see tsp_mlp_forward).
+ * Weight magnitudes: W1 and W2 elements beyond the fp16 range (|w| > 65504)
+ * saturate to +-65504 in their copies, and those below 2^-14 keep an absolute
+ * error under 2^-25; no status reports either (N(0, 0.02) weights are far
+ * inside both limits).
  *   dims      : as for tsp_layer_forward.
  *   attn      : device, bf16 [n_tokens x hidden] (tsp_attn_core output).
  *   attn_lo   : device, bf16, nullable: its low part (see tsp_attn_core).
@@ -338,7 +343,8 @@ tsp_status tsp_layer_post(int64_t n_tokens, const tsp_dims* dims, int32_t D, int
 /*
  * One decoder layer for the rank's local tokens: tsp_attn_project, then
  * tsp_attn_core, then tsp_layer_post with start_shard = plan->rank, i.e.
- *   h1 = x + Attn(x), out = h1 + MLP(h1).  No norm, no bias.
+ *   h1 = x + Attn(x), out = h1 + MLP(h1).  No norm, no bias.  The MLP's
+ * precision and weight-magnitude limits are tsp_layer_post's.
  *   out       : device, bf16 [n_local x hidden]; must not alias x_local.
  *   workspace : >= tsp_workspace_size(n_local, dims, D, TSP_WS_LAYER) bytes.
  */

@@ -142,13 +142,31 @@ def test_core_rejects(L):
     assert L.tsp_attn_core(ctypes.byref(p), ctypes.byref(d), A, A, A, A + 64, A + 64, A + 128, 1 << 40, None) == tsp.TSP_ERR_INVALID_ARG
     assert L.tsp_attn_core(ctypes.byref(p), ctypes.byref(d), A, A, A, A + 64, MIS, A + 128, 1 << 40, None) == tsp.TSP_ERR_ALIGNMENT
     need = tsp.workspace_size(p.n_local, d, p.D, tsp.WS_CORE)
-    # V^T copy of the gathered V (S a multiple of 64 here), then the partials of
-    # the late chunk's two key halves (a short sequence: the grid is small)
+    # the partials of the late chunk's two key halves (a short sequence: the
+    # grid is small); nothing else
     C, H = p.chunk_len, d.n_heads
-    assert need == p.seq_len * 256 * 2 + 2 * C * 256 * 4 + 2 * H * C * 2 * 4
+    assert need == 2 * C * 256 * 4 + 2 * H * C * 2 * 4
     assert L.tsp_attn_core(ctypes.byref(p), ctypes.byref(d), A, A, A, A + 64, None, A + 128, need - 1, None) == tsp.TSP_ERR_WORKSPACE
     assert L.tsp_attn_core(ctypes.byref(p), ctypes.byref(d), A, A, A, A + 64, None, None, need, None) == tsp.TSP_ERR_WORKSPACE
     assert L.tsp_attn_core(ctypes.byref(p), ctypes.byref(d), A, A, A, A + 64, None, MIS, need, None) == tsp.TSP_ERR_ALIGNMENT
+
+
+def test_core_workspace_none_on_large_grids(L):
+    """A grid of 512 or more query tiles is not split: the attention core then
+    needs no workspace, and a null one is accepted (nothing is launched here:
+    argument checks only, on a shape whose launch would need a GPU)."""
+    d = tsp.make_dims(4096, 32, 128, 16384)
+    p, _, _ = tsp.zigzag_plan(131072, 8, 0)
+    assert tsp.workspace_size(p.n_local, d, 8, tsp.WS_CORE) == 0
+    p2, _, _ = tsp.zigzag_plan(16384, 8, 0)
+    C = p2.chunk_len
+    assert tsp.workspace_size(p2.n_local, d, 8, tsp.WS_CORE) == 2 * C * 4096 * 4 + 2 * 32 * C * 2 * 4
+    # the split threshold: 2 * heads * ceil(C / 256) work items below 512
+    d4 = tsp.make_dims(256, 4, 64, 1024)
+    for S, D in [(2048, 4), (131072, 8)]:
+        q, _, _ = tsp.zigzag_plan(S, D, 0)
+        items = 2 * 4 * ((q.chunk_len + 255) // 256)
+        assert (tsp.workspace_size(q.n_local, d4, D, tsp.WS_CORE) > 0) == (items < 512)
 
 
 def test_out_rejects(L):
@@ -235,19 +253,18 @@ def test_workspace_sizes(L):
     # post: fp32 h1, fp16 h1, row exponents, fp16 W1 and W2, fp16 GELU block
     assert post == n * 256 * 4 + n * 256 * 2 + n * 4 + 2 * 1024 * 256 * 2 + n * 1024 * 2
     core = tsp.workspace_size(n, d, 4, tsp.WS_CORE)
-    # V^T tiles for S = D * n keys; the grid of this short sequence is small
-    # (2 chunks x 4 heads x 1 query tile), so the late chunk's keys are split in
-    # two and the halves' fp32 outputs [2][C][h] and (max, sum) pairs
-    # [2][H][C][2] follow
+    # the grid of this short sequence is small (2 chunks x 4 heads x 1 query
+    # tile), so the late chunk's keys are split in two: the halves' fp32
+    # outputs [2][C][h] and (max, sum) pairs [2][H][C][2]
     C = n // 2
-    assert core == 4 * n * 256 * 2 + 2 * C * 256 * 4 + 2 * 4 * C * 2 * 4
-    assert attn == 3 * n * 256 * 2 + core  # Q, the attention output as a (hi, lo) bf16 pair, V^T
+    assert core == 2 * C * 256 * 4 + 2 * 4 * C * 2 * 4
+    assert attn == 3 * n * 256 * 2 + core  # Q, the attention output as a (hi, lo) bf16 pair, the partials
     assert layer == attn + post
     assert tsp.workspace_size(n, d, 4, 99) == 0
     assert tsp.workspace_size(n, _dims(hidden=300), 4, tsp.WS_LAYER) == 0
-    # a long sequence (2 x 32 heads x 32 query tiles) is not split: V^T tiles only
+    # a long sequence (2 x 32 heads x 32 query tiles) is not split: no workspace
     big = tsp.make_dims(4096, 32, 128, 16384)
-    assert tsp.workspace_size(16384, big, 8, tsp.WS_CORE) == 131072 * 4096 * 2
+    assert tsp.workspace_size(16384, big, 8, tsp.WS_CORE) == 0
     assert tsp.workspace_size(-1, d, 4, tsp.WS_ATTN) == 0
 
 
