@@ -8,15 +8,31 @@ the 32 layers, the shard-iterated QKV projection with the K/V scatter, causal
 attention of the two zigzag chunks against that layer's gathered K/V, the O
 projection split-K with the residual, and the ring MLP with the residual; the
 output of layer l is the input of layer l+1.  All inputs (weights, generated
-per-layer K/V, x) are resident in HBM before timing starts.
+per-layer K/V, x) are resident in HBM before timing starts.  ``value`` is
+local tokens/s per layer over the timed steps.
 
 The step calls the three entry points that tsp_layer_forward composes
 (tsp_attn_project, tsp_attn_core, tsp_layer_post), with HIP events recorded
-between them on the launch stream: the per-launch time of the attention kernel
-(the dominant one, about 73% of the layer's FLOPs) gives the roofline figure.
-``--workload stream_7b_16k`` runs the weight-streaming regime instead (S =
-16384, 2048 local tokens, 32 distinct layers): there the roofline figure is the
-whole layer, and ``hbm`` reports its bytes per second against the HBM peak.
+between them on the launch stream.
+
+Roofline.  The dominant kernel is the attention core (about 73% of the
+layer's FLOPs).  Its roofline figure is taken on unit-scale inputs: before
+any other attention work, the core is launched on layer 0's inputs (x ~ N(0,1),
+the layer's generated K/V) once untimed and then ``--roofline-launches`` times,
+each bracketed by HIP events on the launch stream.  The layer has no norm, so
+in the chained steps the activations grow about 2.5x per layer and the
+softmax rows of later layers are close to one-hot, which makes the same kernel
+faster; that chained per-launch figure is reported beside it
+(``roofline.chained``).  Because the unit-scale launches are the run's first
+attention dispatches, a ``--kernel-trace`` profile of this command averages
+exactly them (profile_summary ``--first``).
+
+``stream_7b_16k``: the weight-streaming regime, timed in the same run (S =
+16384, 2048 local tokens, 32 distinct layers whose 402.65 MB of weights each
+are read from HBM): layer time, local tokens/s, fraction of the bf16 MFMA peak,
+and HBM bytes per second (algorithmic, and counted from the counter summary
+of ``bench.py --workload stream_7b_16k``).  ``--workload stream_7b_16k`` makes
+that regime the main workload instead.
 
 After the timed steps, each step's entry point is also timed alone on layer
 0's inputs (``rows_layer0``: QKV projection, attention, O projection, MLP),
@@ -26,6 +42,11 @@ resident), the backward of every step (MLP ring, attention core, O and QKV
 projections), and the layer variants (RMSNorm and RoPE
 against the HBM peak, grouped-query attention with 8 K/V heads); ``--no-rows``
 skips them.
+
+``cpu_baseline``: the fp64 oracle timed on the host cores the process may run
+on, on a bounded sample of layer 0 (the K/V projection of all local rows, the
+attention half for 64 query rows stratified over both zigzag chunks, the MLP
+for 256 rows), extrapolated to local tokens/s per layer.
 
 Prints ONE JSON line.  ``--gpus`` above 1 is refused: this build runs on one GPU.
 """
@@ -48,7 +69,7 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 # streams).  A figure is used only while the kernels' sources are the ones
 # profiled.
 TRAFFIC_SUMMARY = {
-    "full_7b_128k": (os.path.join(ROOT, "profiles", "tsp_attn_core_7b_128k_rank0_32layers.md"), "tsp_attn_core"),
+    "full_7b_128k": (os.path.join(ROOT, "profiles", "tsp_attn_core_7b_128k_rank0_unit_scale.md"), "tsp_attn_core"),
     "stream_7b_16k": (os.path.join(ROOT, "profiles", "tsp_layer_forward_7b_16k_rank0_32layers.md"),
                       "tsp_layer_forward"),
 }
@@ -56,6 +77,7 @@ TRAFFIC_SUMMARY = {
 PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
 PEAK_HBM_GBS = 8000.0        # MI355X HBM3E
 METRIC = "local tokens/sec per 7B TSP layer (D=8, 128K seq) + % bf16 MFMA peak"
+DTYPE = "bf16 (MLP GEMMs on fp16 operands scaled per row by a power of two)"
 
 
 def layer_flops(n, S, D, C, d):
@@ -222,11 +244,15 @@ def parse():
     ap.add_argument("--warmup", type=int, default=2)
     ap.add_argument("--workload", default="full_7b_128k", choices=["full_7b_128k", "stream_7b_16k"])
     ap.add_argument("--layers", type=int, default=None, help="layers per step (default: the workload's)")
+    ap.add_argument("--roofline-launches", type=int, default=10,
+                    help="timed unit-scale launches of the attention core for the roofline figure")
+    ap.add_argument("--no-stream", action="store_true",
+                    help="skip the weight-streaming regime's object (timed after the main workload)")
+    ap.add_argument("--stream-steps", type=int, default=10, help="timed steps of the weight-streaming stack")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-rows", action="store_true",
                     help="skip the per-entry-point timings after the timed steps (a kernel-trace profile of the "
                          "timed steps alone then averages only their launches)")
-    ap.add_argument("--cpu-rows", type=int, default=4, help="oracle sample rows per timing call")
     ap.add_argument("--copy-probe-mib", type=int, default=0,
                     help="also run one plain device copy of this many MiB before timing, so that a counter "
                          "profile of the same command holds a reference kernel of known traffic")
@@ -243,45 +269,174 @@ def build_inputs(W, n_layers, dev):
     return layers
 
 
-def cpu_baseline(W, plan, x_local, layer0, rows_per_call):
+class Stack:
+    """One workload's resident inputs and buffers, and its chained step:
+    tsp_layer_forward's three parts per layer, optionally with HIP events
+    recorded between them on the launch stream."""
+
+    def __init__(self, W, n_layers, dev):
+        self.W, self.n_layers = W, n_layers
+        d, D, S = W.dims, W.D, W.seq_len
+        self.plan, _, _ = tsp.zigzag_plan(S, D, W.rank)
+        n, h = self.plan.n_local, d.hidden
+        self.dims = tsp.make_dims(d.hidden, d.n_heads, d.head_dim, d.ffn)
+        self.layers = build_inputs(W, n_layers, dev)
+        self.x0 = synth.activations(W.wid, n, h, device=dev)
+        self.q = torch.empty(n, h, dtype=torch.bfloat16, device=dev)
+        self.a = torch.empty(n, h, dtype=torch.bfloat16, device=dev)
+        self.a_lo = torch.empty(n, h, dtype=torch.bfloat16, device=dev)
+        self.bufs = [torch.empty(n, h, dtype=torch.bfloat16, device=dev) for _ in range(2)]
+        self.ws = tsp.alloc_workspace(n, self.dims, D, tsp.WS_POST, device=dev)
+        self.ws_core = tsp.alloc_workspace(n, self.dims, D, tsp.WS_CORE, device=dev)
+        self.fl = layer_flops(n, S, D, self.plan.chunk_len, d)
+
+    def step(self, stream, events=None):
+        plan, dims, D = self.plan, self.dims, self.W.D
+        x = self.x0
+        for l, (lw, kf, vf) in enumerate(self.layers):
+            out = self.bufs[l % 2]
+            ev = events[l] if events is not None else None
+            if ev: ev[0].record(stream)
+            tsp.attn_project(plan, dims, x, lw.wqkv, kf, vf, self.q)
+            if ev: ev[1].record(stream)
+            tsp.attn_core(plan, dims, self.q, kf, vf, self.a, self.a_lo, workspace=self.ws_core)
+            if ev: ev[2].record(stream)
+            tsp.layer_post(dims, D, plan.rank, self.a, x, lw.wo, lw.w1, lw.w2, out, self.ws, attn_lo=self.a_lo)
+            if ev: ev[3].record(stream)
+            x = out
+        return x
+
+    def timed(self, stream, steps, warmup):
+        """(ms per step, per-stage ms per launch over all layers, per-stage ms of layer 0)."""
+        for _ in range(warmup):
+            self.step(stream)
+        torch.cuda.synchronize()
+        events = [[[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(self.n_layers)]
+                  for _ in range(steps)]
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for s in range(steps):
+            self.step(stream, events[s])
+        torch.cuda.synchronize()
+        elapsed = time.perf_counter() - t0
+        stages = ["qkv", "attn", "post"]
+        stage_ms = {k: 0.0 for k in stages}
+        first_ms = {k: 0.0 for k in stages}
+        for s in range(steps):
+            for l in range(self.n_layers):
+                ev = events[s][l]
+                for i, k in enumerate(stages):
+                    t = ev[i].elapsed_time(ev[i + 1])
+                    stage_ms[k] += t
+                    if l == 0:
+                        first_ms[k] += t / steps
+        stage_ms = {k: v / (steps * self.n_layers) for k, v in stage_ms.items()}
+        return elapsed * 1e3 / steps, stage_ms, first_ms
+
+
+def unit_scale_attention(stack, stream, launches):
+    """The roofline figure's launches: tsp_attn_core on layer 0's unit-scale
+    inputs (Q projected from x0, the layer's generated K/V with the rank's own
+    rows), one untimed, then `launches` each between HIP events on the launch
+    stream.  Returns the mean ms per launch."""
+    lw, kf, vf = stack.layers[0]
+    tsp.attn_project(stack.plan, stack.dims, stack.x0, lw.wqkv, kf, vf, stack.q)
+    call = lambda: tsp.attn_core(stack.plan, stack.dims, stack.q, kf, vf, stack.a, stack.a_lo,
+                                 workspace=stack.ws_core)
+    call()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(launches)]
+    for e0, e1 in ev:
+        e0.record(stream)
+        call()
+        e1.record(stream)
+    torch.cuda.synchronize()
+    return sum(e0.elapsed_time(e1) for e0, e1 in ev) / launches
+
+
+def cpu_baseline(W, plan, x_local, layer0):
     """Time the fp64 oracle on a bounded sample of layer 0 of the same workload
     and extrapolate to local tokens/s per layer.
 
-    Call A: attention half for `rows_per_call` rows, which also computes the K/V
-    projections of all local rows (the fixed cost).  Call B: attention half for
-    2*rows_per_call other rows with those K/V reused (per-row cost).  Call C:
-    the MLP for the same rows.  Full layer = fixed + n * per-row."""
+    The oracle computes each row from its definition, so rows are independent
+    given the K/V: the fixed cost is the K/V projection of all local rows, the
+    rest is a cost per row.  Call A: the attention half (attention, O
+    projection, residual) for the first row, which also computes the K/V
+    projection of all local rows.  Call B: the attention half for 64 query rows
+    stratified over the two zigzag chunks (32 evenly spaced rows of each chunk,
+    its first and last row included), with those K/V reused.  Call C: the MLP
+    (with its residual) for 256 rows evenly spaced over the local rows.
+    Full layer = fixed + n * (attention per row + MLP per row).  The threads
+    are the host cores this process may run on (its affinity mask)."""
     from oracle import tsp_oracle as O  # test infrastructure, used only here
-    lw, kf, vf = layer0
-    d = W.dims
-    lc = lw.to("cpu")
-    x = x_local.cpu()
-    kf_c, vf_c = kf.cpu(), vf.cpu()
-    oplan = O.zigzag_plan(W.seq_len, W.D, W.rank)
-    n = plan.n_local
-    g = torch.Generator().manual_seed(7)
-    perm = torch.randperm(n, generator=g)
-    ra, rb = perm[:rows_per_call], perm[rows_per_call:3 * rows_per_call]
-    t0 = time.perf_counter()
-    _, _, k_own, v_own = O.attn_forward(oplan, x, lc.wqkv, lc.wo, d.n_heads, d.head_dim, kf_c, vf_c, rows=ra)
-    t1 = time.perf_counter()
-    h1, _, _, _ = O.attn_forward(oplan, x, lc.wqkv, lc.wo, d.n_heads, d.head_dim, kf_c, vf_c, rows=rb,
-                                 k_own=k_own, v_own=v_own)
-    t2 = time.perf_counter()
-    O.mlp_forward(h1, lc.w1, lc.w2, residual=True)
-    t3 = time.perf_counter()
-    per_row = (t2 - t1 + t3 - t2) / len(rb)
-    fixed = max((t1 - t0) - len(ra) * (t2 - t1) / len(rb), 0.0)
-    layer_s = fixed + n * per_row
+    cores = len(os.sched_getaffinity(0))
+    prev_threads = torch.get_num_threads()
+    torch.set_num_threads(cores)
+    try:
+        lw, kf, vf = layer0
+        d = W.dims
+        lc = lw.to("cpu")
+        x = x_local.cpu()
+        kf_c, vf_c = kf.cpu(), vf.cpu()
+        oplan = O.zigzag_plan(W.seq_len, W.D, W.rank)
+        n, C = plan.n_local, plan.chunk_len
+        per_chunk = torch.linspace(0, C - 1, 32).round().to(torch.int64)
+        rows_attn = torch.cat([per_chunk, C + per_chunk])
+        rows_mlp = torch.linspace(0, n - 1, 256).round().to(torch.int64)
+        t0 = time.perf_counter()
+        _, _, k_own, v_own = O.attn_forward(oplan, x, lc.wqkv, lc.wo, d.n_heads, d.head_dim, kf_c, vf_c,
+                                            rows=rows_attn[:1])
+        t1 = time.perf_counter()
+        O.attn_forward(oplan, x, lc.wqkv, lc.wo, d.n_heads, d.head_dim, kf_c, vf_c, rows=rows_attn,
+                       k_own=k_own, v_own=v_own)
+        t2 = time.perf_counter()
+        O.mlp_forward(x, lc.w1, lc.w2, residual=True, rows=rows_mlp)
+        t3 = time.perf_counter()
+    finally:
+        torch.set_num_threads(prev_threads)
+    attn_row = (t2 - t1) / len(rows_attn)
+    mlp_row = (t3 - t2) / len(rows_mlp)
+    fixed = max((t1 - t0) - attn_row, 0.0)
+    layer_s = fixed + n * (attn_row + mlp_row)
     return {
         "value": n / layer_s,
         "unit": "local tokens/s per layer",
-        "cores": torch.get_num_threads(),
+        "cores": cores,
         "kind": "oracle",
-        "sample": (f"fp64 oracle on layer 0 of the same workload: attention half for {len(ra)} rows with the K/V "
-                   f"projection of all {n} local rows ({t1 - t0:.1f} s), attention half + MLP for {len(rb)} more "
-                   f"rows ({t3 - t1:.1f} s); per layer = fixed + {n} x per-row = {layer_s:.0f} s"),
+        "sample": (f"fp64 oracle on layer 0 of the same workload, {cores} threads: K/V projection of all {n} local "
+                   f"rows ({fixed:.1f} s), attention half for {len(rows_attn)} query rows stratified over both "
+                   f"zigzag chunks ({t2 - t1:.1f} s), MLP for {len(rows_mlp)} rows ({t3 - t2:.1f} s); per layer = "
+                   f"fixed + {n} x per-row = {layer_s:.0f} s"),
         "measured_s": round(t3 - t0, 2),
+    }
+
+
+def stream_object(stack, stream, steps, warmup):
+    """The weight-streaming regime's figures, timed in this run."""
+    W, plan, d = stack.W, stack.plan, stack.W.dims
+    ms_step, stage_ms, _ = stack.timed(stream, steps, warmup)
+    layer_ms = ms_step / stack.n_layers
+    total_flops = sum(stack.fl.values())
+    tflops = total_flops / (layer_ms * 1e-3) / 1e12
+    alg_bytes = layer_bytes(plan, d)
+    summary, unit = TRAFFIC_SUMMARY["stream_7b_16k"]
+    counted = profile_summary.read_traffic(summary, unit)
+    return {
+        "workload": W.name,
+        "layers_per_step": stack.n_layers,
+        "steps": steps,
+        "layer_ms": round(layer_ms, 4),
+        "local_tokens_per_s": round(plan.n_local / (layer_ms * 1e-3), 1),
+        "tflops": round(tflops, 1),
+        "mfma_frac": round(tflops / PEAK_BF16_TFLOPS, 4),
+        "stages_ms_per_launch": {k: round(v, 4) for k, v in stage_ms.items()},
+        "hbm_algorithmic_bytes_per_layer": alg_bytes,
+        "hbm_algorithmic_GBs": round(alg_bytes / (layer_ms * 1e-3) / 1e9, 1),
+        "hbm_counted_bytes_per_layer": counted,
+        "hbm_counted_GBs": round(counted / (layer_ms * 1e-3) / 1e9, 1) if counted else None,
+        "hbm_peak_GBs": PEAK_HBM_GBS,
+        "hbm_counted_frac": round(counted / (layer_ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 4) if counted else None,
+        "hbm_counted_over_algorithmic": round(counted / alg_bytes, 3) if counted else None,
+        "traffic_source": os.path.relpath(summary, ROOT),
     }
 
 
@@ -301,39 +456,11 @@ def main():
     W = synth.WORKLOADS[args.workload]
     n_layers = args.layers or W.n_layers
     d, D, S = W.dims, W.D, W.seq_len
-    plan, _, _ = tsp.zigzag_plan(S, D, W.rank)
-    n, h = plan.n_local, d.hidden
-    dims = tsp.make_dims(d.hidden, d.n_heads, d.head_dim, d.ffn)
-
     print(f"[bench] generating inputs: {W.name}, {n_layers} layers", file=sys.stderr, flush=True)
-    layers = build_inputs(W, n_layers, dev)
-    x0 = synth.activations(W.wid, n, h, device=dev)
-    q = torch.empty(n, h, dtype=torch.bfloat16, device=dev)
-    a = torch.empty(n, h, dtype=torch.bfloat16, device=dev)
-    a_lo = torch.empty(n, h, dtype=torch.bfloat16, device=dev)
-    bufs = [torch.empty(n, h, dtype=torch.bfloat16, device=dev) for _ in range(2)]
-    ws = tsp.alloc_workspace(n, dims, D, tsp.WS_POST)
-    ws_core = tsp.alloc_workspace(n, dims, D, tsp.WS_CORE)
+    main_stack = Stack(W, n_layers, dev)
+    plan, dims, n = main_stack.plan, main_stack.dims, main_stack.plan.n_local
     torch.cuda.synchronize()
-
     stream = torch.cuda.current_stream()
-    stages = ["qkv", "attn", "post"]
-
-    def step(events=None):
-        # tsp_layer_forward's three parts, with events between them on the launch stream
-        x = x0
-        for l, (lw, kf, vf) in enumerate(layers):
-            out = bufs[l % 2]
-            ev = events[l] if events is not None else None
-            if ev: ev[0].record(stream)
-            tsp.attn_project(plan, dims, x, lw.wqkv, kf, vf, q)
-            if ev: ev[1].record(stream)
-            tsp.attn_core(plan, dims, q, kf, vf, a, a_lo, workspace=ws_core)
-            if ev: ev[2].record(stream)
-            tsp.layer_post(dims, D, plan.rank, a, x, lw.wo, lw.w1, lw.w2, out, ws, attn_lo=a_lo)
-            if ev: ev[3].record(stream)
-            x = out
-        return x
 
     if args.copy_probe_mib > 0:
         nb = args.copy_probe_mib << 20
@@ -344,46 +471,25 @@ def main():
         print(f"[bench] copy probe: {nb} bytes read, {nb} bytes written", file=sys.stderr, flush=True)
         del src, dst
 
-    print(f"[bench] warmup {args.warmup}", file=sys.stderr, flush=True)
-    for _ in range(args.warmup):
-        step()
-    torch.cuda.synchronize()
+    summary, unit = TRAFFIC_SUMMARY[args.workload]
+    unit_ms = None
+    if unit == "tsp_attn_core":
+        print(f"[bench] roofline: 1 + {args.roofline_launches} unit-scale launches of tsp_attn_core",
+              file=sys.stderr, flush=True)
+        unit_ms = unit_scale_attention(main_stack, stream, args.roofline_launches)
 
-    events = [[[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(n_layers)]
-              for _ in range(args.steps)]
-    print(f"[bench] timing {args.steps} steps", file=sys.stderr, flush=True)
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for s in range(args.steps):
-        step(events[s])
-    torch.cuda.synchronize()
-    elapsed = time.perf_counter() - t0
-
-    stage_ms = {k: 0.0 for k in stages}
-    first_ms = {k: 0.0 for k in stages}  # layer 0 alone: unit-scale activations
-    for s in range(args.steps):
-        for l in range(n_layers):
-            ev = events[s][l]
-            for i, k in enumerate(stages):
-                t = ev[i].elapsed_time(ev[i + 1])
-                stage_ms[k] += t
-                if l == 0:
-                    first_ms[k] += t / args.steps
-    launches = args.steps * n_layers
-    stage_ms = {k: v / launches for k, v in stage_ms.items()}   # ms per launch
-    fl_rows = layer_flops(n, S, D, plan.chunk_len, d)
+    print(f"[bench] warmup {args.warmup}, timing {args.steps} steps", file=sys.stderr, flush=True)
+    ms_per_step, stage_ms, first_ms = main_stack.timed(stream, args.steps, args.warmup)
+    fl_rows = main_stack.fl
     fl = dict(fl_rows)
     fl["post"] = fl.pop("oproj") + fl.pop("mlp")
-
-    ms_per_step = elapsed * 1e3 / args.steps
     layer_ms = ms_per_step / n_layers
     value = n / (layer_ms * 1e-3)
     total_flops = sum(fl.values())
 
-    summary, unit = TRAFFIC_SUMMARY[args.workload]
     if unit == "tsp_attn_core":
-        roof = {"kernel": "tsp_attn_core (vt_prep_kernel + attn_kernel<128, false>)", "flops": fl["attn"],
-                "ms": stage_ms["attn"]}
+        roof = {"kernel": "tsp_attn_core (vt_prep_kernel + attn_kernel<128, false>), unit-scale layer-0 inputs",
+                "flops": fl["attn"], "ms": unit_ms}
     else:
         roof = {"kernel": "tsp_layer_forward (QKV, attention, O projection, MLP)", "flops": total_flops,
                 "ms": sum(stage_ms.values())}
@@ -404,7 +510,7 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "bf16",
+        "dtype": DTYPE,
         "data": "synthetic",
         "config": {
             "workload": W.name,
@@ -416,7 +522,7 @@ def main():
         "layer_tflops": round(total_flops / (layer_ms * 1e-3) / 1e12, 1),
         "layer_mfma_frac": round(total_flops / (layer_ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4),
         "stages_ms_per_launch": {k: round(v, 4) for k, v in stage_ms.items()},
-        "stages_tflops": {k: round(fl[k] / (stage_ms[k] * 1e-3) / 1e12, 1) for k in stages},
+        "stages_tflops": {k: round(fl[k] / (stage_ms[k] * 1e-3) / 1e12, 1) for k in stage_ms},
         "stages_ms_layer0": {k: round(v, 4) for k, v in first_ms.items()},
         "roofline": {
             "kernel": roof["kernel"],
@@ -425,9 +531,10 @@ def main():
             "peak": PEAK_BF16_TFLOPS,
             "unit": "TFLOP/s",
             "frac": round(roof_tflops / PEAK_BF16_TFLOPS, 4),
+            "traffic": traffic,
             "flops_per_launch": roof["flops"],
             "ms_per_launch": round(roof["ms"], 4),
-            "traffic": traffic,
+            "launches": args.roofline_launches if unit == "tsp_attn_core" else args.steps * n_layers,
             "traffic_source": os.path.relpath(summary, ROOT),
             "profile_ms_per_launch": profile_summary.read_avg_ms(summary, unit),
         },
@@ -445,13 +552,32 @@ def main():
         },
         "cpu_baseline": None,
     }
-    print("[bench] per-step timing on layer 0", file=sys.stderr, flush=True)
+    if unit == "tsp_attn_core":
+        chained_tf = fl["attn"] / (stage_ms["attn"] * 1e-3) / 1e12
+        result["roofline"]["chained"] = {
+            "what": "the same kernel's mean over all layers of the timed chained steps (activations grow about "
+                    "2.5x per layer without a norm)",
+            "ms_per_launch": round(stage_ms["attn"], 4),
+            "achieved": round(chained_tf, 1),
+            "frac": round(chained_tf / PEAK_BF16_TFLOPS, 4),
+        }
     if not args.no_rows:
-        result["rows_layer0"] = row_timings(plan, dims, D, layers[0], x0, q, a, a_lo, bufs[0], ws_core, fl_rows,
-                                            dev)
+        print("[bench] per-step timing on layer 0", file=sys.stderr, flush=True)
+        result["rows_layer0"] = row_timings(plan, dims, D, main_stack.layers[0], main_stack.x0, main_stack.q,
+                                            main_stack.a, main_stack.a_lo, main_stack.bufs[0], main_stack.ws_core,
+                                            fl_rows, dev)
     if not args.no_cpu_baseline:
         print("[bench] cpu baseline (fp64 oracle, bounded sample)", file=sys.stderr, flush=True)
-        result["cpu_baseline"] = cpu_baseline(W, plan, x0, layers[0], args.cpu_rows)
+        result["cpu_baseline"] = cpu_baseline(W, plan, main_stack.x0, main_stack.layers[0])
+    if args.workload != "stream_7b_16k" and not args.no_stream:
+        SW = synth.WORKLOADS["stream_7b_16k"]
+        del main_stack
+        torch.cuda.empty_cache()
+        print(f"[bench] weight-streaming regime: {SW.name}, {SW.n_layers} layers", file=sys.stderr, flush=True)
+        sstack = Stack(SW, SW.n_layers, dev)
+        torch.cuda.synchronize()
+        result["stream_7b_16k"] = stream_object(sstack, stream, args.stream_steps, 2)
+        del sstack
     print(json.dumps(result), flush=True)
 
 

@@ -9,7 +9,12 @@ Reads the CSV output of three rocprofv3 runs of the same ``bench.py`` command:
 
 A summary covers one unit: an entry point's kernels (``tsp_attn_core`` launches
 ``vt_prep_kernel`` then ``attn_kernel``), whose per-launch durations and bytes
-are summed.
+are summed.  With ``--first N --skip K`` the durations come from the
+per-dispatch kernel trace (``*_kernel_trace.csv``) instead: the first N
+dispatches of each of the unit's kernels, in dispatch order, less the first K
+of them (the benchmark makes its unit-scale roofline launches of the attention
+core before any other attention work, one untimed launch and then the timed
+ones).
 
 The counter runs also hold a plain device copy of known size (``bench.py
 --copy-probe-mib``); the ratio of its true bytes to what each counter reads for
@@ -97,6 +102,23 @@ def kernel_stats(trace_dir: str):
     return [(_short(r["Name"]), int(r["Calls"]), float(r["AverageNs"]) / 1e6, float(r["Percentage"])) for r in rows]
 
 
+def first_dispatch_ms(trace_dir: str, kernels, first: int, skip: int):
+    """Per-call ms of a unit from the kernel trace: for each kernel prefix, the
+    mean duration of its dispatches [skip, first) in dispatch order; summed over
+    the unit's kernels (each launches once per call).  Returns (ms, calls)."""
+    rows = list(csv.DictReader(open(_one(os.path.join(trace_dir, "*kernel_trace.csv")))))
+    rows.sort(key=lambda r: int(r["Dispatch_Id"]))
+    total, calls = 0.0, None
+    for k in kernels:
+        durs = [(int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e6 for r in rows
+                if _short(r["Kernel_Name"]).startswith(k)][:first][skip:]
+        if not durs:
+            continue
+        total += sum(durs) / len(durs)
+        calls = len(durs) if calls is None else min(calls, len(durs))
+    return total, calls or 0
+
+
 def counters(pmc_dir: str):
     """{dispatch id: (kernel name, counter value KiB)}"""
     rows = list(csv.DictReader(open(_one(os.path.join(pmc_dir, "*counter_collection.csv")))))
@@ -110,14 +132,20 @@ def _copy_factor(cnt, copy_bytes: int) -> tuple:
     return copy_bytes / (vals[0] * 1024.0), vals[0]
 
 
-def summarise(trace, fetch, write, unit, copy_mib, command, workload):
+def summarise(trace, fetch, write, unit, copy_mib, command, workload, first=None, skip=0):
     """Markdown summary of a kernel-trace run and, when fetch and write are
     given, of its two counter runs (traffic of the unit's kernels)."""
     stats = kernel_stats(trace)
     kernels = UNITS[unit][0]
     per = PER_CALL.get(unit)
     avg_ms = 0.0
-    if per:
+    first_note = None
+    if first:
+        avg_ms, n_calls = first_dispatch_ms(trace, kernels, first, skip)
+        first_note = (f"avg_ms_per_launch is the mean over dispatches {skip + 1}..{first} (in dispatch order, "
+                      f"{n_calls} calls) of each of the unit's kernels, from the per-dispatch kernel trace: "
+                      f"{avg_ms:.4f} ms per call.")
+    elif per:
         calls = sum(c for n, c, _, _ in stats if n.startswith(per))
         avg_ms = sum(c * ms for n, c, ms, _ in stats if n.startswith(tuple(kernels))) / calls
     else:
@@ -146,6 +174,8 @@ def summarise(trace, fetch, write, unit, copy_mib, command, workload):
              "## Kernel time (--kernel-trace --stats)", "",
              "| kernel | calls | avg ms | % of GPU time |", "|---|---|---|---|"]
     lines += [f"| {n} | {c} | {ms:.4f} | {p:.2f} |" for n, c, ms, p in stats if "at::native" not in n]
+    if first_note:
+        lines += ["", first_note]
     if not (fetch and write):
         lines += ["", "## Machine-readable", "",
                   f"kernel: {unit}",
@@ -226,8 +256,11 @@ def main():
     ap.add_argument("--command", required=True, help="the profiling commands, separated by ' ;; '")
     ap.add_argument("--workload", required=True)
     ap.add_argument("--out", required=True)
+    ap.add_argument("--first", type=int, default=None,
+                    help="per-call time from the first N dispatches of the unit's kernels (kernel trace)")
+    ap.add_argument("--skip", type=int, default=0, help="of those, leave out the first K (untimed warmup)")
     a = ap.parse_args()
-    text = summarise(a.trace, a.fetch, a.write, a.kernel, a.copy_mib, a.command, a.workload)
+    text = summarise(a.trace, a.fetch, a.write, a.kernel, a.copy_mib, a.command, a.workload, a.first, a.skip)
     with open(a.out, "w") as fh:
         fh.write(text)
     print(text)
