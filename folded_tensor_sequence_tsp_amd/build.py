@@ -16,7 +16,7 @@ PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 LIB = os.path.join(PKG, "libtsp.so")
-SOURCES = ["tsp_api.cpp", "layout.cpp", "gemm.hip", "attention.hip", "prep.hip", "variants.hip", "backward.hip", "attn_backward.hip"]
+SOURCES = ["tsp_api.cpp", "layout.cpp", "gemm.hip", "attention.hip", "prep.hip", "variants.hip", "backward.hip", "attn_backward.hip", "noalloc.hip"]
 
 ARCH = "gfx950"
 # Packed fp32 VALU forms are switched off (they are only a codegen choice here).

@@ -1366,6 +1366,7 @@ const char* tsp_status_string(tsp_status status) {
     case TSP_ERR_WORKSPACE: return "TSP_ERR_WORKSPACE: workspace missing or too small";
     case TSP_ERR_UNSUPPORTED: return "TSP_ERR_UNSUPPORTED: head_dim or width not supported by the kernels";
     case TSP_ERR_HIP: return "TSP_ERR_HIP: a kernel launch failed";
+    case TSP_ERR_SCRATCH: return "TSP_ERR_SCRATCH: more scratch than the allocation-free entry point's fixed array";
     default: return "TSP: unknown status";
   }
 }

@@ -17,7 +17,9 @@ import torch
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libtsp.so")
 
-TSP_OK, TSP_ERR_INVALID_ARG, TSP_ERR_SHAPE, TSP_ERR_ALIGNMENT, TSP_ERR_WORKSPACE, TSP_ERR_UNSUPPORTED, TSP_ERR_HIP = range(7)
+(TSP_OK, TSP_ERR_INVALID_ARG, TSP_ERR_SHAPE, TSP_ERR_ALIGNMENT, TSP_ERR_WORKSPACE, TSP_ERR_UNSUPPORTED, TSP_ERR_HIP,
+ TSP_ERR_SCRATCH) = range(8)
+NOALLOC_SCRATCH_BYTES = 96 * 1024 * 1024
 (WS_ATTN, WS_MLP, WS_LAYER, WS_POST, WS_CORE, WS_OUT_SHARD, WS_MLP_SHARD, WS_MLP_BWD, WS_ATTN_BWD, WS_OUT_BWD,
  WS_PROJ_BWD, WS_RMS_BWD) = range(12)
 MAX_D = 16
@@ -27,7 +29,8 @@ EXPORTS = ["tsp_zigzag_plan", "tsp_workspace_size", "tsp_attn_project", "tsp_att
            "tsp_attn_out_shard", "tsp_mlp_shard", "tsp_rms_norm", "tsp_rope", "tsp_attn_project_gqa",
            "tsp_attn_core_gqa", "tsp_mlp_backward", "tsp_attn_core_lse", "tsp_attn_core_backward",
            "tsp_attn_out_backward", "tsp_attn_project_backward", "tsp_rope_backward", "tsp_rms_norm_backward",
-           "tsp_attn_core_gqa_lse", "tsp_attn_core_gqa_backward", "tsp_memory_footprint", "tsp_status_string"]
+           "tsp_attn_core_gqa_lse", "tsp_attn_core_gqa_backward", "tsp_memory_footprint", "tsp_status_string",
+           "tsp_attn_forward_noalloc"]
 MEM_TSP, MEM_TP = range(2)
 
 
@@ -69,6 +72,7 @@ def lib() -> ctypes.CDLL:
             "tsp_attn_core": [POINTER(Plan), POINTER(Dims), P, P, P, P, P, P, c_size_t, P],
             "tsp_attn_out": [c_int64, POINTER(Dims), c_int32, c_int32, P, P, PP, P, P, P],
             "tsp_attn_forward": [POINTER(Plan), POINTER(Dims), P, PP, PP, P, P, P, P, P, c_size_t, P],
+            "tsp_attn_forward_noalloc": [POINTER(Plan), POINTER(Dims), P, PP, PP, P, P, P, P, P],
             "tsp_mlp_forward": [c_int64, POINTER(Dims), c_int32, c_int32, P, PP, PP, P, P, P, c_size_t, P],
             "tsp_layer_post": [c_int64, POINTER(Dims), c_int32, c_int32, P, P, P, PP, PP, PP, P, P, c_size_t, P],
             "tsp_layer_forward": [POINTER(Plan), POINTER(Dims), P, PP, PP, PP, PP, P, P, P, P, c_size_t, P],
@@ -272,6 +276,19 @@ def attn_forward(plan: Plan, dims: Dims, x_local, wqkv, wo, k_full, v_full, resi
             _dev_tensor(out, (n, h), "out"))
     _check(lib().tsp_attn_forward(ctypes.byref(plan), ctypes.byref(dims), *args, ws, nbytes, _stream(stream)),
            "tsp_attn_forward")
+
+
+def attn_forward_noalloc(plan: Plan, dims: Dims, x_local, wqkv, wo, k_full, v_full, residual, out, stream=None):
+    """tsp_attn_forward with its scratch in the library's fixed device array
+    (no workspace argument; see tsp_attn_forward_noalloc in tsp.h)."""
+    n, h, S, D = plan.n_local, dims.hidden, plan.seq_len, plan.D
+    Hs = dims.n_heads // D if D > 0 else 0
+    args = (_dev_tensor(x_local, (n, h), "x_local"), _shards(wqkv, D, (3 * Hs * dims.head_dim, h), "wqkv"),
+            _shards(wo, D, (h, Hs * dims.head_dim), "wo"), _dev_tensor(k_full, (S, h), "k_full"),
+            _dev_tensor(v_full, (S, h), "v_full"), _opt_tensor(residual, (n, h), "residual"),
+            _dev_tensor(out, (n, h), "out"))
+    _check(lib().tsp_attn_forward_noalloc(ctypes.byref(plan), ctypes.byref(dims), *args, _stream(stream)),
+           "tsp_attn_forward_noalloc")
 
 
 def mlp_forward(dims: Dims, D: int, start_shard: int, x, w1, w2, residual, y, workspace, stream=None):

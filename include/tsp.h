@@ -55,7 +55,8 @@ typedef enum {
   TSP_ERR_ALIGNMENT = 3,   /* a device pointer is not 16-byte aligned */
   TSP_ERR_WORKSPACE = 4,   /* workspace null or smaller than tsp_workspace_size() */
   TSP_ERR_UNSUPPORTED = 5, /* valid for the method but not implemented (head_dim, widths) */
-  TSP_ERR_HIP = 6          /* a kernel launch failed */
+  TSP_ERR_HIP = 6,         /* a kernel launch failed */
+  TSP_ERR_SCRATCH = 7      /* more scratch than the fixed array of tsp_attn_forward_noalloc */
 } tsp_status;
 
 /* Rank's share of the sequence (plain data, host memory). */
@@ -291,6 +292,29 @@ tsp_status tsp_attn_forward(const tsp_plan* plan, const tsp_dims* dims, const ui
                             const uint16_t* const* wqkv, const uint16_t* const* wo,
                             uint16_t* k_full, uint16_t* v_full, const uint16_t* residual,
                             uint16_t* out, void* workspace, size_t ws_bytes, hipStream_t stream);
+
+/*
+ * tsp_attn_forward without a workspace argument, for callers that cannot
+ * allocate device memory (code under HIP graph capture, serving loops that
+ * must not call hipMalloc, harnesses that forbid it).  The scratch that
+ * tsp_attn_forward takes from its workspace (Q, the attention output as a bf16
+ * pair, the split partials of short sequences: tsp_workspace_size(n_local,
+ * dims, D, TSP_WS_ATTN) bytes) lives in a fixed device array of the library of
+ * TSP_NOALLOC_SCRATCH_BYTES (96 MiB) per GPU, held until the process ends; a
+ * call that needs more returns TSP_ERR_SCRATCH and enqueues nothing (the 7B
+ * attention half fits at 2048 local tokens, 84 MB; not at 16384).
+ * Every call on one GPU uses that GPU's one array: calls that overlap on one
+ * GPU (other streams, other threads) race and must be ordered by the caller.
+ * Nothing in the array needs to start at zero: each call writes every byte it
+ * reads.  The array's device address is resolved on the first call on each
+ * device (hipGetSymbolAddress, with that device current); make that first call
+ * before capturing a graph.  Arguments, results and other errors as
+ * tsp_attn_forward.
+ */
+#define TSP_NOALLOC_SCRATCH_BYTES (96u * 1024u * 1024u)
+tsp_status tsp_attn_forward_noalloc(const tsp_plan* plan, const tsp_dims* dims, const uint16_t* x_local,
+                                    const uint16_t* const* wqkv, const uint16_t* const* wo, uint16_t* k_full,
+                                    uint16_t* v_full, const uint16_t* residual, uint16_t* out, hipStream_t stream);
 
 /*
  * MLP with the shard pairs in ring order (para. 2): the shard loop is a split-K

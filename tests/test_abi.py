@@ -35,7 +35,7 @@ def test_exports_every_declared_symbol(L):
 
 
 def test_status_strings(L):
-    for s in range(7):
+    for s in range(8):
         assert tsp.status_string(s).startswith("TSP_")
     assert "unknown" in tsp.status_string(99)
 
@@ -149,6 +149,23 @@ def test_core_rejects(L):
     assert L.tsp_attn_core(ctypes.byref(p), ctypes.byref(d), A, A, A, A + 64, None, A + 128, need - 1, None) == tsp.TSP_ERR_WORKSPACE
     assert L.tsp_attn_core(ctypes.byref(p), ctypes.byref(d), A, A, A, A + 64, None, None, need, None) == tsp.TSP_ERR_WORKSPACE
     assert L.tsp_attn_core(ctypes.byref(p), ctypes.byref(d), A, A, A, A + 64, None, MIS, need, None) == tsp.TSP_ERR_ALIGNMENT
+
+
+def test_noalloc_rejects(L):
+    """tsp_attn_forward_noalloc: a call that needs more scratch than the fixed
+    array returns TSP_ERR_SCRATCH before any HIP call; invalid plans or dims
+    return tsp_attn_forward's statuses (argument checks only, no GPU)."""
+    d = tsp.make_dims(4096, 32, 128, 16384)
+    p, _, _ = tsp.zigzag_plan(131072, 8, 0)
+    assert tsp.workspace_size(p.n_local, d, 8, tsp.WS_ATTN) > tsp.NOALLOC_SCRATCH_BYTES
+    w = _arr([A] * 8)
+    call = lambda plan, dims: L.tsp_attn_forward_noalloc(plan, dims, A, w, w, A + 64, A + 128, None, A + 192, None)
+    assert call(ctypes.byref(p), ctypes.byref(d)) == tsp.TSP_ERR_SCRATCH
+    assert call(None, ctypes.byref(d)) == tsp.TSP_ERR_INVALID_ARG
+    assert call(ctypes.byref(p), None) == tsp.TSP_ERR_INVALID_ARG
+    bad = tsp.make_dims(4096, 32, 96, 16384)
+    assert call(ctypes.byref(p), ctypes.byref(bad)) == tsp.TSP_ERR_SHAPE
+    assert "fixed array" in tsp.status_string(tsp.TSP_ERR_SCRATCH)
 
 
 def test_core_workspace_none_on_large_grids(L):
