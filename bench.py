@@ -16,16 +16,16 @@ The step calls the three entry points that tsp_layer_forward composes
 between them on the launch stream.
 
 Roofline.  The dominant kernel is the attention core (about 73% of the
-layer's FLOPs).  Its roofline figure is taken on unit-scale inputs: before
-any other attention work, the core is launched on layer 0's inputs (x ~ N(0,1),
-the layer's generated K/V) once untimed and then ``--roofline-launches`` times,
-each bracketed by HIP events on the launch stream.  The layer has no norm, so
-in the chained steps the activations grow about 2.5x per layer and the
-softmax rows of later layers are close to one-hot, which makes the same kernel
-faster; that chained per-launch figure is reported beside it
-(``roofline.chained``).  Because the unit-scale launches are the run's first
-attention dispatches, a ``--kernel-trace`` profile of this command averages
-exactly them (profile_summary ``--first``).
+layer's FLOPs).  Its roofline figure is taken on unit-scale inputs: after the
+warmup steps and before the timed ones, the core is launched on layer 0's
+inputs (x ~ N(0,1), the layer's generated K/V) twice untimed and then
+``--roofline-launches`` times, each bracketed by HIP events on the launch
+stream.  The layer has no norm, so in the chained steps the activations grow
+about 2.5x per layer and the softmax rows of later layers are close to
+one-hot, which makes the same kernel faster; that chained per-launch figure is
+reported beside it (``roofline.chained``).  A ``--kernel-trace`` profile of
+this command averages exactly the timed unit-scale launches by their place in
+the dispatch order (profile_summary ``--first``/``--skip``).
 
 ``stream_7b_16k``: the weight-streaming regime, timed in the same run (S =
 16384, 2048 local tokens, 32 distinct layers whose 402.65 MB of weights each
@@ -334,16 +334,23 @@ class Stack:
         return elapsed * 1e3 / steps, stage_ms, first_ms
 
 
+ROOF_UNTIMED = 2  # untimed unit-scale launches before the timed ones
+
+
 def unit_scale_attention(stack, stream, launches):
     """The roofline figure's launches: tsp_attn_core on layer 0's unit-scale
     inputs (Q projected from x0, the layer's generated K/V with the rank's own
-    rows), one untimed, then `launches` each between HIP events on the launch
-    stream.  Returns the mean ms per launch."""
+    rows), ROOF_UNTIMED untimed, then `launches` each between HIP events on the
+    launch stream.  Made after the warmup steps (the chip in its sustained
+    state) and before the timed steps, so in a kernel trace of the command they
+    are the attention dispatches warmup*layers + ROOF_UNTIMED + 1 ..
+    warmup*layers + ROOF_UNTIMED + launches.  Returns the mean ms per launch."""
     lw, kf, vf = stack.layers[0]
     tsp.attn_project(stack.plan, stack.dims, stack.x0, lw.wqkv, kf, vf, stack.q)
     call = lambda: tsp.attn_core(stack.plan, stack.dims, stack.q, kf, vf, stack.a, stack.a_lo,
                                  workspace=stack.ws_core)
-    call()
+    for _ in range(ROOF_UNTIMED):
+        call()
     ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(launches)]
     for e0, e1 in ev:
         e0.record(stream)
@@ -472,14 +479,18 @@ def main():
         del src, dst
 
     summary, unit = TRAFFIC_SUMMARY[args.workload]
+    print(f"[bench] warmup {args.warmup}", file=sys.stderr, flush=True)
+    for _ in range(args.warmup):
+        main_stack.step(stream)
+    torch.cuda.synchronize()
     unit_ms = None
     if unit == "tsp_attn_core":
-        print(f"[bench] roofline: 1 + {args.roofline_launches} unit-scale launches of tsp_attn_core",
+        print(f"[bench] roofline: {ROOF_UNTIMED} + {args.roofline_launches} unit-scale launches of tsp_attn_core",
               file=sys.stderr, flush=True)
         unit_ms = unit_scale_attention(main_stack, stream, args.roofline_launches)
 
-    print(f"[bench] warmup {args.warmup}, timing {args.steps} steps", file=sys.stderr, flush=True)
-    ms_per_step, stage_ms, first_ms = main_stack.timed(stream, args.steps, args.warmup)
+    print(f"[bench] timing {args.steps} steps", file=sys.stderr, flush=True)
+    ms_per_step, stage_ms, first_ms = main_stack.timed(stream, args.steps, 0)
     fl_rows = main_stack.fl
     fl = dict(fl_rows)
     fl["post"] = fl.pop("oproj") + fl.pop("mlp")
@@ -488,7 +499,7 @@ def main():
     total_flops = sum(fl.values())
 
     if unit == "tsp_attn_core":
-        roof = {"kernel": "tsp_attn_core (vt_prep_kernel + attn_kernel<128, false>), unit-scale layer-0 inputs",
+        roof = {"kernel": "tsp_attn_core (attn_kernel<128, false>), unit-scale layer-0 inputs",
                 "flops": fl["attn"], "ms": unit_ms}
     else:
         roof = {"kernel": "tsp_layer_forward (QKV, attention, O projection, MLP)", "flops": total_flops,

@@ -7,9 +7,9 @@ Reads the CSV output of three rocprofv3 runs of the same ``bench.py`` command:
 * ``--pmc FETCH_SIZE`` and ``--pmc WRITE_SIZE`` (``*_counter_collection.csv``):
   KiB per dispatch.
 
-A summary covers one unit: an entry point's kernels (``tsp_attn_core`` launches
-``vt_prep_kernel`` then ``attn_kernel``), whose per-launch durations and bytes
-are summed.  With ``--first N --skip K`` the durations come from the
+A summary covers one unit: an entry point's kernels (``tsp_attn_core``
+launches ``attn_kernel``, and for short sequences ``attn_combine_kernel``),
+whose per-launch durations and bytes are summed.  With ``--first N --skip K`` the durations come from the
 per-dispatch kernel trace (``*_kernel_trace.csv``) instead: the first N
 dispatches of each of the unit's kernels, in dispatch order, less the first K
 of them (the benchmark makes its unit-scale roofline launches of the attention
@@ -46,7 +46,7 @@ CSRC = os.path.join(PKG, "csrc")
 # definition of struct Name in kernels.h only (the arguments the kernels read),
 # so that unrelated declarations added there leave a summary valid.
 UNITS = {
-    "tsp_attn_core": (["vt_prep_kernel", "attn_kernel", "attn_combine_kernel"],
+    "tsp_attn_core": (["attn_kernel", "attn_combine_kernel"],
                       ["attention.hip", "device_common.h", "kernels.h:AttnArgs"]),
     "attn_kernel": (["attn_kernel"], ["attention.hip", "device_common.h", "kernels.h:AttnArgs"]),
     "gemm_kernel": (["gemm_kernel"], ["gemm.hip", "device_common.h", "kernels.h:GemmArgs"]),
@@ -55,7 +55,7 @@ UNITS = {
     "tsp_attn_core_backward": (["bwd_stats_kernel", "dkv_kernel", "dq_kernel"],
                                ["attn_backward.hip", "device_common.h", "kernels.h:AttnBwdArgs"]),
     # one whole forward layer (tsp_attn_project + tsp_attn_core + tsp_layer_post)
-    "tsp_layer_forward": (["gemm_kernel", "vt_prep_kernel", "attn_kernel", "attn_combine_kernel", "row_prep_kernel",
+    "tsp_layer_forward": (["gemm_kernel", "attn_kernel", "attn_combine_kernel", "row_prep_kernel",
                            "bf16_to_f16_kernel"],
                           ["gemm.hip", "attention.hip", "prep.hip", "device_common.h", "kernels.h:GemmArgs",
                            "kernels.h:AttnArgs"]),
