@@ -54,16 +54,55 @@ struct Cfg {
   static_assert(A_LOADS >= 1 && B_LOADS >= 1 && A_BYTES % (NT * 16) == 0 && B_BYTES % (NT * 16) == 0, "tile split");
 };
 
-// Epilogue of 8 consecutive output columns of one row (fp32 values v[0..7]):
-// GELU (stored as fp16 scaled by 2^-row_exp) / row rescale and residual /
-// Q-K-V routing, then 16-byte stores.  `col` is the column inside the shard's
-// N_s block and a multiple of 8, so the 8 values never straddle a head or a
-// Q/K/V part (head_dim is a multiple of 32).
+// Inputs that the epilogue of 8 consecutive output columns of one row reads
+// from memory (the residual or the GELU inputs as raw bits, the row's
+// exponent), loaded one 32-row strip ahead of their use so that their latency
+// overlaps the staging of the previous strip.
+struct EpiIn {
+  u32x4 a, b;  // EPI_RESID: residual (bf16: a; fp32: a, b); EPI_DGELU: aux (a, b)
+  int e;       // row exponent (EPI_RESID, EPI_GELU)
+};
+
+// Offset of output element (row, col) of shard column block nshard in the
+// default output / residual layout: row * ldo + nshard * N_s + col.
+__device__ __forceinline__ int64_t epi_index(const GemmArgs& g, int nshard, int row, int col) {
+  return (int64_t)row * g.ldo + (int64_t)nshard * g.N_s + col;
+}
+
 template <int EPI>
-__device__ __forceinline__ void store_row8(const GemmArgs& g, int nshard, int row, int col, float* v) {
+__device__ __forceinline__ void load_row8(const GemmArgs& g, int nshard, int row, int col, EpiIn& in) {
+  if constexpr (EPI == EPI_RESID) {
+    in.e = g.row_exp ? g.row_exp[row] : 0;
+    if (g.residual) {
+      const int64_t idx = epi_index(g, nshard, row, col);
+      if (g.res_f32) {
+        const float* rp = static_cast<const float*>(g.residual) + idx;
+        in.a = *reinterpret_cast<const u32x4*>(rp);
+        in.b = *reinterpret_cast<const u32x4*>(rp + 4);
+      } else {
+        in.a = *reinterpret_cast<const u32x4*>(static_cast<const uint16_t*>(g.residual) + idx);
+      }
+    }
+  } else if constexpr (EPI == EPI_DGELU) {
+    const float* up = g.aux + (int64_t)row * g.N_s + col;
+    in.a = *reinterpret_cast<const u32x4*>(up);
+    in.b = *reinterpret_cast<const u32x4*>(up + 4);
+  } else if constexpr (EPI == EPI_GELU) {
+    in.e = g.row_exp ? g.row_exp[row] : 0;
+  }
+}
+
+// Epilogue of 8 consecutive output columns of one row (fp32 values v[0..7],
+// inputs `in` from load_row8): GELU (stored as fp16 scaled by 2^-row_exp) /
+// row rescale and residual / Q-K-V routing, then 16-byte stores.  `col` is the
+// column inside the shard's N_s block and a multiple of 8, so the 8 values
+// never straddle a head or a Q/K/V part (head_dim is a multiple of 32).
+template <int EPI>
+__device__ __forceinline__ void store_row8(const GemmArgs& g, int nshard, int row, int col, float* v,
+                                           const EpiIn& in) {
   u32x4 packed;
   if constexpr (EPI == EPI_RESID) {  // N-sharded: shard nshard writes column block nshard of the output
-    const int64_t idx = (int64_t)row * g.ldo + (int64_t)nshard * g.N_s + col;
+    const int64_t idx = epi_index(g, nshard, row, col);
     void* outp = g.out;  // separate output buffers per shard or per row block
     int64_t oidx = idx;
     if (g.outs[0]) {
@@ -77,26 +116,21 @@ __device__ __forceinline__ void store_row8(const GemmArgs& g, int nshard, int ro
       }
     }
     if (g.row_exp) {
-      const int e = g.row_exp[row];
 #pragma unroll
-      for (int j = 0; j < 8; ++j) v[j] = __builtin_amdgcn_ldexpf(v[j], e);
+      for (int j = 0; j < 8; ++j) v[j] = __builtin_amdgcn_ldexpf(v[j], in.e);
     }
     if (g.residual) {
       if (g.res_f32) {
-        const float* rp = static_cast<const float*>(g.residual) + idx;
-        const f32x4 r0 = *reinterpret_cast<const f32x4*>(rp);
-        const f32x4 r1 = *reinterpret_cast<const f32x4*>(rp + 4);
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
-          v[j] += r0[j];
-          v[4 + j] += r1[j];
+          v[j] += __uint_as_float(in.a[j]);
+          v[4 + j] += __uint_as_float(in.b[j]);
         }
       } else {
-        const u32x4 r = *reinterpret_cast<const u32x4*>(static_cast<const uint16_t*>(g.residual) + idx);
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
-          v[2 * j] += __uint_as_float(r[j] << 16);
-          v[2 * j + 1] += __uint_as_float(r[j] & 0xffff0000u);
+          v[2 * j] += __uint_as_float(in.a[j] << 16);
+          v[2 * j + 1] += __uint_as_float(in.a[j] & 0xffff0000u);
         }
       }
     }
@@ -110,27 +144,22 @@ __device__ __forceinline__ void store_row8(const GemmArgs& g, int nshard, int ro
       *reinterpret_cast<u32x4*>(static_cast<uint16_t*>(outp) + oidx) = packed;
     }
   } else if constexpr (EPI == EPI_DGELU) {
-    const float* up = g.aux + (int64_t)row * g.N_s + col;
-    const f32x4 u0 = *reinterpret_cast<const f32x4*>(up);
-    const f32x4 u1 = *reinterpret_cast<const f32x4*>(up + 4);
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
-      v[j] *= gelu_tanh_grad(u0[j]);
-      v[4 + j] *= gelu_tanh_grad(u1[j]);
+      v[j] *= gelu_tanh_grad(__uint_as_float(in.a[j]));
+      v[4 + j] *= gelu_tanh_grad(__uint_as_float(in.b[j]));
     }
 #pragma unroll
     for (int j = 0; j < 4; ++j) packed[j] = pack_bf16x2(v[2 * j], v[2 * j + 1]);
-    *reinterpret_cast<u32x4*>(static_cast<uint16_t*>(g.out) + (int64_t)row * g.ldo + (int64_t)nshard * g.N_s +
-                              col) = packed;
+    *reinterpret_cast<u32x4*>(static_cast<uint16_t*>(g.out) + epi_index(g, nshard, row, col)) = packed;
   } else if constexpr (EPI == EPI_GELU) {
-    const int e = g.row_exp ? g.row_exp[row] : 0;
+    const int e = in.e;
     const int e_in = g.gelu_in_scaled ? e : 0;
 #pragma unroll
     for (int j = 0; j < 4; ++j)
       packed[j] = pack_f16x2_sat(__builtin_amdgcn_ldexpf(gelu_tanh(__builtin_amdgcn_ldexpf(v[2 * j], e_in)), -e),
                                  __builtin_amdgcn_ldexpf(gelu_tanh(__builtin_amdgcn_ldexpf(v[2 * j + 1], e_in)), -e));
-    *reinterpret_cast<u32x4*>(static_cast<uint16_t*>(g.out) + (int64_t)row * g.ldo + (int64_t)nshard * g.N_s +
-                              col) = packed;
+    *reinterpret_cast<u32x4*>(static_cast<uint16_t*>(g.out) + epi_index(g, nshard, row, col)) = packed;
   } else {
 #pragma unroll
     for (int j = 0; j < 4; ++j) packed[j] = pack_bf16x2(v[2 * j], v[2 * j + 1]);
@@ -304,15 +333,37 @@ __global__ __launch_bounds__((Cfg<BM, BN>::NT)) void gemm_kernel(const GemmArgs 
   // stores are 16-byte row segments.  The 32x32 accumulator layout: lane holds
   // column (lane % 32) and rows 8*(e/4) + 4*(lane/32) + e%4 of its 16 values e.
   // Each wave stages one 32-row strip of its sub-tile at a time in fp32
-  // ([32][WN + 4] floats), then reads it back as 8-column row pieces.
+  // ([32][WN + 4] floats), then reads it back as 8-column row pieces.  The
+  // memory inputs of a strip's pieces (residual, GELU inputs, row exponents)
+  // are loaded while the previous strip is staged and stored, so each tile
+  // waits for that latency once instead of once per piece.
   {
     constexpr int SLD = C::WN + 4;  // padded fp32 row
     float* stage = reinterpret_cast<float*>(smem) + wave * 32 * SLD;
     const int col_l = lane & 31;
     const int row_l = 4 * (lane >> 5);
     constexpr int PIECES = 32 * (C::WN / 8);  // 8-column pieces in a strip
+    constexpr int PPL = PIECES / 64;          // pieces per lane
+    auto piece_rc = [&](int i, int it, int& row, int& col, int& r, int& c8) __attribute__((always_inline)) {
+      const int piece = it * 64 + lane;
+      r = piece / (C::WN / 8);
+      c8 = (piece - r * (C::WN / 8)) * 8;
+      row = m0 + wm * C::WM + i * 32 + r;
+      col = n0 + wn * C::WN + c8;
+    };
+    EpiIn in[2][PPL];
+    auto load_strip = [&](int i, EpiIn (&dst)[PPL]) __attribute__((always_inline)) {
+#pragma unroll
+      for (int it = 0; it < PPL; ++it) {
+        int row, col, r, c8;
+        piece_rc(i, it, row, col, r, c8);
+        if (row < g.M && col < g.N_s) load_row8<EPI>(g, nshard, row, col, dst[it]);
+      }
+    };
+    load_strip(0, in[0]);
 #pragma unroll
     for (int i = 0; i < C::FM; ++i) {
+      if (i + 1 < C::FM) load_strip(i + 1, in[(i + 1) & 1]);
 #pragma unroll
       for (int j = 0; j < C::FN; ++j)
 #pragma unroll
@@ -320,18 +371,15 @@ __global__ __launch_bounds__((Cfg<BM, BN>::NT)) void gemm_kernel(const GemmArgs 
           stage[(8 * (e >> 2) + row_l + (e & 3)) * SLD + j * 32 + col_l] = acc[i][j][e];
       __syncthreads();
 #pragma unroll
-      for (int it = 0; it < PIECES / 64; ++it) {
-        const int piece = it * 64 + lane;
-        const int r = piece / (C::WN / 8);
-        const int c8 = (piece - r * (C::WN / 8)) * 8;
-        const int row = m0 + wm * C::WM + i * 32 + r;
-        const int col = n0 + wn * C::WN + c8;
+      for (int it = 0; it < PPL; ++it) {
+        int row, col, r, c8;
+        piece_rc(i, it, row, col, r, c8);
         float v[8];
         const f32x4 lo = *reinterpret_cast<const f32x4*>(stage + r * SLD + c8);
         const f32x4 hi = *reinterpret_cast<const f32x4*>(stage + r * SLD + c8 + 4);
 #pragma unroll
         for (int k = 0; k < 4; ++k) { v[k] = lo[k]; v[4 + k] = hi[k]; }
-        if (row < g.M && col < g.N_s) store_row8<EPI>(g, nshard, row, col, v);
+        if (row < g.M && col < g.N_s) store_row8<EPI>(g, nshard, row, col, v, in[i & 1][it]);
       }
       __syncthreads();
     }
