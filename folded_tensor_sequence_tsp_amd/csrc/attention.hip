@@ -139,7 +139,25 @@ __global__ __launch_bounds__(128) void vt_prep_kernel(const uint16_t* __restrict
 template <int HD, bool SPLIT>
 __global__ __launch_bounds__(NTHREADS) void attn_kernel(const AttnArgs a) {
   using C = ACfg<HD>;
-  __shared__ __attribute__((aligned(1024))) uint8_t smem[NSTAGE * C::STAGE_BYTES];
+  // The ring's stages are four distinct arrays, and every access names its
+  // stage statically (the tile loops are unrolled by four): the compiler then
+  // knows that a transposing read of one stage does not alias the DMA filling
+  // another, and does not make it wait for every load in flight (it does when
+  // they may alias, as for offsets into one array).
+  __shared__ __attribute__((aligned(1024))) uint8_t stage0[C::STAGE_BYTES];
+  __shared__ __attribute__((aligned(1024))) uint8_t stage1[C::STAGE_BYTES];
+  __shared__ __attribute__((aligned(1024))) uint8_t stage2[C::STAGE_BYTES];
+  __shared__ __attribute__((aligned(1024))) uint8_t stage3[C::STAGE_BYTES];
+  static_assert(NSTAGE == 4, "one array per stage");
+  // stage J (a compile-time constant) holds the tiles t_begin + J, + J + 4, ...
+  auto stage_of = [&](auto J) __attribute__((always_inline)) -> uint8_t* {
+    constexpr int j = decltype(J)::value & 3;
+    if constexpr (j == 0) return stage0;
+    else if constexpr (j == 1) return stage1;
+    else if constexpr (j == 2) return stage2;
+    else return stage3;
+  };
+
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -226,15 +244,17 @@ __global__ __launch_bounds__(NTHREADS) void attn_kernel(const AttnArgs a) {
   const uint16_t* k_head = a.k + kcol;
   const uint16_t* v_head = a.v + kcol;
 
-  auto issue_tile = [&](int t) __attribute__((always_inline)) {
-    uint8_t* stage = smem + (t % NSTAGE) * C::STAGE_BYTES;
+  // WHOLE: the caller knows that the tile lies inside the key range (no
+  // branch on it).
+  auto issue_tile = [&](int t, auto J, auto WHOLE) __attribute__((always_inline)) {
+    uint8_t* stage = stage_of(J);
     const int64_t k0 = (int64_t)t * BKV;
     // bytes from the tile's first row (head column) to the end of the sequence
     const int64_t span = (a.seq_len - k0) * kld * 2 - (int64_t)kcol * 2;
     const uint32_t bytes = (uint32_t)min(span, (int64_t)0x7fffffff);
     const __amdgpu_buffer_rsrc_t rk = buffer_rsrc(k_head + k0 * kld, bytes);
     const __amdgpu_buffer_rsrc_t rv = buffer_rsrc(v_head + k0 * kld, bytes);
-    if (k0 + BKV <= key_end) {  // whole tile inside the key range (wave-uniform)
+    if (decltype(WHOLE)::value || k0 + BKV <= key_end) {  // whole tile inside the key range (wave-uniform)
 #pragma unroll
       for (int i = 0; i < C::K_LOADS; ++i) dma16_buf(rk, k_off[i], stage + (i * NW + wave) * 1024);
 #pragma unroll
@@ -274,27 +294,32 @@ __global__ __launch_bounds__(NTHREADS) void attn_kernel(const AttnArgs a) {
     vr_b = C::K_BYTES + (uint32_t)kb * C::ROW_BYTES + piece;
   }
 
-  // S^T for tile t: lane holds query ql, keys 8*(e/4) + 4*half + e%4 of each 32-key block.
-  auto compute_s = [&](int t, f32x16 (&s)[2]) __attribute__((always_inline)) {
-    const uint8_t* stage = smem + (t % NSTAGE) * C::STAGE_BYTES;
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb) {
-      s[kb] = f32x16{};
-#pragma unroll
-      for (int kk = 0; kk < C::KK; ++kk) {
-        const u32x4 kf = *reinterpret_cast<const u32x4*>(stage + kb * 32 * C::ROW_BYTES + (k_a0 ^ (uint32_t)(kk << 5)));
-        s[kb] = mfma32(as_bf16x8(kf), qf[kk], s[kb]);
-      }
-    }
-  };
-
-  // ---- running state: m = running reference max of the raw scores (the
-  // exponent of a score s is (s - m) * scale_log2), l = lane-partial sum of
-  // the probabilities.
+  // ---- running state: m = running reference max of the raw scores, l =
+  // lane-partial sum of the probabilities, relative to the reference r (log2
+  // units): a probability is 2^(s * scale_log2 - r).
+  //   * fma form (|m * scale_log2| < 2^10): r = mc = fl(m * scale_log2) and
+  //     the exponent is one fma, s * scale_log2 - mc rounded once.  mc differs
+  //     from m * scale_log2 by d, at most half its ulp (2^-14): a factor 2^d
+  //     common to every probability of the row, which cancels in O / l and is
+  //     part of the stored normaliser.  The bound keeps d negligible where it
+  //     does not cancel: the max's probability 2^d enters O rounded to bf16
+  //     but l in fp32, a relative error of about d ln 2 (at most 2^-9 for a
+  //     larger d), which matters in rows that one key dominates.
+  //   * exact form (larger scores, as in a deep stack without a norm):
+  //     r = m * scale_log2 and the exponent is (s - m) * scale_log2, whose
+  //     difference is exact near the max, so the exponent of the max is
+  //     exactly 0 at any magnitude.
+  // The form is wave-uniform and only moves from fma to exact.
   constexpr float inv_sqrt_hd = HD == 128 ? 0.08838834764831844055f : 0.125f;
   const float scale_log2 = 1.44269504088896340736f * inv_sqrt_hd;
   const float tau_raw = LAZY_TAU / scale_log2;  // the rescale threshold in raw score units
+  constexpr float FMA_LIMIT = 1024.0f;          // 2^10: |mc| below it keeps the fma form
+  // A lane's 32 probabilities of a tile sum to at most 2^13 while none exceeds
+  // 2^LAZY_TAU; above it (or non-finite) the fma form's tile is redone.
+  constexpr float LSUM_MAX = 8192.0f;
   float m_run = -INFINITY;
+  float mc = -INFINITY;  // fl(m_run * scale_log2)
+  bool exact = false;    // wave-uniform
   float l_run = 0.0f;
   f32x16 o[C::DT];
 #pragma unroll
@@ -326,42 +351,127 @@ __global__ __launch_bounds__(NTHREADS) void attn_kernel(const AttnArgs a) {
     return pair_max(mx);
   };
 
-  // The fused block of a step: S of tile t+1 as two interleaved MFMA chains
-  // (the two 32-key blocks) over the head_dim steps, with the K fragments of
-  // the next step read before the current MFMAs and the exponentials of tile
-  // t's keys 0..31 spread over the steps; then PV of tile t as DT independent
-  // chains over the four 16-key steps, V fragments again one step ahead, the
-  // exponentials of keys 32..63 under its first two steps and the max of tile
-  // t+1's (unmasked) scores under the last two.  The vector work is
-  // split so that each MFMA carries a few vector instructions (co-issued), and
-  // LDS latency hides behind MFMAs.
-  auto fused_block = [&](int t, f32x16 (&s_cu)[2], f32x16 (&s_nx)[2], float& mt) __attribute__((always_inline)) {
-    const uint8_t* kst = smem + ((t + 1) % NSTAGE) * C::STAGE_BYTES;
-    const uint8_t* vst = smem + (t % NSTAGE) * C::STAGE_BYTES;
-    auto kfrag = [&](int kb, int kk) __attribute__((always_inline)) {
-      return *reinterpret_cast<const u32x4*>(kst + kb * 32 * C::ROW_BYTES + (k_a0 ^ (uint32_t)(kk << 5)));
-    };
+  // ---- ping-pong schedule.  Per tile t every wave runs two phases, each
+  // ended by a workgroup barrier:
+  //   softmax(t): mask (diagonal tiles), max, lazy rescale, exponentials and
+  //               row sum of its scores S(t) -> P(t) as bf16 pairs (vector work);
+  //   matmul(t):  load tile t+3, O += V(t)^T P(t), S(t+1) = K(t+1) Q^T
+  //               (32 MFMAs), then wait for this wave's loads of tile t+2.
+  // Waves 4-7 pass one extra barrier before their first phase and waves 0-3
+  // one after their last, so waves 4-7 run one phase behind waves 0-3: with
+  // one wave of each group per SIMD, one wave's MFMAs run while the other's
+  // vector work issues beside them.  Both groups run the same code.
+  // Stage J of the ring holds tiles t_begin + J (mod 4).  Tile t+3 refills the
+  // stage of tile t-1, whose last reader (a group-1 matmul(t-1)) ended before
+  // a group-0 matmul(t) starts; tile t+1, read by matmul(t), was waited for by
+  // every wave in its matmul(t-1), before the barrier that precedes a group-0
+  // matmul(t).
+  const int grp = wave >> 2;                     // one wave of each group per SIMD
+  const int wave_last = min(wave_tiles, t_end);  // tiles t < wave_last are computed by this wave
+  f32x16 s[2];      // scores S(t) of the wave's current tile
+  uint32_t pk[16];  // P(t): bf16 pairs, pk[4*ks + j] holds keys of 16-key step ks
+
+  // Probabilities of the scores s in the fma or the exact form -> pk, and
+  // their lane sum.
+  auto probs = [&](auto EXACT) __attribute__((always_inline)) {
+    float lsum = 0.0f;
+#pragma unroll
+    for (int idx = 0; idx < 16; ++idx) {
+      const int kb = idx >> 3, e = (2 * idx) & 15;
+      float p0, p1;
+      if constexpr (decltype(EXACT)::value) {
+        p0 = __builtin_amdgcn_exp2f((s[kb][e] - m_run) * scale_log2);
+        p1 = __builtin_amdgcn_exp2f((s[kb][e + 1] - m_run) * scale_log2);
+      } else {
+        p0 = __builtin_amdgcn_exp2f(__builtin_fmaf(s[kb][e], scale_log2, -mc));
+        p1 = __builtin_amdgcn_exp2f(__builtin_fmaf(s[kb][e + 1], scale_log2, -mc));
+      }
+      lsum += p0 + p1;
+      pk[idx] = pack_bf16x2(p0, p1);
+    }
+    return lsum;
+  };
+
+  // Softmax of tile t: in the fma form the probabilities are taken against
+  // the current reference straight away, and the tile is redone only when a
+  // lane's sum says that some score exceeds the reference by more than
+  // 2^LAZY_TAU (a new max; the first tile, whose reference is -inf, always).
+  // Redone, or in the exact form: the tile max, the lazy rescale (the
+  // reference moves only when the max exceeds it by more than LAZY_TAU in
+  // log2 units, so probabilities stay below 2^8), then the probabilities.
+  auto softmax = [&](int t, auto masked) __attribute__((always_inline)) {
+    if constexpr (decltype(masked)::value) mask_tile(t, s);
+    float lsum = 0.0f;
+    bool done = false;
+    if (!exact) {
+      lsum = probs(std::false_type{});
+      done = __builtin_amdgcn_ballot_w64(!(lsum <= LSUM_MAX)) == 0;  // wave-uniform
+    }
+    if (!done) {  // rare in the fma form
+      const float mt = tile_max(s);
+      if (__builtin_amdgcn_ballot_w64(mt > m_run + tau_raw) != 0) {  // wave-uniform
+        const float m_new = fmaxf(m_run, mt);
+        const float mc_new = m_new * scale_log2;
+        const bool exact_new = exact || __builtin_amdgcn_ballot_w64(!(fabsf(mc_new) < FMA_LIMIT)) != 0;
+        // old reference -> new: exact m*c, or the rounded mc of the fma form
+        float alpha;
+        if (exact)
+          alpha = __builtin_amdgcn_exp2f((m_run - m_new) * scale_log2);
+        else if (exact_new)
+          alpha = __builtin_amdgcn_exp2f(__builtin_fmaf(-m_new, scale_log2, mc));
+        else
+          alpha = __builtin_amdgcn_exp2f(mc - mc_new);
+        m_run = m_new;
+        mc = mc_new;
+        exact = exact_new;
+        l_run *= alpha;
+#pragma unroll
+        for (int dt = 0; dt < C::DT; ++dt) o[dt] *= alpha;
+      }
+      lsum = exact ? probs(std::true_type{}) : probs(std::false_type{});
+    }
+    l_run += lsum;
+  };
+
+  // O += V^T P from stage J (DT chains over the four 16-key steps, V
+  // fragments one step ahead).
+  auto pv = [&](auto J) __attribute__((always_inline)) {
+    const uint8_t* vst = stage_of(J);
     auto vfrag = [&](int dt, int ks) __attribute__((always_inline)) {
       const uint8_t* sb = vst + ks * 16 * C::ROW_BYTES;
       const u32x2 ra = lds_read_tr16x4(sb + (vr_a ^ (uint32_t)(dt << 6)));
       const u32x2 rb = lds_read_tr16x4(sb + (vr_b ^ (uint32_t)(dt << 6)));
       return u32x4{ra[0], ra[1], rb[0], rb[1]};
     };
-    constexpr int PAIRS = 8 / C::KK;  // probability pairs of keys 0..31 per head_dim step
-    const float m_ref = m_run;
-    float lsum = 0.0f;
-    uint32_t pk[16];  // bf16 pairs: pk[4*ks + j] holds keys of 16-key step ks
-    // probabilities of the score pair idx (keys 2*idx, 2*idx+1 of the lane's order)
-    auto prob_pair = [&](int idx) __attribute__((always_inline)) {
-      const int kb = idx >> 3, e = (2 * idx) & 15;
-      const float p0 = __builtin_amdgcn_exp2f((s_cu[kb][e] - m_ref) * scale_log2);
-      const float p1 = __builtin_amdgcn_exp2f((s_cu[kb][e + 1] - m_ref) * scale_log2);
-      lsum += p0 + p1;
-      pk[idx] = pack_bf16x2(p0, p1);
+    u32x4 v[C::DT];
+#pragma unroll
+    for (int dt = 0; dt < C::DT; ++dt) v[dt] = vfrag(dt, 0);
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) {
+      u32x4 w[C::DT];
+      if (ks + 1 < 4) {
+#pragma unroll
+        for (int dt = 0; dt < C::DT; ++dt) w[dt] = vfrag(dt, ks + 1);
+      }
+      const bf16x8 p = as_bf16x8(u32x4{pk[4 * ks], pk[4 * ks + 1], pk[4 * ks + 2], pk[4 * ks + 3]});
+#pragma unroll
+      for (int dt = 0; dt < C::DT; ++dt) o[dt] = mfma32(as_bf16x8(v[dt]), p, o[dt]);
+      if (ks + 1 < 4) {
+#pragma unroll
+        for (int dt = 0; dt < C::DT; ++dt) v[dt] = w[dt];
+      }
+    }
+  };
+  // S = K Q^T from stage J (two chains over the head_dim steps, K fragments
+  // one step ahead).
+  auto qk = [&](auto J) __attribute__((always_inline)) {
+    const uint8_t* kst = stage_of(J);
+    auto kfrag = [&](int kb, int kk) __attribute__((always_inline)) {
+      return *reinterpret_cast<const u32x4*>(kst + kb * 32 * C::ROW_BYTES + (k_a0 ^ (uint32_t)(kk << 5)));
     };
     u32x4 a0 = kfrag(0, 0), a1 = kfrag(1, 0);
-    s_nx[0] = f32x16{};
-    s_nx[1] = f32x16{};
+    s[0] = f32x16{};
+    s[1] = f32x16{};
 #pragma unroll
     for (int kk = 0; kk < C::KK; ++kk) {
       u32x4 b0 = a0, b1 = a1;
@@ -369,81 +479,66 @@ __global__ __launch_bounds__(NTHREADS) void attn_kernel(const AttnArgs a) {
         b0 = kfrag(0, kk + 1);
         b1 = kfrag(1, kk + 1);
       }
-      s_nx[0] = mfma32(as_bf16x8(a0), qf[kk], s_nx[0]);
-      s_nx[1] = mfma32(as_bf16x8(a1), qf[kk], s_nx[1]);
-#pragma unroll
-      for (int q = 0; q < PAIRS; ++q) prob_pair(kk * PAIRS + q);  // keys 0..31
+      s[0] = mfma32(as_bf16x8(a0), qf[kk], s[0]);
+      s[1] = mfma32(as_bf16x8(a1), qf[kk], s[1]);
       a0 = b0;
       a1 = b1;
     }
-    u32x4 v[C::DT];
-#pragma unroll
-    for (int dt = 0; dt < C::DT; ++dt) v[dt] = vfrag(dt, 0);
-    float mx = -INFINITY;  // max of tile t+1's unmasked scores, under the PV MFMAs
-#pragma unroll
-    for (int ks = 0; ks < 4; ++ks) {
-      u32x4 w[C::DT];
-#pragma unroll
-      for (int dt = 0; dt < C::DT; ++dt) w[dt] = ks + 1 < 4 ? vfrag(dt, ks + 1) : v[dt];
-      const bf16x8 p = as_bf16x8(u32x4{pk[4 * ks], pk[4 * ks + 1], pk[4 * ks + 2], pk[4 * ks + 3]});
-#pragma unroll
-      for (int dt = 0; dt < C::DT; ++dt) o[dt] = mfma32(as_bf16x8(v[dt]), p, o[dt]);
-      if (ks < 2) {  // keys 32..63, needed from step 2 on, under the MFMAs of steps 0 and 1
-#pragma unroll
-        for (int q = 0; q < 4; ++q) prob_pair(8 + 4 * ks + q);
-      } else {
-#pragma unroll
-        for (int e = 0; e < 16; ++e) mx = fmaxf(mx, s_nx[ks - 2][e]);
-      }
-#pragma unroll
-      for (int dt = 0; dt < C::DT; ++dt) v[dt] = w[dt];
-    }
-    l_run += lsum;
-    asm volatile("" : "+v"(l_run));  // keep the sum in this block, under the MFMAs
-    mt = pair_max(mx);
   };
 
-  // One pipeline step: make tile t+1 visible (and the stage of tile t-1 free);
-  // for tile t: the rare lazy rescale (a wave-uniform branch on the max mt of
-  // tile t, found in the previous step), then the fused block (S of tile t+1,
-  // exponentials and PV of tile t, then the mask and max of tile t+1 under the
-  // PV MFMAs); last, issue the loads of tile t+NSTAGE-1 (issued after the
-  // compute, the loads do not hold up the wave's MFMAs).
-  auto step = [&](int t, f32x16 (&s_cu)[2], f32x16 (&s_nx)[2], float& mt, auto masked) __attribute__((always_inline)) {
-    if (t + 1 < t_end) {
-      if (t + 2 < t_end)
-        wait_vmcnt<C::LOADS>();
-      else
-        wait_vmcnt<0>();
-    }
+  // Phase boundary: no instruction moves across it.
+  auto phase_end = [&]() __attribute__((always_inline)) {
+    __builtin_amdgcn_sched_barrier(0);
     lds_barrier();
-    if (t < wave_tiles) {  // wave-uniform
-      if (__builtin_amdgcn_ballot_w64(mt > m_run + tau_raw) != 0) {  // wave-uniform, rare
-        const float m_new = fmaxf(m_run, mt);
-        const float alpha = __builtin_amdgcn_exp2f((m_run - m_new) * scale_log2);
-        m_run = m_new;
-        l_run *= alpha;
-#pragma unroll
-        for (int dt = 0; dt < C::DT; ++dt) o[dt] *= alpha;
-      }
-      // S of tile t+1 is computed even past the wave's last tile (it then reads
-      // a stale stage and is never used), keeping the block branch-free.
-      fused_block(t, s_cu, s_nx, mt);
-      // tile t+1 crosses the wave's diagonal (rare): mask it and take its max
-      // again (the block's max is of the unmasked scores)
-      if constexpr (decltype(masked)::value) {
-        if ((int64_t)(t + 1) * BKV + BKV - 1 > wave_min_pos) {  // wave-uniform
-          mask_tile(t + 1, s_nx);
-          mt = tile_max(s_nx);
-        }
-      }
-    }
-    if (t + NSTAGE - 1 < t_end) issue_tile(t + NSTAGE - 1);
+    __builtin_amdgcn_sched_barrier(0);
   };
+
+  using TT = std::true_type;
+  using FT = std::false_type;
+  // Both phases of tile t (stage J).  FAST: tile t needs no mask, the wave
+  // computes tiles t and t+1, tiles t+1 .. t+3 lie inside the range and are
+  // whole (no branch at all).
+  auto tile_phases = [&](int t, auto J, auto FAST) __attribute__((always_inline)) {
+    using JN = std::integral_constant<int, decltype(J)::value + 1>;
+    using JL = std::integral_constant<int, decltype(J)::value + 3>;  // stage of tile t+3 (= t-1)
+    if constexpr (decltype(FAST)::value) {
+      softmax(t, FT{});
+      phase_end();
+      issue_tile(t + NSTAGE - 1, JL{}, TT{});
+      __builtin_amdgcn_s_setprio(1);  // this wave's MFMAs first, the other wave's vector work beside them
+      pv(J);
+      qk(JN{});
+      __builtin_amdgcn_s_setprio(0);
+      wait_vmcnt<C::LOADS>();
+      phase_end();
+    } else {
+      if (t < wave_last) softmax(t, TT{});
+      phase_end();
+      if (t + NSTAGE - 1 < t_end) issue_tile(t + NSTAGE - 1, JL{}, FT{});
+      if (t < wave_last) {
+        pv(J);
+        if (t + 1 < wave_last) qk(JN{});
+      }
+      if (t + 2 < t_end) {
+        if (t + 3 < t_end)
+          wait_vmcnt<C::LOADS>();
+        else
+          wait_vmcnt<0>();
+      }
+      phase_end();
+    }
+  };
+
+  using J0 = std::integral_constant<int, 0>;
+  using J1 = std::integral_constant<int, 1>;
+  using J2 = std::integral_constant<int, 2>;
+  using J3 = std::integral_constant<int, 3>;
 
   // ---- prologue: tiles t_begin .. t_begin+NSTAGE-2 in flight, wait for the first.
   const int pro = max(min(NSTAGE - 1, t_end - t_begin), 0);
-  for (int t = t_begin; t < t_begin + pro; ++t) issue_tile(t);
+  if (pro > 0) issue_tile(t_begin, J0{}, FT{});
+  if (pro > 1) issue_tile(t_begin + 1, J1{}, FT{});
+  if (pro > 2) issue_tile(t_begin + 2, J2{}, FT{});
   if (pro >= 3)
     wait_vmcnt<2 * C::LOADS>();
   else if (pro == 2)
@@ -451,28 +546,46 @@ __global__ __launch_bounds__(NTHREADS) void attn_kernel(const AttnArgs a) {
   else
     wait_vmcnt<0>();
   lds_barrier();
+  if (grp == 1) phase_end();  // group 1 runs one phase behind
+  if (t_begin < wave_last) qk(J0{});
+  if (t_begin + 1 < t_end) {  // tile t_begin+1, read by matmul(t_begin)
+    if (t_begin + 2 < t_end)
+      wait_vmcnt<C::LOADS>();
+    else
+      wait_vmcnt<0>();
+  }
+  phase_end();
 
-  f32x16 sA[2], sB[2];
-  float mt = -INFINITY;  // raw max of the current tile's masked scores
-  if (t_begin < t_end && t_begin < wave_tiles) {
-    compute_s(t_begin, sA);
-    mask_tile(t_begin, sA);
-    mt = tile_max(sA);
-  }
-  // Steps whose next tiles lie wholly at or before the workgroup's first
-  // query carry no mask code (a wave-uniform branch there is if-converted by
-  // the compiler into selects on every step); the rest, the diagonal tail,
-  // mask.  Pairs keep the two score buffers' roles.
+  // Fast iterations: tiles t .. t+3 lie before the workgroup's first query
+  // (no mask for any wave, and every active wave computes tiles up to t+4),
+  // tiles up to t+6 are whole and inside [t_begin, t_end).  Waves without a
+  // valid query take the general form, with the same barriers.  Iterations of
+  // four tiles keep each tile's stage static.
   const int t_m = (int)((pos0 + 1) / BKV);  // first tile that some wave masks
+  const int64_t key_lim = min(key_end, (int64_t)t_end * BKV);
   int t = t_begin;
-  for (; t + 1 < t_end && t + 2 < t_m; t += 2) {
-    step(t, sA, sB, mt, std::false_type{});
-    step(t + 1, sB, sA, mt, std::false_type{});
+  if (wave_active) {
+    for (; t + 4 <= t_m && (int64_t)(t + 7) * BKV <= key_lim; t += 4) {
+      tile_phases(t, J0{}, TT{});
+      tile_phases(t + 1, J1{}, TT{});
+      tile_phases(t + 2, J2{}, TT{});
+      tile_phases(t + 3, J3{}, TT{});
+    }
+  } else {
+    for (; t + 4 <= t_m && (int64_t)(t + 7) * BKV <= key_lim; t += 4) {
+      tile_phases(t, J0{}, FT{});
+      tile_phases(t + 1, J1{}, FT{});
+      tile_phases(t + 2, J2{}, FT{});
+      tile_phases(t + 3, J3{}, FT{});
+    }
   }
-  for (; t < t_end; t += 2) {
-    step(t, sA, sB, mt, std::true_type{});
-    if (t + 1 < t_end) step(t + 1, sB, sA, mt, std::true_type{});
+  for (; t < t_end; t += 4) {
+    tile_phases(t, J0{}, FT{});
+    if (t + 1 < t_end) tile_phases(t + 1, J1{}, FT{});
+    if (t + 2 < t_end) tile_phases(t + 2, J2{}, FT{});
+    if (t + 3 < t_end) tile_phases(t + 3, J3{}, FT{});
   }
+  if (grp == 0) phase_end();  // pairs with group 1's first extra barrier
   wait_vmcnt<0>();
 
   if (SPLIT && part >= 0) {
@@ -489,7 +602,7 @@ __global__ __launch_bounds__(NTHREADS) void attn_kernel(const AttnArgs a) {
               f32x4{o[dt][4 * g], o[dt][4 * g + 1], o[dt][4 * g + 2], o[dt][4 * g + 3]};
       if (half == 0) {
         float* ml = a.part_ml + (((int64_t)part * a.n_heads + head) * a.chunk_len + r1) * 2;
-        ml[0] = m_run * scale_log2;
+        ml[0] = mc;  // the reference r (fl(m * scale_log2) in the exact form)
         ml[1] = l_tot;
       }
     }
@@ -499,9 +612,9 @@ __global__ __launch_bounds__(NTHREADS) void attn_kernel(const AttnArgs a) {
   // ---- normalise and store: lane holds query ql, dims dt*32 + 8*(e/4) + 4*half + e%4.
   if (wave_active) {
     const float l_tot = l_run + __shfl_xor(l_run, 32);
-    if (a.lse && half == 0 && wave_first + ql < valid)  // sum_j exp(s_j) = 2^(m_run * scale_log2) * l_tot
+    if (a.lse && half == 0 && wave_first + ql < valid)  // sum_j exp(s_j) = 2^r * l_tot
       a.lse[(int64_t)head * 2 * a.chunk_len + row0 + wave_first + ql] =
-          (m_run * scale_log2 + log2f(l_tot)) * 0.69314718055994530942f;
+          (mc + log2f(l_tot)) * 0.69314718055994530942f;
     if (wave_first + ql < valid) {
       const float inv = 1.0f / l_tot;
       const int64_t off = (row0 + wave_first + ql) * ld + hcol + 4 * half;
