@@ -354,9 +354,13 @@ __global__ __launch_bounds__(NTHREADS) void attn_kernel(const AttnArgs a) {
   // ---- ping-pong schedule.  Per tile t every wave runs two phases, each
   // ended by a workgroup barrier:
   //   softmax(t): mask (diagonal tiles), max, lazy rescale, exponentials and
-  //               row sum of its scores S(t) -> P(t) as bf16 pairs (vector work);
-  //   matmul(t):  load tile t+3, O += V(t)^T P(t), S(t+1) = K(t+1) Q^T
-  //               (32 MFMAs), then wait for this wave's loads of tile t+2.
+  //               row sum of its scores S(t) -> P(t) as bf16 pairs (vector
+  //               work); on the fast path the V(t) fragments are then read
+  //               into registers (tile t is visible since matmul(t-2));
+  //   matmul(t):  load tile t+3, O += V(t)^T P(t) (on the fast path with the
+  //               K(t+1) fragment reads between its MFMA steps), S(t+1) =
+  //               K(t+1) Q^T (32 MFMAs), then wait for this wave's loads of
+  //               tile t+2.
   // Waves 4-7 pass one extra barrier before their first phase and waves 0-3
   // one after their last, so waves 4-7 run one phase behind waves 0-3: with
   // one wave of each group per SIMD, one wave's MFMAs run while the other's
@@ -433,16 +437,53 @@ __global__ __launch_bounds__(NTHREADS) void attn_kernel(const AttnArgs a) {
     l_run += lsum;
   };
 
-  // O += V^T P from stage J (DT chains over the four 16-key steps, V
-  // fragments one step ahead).
+  auto vfrag_at = [&](const uint8_t* vst, int dt, int ks) __attribute__((always_inline)) {
+    const uint8_t* sb = vst + ks * 16 * C::ROW_BYTES;
+    const u32x2 ra = lds_read_tr16x4(sb + (vr_a ^ (uint32_t)(dt << 6)));
+    const u32x2 rb = lds_read_tr16x4(sb + (vr_b ^ (uint32_t)(dt << 6)));
+    return u32x4{ra[0], ra[1], rb[0], rb[1]};
+  };
+  u32x4 vpre[4][C::DT];  // V(t) fragments, read during softmax(t)
+  auto vload = [&](auto J) __attribute__((always_inline)) {
+    const uint8_t* vst = stage_of(J);
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks)
+#pragma unroll
+      for (int dt = 0; dt < C::DT; ++dt) vpre[ks][dt] = vfrag_at(vst, dt, ks);
+  };
+  // Fast path: PV from the V fragments read during softmax, with the K(t+1)
+  // fragment reads of stage JN spread between its MFMA steps, then S(t+1).
+  auto matmul_fast = [&](auto JN) __attribute__((always_inline)) {
+    const uint8_t* kst = stage_of(JN);
+    constexpr int KPS = 2 * C::KK / 4;  // K fragment reads per PV step
+    u32x4 kf[2 * C::KK];                // index 2*kk + kb
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) {
+      const bf16x8 p = as_bf16x8(u32x4{pk[4 * ks], pk[4 * ks + 1], pk[4 * ks + 2], pk[4 * ks + 3]});
+#pragma unroll
+      for (int dt = 0; dt < C::DT; ++dt) o[dt] = mfma32(as_bf16x8(vpre[ks][dt]), p, o[dt]);
+#pragma unroll
+      for (int i = 0; i < KPS; ++i) {
+        const int f = ks * KPS + i, kk = f >> 1, kb = f & 1;
+        kf[f] = *reinterpret_cast<const u32x4*>(kst + kb * 32 * C::ROW_BYTES + (k_a0 ^ (uint32_t)(kk << 5)));
+      }
+      __builtin_amdgcn_sched_group_barrier(0x008, C::DT, 0);  // MFMA
+      __builtin_amdgcn_sched_group_barrier(0x100, KPS, 0);    // DS read
+    }
+    s[0] = f32x16{};
+    s[1] = f32x16{};
+#pragma unroll
+    for (int kk = 0; kk < C::KK; ++kk) {
+      s[0] = mfma32(as_bf16x8(kf[2 * kk]), qf[kk], s[0]);
+      s[1] = mfma32(as_bf16x8(kf[2 * kk + 1]), qf[kk], s[1]);
+    }
+    __builtin_amdgcn_sched_group_barrier(0x008, 2 * C::KK, 0);
+  };
+  // General path: O += V^T P from stage J (DT chains over the four 16-key
+  // steps, V fragments one step ahead).
   auto pv = [&](auto J) __attribute__((always_inline)) {
     const uint8_t* vst = stage_of(J);
-    auto vfrag = [&](int dt, int ks) __attribute__((always_inline)) {
-      const uint8_t* sb = vst + ks * 16 * C::ROW_BYTES;
-      const u32x2 ra = lds_read_tr16x4(sb + (vr_a ^ (uint32_t)(dt << 6)));
-      const u32x2 rb = lds_read_tr16x4(sb + (vr_b ^ (uint32_t)(dt << 6)));
-      return u32x4{ra[0], ra[1], rb[0], rb[1]};
-    };
+    auto vfrag = [&](int dt, int ks) __attribute__((always_inline)) { return vfrag_at(vst, dt, ks); };
     u32x4 v[C::DT];
 #pragma unroll
     for (int dt = 0; dt < C::DT; ++dt) v[dt] = vfrag(dt, 0);
@@ -462,8 +503,8 @@ __global__ __launch_bounds__(NTHREADS) void attn_kernel(const AttnArgs a) {
       }
     }
   };
-  // S = K Q^T from stage J (two chains over the head_dim steps, K fragments
-  // one step ahead).
+  // General path: S = K Q^T from stage J (two chains over the head_dim
+  // steps, K fragments one step ahead).
   auto qk = [&](auto J) __attribute__((always_inline)) {
     const uint8_t* kst = stage_of(J);
     auto kfrag = [&](int kb, int kk) __attribute__((always_inline)) {
@@ -503,11 +544,11 @@ __global__ __launch_bounds__(NTHREADS) void attn_kernel(const AttnArgs a) {
     using JL = std::integral_constant<int, decltype(J)::value + 3>;  // stage of tile t+3 (= t-1)
     if constexpr (decltype(FAST)::value) {
       softmax(t, FT{});
+      vload(J);
       phase_end();
       issue_tile(t + NSTAGE - 1, JL{}, TT{});
       __builtin_amdgcn_s_setprio(1);  // this wave's MFMAs first, the other wave's vector work beside them
-      pv(J);
-      qk(JN{});
+      matmul_fast(JN{});
       __builtin_amdgcn_s_setprio(0);
       wait_vmcnt<C::LOADS>();
       phase_end();
