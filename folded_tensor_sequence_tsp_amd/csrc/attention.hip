@@ -355,12 +355,13 @@ __global__ __launch_bounds__(NTHREADS) void attn_kernel(const AttnArgs a) {
   // ended by a workgroup barrier:
   //   softmax(t): mask (diagonal tiles), max, lazy rescale, exponentials and
   //               row sum of its scores S(t) -> P(t) as bf16 pairs (vector
-  //               work); on the fast path the V(t) fragments are then read
-  //               into registers (tile t is visible since matmul(t-2));
+  //               work); on the fast path the V(t) fragments of the first two
+  //               16-key steps are then read into registers (tile t is
+  //               visible since matmul(t-2));
   //   matmul(t):  load tile t+3, O += V(t)^T P(t) (on the fast path with the
-  //               K(t+1) fragment reads between its MFMA steps), S(t+1) =
-  //               K(t+1) Q^T (32 MFMAs), then wait for this wave's loads of
-  //               tile t+2.
+  //               other V(t) fragment reads, then the K(t+1) reads, between
+  //               its MFMA steps), S(t+1) = K(t+1) Q^T (32 MFMAs), then wait
+  //               for this wave's loads of tile t+2.
   // Waves 4-7 pass one extra barrier before their first phase and waves 0-3
   // one after their last, so waves 4-7 run one phase behind waves 0-3: with
   // one wave of each group per SIMD, one wave's MFMAs run while the other's
@@ -443,32 +444,45 @@ __global__ __launch_bounds__(NTHREADS) void attn_kernel(const AttnArgs a) {
     const u32x2 rb = lds_read_tr16x4(sb + (vr_b ^ (uint32_t)(dt << 6)));
     return u32x4{ra[0], ra[1], rb[0], rb[1]};
   };
-  u32x4 vpre[4][C::DT];  // V(t) fragments, read during softmax(t)
+  // V(t) fragments: steps 0, 1 read at the end of softmax(t), steps 2, 3 under
+  // the first PV MFMAs.  All four in the softmax phase is faster at unit
+  // scale but lengthens that phase where it is already the longer one (the
+  // exact form, larger scores); half is as fast as either in both regimes.
+  u32x4 vpre[4][C::DT];
   auto vload = [&](auto J) __attribute__((always_inline)) {
     const uint8_t* vst = stage_of(J);
 #pragma unroll
-    for (int ks = 0; ks < 4; ++ks)
+    for (int ks = 0; ks < 2; ++ks)
 #pragma unroll
       for (int dt = 0; dt < C::DT; ++dt) vpre[ks][dt] = vfrag_at(vst, dt, ks);
   };
-  // Fast path: PV from the V fragments read during softmax, with the K(t+1)
-  // fragment reads of stage JN spread between its MFMA steps, then S(t+1).
-  auto matmul_fast = [&](auto JN) __attribute__((always_inline)) {
+  // Fast path: PV from stage J's V fragments (two steps already in
+  // registers), with the remaining V reads and then the K(t+1) fragment reads
+  // of stage JN spread between its MFMA steps, then S(t+1).
+  auto matmul_fast = [&](auto J, auto JN) __attribute__((always_inline)) {
+    const uint8_t* vst = stage_of(J);
     const uint8_t* kst = stage_of(JN);
-    constexpr int KPS = 2 * C::KK / 4;  // K fragment reads per PV step
+    constexpr int KPS = 2 * C::KK / 2;  // K fragment reads per PV step (steps 2, 3)
     u32x4 kf[2 * C::KK];                // index 2*kk + kb
 #pragma unroll
     for (int ks = 0; ks < 4; ++ks) {
       const bf16x8 p = as_bf16x8(u32x4{pk[4 * ks], pk[4 * ks + 1], pk[4 * ks + 2], pk[4 * ks + 3]});
 #pragma unroll
       for (int dt = 0; dt < C::DT; ++dt) o[dt] = mfma32(as_bf16x8(vpre[ks][dt]), p, o[dt]);
+      if (ks < 2) {  // V fragments of steps 2, 3
 #pragma unroll
-      for (int i = 0; i < KPS; ++i) {
-        const int f = ks * KPS + i, kk = f >> 1, kb = f & 1;
-        kf[f] = *reinterpret_cast<const u32x4*>(kst + kb * 32 * C::ROW_BYTES + (k_a0 ^ (uint32_t)(kk << 5)));
+        for (int dt = 0; dt < C::DT; ++dt) vpre[ks + 2][dt] = vfrag_at(vst, dt, ks + 2);
+        __builtin_amdgcn_sched_group_barrier(0x008, C::DT, 0);    // MFMA
+        __builtin_amdgcn_sched_group_barrier(0x100, 2 * C::DT, 0);  // DS read
+      } else {
+#pragma unroll
+        for (int i = 0; i < KPS; ++i) {
+          const int f = (ks - 2) * KPS + i, kk = f >> 1, kb = f & 1;
+          kf[f] = *reinterpret_cast<const u32x4*>(kst + kb * 32 * C::ROW_BYTES + (k_a0 ^ (uint32_t)(kk << 5)));
+        }
+        __builtin_amdgcn_sched_group_barrier(0x008, C::DT, 0);  // MFMA
+        __builtin_amdgcn_sched_group_barrier(0x100, KPS, 0);    // DS read
       }
-      __builtin_amdgcn_sched_group_barrier(0x008, C::DT, 0);  // MFMA
-      __builtin_amdgcn_sched_group_barrier(0x100, KPS, 0);    // DS read
     }
     s[0] = f32x16{};
     s[1] = f32x16{};
@@ -548,7 +562,7 @@ __global__ __launch_bounds__(NTHREADS) void attn_kernel(const AttnArgs a) {
       phase_end();
       issue_tile(t + NSTAGE - 1, JL{}, TT{});
       __builtin_amdgcn_s_setprio(1);  // this wave's MFMAs first, the other wave's vector work beside them
-      matmul_fast(JN{});
+      matmul_fast(J, JN{});
       __builtin_amdgcn_s_setprio(0);
       wait_vmcnt<C::LOADS>();
       phase_end();
