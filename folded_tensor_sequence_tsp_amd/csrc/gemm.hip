@@ -15,8 +15,12 @@
 // waves of 128 x 64, two per SIMD; 128 x 256 tiles: eight waves of 64 x 64, for
 // short token counts; 128 x 128 tiles: four waves of 64 x 64), each a grid of
 // 32 x 32 MFMA tiles.  A and B k-tiles stream into a 4-stage LDS ring
-// with direct global->LDS loads (global_load_lds_dwordx4, no register staging),
-// three k-tiles ahead, one vmcnt wait and one barrier per k-tile.  LDS rows are
+// with direct buffer->LDS loads (buffer_load_dwordx4 ... lds, no register
+// staging; the descriptors are rebased per k-tile in SGPRs), three k-tiles
+// ahead, one vmcnt wait and one barrier per k-tile.  Buffer rather than
+// global loads: the compiler counts a global->LDS load against the LDS
+// counter as well, so with loads always in flight every fragment wait became
+// a wait for all of them; with buffer loads the waits are graduated.  LDS rows are
 // 64 bytes (32 k values); the four 16-byte chunks of row r sit at chunk
 // positions c ^ ((r / 4) % 4), so the 16 lanes of one LDS cycle, reading 16
 // consecutive rows at one k offset, hit distinct banks of the 64-bank LDS.
@@ -213,51 +217,69 @@ __global__ __launch_bounds__((Cfg<BM, BN>::NT)) void gemm_kernel(const GemmArgs 
   const int kt_per_rep = kt_per_shard * reps;
   const int k_tiles = kt_per_rep * g.k_shards;
 
-  // ---- direct-load sources.  Instruction i of wave w fills the 1 KB block
-  // (i*NW + w) of the A (or B) region: 16 rows of 64 bytes; lane L -> row
-  // L/4 of the block, physical chunk L%4 = logical chunk (L%4) ^ ((row/4)%4).
-  int64_t a_off[C::A_LOADS];
+  // ---- direct buffer->LDS loads.  Instruction i of wave w fills the 1 KB
+  // block (i*NW + w) of the A (or B) region: 16 rows of 64 bytes; lane L ->
+  // row L/4 of the block, physical chunk L%4 = logical chunk (L%4) ^
+  // ((row/4)%4).  The byte offsets are relative to the tile's first row at
+  // the k-tile's first column (the descriptors' base, rebased per k-tile in
+  // SGPRs); rows past the matrix re-read its last row.
+  uint32_t a_off[C::A_LOADS];
 #pragma unroll
   for (int i = 0; i < C::A_LOADS; ++i) {
     const int r = (i * C::NW + wave) * 16 + lane / 4;
     const int c = (lane & 3) ^ ((r >> 2) & 3);
-    a_off[i] = (int64_t)min(m0 + r, g.M - 1) * g.lda + c * 8;
+    a_off[i] = (uint32_t)(((int64_t)(min(m0 + r, g.M - 1) - m0) * g.lda + c * 8) * 2);
   }
-  int64_t b_off[C::B_LOADS];
+  uint32_t b_off[C::B_LOADS];
 #pragma unroll
   for (int i = 0; i < C::B_LOADS; ++i) {
     const int r = (i * C::NW + wave) * 16 + lane / 4;
     const int c = (lane & 3) ^ ((r >> 2) & 3);
-    b_off[i] = (int64_t)min(n0 + r, g.N_s - 1) * g.K_s + c * 8;
+    b_off[i] = (uint32_t)(((int64_t)(min(n0 + r, g.N_s - 1) - n0) * g.K_s + c * 8) * 2);
   }
+  // bytes a descriptor covers: the tile's rows (the launch checks that they
+  // fit in 2^31)
+  const uint32_t a_bytes = (uint32_t)((int64_t)BM * g.lda * 2);
+  const uint32_t b_bytes = (uint32_t)((int64_t)BN * g.K_s * 2);
 
   // Tiles are issued in order t = 0, 1, ...; the position of the next one
   // (k-tile within the shard, part of A, shard step of the ring) is walked
   // incrementally (wave-uniform scalars, no divisions).
   int nx_kt = 0, nx_part = 0, nx_d = g.k_shards > 1 ? g.ring_start : nshard;
+  // The matrices' pointers are kernel arguments; the current shard's weight
+  // pointer is read again only at shard boundaries, and that scalar load is
+  // waited for at once: a scalar load in flight shares the lgkm counter with
+  // the fragment reads and would make the compiler wait for all of them.
+  const uint16_t* a_hi = g.A + (int64_t)m0 * g.lda;
+  const uint16_t* a_lo = g.A_lo + (int64_t)m0 * g.lda;
+  const uint16_t* bshard = g.B[nx_d] + (int64_t)n0 * g.K_s;
+  asm volatile("" ::"s"(a_hi), "s"(a_lo), "s"(bshard));  // in registers before the loop
   auto issue_tile = [&](int t) __attribute__((always_inline)) {
     const int64_t acol = (g.k_shards > 1 ? (int64_t)nx_d * g.K_s : 0) + nx_kt * BK;
-    const uint16_t* abase = (nx_part ? g.A_lo : g.A) + acol;
-    const uint16_t* bbase = g.B[nx_d] + nx_kt * BK;
+    const __amdgpu_buffer_rsrc_t ra = buffer_rsrc((nx_part ? a_lo : a_hi) + acol, a_bytes);
+    const __amdgpu_buffer_rsrc_t rb = buffer_rsrc(bshard + nx_kt * BK, b_bytes);
+    [[maybe_unused]] const __amdgpu_buffer_rsrc_t rl = buffer_rsrc(a_lo + acol, a_bytes);
     if (++nx_kt == kt_per_shard) {
       nx_kt = 0;
       if (++nx_part == reps) {
         nx_part = 0;
-        if (g.k_shards > 1 && ++nx_d == g.k_shards) nx_d = 0;
+        if (g.k_shards > 1) {
+          if (++nx_d == g.k_shards) nx_d = 0;
+          bshard = g.B[nx_d] + (int64_t)n0 * g.K_s;
+          __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0)
+        }
       }
     }
     uint8_t* stage = smem + (t % C::ST) * C::STAGE_BYTES;
 #pragma unroll
-    for (int i = 0; i < C::A_LOADS; ++i) dma16(abase + a_off[i], stage + (i * C::NW + wave) * 1024);
+    for (int i = 0; i < C::A_LOADS; ++i) dma16_buf(ra, a_off[i], stage + (i * C::NW + wave) * 1024);
     if constexpr (LO) {
-      const uint16_t* lbase = g.A_lo + acol;
 #pragma unroll
-      for (int i = 0; i < C::A_LOADS; ++i)
-        dma16(lbase + a_off[i], stage + C::A_BYTES + (i * C::NW + wave) * 1024);
+      for (int i = 0; i < C::A_LOADS; ++i) dma16_buf(rl, a_off[i], stage + C::A_BYTES + (i * C::NW + wave) * 1024);
     }
 #pragma unroll
     for (int i = 0; i < C::B_LOADS; ++i)
-      dma16(bbase + b_off[i], stage + C::PARTS * C::A_BYTES + (i * C::NW + wave) * 1024);
+      dma16_buf(rb, b_off[i], stage + C::PARTS * C::A_BYTES + (i * C::NW + wave) * 1024);
   };
 
   f32x16 acc[C::FM][C::FN];
@@ -274,7 +296,8 @@ __global__ __launch_bounds__((Cfg<BM, BN>::NT)) void gemm_kernel(const GemmArgs 
   const uint32_t a_row = (uint32_t)(wm * C::WM + ql) * 64;
   const uint32_t b_row = (uint32_t)(C::PARTS * C::A_BYTES) + (uint32_t)(wn * C::WN + ql) * 64;
 
-  // Both k-steps' fragments are read before the first step's MFMAs.
+  // Both k-steps' fragments are read before the first step's MFMAs (step 0's
+  // first), so each MFMA waits only for its own fragments.
   auto compute_tile = [&](int t) __attribute__((always_inline)) {
     const uint8_t* stage = smem + (t % C::ST) * C::STAGE_BYTES;
     u32x4 af[2][C::FM], bfv[2][C::FN];
@@ -285,6 +308,7 @@ __global__ __launch_bounds__((Cfg<BM, BN>::NT)) void gemm_kernel(const GemmArgs 
       for (int i = 0; i < C::FM; ++i) af[kk][i] = *reinterpret_cast<const u32x4*>(stage + a_row + i * 32 * 64 + kx);
 #pragma unroll
       for (int j = 0; j < C::FN; ++j) bfv[kk][j] = *reinterpret_cast<const u32x4*>(stage + b_row + j * 32 * 64 + kx);
+      if constexpr (!LO) __builtin_amdgcn_sched_barrier(0);  // step 0's reads first
     }
 #pragma unroll
     for (int kk = 0; kk < BK / 16; ++kk)
@@ -292,6 +316,10 @@ __global__ __launch_bounds__((Cfg<BM, BN>::NT)) void gemm_kernel(const GemmArgs 
       for (int i = 0; i < C::FM; ++i)
 #pragma unroll
         for (int j = 0; j < C::FN; ++j) acc[i][j] = mfma32_bits<F16>(af[kk][i], bfv[kk][j], acc[i][j]);
+    if constexpr (!LO) {
+      __builtin_amdgcn_sched_group_barrier(0x008, C::FM * C::FN, 0);
+      __builtin_amdgcn_sched_group_barrier(0x008, C::FM * C::FN, 0);
+    }
     if constexpr (LO) {  // the low part of A against the same B fragments
 #pragma unroll
       for (int kk = 0; kk < BK / 16; ++kk) {
@@ -314,6 +342,7 @@ __global__ __launch_bounds__((Cfg<BM, BN>::NT)) void gemm_kernel(const GemmArgs 
   // compute tile t, then refill the stage of tile t-1 with tile t+3.
   const int pro = min(C::ST - 1, k_tiles);
   for (int t = 0; t < pro; ++t) issue_tile(t);
+  __builtin_amdgcn_s_waitcnt(0xC07F);  // no scalar load in flight in the loop
   for (int t = 0; t < k_tiles; ++t) {
     const int ahead = min(k_tiles - 1 - t, C::ST - 2);  // tiles issued after t
     if (ahead >= 2)
@@ -418,6 +447,8 @@ hipError_t launch_tiles(const GemmArgs& g, hipStream_t stream) {
 
 hipError_t launch_gemm(const GemmArgs& g, hipStream_t stream) {
   if (g.M <= 0) return hipSuccess;
+  // a tile's rows must fit one buffer descriptor (32-bit byte offsets)
+  if ((int64_t)256 * g.lda * 2 > INT32_MAX || (int64_t)256 * g.K_s * 2 > INT32_MAX) return hipErrorInvalidValue;
   // 256 x 256 tiles keep the LDS traffic per MFMA low; fall back to 128 x 128
   // when the big tiles would leave most of the 256 CUs idle.
   const long big = (long)((g.M + 255) / 256) * (((g.N_s + 255) / 256) * g.n_shards);

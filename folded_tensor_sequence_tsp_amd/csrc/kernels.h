@@ -66,6 +66,9 @@ struct GemmArgs {
   int64_t chunk_len, chunk_start0, chunk_start1;
 };
 
+// hipErrorInvalidValue when 256 rows of A (lda) or of a B shard (K_s) span
+// more than 2^31 bytes (the loads address a tile through one buffer
+// descriptor with 32-bit offsets): lda, K_s < 4,194,304 elements.
 hipError_t launch_gemm(const GemmArgs& args, hipStream_t stream);
 
 // For each row i of x [n x h] (fp32 when x_f32, else bf16):
