@@ -149,7 +149,22 @@ __global__ __launch_bounds__(64 * BW) void dkv_kernel(const AttnBwdArgs a) {
   constexpr int STAGE = (TR ? 2 : 4) * C::TILE_BYTES + BW * STATS;
   constexpr int NST = TR ? 4 : 2;                // ring depth: 144 KB of LDS either way
   constexpr int PER_ISSUE = (TR ? 2 : 4) * C::TLOADS + 1;  // DMA instructions per thread per tile
-  __shared__ __attribute__((aligned(1024))) uint8_t smem[NST * STAGE];
+  // The ring's stages are distinct arrays and every access names its stage
+  // statically (the tile loops run NST tiles per iteration): the compiler
+  // then knows that a transposing read of one stage does not alias the loads
+  // filling another, and does not make it wait for every load in flight.
+  __shared__ __attribute__((aligned(1024))) uint8_t stage0[STAGE];
+  __shared__ __attribute__((aligned(1024))) uint8_t stage1[STAGE];
+  __shared__ __attribute__((aligned(1024))) uint8_t stage2[NST > 2 ? STAGE : 16];
+  __shared__ __attribute__((aligned(1024))) uint8_t stage3[NST > 3 ? STAGE : 16];
+  static_assert(NST == 2 || NST == 4, "two or four stages");
+  auto stage_of = [&](auto J) __attribute__((always_inline)) -> uint8_t* {
+    constexpr int j = decltype(J)::value % NST;
+    if constexpr (j == 0) return stage0;
+    else if constexpr (j == 1) return stage1;
+    else if constexpr (j == 2) return stage2;
+    else return stage3;
+  };
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -219,15 +234,16 @@ __global__ __launch_bounds__(64 * BW) void dkv_kernel(const AttnBwdArgs a) {
     if constexpr (TR) return ((r & 3) << 2) | ((r >> 2) & 3);
     else return r & (C::NCH - 1);
   };
-  int rm_row[C::TLOADS], rm_col[C::TLOADS], tr_off[C::TLOADS];
+  // Byte offsets of this lane's loads relative to the tile's first row at the
+  // head's first column (row-major) or to the transposed tile's start.
+  uint32_t rm_off[C::TLOADS], tr_off[C::TLOADS];
 #pragma unroll
   for (int j = 0; j < C::TLOADS; ++j) {
     const int b = j * BW + wave;
     const int r = b * C::RPL + lane / C::NCH;
-    rm_row[j] = r;
-    rm_col[j] = ((lane % C::NCH) ^ rm_swz(r)) * 8;
+    rm_off[j] = (uint32_t)((r * ld + ((lane % C::NCH) ^ rm_swz(r)) * 8) * 2);
     const int d = b * 8 + lane / 8;
-    tr_off[j] = d * 64 + ((lane % 8) ^ ((d >> 1) & 7)) * 8;
+    tr_off[j] = (uint32_t)((d * 64 + ((lane % 8) ^ ((d >> 1) & 7)) * 8) * 2);
   }
 
   // tile i: first the masked tiles (per query head: chunk 0's, chunk 1's),
@@ -258,29 +274,37 @@ __global__ __launch_bounds__(64 * BW) void dkv_kernel(const AttnBwdArgs a) {
     }
   };
 
-  auto issue = [&](int i) __attribute__((always_inline)) {
+  // Loads of tile i into stage J through buffer descriptors rebased per tile
+  // (scalar work).  The Q/dO descriptors end at the chunk's last row, so the
+  // padding rows of a chunk's last tile read as zeros (their normaliser makes
+  // every probability 0 anyway).
+  auto issue = [&](int i, auto J) __attribute__((always_inline)) {
     int c, t, qh;
     tile_of(i, c, t, qh);
     const int hcol = qh * HD;
-    uint8_t* stage = smem + (i % NST) * STAGE;
-    const int64_t rbase = c * CL;
+    uint8_t* stage = stage_of(J);
+    const int64_t row0 = c * CL + (int64_t)t * 64;
+    const int64_t last = min((int64_t)63, CL - 1 - (int64_t)t * 64);  // the tile's last valid row
+    const uint32_t bytes = (uint32_t)((last * ld + HD) * 2);
+    const __amdgpu_buffer_rsrc_t rq = buffer_rsrc(a.q + row0 * ld + hcol, bytes);
+    const __amdgpu_buffer_rsrc_t rd = buffer_rsrc(a.dout + row0 * ld + hcol, bytes);
 #pragma unroll
     for (int j = 0; j < C::TLOADS; ++j) {
-      const int64_t row = rbase + min((int64_t)t * 64 + rm_row[j], CL - 1);  // padding rows: any row of the chunk
-      const int64_t off = row * ld + hcol + rm_col[j];
-      dma16(a.q + off, stage + (j * BW + wave) * 1024);
-      dma16(a.dout + off, stage + C::TILE_BYTES + (j * BW + wave) * 1024);
+      dma16_buf(rq, rm_off[j], stage + (j * BW + wave) * 1024);
+      dma16_buf(rd, rm_off[j], stage + C::TILE_BYTES + (j * BW + wave) * 1024);
     }
     if constexpr (!TR) {
       const int64_t tbase = ((c * (int64_t)a.n_heads + qh) * a.tpc + t) * (int64_t)(HD * 64);
+      const __amdgpu_buffer_rsrc_t rqt = buffer_rsrc(a.qt + tbase, C::TILE_BYTES);
+      const __amdgpu_buffer_rsrc_t rdt = buffer_rsrc(a.dot + tbase, C::TILE_BYTES);
 #pragma unroll
       for (int j = 0; j < C::TLOADS; ++j) {
-        dma16(a.qt + tbase + tr_off[j], stage + 2 * C::TILE_BYTES + (j * BW + wave) * 1024);
-        dma16(a.dot + tbase + tr_off[j], stage + 3 * C::TILE_BYTES + (j * BW + wave) * 1024);
+        dma16_buf(rqt, tr_off[j], stage + 2 * C::TILE_BYTES + (j * BW + wave) * 1024);
+        dma16_buf(rdt, tr_off[j], stage + 3 * C::TILE_BYTES + (j * BW + wave) * 1024);
       }
     }
     const float* st = a.stats + ((c * (int64_t)a.n_heads + qh) * a.tpc + t) * 256;
-    dma16(st + lane * 4, stage + (TR ? 2 : 4) * C::TILE_BYTES + wave * STATS);
+    dma16_buf(buffer_rsrc(st, 1024), (uint32_t)lane * 16, stage + (TR ? 2 : 4) * C::TILE_BYTES + wave * STATS);
   };
 
   // fragment addresses within a stage (see the DMA swizzles above)
@@ -305,7 +329,7 @@ __global__ __launch_bounds__(64 * BW) void dkv_kernel(const AttnBwdArgs a) {
   // step ahead; the exponentials and dS of queries 0..31 run under the S/dP
   // MFMAs of queries 32..63, those of queries 32..63 under the first half of
   // the dV/dK MFMAs (which need only queries 0..31).
-  auto compute = [&](int i, auto masked) __attribute__((always_inline)) {
+  auto compute = [&](int i, auto J, auto masked) __attribute__((always_inline)) {
     constexpr bool MASKED = decltype(masked)::value;
     int c, t, qh;
     tile_of(i, c, t, qh);
@@ -316,7 +340,7 @@ __global__ __launch_bounds__(64 * BW) void dkv_kernel(const AttnBwdArgs a) {
     // queries of the tile before this lane's key are masked (MASKED tiles
     // only): offsets below qmin
     const int qmin = kw0 + 31 > qp0 ? (int)min(max(key - qp0, (int64_t)0), (int64_t)64) : 0;
-    const uint8_t* stage = smem + (i % NST) * STAGE;
+    const uint8_t* stage = stage_of(J);
     const uint8_t* q_st = stage;
     const uint8_t* do_st = stage + C::TILE_BYTES;
     const uint8_t* qt_st = TR ? q_st : stage + 2 * C::TILE_BYTES;
@@ -420,8 +444,15 @@ __global__ __launch_bounds__(64 * BW) void dkv_kernel(const AttnBwdArgs a) {
   // frees the stage that tile i-1 was computed from, so tile i+NST-1's loads go
   // there right after it, and land during the compute of tiles i..i+NST-2.
   // The wait leaves the loads of the tiles issued after tile i in flight.
-  for (int i = 0; i < NST - 1 && i < n_all; ++i) issue(i);
-  auto step = [&](int i, auto masked) __attribute__((always_inline)) {
+  using J0 = std::integral_constant<int, 0>;
+  using J1 = std::integral_constant<int, 1>;
+  using J2 = std::integral_constant<int, 2>;
+  using J3 = std::integral_constant<int, 3>;
+  if (n_all > 0) issue(0, J0{});
+  if (NST > 2 && n_all > 1) issue(1, J1{});
+  if (NST > 3 && n_all > 2) issue(2, J2{});
+  // tile i in stage J = i mod NST
+  auto step = [&](int i, auto J, auto masked) __attribute__((always_inline)) {
     const int ahead = min(NST - 2, n_all - 1 - i);  // tiles issued after tile i
     if (NST >= 4 && ahead >= 2)
       wait_vmcnt<2 * PER_ISSUE>();
@@ -430,14 +461,26 @@ __global__ __launch_bounds__(64 * BW) void dkv_kernel(const AttnBwdArgs a) {
     else
       wait_vmcnt<0>();
     lds_barrier();
-    if (i + NST - 1 < n_all) issue(i + NST - 1);
-    compute(i, masked);
+    if (i + NST - 1 < n_all) issue(i + NST - 1, std::integral_constant<int, decltype(J)::value + NST - 1>{});
+    compute(i, J, masked);
+  };
+  // NST tiles per iteration, with the tail's tiles conditional
+  auto steps = [&](int i, int end, auto masked) __attribute__((always_inline)) {
+    step(i, J0{}, masked);
+    if (i + 1 < end) step(i + 1, J1{}, masked);
+    if constexpr (NST > 2) {
+      if (i + 2 < end) step(i + 2, J2{}, masked);
+      if (i + 3 < end) step(i + 3, J3{}, masked);
+    }
   };
   // two loops, so that the unmasked one carries no mask code (a branch per
-  // tile would split the accumulators' live ranges)
+  // tile would split the accumulators' live ranges); the masked one runs a
+  // whole number of NST-tile iterations (the mask is right on any tile), so
+  // that the unmasked one starts at stage 0
+  const int n_masked = min(n_all, (n_diag + NST - 1) / NST * NST);
   int i = 0;
-  for (; i < n_diag; ++i) step(i, std::true_type{});
-  for (; i < n_all; ++i) step(i, std::false_type{});
+  for (; i < n_masked; i += NST) steps(i, n_masked, std::true_type{});
+  for (; i < n_all; i += NST) steps(i, n_all, std::false_type{});
 
   // store this lane's key row of dK (scaled) and dV; zeros where no query sees the key
   if (key < S) {
@@ -465,7 +508,14 @@ __global__ __launch_bounds__(64 * QW) void dq_kernel(const AttnBwdArgs a) {
   constexpr int STAGE = (TR ? 2 : 3) * C::TILE_BYTES;
   constexpr int NST = TR ? NST_DQ : 2;
   constexpr int PER_ISSUE = (TR ? 2 : 3) * C::TLOADS;  // DMA instructions per thread per tile
-  __shared__ __attribute__((aligned(1024))) uint8_t smem[NST * STAGE];
+  // distinct stage arrays named statically, as in dkv_kernel
+  __shared__ __attribute__((aligned(1024))) uint8_t stage0[STAGE];
+  __shared__ __attribute__((aligned(1024))) uint8_t stage1[STAGE];
+  static_assert(NST == 2, "two stages");
+  auto stage_of = [&](auto J) __attribute__((always_inline)) -> uint8_t* {
+    if constexpr (decltype(J)::value % 2 == 0) return stage0;
+    else return stage1;
+  };
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -526,29 +576,34 @@ __global__ __launch_bounds__(64 * QW) void dq_kernel(const AttnBwdArgs a) {
     if constexpr (TR) return ((r & 3) << 2) | ((r >> 2) & 3);
     else return r & (C::NCH - 1);
   };
-  int rm_row[C::TLOADS], rm_col[C::TLOADS], tr_off[C::TLOADS];
+  // byte offsets of this lane's loads (as in dkv_kernel)
+  uint32_t rm_off[C::TLOADS], tr_off[C::TLOADS];
 #pragma unroll
   for (int j = 0; j < C::TLOADS; ++j) {
     const int b = j * QW + wave;
     const int r = b * C::RPL + lane / C::NCH;
-    rm_row[j] = r;
-    rm_col[j] = ((lane % C::NCH) ^ rm_swz(r)) * 8;
+    rm_off[j] = (uint32_t)((r * kld + ((lane % C::NCH) ^ rm_swz(r)) * 8) * 2);
     const int d = b * 8 + lane / 8;
-    tr_off[j] = d * 64 + ((lane % 8) ^ ((d >> 1) & 7)) * 8;
+    tr_off[j] = (uint32_t)((d * 64 + ((lane % 8) ^ ((d >> 1) & 7)) * 8) * 2);
   }
   const uint16_t* kt_head = TR ? nullptr : a.kt + (int64_t)kvh * a.n_kv_tiles * HD * 64;
 
-  auto issue = [&](int t) __attribute__((always_inline)) {
-    uint8_t* stage = smem + (t % NST) * STAGE;
+  // Loads of key tile t into stage J; the K/V descriptors end at the item's
+  // last key, so rows past it read as zeros (they are masked).
+  auto issue = [&](int t, auto J) __attribute__((always_inline)) {
+    uint8_t* stage = stage_of(J);
     const int64_t k0 = (int64_t)t * 64;
+    const int64_t last = min((int64_t)63, key_end - 1 - k0);
+    const uint32_t bytes = (uint32_t)((last * kld + HD) * 2);
+    const __amdgpu_buffer_rsrc_t rk = buffer_rsrc(a.k + k0 * kld + kcol, bytes);
+    const __amdgpu_buffer_rsrc_t rv = buffer_rsrc(a.v + k0 * kld + kcol, bytes);
+    [[maybe_unused]] const __amdgpu_buffer_rsrc_t rt =
+        buffer_rsrc(TR ? a.k : kt_head + (int64_t)t * HD * 64, C::TILE_BYTES);
 #pragma unroll
     for (int j = 0; j < C::TLOADS; ++j) {
-      const int64_t kr = min(k0 + rm_row[j], key_end - 1);  // rows past the range: masked anyway
-      const int64_t off = kr * kld + kcol + rm_col[j];
-      dma16(a.k + off, stage + (j * QW + wave) * 1024);
-      dma16(a.v + off, stage + C::TILE_BYTES + (j * QW + wave) * 1024);
-      if constexpr (!TR)
-        dma16(kt_head + (int64_t)t * HD * 64 + tr_off[j], stage + 2 * C::TILE_BYTES + (j * QW + wave) * 1024);
+      dma16_buf(rk, rm_off[j], stage + (j * QW + wave) * 1024);
+      dma16_buf(rv, rm_off[j], stage + C::TILE_BYTES + (j * QW + wave) * 1024);
+      if constexpr (!TR) dma16_buf(rt, tr_off[j], stage + 2 * C::TILE_BYTES + (j * QW + wave) * 1024);
     }
   };
 
@@ -561,10 +616,10 @@ __global__ __launch_bounds__(64 * QW) void dq_kernel(const AttnBwdArgs a) {
 #pragma unroll
   for (int dt = 0; dt < C::DT; ++dt) dqT[dt] = f32x16{};
 
-  auto compute = [&](int t, auto masked) __attribute__((always_inline)) {
+  auto compute = [&](int t, auto J, auto masked) __attribute__((always_inline)) {
     constexpr bool MASKED = decltype(masked)::value;
     if (t >= wave_tiles) return;  // wave-uniform
-    const uint8_t* stage = smem + (t % NST) * STAGE;
+    const uint8_t* stage = stage_of(J);
     const int64_t k0 = (int64_t)t * 64;
     uint32_t ps[16];
     // dS of entries 4g..4g+3 of key block kb: keys k0 + 32 kb + 8 g + 4 half + 0..3
@@ -644,26 +699,29 @@ __global__ __launch_bounds__(64 * QW) void dq_kernel(const AttnBwdArgs a) {
     }
   };
 
-  for (int t = 0; t < NST - 1 && t < n_tiles; ++t) issue(t);
-  auto step = [&](int t, auto masked) __attribute__((always_inline)) {
-    // NST-stage ring, one barrier per tile, as in dkv_kernel
-    const int ahead = min(NST - 2, n_tiles - 1 - t);
-    if (NST >= 4 && ahead >= 2)
-      wait_vmcnt<2 * PER_ISSUE>();
-    else if (NST >= 3 && ahead >= 1)
-      wait_vmcnt<PER_ISSUE>();
-    else
-      wait_vmcnt<0>();
+  using J0 = std::integral_constant<int, 0>;
+  using J1 = std::integral_constant<int, 1>;
+  if (n_tiles > 0) issue(0, J0{});
+  // tile t in stage t mod 2; two-stage ring, one barrier per tile, as in dkv_kernel
+  auto step = [&](int t, auto J, auto masked) __attribute__((always_inline)) {
+    wait_vmcnt<0>();
     lds_barrier();
-    if (t + NST - 1 < n_tiles) issue(t + NST - 1);
-    compute(t, masked);
+    if (t + 1 < n_tiles) issue(t + 1, std::integral_constant<int, decltype(J)::value + 1>{});
+    compute(t, J, masked);
   };
   // key tiles wholly at or before the first query need no mask: a loop of
-  // their own, then the masked tail (as in dkv_kernel)
-  const int t_m = (int)min((int64_t)n_tiles, (pos0 + 1) / 64);
+  // their own (an even number of tiles, so that both loops start at stage 0),
+  // then the masked tail (as in dkv_kernel)
+  const int t_m = (int)min((int64_t)n_tiles, (pos0 + 1) / 64) & ~1;
   int t = 0;
-  for (; t < t_m; ++t) step(t, std::false_type{});
-  for (; t < n_tiles; ++t) step(t, std::true_type{});
+  for (; t < t_m; t += 2) {
+    step(t, J0{}, std::false_type{});
+    step(t + 1, J1{}, std::false_type{});
+  }
+  for (; t < n_tiles; t += 2) {
+    step(t, J0{}, std::true_type{});
+    if (t + 1 < n_tiles) step(t + 1, J1{}, std::true_type{});
+  }
 
   if (wave_active && wave_first + ql < valid) {
     float* dqp = a.dq + (row0 + wave_first + ql) * ld + hcol + 4 * half;
