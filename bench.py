@@ -138,6 +138,20 @@ def row_timings(plan, dims, D, layer0, x0, q, a, a_lo, out, ws_core, fl, dev, re
         ("A5 streamed: D x tsp_attn_out_shard", "oproj", out_streamed),
         ("A6+A7 streamed: D x tsp_mlp_shard", "mlp", mlp_streamed),
     ]
+    # the all-shard calls that wait for each shard inside the kernels, with
+    # every shard already arrived (the counter preset): the cost of streaming
+    # when the next shards are prefetched while the current ones compute
+    counter = torch.full((4,), D, dtype=torch.int32, device=dev)
+    status = torch.zeros(4, dtype=torch.int32, device=dev)
+    arr = tsp.make_arrival(counter, 0, status)
+    calls += [
+        ("A2 shards awaited in the kernel, all arrived (tsp_attn_project_arrival)", "qkv",
+         lambda: tsp.attn_project_arrival(plan, dims, plan.rank, x0, lw.wqkv, kf, vf, q, arr)),
+        ("A5 shards awaited in the kernel, all arrived (tsp_attn_out_arrival)", "oproj",
+         lambda: tsp.attn_out_arrival(dims, D, plan.rank, a, lw.wo, x0, out, arr, attn_lo=a_lo)),
+        ("A6+A7 shards awaited in the kernel, all arrived (tsp_mlp_forward_arrival)", "mlp",
+         lambda: tsp.mlp_forward_arrival(dims, D, plan.rank, x0, lw.w1, lw.w2, x0, out, ws_mlp, arr)),
+    ]
     # backward of the MLP ring on layer 0's shapes: recomputes U = x W1^T, then
     # dU, dW2, dW1 and dx (five n x h x F products, 10 n h F FLOPs)
     dy = (torch.randn(n, dims.hidden, device=dev) * 0.02).to(torch.bfloat16)
@@ -232,6 +246,9 @@ def row_timings(plan, dims, D, layer0, x0, q, a, a_lo, out, ws_core, fl, dev, re
         else:
             tf = fl[key] / (ms * 1e-3) / 1e12
             rows[name] = {"ms": round(ms, 4), "tflops": round(tf, 1), "frac": round(tf / PEAK_BF16_TFLOPS, 4)}
+    torch.cuda.synchronize()
+    if int(status[0]) != 0:
+        raise RuntimeError("an arrival wait gave up with every shard arrived")
     del ws_mlp, ws_mlp_s, ws_out_s, k8, v8, ws_bwd, dw1, dw2, dy, dx, ws_abwd, dq_b, dk_b, dv_b, lse, d_attn
     del dwo_b, dwqkv_b, d_attn_b, dx_b, ws_obwd, ws_pbwd, lse8, dk8, dv8, dgain, dq_rope, dk_rope, ws_rms
     return rows

@@ -186,7 +186,10 @@ __device__ __forceinline__ void store_row8(const GemmArgs& g, int nshard, int ro
 template <int BM, int BN, int EPI, bool F16, bool LO = false>
 __global__ __launch_bounds__((Cfg<BM, BN>::NT)) void gemm_kernel(const GemmArgs g) {
   using C = Cfg<BM, BN, LO>;
-  __shared__ __attribute__((aligned(1024))) uint8_t smem[C::LDS_BYTES];
+  // the LDS ring, then one word for the shard-arrival broadcast (a second
+  // __shared__ object would make the compiler order every fragment read
+  // behind all LDS-bound loads in flight)
+  __shared__ __attribute__((aligned(1024))) uint8_t smem[C::LDS_BYTES + 16];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -246,6 +249,44 @@ __global__ __launch_bounds__((Cfg<BM, BN>::NT)) void gemm_kernel(const GemmArgs 
   // (k-tile within the shard, part of A, shard step of the ring) is walked
   // incrementally (wave-uniform scalars, no divisions).
   int nx_kt = 0, nx_part = 0, nx_d = g.k_shards > 1 ? g.ring_start : nshard;
+  // Shard arrival: ring position of the next tile's shard, and the positions
+  // known to have arrived (workgroup-uniform; INT32_MAX without a counter).
+  uint32_t* const arrival_word = reinterpret_cast<uint32_t*>(smem + C::LDS_BYTES);
+  int32_t avail = INT32_MAX, nx_pos = 0;
+  if (g.arrived) {
+    avail = -1;
+    nx_pos = g.k_shards > 1 ? 0 : (nshard - g.ring_start + g.n_shards) % g.n_shards;
+  }
+  // Called by all waves alike: wave 0 polls until position `pos` has arrived
+  // (or the poll budget is spent), then the count seen is passed to every
+  // wave through LDS between two barriers, so all waves take the same
+  // branches afterwards.
+  auto await_arrival = [&](int32_t pos) __attribute__((always_inline)) -> int32_t {
+    if (wave == 0) {
+      typedef __attribute__((address_space(1))) uint32_t gu32;  // global, not flat: vm counter only
+      const gu32* counter = (const gu32*)g.arrived;
+      uint32_t seen = 0x7fffffffu;
+      for (uint32_t k = 0;; ++k) {
+        const uint32_t c = __hip_atomic_load(counter, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM) - g.arrived_base;
+        if ((int32_t)c > pos) {
+          seen = c;
+          break;
+        }
+        if (k >= g.spin_limit) {
+          if (lane == 0)
+            __hip_atomic_store((gu32*)g.arrival_status, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
+          break;
+        }
+        __builtin_amdgcn_s_sleep(32);
+      }
+      if (lane == 0) *arrival_word = seen;
+    }
+    __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): the LDS write is done
+    lds_barrier();
+    const int32_t a = (int32_t)__builtin_amdgcn_readfirstlane(*arrival_word);
+    lds_barrier();  // every wave has read the word before it can change
+    return a;
+  };
   // The matrices' pointers are kernel arguments; the current shard's weight
   // pointer is read again only at shard boundaries, and that scalar load is
   // waited for at once: a scalar load in flight shares the lgkm counter with
@@ -255,6 +296,7 @@ __global__ __launch_bounds__((Cfg<BM, BN>::NT)) void gemm_kernel(const GemmArgs 
   const uint16_t* bshard = g.B[nx_d] + (int64_t)n0 * g.K_s;
   asm volatile("" ::"s"(a_hi), "s"(a_lo), "s"(bshard));  // in registers before the loop
   auto issue_tile = [&](int t) __attribute__((always_inline)) {
+    if (nx_pos >= avail) avail = await_arrival(nx_pos);
     const int64_t acol = (g.k_shards > 1 ? (int64_t)nx_d * g.K_s : 0) + nx_kt * BK;
     const __amdgpu_buffer_rsrc_t ra = buffer_rsrc((nx_part ? a_lo : a_hi) + acol, a_bytes);
     const __amdgpu_buffer_rsrc_t rb = buffer_rsrc(bshard + nx_kt * BK, b_bytes);
@@ -265,6 +307,7 @@ __global__ __launch_bounds__((Cfg<BM, BN>::NT)) void gemm_kernel(const GemmArgs 
         nx_part = 0;
         if (g.k_shards > 1) {
           if (++nx_d == g.k_shards) nx_d = 0;
+          ++nx_pos;
           bshard = g.B[nx_d] + (int64_t)n0 * g.K_s;
           __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0)
         }

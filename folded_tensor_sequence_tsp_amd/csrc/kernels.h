@@ -64,12 +64,35 @@ struct GemmArgs {
   // v_full (0: as many as the query heads, stride hidden)
   int32_t kv_heads_per_shard, kv_ld;
   int64_t chunk_len, chunk_start0, chunk_start1;
+  // Shard arrival (nullable `arrived`): a shard is read only once
+  // (int32_t)(*arrived - arrived_base) exceeds its ring position (K-sharded:
+  // the count of shards walked before it from ring_start; N-sharded shard s:
+  // (s - ring_start) mod n_shards).  Wave 0 of a workgroup polls the counter
+  // with system-scope loads at the tile's first load and at each later shard
+  // not yet known to have arrived; a wait that has polled spin_limit times
+  // sets *arrival_status = 1 and the tile goes on as if everything had arrived.
+  const uint32_t* arrived;
+  uint32_t arrived_base, spin_limit;
+  uint32_t* arrival_status;
 };
 
 // hipErrorInvalidValue when 256 rows of A (lda) or of a B shard (K_s) span
 // more than 2^31 bytes (the loads address a tile through one buffer
 // descriptor with 32-bit offsets): lda, K_s < 4,194,304 elements.
 hipError_t launch_gemm(const GemmArgs& args, hipStream_t stream);
+
+// Simulated shard arrival on one workgroup: for i = 0..n-1, wait until
+// (i + 1) * delay_ticks of the 100 MHz wall clock have passed since the kernel
+// started, copy bytes[i] (a multiple of 16) from src[i] to dst[i], write the
+// copy back to memory, then store base + i + 1 into *counter (system scope).
+constexpr int ARRIVAL_MAX = 64;
+struct ArrivalCopies {
+  const void* src[ARRIVAL_MAX];
+  void* dst[ARRIVAL_MAX];
+  uint64_t bytes[ARRIVAL_MAX];
+};
+hipError_t launch_simulate_arrival(const ArrivalCopies& c, int32_t n, uint32_t* counter, uint32_t base,
+                                   uint64_t delay_ticks, hipStream_t stream);
 
 // For each row i of x [n x h] (fp32 when x_f32, else bf16):
 //   row_exp[i] = floor(log2(rms of the row)) (0 for a zero or non-finite rms),

@@ -92,7 +92,46 @@ __global__ __launch_bounds__(256) void bf16_to_f16_kernel(const ShardPtrs src, u
   }
 }
 
+// Simulated arrival of weight shards (one workgroup).  Shard i is released
+// (i + 1) * delay_ticks after the kernel starts: its bytes are copied, written
+// back to memory by a system-scope release fence in every wave, and after a
+// barrier the counter is raised to base + i + 1 with a system-scope store.
+__global__ __launch_bounds__(1024) void simulate_arrival_kernel(const ArrivalCopies c, int32_t n,
+                                                                uint32_t* __restrict__ counter, uint32_t base,
+                                                                uint64_t delay_ticks) {
+  typedef __attribute__((address_space(1))) uint32_t gu32;
+  const uint64_t t0 = wall_clock64();  // 100 MHz
+  for (int i = 0; i < n; ++i) {
+    const uint64_t due = (uint64_t)(i + 1) * delay_ticks;
+    while (wall_clock64() - t0 < due) __builtin_amdgcn_s_sleep(8);  // ends: the clock advances
+    const u32x4* src = static_cast<const u32x4*>(c.src[i]);
+    u32x4* dst = static_cast<u32x4*>(c.dst[i]);
+    const int64_t n16 = (int64_t)(c.bytes[i] / 16);
+    constexpr int U = 8;  // loads in flight per thread
+    int64_t j = threadIdx.x;
+    for (; j + (U - 1) * (int64_t)blockDim.x < n16; j += U * (int64_t)blockDim.x) {
+      u32x4 v[U];
+#pragma unroll
+      for (int u = 0; u < U; ++u) v[u] = src[j + u * (int64_t)blockDim.x];
+#pragma unroll
+      for (int u = 0; u < U; ++u) dst[j + u * (int64_t)blockDim.x] = v[u];
+    }
+    for (; j < n16; j += blockDim.x) dst[j] = src[j];
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "");
+    __syncthreads();
+    if (threadIdx.x == 0) __hip_atomic_store((gu32*)counter, base + (uint32_t)i + 1u, __ATOMIC_RELAXED,
+                                             __HIP_MEMORY_SCOPE_SYSTEM);
+  }
+}
+
 }  // namespace
+
+hipError_t launch_simulate_arrival(const ArrivalCopies& c, int32_t n, uint32_t* counter, uint32_t base,
+                                   uint64_t delay_ticks, hipStream_t stream) {
+  if (n <= 0) return hipSuccess;
+  hipLaunchKernelGGL(simulate_arrival_kernel, dim3(1), dim3(1024), 0, stream, c, n, counter, base, delay_ticks);
+  return hipGetLastError();
+}
 
 hipError_t launch_row_prep(const void* x, int32_t x_f32, int64_t n, int32_t h, int32_t* row_exp, uint16_t* x16,
                            hipStream_t stream) {

@@ -3,6 +3,8 @@
 // before the first launch, so an error status means nothing was enqueued.
 #include <string.h>
 
+#include <functional>
+
 #include "kernels.h"
 
 using namespace tsp;
@@ -23,6 +25,21 @@ tsp_status check_ptr(const void* p) {
 }
 
 tsp_status check_ptr_nullable(const void* p) { return (p && !aligned16(p)) ? TSP_ERR_ALIGNMENT : TSP_OK; }
+
+tsp_status check_arrival(const tsp_arrival* a) {
+  if (!a || !a->counter || !a->status) return TSP_ERR_INVALID_ARG;
+  if (((uintptr_t)a->counter & 3u) || ((uintptr_t)a->status & 3u)) return TSP_ERR_ALIGNMENT;
+  return TSP_OK;
+}
+
+// The GEMM's shard-arrival fields (nothing when a is null).
+void set_arrival(GemmArgs& g, const tsp_arrival* a) {
+  if (!a) return;
+  g.arrived = a->counter;
+  g.arrived_base = a->base;
+  g.spin_limit = a->spin_limit ? a->spin_limit : TSP_ARRIVAL_SPIN_DEFAULT;
+  g.arrival_status = a->status;
+}
 
 // A workspace of `need` bytes: null, misaligned or short is an error unless
 // nothing is needed (then the pointer is not used and may be null).
@@ -115,9 +132,11 @@ tsp_status from_hip(hipError_t e) { return e == hipSuccess ? TSP_OK : TSP_ERR_HI
 
 // ---- launches (arguments already validated) ---------------------------------
 
+// QKV projection over all D shards; with an arrival counter, shard d is read
+// once ring position (d - start) mod D has arrived.
 tsp_status run_project(const tsp_plan* plan, const tsp_dims* dims, const uint16_t* x,
                        const uint16_t* const* wqkv, uint16_t* k_full, uint16_t* v_full, uint16_t* q_out,
-                       hipStream_t stream) {
+                       hipStream_t stream, int32_t start = 0, const tsp_arrival* arr = nullptr) {
   GemmArgs g{};
   g.A = x;
   g.lda = dims->hidden;
@@ -128,7 +147,8 @@ tsp_status run_project(const tsp_plan* plan, const tsp_dims* dims, const uint16_
   g.K_s = dims->hidden;
   g.n_shards = plan->D;
   g.k_shards = 1;
-  g.ring_start = 0;
+  g.ring_start = start;
+  set_arrival(g, arr);
   g.epilogue = EPI_QKV;
   g.q_out = q_out;
   g.k_full = k_full;
@@ -167,8 +187,9 @@ tsp_status run_core(const tsp_plan* plan, const tsp_dims* dims, const uint16_t* 
 
 tsp_status run_out(int64_t n, const tsp_dims* dims, int32_t D, int32_t start, const uint16_t* attn,
                    const uint16_t* attn_lo, const uint16_t* const* wo, const uint16_t* residual, void* out,
-                   bool out_f32, hipStream_t stream) {
+                   bool out_f32, hipStream_t stream, const tsp_arrival* arr = nullptr) {
   GemmArgs g{};
+  set_arrival(g, arr);
   g.A = attn;
   g.A_lo = attn_lo;
   g.lda = dims->hidden;
@@ -191,9 +212,13 @@ tsp_status run_out(int64_t n, const tsp_dims* dims, int32_t D, int32_t start, co
 // (a_f16) fp16 scaled by 2^-row_exp.  `w1` are bf16 or fp16 shards to match;
 // `w2h` is the fp16 copy of the W2 shards (D blocks of [hidden x F_s]).
 // y = [residual +] sum_k GELU(x W1_{d_k}^T) W2_{d_k}^T, fp32 across all shards.
+// With an arrival counter the W1 GEMMs wait for their shards; `after_w1`
+// (nullable) runs after the first token block's W1 GEMM, which has then seen
+// every shard pair arrive.
 tsp_status run_mlp_core(int64_t n, const tsp_dims* dims, int32_t D, int32_t start, const uint16_t* a, bool a_f16,
                         const uint16_t* const* w1, const uint16_t* w2h, const int32_t* row_exp,
-                        const void* residual, bool res_f32, uint16_t* y, uint16_t* hbuf, hipStream_t stream) {
+                        const void* residual, bool res_f32, uint16_t* y, uint16_t* hbuf, hipStream_t stream,
+                        const tsp_arrival* arr = nullptr, const std::function<tsp_status()>& after_w1 = {}) {
   const int64_t h = dims->hidden;
   const int32_t fs = dims->ffn / D;
   for (int64_t b0 = 0; b0 < n; b0 += MLP_TOKEN_BLOCK) {
@@ -214,8 +239,11 @@ tsp_status run_mlp_core(int64_t n, const tsp_dims* dims, int32_t D, int32_t star
     g1.ldo = dims->ffn;
     g1.row_exp = row_exp + b0;
     g1.gelu_in_scaled = a_f16;
+    g1.ring_start = start;
+    set_arrival(g1, arr);
     tsp_status s = from_hip(launch_gemm(g1, stream));
     if (s != TSP_OK) return s;
+    if (b0 == 0 && after_w1 && (s = after_w1()) != TSP_OK) return s;
     // y = [residual +] 2^row_exp * sum over shards in ring order of hbuf[:, d block] W2_d^T
     GemmArgs g2{};
     g2.f16 = 1;
@@ -244,7 +272,7 @@ tsp_status run_mlp_core(int64_t n, const tsp_dims* dims, int32_t D, int32_t star
 
 tsp_status run_mlp(int64_t n, const tsp_dims* dims, int32_t D, int32_t start, const uint16_t* x,
                    const uint16_t* const* w1, const uint16_t* const* w2, const uint16_t* residual, uint16_t* y,
-                   void* ws, hipStream_t stream) {
+                   void* ws, hipStream_t stream, const tsp_arrival* arr = nullptr) {
   if (n == 0) return TSP_OK;
   const MlpWs lay = mlp_ws(n, dims);
   char* base = static_cast<char*>(ws);
@@ -253,9 +281,13 @@ tsp_status run_mlp(int64_t n, const tsp_dims* dims, int32_t D, int32_t start, co
   int32_t* row_exp = reinterpret_cast<int32_t*>(base + lay.exp_off);
   tsp_status s = from_hip(launch_row_prep(x, 0, n, dims->hidden, row_exp, nullptr, stream));
   if (s != TSP_OK) return s;
-  s = from_hip(launch_bf16_to_f16(w2, w2h, D, (int64_t)dims->hidden * (dims->ffn / D), stream));
-  if (s != TSP_OK) return s;
-  return run_mlp_core(n, dims, D, start, x, false, w1, w2h, row_exp, residual, false, y, hbuf, stream);
+  auto convert_w2 = [&]() { return from_hip(launch_bf16_to_f16(w2, w2h, D, (int64_t)dims->hidden * (dims->ffn / D), stream)); };
+  if (!arr) {  // the copy first: the W1 and W2 GEMMs of each token block then run back to back
+    if ((s = convert_w2()) != TSP_OK) return s;
+    return run_mlp_core(n, dims, D, start, x, false, w1, w2h, row_exp, residual, false, y, hbuf, stream);
+  }
+  return run_mlp_core(n, dims, D, start, x, false, w1, w2h, row_exp, residual, false, y, hbuf, stream, arr,
+                      convert_w2);
 }
 
 // Workspace of the post-attention half of the layer: fp32 h1, its scaled fp16
@@ -840,6 +872,76 @@ tsp_status tsp_mlp_shard(int64_t n_tokens, const tsp_dims* dims, int32_t D, int3
 }
 
 // ---- layer variants ------------------------------------------------------------
+
+tsp_status tsp_attn_project_arrival(const tsp_plan* plan, const tsp_dims* dims, int32_t start_shard,
+                                    const uint16_t* x_local, const uint16_t* const* wqkv, uint16_t* k_full,
+                                    uint16_t* v_full, uint16_t* q_out, const tsp_arrival* arrival,
+                                    hipStream_t stream) {
+  tsp_status s;
+  if ((s = check_plan(plan)) != TSP_OK) return s;
+  if ((s = check_dims(dims, plan->D, true, false)) != TSP_OK) return s;
+  if (start_shard < 0 || start_shard >= plan->D) return TSP_ERR_INVALID_ARG;
+  if ((s = check_ptr(x_local)) != TSP_OK || (s = check_shards(wqkv, plan->D)) != TSP_OK ||
+      (s = check_ptr(k_full)) != TSP_OK || (s = check_ptr(v_full)) != TSP_OK || (s = check_ptr(q_out)) != TSP_OK ||
+      (s = check_arrival(arrival)) != TSP_OK)
+    return s;
+  return run_project(plan, dims, x_local, wqkv, k_full, v_full, q_out, stream, start_shard, arrival);
+}
+
+tsp_status tsp_attn_out_arrival(int64_t n_tokens, const tsp_dims* dims, int32_t D, int32_t start_shard,
+                                const uint16_t* attn, const uint16_t* attn_lo, const uint16_t* const* wo,
+                                const uint16_t* residual, uint16_t* out, const tsp_arrival* arrival,
+                                hipStream_t stream) {
+  tsp_status s;
+  if ((s = check_dims(dims, D, true, false)) != TSP_OK) return s;
+  if (n_tokens < 0) return TSP_ERR_SHAPE;
+  if (n_tokens > INT32_MAX) return TSP_ERR_UNSUPPORTED;
+  if (start_shard < 0 || start_shard >= D) return TSP_ERR_INVALID_ARG;
+  if ((s = check_ptr(attn)) != TSP_OK || (s = check_ptr_nullable(attn_lo)) != TSP_OK ||
+      (s = check_shards(wo, D)) != TSP_OK || (s = check_ptr_nullable(residual)) != TSP_OK ||
+      (s = check_ptr(out)) != TSP_OK || (s = check_arrival(arrival)) != TSP_OK)
+    return s;
+  if (out == attn || (attn_lo && out == attn_lo)) return TSP_ERR_INVALID_ARG;
+  return run_out(n_tokens, dims, D, start_shard, attn, attn_lo, wo, residual, out, false, stream, arrival);
+}
+
+tsp_status tsp_mlp_forward_arrival(int64_t n_tokens, const tsp_dims* dims, int32_t D, int32_t start_shard,
+                                   const uint16_t* x, const uint16_t* const* w1, const uint16_t* const* w2,
+                                   const uint16_t* residual, uint16_t* y, void* workspace, size_t ws_bytes,
+                                   const tsp_arrival* arrival, hipStream_t stream) {
+  tsp_status s;
+  if ((s = check_dims(dims, D, false, true)) != TSP_OK) return s;
+  if (n_tokens < 0) return TSP_ERR_SHAPE;
+  if (n_tokens > INT32_MAX) return TSP_ERR_UNSUPPORTED;
+  if (start_shard < 0 || start_shard >= D) return TSP_ERR_INVALID_ARG;
+  if ((s = check_ptr(x)) != TSP_OK || (s = check_shards(w1, D)) != TSP_OK || (s = check_shards(w2, D)) != TSP_OK ||
+      (s = check_ptr_nullable(residual)) != TSP_OK || (s = check_ptr(y)) != TSP_OK ||
+      (s = check_arrival(arrival)) != TSP_OK)
+    return s;
+  if (y == x && residual != x) return TSP_ERR_INVALID_ARG;
+  if (!workspace) return TSP_ERR_WORKSPACE;
+  if (!aligned16(workspace)) return TSP_ERR_ALIGNMENT;
+  if (ws_bytes < ws_mlp(n_tokens, dims)) return TSP_ERR_WORKSPACE;
+  if (n_tokens == 0) return TSP_OK;
+  return run_mlp(n_tokens, dims, D, start_shard, x, w1, w2, residual, y, workspace, stream, arrival);
+}
+
+tsp_status tsp_simulate_arrival(int32_t n, const void* const* src, void* const* dst, const size_t* bytes,
+                                uint32_t* counter, uint32_t base, uint32_t delay_us, hipStream_t stream) {
+  if (n < 0 || n > ARRIVAL_MAX || delay_us > 1000000u || !counter) return TSP_ERR_INVALID_ARG;
+  if ((uintptr_t)counter & 3u) return TSP_ERR_ALIGNMENT;
+  if (n > 0 && (!src || !dst || !bytes)) return TSP_ERR_INVALID_ARG;
+  ArrivalCopies c{};
+  for (int32_t i = 0; i < n; ++i) {
+    tsp_status s;
+    if ((s = check_ptr(src[i])) != TSP_OK || (s = check_ptr(dst[i])) != TSP_OK) return s;
+    if (bytes[i] % 16 != 0) return TSP_ERR_SHAPE;
+    c.src[i] = src[i];
+    c.dst[i] = dst[i];
+    c.bytes[i] = bytes[i];
+  }
+  return from_hip(launch_simulate_arrival(c, n, counter, base, (uint64_t)delay_us * 100u, stream));
+}
 
 tsp_status tsp_rms_norm(int64_t n_tokens, int32_t hidden, const uint16_t* x, const uint16_t* gain, float eps,
                         uint16_t* y, hipStream_t stream) {

@@ -30,7 +30,9 @@ EXPORTS = ["tsp_zigzag_plan", "tsp_workspace_size", "tsp_attn_project", "tsp_att
            "tsp_attn_core_gqa", "tsp_mlp_backward", "tsp_attn_core_lse", "tsp_attn_core_backward",
            "tsp_attn_out_backward", "tsp_attn_project_backward", "tsp_rope_backward", "tsp_rms_norm_backward",
            "tsp_attn_core_gqa_lse", "tsp_attn_core_gqa_backward", "tsp_memory_footprint", "tsp_status_string",
-           "tsp_attn_forward_noalloc"]
+           "tsp_attn_forward_noalloc", "tsp_attn_project_arrival", "tsp_attn_out_arrival",
+           "tsp_mlp_forward_arrival", "tsp_simulate_arrival"]
+ARRIVAL_SPIN_DEFAULT = 1 << 20
 MEM_TSP, MEM_TP = range(2)
 
 
@@ -47,6 +49,13 @@ class Plan(ctypes.Structure):
 
 class Dims(ctypes.Structure):
     _fields_ = [("hidden", c_int32), ("n_heads", c_int32), ("head_dim", c_int32), ("ffn", c_int32)]
+
+
+class Arrival(ctypes.Structure):
+    """tsp_arrival: a device counter of delivered shards, its value before the
+    call's first shard, the poll budget of one wait and a device status word."""
+    _fields_ = [("counter", c_void_p), ("base", ctypes.c_uint32), ("spin_limit", ctypes.c_uint32),
+                ("status", c_void_p)]
 
 
 class Memory(ctypes.Structure):
@@ -97,6 +106,11 @@ def lib() -> ctypes.CDLL:
                                            c_size_t, P],
             "tsp_memory_footprint": [c_int64, POINTER(Dims), c_int32, c_int32, c_int32, c_int32, POINTER(Memory)],
             "tsp_status_string": [c_int32],
+            "tsp_attn_project_arrival": [POINTER(Plan), POINTER(Dims), c_int32, P, PP, P, P, P, POINTER(Arrival), P],
+            "tsp_attn_out_arrival": [c_int64, POINTER(Dims), c_int32, c_int32, P, P, PP, P, P, POINTER(Arrival), P],
+            "tsp_mlp_forward_arrival": [c_int64, POINTER(Dims), c_int32, c_int32, P, PP, PP, P, P, P, c_size_t,
+                                        POINTER(Arrival), P],
+            "tsp_simulate_arrival": [c_int32, PP, PP, POINTER(c_size_t), P, ctypes.c_uint32, ctypes.c_uint32, P],
         }
         for name, args in sig.items():
             f = getattr(L, name)
@@ -362,6 +376,72 @@ def mlp_shard(dims: Dims, D: int, pos: int, x, w1_d, w2_d, residual, y, workspac
     args = (_dev_tensor(x, (n, h), "x"), _dev_tensor(w1_d, (Fs, h), "w1_d"), _dev_tensor(w2_d, (h, Fs), "w2_d"),
             _opt_tensor(residual, (n, h), "residual"), _dev_tensor(y, (n, h), "y"))
     _check(lib().tsp_mlp_shard(n, ctypes.byref(dims), D, pos, *args, ws, nbytes, _stream(stream)), "tsp_mlp_shard")
+
+
+# ---- calls that wait for their shards inside the kernels (see include/tsp.h)
+def _word(t, name: str) -> c_void_p:
+    if not isinstance(t, torch.Tensor) or t.device.type != "cuda" or t.dtype not in (torch.int32, torch.uint32) \
+            or t.numel() < 1:
+        raise ValueError(f"{name}: expected a 32-bit integer tensor on the HIP device")
+    return c_void_p(t.data_ptr())
+
+
+def make_arrival(counter, base: int, status, spin_limit: int = 0) -> Arrival:
+    """An arrival descriptor over the first element of the device tensors
+    ``counter`` and ``status`` (32-bit integers)."""
+    return Arrival(_word(counter, "counter").value, base & 0xFFFFFFFF, spin_limit, _word(status, "status").value)
+
+
+def attn_project_arrival(plan: Plan, dims: Dims, start_shard: int, x_local, wqkv, k_full, v_full, q_out,
+                         arrival: Arrival, stream=None):
+    n, h, S, D = plan.n_local, dims.hidden, plan.seq_len, plan.D
+    Hs = dims.n_heads // D if D > 0 else 0
+    args = (_dev_tensor(x_local, (n, h), "x_local"), _shards(wqkv, D, (3 * Hs * dims.head_dim, h), "wqkv"),
+            _dev_tensor(k_full, (S, h), "k_full"), _dev_tensor(v_full, (S, h), "v_full"),
+            _dev_tensor(q_out, (n, h), "q_out"))
+    _check(lib().tsp_attn_project_arrival(ctypes.byref(plan), ctypes.byref(dims), start_shard, *args,
+                                          ctypes.byref(arrival), _stream(stream)), "tsp_attn_project_arrival")
+
+
+def attn_out_arrival(dims: Dims, D: int, start_shard: int, attn, wo, residual, out, arrival: Arrival,
+                     attn_lo=None, stream=None):
+    n, h = attn.shape[0], dims.hidden
+    Hs = dims.n_heads // D if D > 0 else 0
+    args = (_dev_tensor(attn, (n, h), "attn"), _opt_tensor(attn_lo, (n, h), "attn_lo"),
+            _shards(wo, D, (h, Hs * dims.head_dim), "wo"),
+            _opt_tensor(residual, (n, h), "residual"), _dev_tensor(out, (n, h), "out"))
+    _check(lib().tsp_attn_out_arrival(n, ctypes.byref(dims), D, start_shard, *args, ctypes.byref(arrival),
+                                      _stream(stream)), "tsp_attn_out_arrival")
+
+
+def mlp_forward_arrival(dims: Dims, D: int, start_shard: int, x, w1, w2, residual, y, workspace,
+                        arrival: Arrival, stream=None):
+    n, h = x.shape[0], dims.hidden
+    Fs = dims.ffn // D if D > 0 else 0
+    need = workspace_size(n, dims, D, WS_MLP)
+    ws, nbytes = _workspace(workspace, need)
+    args = (_dev_tensor(x, (n, h), "x"), _shards(w1, D, (Fs, h), "w1"), _shards(w2, D, (h, Fs), "w2"),
+            _opt_tensor(residual, (n, h), "residual"), _dev_tensor(y, (n, h), "y"))
+    _check(lib().tsp_mlp_forward_arrival(n, ctypes.byref(dims), D, start_shard, *args, ws, nbytes,
+                                         ctypes.byref(arrival), _stream(stream)), "tsp_mlp_forward_arrival")
+
+
+def simulate_arrival(srcs, dsts, counter, base: int, delay_us: int, stream=None):
+    """Copy srcs[i] -> dsts[i] (device tensors of equal byte size) one after
+    another, (i + 1) * delay_us after the kernel starts, raising the counter to
+    base + i + 1 after each copy (tsp_simulate_arrival)."""
+    n = len(srcs)
+    if len(dsts) != n:
+        raise ValueError("simulate_arrival: srcs and dsts differ in length")
+    src, dst, nb = (c_void_p * max(n, 1))(), (c_void_p * max(n, 1))(), (c_size_t * max(n, 1))()
+    for i, (a, b) in enumerate(zip(srcs, dsts)):
+        if a.device.type != "cuda" or b.device.type != "cuda" or not a.is_contiguous() or not b.is_contiguous():
+            raise ValueError(f"simulate_arrival: shard {i} is not a contiguous device tensor")
+        if a.numel() * a.element_size() != b.numel() * b.element_size():
+            raise ValueError(f"simulate_arrival: shard {i} sizes differ")
+        src[i], dst[i], nb[i] = a.data_ptr(), b.data_ptr(), a.numel() * a.element_size()
+    _check(lib().tsp_simulate_arrival(n, src, dst, nb, _word(counter, "counter"), base & 0xFFFFFFFF, delay_us,
+                                      _stream(stream)), "tsp_simulate_arrival")
 
 
 # ---- layer variants (see include/tsp.h)

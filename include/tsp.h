@@ -449,6 +449,82 @@ tsp_status tsp_mlp_shard(int64_t n_tokens, const tsp_dims* dims, int32_t D, int3
                          void* workspace, size_t ws_bytes, hipStream_t stream);
 
 /*
+ * ---- Calls that wait for their shards inside the kernels ----
+ * The all-shard calls below take the same arguments as tsp_attn_project,
+ * tsp_attn_out and tsp_mlp_forward, plus an arrival counter: they can be
+ * launched before the layer's shards have arrived (para. 2: the shards reach a
+ * device one after another, by broadcast or around the ring), and each tile
+ * of their GEMMs reads a shard only once the counter shows it.  A shard that
+ * has arrived costs a tile one poll; the fp32 accumulator of the K-sharded
+ * products stays in registers across the shards, as in the all-shard calls,
+ * and the results are bit-identical to theirs.
+ *
+ * The producer (a copy engine, a peer's transfer, tsp_simulate_arrival)
+ * delivers the shards in ring order, position p = 0..D-1 being shard
+ * (start_shard + p) mod D; for the MLP, position p is the pair
+ * (W1_d, W2_d).  After the bytes of position p are in device memory it raises
+ * the counter to base + p + 1 with release semantics (or any larger value).
+ *
+ *   counter    : device, uint32, 4-byte aligned; read with system-scope loads
+ *                by one wave per workgroup, with a sleep between polls.
+ *   base       : the counter's value before this call's first shard; the
+ *                comparison is modulo 2^32, so a counter may run across calls.
+ *   spin_limit : polls of one wait before it gives up (0: TSP_ARRIVAL_SPIN_DEFAULT,
+ *                a few seconds); a wait that gives up sets *status = 1 and the
+ *                call then reads whatever the shard buffers hold.
+ *   status     : device, uint32, 4-byte aligned, required; set to 1 by a wait
+ *                that gave up, never cleared by the library.
+ * The waiting workgroups occupy their CUs: a producer that needs CUs (a copy
+ * kernel) must already be resident, or the grid must leave CUs free.
+ */
+typedef struct {
+  const uint32_t* counter;
+  uint32_t base;
+  uint32_t spin_limit;
+  uint32_t* status;
+} tsp_arrival;
+#define TSP_ARRIVAL_SPIN_DEFAULT (1u << 20)
+
+/* tsp_attn_project with arrival; position p is head shard (start_shard + p) mod D
+ * (0 <= start_shard < D).  Errors: as tsp_attn_project, plus TSP_ERR_INVALID_ARG
+ * for a null arrival, counter or status or start_shard out of range,
+ * TSP_ERR_ALIGNMENT for a counter or status not 4-byte aligned. */
+tsp_status tsp_attn_project_arrival(const tsp_plan* plan, const tsp_dims* dims, int32_t start_shard,
+                                    const uint16_t* x_local, const uint16_t* const* wqkv, uint16_t* k_full,
+                                    uint16_t* v_full, uint16_t* q_out, const tsp_arrival* arrival,
+                                    hipStream_t stream);
+
+/* tsp_attn_out with arrival.  Errors: as tsp_attn_out, plus those of the arrival. */
+tsp_status tsp_attn_out_arrival(int64_t n_tokens, const tsp_dims* dims, int32_t D, int32_t start_shard,
+                                const uint16_t* attn, const uint16_t* attn_lo, const uint16_t* const* wo,
+                                const uint16_t* residual, uint16_t* out, const tsp_arrival* arrival,
+                                hipStream_t stream);
+
+/* tsp_mlp_forward with arrival (workspace TSP_WS_MLP).  The fp16 copy of W2 is
+ * made after the W1 GEMM, which has then seen every pair arrive.  Errors: as
+ * tsp_mlp_forward, plus those of the arrival. */
+tsp_status tsp_mlp_forward_arrival(int64_t n_tokens, const tsp_dims* dims, int32_t D, int32_t start_shard,
+                                   const uint16_t* x, const uint16_t* const* w1, const uint16_t* const* w2,
+                                   const uint16_t* residual, uint16_t* y, void* workspace, size_t ws_bytes,
+                                   const tsp_arrival* arrival, hipStream_t stream);
+
+/*
+ * Simulated arrival, for tests and measurements on one device: a one-workgroup
+ * kernel that, for i = 0..n-1, waits until (i + 1) * delay_us microseconds
+ * after it started, copies bytes[i] from src[i] to dst[i], writes the copy back
+ * to memory and raises *counter to base + i + 1 (system scope).  It stands in
+ * for the shard transfers of the other ranks (para. 2).
+ *   n        : 0 <= n <= 64.   src, dst: host arrays of n device pointers,
+ *              16-byte aligned; dst[i] must not overlap any src or other dst.
+ *   bytes    : host array of n sizes, each a multiple of 16.
+ *   counter  : device, uint32, 4-byte aligned.   delay_us: <= 10^6.
+ * Errors: TSP_ERR_INVALID_ARG (null pointers, n or delay out of range),
+ *         TSP_ERR_ALIGNMENT, TSP_ERR_SHAPE (a size not a multiple of 16).
+ */
+tsp_status tsp_simulate_arrival(int32_t n, const void* const* src, void* const* dst, const size_t* bytes,
+                                uint32_t* counter, uint32_t base, uint32_t delay_us, hipStream_t stream);
+
+/*
  * ---- Layer variants of a real decoder ----
  * Not on the TSP pages (their layer has no norm, no positional encoding, and
  * 32 K/V heads for 32 query heads); these are the published definitions, for

@@ -90,6 +90,25 @@ void layer_calls(const Shape& sh, int32_t r) {
      "layer_post");
   ok(tsp_layer_forward(&plan, &dims, x, wqkv, wo, w1, w2, kf, vf, out, ws(sz(TSP_WS_LAYER)), sz(TSP_WS_LAYER), 0),
      "layer_forward");
+  // shards awaited inside the kernels, and the simulated producer
+  uint32_t* cnt = reinterpret_cast<uint32_t*>(f32(1));
+  uint32_t* st = reinterpret_cast<uint32_t*>(f32(1));
+  const tsp_arrival arr{cnt, 0u, 0u, st};
+  ok(tsp_attn_project_arrival(&plan, &dims, r, x, wqkv, kf, vf, q, &arr, 0), "attn_project_arrival");
+  ok(tsp_attn_out_arrival(n, &dims, D, r, a, alo, wo, x, out, &arr, 0), "attn_out_arrival");
+  ok(tsp_mlp_forward_arrival(n, &dims, D, r, x, w1, w2, x, out, ws(sz(TSP_WS_MLP)), sz(TSP_WS_MLP), &arr, 0),
+     "mlp_forward_arrival");
+  {
+    const void* src[TSP_MAX_D];
+    void* dst[TSP_MAX_D];
+    size_t nb[TSP_MAX_D];
+    for (int d = 0; d < D; ++d) {
+      src[d] = wo[d];
+      dst[d] = bf(h * hs_hd);
+      nb[d] = (size_t)h * hs_hd * 2;
+    }
+    ok(tsp_simulate_arrival(D, src, dst, nb, cnt, 0u, 10u, 0), "simulate_arrival");
+  }
   // shard streaming: one ring
   void* w_os = ws(sz(TSP_WS_OUT_SHARD));
   void* w_ms = ws(sz(TSP_WS_MLP_SHARD));

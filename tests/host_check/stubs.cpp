@@ -83,6 +83,11 @@ hipError_t launch_gemm(const GemmArgs& g, hipStream_t) {
   if (g.A_lo) hc_need(g.A_lo, span(g.M, g.lda, acols, 2), "gemm A_lo");
   for (int d = 0; d < std::max(g.n_shards, g.k_shards); ++d) hc_need(g.B[d], (size_t)g.N_s * g.K_s * 2, "gemm B shard");
   if (g.row_exp) hc_need(g.row_exp, (size_t)g.M * 4, "gemm row_exp");
+  if (g.arrived) {
+    hc_need(g.arrived, 4, "gemm arrival counter");
+    hc_need(g.arrival_status, 4, "gemm arrival status");
+    hc_expect(g.spin_limit > 0, "gemm: a bounded arrival wait");
+  }
   const int64_t ncols = (int64_t)g.N_s * g.n_shards;
   switch (g.epilogue) {
     case EPI_QKV: {
@@ -125,6 +130,20 @@ hipError_t launch_gemm(const GemmArgs& g, hipStream_t) {
       if (g.residual) hc_need(g.residual, span(g.M, g.ldo, ncols, g.res_f32 ? 4 : 2), "resid residual");
       break;
     }
+  }
+  hc_count_launch();
+  return hipSuccess;
+}
+
+hipError_t launch_simulate_arrival(const ArrivalCopies& c, int32_t n, uint32_t* counter, uint32_t, uint64_t,
+                                   hipStream_t) {
+  if (n <= 0) return hipSuccess;
+  hc_expect(n <= ARRIVAL_MAX, "simulate_arrival: copies");
+  hc_need(counter, 4, "simulate_arrival counter");
+  for (int i = 0; i < n; ++i) {
+    hc_expect(c.bytes[i] % 16 == 0, "simulate_arrival: 16-byte multiples");
+    hc_need(c.src[i], c.bytes[i], "simulate_arrival src");
+    hc_need(c.dst[i], c.bytes[i], "simulate_arrival dst");
   }
   hc_count_launch();
   return hipSuccess;

@@ -479,3 +479,51 @@ def test_variant_backward_rejects(L):
     gl = lambda kv: L.tsp_attn_core_gqa_lse(ctypes.byref(p), ctypes.byref(d), kv, A, A + 64, A + 128, A + 192, None,
                                             None, A + 1024, need_b, None)
     assert gl(2) == tsp.TSP_ERR_INVALID_ARG                           # lse missing
+
+
+def test_arrival_rejects(L):
+    p, d = _plan(), _dims()
+    w = _arr([A] * 4)
+    ok = tsp.Arrival(A, 0, 0, A + 16)
+    by = lambda arr: ctypes.byref(arr) if arr is not None else None
+
+    def proj(start=0, arr=ok):
+        return L.tsp_attn_project_arrival(ctypes.byref(p), ctypes.byref(d), start, A, w, A, A, A + 64, by(arr), None)
+
+    assert proj(arr=None) == tsp.TSP_ERR_INVALID_ARG
+    assert proj(arr=tsp.Arrival(None, 0, 0, A)) == tsp.TSP_ERR_INVALID_ARG      # no counter
+    assert proj(arr=tsp.Arrival(A, 0, 0, None)) == tsp.TSP_ERR_INVALID_ARG      # no status word
+    assert proj(arr=tsp.Arrival(A + 2, 0, 0, A)) == tsp.TSP_ERR_ALIGNMENT
+    assert proj(arr=tsp.Arrival(A, 0, 0, A + 1)) == tsp.TSP_ERR_ALIGNMENT
+    assert proj(start=4) == tsp.TSP_ERR_INVALID_ARG
+    assert proj(start=-1) == tsp.TSP_ERR_INVALID_ARG
+
+    def out(n=512, start=0, arr=ok, o=A + 64):
+        return L.tsp_attn_out_arrival(n, ctypes.byref(d), 4, start, A, None, w, None, o, by(arr), None)
+
+    assert out(arr=None) == tsp.TSP_ERR_INVALID_ARG
+    assert out(start=4) == tsp.TSP_ERR_INVALID_ARG
+    assert out(n=-1) == tsp.TSP_ERR_SHAPE
+    assert out(o=A) == tsp.TSP_ERR_INVALID_ARG                                   # out aliases attn
+    assert out(arr=tsp.Arrival(A + 1, 0, 0, A)) == tsp.TSP_ERR_ALIGNMENT
+
+    need = tsp.workspace_size(512, d, 4, tsp.WS_MLP)
+
+    def mlp(arr=ok, nb=need, start=0):
+        return L.tsp_mlp_forward_arrival(512, ctypes.byref(d), 4, start, A, w, w, None, A + 64, A + 128, nb, by(arr),
+                                         None)
+
+    assert mlp(arr=None) == tsp.TSP_ERR_INVALID_ARG
+    assert mlp(nb=need - 1) == tsp.TSP_ERR_WORKSPACE
+    assert mlp(start=5) == tsp.TSP_ERR_INVALID_ARG
+    assert mlp(arr=tsp.Arrival(A, 0, 0, A + 2)) == tsp.TSP_ERR_ALIGNMENT
+
+    src, dst, nb = _arr([A]), _arr([A + 64]), (ctypes.c_size_t * 1)(64)
+    assert L.tsp_simulate_arrival(65, src, dst, nb, A, 0, 0, None) == tsp.TSP_ERR_INVALID_ARG   # more than 64
+    assert L.tsp_simulate_arrival(-1, src, dst, nb, A, 0, 0, None) == tsp.TSP_ERR_INVALID_ARG
+    assert L.tsp_simulate_arrival(1, src, dst, nb, None, 0, 0, None) == tsp.TSP_ERR_INVALID_ARG
+    assert L.tsp_simulate_arrival(1, None, dst, nb, A, 0, 0, None) == tsp.TSP_ERR_INVALID_ARG
+    assert L.tsp_simulate_arrival(1, src, dst, nb, A + 2, 0, 0, None) == tsp.TSP_ERR_ALIGNMENT
+    assert L.tsp_simulate_arrival(1, _arr([MIS]), dst, nb, A, 0, 0, None) == tsp.TSP_ERR_ALIGNMENT
+    assert L.tsp_simulate_arrival(1, src, dst, (ctypes.c_size_t * 1)(40), A, 0, 0, None) == tsp.TSP_ERR_SHAPE
+    assert L.tsp_simulate_arrival(1, src, dst, nb, A, 0, 2_000_000, None) == tsp.TSP_ERR_INVALID_ARG
