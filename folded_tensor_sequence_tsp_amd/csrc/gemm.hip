@@ -11,18 +11,22 @@
 //     fp32 accumulator held in registers, which is the local sum that stands
 //     in for tensor parallelism's all-reduce.
 //
-// Tiling: BM x BN x 32 block tile; waves of WM x WN (256 x 256 tiles: eight
+// Tiling: BM x BN x 64 block tile; waves of WM x WN (256 x 256 tiles: eight
 // waves of 128 x 64, two per SIMD; 128 x 256 tiles: eight waves of 64 x 64, for
 // short token counts; 128 x 128 tiles: four waves of 64 x 64), each a grid of
-// 32 x 32 MFMA tiles.  A and B k-tiles stream into a 4-stage LDS ring
-// with direct buffer->LDS loads (buffer_load_dwordx4 ... lds, no register
-// staging; the descriptors are rebased per k-tile in SGPRs), three k-tiles
-// ahead, one vmcnt wait and one barrier per k-tile.  Buffer rather than
-// global loads: the compiler counts a global->LDS load against the LDS
-// counter as well, so with loads always in flight every fragment wait became
-// a wait for all of them; with buffer loads the waits are graduated.  LDS rows are
-// 64 bytes (32 k values); the four 16-byte chunks of row r sit at chunk
-// positions c ^ ((r / 4) % 4), so the 16 lanes of one LDS cycle, reading 16
+// 32 x 32 MFMA tiles.  A and B k-tiles stream into an LDS ring with direct
+// buffer->LDS loads (buffer_load_dwordx4 ... lds, no register staging; the
+// descriptors are rebased per k-tile in SGPRs), one vmcnt wait and one
+// barrier per k-tile: 256 x 256 tiles have two 64 KB stages (the other stage
+// is refilled right after the barrier, before the MFMAs), 128 x 256 three,
+// 128 x 128 four.  Shard widths that are not a multiple of 64, and the O
+// projection's two-part A, use 32-k tiles in a 4-stage (3 with two parts)
+// ring.  Buffer rather than global loads: the compiler counts a global->LDS
+// load against the LDS counter as well, so with loads always in flight every
+// fragment wait became a wait for all of them; with buffer loads the waits
+// are graduated.  LDS rows are 128 bytes (64 k values; 64 bytes for 32-k
+// tiles); the 16-byte chunk c of row r sits at c ^ ((r / 2) % 8)
+// (c ^ ((r / 4) % 4)), so the 16 lanes of one LDS cycle, reading 16
 // consecutive rows at one k offset, hit distinct banks of the 64-bank LDS.
 // Workgroup ids are remapped so each XCD (ids = x mod 8) gets a contiguous run
 // of tiles, then rasterised in groups of 8 (QKV) or 4 tile rows for L2 reuse.
@@ -35,13 +39,21 @@
 namespace tsp {
 namespace {
 
-constexpr int BK = 32;       // k per tile: one 64-byte LDS row per operand row
-constexpr int STAGES = 4;    // LDS ring depth
+constexpr int STAGES = 4;    // LDS ring depth of 32-k tiles
+#ifndef GEMM_K64_DEFAULT
+#define GEMM_K64_DEFAULT 1
+#endif
+constexpr bool GEMM_K64 = GEMM_K64_DEFAULT;
 
 // LO: the low part of A (A_lo) shares each k-tile with A: a stage holds the
 // A, A_lo and B tiles, and every B fragment feeds two MFMAs (three stages).
-template <int BM, int BN, bool LO = false>
+// K64: 64-k tiles (128-byte LDS rows) in a shallower ring: 2 stages for
+// 256 x 256 tiles, 3 for 128 x 256, 4 for 128 x 128.
+template <int BM, int BN, bool LO = false, bool K64 = false>
 struct Cfg {
+  static constexpr int BK = K64 ? 64 : 32;  // k per tile
+  static constexpr int ROWB = BK * 2;       // bytes per LDS row
+  static constexpr int CPR = BK / 8;        // 16-byte chunks per row
   static constexpr int WM = BM == 256 ? 128 : 64;  // wave tile
   static constexpr int WN = 64;
   static constexpr int WAVES_M = BM / WM, WAVES_N = BN / WN;
@@ -53,7 +65,8 @@ struct Cfg {
   static constexpr int STAGE_BYTES = PARTS * A_BYTES + B_BYTES;
   static constexpr int A_LOADS = A_BYTES / (NT * 16), B_LOADS = B_BYTES / (NT * 16);  // per thread per k-tile
   static constexpr int LOADS = PARTS * A_LOADS + B_LOADS;
-  static constexpr int ST = LO ? 3 : STAGES;  // ring depth
+  static constexpr int ST = LO ? 3 : !K64 ? STAGES : (BM == 256 && BN == 256) ? 2 : (BM * BN > 128 * 128) ? 3 : 4;
+  static_assert(!(LO && K64), "the low part of A uses 32-k tiles");
   static constexpr int LDS_BYTES = ST * STAGE_BYTES;
   static_assert(A_LOADS >= 1 && B_LOADS >= 1 && A_BYTES % (NT * 16) == 0 && B_BYTES % (NT * 16) == 0, "tile split");
 };
@@ -183,9 +196,10 @@ __device__ __forceinline__ void store_row8(const GemmArgs& g, int nshard, int ro
   }
 }
 
-template <int BM, int BN, int EPI, bool F16, bool LO = false>
+template <int BM, int BN, int EPI, bool F16, bool LO = false, bool K64 = false>
 __global__ __launch_bounds__((Cfg<BM, BN>::NT)) void gemm_kernel(const GemmArgs g) {
-  using C = Cfg<BM, BN, LO>;
+  using C = Cfg<BM, BN, LO, K64>;
+  constexpr int BK = C::BK;
   // the LDS ring, then one word for the shard-arrival broadcast (a second
   // __shared__ object would make the compiler order every fragment read
   // behind all LDS-bound loads in flight)
@@ -226,18 +240,21 @@ __global__ __launch_bounds__((Cfg<BM, BN>::NT)) void gemm_kernel(const GemmArgs 
   // ((row/4)%4).  The byte offsets are relative to the tile's first row at
   // the k-tile's first column (the descriptors' base, rebased per k-tile in
   // SGPRs); rows past the matrix re-read its last row.
+  // chunk swizzle: 64-byte rows c ^ ((r/4) % 4), 128-byte rows c ^ ((r/2) % 8)
+  auto swz = [](int r) __attribute__((always_inline)) { return K64 ? ((r >> 1) & 7) : ((r >> 2) & 3); };
+  constexpr int RPB = 1024 / C::ROWB;  // rows per 1 KB block
   uint32_t a_off[C::A_LOADS];
 #pragma unroll
   for (int i = 0; i < C::A_LOADS; ++i) {
-    const int r = (i * C::NW + wave) * 16 + lane / 4;
-    const int c = (lane & 3) ^ ((r >> 2) & 3);
+    const int r = (i * C::NW + wave) * RPB + lane / C::CPR;
+    const int c = (lane % C::CPR) ^ swz(r);
     a_off[i] = (uint32_t)(((int64_t)(min(m0 + r, g.M - 1) - m0) * g.lda + c * 8) * 2);
   }
   uint32_t b_off[C::B_LOADS];
 #pragma unroll
   for (int i = 0; i < C::B_LOADS; ++i) {
-    const int r = (i * C::NW + wave) * 16 + lane / 4;
-    const int c = (lane & 3) ^ ((r >> 2) & 3);
+    const int r = (i * C::NW + wave) * RPB + lane / C::CPR;
+    const int c = (lane % C::CPR) ^ swz(r);
     b_off[i] = (uint32_t)(((int64_t)(min(n0 + r, g.N_s - 1) - n0) * g.K_s + c * 8) * 2);
   }
   // bytes a descriptor covers: the tile's rows (the launch checks that they
@@ -335,22 +352,22 @@ __global__ __launch_bounds__((Cfg<BM, BN>::NT)) void gemm_kernel(const GemmArgs 
   // 2*kk + lane/32, physical chunk (2*kk + lane/32) ^ ((r/4) % 4); the wave
   // row offsets are multiples of 32, so (r/4) % 4 = ((lane%32)/4) % 4.
   const int ql = lane & 31;
-  const uint32_t xr = (uint32_t)(((lane >> 5) ^ ((ql >> 2) & 3)) << 4);
-  const uint32_t a_row = (uint32_t)(wm * C::WM + ql) * 64;
-  const uint32_t b_row = (uint32_t)(C::PARTS * C::A_BYTES) + (uint32_t)(wn * C::WN + ql) * 64;
+  const uint32_t xr = (uint32_t)(((lane >> 5) ^ swz(ql)) << 4);
+  const uint32_t a_row = (uint32_t)(wm * C::WM + ql) * C::ROWB;
+  const uint32_t b_row = (uint32_t)(C::PARTS * C::A_BYTES) + (uint32_t)(wn * C::WN + ql) * C::ROWB;
 
   // Both k-steps' fragments are read before the first step's MFMAs (step 0's
   // first), so each MFMA waits only for its own fragments.
   auto compute_tile = [&](int t) __attribute__((always_inline)) {
     const uint8_t* stage = smem + (t % C::ST) * C::STAGE_BYTES;
-    u32x4 af[2][C::FM], bfv[2][C::FN];
+    u32x4 af[BK / 16][C::FM], bfv[BK / 16][C::FN];
 #pragma unroll
     for (int kk = 0; kk < BK / 16; ++kk) {
       const uint32_t kx = xr ^ (uint32_t)(kk << 5);
 #pragma unroll
-      for (int i = 0; i < C::FM; ++i) af[kk][i] = *reinterpret_cast<const u32x4*>(stage + a_row + i * 32 * 64 + kx);
+      for (int i = 0; i < C::FM; ++i) af[kk][i] = *reinterpret_cast<const u32x4*>(stage + a_row + i * 32 * C::ROWB + kx);
 #pragma unroll
-      for (int j = 0; j < C::FN; ++j) bfv[kk][j] = *reinterpret_cast<const u32x4*>(stage + b_row + j * 32 * 64 + kx);
+      for (int j = 0; j < C::FN; ++j) bfv[kk][j] = *reinterpret_cast<const u32x4*>(stage + b_row + j * 32 * C::ROWB + kx);
       if constexpr (!LO) __builtin_amdgcn_sched_barrier(0);  // step 0's reads first
     }
 #pragma unroll
@@ -360,8 +377,8 @@ __global__ __launch_bounds__((Cfg<BM, BN>::NT)) void gemm_kernel(const GemmArgs 
 #pragma unroll
         for (int j = 0; j < C::FN; ++j) acc[i][j] = mfma32_bits<F16>(af[kk][i], bfv[kk][j], acc[i][j]);
     if constexpr (!LO) {
-      __builtin_amdgcn_sched_group_barrier(0x008, C::FM * C::FN, 0);
-      __builtin_amdgcn_sched_group_barrier(0x008, C::FM * C::FN, 0);
+#pragma unroll
+      for (int kk = 0; kk < BK / 16; ++kk) __builtin_amdgcn_sched_group_barrier(0x008, C::FM * C::FN, 0);
     }
     if constexpr (LO) {  // the low part of A against the same B fragments
 #pragma unroll
@@ -369,7 +386,7 @@ __global__ __launch_bounds__((Cfg<BM, BN>::NT)) void gemm_kernel(const GemmArgs 
         const uint32_t kx = xr ^ (uint32_t)(kk << 5);
 #pragma unroll
         for (int i = 0; i < C::FM; ++i)
-          af[kk][i] = *reinterpret_cast<const u32x4*>(stage + C::A_BYTES + a_row + i * 32 * 64 + kx);
+          af[kk][i] = *reinterpret_cast<const u32x4*>(stage + C::A_BYTES + a_row + i * 32 * C::ROWB + kx);
       }
 #pragma unroll
       for (int kk = 0; kk < BK / 16; ++kk)
@@ -395,8 +412,13 @@ __global__ __launch_bounds__((Cfg<BM, BN>::NT)) void gemm_kernel(const GemmArgs 
     else
       wait_vmcnt<0>();
     lds_barrier();
-    compute_tile(t);
-    if (t + C::ST - 1 < k_tiles) issue_tile(t + C::ST - 1);
+    if constexpr (C::ST == 2) {  // refill the other stage before the MFMAs
+      if (t + 1 < k_tiles) issue_tile(t + 1);
+      compute_tile(t);
+    } else {
+      compute_tile(t);
+      if (t + C::ST - 1 < k_tiles) issue_tile(t + C::ST - 1);
+    }
   }
   wait_vmcnt<0>();
   __syncthreads();
@@ -458,32 +480,38 @@ __global__ __launch_bounds__((Cfg<BM, BN>::NT)) void gemm_kernel(const GemmArgs 
   }
 }
 
-template <int BM, int BN>
-hipError_t launch_tiles(const GemmArgs& g, hipStream_t stream) {
+template <int BM, int BN, bool K64>
+hipError_t launch_tiles_k(const GemmArgs& g, hipStream_t stream) {
   const int tiles_m = (g.M + BM - 1) / BM;
   const int tiles_n = ((g.N_s + BN - 1) / BN) * g.n_shards;
   const dim3 grid(tiles_m * tiles_n), block(Cfg<BM, BN>::NT);
   // Instantiated: QKV (bf16), W1 + GELU (bf16 or fp16), O projection (bf16), W2 (fp16),
   // GELU-derivative product (bf16, MLP backward).
   switch (g.epilogue) {
-    case EPI_QKV: hipLaunchKernelGGL((gemm_kernel<BM, BN, EPI_QKV, false>), grid, block, 0, stream, g); break;
-    case EPI_DGELU: hipLaunchKernelGGL((gemm_kernel<BM, BN, EPI_DGELU, false>), grid, block, 0, stream, g); break;
+    case EPI_QKV: hipLaunchKernelGGL((gemm_kernel<BM, BN, EPI_QKV, false, false, K64>), grid, block, 0, stream, g); break;
+    case EPI_DGELU: hipLaunchKernelGGL((gemm_kernel<BM, BN, EPI_DGELU, false, false, K64>), grid, block, 0, stream, g); break;
     case EPI_GELU:
       if (g.f16)
-        hipLaunchKernelGGL((gemm_kernel<BM, BN, EPI_GELU, true>), grid, block, 0, stream, g);
+        hipLaunchKernelGGL((gemm_kernel<BM, BN, EPI_GELU, true, false, K64>), grid, block, 0, stream, g);
       else
-        hipLaunchKernelGGL((gemm_kernel<BM, BN, EPI_GELU, false>), grid, block, 0, stream, g);
+        hipLaunchKernelGGL((gemm_kernel<BM, BN, EPI_GELU, false, false, K64>), grid, block, 0, stream, g);
       break;
     default:
       if (g.f16)
-        hipLaunchKernelGGL((gemm_kernel<BM, BN, EPI_RESID, true>), grid, block, 0, stream, g);
+        hipLaunchKernelGGL((gemm_kernel<BM, BN, EPI_RESID, true, false, K64>), grid, block, 0, stream, g);
       else if (g.A_lo)  // O projection on the attention output's two parts
-        hipLaunchKernelGGL((gemm_kernel<BM, BN, EPI_RESID, false, true>), grid, block, 0, stream, g);
+        hipLaunchKernelGGL((gemm_kernel<BM, BN, EPI_RESID, false, true, false>), grid, block, 0, stream, g);
       else
-        hipLaunchKernelGGL((gemm_kernel<BM, BN, EPI_RESID, false>), grid, block, 0, stream, g);
+        hipLaunchKernelGGL((gemm_kernel<BM, BN, EPI_RESID, false, false, K64>), grid, block, 0, stream, g);
       break;
   }
   return hipGetLastError();
+}
+
+template <int BM, int BN>
+hipError_t launch_tiles(const GemmArgs& g, hipStream_t stream) {
+  if (GEMM_K64 && g.K_s % 64 == 0 && !g.A_lo) return launch_tiles_k<BM, BN, true>(g, stream);
+  return launch_tiles_k<BM, BN, false>(g, stream);
 }
 
 }  // namespace

@@ -475,7 +475,11 @@ tsp_status tsp_mlp_shard(int64_t n_tokens, const tsp_dims* dims, int32_t D, int3
  *   status     : device, uint32, 4-byte aligned, required; set to 1 by a wait
  *                that gave up, never cleared by the library.
  * The waiting workgroups occupy their CUs: a producer that needs CUs (a copy
- * kernel) must already be resident, or the grid must leave CUs free.
+ * kernel) must already be resident, or the grid must leave CUs free.  A
+ * producer on the same device must also not be queued behind the call: HIP
+ * streams share hardware queues once there are more streams than queues, so
+ * enqueue the producer first (it then either runs alongside or completes
+ * before the call starts).
  */
 typedef struct {
   const uint32_t* counter;

@@ -9,8 +9,8 @@ bit-identity with the all-shard calls on resident weights:
 
   * every shard arrived before the launch (counter preset), for ring starts 0
     and D-1, with a counter base that wraps modulo 2^32;
-  * shards delivered while the call runs: the shard buffers start as NaN, the
-    consumer is launched first and a one-workgroup producer on a side stream
+  * shards delivered while the call runs: the shard buffers start as NaN, and
+    a one-workgroup producer on a side stream, launched just before the call,
     copies the shards in ring order, 150 us apart, raising the counter after
     each; any read before arrival would leave NaN or another value in the
     result;
@@ -136,8 +136,9 @@ def test_arrived_before_launch_bit_identical(h, H, hd, D, S, r, base):
 
 
 def _deliver(c, kind, start, delay_us=150):
-    """Launch the arrival call on NaN shard buffers, then deliver the shards in
-    ring order from a side stream; returns (result, status)."""
+    """Deliver the shards in ring order from a side stream into NaN shard
+    buffers, with the arrival call launched right after the producer; returns
+    (result, status)."""
     D = c.D
     src = {"qkv": c.wqkv, "out": c.wo, "mlp": c.pairs}[kind]
     dst = [torch.full_like(t, float("nan")) for t in src]
@@ -148,14 +149,17 @@ def _deliver(c, kind, start, delay_us=150):
     side = torch.cuda.Stream()
     side.wait_stream(main)  # the NaN fills and the counter are in place first
     arr = tsp.make_arrival(counter, base, status)
+    # the producer goes first: streams may share a hardware queue (more streams
+    # than queues), and a producer queued behind the waiting consumer could not
+    # run until the consumer's waits gave up
+    ring = [(start + p) % D for p in range(D)]
+    tsp.simulate_arrival([src[d] for d in ring], [dst[d] for d in ring], counter, base, delay_us, stream=side)
     if kind == "qkv":
         res = c.project_arr(dst, start, arr)
     elif kind == "out":
         res = c.out_arr(dst, start, True, arr)
     else:
         res = c.mlp_arr(dst, start, arr)
-    ring = [(start + p) % D for p in range(D)]
-    tsp.simulate_arrival([src[d] for d in ring], [dst[d] for d in ring], counter, base, delay_us, stream=side)
     torch.cuda.synchronize()
     for d in range(D):
         assert torch.equal(dst[d], src[d])
