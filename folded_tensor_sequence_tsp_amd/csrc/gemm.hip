@@ -397,9 +397,11 @@ __global__ __launch_bounds__((Cfg<BM, BN>::NT)) void gemm_kernel(const GemmArgs 
     }
   };
 
-  // ---- main loop: wait for tile t (tiles t+1, t+2 may still be in flight),
-  // barrier (tile t visible to all waves; everyone is done with tile t-1),
-  // compute tile t, then refill the stage of tile t-1 with tile t+3.
+  // ---- main loop: wait for tile t (the up to ST-2 tiles issued after it may
+  // still be in flight), barrier (tile t visible to all waves; everyone is
+  // done with tile t-1), compute tile t, then refill the stage of tile t-1
+  // with tile t+ST-1; with two stages that refill (tile t+1) goes before the
+  // MFMAs, so that it has the whole of tile t's compute to land.
   const int pro = min(C::ST - 1, k_tiles);
   for (int t = 0; t < pro; ++t) issue_tile(t);
   __builtin_amdgcn_s_waitcnt(0xC07F);  // no scalar load in flight in the loop
