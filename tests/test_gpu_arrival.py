@@ -17,8 +17,8 @@ bit-identity with the all-shard calls on resident weights:
   * a wait that gives up: the counter is never raised and the poll budget is
     tiny, so every wait gives up, sets the status word and the call finishes
     on the (resident) buffers;
-  * the 7B shapes at S = 16384, D = 8, rank 0 (the weight-streaming workload),
-    all shards arrived.
+  * the 7B shapes at S = 16384 and 131072, D = 8, rank 0 (the two benchmark
+    workloads), all shards arrived.
 """
 import pytest
 import torch
@@ -203,10 +203,11 @@ def test_wait_gives_up(kind):
         assert torch.equal(g_, w_)
 
 
-def test_7b_16k_arrived_bit_identical():
+@pytest.mark.parametrize("S", [16384, 131072])
+def test_7b_arrived_bit_identical(S):
     require_gpu()
     d = synth.DIMS_7B
-    D, S = 8, 16384
+    D = 8
     plan, _, _ = tsp.zigzag_plan(S, D, 0)
     n, h = plan.n_local, d.hidden
     dims = tsp.make_dims(h, d.n_heads, d.head_dim, d.ffn)
@@ -216,19 +217,19 @@ def test_7b_16k_arrived_bit_identical():
     lo = (_rnd((n, h), 44) * 2 ** -9).to(torch.bfloat16)
     counter, status = _preset(0, D)
     arr = tsp.make_arrival(counter, 0, status)
-    say("arrival 7B S=16384 D=8 qkv")
+    say(f"arrival 7B S={S} D=8 qkv")
     k0, v0 = torch.zeros(S, h, dtype=torch.bfloat16, device=DEV), torch.zeros(S, h, dtype=torch.bfloat16, device=DEV)
     q1, k1, v1 = bf16_nan((n, h), DEV), k0.clone(), v0.clone()
     q2, k2, v2 = bf16_nan((n, h), DEV), k0.clone(), v0.clone()
     tsp.attn_project(plan, dims, x, lw.wqkv, k1, v1, q1)
     tsp.attn_project_arrival(plan, dims, 0, x, lw.wqkv, k2, v2, q2, arr)
     assert torch.equal(q1, q2) and torch.equal(k1, k2) and torch.equal(v1, v2)
-    say("arrival 7B S=16384 D=8 out")
+    say(f"arrival 7B S={S} D=8 out")
     o1, o2 = bf16_nan((n, h), DEV), bf16_nan((n, h), DEV)
     tsp.attn_out(dims, D, 0, a, lw.wo, x, o1, attn_lo=lo)
     tsp.attn_out_arrival(dims, D, 0, a, lw.wo, x, o2, arr, attn_lo=lo)
     assert torch.equal(o1, o2)
-    say("arrival 7B S=16384 D=8 mlp")
+    say(f"arrival 7B S={S} D=8 mlp")
     ws = tsp.alloc_workspace(n, dims, D, tsp.WS_MLP, device=DEV)
     y1, y2 = bf16_nan((n, h), DEV), bf16_nan((n, h), DEV)
     tsp.mlp_forward(dims, D, 0, x, lw.w1, lw.w2, x, y1, ws)

@@ -5,7 +5,9 @@ for bit, starting from outputs filled with NaN.
 
   * a whole layer (tsp_layer_forward) at S = 2048, D = 4;
   * the backward of attention (with its forward keeping the normaliser), of
-    the O and QKV projections and of the MLP, captured together.
+    the O and QKV projections and of the MLP, captured together;
+  * the QKV, O and MLP calls that wait for their shards on a device counter
+    (every shard arrived), captured together.
 """
 import torch
 
@@ -116,3 +118,50 @@ def test_backward_graph():
     with torch.cuda.graph(g):
         run(cap)
     _replay_and_compare(g, flat(cap), flat(eager), "backward")
+
+
+def test_arrival_calls_graph():
+    """The calls that wait for their shards on a device counter, captured with
+    the counter showing every shard arrived: each replay equals the eager
+    all-shard calls."""
+    require_gpu()
+    S, D, r, h, H, hd, F = 2048, 4, 1, 256, 4, 64, 1024
+    plan, _, _ = tsp.zigzag_plan(S, D, r)
+    n = plan.n_local
+    Hs, Fs = H // D, F // D
+    dims = tsp.make_dims(h, H, hd, F)
+    x, a = _rnd((n, h), 51), _rnd((n, h), 52)
+    lo = (_rnd((n, h), 53) * 2 ** -9).to(torch.bfloat16)
+    wqkv = [_rnd((3 * Hs * hd, h), 60 + d, 0.05) for d in range(D)]
+    wo = [_rnd((h, Hs * hd), 70 + d, 0.05) for d in range(D)]
+    w1 = [_rnd((Fs, h), 80 + d, 0.05) for d in range(D)]
+    w2 = [_rnd((h, Fs), 90 + d, 0.05) for d in range(D)]
+    kf0, vf0 = _rnd((S, h), 54), _rnd((S, h), 55)
+    ws = tsp.alloc_workspace(n, dims, D, tsp.WS_MLP)
+    counter = torch.full((4,), D, dtype=torch.int32, device=DEV)
+    status = torch.zeros(4, dtype=torch.int32, device=DEV)
+    arr = tsp.make_arrival(counter, 0, status)
+
+    def eager_refs():
+        q, k, v = bf16_nan((n, h), DEV), kf0.clone(), vf0.clone()
+        tsp.attn_project(plan, dims, x, wqkv, k, v, q)
+        o, y = bf16_nan((n, h), DEV), bf16_nan((n, h), DEV)
+        tsp.attn_out(dims, D, r, a, wo, x, o, attn_lo=lo)
+        tsp.mlp_forward(dims, D, r, x, w1, w2, x, y, ws)
+        return [q, k, v, o, y]
+
+    say("graph: eager all-shard calls")
+    refs = eager_refs()
+    torch.cuda.synchronize()
+    q, k, v = bf16_nan((n, h), DEV), kf0.clone(), vf0.clone()
+    o, y = bf16_nan((n, h), DEV), bf16_nan((n, h), DEV)
+    g = torch.cuda.CUDAGraph()
+    say("graph: capture arrival calls")
+    with torch.cuda.graph(g):
+        tsp.attn_project_arrival(plan, dims, r, x, wqkv, k, v, q, arr)
+        tsp.attn_out_arrival(dims, D, r, a, wo, x, o, arr, attn_lo=lo)
+        tsp.mlp_forward_arrival(dims, D, r, x, w1, w2, x, y, ws, arr)
+    # k and v keep their other rows between replays: refill only q, o, y
+    _replay_and_compare(g, [q, o, y], [refs[0], refs[3], refs[4]], "arrival calls")
+    assert torch.equal(k, refs[1]) and torch.equal(v, refs[2])
+    assert int(status[0]) == 0
