@@ -138,6 +138,18 @@ def row_timings(plan, dims, D, layer0, x0, q, a, a_lo, out, ws_core, fl, dev, re
         ("A5 streamed: D x tsp_attn_out_shard", "oproj", out_streamed),
         ("A6+A7 streamed: D x tsp_mlp_shard", "mlp", mlp_streamed),
     ]
+    # the other two 7B configurations at their own parameters: the MLP ring
+    # from shard 3 (config 2) and the attention half at rank 3, whose chunks
+    # are 3 and 12 (config 3: QKV projection, attention, O projection)
+    plan3, _, _ = tsp.zigzag_plan(plan.seq_len, D, 3)
+    ws_attn3 = tsp.alloc_workspace(n, dims, D, tsp.WS_ATTN, device=dev)
+    fl = dict(fl, cfg3=fl["qkv"] + fl["attn"] + fl["oproj"])
+    calls += [
+        ("config 2: MLP ring from shard 3, 16384 tokens (tsp_mlp_forward)", "mlp",
+         lambda: tsp.mlp_forward(dims, D, 3, x0, lw.w1, lw.w2, x0, out, ws_mlp)),
+        ("config 3: attention half at rank 3 (tsp_attn_forward: QKV, attention, O)", "cfg3",
+         lambda: tsp.attn_forward(plan3, dims, x0, lw.wqkv, lw.wo, kf, vf, x0, out, ws_attn3)),
+    ]
     # the all-shard calls that wait for each shard inside the kernels, with
     # every shard already arrived (the counter preset): the cost of streaming
     # when the next shards are prefetched while the current ones compute
@@ -249,6 +261,7 @@ def row_timings(plan, dims, D, layer0, x0, q, a, a_lo, out, ws_core, fl, dev, re
     torch.cuda.synchronize()
     if int(status[0]) != 0:
         raise RuntimeError("an arrival wait gave up with every shard arrived")
+    del ws_attn3
     del ws_mlp, ws_mlp_s, ws_out_s, k8, v8, ws_bwd, dw1, dw2, dy, dx, ws_abwd, dq_b, dk_b, dv_b, lse, d_attn
     del dwo_b, dwqkv_b, d_attn_b, dx_b, ws_obwd, ws_pbwd, lse8, dk8, dv8, dgain, dq_rope, dk_rope, ws_rms
     return rows
