@@ -277,7 +277,13 @@ __global__ __launch_bounds__((Cfg<BM, BN>::NT)) void gemm_kernel(const GemmArgs 
   // Called by all waves alike: wave 0 polls until position `pos` has arrived
   // (or the poll budget is spent), then the count seen is passed to every
   // wave through LDS between two barriers, so all waves take the same
-  // branches afterwards.
+  // branches afterwards.  The poll is a system-scope load (past both cache
+  // levels) and no acquire fence follows it: the shard's loads are issued
+  // only after the poll's value has returned and the barriers have passed,
+  // and no cache level can hold a stale line of the shard, since nothing in
+  // this launch reads a shard before its arrival and the launch itself
+  // starts with both levels invalidated (an agent-scope acquire here would
+  // invalidate the L2 for every other tile of the XCD).
   auto await_arrival = [&](int32_t pos) __attribute__((always_inline)) -> int32_t {
     if (wave == 0) {
       typedef __attribute__((address_space(1))) uint32_t gu32;  // global, not flat: vm counter only
