@@ -280,10 +280,11 @@ __global__ __launch_bounds__((Cfg<BM, BN>::NT)) void gemm_kernel(const GemmArgs 
   // branches afterwards.  The poll is a system-scope load (past both cache
   // levels) and no acquire fence follows it: the shard's loads are issued
   // only after the poll's value has returned and the barriers have passed,
-  // and no cache level can hold a stale line of the shard, since nothing in
-  // this launch reads a shard before its arrival and the launch itself
-  // starts with both levels invalidated (an agent-scope acquire here would
-  // invalidate the L2 for every other tile of the XCD).
+  // and nothing in this launch reads a shard before its arrival, so no line
+  // of it is cached by this launch; lines left by earlier kernels (the
+  // tests fill the shard buffers with NaN first) read fresh after arrival.
+  // An agent-scope acquire here would invalidate the L2 under every other
+  // tile of the XCD.
   auto await_arrival = [&](int32_t pos) __attribute__((always_inline)) -> int32_t {
     if (wave == 0) {
       typedef __attribute__((address_space(1))) uint32_t gu32;  // global, not flat: vm counter only
