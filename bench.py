@@ -101,28 +101,23 @@ def layer_bytes(plan, d):
     return (4 * h * h + 2 * h * F) * 2 + 2 * kv_rows * h * 2 + 2 * plan.n_local * h * 2
 
 
-def arrival_overlap(plan, dims, D, layer0, a, a_lo, x0, out, dev, reps=3):
-    """The O projection of layer 0 with its D weight shards delivered while it
-    runs, by the one-workgroup simulated producer (tsp_simulate_arrival) into
-    separate buffers, one shard every 90 us (about the producer's own copy
-    time per 4.2 MB shard, 47 GB/s).
+def arrival_overlap(plan, dims, D, layer0, x0, q, a, a_lo, out, dev, reps=3):
+    """Layer 0's QKV and O projections with their D weight shards delivered
+    while they run, by the one-workgroup simulated producer
+    (tsp_simulate_arrival) into separate buffers, one shard every `interval`
+    (about the producer's own copy time per shard, 47 GB/s).
 
-    The call's 1024 waiting workgroups would hold every CU, so the producer is
+    A call's waiting workgroups would hold every CU, so the producer is
     launched first on a side stream and given a 1 ms host pause to become
     resident before the call is launched.  So that the shards still arrive
     during the call, the producer first delivers k 16-byte dummies (k = the
-    shard interval's multiples in 1 ms), which raise the counter too: the
-    call's arrival base is k.  The waits are bounded and the status word is
+    interval's multiples in 1 ms), which raise the counter too: the call's
+    arrival base is k.  The waits are bounded and the status word is
     reported.  Times (ms, events on the call's stream around it): the call
     with every shard arrived; delivery then call on one stream; the call with
     its shards arriving (from the call's launch)."""
-    lw = layer0[0]
+    lw, kf, vf = layer0
     ring = [(plan.rank + k) % D for k in range(D)]
-    src = [lw.wo[d] for d in ring]
-    dst = [torch.empty_like(t) for t in src]
-    wo_arr = [None] * D
-    for p, d in enumerate(ring):
-        wo_arr[d] = dst[p]
     counter = torch.zeros(4, dtype=torch.int32, device=dev)
     status = torch.zeros(4, dtype=torch.int32, device=dev)
     dummy_src = torch.zeros(16, dtype=torch.uint8, device=dev)
@@ -131,49 +126,61 @@ def arrival_overlap(plan, dims, D, layer0, a, a_lo, x0, out, dev, reps=3):
     side = torch.cuda.Stream()
     ev = lambda: torch.cuda.Event(enable_timing=True)
 
-    def call(base):
-        tsp.attn_out_arrival(dims, D, plan.rank, a, wo_arr, x0, out,
-                             tsp.make_arrival(counter, base, status, spin_limit=1 << 15), attn_lo=a_lo)
-
-    for d_, s_ in zip(dst, src):
-        d_.copy_(s_)
-    counter.fill_(D)
-    call(0)
-    torch.cuda.synchronize()
-    e0, e1 = ev(), ev()
-    e0.record(main)
-    for _ in range(reps):
+    def measure(shards, run_call):
+        src = [shards[d] for d in ring]
+        dst = [torch.empty_like(t) for t in src]
+        w_arr = [None] * D
+        for p, d in enumerate(ring):
+            w_arr[d] = dst[p]
+        call = lambda base: run_call(w_arr, tsp.make_arrival(counter, base, status, spin_limit=1 << 15))
+        for d_, s_ in zip(dst, src):
+            d_.copy_(s_)
+        counter.fill_(D)
         call(0)
-    e1.record(main)
-    torch.cuda.synchronize()
-    call_ms = e0.elapsed_time(e1) / reps
-    delay_us = 90  # about the one-workgroup producer's own copy time for a 4.2 MB shard
-    k = min(64 - D, -(-1000 // delay_us))
-    res = {"call_all_arrived_ms": round(call_ms, 4), "shard_interval_us": delay_us}
-    for kind in ("deliver_then_call", "arriving_during_call"):
-        times = []
+        torch.cuda.synchronize()
+        e0, e1 = ev(), ev()
+        e0.record(main)
         for _ in range(reps):
-            counter.zero_()
-            torch.cuda.synchronize()
-            e0, e1 = ev(), ev()
-            if kind == "deliver_then_call":
-                e0.record(main)
-                tsp.simulate_arrival(src, dst, counter, 0, delay_us, stream=main)
-                call(0)
-            else:
-                side.wait_stream(main)
-                tsp.simulate_arrival([dummy_src] * k + src, [dummy_dst[i] for i in range(k)] + dst, counter, 0,
-                                     delay_us, stream=side)
-                time.sleep(0.001)
-                e0.record(main)
-                call(k)
-                main.wait_stream(side)
-            e1.record(main)
-            torch.cuda.synchronize()
-            times.append(e0.elapsed_time(e1))
-        res[kind + "_ms"] = round(sum(times) / reps, 4)
+            call(0)
+        e1.record(main)
+        torch.cuda.synchronize()
+        call_ms = e0.elapsed_time(e1) / reps
+        shard_mb = src[0].numel() * src[0].element_size() / 1e6
+        interval_us = int(shard_mb / 47e3 * 1e6) + 1  # MB / (47 GB/s) in microseconds
+        k = min(64 - D, -(-1000 // interval_us))
+        res = {"call_all_arrived_ms": round(call_ms, 4), "shard_interval_us": interval_us,
+               "shards": f"{D} shards of {shard_mb:.1f} MB"}
+        for kind in ("deliver_then_call", "arriving_during_call"):
+            times = []
+            for _ in range(reps):
+                counter.zero_()
+                torch.cuda.synchronize()
+                e0, e1 = ev(), ev()
+                if kind == "deliver_then_call":
+                    e0.record(main)
+                    tsp.simulate_arrival(src, dst, counter, 0, interval_us, stream=main)
+                    call(0)
+                else:
+                    side.wait_stream(main)
+                    tsp.simulate_arrival([dummy_src] * k + src, [dummy_dst[i] for i in range(k)] + dst, counter,
+                                         0, interval_us, stream=side)
+                    time.sleep(0.001)
+                    e0.record(main)
+                    call(k)
+                    main.wait_stream(side)
+                e1.record(main)
+                torch.cuda.synchronize()
+                times.append(e0.elapsed_time(e1))
+            res[kind + "_ms"] = round(sum(times) / reps, 4)
+        return res
+
+    res = {
+        "qkv (N-sharded)": measure(lw.wqkv, lambda w, arr: tsp.attn_project_arrival(
+            plan, dims, plan.rank, x0, w, kf, vf, q, arr)),
+        "oproj (K-sharded)": measure(lw.wo, lambda w, arr: tsp.attn_out_arrival(
+            dims, D, plan.rank, a, w, x0, out, arr, attn_lo=a_lo)),
+    }
     res["status"] = int(status[0])
-    res["shards"] = f"{D} W_o shards of {src[0].numel() * 2 / 1e6:.1f} MB"
     return res
 
 
@@ -687,8 +694,9 @@ def main():
                                             fl_rows, dev)
     if args.arrival_overlap:
         print("[bench] arrival overlap on layer 0's O projection", file=sys.stderr, flush=True)
-        result["arrival_overlap_layer0"] = arrival_overlap(plan, dims, D, main_stack.layers[0], main_stack.a,
-                                                           main_stack.a_lo, main_stack.x0, main_stack.bufs[0], dev)
+        result["arrival_overlap_layer0"] = arrival_overlap(plan, dims, D, main_stack.layers[0], main_stack.x0,
+                                                           main_stack.q, main_stack.a, main_stack.a_lo,
+                                                           main_stack.bufs[0], dev)
     if not args.no_cpu_baseline:
         print("[bench] cpu baseline (fp64 oracle, bounded sample)", file=sys.stderr, flush=True)
         result["cpu_baseline"] = cpu_baseline(W, plan, main_stack.x0, main_stack.layers[0])

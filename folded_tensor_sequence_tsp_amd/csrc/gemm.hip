@@ -225,8 +225,12 @@ __global__ __launch_bounds__((Cfg<BM, BN>::NT)) void gemm_kernel(const GemmArgs 
   const int in_group = pid % group_size;
   const int tm = first_m + in_group % gm;
   const int tn = in_group / gm;
-  const int nshard = tn / tiles_n_shard;
-  const int n0 = (tn - nshard * tiles_n_shard) * BN;
+  // column block in the raster order; with an arrival counter the N-sharded
+  // blocks are taken in ring order from ring_start, so that each XCD's first
+  // rounds of tiles need only the first shards to arrive
+  const int nblock = tn / tiles_n_shard;
+  const int nshard = g.arrived && g.k_shards == 1 ? (nblock + g.ring_start) % g.n_shards : nblock;
+  const int n0 = (tn - nblock * tiles_n_shard) * BN;
   const int m0 = tm * BM;
 
   const int kt_per_shard = g.K_s / BK;
