@@ -44,16 +44,16 @@ __device__ __forceinline__ uint32_t pack_f16x2_sat(float a, float b) {
 
 __device__ __forceinline__ float bf16_to_f32(uint16_t b) { return __uint_as_float((uint32_t)b << 16); }
 
-// GELU, tanh form: 0.5 u (1 + tanh(sqrt(2/pi) (u + 0.044715 u^3))), with
-// tanh(z) = 1 - 2 / (exp(2z) + 1) and exp(2z) = 2^(2z log2 e) on the hardware
-// exp2.  Saturates correctly: exp2 -> inf gives tanh = 1, exp2 -> 0 gives -1.
+// GELU, tanh form: 0.5 u (1 + tanh(z)) with z = sqrt(2/pi) (u + 0.044715 u^3).
+// With r = 1 / (1 + exp(2z)), 1 + tanh(z) = 2 (1 - r), so GELU(u) = u - u r,
+// one fma; exp(2z) = 2^(u (k1 + k2 u^2)) on the hardware exp2, with
+// k1 = 2 log2(e) sqrt(2/pi) and k2 = 0.044715 k1.  Saturates for finite u:
+// exp2 -> inf gives r = 0 (GELU = u), exp2 -> 0 gives r = 1 (GELU = 0).
 __device__ __forceinline__ float gelu_tanh(float u) {
-  const float sqrt_2_over_pi = 0.79788456080286535588f;
-  const float two_log2e = 2.88539008177792681472f;
-  float z = sqrt_2_over_pi * (u + 0.044715f * u * u * u);
-  float e = __builtin_amdgcn_exp2f(two_log2e * z);
-  float t = 1.0f - 2.0f * __builtin_amdgcn_rcpf(e + 1.0f);
-  return 0.5f * u * (1.0f + t);
+  const float k1 = 2.30220819814432488913f, k2 = 0.10294323958002348742f;
+  const float e = __builtin_amdgcn_exp2f(u * __builtin_fmaf(k2, u * u, k1));
+  const float r = __builtin_amdgcn_rcpf(e + 1.0f);
+  return __builtin_fmaf(-u, r, u);
 }
 
 // Derivative of gelu_tanh: 0.5 (1 + t) + 0.5 u (1 - t^2) c (1 + 3 a u^2) with
@@ -117,11 +117,12 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t buffer_rsrc(const void* base, 
 }
 
 // Direct buffer->LDS load of 16 bytes per lane (buffer_load_dwordx4 ... lds):
-// lane L reads rsrc + voffset and writes its 16 bytes at lds_block + 16 * L;
-// lds_block is wave-uniform.
-__device__ __forceinline__ void dma16_buf(__amdgpu_buffer_rsrc_t rsrc, uint32_t voffset, void* lds_block) {
-  __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (__attribute__((address_space(3))) void*)lds_block, 16, voffset, 0,
-                                           0, 0);
+// lane L reads rsrc + voffset + soffset (soffset wave-uniform, in an SGPR) and
+// writes its 16 bytes at lds_block + 16 * L; lds_block is wave-uniform.
+__device__ __forceinline__ void dma16_buf(__amdgpu_buffer_rsrc_t rsrc, uint32_t voffset, void* lds_block,
+                                          uint32_t soffset = 0) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (__attribute__((address_space(3))) void*)lds_block, 16, voffset,
+                                           soffset, 0, 0);
 }
 
 // Transposing LDS read of four 16-bit values per lane (ds_read_b64_tr_b16,

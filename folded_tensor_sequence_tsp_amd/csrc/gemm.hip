@@ -15,19 +15,19 @@
 // waves of 128 x 64, two per SIMD; 128 x 256 tiles: eight waves of 64 x 64, for
 // short token counts; 128 x 128 tiles: four waves of 64 x 64), each a grid of
 // 32 x 32 MFMA tiles.  A and B k-tiles stream into an LDS ring with direct
-// buffer->LDS loads (buffer_load_dwordx4 ... lds, no register staging; the
-// descriptors are rebased per k-tile in SGPRs), one vmcnt wait and one
-// barrier per k-tile: 256 x 256 tiles have two 64 KB stages (the other stage
-// is refilled right after the barrier, before the MFMAs), 128 x 256 three,
-// 128 x 128 four.  Shard widths that are not a multiple of 64, and the O
-// projection's two-part A, use 32-k tiles in a 4-stage (3 with two parts)
-// ring.  Buffer rather than global loads: the compiler counts a global->LDS
-// load against the LDS counter as well, so with loads always in flight every
-// fragment wait became a wait for all of them; with buffer loads the waits
-// are graduated.  LDS rows are 128 bytes (64 k values; 64 bytes for 32-k
-// tiles); the 16-byte chunk c of row r sits at c ^ ((r / 2) % 8)
-// (c ^ ((r / 4) % 4)), so the 16 lanes of one LDS cycle, reading 16
-// consecutive rows at one k offset, hit distinct banks of the 64-bank LDS.
+// buffer->LDS loads (buffer_load_dwordx4 ... lds, no register staging; one
+// descriptor pair per shard, the k-tile's column in the loads' scalar offset),
+// one vmcnt wait and one barrier per k-tile: 256 x 256 tiles have two 64 KB
+// stages (the other stage is refilled right after the barrier, before the
+// MFMAs), 128 x 256 three, 128 x 128 four.  Shard widths that are not a
+// multiple of 64, and the O projection's two-part A, use 32-k tiles in a
+// 4-stage (3 with two parts) ring.  Buffer rather than global loads: the
+// compiler counts a global->LDS load against the LDS counter as well, so with
+// loads always in flight every fragment wait became a wait for all of them;
+// with buffer loads the waits are graduated.  LDS rows are 128 bytes (64 k
+// values; 64 bytes for 32-k tiles); the 16-byte chunk c of row r sits at c ^
+// ((r / 2) % 8) (c ^ ((r / 4) % 4)), so the 16 lanes of one LDS cycle, reading
+// 16 consecutive rows at one k offset, hit distinct banks of the 64-bank LDS.
 // Workgroup ids are remapped so each XCD (ids = x mod 8) gets a contiguous run
 // of tiles, then rasterised in groups of 8 (QKV) or 4 tile rows for L2 reuse.
 // With a low part of A (the O projection contracts the attention output's two
@@ -323,12 +323,33 @@ __global__ __launch_bounds__((Cfg<BM, BN>::NT)) void gemm_kernel(const GemmArgs 
   const uint16_t* a_lo = g.A_lo + (int64_t)m0 * g.lda;
   const uint16_t* bshard = g.B[nx_d] + (int64_t)n0 * g.K_s;
   asm volatile("" ::"s"(a_hi), "s"(a_lo), "s"(bshard));  // in registers before the loop
+  // Descriptors of the current shard's K range (A at the shard's first
+  // column), rebuilt only at shard boundaries; a k-tile's column is the loads'
+  // scalar offset, the same number of bytes into A and into B.
+  __amdgpu_buffer_rsrc_t ra_hi, ra_lo, rb;
+  auto shard_rsrc = [&]() __attribute__((always_inline)) {
+    const int64_t acol = g.k_shards > 1 ? (int64_t)nx_d * g.K_s : 0;
+    ra_hi = buffer_rsrc(a_hi + acol, a_bytes);
+    ra_lo = buffer_rsrc(a_lo + acol, a_bytes);
+    rb = buffer_rsrc(bshard, b_bytes);
+  };
+  shard_rsrc();
   auto issue_tile = [&](int t) __attribute__((always_inline)) {
     if (nx_pos >= avail) avail = await_arrival(nx_pos);
-    const int64_t acol = (g.k_shards > 1 ? (int64_t)nx_d * g.K_s : 0) + nx_kt * BK;
-    const __amdgpu_buffer_rsrc_t ra = buffer_rsrc((nx_part ? a_lo : a_hi) + acol, a_bytes);
-    const __amdgpu_buffer_rsrc_t rb = buffer_rsrc(bshard + nx_kt * BK, b_bytes);
-    [[maybe_unused]] const __amdgpu_buffer_rsrc_t rl = buffer_rsrc(a_lo + acol, a_bytes);
+    const uint32_t soff = (uint32_t)nx_kt * (BK * 2);
+    const __amdgpu_buffer_rsrc_t ra = nx_part ? ra_lo : ra_hi;
+    const __amdgpu_buffer_rsrc_t rbt = rb;
+    uint8_t* stage = smem + (t % C::ST) * C::STAGE_BYTES;
+#pragma unroll
+    for (int i = 0; i < C::A_LOADS; ++i) dma16_buf(ra, a_off[i], stage + (i * C::NW + wave) * 1024, soff);
+    if constexpr (LO) {
+#pragma unroll
+      for (int i = 0; i < C::A_LOADS; ++i)
+        dma16_buf(ra_lo, a_off[i], stage + C::A_BYTES + (i * C::NW + wave) * 1024, soff);
+    }
+#pragma unroll
+    for (int i = 0; i < C::B_LOADS; ++i)
+      dma16_buf(rbt, b_off[i], stage + C::PARTS * C::A_BYTES + (i * C::NW + wave) * 1024, soff);
     if (++nx_kt == kt_per_shard) {
       nx_kt = 0;
       if (++nx_part == reps) {
@@ -338,19 +359,10 @@ __global__ __launch_bounds__((Cfg<BM, BN>::NT)) void gemm_kernel(const GemmArgs 
           ++nx_pos;
           bshard = g.B[nx_d] + (int64_t)n0 * g.K_s;
           __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0)
+          shard_rsrc();
         }
       }
     }
-    uint8_t* stage = smem + (t % C::ST) * C::STAGE_BYTES;
-#pragma unroll
-    for (int i = 0; i < C::A_LOADS; ++i) dma16_buf(ra, a_off[i], stage + (i * C::NW + wave) * 1024);
-    if constexpr (LO) {
-#pragma unroll
-      for (int i = 0; i < C::A_LOADS; ++i) dma16_buf(rl, a_off[i], stage + C::A_BYTES + (i * C::NW + wave) * 1024);
-    }
-#pragma unroll
-    for (int i = 0; i < C::B_LOADS; ++i)
-      dma16_buf(rb, b_off[i], stage + C::PARTS * C::A_BYTES + (i * C::NW + wave) * 1024);
   };
 
   f32x16 acc[C::FM][C::FN];
