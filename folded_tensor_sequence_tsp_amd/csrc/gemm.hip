@@ -12,14 +12,16 @@
 //     in for tensor parallelism's all-reduce.
 //
 // Tiling: BM x BN x 64 block tile; waves of WM x WN (256 x 256 tiles: eight
-// waves of 128 x 64, two per SIMD; 128 x 256 tiles: eight waves of 64 x 64, for
-// short token counts; 128 x 128 tiles: four waves of 64 x 64), each a grid of
+// waves of 128 x 64, two per SIMD; 256 x 192 tiles, for QKV shards whose
+// width is a multiple of 192 when they fill the rounds of tiles better:
+// eight waves of 64 x 96; 128 x 256 tiles: eight waves of 64 x 64, for short
+// token counts; 128 x 128 tiles: four waves of 64 x 64), each a grid of
 // 32 x 32 MFMA tiles.  A and B k-tiles stream into an LDS ring with direct
 // buffer->LDS loads (buffer_load_dwordx4 ... lds, no register staging; one
 // descriptor pair per shard, the k-tile's column in the loads' scalar offset),
 // one vmcnt wait and one barrier per k-tile: 256 x 256 tiles have two 64 KB
 // stages (the other stage is refilled right after the barrier, before the
-// MFMAs), 128 x 256 three, 128 x 128 four.  Shard widths that are not a
+// MFMAs), 256 x 192 two of 56 KB, 128 x 256 three, 128 x 128 four.  Shard widths that are not a
 // multiple of 64, and the O projection's two-part A, use 32-k tiles in a
 // 4-stage (3 with two parts) ring.  Buffer rather than global loads: the
 // compiler counts a global->LDS load against the LDS counter as well, so with
@@ -54,8 +56,9 @@ struct Cfg {
   static constexpr int BK = K64 ? 64 : 32;  // k per tile
   static constexpr int ROWB = BK * 2;       // bytes per LDS row
   static constexpr int CPR = BK / 8;        // 16-byte chunks per row
-  static constexpr int WM = BM == 256 ? 128 : 64;  // wave tile
-  static constexpr int WN = 64;
+  // wave tile: 128 x 64 (256 x 256), 64 x 96 (256 x 192), else 64 x 64
+  static constexpr int WM = BM == 256 && BN == 256 ? 128 : 64;
+  static constexpr int WN = BN == 192 ? 96 : 64;
   static constexpr int WAVES_M = BM / WM, WAVES_N = BN / WN;
   static constexpr int NW = WAVES_M * WAVES_N;
   static constexpr int NT = 64 * NW;
@@ -65,7 +68,7 @@ struct Cfg {
   static constexpr int STAGE_BYTES = PARTS * A_BYTES + B_BYTES;
   static constexpr int A_LOADS = A_BYTES / (NT * 16), B_LOADS = B_BYTES / (NT * 16);  // per thread per k-tile
   static constexpr int LOADS = PARTS * A_LOADS + B_LOADS;
-  static constexpr int ST = LO ? 3 : !K64 ? STAGES : (BM == 256 && BN == 256) ? 2 : (BM * BN > 128 * 128) ? 3 : 4;
+  static constexpr int ST = LO ? 3 : !K64 ? STAGES : (BM == 256 && BN >= 192) ? 2 : (BM * BN > 128 * 128) ? 3 : 4;
   static_assert(!(LO && K64), "the low part of A uses 32-k tiles");
   static constexpr int LDS_BYTES = ST * STAGE_BYTES;
   static_assert(A_LOADS >= 1 && B_LOADS >= 1 && A_BYTES % (NT * 16) == 0 && B_BYTES % (NT * 16) == 0, "tile split");
@@ -197,7 +200,7 @@ __device__ __forceinline__ void store_row8(const GemmArgs& g, int nshard, int ro
 }
 
 template <int BM, int BN, int EPI, bool F16, bool LO = false, bool K64 = false>
-__global__ __launch_bounds__((Cfg<BM, BN>::NT)) void gemm_kernel(const GemmArgs g) {
+__global__ __launch_bounds__((Cfg<BM, BN, LO, K64>::NT)) void gemm_kernel(const GemmArgs g) {
   using C = Cfg<BM, BN, LO, K64>;
   constexpr int BK = C::BK;
   // the LDS ring, then one word for the shard-arrival broadcast (a second
@@ -539,6 +542,26 @@ hipError_t launch_tiles(const GemmArgs& g, hipStream_t stream) {
   return launch_tiles_k<BM, BN, false>(g, stream);
 }
 
+// The QKV projection on 256 x 192 tiles of 64-k (eight waves of 64 x 96), for
+// shard widths that are multiples of 192.
+hipError_t launch_qkv192(const GemmArgs& g, hipStream_t stream) {
+  const dim3 grid(((g.M + 255) / 256) * (g.N_s / 192) * g.n_shards), block(Cfg<256, 192, false, true>::NT);
+  hipLaunchKernelGGL((gemm_kernel<256, 192, EPI_QKV, false, false, true>), grid, block, 0, stream, g);
+  return hipGetLastError();
+}
+
+int cu_count() {
+  static int n = 0;
+  if (n == 0) {
+    int dev = 0, v = 0;
+    if (hipGetDevice(&dev) == hipSuccess && hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess && v > 0)
+      n = v;
+    else
+      n = 256;
+  }
+  return n;
+}
+
 }  // namespace
 
 hipError_t launch_gemm(const GemmArgs& g, hipStream_t stream) {
@@ -548,7 +571,20 @@ hipError_t launch_gemm(const GemmArgs& g, hipStream_t stream) {
   // 256 x 256 tiles keep the LDS traffic per MFMA low; fall back to 128 x 128
   // when the big tiles would leave most of the 256 CUs idle.
   const long big = (long)((g.M + 255) / 256) * (((g.N_s + 255) / 256) * g.n_shards);
-  if (big >= 192) return launch_tiles<256, 256>(g, stream);
+  if (big >= 192) {
+    // The QKV projection's shards are multiples of 192 wide: 256 x 192 tiles
+    // (0.75 of the work of a 256 x 256 one, counted as 0.79 for their lower
+    // operand reuse) when they fill the rounds of tiles on the CUs better,
+    // e.g. 2048 tokens: 384 tiles of 256 x 256 (1.5 rounds) or 512 of
+    // 256 x 192 (2 rounds).
+    if (g.epilogue == EPI_QKV && g.N_s % 192 == 0 && GEMM_K64 && g.K_s % 64 == 0 && !g.A_lo) {
+      const long cu = cu_count();
+      const long mid = (long)((g.M + 255) / 256) * ((g.N_s / 192) * g.n_shards);
+      const double r256 = (double)((big + cu - 1) / cu), r192 = 0.7875 * (double)((mid + cu - 1) / cu);
+      if (r192 < r256) return launch_qkv192(g, stream);
+    }
+    return launch_tiles<256, 256>(g, stream);
+  }
   // short token counts: 128 x 256 tiles (eight waves, 1.33x the bytes per flop
   // of 256 x 256) while they still fill the CUs, then 128 x 128
   const long mid = (long)((g.M + 127) / 128) * (((g.N_s + 255) / 256) * g.n_shards);

@@ -43,6 +43,7 @@ PROJECT_CASES = [
     (256, 4, 64, 2, 800, 1),      # C = 200: ragged token tiles
     (512, 4, 128, 2, 1288, 0),    # hd = 128, C = 322
     (256, 4, 64, 1, 300, 0),      # D = 1
+    (512, 8, 64, 8, 48000, 3),    # 192-wide shards, 6000 tokens (ragged): 256 x 192 tiles
 ]
 
 
