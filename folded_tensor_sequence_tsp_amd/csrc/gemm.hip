@@ -550,14 +550,14 @@ hipError_t launch_qkv192(const GemmArgs& g, hipStream_t stream) {
   return hipGetLastError();
 }
 
+// Compute units of the current device (queried once; 256 if the query fails).
 int cu_count() {
   static int n = 0;
   if (n == 0) {
     int dev = 0, v = 0;
-    if (hipGetDevice(&dev) == hipSuccess && hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess && v > 0)
-      n = v;
-    else
-      n = 256;
+    const bool ok = hipGetDevice(&dev) == hipSuccess &&
+                    hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess;
+    n = ok && v > 0 ? v : 256;
   }
   return n;
 }
@@ -579,8 +579,8 @@ hipError_t launch_gemm(const GemmArgs& g, hipStream_t stream) {
     // 256 x 192 (2 rounds).
     if (g.epilogue == EPI_QKV && g.N_s % 192 == 0 && GEMM_K64 && g.K_s % 64 == 0 && !g.A_lo) {
       const long cu = cu_count();
-      const long mid = (long)((g.M + 255) / 256) * ((g.N_s / 192) * g.n_shards);
-      const double r256 = (double)((big + cu - 1) / cu), r192 = 0.7875 * (double)((mid + cu - 1) / cu);
+      const long t192 = (long)((g.M + 255) / 256) * ((g.N_s / 192) * g.n_shards);
+      const double r256 = (double)((big + cu - 1) / cu), r192 = 0.7875 * (double)((t192 + cu - 1) / cu);
       if (r192 < r256) return launch_qkv192(g, stream);
     }
     return launch_tiles<256, 256>(g, stream);
