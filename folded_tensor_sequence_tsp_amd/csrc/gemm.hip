@@ -573,14 +573,14 @@ hipError_t launch_gemm(const GemmArgs& g, hipStream_t stream) {
   const long big = (long)((g.M + 255) / 256) * (((g.N_s + 255) / 256) * g.n_shards);
   if (big >= 192) {
     // The QKV projection's shards are multiples of 192 wide: 256 x 192 tiles
-    // (0.75 of the work of a 256 x 256 one, counted as 0.79 for their lower
-    // operand reuse) when they fill the rounds of tiles on the CUs better,
-    // e.g. 2048 tokens: 384 tiles of 256 x 256 (1.5 rounds) or 512 of
-    // 256 x 192 (2 rounds).
+    // when they fill the rounds of tiles on the CUs better.  A round of them
+    // takes about 0.9 of a round of 256 x 256 tiles (measured at 2048 tokens,
+    // for 0.75 of the work: lower operand reuse), e.g. 2048 tokens: 384 tiles
+    // of 256 x 256 (1.5 rounds, so 2) or 512 of 256 x 192 (2 rounds, 1.8).
     if (g.epilogue == EPI_QKV && g.N_s % 192 == 0 && GEMM_K64 && g.K_s % 64 == 0 && !g.A_lo) {
       const long cu = cu_count();
       const long t192 = (long)((g.M + 255) / 256) * ((g.N_s / 192) * g.n_shards);
-      const double r256 = (double)((big + cu - 1) / cu), r192 = 0.7875 * (double)((t192 + cu - 1) / cu);
+      const double r256 = (double)((big + cu - 1) / cu), r192 = 0.9 * (double)((t192 + cu - 1) / cu);
       if (r192 < r256) return launch_qkv192(g, stream);
     }
     return launch_tiles<256, 256>(g, stream);
