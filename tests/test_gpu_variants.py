@@ -94,6 +94,35 @@ def test_gqa_with_all_heads_is_mha():
     assert torch.equal(oa, ob)
 
 
+def test_gqa_project_wide_tiles():
+    """The GQA projection at a size that takes the 256 x 192 tiles: shards of
+    (4 + 2*1) heads of 64 = 384 columns, 6000 local tokens (a ragged last tile
+    row), against the oracle's projection (bf16 tensors)."""
+    require_gpu()
+    S, D, r, H, Hkv, hd = 24000, 4, 1, 16, 4, 64
+    h = H * hd
+    plan, l2g, _ = tsp.zigzag_plan(S, D, r)
+    n = plan.n_local
+    Hs, Ks = H // D, Hkv // D
+    dims = tsp.make_dims(h, H, hd, 4 * h)
+    x = _rnd((n, h), 12)
+    w = [_rnd(((Hs + 2 * Ks) * hd, h), 40 + d, 0.02) for d in range(D)]
+    k0, v0 = _rnd((S, Hkv * hd), 13), _rnd((S, Hkv * hd), 14)
+    q_ref, k_ref, v_ref = (O.proj_rows(t) for t in O.qkv_projection_gqa(x, w, hd, Hs, Ks))
+    kd, vd = _bf16(k0).to(DEV), _bf16(v0).to(DEV)
+    q = bf16_nan((n, h), DEV)
+    say(f"gqa projection, wide tiles: S={S} D={D} H={H} Hkv={Hkv} hd={hd} n={n}")
+    tsp.attn_project_gqa(plan, dims, Hkv, x.to(DEV), [t.to(DEV) for t in w], kd, vd, q)
+    torch.cuda.synchronize()
+    check(q, q_ref, "gqa q")
+    check(kd[l2g.to(DEV)], k_ref, "gqa own k rows")
+    check(vd[l2g.to(DEV)], v_ref, "gqa own v rows")
+    others = torch.ones(S, dtype=torch.bool)
+    others[l2g] = False
+    assert torch.equal(kd.cpu()[others], _bf16(k0)[others]), "rows of other ranks must be untouched"
+    assert torch.equal(vd.cpu()[others], _bf16(v0)[others])
+
+
 @pytest.mark.parametrize("S,D,r,H,Hkv,hd", [(2048, 4, 1, 8, 4, 64), (2048, 2, 0, 8, 2, 64),
                                              (1288, 2, 1, 4, 2, 128), (640, 1, 0, 4, 1, 64)])
 def test_gqa_project_rope_attention(S, D, r, H, Hkv, hd):
