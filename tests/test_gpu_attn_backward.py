@@ -67,11 +67,11 @@ def _check(got, ref, bound, name):
         f"{st['derived_only']}/{st['n']} admitted by the derived bound only")
 
 
-def _run(S, D, r, H, hd, with_lo, seed):
+def _run(S, D, r, H, hd, with_lo, seed, qk_scale=1.0):
     plan, l2g, _ = tsp.zigzag_plan(S, D, r)
     n, h = plan.n_local, H * hd
     dims = tsp.make_dims(h, H, hd, 4 * h)
-    q, k, v = _rnd((n, h), seed), _rnd((S, h), seed + 1), _rnd((S, h), seed + 2)
+    q, k, v = _rnd((n, h), seed, qk_scale), _rnd((S, h), seed + 1, qk_scale), _rnd((S, h), seed + 2)
     do = _rnd((n, h), seed + 3)
     qd, kd, vd, dod = (t.to(DEV) for t in (q, k, v, do))
     out = bf16_nan((n, h), DEV)
@@ -118,6 +118,26 @@ def test_attn_backward(S, D, r, H, hd, with_lo):
     last = int(l2g.max()) + 1
     if last < S:
         assert torch.count_nonzero(dk[last:]).item() == 0 and torch.count_nonzero(dv[last:]).item() == 0
+
+
+@pytest.mark.parametrize("k", [2, 4])
+@pytest.mark.parametrize("S,D,r,H,hd", [(2048, 4, 1, 4, 64), (2048, 2, 0, 2, 128)])
+def test_attn_backward_scaled(S, D, r, H, hd, k):
+    """q and K at 2.5^k times unit scale, as a chained stack without a norm
+    gives them at layer k: scores 2.5^(2k) times the unit ones (39x at k = 2,
+    1526x at k = 4), softmax rows near one-hot.  P is recomputed against the
+    forward's fp32 normaliser (natural log), which carries about 2^-24 of the
+    row's largest score as an error in the exponent: below a bf16 rounding of
+    P up to k = 4; at k = 6 (scores near 10^5) it reaches about 1 % of P."""
+    require_gpu()
+    s = 2.5 ** k
+    plan, l2g, (q, kk, v, do), (_, _, dq, dk, dv) = _run(S, D, r, H, hd, True, 40, qk_scale=s)
+    qf, kf, vf, dof = (O.f64(t) for t in (q, kk, v, do))
+    rq, rk, rv = O.causal_attention_backward(qf, l2g, kf, vf, dof, H, hd)
+    bq, bk, bv = _bounds(qf, kf, vf, dof, l2g, H, hd, True)
+    _check(dq, rq, bq, f"dq (q, K x 2.5^{k})")
+    _check(dk, rk, bk, f"dk (q, K x 2.5^{k})")
+    _check(dv, rv, bv, f"dv (q, K x 2.5^{k})")
 
 
 def test_attn_backward_7b_sampled():
