@@ -39,11 +39,23 @@ def check_rounded_product(got, ref, a_abs, b_abs, name):
                                      (256, 512, 1, 100), (1024, 4096, 4, 2048)])
 @pytest.mark.parametrize("residual", [False, True])
 def test_mlp_backward(h, F, D, n, residual):
+    _mlp_backward_case(h, F, D, n, residual, 1.0)
+
+
+@pytest.mark.parametrize("k", [2, 6, 12])
+def test_mlp_backward_scaled(k):
+    """x at 2.5^k times unit scale (layer k of a chained stack without a norm):
+    U = x W1 far out on both tails of GELU and GELU', U up to about 10^5 at
+    k = 12 (beyond fp16's range before the per-row scaling)."""
+    _mlp_backward_case(512, 2048, 8, 257, True, 2.5 ** k)
+
+
+def _mlp_backward_case(h, F, D, n, residual, x_scale):
     require_gpu()
     Fs = F // D
     w1 = [_rnd((Fs, h), 10 + d, 0.02) for d in range(D)]
     w2 = [_rnd((h, Fs), 30 + d, 0.02) for d in range(D)]
-    x = _rnd((n, h), 1)
+    x = _rnd((n, h), 1, x_scale)
     dy = _rnd((n, h), 2)
     dx_ref, dw1_ref, dw2_ref = O.mlp_backward(x, w1, w2, dy, residual=residual)
     # the oracle's per-shard factors of the weight gradients, for their rounding bounds
@@ -55,7 +67,7 @@ def test_mlp_backward(h, F, D, n, residual):
     ws = tsp.alloc_workspace(n, dims, D, tsp.WS_MLP_BWD)
     xd, dyd, w1d, w2d = x.to(DEV), dy.to(DEV), [t.to(DEV) for t in w1], [t.to(DEV) for t in w2]
     for start in sorted({0, D - 1}):
-        say(f"mlp backward h={h} F={F} D={D} n={n} start={start} residual={residual}")
+        say(f"mlp backward h={h} F={F} D={D} n={n} start={start} residual={residual} x scale={x_scale:g}")
         dx = bf16_nan((n, h), DEV)
         dw1 = [torch.full((Fs, h), float("nan"), device=DEV) for _ in range(D)]
         dw2 = [torch.full((h, Fs), float("nan"), device=DEV) for _ in range(D)]
